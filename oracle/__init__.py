@@ -1,0 +1,332 @@
+"""Scalar CPU oracle for the ZeRO-DP owner-rank step -- TEST INFRASTRUCTURE.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product library never loads it, and it imports
+nothing from the product package: the two share no code.
+
+The arithmetic lives in ``zero_oracle.c`` (plain scalar C, one element at a
+time, in the order the method defines).  This module marshals numpy arrays to
+it and composes whole steps, in the order the pages describe:
+
+  reduce each C_B bucket of the owner's shard   ("ZeRO：大模型训练的内存优化革命",
+                                                  3.1.2 and 3.2.2)
+  -> overflow flag and gradient norm            (pages silent; reading below)
+  -> Adam on the fp32 shard, cast to 2 bytes     (same page, 3.1.1; "SC-2020 ZeRO"
+                                                  notes, "Where Did All the Memory Go?")
+
+It also holds the per-rank byte ledger of the blog.vllbc.top ZeRO/DeepSpeed
+page (stage formulas, Table 1, worked examples) and that page's GB display
+rule, so the ledger can be compared with the printed tables.
+
+Parity status: every function here is pinned by tests/test_oracle*.py against
+the pages' printed tables, closed forms of Adam, library conversions (numpy
+float16, torch bfloat16) or brute force; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from fractions import Fraction
+from typing import Callable, List, Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+
+FP16 = 1
+BF16 = 2
+
+_lib = None
+
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+class _Bytes(ctypes.Structure):
+    _fields_ = [
+        ("shard_elems", ctypes.c_int64),
+        ("bytes_master", ctypes.c_int64), ("bytes_m", ctypes.c_int64),
+        ("bytes_v", ctypes.c_int64), ("bytes_grad", ctypes.c_int64),
+        ("bytes_param", ctypes.c_int64), ("bytes_shard_total", ctypes.c_int64),
+        ("bytes_staging", ctypes.c_int64),
+        ("per_rank_stage", ctypes.c_double * 4),
+        ("comm_bytes_stage", ctypes.c_double * 4),
+        ("comm_bytes_stage1_with_gather", ctypes.c_double),
+        ("comp_params", ctypes.c_double * 4),
+        ("comp_grads", ctypes.c_double * 4),
+        ("comp_optim", ctypes.c_double * 4),
+    ]
+
+
+def lib():
+    """Load liboracle.so, building it with gcc if it is not there yet."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = ctypes.CDLL(LIB_PATH)
+        L.oracle_f16_to_f32.restype = ctypes.c_float
+        L.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_f32.restype = ctypes.c_float
+        L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_f32_to_f16.restype = ctypes.c_uint16
+        L.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.oracle_lp_to_f32_array.argtypes = [_i32, _u16p, _i64, _f32p]
+        L.oracle_f32_to_lp_array.argtypes = [_i32, _f32p, _i64, _u16p]
+        L.oracle_partition.argtypes = [_i64, _i32, _i32, ctypes.POINTER(_i64),
+                                       ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
+        L.oracle_take_shard_u16.argtypes = [_u16p, _i64, _i32, _i32, _u16p]
+        L.oracle_take_shard_f32.argtypes = [_f32p, _i64, _i32, _i32, _f32p]
+        L.oracle_bucket_reduce.argtypes = [_i32, _i32, ctypes.POINTER(_u16p), _i64, _u16p]
+        L.oracle_flag_sumsq.argtypes = [_i32, _u16p, _i64, ctypes.c_float,
+                                        ctypes.POINTER(_i32), ctypes.POINTER(ctypes.c_double)]
+        L.oracle_adam_scalars.argtypes = [ctypes.c_double] * 5 + [_i32, _i64, ctypes.c_double, _f32p]
+        L.oracle_adam_update.argtypes = [_i32, _i64, _u16p, _f32p, _f32p, _f32p, _u16p, _f32p, _i32]
+        L.oracle_loss_scale_next.argtypes = [_i32, _i32, _i32, ctypes.c_double,
+                                             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]
+        L.oracle_state_bytes.argtypes = [_i64, _i32, _i32, _i64, _i32, _i32, _i32,
+                                         ctypes.POINTER(_Bytes)]
+        _lib = L
+    return _lib
+
+
+def _p16(a: np.ndarray):
+    assert a.dtype == np.uint16 and a.flags.c_contiguous
+    return a.ctypes.data_as(_u16p)
+
+
+def _p32(a: np.ndarray):
+    assert a.dtype == np.float32 and a.flags.c_contiguous
+    return a.ctypes.data_as(_f32p)
+
+
+# ---------------------------------------------------------------- 2-byte formats
+
+def lp_to_f32(lp: int, bits: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, np.float32)
+    lib().oracle_lp_to_f32_array(lp, _p16(bits), bits.size, _p32(out))
+    return out
+
+
+def f32_to_lp(lp: int, x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().oracle_f32_to_lp_array(lp, _p32(x), x.size, _p16(out))
+    return out
+
+
+# ---------------------------------------------------------------- partition (a1)
+
+def partition(psi: int, nd: int, rank: int):
+    """(S, begin, valid) of rank's shard of a flat Psi-element buffer."""
+    s, b, v = _i64(), _i64(), _i64()
+    lib().oracle_partition(psi, nd, rank, ctypes.byref(s), ctypes.byref(b), ctypes.byref(v))
+    return s.value, b.value, v.value
+
+
+def take_shard(flat: np.ndarray, nd: int, rank: int) -> np.ndarray:
+    flat = np.ascontiguousarray(flat)
+    s, _, _ = partition(flat.size, nd, rank)
+    if flat.dtype == np.uint16:
+        out = np.empty(s, np.uint16)
+        lib().oracle_take_shard_u16(_p16(flat), flat.size, nd, rank, _p16(out))
+    else:
+        flat = flat.astype(np.float32, copy=False)
+        out = np.empty(s, np.float32)
+        lib().oracle_take_shard_f32(_p32(flat), flat.size, nd, rank, _p32(out))
+    return out
+
+
+# ---------------------------------------------------------------- reduce (a2)
+
+def bucket_reduce(lp: int, contribs: Sequence[np.ndarray]) -> np.ndarray:
+    """Mean of R 2-byte contributions, fp32 accumulate in ascending order."""
+    cs = [np.ascontiguousarray(c, dtype=np.uint16) for c in contribs]
+    n = cs[0].size
+    assert all(c.size == n for c in cs)
+    arr = (_u16p * len(cs))(*[_p16(c) for c in cs])
+    out = np.empty(n, np.uint16)
+    lib().oracle_bucket_reduce(lp, len(cs), arr, n, _p16(out))
+    return out
+
+
+def reduce_shard(lp: int, contribs: Sequence[np.ndarray], bucket_elems: int) -> np.ndarray:
+    """Reduce a whole shard one C_B bucket at a time, buckets in ascending order."""
+    n = contribs[0].size
+    out = np.empty(n, np.uint16)
+    for off in range(0, n, bucket_elems):
+        end = min(n, off + bucket_elems)
+        out[off:end] = bucket_reduce(lp, [c[off:end] for c in contribs])
+    return out
+
+
+# ---------------------------------------------------------------- flag / norm (a3)
+
+def flag_sumsq(lp: int, g: np.ndarray, scale: float, flag: int = 0, sumsq: float = 0.0):
+    g = np.ascontiguousarray(g, dtype=np.uint16)
+    f = _i32(flag)
+    s = ctypes.c_double(sumsq)
+    inv = float(np.float32(1.0 / scale))
+    lib().oracle_flag_sumsq(lp, _p16(g), g.size, inv, ctypes.byref(f), ctypes.byref(s))
+    return f.value, s.value
+
+
+# ---------------------------------------------------------------- Adam (a4, a5)
+
+@dataclass
+class AdamHP:
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.0
+    bias_correction: int = 1
+    wd_mode: int = 0          # 0 decoupled (AdamW form), 1 L2
+    initial_step: int = 0
+
+
+@dataclass
+class LossScale:
+    init_scale: float = 1.0
+    dynamic: int = 1
+    growth_interval: int = 1000
+    min_scale: float = 1.0
+
+
+def adam_scalars(hp: AdamHP, t: int, scale: float) -> np.ndarray:
+    out = np.empty(10, np.float32)
+    lib().oracle_adam_scalars(hp.beta1, hp.beta2, hp.lr, hp.eps, hp.weight_decay,
+                              hp.bias_correction, t, scale, _p32(out))
+    return out
+
+
+def adam_update(lp: int, grad: np.ndarray, master: np.ndarray, m: np.ndarray,
+                v: np.ndarray, param: np.ndarray, sc: np.ndarray, wd_mode: int = 0) -> None:
+    """In place: master, m, v (fp32) and param (2-byte bits)."""
+    n = master.size
+    for a in (grad, param):
+        assert a.size == n and a.dtype == np.uint16
+    for a in (master, m, v):
+        assert a.size == n and a.dtype == np.float32
+    lib().oracle_adam_update(lp, n, _p16(grad), _p32(master), _p32(m), _p32(v),
+                             _p16(param), _p32(np.ascontiguousarray(sc, np.float32)), wd_mode)
+
+
+def loss_scale_next(overflow: int, ls: LossScale, scale: float, good_steps: int):
+    s = ctypes.c_double(scale)
+    g = _i64(good_steps)
+    lib().oracle_loss_scale_next(overflow, ls.dynamic, ls.growth_interval, ls.min_scale,
+                                 ctypes.byref(s), ctypes.byref(g))
+    return s.value, g.value
+
+
+# ---------------------------------------------------------------- whole steps
+
+@dataclass
+class StepInfo:
+    overflow: int
+    skipped: int
+    step_t: int
+    grad_norm: float
+    scale_used: float
+    scale_next: float
+
+
+@dataclass
+class ShardState:
+    """The owner's shard: fp32 master / m / v and 2-byte grad / param bits."""
+    lp: int
+    master: np.ndarray
+    m: np.ndarray
+    v: np.ndarray
+    grad: np.ndarray
+    param: np.ndarray
+    t: int = 0
+    scale: float = 1.0
+    good_steps: int = 0
+
+    def copy(self) -> "ShardState":
+        return ShardState(self.lp, self.master.copy(), self.m.copy(), self.v.copy(),
+                          self.grad.copy(), self.param.copy(), self.t, self.scale,
+                          self.good_steps)
+
+
+def new_state(lp: int, master: np.ndarray, m: np.ndarray, v: np.ndarray,
+              hp: AdamHP, ls: LossScale) -> ShardState:
+    n = master.size
+    st = ShardState(lp, np.array(master, np.float32), np.array(m, np.float32),
+                    np.array(v, np.float32), np.zeros(n, np.uint16), np.zeros(n, np.uint16),
+                    t=hp.initial_step, scale=float(ls.init_scale), good_steps=0)
+    st.param = f32_to_lp(lp, st.master)
+    return st
+
+
+def step(st: ShardState, contribs: Sequence[np.ndarray], bucket_elems: int,
+         hp: AdamHP, ls: LossScale, forced_flag: Optional[int] = None) -> StepInfo:
+    """One owner-rank step on the whole shard held in memory.
+
+    forced_flag lets a caller that evaluates a sample of a larger shard supply
+    the overflow decision taken over the full shard (chunked evaluation)."""
+    st.grad = reduce_shard(st.lp, contribs, bucket_elems)
+    flag, sumsq = flag_sumsq(st.lp, st.grad, st.scale)
+    if forced_flag is not None:
+        flag = int(forced_flag)
+    scale_used = st.scale
+    if flag:
+        skipped = 1
+    else:
+        skipped = 0
+        st.t += 1
+        sc = adam_scalars(hp, st.t, st.scale)
+        adam_update(st.lp, st.grad, st.master, st.m, st.v, st.param, sc, hp.wd_mode)
+    st.scale, st.good_steps = loss_scale_next(flag, ls, st.scale, st.good_steps)
+    return StepInfo(flag, skipped, st.t, float(np.sqrt(sumsq)), scale_used, st.scale)
+
+
+def run_steps(st: ShardState, contribs_for_step: Callable[[int, float], Sequence[np.ndarray]],
+              nsteps: int, bucket_elems: int, hp: AdamHP, ls: LossScale) -> List[StepInfo]:
+    """contribs_for_step(step_index, loss_scale) -> the R contributions of that step."""
+    infos = []
+    for s in range(nsteps):
+        infos.append(step(st, contribs_for_step(s, st.scale), bucket_elems, hp, ls))
+    return infos
+
+
+# ---------------------------------------------------------------- ledger (a6)
+
+def state_bytes(psi: int, nd: int, n_contrib: int = 1, bucket_elems: int = 1,
+                lp_bytes: int = 2, param_bytes: int = 2, k_optim: int = 12) -> dict:
+    out = _Bytes()
+    lib().oracle_state_bytes(psi, nd, n_contrib, bucket_elems, lp_bytes, param_bytes,
+                             k_optim, ctypes.byref(out))
+    d = {}
+    for name, _ in _Bytes._fields_:
+        val = getattr(out, name)
+        d[name] = list(val) if hasattr(val, "__len__") else val
+    return d
+
+
+def display_gb(x) -> str:
+    """GB display rule of the blog.vllbc.top ZeRO/DeepSpeed page (calculator
+    rules under the stage formulas): GB = 1e9 bytes; at or above 100 GB the
+    integer part is shown; from 10 to 100 GB at most one decimal; below 10 GB
+    at most two decimals; trailing zeros are dropped.  Table 1 shows that the
+    >= 100 case truncates (4187.5 -> 4187) and that smaller values round half
+    up (41.25 -> 41.3).  x is an exact byte count (int or Fraction)."""
+    g = Fraction(x) / Fraction(10 ** 9)
+    if g >= 100:
+        q = int(g)                       # floor for non-negative values
+        return str(q)
+    digits = 1 if g >= 10 else 2
+    scale = 10 ** digits
+    q = (g * scale + Fraction(1, 2)).__floor__()
+    s = f"{q // scale}.{q % scale:0{digits}d}".rstrip("0").rstrip(".")
+    return s
