@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Throughput of the owner-rank ZeRO-DP step on one MI355X.
+
+One step = every C_B bucket reduce of the owner's shard, the overflow check
+(with its one host synchronisation) and the fused Adam + cast, through the C
+ABI, on the 128B-parameter workload at Nd = 64: a 2.0e9-element shard, 4
+contributions, C_B = 2e8, fp16 storage, loss scale 4096, AdamW lr 6e-5, wd 0.1.
+Inputs are seeded synthetic tensors resident in HBM before timing starts; the
+same contribution batch feeds every step (each step still reads and writes
+every byte).
+
+Prints one JSON line: params/s of the shard (Adam-updated parameters per
+second), the step time, the dominant kernel's achieved HBM bandwidth against
+the 8 TB/s peak (HIP events on the launch stream), and the CPU oracle timed on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, AMD public spec
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_adam_128b.json")
+KERNEL_SRC = os.path.join(ROOT, "zero_dp_sharded_amd", "csrc", "zero_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(per_launch_elems: int):
+    """HBM bytes per Adam launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    if t.get("elems_per_launch") != per_launch_elems:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, state_host, contribs_host, bucket_elems):
+    import oracle
+    hp = oracle.AdamHP(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                       weight_decay=w.weight_decay)
+    ls = oracle.LossScale(init_scale=w.scale, dynamic=w.dynamic)
+    master, m, v = state_host
+    st = oracle.new_state(oracle.FP16 if w.lp == "fp16" else oracle.BF16, master, m, v, hp, ls)
+    t0 = time.perf_counter()
+    oracle.step(st, contribs_host, bucket_elems, hp, ls)
+    dt = time.perf_counter() - t0
+    return master.size / dt, dt
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="128b")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 27,
+                    help="shard elements the CPU oracle runs on (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the owner-rank step on one GPU only; "
+              "multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import zero_dp_sharded_amd as zs
+    from zero_dp_sharded_amd import synth
+
+    zs.lib()  # fails loudly when the HIP library is not built
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    w = synth.WORKLOADS[args.workload]
+    S, R, cb = w.shard, w.R, w.bucket_elems
+    lp_t = w.torch_lp
+    print(f"[bench] workload {w.name}: S={S} R={R} C_B={cb}", file=sys.stderr, flush=True)
+
+    master, m, v = synth.init_state(w, dev, seed=0)
+    grad = torch.zeros(S, dtype=lp_t, device=dev)
+    param = master.to(lp_t)
+    bufs = synth.alloc_contribs(w, dev)
+    synth.fill_contribs(w, bufs, 0, w.scale, seed=0)
+    torch.cuda.synchronize()
+    print("[bench] inputs resident", file=sys.stderr, flush=True)
+
+    hp = zs.AdamHParams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                        weight_decay=w.weight_decay)
+    ls = zs.LossScaleCfg(init_scale=w.scale, dynamic=w.dynamic)
+    h = zs.zero_shard_init(master, m, v, grad, param, psi=w.psi, nd=w.nd, rank=w.rank,
+                           bucket_elems=cb, hp=hp, ls=ls)
+    stream = torch.cuda.current_stream()
+    ptrs = [b.data_ptr() for b in bufs]
+    offs = [(off, min(cb, S - off)) for off in range(0, S, cb)]
+
+    def step(ev=None):
+        for k, (off, ln) in enumerate(offs):
+            if ev is not None:
+                ev["r"][k][0].record(stream)
+            zs.zero_bucket_reduce(h, [p + 2 * off for p in ptrs], off, ln, stream)
+            if ev is not None:
+                ev["r"][k][1].record(stream)
+        info = zs.zero_overflow_check(h, stream)
+        if ev is not None:
+            ev["a"][0].record(stream)
+        zs.zero_adam_step(h, None, stream)
+        if ev is not None:
+            ev["a"][1].record(stream)
+        return info
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done", file=sys.stderr, flush=True)
+
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [{"r": [(mk(), mk()) for _ in offs], "a": (mk(), mk())} for _ in range(args.steps)]
+    skipped = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        info = step(evs[k])
+        skipped += info.overflow
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    adam_ms = [e["a"][0].elapsed_time(e["a"][1]) for e in evs]
+    red_ms = [sum(a.elapsed_time(b) for a, b in e["r"]) for e in evs]
+    adam_avg = sum(adam_ms) / len(adam_ms)
+    red_avg = sum(red_ms) / len(red_ms)
+    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step, adam {adam_avg:.3f} ms, "
+          f"reduce {red_avg:.3f} ms, skipped {skipped}", file=sys.stderr, flush=True)
+
+    adam_bytes = 28 * S                      # grad 2 + master/m/v 12 read; 12 + param 2 written
+    reduce_bytes = (2 * R + 2) * S
+    achieved = adam_bytes / (adam_avg * 1e-3) / 1e9
+    step_bytes = adam_bytes + reduce_bytes
+    traffic = measured_traffic(S)
+
+    cpu = None
+    if args.cpu_sample > 0:
+        n = min(args.cpu_sample, S)
+        state_host = tuple(t[:n].cpu().numpy() for t in (master, m, v))
+        contribs_host = [b[:n].view(torch.int16).cpu().numpy().view(np.uint16) for b in bufs]
+        rate, dt = cpu_baseline(w, state_host, contribs_host, cb)
+        cpu = {"value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
+               "sample": f"one full step (reduce of {R} contributions, flag/norm, Adam) on the "
+                         f"first {n} elements of the same shard; {dt:.1f} s single-threaded"}
+        del state_host, contribs_host
+    zs.zero_shard_destroy(h)
+
+    out = {
+        "metric": "Adam-updated params/sec per rank shard + achieved HBM GB/s vs MI355X peak",
+        "value": S / (ms_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; same contribution batch every step)",
+        "config": {"workload": w.name, "psi": w.psi, "nd": w.nd, "rank": w.rank,
+                   "shard_elems": S, "contributions": R, "bucket_elems": cb,
+                   "storage": w.lp, "loss_scale": w.scale, "lr": w.lr,
+                   "weight_decay": w.weight_decay},
+        "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
+        "step_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "kernels_ms": {"adam": adam_avg, "reduce_all_buckets": red_avg,
+                       "reduce_gbs": reduce_bytes / (red_avg * 1e-3) / 1e9},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "adam_kernel<fp16, decoupled wd>",
+                     "algorithmic_bytes_per_launch": adam_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,251 @@
+/*
+ * zero_shard.h -- C ABI of libzeroshard.so: the owner-rank step of ZeRO-DP
+ * optimizer-state and gradient partitioning (P_os / P_os+g) on one gfx950 GPU.
+ *
+ * The method (pages cited by title and section):
+ *  - "ZeRO：大模型训练的内存优化革命", 3.1.1: with P_os each of the Nd
+ *    data-parallel processes keeps and updates only 1/Nd of the optimizer
+ *    state; at the end of the step the updated parameters are all-gathered.
+ *  - same page, 3.1.2: with P_os+g the gradients are reduced only on the process
+ *    that owns the partition (a reduce-scatter in place of the all-reduce).
+ *  - same page, 3.2.2, and the "SC-2020 ZeRO" notes, "C_B: Constant Size
+ *    Buffers": the reduce works through constant-size fused buffers.
+ *  - "AI论文陪读·ZeRO" section 01 and the blog.vllbc.top ZeRO/DeepSpeed page
+ *    (ledger and stage formulas): 2-byte params and grads, 12 bytes of fp32
+ *    master / momentum / variance per parameter, 16 Psi in total, 16 Psi/Nd per
+ *    rank when everything is partitioned.
+ *  - "SC-2020 ZeRO" notes, "Where Did All the Memory Go?": the update runs on the
+ *    fp32 master weights, which are then cast back to the 2-byte format.
+ *
+ * One call sequence per training step, on one handle:
+ *     zero_bucket_reduce   x nbuckets  (ascending, contiguous, covering [0, S))
+ *     zero_overflow_check            (synchronises the stream once)
+ *     zero_adam_step                 (skipped when the check found inf/nan)
+ *
+ * Conventions for every function:
+ *  - Returns a zero_status.  Arguments are validated before anything is
+ *    launched; on any error nothing is launched and no handle state changes.
+ *    zero_last_error() then holds a one-line explanation (thread-local).
+ *  - No exceptions, aborts or prints cross this boundary.
+ *  - "Device pointer" means memory of the device that was current when the
+ *    handle was created.  Any 2-byte-aligned address is accepted for 2-byte
+ *    arrays and any 4-byte-aligned address for fp32 arrays; the kernels peel
+ *    unaligned heads and tails.
+ *  - A handle is not thread-safe.  Separate handles are independent.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZERO_SHARD_ABI_VERSION 1
+/* Largest number of contributions one bucket reduce accepts. */
+#define ZERO_MAX_CONTRIB 64
+
+typedef enum {
+    ZERO_OK = 0,
+    ZERO_ERR_INVALID_ARG = 1, /* NULL pointer, value out of range, misaligned */
+    ZERO_ERR_STATE = 2,       /* call out of order, bad coverage, dead handle */
+    ZERO_ERR_HIP = 3,         /* the HIP runtime reported an error            */
+    ZERO_ERR_OOM = 4,         /* workspace allocation failed                  */
+    ZERO_ERR_UNSUPPORTED = 5  /* valid request this build does not implement  */
+} zero_status;
+
+/* 2-byte storage format of grads and params (IEEE binary16 or bfloat16). */
+typedef enum { ZERO_FP16 = 1, ZERO_BF16 = 2 } zero_lp_dtype;
+
+/* Weight decay: decoupled (AdamW form, u += wd * p before p -= lr * u) or L2
+ * (g += wd * p before the moments). */
+typedef enum { ZERO_WD_DECOUPLED = 0, ZERO_WD_L2 = 1 } zero_wd_mode;
+
+typedef struct zero_shard_s* zero_shard_t; /* opaque */
+
+/*
+ * The owner's shard.  Rank `rank` of `nd` owns elements [rank*S, (rank+1)*S) of
+ * the flat Psi-element parameter space, S = ceil(psi / nd) (the last shard is
+ * zero-padded).  All five arrays hold S elements, are caller-owned device
+ * memory, must not overlap, and must outlive the handle:
+ *   master, exp_avg, exp_avg_sq : fp32 master weights, first and second moments
+ *   grad_shard                  : 2-byte reduced gradient (written by the reduce)
+ *   param_shard                 : 2-byte params: the owner's slice of the
+ *                                 parameter all-gather buffer (written by Adam)
+ * bucket_elems is C_B: every bucket but the last of a step holds exactly C_B
+ * elements.
+ */
+typedef struct {
+    int64_t psi;
+    int32_t nd;
+    int32_t rank;
+    int64_t bucket_elems;
+    zero_lp_dtype lp;
+    float* master;
+    float* exp_avg;
+    float* exp_avg_sq;
+    void* grad_shard;
+    void* param_shard;
+} zero_shard_desc;
+
+/* Textbook Adam (Kingma & Ba 2015, Algorithm 1); the pages give no formula.
+ * Ranges: lr >= 0, 0 <= beta1 < 1, 0 <= beta2 < 1, eps > 0, weight_decay >= 0,
+ * initial_step >= 0 (number of steps already applied). */
+typedef struct {
+    double lr, beta1, beta2, eps, weight_decay;
+    int32_t bias_correction; /* 0 or 1 */
+    zero_wd_mode wd_mode;
+    int64_t initial_step;
+} zero_adam_hparams;
+
+/* Loss scaling (not on the pages).  dynamic = 1: an overflowing step halves
+ * the scale (not below min_scale); growth_interval clean steps in a row double
+ * it.  dynamic = 0: the scale stays at init_scale; an overflowing step is still
+ * skipped.  init_scale > 0, min_scale > 0, growth_interval >= 1. */
+typedef struct {
+    double init_scale;
+    int32_t dynamic;
+    int32_t growth_interval;
+    double min_scale;
+} zero_loss_scale_cfg;
+
+/* Result of a check or a step.  grad_norm is the L2 norm of the unscaled
+ * shard gradient (fp64 accumulation; inf or nan when the step overflows).
+ * step_t counts applied steps.  scale_used is the loss scale the gradients of
+ * this step carry; scale_next the one the next step's gradients must carry. */
+typedef struct {
+    int32_t overflow;
+    int32_t skipped;
+    int64_t step_t;
+    double grad_norm;
+    double scale_used;
+    double scale_next;
+} zero_step_info;
+
+/* Per-rank ledger.  Allocation of this build's shard, and the analytic per-rank
+ * model-state bytes of stages 0..3 with their components (params, grads,
+ * optimizer state) and the per-step communication volume in bytes, from the
+ * blog.vllbc.top ZeRO/DeepSpeed page (stage formulas, Table 1, worked examples,
+ * communication ledger):
+ *   Stage 0 = (2b+K) Psi, Stage 1 = 2b Psi + K Psi/Nd,
+ *   Stage 2 = b Psi + (b+K) Psi/Nd, Stage 3 = (2b+K) Psi/Nd,
+ *   communication 2 b Psi for stages 0-2 and 3 b Psi for stage 3 (stage 1 with
+ *   the step-end parameter gather: 3 b Psi). */
+typedef struct {
+    int64_t shard_elems;
+    int64_t bytes_master, bytes_m, bytes_v, bytes_grad, bytes_param;
+    int64_t bytes_shard_total; /* = 16 * S for 2-byte grads and params */
+    int64_t bytes_staging;     /* = n_contrib * C_B * 2: one bucket of contributions */
+    double per_rank_stage[4];
+    double comm_bytes_stage[4];
+    double comm_bytes_stage1_with_gather;
+    double comp_params[4], comp_grads[4], comp_optim[4];
+} zero_state_bytes_t;
+
+/*
+ * Ledger for mixed-precision Adam (b = 2, K = 12).  Pure host arithmetic, no
+ * device access.  psi >= 1, nd >= 1, n_contrib in [1, ZERO_MAX_CONTRIB],
+ * bucket_elems >= 1, lp a zero_lp_dtype, out non-NULL.
+ */
+zero_status zero_state_bytes(int64_t psi, int32_t nd, int32_t n_contrib,
+                             int64_t bucket_elems, zero_lp_dtype lp,
+                             zero_state_bytes_t* out);
+
+/*
+ * Same ledger with the parameter byte width b (2 or 4) and optimizer multiplier
+ * K (12 mixed-precision Adam, 8 fp32 Adam, 4 SGD with momentum, 0 SGD) of the
+ * page's (2b+K) Psi extension (its group C examples).  Allocation fields still
+ * describe this build's Adam shard.
+ */
+zero_status zero_state_bytes_ex(int64_t psi, int32_t nd, int32_t n_contrib,
+                                int64_t bucket_elems, zero_lp_dtype lp,
+                                int32_t param_bytes, int32_t k_optim,
+                                zero_state_bytes_t* out);
+
+/*
+ * Create a handle bound to the current device.  Copies *desc, *hp and *ls.
+ * Allocates a small device workspace (per-block partials, under 64 KiB) and 64
+ * bytes of pinned host memory; touches none of the caller's arrays.
+ * Errors: INVALID_ARG (NULL argument or pointer in desc, psi < 1, nd < 1, rank
+ * outside [0, nd), bucket_elems < 1, unknown lp, misaligned array, hp or ls
+ * out of range), OOM, HIP.
+ */
+zero_status zero_shard_init(const zero_shard_desc* desc, const zero_adam_hparams* hp,
+                            const zero_loss_scale_cfg* ls, zero_shard_t* out);
+
+/*
+ * Reduce one C_B bucket of the owner's shard from n_contrib contributions
+ * ("ZeRO：大模型训练的内存优化革命" 3.1.2: gradients reduced on the owner).
+ * contribs: host array of n_contrib device pointers, each to bucket_len
+ * 2-byte gradients (contribution r, elements [bucket_off, bucket_off+len) of
+ * the shard).  Per element: fp32 sum over r = 0..R-1 in that order starting
+ * from +0, times fp32(1/R), rounded to the 2-byte format into
+ * grad_shard[bucket_off + i].  The same pass records the overflow flag and the
+ * squared norm of the unscaled values for zero_overflow_check.
+ * Asynchronous on `stream`; contribution memory must stay valid until the
+ * kernel has run.  Buckets of one step must be submitted in ascending,
+ * contiguous order starting at 0; bucket_len must equal bucket_elems except
+ * for the last bucket, which ends at S.
+ * Errors: INVALID_ARG (NULL, n_contrib outside [1, 64], bucket outside [0, S),
+ * bucket_len < 1 or > bucket_elems, misaligned pointer), STATE (dead handle,
+ * bucket not the next one, step already checked), HIP.
+ */
+zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int32_t n_contrib,
+                               int64_t bucket_off, int64_t bucket_len, void* stream);
+
+/*
+ * Finish the overflow check of the step: OR of "not finite" over the stored
+ * 2-byte gradient shard and its unscaled squared norm, summed over per-block
+ * partials in a fixed order (bitwise reproducible).  If no bucket was reduced
+ * this step, the stored grad_shard is scanned instead (for callers that fill
+ * it themselves).  Synchronises `stream` and fills *out (skipped = overflow;
+ * step_t is the count before this step).  Calling it again before
+ * zero_adam_step returns the same result.
+ * Errors: INVALID_ARG (NULL out), STATE (dead handle, buckets cover only part
+ * of the shard), HIP.
+ */
+zero_status zero_overflow_check(zero_shard_t h, void* stream, zero_step_info* out);
+
+/*
+ * Apply the step decided by zero_overflow_check.  On overflow: nothing is
+ * launched, the states are unchanged, t is unchanged, and with dynamic scaling
+ * the scale halves.  Otherwise t += 1 and, per element (fp32, every operation
+ * rounded to nearest even, no fused multiply-add):
+ *     g = f32(grad) * fp32(1/scale)            [L2 mode: g = g + wd*p]
+ *     m = b1*m + (1-b1)*g ;  v = b2*v + (1-b2)*(g*g)
+ *     u = (m/bc1) / (sqrt(v/bc2) + eps)         [decoupled: u = u + wd*p]
+ *     p = p - lr*u ;  param = rne_2byte(p)
+ * with b1, b2, lr, eps, wd the fp32 roundings of the hyper-parameters,
+ * bc_k = fp32(1 - b_k^t) (b_k^t a product of t fp64 factors; 1 when bias
+ * correction is off).  hp = NULL uses the values given at init; otherwise *hp
+ * is used for this step only (its initial_step is ignored).  Asynchronous on
+ * `stream`; *out (may be NULL) gets the step's result.
+ * Errors: STATE (dead handle, no completed check this step), INVALID_ARG (hp out
+ * of range), HIP.
+ */
+zero_status zero_adam_step(zero_shard_t h, const zero_adam_hparams* hp, void* stream,
+                           zero_step_info* out);
+
+/* Step counter, current loss scale and clean-step count (for checkpoints). */
+zero_status zero_shard_get_counters(zero_shard_t h, int64_t* step_t, double* scale,
+                                    int64_t* good_steps);
+/* Restore them between steps (phase must be idle).  step_t >= 0, scale > 0,
+ * good_steps >= 0. */
+zero_status zero_shard_set_counters(zero_shard_t h, int64_t step_t, double scale,
+                                    int64_t good_steps);
+
+/* Release the workspace.  The caller's arrays are untouched.  The handle is
+ * dead afterwards; a second destroy returns ZERO_ERR_STATE. */
+zero_status zero_shard_destroy(zero_shard_t h);
+
+const char* zero_status_str(zero_status s);
+const char* zero_last_error(void);
+int zero_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_SHARD_H */

@@ -1,0 +1,158 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/zero_shard.h declares, its pure-host ledger equals the oracle's, and
+argument validation rejects bad calls before any device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import zero_dp_sharded_amd as zs
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "zero_shard.h")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zero_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = zs.lib()
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(zs.ABI_SYMBOLS)
+
+
+def test_abi_version_and_status_strings():
+    assert zs.zero_abi_version() == 1
+    for code, name in [(0, "ZERO_OK"), (1, "ZERO_ERR_INVALID_ARG"), (2, "ZERO_ERR_STATE"),
+                       (3, "ZERO_ERR_HIP"), (4, "ZERO_ERR_OOM"), (5, "ZERO_ERR_UNSUPPORTED")]:
+        assert zs.zero_status_str(code) == name
+
+
+def test_struct_layouts_match_header():
+    # sizes fixed by the header's field order on x86-64
+    assert ctypes.sizeof(zs.ZeroShardDesc) == 72
+    assert ctypes.sizeof(zs.ZeroAdamHParams) == 56
+    assert ctypes.sizeof(zs.ZeroLossScaleCfg) == 24
+    assert ctypes.sizeof(zs.ZeroStepInfo) == 40
+    assert ctypes.sizeof(zs.ZeroStateBytes) == 8 * 8 + 8 * 4 * 2 + 8 + 8 * 4 * 3
+
+
+CASES = [(1_048_576, 4, 4, 50_000_000), (1_500_000_000, 8, 8, 50_000_000),
+         (7_500_000_000, 64, 8, 50_000_000), (13_000_000_000, 16, 16, 50_000_000),
+         (128_000_000_000, 64, 4, 200_000_000), (10, 4, 1, 1), (10**12, 1024, 64, 7),
+         (999_999_937, 3, 5, 12345)]
+
+
+@pytest.mark.parametrize("psi,nd,R,cb", CASES)
+def test_state_bytes_equals_oracle(oracle, psi, nd, R, cb):
+    a = zs.zero_state_bytes(psi, nd, R, cb, zs.ZERO_FP16)
+    b = oracle.state_bytes(psi, nd, R, cb)
+    assert a == b
+
+
+@pytest.mark.parametrize("b,K", [(2, 12), (4, 8), (4, 4), (4, 0)])
+def test_state_bytes_ex_equals_oracle(oracle, b, K):
+    for psi, nd, R, cb in CASES:
+        a = zs.zero_state_bytes_ex(psi, nd, R, cb, zs.ZERO_BF16, b, K)
+        o = oracle.state_bytes(psi, nd, R, cb, param_bytes=b, k_optim=K)
+        assert a == o
+
+
+def test_state_bytes_128b_allocation():
+    d = zs.zero_state_bytes(128_000_000_000, 64, 4, 200_000_000, zs.ZERO_FP16)
+    assert d["shard_elems"] == 2_000_000_000
+    assert d["bytes_shard_total"] == 32_000_000_000 == d["per_rank_stage"][3]
+
+
+@pytest.mark.parametrize("args", [(0, 4, 1, 1), (10, 0, 1, 1), (10, 4, 0, 1), (10, 4, 65, 1),
+                                  (10, 4, 1, 0)])
+def test_state_bytes_rejects(args):
+    with pytest.raises(zs.ZeroError) as e:
+        zs.zero_state_bytes(*args, zs.ZERO_FP16)
+    assert e.value.status == zs.ZERO_ERR_INVALID_ARG
+    with pytest.raises(zs.ZeroError):
+        zs.zero_state_bytes(10, 4, 1, 1, 3)
+    with pytest.raises(zs.ZeroError):
+        zs.zero_state_bytes_ex(10, 4, 1, 1, zs.ZERO_FP16, 3, 12)
+
+
+def _desc(**over):
+    d = dict(psi=1000, nd=4, rank=0, bucket_elems=100, lp=zs.ZERO_FP16, master=0x1000,
+             exp_avg=0x20000, exp_avg_sq=0x40000, grad_shard=0x60000, param_shard=0x80000)
+    d.update(over)
+    return zs.ZeroShardDesc(**d)
+
+
+GOOD_HP = zs.ZeroAdamHParams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 0, 0)
+GOOD_LS = zs.ZeroLossScaleCfg(1024.0, 1, 1000, 1.0)
+
+
+@pytest.mark.parametrize("over", [
+    dict(psi=0), dict(nd=0), dict(rank=4), dict(rank=-1), dict(bucket_elems=0), dict(lp=7),
+    dict(master=0), dict(exp_avg=0), dict(exp_avg_sq=0), dict(grad_shard=0), dict(param_shard=0),
+    dict(master=0x1002), dict(grad_shard=0x60001), dict(exp_avg=0x1100),  # misaligned, overlap
+])
+def test_init_rejects_bad_desc_before_device_work(over):
+    h = ctypes.c_void_p()
+    s = zs.lib().zero_shard_init(ctypes.byref(_desc(**over)), ctypes.byref(GOOD_HP),
+                                 ctypes.byref(GOOD_LS), ctypes.byref(h))
+    assert s == zs.ZERO_ERR_INVALID_ARG, zs.zero_last_error()
+    assert h.value is None
+    assert zs.zero_last_error()
+
+
+@pytest.mark.parametrize("field,val", [("lr", -1.0), ("lr", float("nan")), ("beta1", 1.0),
+                                       ("beta2", -0.1), ("eps", 0.0), ("eps", 1e-50),
+                                       ("weight_decay", -0.1), ("bias_correction", 2),
+                                       ("wd_mode", 5), ("initial_step", -1)])
+def test_init_rejects_bad_hparams(field, val):
+    hp = zs.ZeroAdamHParams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 0, 0)
+    setattr(hp, field, val)
+    h = ctypes.c_void_p()
+    s = zs.lib().zero_shard_init(ctypes.byref(_desc()), ctypes.byref(hp), ctypes.byref(GOOD_LS),
+                                 ctypes.byref(h))
+    assert s == zs.ZERO_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field,val", [("init_scale", 0.0), ("init_scale", float("inf")),
+                                       ("dynamic", 2), ("growth_interval", 0), ("min_scale", -1.0)])
+def test_init_rejects_bad_loss_scale(field, val):
+    ls = zs.ZeroLossScaleCfg(1024.0, 1, 1000, 1.0)
+    setattr(ls, field, val)
+    h = ctypes.c_void_p()
+    s = zs.lib().zero_shard_init(ctypes.byref(_desc()), ctypes.byref(GOOD_HP), ctypes.byref(ls),
+                                 ctypes.byref(h))
+    assert s == zs.ZERO_ERR_INVALID_ARG
+
+
+def test_null_and_dead_handles():
+    L = zs.lib()
+    h = ctypes.c_void_p()
+    assert L.zero_shard_init(None, ctypes.byref(GOOD_HP), ctypes.byref(GOOD_LS),
+                             ctypes.byref(h)) == zs.ZERO_ERR_INVALID_ARG
+    assert L.zero_shard_init(ctypes.byref(_desc()), None, ctypes.byref(GOOD_LS),
+                             ctypes.byref(h)) == zs.ZERO_ERR_INVALID_ARG
+    assert L.zero_shard_init(ctypes.byref(_desc()), ctypes.byref(GOOD_HP), None,
+                             ctypes.byref(h)) == zs.ZERO_ERR_INVALID_ARG
+    assert L.zero_shard_destroy(None) == zs.ZERO_ERR_STATE
+    bogus = ctypes.c_void_p(0xDEAD0)
+    info = zs.ZeroStepInfo()
+    arr = (ctypes.c_void_p * 1)(0x1000)
+    assert L.zero_bucket_reduce(bogus, arr, 1, 0, 1, None) == zs.ZERO_ERR_STATE
+    assert L.zero_overflow_check(bogus, None, ctypes.byref(info)) == zs.ZERO_ERR_STATE
+    assert L.zero_adam_step(bogus, None, None, ctypes.byref(info)) == zs.ZERO_ERR_STATE
+    assert L.zero_shard_destroy(bogus) == zs.ZERO_ERR_STATE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(zs, "_lib", None)
+    monkeypatch.setattr(zs, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        zs.zero_abi_version()

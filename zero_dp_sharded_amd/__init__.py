@@ -1,0 +1,311 @@
+"""zero_dp_sharded_amd -- the owner-rank step of ZeRO-DP (P_os / P_os+g) on gfx950.
+
+A thin ctypes binding of libzeroshard.so (include/zero_shard.h).  Functions
+carry the C names and do argument marshalling only: torch tensors become
+device pointers and a torch stream becomes its hipStream_t.  Every step of the
+path runs in the library's HIP kernels; there is no CPU fallback, and calling
+anything without the built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libzeroshard.so")
+
+ZERO_OK = 0
+ZERO_ERR_INVALID_ARG = 1
+ZERO_ERR_STATE = 2
+ZERO_ERR_HIP = 3
+ZERO_ERR_OOM = 4
+ZERO_ERR_UNSUPPORTED = 5
+
+ZERO_FP16 = 1
+ZERO_BF16 = 2
+ZERO_WD_DECOUPLED = 0
+ZERO_WD_L2 = 1
+ZERO_MAX_CONTRIB = 64
+
+ABI_SYMBOLS = (
+    "zero_state_bytes", "zero_state_bytes_ex", "zero_shard_init", "zero_bucket_reduce",
+    "zero_overflow_check", "zero_adam_step", "zero_shard_get_counters",
+    "zero_shard_set_counters", "zero_shard_destroy", "zero_status_str", "zero_last_error",
+    "zero_abi_version",
+)
+
+_i32, _i64, _f64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+
+
+class ZeroShardDesc(ctypes.Structure):
+    _fields_ = [("psi", _i64), ("nd", _i32), ("rank", _i32), ("bucket_elems", _i64),
+                ("lp", ctypes.c_int), ("master", _vp), ("exp_avg", _vp), ("exp_avg_sq", _vp),
+                ("grad_shard", _vp), ("param_shard", _vp)]
+
+
+class ZeroAdamHParams(ctypes.Structure):
+    _fields_ = [("lr", _f64), ("beta1", _f64), ("beta2", _f64), ("eps", _f64),
+                ("weight_decay", _f64), ("bias_correction", _i32), ("wd_mode", ctypes.c_int),
+                ("initial_step", _i64)]
+
+
+class ZeroLossScaleCfg(ctypes.Structure):
+    _fields_ = [("init_scale", _f64), ("dynamic", _i32), ("growth_interval", _i32),
+                ("min_scale", _f64)]
+
+
+class ZeroStepInfo(ctypes.Structure):
+    _fields_ = [("overflow", _i32), ("skipped", _i32), ("step_t", _i64), ("grad_norm", _f64),
+                ("scale_used", _f64), ("scale_next", _f64)]
+
+
+class ZeroStateBytes(ctypes.Structure):
+    _fields_ = [("shard_elems", _i64), ("bytes_master", _i64), ("bytes_m", _i64),
+                ("bytes_v", _i64), ("bytes_grad", _i64), ("bytes_param", _i64),
+                ("bytes_shard_total", _i64), ("bytes_staging", _i64),
+                ("per_rank_stage", _f64 * 4), ("comm_bytes_stage", _f64 * 4),
+                ("comm_bytes_stage1_with_gather", _f64), ("comp_params", _f64 * 4),
+                ("comp_grads", _f64 * 4), ("comp_optim", _f64 * 4)]
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {_status_name(status)}: {detail}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m zero_dp_sharded_amd.build` "
+                "(or __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        L.zero_state_bytes.argtypes = [_i64, _i32, _i32, _i64, ctypes.c_int,
+                                       ctypes.POINTER(ZeroStateBytes)]
+        L.zero_state_bytes_ex.argtypes = [_i64, _i32, _i32, _i64, ctypes.c_int, _i32, _i32,
+                                          ctypes.POINTER(ZeroStateBytes)]
+        L.zero_shard_init.argtypes = [ctypes.POINTER(ZeroShardDesc),
+                                      ctypes.POINTER(ZeroAdamHParams),
+                                      ctypes.POINTER(ZeroLossScaleCfg), ctypes.POINTER(_vp)]
+        L.zero_bucket_reduce.argtypes = [_vp, ctypes.POINTER(_vp), _i32, _i64, _i64, _vp]
+        L.zero_overflow_check.argtypes = [_vp, _vp, ctypes.POINTER(ZeroStepInfo)]
+        L.zero_adam_step.argtypes = [_vp, ctypes.POINTER(ZeroAdamHParams), _vp,
+                                     ctypes.POINTER(ZeroStepInfo)]
+        L.zero_shard_get_counters.argtypes = [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_f64),
+                                              ctypes.POINTER(_i64)]
+        L.zero_shard_set_counters.argtypes = [_vp, _i64, _f64, _i64]
+        L.zero_shard_destroy.argtypes = [_vp]
+        L.zero_status_str.argtypes = [ctypes.c_int]
+        L.zero_status_str.restype = ctypes.c_char_p
+        L.zero_last_error.restype = ctypes.c_char_p
+        L.zero_last_error.argtypes = []
+        L.zero_abi_version.restype = ctypes.c_int
+        L.zero_abi_version.argtypes = []
+        for name in ("zero_state_bytes", "zero_state_bytes_ex", "zero_shard_init",
+                     "zero_bucket_reduce", "zero_overflow_check", "zero_adam_step",
+                     "zero_shard_get_counters", "zero_shard_set_counters", "zero_shard_destroy"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _status_name(s: int) -> str:
+    return lib().zero_status_str(s).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != ZERO_OK:
+        raise ZeroError(status, where, lib().zero_last_error().decode())
+
+
+def zero_abi_version() -> int:
+    return int(lib().zero_abi_version())
+
+
+def zero_status_str(status: int) -> str:
+    return _status_name(status)
+
+
+def zero_last_error() -> str:
+    return lib().zero_last_error().decode()
+
+
+# ------------------------------------------------------------------ parameters
+
+@dataclass
+class AdamHParams:
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.0
+    bias_correction: int = 1
+    wd_mode: int = ZERO_WD_DECOUPLED
+    initial_step: int = 0
+
+    def to_c(self) -> ZeroAdamHParams:
+        return ZeroAdamHParams(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay,
+                               self.bias_correction, self.wd_mode, self.initial_step)
+
+
+@dataclass
+class LossScaleCfg:
+    init_scale: float = 1.0
+    dynamic: int = 1
+    growth_interval: int = 1000
+    min_scale: float = 1.0
+
+    def to_c(self) -> ZeroLossScaleCfg:
+        return ZeroLossScaleCfg(self.init_scale, self.dynamic, self.growth_interval,
+                                self.min_scale)
+
+
+@dataclass
+class StepInfo:
+    overflow: int
+    skipped: int
+    step_t: int
+    grad_norm: float
+    scale_used: float
+    scale_next: float
+
+    @staticmethod
+    def from_c(c: ZeroStepInfo) -> "StepInfo":
+        return StepInfo(c.overflow, c.skipped, c.step_t, c.grad_norm, c.scale_used, c.scale_next)
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _stream_ptr(stream) -> Optional[int]:
+    """hipStream_t of a torch stream, or of torch's current stream if None."""
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dptr(x) -> int:
+    """Device address of a tensor (or an int address)."""
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _ledger(out: ZeroStateBytes) -> dict:
+    d = {}
+    for name, _ in ZeroStateBytes._fields_:
+        v = getattr(out, name)
+        d[name] = list(v) if hasattr(v, "__len__") else v
+    return d
+
+
+def zero_state_bytes(psi: int, nd: int, n_contrib: int, bucket_elems: int,
+                     lp: int = ZERO_FP16) -> dict:
+    out = ZeroStateBytes()
+    _check(lib().zero_state_bytes(psi, nd, n_contrib, bucket_elems, lp, ctypes.byref(out)),
+           "zero_state_bytes")
+    return _ledger(out)
+
+
+def zero_state_bytes_ex(psi: int, nd: int, n_contrib: int, bucket_elems: int, lp: int,
+                        param_bytes: int, k_optim: int) -> dict:
+    out = ZeroStateBytes()
+    _check(lib().zero_state_bytes_ex(psi, nd, n_contrib, bucket_elems, lp, param_bytes,
+                                     k_optim, ctypes.byref(out)), "zero_state_bytes_ex")
+    return _ledger(out)
+
+
+def _check_tensor(name, t, dtype, n):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must live on the GPU, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous() or t.numel() < n:
+        raise ValueError(f"{name}: must be contiguous with at least {n} elements")
+
+
+def zero_shard_init(master, exp_avg, exp_avg_sq, grad_shard, param_shard, *, psi: int,
+                    nd: int, rank: int, bucket_elems: int, hp: AdamHParams,
+                    ls: LossScaleCfg) -> int:
+    """Create a handle over caller-owned torch tensors; returns the handle."""
+    import torch
+    lp_t = grad_shard.dtype
+    lp = {torch.float16: ZERO_FP16, torch.bfloat16: ZERO_BF16}.get(lp_t)
+    if lp is None:
+        raise TypeError(f"grad_shard must be float16 or bfloat16, got {lp_t}")
+    S = -(-psi // nd)
+    for name, t, dt in (("master", master, torch.float32), ("exp_avg", exp_avg, torch.float32),
+                        ("exp_avg_sq", exp_avg_sq, torch.float32),
+                        ("grad_shard", grad_shard, lp_t), ("param_shard", param_shard, lp_t)):
+        _check_tensor(name, t, dt, S)
+    desc = ZeroShardDesc(psi, nd, rank, bucket_elems, lp, master.data_ptr(),
+                         exp_avg.data_ptr(), exp_avg_sq.data_ptr(), grad_shard.data_ptr(),
+                         param_shard.data_ptr())
+    h = _vp()
+    _check(lib().zero_shard_init(ctypes.byref(desc), ctypes.byref(hp.to_c()),
+                                 ctypes.byref(ls.to_c()), ctypes.byref(h)), "zero_shard_init")
+    return h.value
+
+
+def zero_bucket_reduce(h: int, contribs: Sequence, bucket_off: int, bucket_len: int,
+                       stream=None) -> None:
+    """contribs: R tensors (or device addresses), each holding this bucket's
+    bucket_len 2-byte gradients of one contribution."""
+    arr = (_vp * len(contribs))(*[_dptr(c) for c in contribs])
+    _check(lib().zero_bucket_reduce(h, arr, len(contribs), bucket_off, bucket_len,
+                                    _stream_ptr(stream)), "zero_bucket_reduce")
+
+
+def zero_overflow_check(h: int, stream=None) -> StepInfo:
+    out = ZeroStepInfo()
+    _check(lib().zero_overflow_check(h, _stream_ptr(stream), ctypes.byref(out)),
+           "zero_overflow_check")
+    return StepInfo.from_c(out)
+
+
+def zero_adam_step(h: int, hp: Optional[AdamHParams] = None, stream=None) -> StepInfo:
+    out = ZeroStepInfo()
+    hpc = ctypes.byref(hp.to_c()) if hp is not None else None
+    _check(lib().zero_adam_step(h, hpc, _stream_ptr(stream), ctypes.byref(out)),
+           "zero_adam_step")
+    return StepInfo.from_c(out)
+
+
+def zero_shard_get_counters(h: int):
+    t, s, g = _i64(), _f64(), _i64()
+    _check(lib().zero_shard_get_counters(h, ctypes.byref(t), ctypes.byref(s), ctypes.byref(g)),
+           "zero_shard_get_counters")
+    return t.value, s.value, g.value
+
+
+def zero_shard_set_counters(h: int, step_t: int, scale: float, good_steps: int) -> None:
+    _check(lib().zero_shard_set_counters(h, step_t, scale, good_steps),
+           "zero_shard_set_counters")
+
+
+def zero_shard_destroy(h: int) -> None:
+    _check(lib().zero_shard_destroy(h), "zero_shard_destroy")
+
+
+def reduce_buckets(h: int, contribs: Sequence, shard_elems: int, bucket_elems: int,
+                   stream=None) -> None:
+    """Submit every C_B bucket of a step in ascending order.  contribs are R
+    shard-sized tensors; bucket b passes the views [off, off + len)."""
+    esz = 2
+    ptrs = [_dptr(c) for c in contribs]
+    for off in range(0, shard_elems, bucket_elems):
+        ln = min(bucket_elems, shard_elems - off)
+        zero_bucket_reduce(h, [p + off * esz for p in ptrs], off, ln, stream)

@@ -1,0 +1,499 @@
+// C ABI of the owner-rank ZeRO-DP step: argument validation, the per-step
+// phase machine (reduce buckets -> check -> Adam), the host scalars of each
+// Adam step, loss-scale bookkeeping, and the kernel launches.
+//
+// Method: "ZeRO：大模型训练的内存优化革命" 3.1.1 (each process updates its 1/Nd of
+// the optimizer state, then parameters are all-gathered) and 3.1.2 (gradients
+// reduced on the owner of the partition); 3.2.2 (constant-size buffers).
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <unordered_set>
+
+#include "../../include/zero_shard.h"
+#include "zero_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+zero_status fail(zero_status s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+zero_status hip_fail(hipError_t e, const char* what)
+{
+    return fail(ZERO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+enum Phase { kIdle = 0, kReducing = 1, kChecked = 2 };
+
+}  // namespace
+
+struct zero_shard_s {
+    int device = -1;
+    zero_shard_desc d{};
+    int64_t S = 0;
+    zero_adam_hparams hp{};
+    zero_loss_scale_cfg ls{};
+    // step state
+    int64_t t = 0;
+    double scale = 1.0;
+    int64_t good_steps = 0;
+    // beta^t cache for the init betas: product of t fp32-rounded betas in fp64
+    double pw1 = 1.0, pw2 = 1.0;
+    int64_t pw_t = 0;
+    Phase phase = kIdle;
+    int64_t covered = 0;
+    zero_step_info check{};
+    // device workspace and pinned host copy of the check result
+    void* ws = nullptr;
+    double* part_sumsq = nullptr;
+    int32_t* part_flag = nullptr;
+    zk::CheckResult* result = nullptr;
+    zk::CheckResult* host_result = nullptr;
+};
+
+namespace {
+
+std::mutex g_live_mu;
+std::unordered_set<zero_shard_s*> g_live;
+
+bool live(zero_shard_t h)
+{
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    return h != nullptr && g_live.count(h) != 0;
+}
+
+bool finite_pos(double x) { return std::isfinite(x) && x > 0.0; }
+
+zero_status check_hparams(const zero_adam_hparams* hp)
+{
+    if (!hp) return fail(ZERO_ERR_INVALID_ARG, "adam hparams: NULL");
+    if (!(std::isfinite(hp->lr) && hp->lr >= 0.0))
+        return fail(ZERO_ERR_INVALID_ARG, "adam hparams: lr must be finite and >= 0");
+    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
+        return fail(ZERO_ERR_INVALID_ARG, "adam hparams: betas must lie in [0, 1)");
+    if (!finite_pos(hp->eps) || (float)hp->eps <= 0.0f)
+        return fail(ZERO_ERR_INVALID_ARG, "adam hparams: eps must be > 0 in fp32");
+    if (!(std::isfinite(hp->weight_decay) && hp->weight_decay >= 0.0))
+        return fail(ZERO_ERR_INVALID_ARG, "adam hparams: weight_decay must be finite and >= 0");
+    if (hp->bias_correction != 0 && hp->bias_correction != 1)
+        return fail(ZERO_ERR_INVALID_ARG, "adam hparams: bias_correction must be 0 or 1");
+    if (hp->wd_mode != ZERO_WD_DECOUPLED && hp->wd_mode != ZERO_WD_L2)
+        return fail(ZERO_ERR_INVALID_ARG, "adam hparams: unknown wd_mode %d", (int)hp->wd_mode);
+    if (hp->initial_step < 0)
+        return fail(ZERO_ERR_INVALID_ARG, "adam hparams: initial_step must be >= 0");
+    return ZERO_OK;
+}
+
+zero_status check_ls(const zero_loss_scale_cfg* ls)
+{
+    if (!ls) return fail(ZERO_ERR_INVALID_ARG, "loss scale: NULL");
+    if (!finite_pos(ls->init_scale) || !finite_pos(ls->min_scale))
+        return fail(ZERO_ERR_INVALID_ARG, "loss scale: init_scale and min_scale must be finite and > 0");
+    if (ls->dynamic != 0 && ls->dynamic != 1)
+        return fail(ZERO_ERR_INVALID_ARG, "loss scale: dynamic must be 0 or 1");
+    if (ls->growth_interval < 1)
+        return fail(ZERO_ERR_INVALID_ARG, "loss scale: growth_interval must be >= 1");
+    return ZERO_OK;
+}
+
+// Both 2-byte formats take two bytes per element.
+constexpr size_t kLpBytes = 2;
+
+// Leading elements to peel so that every listed address is 16-byte aligned,
+// or -1 if no common head exists.  elt[k] is the element size of address k.
+int64_t common_head(const uintptr_t* addr, const int* elt, int count)
+{
+    for (int64_t h = 0; h < 8; ++h) {
+        bool ok = true;
+        for (int k = 0; k < count && ok; ++k) ok = ((addr[k] + (uintptr_t)h * elt[k]) & 15u) == 0;
+        if (ok) return h;
+    }
+    return -1;
+}
+
+// Vector layout of n elements: `head` scalar elements, then nvec runs of 8
+// aligned elements, then a scalar tail.  head < 0 (no common alignment)
+// selects the element-wise path.
+void split(int64_t n, int64_t head, int64_t* out_head, int64_t* out_nvec, int32_t* vec_ok)
+{
+    if (head < 0) {
+        *vec_ok = 0;
+        *out_head = 0;
+        *out_nvec = 0;
+        return;
+    }
+    if (head > n) head = n;
+    *vec_ok = 1;
+    *out_head = head;
+    *out_nvec = (n - head) / 8;
+}
+
+// beta^t as a product of t copies of (double)(float)beta, as the header says.
+double beta_pow(double beta, int64_t t)
+{
+    const double b = (double)(float)beta;
+    double p = 1.0;
+    for (int64_t k = 0; k < t; ++k) p = p * b;
+    return p;
+}
+
+void next_scale(zero_shard_s* h, int overflow, double* scale, int64_t* good)
+{
+    double s = h->scale;
+    int64_t g = h->good_steps;
+    if (h->ls.dynamic) {
+        if (overflow) {
+            s = s / 2.0;
+            if (s < h->ls.min_scale) s = h->ls.min_scale;
+            g = 0;
+        } else {
+            g += 1;
+            if (g == h->ls.growth_interval) {
+                s = s * 2.0;
+                g = 0;
+            }
+        }
+    }
+    *scale = s;
+    *good = g;
+}
+
+bool overlaps(uintptr_t a, size_t na, uintptr_t b, size_t nb)
+{
+    return a < b + nb && b < a + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+int zero_abi_version(void) { return ZERO_SHARD_ABI_VERSION; }
+
+const char* zero_last_error(void) { return g_last_error; }
+
+const char* zero_status_str(zero_status s)
+{
+    switch (s) {
+    case ZERO_OK: return "ZERO_OK";
+    case ZERO_ERR_INVALID_ARG: return "ZERO_ERR_INVALID_ARG";
+    case ZERO_ERR_STATE: return "ZERO_ERR_STATE";
+    case ZERO_ERR_HIP: return "ZERO_ERR_HIP";
+    case ZERO_ERR_OOM: return "ZERO_ERR_OOM";
+    case ZERO_ERR_UNSUPPORTED: return "ZERO_ERR_UNSUPPORTED";
+    }
+    return "ZERO_ERR_UNKNOWN";
+}
+
+zero_status zero_shard_init(const zero_shard_desc* desc, const zero_adam_hparams* hp,
+                            const zero_loss_scale_cfg* ls, zero_shard_t* out)
+{
+    if (!desc || !out) return fail(ZERO_ERR_INVALID_ARG, "init: NULL desc or out");
+    const zero_shard_desc& d = *desc;
+    if (d.psi < 1) return fail(ZERO_ERR_INVALID_ARG, "init: psi must be >= 1");
+    if (d.nd < 1) return fail(ZERO_ERR_INVALID_ARG, "init: nd must be >= 1");
+    if (d.rank < 0 || d.rank >= d.nd) return fail(ZERO_ERR_INVALID_ARG, "init: rank outside [0, nd)");
+    if (d.bucket_elems < 1) return fail(ZERO_ERR_INVALID_ARG, "init: bucket_elems must be >= 1");
+    if (d.lp != ZERO_FP16 && d.lp != ZERO_BF16)
+        return fail(ZERO_ERR_INVALID_ARG, "init: unknown lp dtype %d", (int)d.lp);
+    if (!d.master || !d.exp_avg || !d.exp_avg_sq || !d.grad_shard || !d.param_shard)
+        return fail(ZERO_ERR_INVALID_ARG, "init: NULL shard array");
+    const uintptr_t a32[3] = {(uintptr_t)d.master, (uintptr_t)d.exp_avg, (uintptr_t)d.exp_avg_sq};
+    const uintptr_t a16[2] = {(uintptr_t)d.grad_shard, (uintptr_t)d.param_shard};
+    for (uintptr_t a : a32)
+        if (a & 3u) return fail(ZERO_ERR_INVALID_ARG, "init: fp32 array not 4-byte aligned");
+    for (uintptr_t a : a16)
+        if (a & 1u) return fail(ZERO_ERR_INVALID_ARG, "init: 2-byte array not 2-byte aligned");
+    const int64_t S = (d.psi + d.nd - 1) / d.nd;
+    {
+        const uintptr_t all[5] = {a32[0], a32[1], a32[2], a16[0], a16[1]};
+        const size_t len[5] = {(size_t)S * 4, (size_t)S * 4, (size_t)S * 4,
+                               (size_t)S * kLpBytes, (size_t)S * kLpBytes};
+        for (int i = 0; i < 5; ++i)
+            for (int j = i + 1; j < 5; ++j)
+                if (overlaps(all[i], len[i], all[j], len[j]))
+                    return fail(ZERO_ERR_INVALID_ARG, "init: shard arrays %d and %d overlap", i, j);
+    }
+    zero_status st = check_hparams(hp);
+    if (st != ZERO_OK) return st;
+    st = check_ls(ls);
+    if (st != ZERO_OK) return st;
+
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "init: hipGetDevice");
+
+    zero_shard_s* h = new (std::nothrow) zero_shard_s();
+    if (!h) return fail(ZERO_ERR_OOM, "init: host allocation failed");
+    h->device = dev;
+    h->d = d;
+    h->S = S;
+    h->hp = *hp;
+    h->ls = *ls;
+    h->t = hp->initial_step;
+    h->scale = ls->init_scale;
+    h->good_steps = 0;
+
+    const size_t ws_bytes = sizeof(double) * zk::kSlots + sizeof(int32_t) * zk::kSlots + 256;
+    e = hipMalloc(&h->ws, ws_bytes);
+    if (e != hipSuccess) {
+        delete h;
+        (void)hipGetLastError();
+        return fail(e == hipErrorOutOfMemory ? ZERO_ERR_OOM : ZERO_ERR_HIP,
+                    "init: hipMalloc of %zu bytes: %s", ws_bytes, hipGetErrorString(e));
+    }
+    h->part_sumsq = static_cast<double*>(h->ws);
+    h->part_flag = reinterpret_cast<int32_t*>(h->part_sumsq + zk::kSlots);
+    h->result = reinterpret_cast<zk::CheckResult*>(
+        reinterpret_cast<char*>(h->ws) + sizeof(double) * zk::kSlots + sizeof(int32_t) * zk::kSlots);
+    e = hipHostMalloc(reinterpret_cast<void**>(&h->host_result), 64, hipHostMallocDefault);
+    if (e != hipSuccess) {
+        (void)hipFree(h->ws);
+        delete h;
+        (void)hipGetLastError();
+        return fail(ZERO_ERR_OOM, "init: hipHostMalloc: %s", hipGetErrorString(e));
+    }
+    std::memset(h->host_result, 0, 64);
+    {
+        std::lock_guard<std::mutex> lk(g_live_mu);
+        g_live.insert(h);
+    }
+    *out = h;
+    return ZERO_OK;
+}
+
+zero_status zero_shard_destroy(zero_shard_t h)
+{
+    {
+        std::lock_guard<std::mutex> lk(g_live_mu);
+        if (h == nullptr || g_live.erase(h) == 0)
+            return fail(ZERO_ERR_STATE, "destroy: not a live handle");
+    }
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != h->device) (void)hipSetDevice(h->device);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(h->ws);
+    (void)hipHostFree(h->host_result);
+    if (cur != h->device && cur >= 0) (void)hipSetDevice(cur);
+    delete h;
+    return ZERO_OK;
+}
+
+zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int32_t n_contrib,
+                               int64_t bucket_off, int64_t bucket_len, void* stream)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "bucket_reduce: not a live handle");
+    if (!contribs) return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: NULL contribs");
+    if (n_contrib < 1 || n_contrib > ZERO_MAX_CONTRIB)
+        return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: n_contrib %d outside [1, %d]", n_contrib,
+                    ZERO_MAX_CONTRIB);
+    for (int r = 0; r < n_contrib; ++r) {
+        if (!contribs[r]) return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: contribution %d is NULL", r);
+        if ((uintptr_t)contribs[r] & 1u)
+            return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: contribution %d not 2-byte aligned", r);
+    }
+    if (bucket_len < 1) return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: bucket_len must be >= 1");
+    if (bucket_off < 0 || bucket_off >= h->S || bucket_len > h->S - bucket_off)
+        return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: bucket [%lld, +%lld) outside [0, %lld)",
+                    (long long)bucket_off, (long long)bucket_len, (long long)h->S);
+    if (bucket_len > h->d.bucket_elems)
+        return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: bucket_len %lld exceeds C_B %lld",
+                    (long long)bucket_len, (long long)h->d.bucket_elems);
+    if (h->phase == kChecked)
+        return fail(ZERO_ERR_STATE, "bucket_reduce: step already checked; call zero_adam_step");
+    const int64_t expect = h->phase == kIdle ? 0 : h->covered;
+    if (bucket_off != expect)
+        return fail(ZERO_ERR_STATE, "bucket_reduce: expected bucket at %lld, got %lld",
+                    (long long)expect, (long long)bucket_off);
+    if (bucket_off + bucket_len < h->S && bucket_len != h->d.bucket_elems)
+        return fail(ZERO_ERR_STATE, "bucket_reduce: only the last bucket may be shorter than C_B");
+
+    zk::ReduceLaunch L;
+    std::memset(&L, 0, sizeof(L));
+    uintptr_t addr[ZERO_MAX_CONTRIB + 1];
+    int elt[ZERO_MAX_CONTRIB + 1];
+    for (int r = 0; r < n_contrib; ++r) {
+        L.c.p[r] = contribs[r];
+        addr[r] = (uintptr_t)contribs[r];
+        elt[r] = 2;
+    }
+    char* out = static_cast<char*>(h->d.grad_shard) + bucket_off * 2;
+    addr[n_contrib] = (uintptr_t)out;
+    elt[n_contrib] = 2;
+    L.out = out;
+    L.n = bucket_len;
+    split(bucket_len, common_head(addr, elt, n_contrib + 1), &L.head, &L.nvec, &L.vec_ok);
+    L.R = n_contrib;
+    L.lp = (int32_t)h->d.lp;
+    L.first = h->phase == kIdle ? 1 : 0;
+    L.inv_r = (float)(1.0 / (double)n_contrib);
+    L.inv_scale = (float)(1.0 / h->scale);
+    L.part_sumsq = h->part_sumsq;
+    L.part_flag = h->part_flag;
+    hipError_t e = zk::launch_reduce(L, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "bucket_reduce: launch");
+    h->covered = bucket_off + bucket_len;
+    h->phase = kReducing;
+    return ZERO_OK;
+}
+
+zero_status zero_overflow_check(zero_shard_t h, void* stream, zero_step_info* out)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "overflow_check: not a live handle");
+    if (!out) return fail(ZERO_ERR_INVALID_ARG, "overflow_check: NULL out");
+    if (h->phase == kChecked) {
+        *out = h->check;
+        return ZERO_OK;
+    }
+    if (h->phase == kReducing && h->covered != h->S)
+        return fail(ZERO_ERR_STATE, "overflow_check: buckets cover [0, %lld) of [0, %lld)",
+                    (long long)h->covered, (long long)h->S);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (h->phase == kIdle) {
+        zk::ScanLaunch L;
+        std::memset(&L, 0, sizeof(L));
+        const uintptr_t a = (uintptr_t)h->d.grad_shard;
+        const int el = 2;
+        L.g = h->d.grad_shard;
+        L.n = h->S;
+        split(h->S, common_head(&a, &el, 1), &L.head, &L.nvec, &L.vec_ok);
+        L.lp = (int32_t)h->d.lp;
+        L.inv_scale = (float)(1.0 / h->scale);
+        L.part_sumsq = h->part_sumsq;
+        L.part_flag = h->part_flag;
+        e = zk::launch_scan(L, s);
+        if (e != hipSuccess) return hip_fail(e, "overflow_check: scan launch");
+    }
+    e = zk::launch_finalize(h->part_sumsq, h->part_flag, h->result, s);
+    if (e != hipSuccess) return hip_fail(e, "overflow_check: finalize launch");
+    e = hipMemcpyAsync(h->host_result, h->result, sizeof(zk::CheckResult), hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "overflow_check: copy");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "overflow_check: synchronize");
+
+    zero_step_info info;
+    std::memset(&info, 0, sizeof(info));
+    info.overflow = h->host_result->flag ? 1 : 0;
+    info.skipped = info.overflow;
+    info.step_t = h->t;
+    info.grad_norm = std::sqrt(h->host_result->sumsq);
+    info.scale_used = h->scale;
+    int64_t g;
+    next_scale(h, info.overflow, &info.scale_next, &g);
+    h->check = info;
+    h->phase = kChecked;
+    *out = info;
+    return ZERO_OK;
+}
+
+zero_status zero_adam_step(zero_shard_t h, const zero_adam_hparams* hp_in, void* stream,
+                           zero_step_info* out)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "adam_step: not a live handle");
+    if (h->phase != kChecked)
+        return fail(ZERO_ERR_STATE, "adam_step: zero_overflow_check has not completed this step");
+    if (hp_in) {
+        zero_status st = check_hparams(hp_in);
+        if (st != ZERO_OK) return st;
+    }
+    const zero_adam_hparams& hp = hp_in ? *hp_in : h->hp;
+    zero_step_info info = h->check;
+    double scale_next;
+    int64_t good_next;
+    next_scale(h, info.overflow, &scale_next, &good_next);
+    if (!info.overflow) {
+        const int64_t t = h->t + 1;
+        double pw1, pw2;
+        const bool same_betas = hp.beta1 == h->hp.beta1 && hp.beta2 == h->hp.beta2;
+        if (same_betas && h->pw_t == t - 1) {
+            pw1 = h->pw1 * (double)(float)hp.beta1;
+            pw2 = h->pw2 * (double)(float)hp.beta2;
+        } else {
+            pw1 = beta_pow(hp.beta1, t);
+            pw2 = beta_pow(hp.beta2, t);
+        }
+        zk::AdamLaunch a;
+        std::memset(&a, 0, sizeof(a));
+        a.grad = h->d.grad_shard;
+        a.master = h->d.master;
+        a.m = h->d.exp_avg;
+        a.v = h->d.exp_avg_sq;
+        a.param = h->d.param_shard;
+        a.n = h->S;
+        const uintptr_t addr[5] = {(uintptr_t)a.grad, (uintptr_t)a.param, (uintptr_t)a.master,
+                                   (uintptr_t)a.m, (uintptr_t)a.v};
+        const int elt[5] = {2, 2, 4, 4, 4};
+        split(h->S, common_head(addr, elt, 5), &a.head, &a.nvec, &a.vec_ok);
+        a.lp = (int32_t)h->d.lp;
+        a.b1 = (float)hp.beta1;
+        a.b2 = (float)hp.beta2;
+        a.omb1 = 1.0f - a.b1;
+        a.omb2 = 1.0f - a.b2;
+        a.bc1 = hp.bias_correction ? (float)(1.0 - pw1) : 1.0f;
+        a.bc2 = hp.bias_correction ? (float)(1.0 - pw2) : 1.0f;
+        a.lr = (float)hp.lr;
+        a.eps = (float)hp.eps;
+        a.wd = (float)hp.weight_decay;
+        a.inv_scale = (float)(1.0 / h->scale);
+        a.wd_kind = a.wd == 0.0f ? zk::kWdNone
+                  : (hp.wd_mode == ZERO_WD_L2 ? zk::kWdL2 : zk::kWdDecoupled);
+        hipError_t e = zk::launch_adam(a, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail(e, "adam_step: launch");
+        h->t = t;
+        if (same_betas) {
+            h->pw1 = pw1;
+            h->pw2 = pw2;
+            h->pw_t = t;
+        }
+        info.step_t = t;
+    }
+    info.scale_next = scale_next;
+    h->scale = scale_next;
+    h->good_steps = good_next;
+    h->phase = kIdle;
+    h->covered = 0;
+    if (out) *out = info;
+    return ZERO_OK;
+}
+
+zero_status zero_shard_get_counters(zero_shard_t h, int64_t* step_t, double* scale,
+                                    int64_t* good_steps)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "get_counters: not a live handle");
+    if (!step_t || !scale || !good_steps) return fail(ZERO_ERR_INVALID_ARG, "get_counters: NULL");
+    *step_t = h->t;
+    *scale = h->scale;
+    *good_steps = h->good_steps;
+    return ZERO_OK;
+}
+
+zero_status zero_shard_set_counters(zero_shard_t h, int64_t step_t, double scale,
+                                    int64_t good_steps)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "set_counters: not a live handle");
+    if (step_t < 0 || !finite_pos(scale) || good_steps < 0)
+        return fail(ZERO_ERR_INVALID_ARG, "set_counters: values out of range");
+    if (h->phase != kIdle) return fail(ZERO_ERR_STATE, "set_counters: a step is in progress");
+    h->t = step_t;
+    h->scale = scale;
+    h->good_steps = good_steps;
+    h->pw_t = -1;
+    return ZERO_OK;
+}
+
+}  // extern "C"
