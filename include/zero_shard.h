@@ -166,11 +166,14 @@ zero_status zero_state_bytes_ex(int64_t psi, int32_t nd, int32_t n_contrib,
 
 /*
  * Create a handle bound to the current device.  Copies *desc, *hp and *ls.
- * Allocates a small device workspace (per-block partials, under 64 KiB) and 64
- * bytes of pinned host memory; touches none of the caller's arrays.
+ * Allocates a device workspace for the check's per-workgroup partials, 8 bytes
+ * per 2048 shard elements plus 16 bytes per bucket plus 8 KiB (7.8 MB for a
+ * 2e9-element shard), and 64 bytes of pinned host memory; touches none of the
+ * caller's arrays.
  * Errors: INVALID_ARG (NULL argument or pointer in desc, psi < 1, nd < 1, rank
- * outside [0, nd), bucket_elems < 1, unknown lp, misaligned array, hp or ls
- * out of range), OOM, HIP.
+ * outside [0, nd), bucket_elems < 1, unknown lp, misaligned or overlapping
+ * arrays, hp or ls out of range), UNSUPPORTED (buckets so small that the
+ * partials would need more than 2^25 slots), OOM, HIP.
  */
 zero_status zero_shard_init(const zero_shard_desc* desc, const zero_adam_hparams* hp,
                             const zero_loss_scale_cfg* ls, zero_shard_t* out);

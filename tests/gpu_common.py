@@ -124,7 +124,8 @@ def run_gpu(w: synth.Workload, *, elems: Optional[int] = None, steps: Optional[i
             zs.reduce_buckets(h, bufs, S, cb)
             chk = zs.zero_overflow_check(h)
             info = zs.zero_adam_step(h)
-            assert info.overflow == chk.overflow and info.grad_norm == chk.grad_norm
+            assert info.overflow == chk.overflow
+            assert info.grad_norm == chk.grad_norm or (np.isnan(info.grad_norm) and np.isnan(chk.grad_norm))
             infos.append(info)
             scale = info.scale_next
         torch.cuda.synchronize()

@@ -8,8 +8,27 @@
 namespace zk {
 
 constexpr int kMaxContrib = 64;
-constexpr int kBlock = 256;           // 4 wave64 per workgroup
-constexpr int kSlots = 4096;          // per-block partial slots of the check
+
+// Reduce / scan: 256 lanes per workgroup, each lane two runs of 8 two-byte
+// elements (each load instruction of a wave covers 1 KiB contiguously);
+// residency capped at 4 workgroups (16 waves) per CU.
+constexpr int kRedBlock = 256;
+constexpr int kRedRuns = 2;
+constexpr int64_t kRedElemsPerBlock = (int64_t)kRedBlock * kRedRuns * 8;   // 4096
+constexpr int kRedPerCU = 4;
+// Adam: 128 lanes per workgroup, each lane two groups of 4 elements;
+// residency capped at 5 workgroups (10 waves) per CU.
+constexpr int kAdamBlock = 128;
+constexpr int kAdamGroups = 2;
+constexpr int64_t kAdamElemsPerBlock = (int64_t)kAdamBlock * kAdamGroups * 4;  // 1024
+constexpr int kAdamPerCU = 5;
+// Element-wise kernels (unaligned heads and tails, or arrays without a common
+// alignment): 256 lanes, 8 elements per lane, lane-consecutive per step.
+constexpr int kScalarBlock = 256;
+constexpr int64_t kScalarElemsPerBlock = (int64_t)kScalarBlock * 8;
+// Fixed-order fold of the per-workgroup partials.
+constexpr int kFoldBlock = 256;
+constexpr int kFoldMaxBlocks = 1024;
 
 struct ContribPtrs {
     const void* p[kMaxContrib];
@@ -17,7 +36,10 @@ struct ContribPtrs {
 
 // One bucket of the reduce.  Elements [0, n) of the bucket; the vector body
 // starts at `head` and holds `nvec` runs of 8 elements that are 16-byte aligned
-// in every contribution and in `out`.  vec_ok = 0 selects the element-wise path.
+// in every contribution and in `out`.  vec_ok = 0 selects the element-wise
+// path.  Workgroup b writes partial[slot_base + b]: the fp64 sum of the squared
+// unscaled stored values of its elements, or NaN if any stored value is not
+// finite.
 struct ReduceLaunch {
     ContribPtrs c;
     void* out;
@@ -27,11 +49,11 @@ struct ReduceLaunch {
     int32_t R;
     int32_t lp;            // 1 fp16, 2 bf16
     int32_t vec_ok;
-    int32_t first;         // first bucket of the step: slots are overwritten
     float inv_r;
     float inv_scale;
-    double* part_sumsq;    // kSlots
-    int32_t* part_flag;    // kSlots
+    double* partial;
+    int64_t slot_base;
+    uint32_t lds_reserve;  // dynamic LDS that caps workgroups per CU
 };
 
 // Stand-alone check of a stored gradient shard (no reduce this step).
@@ -43,18 +65,21 @@ struct ScanLaunch {
     int32_t lp;
     int32_t vec_ok;
     float inv_scale;
-    double* part_sumsq;
-    int32_t* part_flag;
+    double* partial;
+    int64_t slot_base;
+    uint32_t lds_reserve;
 };
 
 struct CheckResult {
-    double sumsq;
-    int32_t flag;
-    int32_t pad;
+    double sumsq;          // NaN when a stored value was not finite
+    double pad;
 };
 
 enum WdKind { kWdNone = 0, kWdDecoupled = 1, kWdL2 = 2 };
 
+// Adam over n elements: `head` scalar elements, then ngroups groups of 4
+// elements aligned to 16 bytes in the fp32 arrays and 8 bytes in the 2-byte
+// arrays, then a scalar tail.  vec_ok = 0 selects the element-wise path.
 struct AdamLaunch {
     const void* grad;
     float* master;
@@ -63,17 +88,23 @@ struct AdamLaunch {
     void* param;
     int64_t n;
     int64_t head;
-    int64_t nvec;
+    int64_t ngroups;
     int32_t lp;
     int32_t vec_ok;
     int32_t wd_kind;
+    uint32_t lds_reserve;
     float b1, b2, omb1, omb2, bc1, bc2, lr, eps, wd, inv_scale;
 };
 
+// Partial slots a reduce / scan of this layout writes: one per workgroup of
+// the vector kernel plus one per workgroup of the element-wise kernel.
+int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok);
+
 hipError_t launch_reduce(const ReduceLaunch& L, hipStream_t s);
 hipError_t launch_scan(const ScanLaunch& L, hipStream_t s);
-hipError_t launch_finalize(const double* part_sumsq, const int32_t* part_flag,
+// Sum partial[0, nslots) in a fixed order into out->sumsq (two launches).
+hipError_t launch_finalize(const double* partial, int64_t nslots, double* level1,
                            CheckResult* out, hipStream_t s);
-hipError_t launch_adam(const AdamLaunch& L, hipStream_t s);
+hipError_t launch_adam(const AdamLaunch& a, hipStream_t s);
 
 }  // namespace zk

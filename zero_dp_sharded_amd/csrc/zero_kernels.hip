@@ -1,16 +1,26 @@
 // gfx950 kernels of the owner-rank ZeRO-DP step.
 //
 // Everything here is HBM-bound elementwise streaming (about 0.5 flop per byte
-// against a ridge near 20), so there is no MFMA and no LDS staging of data:
-// each lane moves 16-byte vectors (8 two-byte values, or 2 x 4 fp32 values),
-// the loads of one vector run are all issued before their arithmetic, and the
-// only cross-lane work is the fixed-shape reduction of the overflow flag and
-// the squared gradient norm (wave butterfly, then one LDS slot per wave).
+// against a ridge near 20), so there is no MFMA and no LDS staging of data.
+// The shapes were chosen by measurement on MI355X:
+//  - one tile per lane on an exact grid (no grid-stride loop): the workgroups
+//    in flight then sweep each array as one narrow front, which keeps DRAM
+//    row locality; grid-stride launches lost about 15 points of bandwidth;
+//  - every load and store instruction of a wave covers one contiguous span
+//    (lane-consecutive 16-byte or 8-byte pieces);
+//  - nontemporal loads and stores (each byte is touched once per step);
+//  - a cap on resident workgroups per CU, set by reserving dynamic LDS the
+//    kernels never touch: with the 5 to 7 concurrent streams of these kernels,
+//    fewer resident waves (8 per CU for Adam, 16 for the reduce) sustain more
+//    HBM bandwidth than full occupancy.
+// The only cross-lane work is the fixed-shape reduction of the overflow flag
+// and the squared gradient norm: wave butterfly, one LDS slot per wave, one
+// fp64 partial per workgroup, then a fixed-order two-level fold.
 //
 // Floating point: built with -ffp-contract=off, correctly rounded fp32 divide
 // and square root, fp32 denormals kept, and packed-fp32 instructions disabled.
-// Every per-element operation therefore rounds to nearest even exactly once,
-// in the order written.
+// Every per-element operation rounds to nearest even exactly once, in the
+// order written.
 
 #include "zero_kernels.h"
 
@@ -18,7 +28,9 @@ namespace zk {
 namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b4 __attribute__((ext_vector_type(4)));
 typedef float f8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
@@ -26,48 +38,49 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 template <int LP> struct Fmt;
 template <> struct Fmt<1> {            // IEEE binary16
     using T = _Float16;
-    using V = h8;
+    using V8 = h8;
+    using V4 = h4;
     static constexpr unsigned short kExp = 0x7c00;
 };
 template <> struct Fmt<2> {            // bfloat16
     using T = __bf16;
-    using V = b8;
+    using V8 = b8;
+    using V4 = b4;
     static constexpr unsigned short kExp = 0x7f80;
 };
 
-template <int LP>
-__device__ __forceinline__ typename Fmt<LP>::V load_v(const void* base, int64_t e)
+template <typename V>
+__device__ __forceinline__ V ld_nt(const void* base, int64_t idx)
 {
-    using F = Fmt<LP>;
-    return *reinterpret_cast<const typename F::V*>(static_cast<const typename F::T*>(base) + e);
+    return __builtin_nontemporal_load(static_cast<const V*>(base) + idx);
 }
 
-template <int LP>
-__device__ __forceinline__ void store_v(void* base, int64_t e, typename Fmt<LP>::V x)
+template <typename V>
+__device__ __forceinline__ void st_nt(void* base, int64_t idx, V x)
 {
-    using F = Fmt<LP>;
-    *reinterpret_cast<typename F::V*>(static_cast<typename F::T*>(base) + e) = x;
+    __builtin_nontemporal_store(x, static_cast<V*>(base) + idx);
 }
 
 template <int LP>
 __device__ __forceinline__ float load_s(const void* base, int64_t e)
 {
-    using F = Fmt<LP>;
-    return static_cast<float>(static_cast<const typename F::T*>(base)[e]);
+    return static_cast<float>(static_cast<const typename Fmt<LP>::T*>(base)[e]);
 }
+
+// ----------------------------------------------------------------- check
 
 // Overflow flag and squared unscaled norm of stored 2-byte values.
 template <int LP>
-__device__ __forceinline__ void check_v(typename Fmt<LP>::V o, float inv_scale, int& flag,
+__device__ __forceinline__ void check_v(typename Fmt<LP>::V8 o, float inv_scale, int& flag,
                                         double& ss)
 {
     using F = Fmt<LP>;
-    u16x8 bits = __builtin_bit_cast(u16x8, o);
-    f8 of = __builtin_convertvector(o, f8);
+    const u16x8 bits = __builtin_bit_cast(u16x8, o);
+    const f8 of = __builtin_convertvector(o, f8);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         flag |= (bits[k] & F::kExp) == F::kExp;
-        float u = of[k] * inv_scale;
+        const float u = of[k] * inv_scale;
         ss += (double)u * (double)u;
     }
 }
@@ -77,180 +90,222 @@ __device__ __forceinline__ void check_s(typename Fmt<LP>::T o, float inv_scale, 
                                         double& ss)
 {
     using F = Fmt<LP>;
-    unsigned short bits = __builtin_bit_cast(unsigned short, o);
+    const unsigned short bits = __builtin_bit_cast(unsigned short, o);
     flag |= (bits & F::kExp) == F::kExp;
-    float u = static_cast<float>(o) * inv_scale;
+    const float u = static_cast<float>(o) * inv_scale;
     ss += (double)u * (double)u;
 }
 
-// Reduce of one 8-element run: fp32 sum over r in ascending order from +0,
-// times fp32(1/R), rounded to the 2-byte format.
-template <int LP, int RT>
-__device__ __forceinline__ void reduce_v(const ReduceLaunch& L, int64_t e, int& flag, double& ss)
+// One fp64 partial per workgroup: the sum of its lanes' squares, or NaN when
+// any lane saw a non-finite stored value.  Fixed reduction shape, so the
+// value is bitwise reproducible.
+template <int BS>
+__device__ __forceinline__ void block_partial(double* slot, int flag, double ss)
 {
-    using F = Fmt<LP>;
-    using V = typename F::V;
-    f8 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if constexpr (RT > 0) {
-        V x[RT];
-#pragma unroll
-        for (int r = 0; r < RT; ++r) x[r] = load_v<LP>(L.c.p[r], e);
-#pragma unroll
-        for (int r = 0; r < RT; ++r) acc = acc + __builtin_convertvector(x[r], f8);
-    } else {
-        for (int r0 = 0; r0 < L.R; r0 += 8) {
-            const int cnt = L.R - r0 < 8 ? L.R - r0 : 8;
-            V x[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (k < cnt) x[k] = load_v<LP>(L.c.p[r0 + k], e);
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (k < cnt) acc = acc + __builtin_convertvector(x[k], f8);
-        }
-    }
-    acc = acc * L.inv_r;
-    V o = __builtin_convertvector(acc, V);
-    store_v<LP>(L.out, e, o);
-    check_v<LP>(o, L.inv_scale, flag, ss);
-}
-
-template <int LP>
-__device__ __forceinline__ void reduce_s(const ReduceLaunch& L, int64_t e, int& flag, double& ss)
-{
-    using F = Fmt<LP>;
-    float acc = 0.f;
-    for (int r = 0; r < L.R; ++r) acc = acc + load_s<LP>(L.c.p[r], e);
-    typename F::T o = static_cast<typename F::T>(acc * L.inv_r);
-    static_cast<typename F::T*>(L.out)[e] = o;
-    check_s<LP>(o, L.inv_scale, flag, ss);
-}
-
-// Fold the lane values of a workgroup into its partial slot.  The shape of the
-// reduction is fixed, so the result is bitwise reproducible.  On the first
-// bucket of a step the slot is overwritten and the slots past the grid are
-// cleared; later buckets add to them in stream order.
-__device__ __forceinline__ void block_partial(double* ps, int32_t* pf, int first, int flag,
-                                              double ss)
-{
-    __shared__ double sh_ss[kBlock / 64];
-    __shared__ int sh_f[kBlock / 64];
+    __shared__ double sh_ss[BS / 64];
+    __shared__ int sh_f[BS / 64];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         ss += __shfl_xor(ss, off, 64);
         flag |= __shfl_xor(flag, off, 64);
     }
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    if (lane == 0) {
-        sh_ss[w] = ss;
-        sh_f[w] = flag;
+    if ((threadIdx.x & 63) == 0) {
+        sh_ss[threadIdx.x >> 6] = ss;
+        sh_f[threadIdx.x >> 6] = flag;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
         double s = sh_ss[0];
         int f = sh_f[0];
 #pragma unroll
-        for (int k = 1; k < kBlock / 64; ++k) {
+        for (int k = 1; k < BS / 64; ++k) {
             s += sh_ss[k];
             f |= sh_f[k];
         }
-        const int b = blockIdx.x;
-        if (first) {
-            ps[b] = s;
-            pf[b] = f;
-        } else {
-            ps[b] += s;
-            pf[b] |= f;
-        }
-    }
-    if (first) {
-        for (int k = gridDim.x + blockIdx.x * kBlock + threadIdx.x; k < kSlots;
-             k += gridDim.x * kBlock) {
-            ps[k] = 0.0;
-            pf[k] = 0;
-        }
+        *slot = f ? __builtin_nan("") : s;
     }
 }
 
-template <int LP, int RT>
-__global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceLaunch L)
-{
-    const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    int flag = 0;
-    double ss = 0.0;
-    if (L.vec_ok) {
-        for (int64_t v = gid; v < L.nvec; v += stride)
-            reduce_v<LP, RT>(L, L.head + v * 8, flag, ss);
-        const int64_t tail0 = L.head + L.nvec * 8;
-        const int64_t nsc = L.head + (L.n - tail0);
-        if (gid < nsc)
-            reduce_s<LP>(L, gid < L.head ? gid : tail0 + (gid - L.head), flag, ss);
-    } else {
-        for (int64_t e = gid; e < L.n; e += stride) reduce_s<LP>(L, e, flag, ss);
+// ----------------------------------------------------------------- element lists
+
+// The element-wise kernels walk a list of at most two index ranges: the
+// unaligned head [0, a_len) and the tail [b_start, b_start + b_len) of a
+// vector layout, or the whole array as range a.
+struct Ranges {
+    int64_t a_len;
+    int64_t b_start;
+    int64_t b_len;
+    __device__ __forceinline__ int64_t count() const { return a_len + b_len; }
+    __device__ __forceinline__ int64_t at(int64_t k) const
+    {
+        return k < a_len ? k : b_start + (k - a_len);
     }
-    block_partial(L.part_sumsq, L.part_flag, L.first, flag, ss);
+};
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ----------------------------------------------------------------- reduce
+
+// Finish the 8-element run vi of the vector body (elements head + 8 vi ..):
+// acc holds the fp32 sum over r = 0..R-1 in order from +0; scale by
+// fp32(1/R), round to the 2-byte format, store, check.
+template <int LP>
+__device__ __forceinline__ void reduce_finish(const ReduceLaunch& L, int64_t vi, f8 acc, int& flag,
+                                              double& ss)
+{
+    using V8 = typename Fmt<LP>::V8;
+    acc = acc * L.inv_r;
+    const V8 o = __builtin_convertvector(acc, V8);
+    st_nt<V8>(static_cast<char*>(L.out) + 2 * L.head, vi, o);
+    check_v<LP>(o, L.inv_scale, flag, ss);
 }
 
 template <int LP>
-__global__ __launch_bounds__(kBlock) void scan_kernel(ScanLaunch L)
+__device__ __forceinline__ void reduce_s(const ReduceLaunch& L, int64_t e, int& flag, double& ss)
 {
-    using F = Fmt<LP>;
-    const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    int flag = 0;
-    double ss = 0.0;
-    if (L.vec_ok) {
-        for (int64_t v = gid; v < L.nvec; v += stride)
-            check_v<LP>(load_v<LP>(L.g, L.head + v * 8), L.inv_scale, flag, ss);
-        const int64_t tail0 = L.head + L.nvec * 8;
-        const int64_t nsc = L.head + (L.n - tail0);
-        if (gid < nsc) {
-            const int64_t e = gid < L.head ? gid : tail0 + (gid - L.head);
-            check_s<LP>(static_cast<const typename F::T*>(L.g)[e], L.inv_scale, flag, ss);
-        }
-    } else {
-        for (int64_t e = gid; e < L.n; e += stride)
-            check_s<LP>(static_cast<const typename F::T*>(L.g)[e], L.inv_scale, flag, ss);
-    }
-    block_partial(L.part_sumsq, L.part_flag, 1, flag, ss);
+    using T = typename Fmt<LP>::T;
+    float acc = 0.f;
+    for (int r = 0; r < L.R; ++r) acc = acc + load_s<LP>(L.c.p[r], e);
+    const T o = static_cast<T>(acc * L.inv_r);
+    static_cast<T*>(L.out)[e] = o;
+    check_s<LP>(o, L.inv_scale, flag, ss);
 }
 
-// One workgroup sums the kSlots partials in a fixed order.
-__global__ __launch_bounds__(kBlock) void finalize_kernel(const double* ps, const int32_t* pf,
-                                                          CheckResult* out)
+// Vector body: workgroup b covers runs [b*512, b*512 + 512); lane l owns runs
+// b*512 + l and b*512 + 256 + l.  Element offsets past `head` are multiples of
+// 8, so contribution and output pointers advanced by `head` are 16-byte
+// aligned and are indexed in units of 8 elements.
+template <int LP, int RT>
+__global__ __launch_bounds__(kRedBlock) void reduce_vec_kernel(ReduceLaunch L)
 {
-    double s = 0.0;
-    int f = 0;
-    for (int k = threadIdx.x; k < kSlots; k += kBlock) {
-        s += ps[k];
-        f |= pf[k];
+    using V8 = typename Fmt<LP>::V8;
+    int flag = 0;
+    double ss = 0.0;
+    const int64_t v0 = (int64_t)blockIdx.x * (kRedBlock * kRedRuns) + threadIdx.x;
+    if constexpr (RT > 0 && RT * kRedRuns <= 16) {
+        // every load of both runs in flight before the arithmetic
+        V8 x[kRedRuns][RT];
+#pragma unroll
+        for (int u = 0; u < kRedRuns; ++u) {
+            const int64_t vi = v0 + u * kRedBlock;
+            if (vi < L.nvec) {
+#pragma unroll
+                for (int r = 0; r < RT; ++r)
+                    x[u][r] = ld_nt<V8>(static_cast<const char*>(L.c.p[r]) + 2 * L.head, vi);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kRedRuns; ++u) {
+            const int64_t vi = v0 + u * kRedBlock;
+            if (vi < L.nvec) {
+                f8 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int r = 0; r < RT; ++r) acc = acc + __builtin_convertvector(x[u][r], f8);
+                reduce_finish<LP>(L, vi, acc, flag, ss);
+            }
+        }
+    } else {
+        for (int u = 0; u < kRedRuns; ++u) {
+            const int64_t vi = v0 + u * kRedBlock;
+            if (vi >= L.nvec) break;
+            f8 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if constexpr (RT > 0) {
+                V8 x[RT];
+#pragma unroll
+                for (int r = 0; r < RT; ++r)
+                    x[r] = ld_nt<V8>(static_cast<const char*>(L.c.p[r]) + 2 * L.head, vi);
+#pragma unroll
+                for (int r = 0; r < RT; ++r) acc = acc + __builtin_convertvector(x[r], f8);
+            } else {
+                for (int r0 = 0; r0 < L.R; r0 += 8) {
+                    const int cnt = L.R - r0 < 8 ? L.R - r0 : 8;
+                    V8 x[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        if (k < cnt)
+                            x[k] = ld_nt<V8>(static_cast<const char*>(L.c.p[r0 + k]) + 2 * L.head, vi);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        if (k < cnt) acc = acc + __builtin_convertvector(x[k], f8);
+                }
+            }
+            reduce_finish<LP>(L, vi, acc, flag, ss);
+        }
+    }
+    block_partial<kRedBlock>(L.partial + L.slot_base + blockIdx.x, flag, ss);
+}
+
+template <int LP>
+__global__ __launch_bounds__(kScalarBlock) void reduce_elem_kernel(ReduceLaunch L, Ranges rg,
+                                                                    int64_t slot)
+{
+    int flag = 0;
+    double ss = 0.0;
+    const int64_t cnt = rg.count();
+#pragma unroll 2
+    for (int j = 0; j < (int)(kScalarElemsPerBlock / kScalarBlock); ++j) {
+        const int64_t k = (int64_t)blockIdx.x * kScalarElemsPerBlock + j * kScalarBlock + threadIdx.x;
+        if (k < cnt) reduce_s<LP>(L, rg.at(k), flag, ss);
+    }
+    block_partial<kScalarBlock>(L.partial + slot + blockIdx.x, flag, ss);
+}
+
+template <int LP>
+__global__ __launch_bounds__(kRedBlock) void scan_vec_kernel(ScanLaunch L)
+{
+    using V8 = typename Fmt<LP>::V8;
+    int flag = 0;
+    double ss = 0.0;
+    const int64_t v0 = (int64_t)blockIdx.x * (kRedBlock * kRedRuns) + threadIdx.x;
+    V8 x[kRedRuns];
+#pragma unroll
+    for (int u = 0; u < kRedRuns; ++u) {
+        const int64_t vi = v0 + u * kRedBlock;
+        if (vi < L.nvec) x[u] = ld_nt<V8>(static_cast<const char*>(L.g) + 2 * L.head, vi);
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        s += __shfl_xor(s, off, 64);
-        f |= __shfl_xor(f, off, 64);
+    for (int u = 0; u < kRedRuns; ++u)
+        if (v0 + u * kRedBlock < L.nvec) check_v<LP>(x[u], L.inv_scale, flag, ss);
+    block_partial<kRedBlock>(L.partial + L.slot_base + blockIdx.x, flag, ss);
+}
+
+template <int LP>
+__global__ __launch_bounds__(kScalarBlock) void scan_elem_kernel(ScanLaunch L, Ranges rg,
+                                                                  int64_t slot)
+{
+    using T = typename Fmt<LP>::T;
+    int flag = 0;
+    double ss = 0.0;
+    const int64_t cnt = rg.count();
+    for (int j = 0; j < (int)(kScalarElemsPerBlock / kScalarBlock); ++j) {
+        const int64_t k = (int64_t)blockIdx.x * kScalarElemsPerBlock + j * kScalarBlock + threadIdx.x;
+        if (k < cnt) check_s<LP>(static_cast<const T*>(L.g)[rg.at(k)], L.inv_scale, flag, ss);
     }
-    __shared__ double sh_s[kBlock / 64];
-    __shared__ int sh_f[kBlock / 64];
-    if ((threadIdx.x & 63) == 0) {
-        sh_s[threadIdx.x >> 6] = s;
-        sh_f[threadIdx.x >> 6] = f;
-    }
+    block_partial<kScalarBlock>(L.partial + slot + blockIdx.x, flag, ss);
+}
+
+// Workgroup b sums in[b*chunk, min(n, (b+1)*chunk)) with a fixed shape.
+__global__ __launch_bounds__(kFoldBlock) void fold_kernel(const double* in, int64_t n, int64_t chunk,
+                                                          double* out)
+{
+    const int64_t lo = (int64_t)blockIdx.x * chunk;
+    const int64_t hi = lo + chunk < n ? lo + chunk : n;
+    double s = 0.0;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += kFoldBlock) s += in[i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    __shared__ double sh[kFoldBlock / 64];
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = s;
     __syncthreads();
     if (threadIdx.x == 0) {
-        double t = sh_s[0];
-        int g = sh_f[0];
-        for (int k = 1; k < kBlock / 64; ++k) {
-            t += sh_s[k];
-            g |= sh_f[k];
-        }
-        out->sumsq = t;
-        out->flag = g;
-        out->pad = 0;
+        double t = sh[0];
+#pragma unroll
+        for (int k = 1; k < kFoldBlock / 64; ++k) t += sh[k];
+        out[blockIdx.x] = t;
     }
 }
+
+// ----------------------------------------------------------------- Adam
 
 // Textbook Adam on one element (Kingma & Ba 2015, Algorithm 1), in the order
 // the public header states; p, m, v are updated in place.
@@ -269,132 +324,181 @@ __device__ __forceinline__ void adam_e(float graw, float& p, float& m, float& v,
     p = p - a.lr * u;
 }
 
+// Vector body: groups of 4 elements past `head` (fp32 pointers advanced by
+// head are 16-byte aligned, 2-byte pointers 8-byte aligned).  Workgroup b
+// covers groups [b*256, b*256 + 256); lane l owns groups b*256 + l and
+// b*256 + 128 + l, and issues all eight loads before any arithmetic.
 template <int LP, int WD>
-__device__ __forceinline__ void adam_v(const AdamLaunch& a, int64_t e)
+__global__ __launch_bounds__(kAdamBlock) void adam_vec_kernel(AdamLaunch a)
 {
-    using F = Fmt<LP>;
-    using V = typename F::V;
-    const V gv = load_v<LP>(a.grad, e);
-    f4* mp = reinterpret_cast<f4*>(a.master + e);
-    f4* m1p = reinterpret_cast<f4*>(a.m + e);
-    f4* v2p = reinterpret_cast<f4*>(a.v + e);
-    const f4 p0 = mp[0], p1 = mp[1];
-    const f4 m0 = m1p[0], m1 = m1p[1];
-    const f4 v0 = v2p[0], v1 = v2p[1];
-    const f8 g = __builtin_convertvector(gv, f8);
-    f8 p = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
-    f8 m = __builtin_shufflevector(m0, m1, 0, 1, 2, 3, 4, 5, 6, 7);
-    f8 v = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    using V4 = typename Fmt<LP>::V4;
+    const void* gb = static_cast<const char*>(a.grad) + 2 * a.head;
+    void* qb = static_cast<char*>(a.param) + 2 * a.head;
+    float* pb = a.master + a.head;
+    float* mb = a.m + a.head;
+    float* vb = a.v + a.head;
+    const int64_t q0 = (int64_t)blockIdx.x * (kAdamBlock * kAdamGroups) + threadIdx.x;
+    V4 g[kAdamGroups];
+    f4 p[kAdamGroups], m[kAdamGroups], v[kAdamGroups];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        float pk = p[k], mk = m[k], vk = v[k];
-        adam_e<WD>(g[k], pk, mk, vk, a);
-        p[k] = pk;
-        m[k] = mk;
-        v[k] = vk;
+    for (int u = 0; u < kAdamGroups; ++u) {
+        const int64_t q = q0 + u * kAdamBlock;
+        if (q < a.ngroups) {
+            g[u] = ld_nt<V4>(gb, q);
+            p[u] = ld_nt<f4>(pb, q);
+            m[u] = ld_nt<f4>(mb, q);
+            v[u] = ld_nt<f4>(vb, q);
+        }
     }
-    mp[0] = __builtin_shufflevector(p, p, 0, 1, 2, 3);
-    mp[1] = __builtin_shufflevector(p, p, 4, 5, 6, 7);
-    m1p[0] = __builtin_shufflevector(m, m, 0, 1, 2, 3);
-    m1p[1] = __builtin_shufflevector(m, m, 4, 5, 6, 7);
-    v2p[0] = __builtin_shufflevector(v, v, 0, 1, 2, 3);
-    v2p[1] = __builtin_shufflevector(v, v, 4, 5, 6, 7);
-    store_v<LP>(a.param, e, __builtin_convertvector(p, V));
+#pragma unroll
+    for (int u = 0; u < kAdamGroups; ++u) {
+        const int64_t q = q0 + u * kAdamBlock;
+        if (q < a.ngroups) {
+            const f4 gf = __builtin_convertvector(g[u], f4);
+            f4 pp = p[u], mm = m[u], vv = v[u];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float pk = pp[k], mk = mm[k], vk = vv[k];
+                adam_e<WD>(gf[k], pk, mk, vk, a);
+                pp[k] = pk;
+                mm[k] = mk;
+                vv[k] = vk;
+            }
+            st_nt<f4>(pb, q, pp);
+            st_nt<f4>(mb, q, mm);
+            st_nt<f4>(vb, q, vv);
+            st_nt<V4>(qb, q, __builtin_convertvector(pp, V4));
+        }
+    }
 }
 
 template <int LP, int WD>
-__device__ __forceinline__ void adam_s(const AdamLaunch& a, int64_t e)
+__global__ __launch_bounds__(kScalarBlock) void adam_elem_kernel(AdamLaunch a, Ranges rg)
 {
-    using F = Fmt<LP>;
-    float p = a.master[e], m = a.m[e], v = a.v[e];
-    adam_e<WD>(load_s<LP>(a.grad, e), p, m, v, a);
-    a.master[e] = p;
-    a.m[e] = m;
-    a.v[e] = v;
-    static_cast<typename F::T*>(a.param)[e] = static_cast<typename F::T>(p);
+    using T = typename Fmt<LP>::T;
+    const int64_t cnt = rg.count();
+    for (int j = 0; j < (int)(kScalarElemsPerBlock / kScalarBlock); ++j) {
+        const int64_t k = (int64_t)blockIdx.x * kScalarElemsPerBlock + j * kScalarBlock + threadIdx.x;
+        if (k < cnt) {
+            const int64_t e = rg.at(k);
+            float p = a.master[e], m = a.m[e], v = a.v[e];
+            adam_e<WD>(load_s<LP>(a.grad, e), p, m, v, a);
+            a.master[e] = p;
+            a.m[e] = m;
+            a.v[e] = v;
+            static_cast<T*>(a.param)[e] = static_cast<T>(p);
+        }
+    }
 }
 
-template <int LP, int WD>
-__global__ __launch_bounds__(kBlock) void adam_kernel(AdamLaunch a)
+// Element lists of a layout: head and tail of the vector path, or everything.
+Ranges ranges_of(int64_t n, int64_t head, int64_t body, int32_t vec_ok)
 {
-    const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    if (a.vec_ok) {
-        for (int64_t v = gid; v < a.nvec; v += stride) adam_v<LP, WD>(a, a.head + v * 8);
-        const int64_t tail0 = a.head + a.nvec * 8;
-        const int64_t nsc = a.head + (a.n - tail0);
-        if (gid < nsc) adam_s<LP, WD>(a, gid < a.head ? gid : tail0 + (gid - a.head));
+    Ranges rg;
+    if (!vec_ok) {
+        rg.a_len = n;
+        rg.b_start = n;
+        rg.b_len = 0;
     } else {
-        for (int64_t e = gid; e < a.n; e += stride) adam_s<LP, WD>(a, e);
+        rg.a_len = head;
+        rg.b_start = head + body;
+        rg.b_len = n - (head + body);
     }
-}
-
-// Grid of a grid-stride launch: enough workgroups for `work` lane items,
-// capped at `cap`, at least one.
-inline unsigned grid_for(int64_t work, int64_t cap)
-{
-    int64_t g = (work + kBlock - 1) / kBlock;
-    if (g < 1) g = 1;
-    if (g > cap) g = cap;
-    return (unsigned)g;
+    return rg;
 }
 
 template <int LP>
-hipError_t reduce_dispatch(const ReduceLaunch& L, unsigned grid, hipStream_t s)
+hipError_t reduce_dispatch(const ReduceLaunch& L, hipStream_t s)
 {
-    switch (L.vec_ok ? L.R : 0) {
-    case 1: reduce_kernel<LP, 1><<<grid, kBlock, 0, s>>>(L); break;
-    case 2: reduce_kernel<LP, 2><<<grid, kBlock, 0, s>>>(L); break;
-    case 4: reduce_kernel<LP, 4><<<grid, kBlock, 0, s>>>(L); break;
-    case 8: reduce_kernel<LP, 8><<<grid, kBlock, 0, s>>>(L); break;
-    case 16: reduce_kernel<LP, 16><<<grid, kBlock, 0, s>>>(L); break;
-    default: reduce_kernel<LP, 0><<<grid, kBlock, 0, s>>>(L); break;
+    const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, (int64_t)kRedBlock * kRedRuns) : 0;
+    if (vblocks > 0) {
+        const unsigned grid = (unsigned)vblocks;
+        const unsigned lds = L.lds_reserve;
+        switch (L.R) {
+        case 1: reduce_vec_kernel<LP, 1><<<grid, kRedBlock, lds, s>>>(L); break;
+        case 2: reduce_vec_kernel<LP, 2><<<grid, kRedBlock, lds, s>>>(L); break;
+        case 4: reduce_vec_kernel<LP, 4><<<grid, kRedBlock, lds, s>>>(L); break;
+        case 8: reduce_vec_kernel<LP, 8><<<grid, kRedBlock, lds, s>>>(L); break;
+        case 16: reduce_vec_kernel<LP, 16><<<grid, kRedBlock, lds, s>>>(L); break;
+        default: reduce_vec_kernel<LP, 0><<<grid, kRedBlock, lds, s>>>(L); break;
+        }
     }
+    const Ranges rg = ranges_of(L.n, L.head, 8 * L.nvec, L.vec_ok);
+    const int64_t sblocks = ceil_div(rg.a_len + rg.b_len, kScalarElemsPerBlock);
+    if (sblocks > 0)
+        reduce_elem_kernel<LP><<<(unsigned)sblocks, kScalarBlock, 0, s>>>(L, rg, L.slot_base + vblocks);
+    return hipGetLastError();
+}
+
+template <int LP, int WD>
+hipError_t adam_dispatch(const AdamLaunch& a, hipStream_t s)
+{
+    const int64_t vblocks = a.vec_ok ? ceil_div(a.ngroups, (int64_t)kAdamBlock * kAdamGroups) : 0;
+    if (vblocks > 0)
+        adam_vec_kernel<LP, WD><<<(unsigned)vblocks, kAdamBlock, a.lds_reserve, s>>>(a);
+    const Ranges rg = ranges_of(a.n, a.head, 4 * a.ngroups, a.vec_ok);
+    const int64_t sblocks = ceil_div(rg.a_len + rg.b_len, kScalarElemsPerBlock);
+    if (sblocks > 0) adam_elem_kernel<LP, WD><<<(unsigned)sblocks, kScalarBlock, 0, s>>>(a, rg);
     return hipGetLastError();
 }
 
 template <int LP>
-hipError_t adam_dispatch(const AdamLaunch& a, unsigned grid, hipStream_t s)
+hipError_t adam_dispatch_wd(const AdamLaunch& a, hipStream_t s)
 {
     switch (a.wd_kind) {
-    case kWdDecoupled: adam_kernel<LP, kWdDecoupled><<<grid, kBlock, 0, s>>>(a); break;
-    case kWdL2: adam_kernel<LP, kWdL2><<<grid, kBlock, 0, s>>>(a); break;
-    default: adam_kernel<LP, kWdNone><<<grid, kBlock, 0, s>>>(a); break;
+    case kWdDecoupled: return adam_dispatch<LP, kWdDecoupled>(a, s);
+    case kWdL2: return adam_dispatch<LP, kWdL2>(a, s);
+    default: return adam_dispatch<LP, kWdNone>(a, s);
     }
+}
+
+template <int LP>
+hipError_t scan_dispatch(const ScanLaunch& L, hipStream_t s)
+{
+    const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, (int64_t)kRedBlock * kRedRuns) : 0;
+    if (vblocks > 0)
+        scan_vec_kernel<LP><<<(unsigned)vblocks, kRedBlock, L.lds_reserve, s>>>(L);
+    const Ranges rg = ranges_of(L.n, L.head, 8 * L.nvec, L.vec_ok);
+    const int64_t sblocks = ceil_div(rg.a_len + rg.b_len, kScalarElemsPerBlock);
+    if (sblocks > 0)
+        scan_elem_kernel<LP><<<(unsigned)sblocks, kScalarBlock, 0, s>>>(L, rg, L.slot_base + vblocks);
     return hipGetLastError();
 }
 
 }  // namespace
 
+int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok)
+{
+    const int64_t vblocks = vec_ok ? ceil_div(nvec, (int64_t)kRedBlock * kRedRuns) : 0;
+    const int64_t scalars = vec_ok ? n - 8 * nvec : n;
+    return vblocks + ceil_div(scalars, kScalarElemsPerBlock);
+}
+
 hipError_t launch_reduce(const ReduceLaunch& L, hipStream_t s)
 {
-    const int64_t work = L.vec_ok ? (L.nvec > 16 ? L.nvec : 16) : L.n;
-    const unsigned grid = grid_for(work, kSlots);
-    return L.lp == 2 ? reduce_dispatch<2>(L, grid, s) : reduce_dispatch<1>(L, grid, s);
+    return L.lp == 2 ? reduce_dispatch<2>(L, s) : reduce_dispatch<1>(L, s);
 }
 
 hipError_t launch_scan(const ScanLaunch& L, hipStream_t s)
 {
-    const int64_t work = L.vec_ok ? (L.nvec > 16 ? L.nvec : 16) : L.n;
-    const unsigned grid = grid_for(work, kSlots);
-    if (L.lp == 2)
-        scan_kernel<2><<<grid, kBlock, 0, s>>>(L);
-    else
-        scan_kernel<1><<<grid, kBlock, 0, s>>>(L);
-    return hipGetLastError();
+    return L.lp == 2 ? scan_dispatch<2>(L, s) : scan_dispatch<1>(L, s);
 }
 
-hipError_t launch_finalize(const double* ps, const int32_t* pf, CheckResult* out, hipStream_t s)
+hipError_t launch_finalize(const double* partial, int64_t nslots, double* level1,
+                           CheckResult* out, hipStream_t s)
 {
-    finalize_kernel<<<1, kBlock, 0, s>>>(ps, pf, out);
+    int64_t g1 = ceil_div(nslots, 1024);
+    if (g1 < 1) g1 = 1;
+    if (g1 > kFoldMaxBlocks) g1 = kFoldMaxBlocks;
+    const int64_t chunk = ceil_div(nslots, g1);
+    fold_kernel<<<(unsigned)g1, kFoldBlock, 0, s>>>(partial, nslots, chunk, level1);
+    fold_kernel<<<1, kFoldBlock, 0, s>>>(level1, g1, g1, &out->sumsq);
     return hipGetLastError();
 }
 
 hipError_t launch_adam(const AdamLaunch& a, hipStream_t s)
 {
-    const int64_t work = a.vec_ok ? (a.nvec > 16 ? a.nvec : 16) : a.n;
-    const unsigned grid = grid_for(work, int64_t(1) << 20);
-    return a.lp == 2 ? adam_dispatch<2>(a, grid, s) : adam_dispatch<1>(a, grid, s);
+    return a.lp == 2 ? adam_dispatch_wd<2>(a, s) : adam_dispatch_wd<1>(a, s);
 }
 
 }  // namespace zk

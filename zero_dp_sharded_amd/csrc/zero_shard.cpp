@@ -57,12 +57,18 @@ struct zero_shard_s {
     Phase phase = kIdle;
     int64_t covered = 0;
     zero_step_info check{};
-    // device workspace and pinned host copy of the check result
+    int64_t slot_cursor = 0;      // partial slots written this step
+    // device workspace: per-workgroup partials, the fold's first level and
+    // the check result; pinned host copy of the result
     void* ws = nullptr;
-    double* part_sumsq = nullptr;
-    int32_t* part_flag = nullptr;
+    int64_t nslots = 0;
+    double* partial = nullptr;
+    double* level1 = nullptr;
     zk::CheckResult* result = nullptr;
     zk::CheckResult* host_result = nullptr;
+    // dynamic LDS reserved per workgroup to cap residency per CU
+    uint32_t lds_adam = 0;
+    uint32_t lds_reduce = 0;
 };
 
 namespace {
@@ -113,33 +119,45 @@ zero_status check_ls(const zero_loss_scale_cfg* ls)
 // Both 2-byte formats take two bytes per element.
 constexpr size_t kLpBytes = 2;
 
-// Leading elements to peel so that every listed address is 16-byte aligned,
-// or -1 if no common head exists.  elt[k] is the element size of address k.
-int64_t common_head(const uintptr_t* addr, const int* elt, int count)
+// Leading elements to peel so that every listed address, advanced by that many
+// elements of size elt[k], is aligned to align[k] bytes; -1 if none below 8
+// exists.
+int64_t common_head(const uintptr_t* addr, const int* elt, const int* align, int count)
 {
     for (int64_t h = 0; h < 8; ++h) {
         bool ok = true;
-        for (int k = 0; k < count && ok; ++k) ok = ((addr[k] + (uintptr_t)h * elt[k]) & 15u) == 0;
+        for (int k = 0; k < count && ok; ++k)
+            ok = ((addr[k] + (uintptr_t)h * elt[k]) % (uintptr_t)align[k]) == 0;
         if (ok) return h;
     }
     return -1;
 }
 
-// Vector layout of n elements: `head` scalar elements, then nvec runs of 8
-// aligned elements, then a scalar tail.  head < 0 (no common alignment)
-// selects the element-wise path.
-void split(int64_t n, int64_t head, int64_t* out_head, int64_t* out_nvec, int32_t* vec_ok)
+// Layout of n elements for a kernel working on runs of `run` elements:
+// `head` scalar elements, then nrun aligned runs, then a scalar tail.
+// head < 0 (no common alignment) selects the element-wise path.
+void split(int64_t n, int64_t head, int64_t run, int64_t* out_head, int64_t* out_nrun,
+           int32_t* vec_ok)
 {
     if (head < 0) {
         *vec_ok = 0;
         *out_head = 0;
-        *out_nvec = 0;
+        *out_nrun = 0;
         return;
     }
     if (head > n) head = n;
     *vec_ok = 1;
     *out_head = head;
-    *out_nvec = (n - head) / 8;
+    *out_nrun = (n - head) / run;
+}
+
+// Dynamic LDS that leaves room for `per_cu` workgroups of a kernel per CU.
+uint32_t lds_reserve_for(int lds_per_cu, int lds_per_block_max, int per_cu)
+{
+    int64_t r = (int64_t)lds_per_cu / per_cu - 1024;   // room for static LDS
+    if (r > lds_per_block_max) r = lds_per_block_max;
+    if (r < 0) r = 0;
+    return (uint32_t)(r & ~(int64_t)511);
 }
 
 // beta^t as a product of t copies of (double)(float)beta, as the header says.
@@ -247,7 +265,22 @@ zero_status zero_shard_init(const zero_shard_desc* desc, const zero_adam_hparams
     h->scale = ls->init_scale;
     h->good_steps = 0;
 
-    const size_t ws_bytes = sizeof(double) * zk::kSlots + sizeof(int32_t) * zk::kSlots + 256;
+    // One fp64 partial per reduce workgroup of a step.  A bucket of len
+    // elements uses at most len/2048 + 2 workgroups (the element-wise path
+    // covers 2048 elements per workgroup, the vector path 4096 plus a ragged
+    // end), and the stand-alone scan needs no more.
+    const int64_t nbuckets = (S + d.bucket_elems - 1) / d.bucket_elems;
+    const int64_t nslots = S / zk::kScalarElemsPerBlock + 2 * nbuckets + 4;
+    if (nslots > (int64_t(1) << 25)) {
+        delete h;
+        return fail(ZERO_ERR_UNSUPPORTED,
+                    "init: %lld buckets of %lld elements need %lld partial slots (limit 2^25); "
+                    "use a larger bucket_elems", (long long)nbuckets, (long long)d.bucket_elems,
+                    (long long)nslots);
+    }
+    h->nslots = nslots;
+    const size_t ws_bytes = sizeof(double) * (size_t)(nslots + zk::kFoldMaxBlocks) +
+                            sizeof(zk::CheckResult);
     e = hipMalloc(&h->ws, ws_bytes);
     if (e != hipSuccess) {
         delete h;
@@ -255,10 +288,20 @@ zero_status zero_shard_init(const zero_shard_desc* desc, const zero_adam_hparams
         return fail(e == hipErrorOutOfMemory ? ZERO_ERR_OOM : ZERO_ERR_HIP,
                     "init: hipMalloc of %zu bytes: %s", ws_bytes, hipGetErrorString(e));
     }
-    h->part_sumsq = static_cast<double*>(h->ws);
-    h->part_flag = reinterpret_cast<int32_t*>(h->part_sumsq + zk::kSlots);
-    h->result = reinterpret_cast<zk::CheckResult*>(
-        reinterpret_cast<char*>(h->ws) + sizeof(double) * zk::kSlots + sizeof(int32_t) * zk::kSlots);
+    h->partial = static_cast<double*>(h->ws);
+    h->level1 = h->partial + nslots;
+    h->result = reinterpret_cast<zk::CheckResult*>(h->level1 + zk::kFoldMaxBlocks);
+
+    int lds_cu = 0, lds_blk = 0;
+    if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess || lds_cu <= 0)
+        lds_cu = 160 * 1024;
+    if (hipDeviceGetAttribute(&lds_blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess || lds_blk <= 0)
+        lds_blk = 64 * 1024;
+    (void)hipGetLastError();
+    h->lds_adam = lds_reserve_for(lds_cu, lds_blk, zk::kAdamPerCU);
+    h->lds_reduce = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCU);
     e = hipHostMalloc(reinterpret_cast<void**>(&h->host_result), 64, hipHostMallocDefault);
     if (e != hipSuccess) {
         (void)hipFree(h->ws);
@@ -325,28 +368,34 @@ zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int3
     zk::ReduceLaunch L;
     std::memset(&L, 0, sizeof(L));
     uintptr_t addr[ZERO_MAX_CONTRIB + 1];
-    int elt[ZERO_MAX_CONTRIB + 1];
+    int elt[ZERO_MAX_CONTRIB + 1], align[ZERO_MAX_CONTRIB + 1];
     for (int r = 0; r < n_contrib; ++r) {
         L.c.p[r] = contribs[r];
         addr[r] = (uintptr_t)contribs[r];
         elt[r] = 2;
+        align[r] = 16;
     }
     char* out = static_cast<char*>(h->d.grad_shard) + bucket_off * 2;
     addr[n_contrib] = (uintptr_t)out;
     elt[n_contrib] = 2;
+    align[n_contrib] = 16;
     L.out = out;
     L.n = bucket_len;
-    split(bucket_len, common_head(addr, elt, n_contrib + 1), &L.head, &L.nvec, &L.vec_ok);
+    split(bucket_len, common_head(addr, elt, align, n_contrib + 1), 8, &L.head, &L.nvec, &L.vec_ok);
     L.R = n_contrib;
     L.lp = (int32_t)h->d.lp;
-    L.first = h->phase == kIdle ? 1 : 0;
     L.inv_r = (float)(1.0 / (double)n_contrib);
     L.inv_scale = (float)(1.0 / h->scale);
-    L.part_sumsq = h->part_sumsq;
-    L.part_flag = h->part_flag;
+    L.partial = h->partial;
+    L.slot_base = h->phase == kIdle ? 0 : h->slot_cursor;
+    L.lds_reserve = h->lds_reduce;
+    const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok);
+    if (L.slot_base + blocks > h->nslots)
+        return fail(ZERO_ERR_UNSUPPORTED, "bucket_reduce: partial slots exhausted");
     hipError_t e = zk::launch_reduce(L, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "bucket_reduce: launch");
     h->covered = bucket_off + bucket_len;
+    h->slot_cursor = L.slot_base + blocks;
     h->phase = kReducing;
     return ZERO_OK;
 }
@@ -368,18 +417,20 @@ zero_status zero_overflow_check(zero_shard_t h, void* stream, zero_step_info* ou
         zk::ScanLaunch L;
         std::memset(&L, 0, sizeof(L));
         const uintptr_t a = (uintptr_t)h->d.grad_shard;
-        const int el = 2;
+        const int el = 2, al = 16;
         L.g = h->d.grad_shard;
         L.n = h->S;
-        split(h->S, common_head(&a, &el, 1), &L.head, &L.nvec, &L.vec_ok);
+        split(h->S, common_head(&a, &el, &al, 1), 8, &L.head, &L.nvec, &L.vec_ok);
         L.lp = (int32_t)h->d.lp;
         L.inv_scale = (float)(1.0 / h->scale);
-        L.part_sumsq = h->part_sumsq;
-        L.part_flag = h->part_flag;
+        L.partial = h->partial;
+        L.slot_base = 0;
+        L.lds_reserve = h->lds_reduce;
         e = zk::launch_scan(L, s);
         if (e != hipSuccess) return hip_fail(e, "overflow_check: scan launch");
+        h->slot_cursor = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok);
     }
-    e = zk::launch_finalize(h->part_sumsq, h->part_flag, h->result, s);
+    e = zk::launch_finalize(h->partial, h->slot_cursor, h->level1, h->result, s);
     if (e != hipSuccess) return hip_fail(e, "overflow_check: finalize launch");
     e = hipMemcpyAsync(h->host_result, h->result, sizeof(zk::CheckResult), hipMemcpyDeviceToHost, s);
     if (e != hipSuccess) return hip_fail(e, "overflow_check: copy");
@@ -388,10 +439,13 @@ zero_status zero_overflow_check(zero_shard_t h, void* stream, zero_step_info* ou
 
     zero_step_info info;
     std::memset(&info, 0, sizeof(info));
-    info.overflow = h->host_result->flag ? 1 : 0;
+    // a non-finite stored gradient turns its workgroup partial, and so the
+    // total, into NaN; finite values alone never produce NaN
+    const double total = h->host_result->sumsq;
+    info.overflow = std::isnan(total) ? 1 : 0;
     info.skipped = info.overflow;
     info.step_t = h->t;
-    info.grad_norm = std::sqrt(h->host_result->sumsq);
+    info.grad_norm = std::sqrt(total);
     info.scale_used = h->scale;
     int64_t g;
     next_scale(h, info.overflow, &info.scale_next, &g);
@@ -438,7 +492,9 @@ zero_status zero_adam_step(zero_shard_t h, const zero_adam_hparams* hp_in, void*
         const uintptr_t addr[5] = {(uintptr_t)a.grad, (uintptr_t)a.param, (uintptr_t)a.master,
                                    (uintptr_t)a.m, (uintptr_t)a.v};
         const int elt[5] = {2, 2, 4, 4, 4};
-        split(h->S, common_head(addr, elt, 5), &a.head, &a.nvec, &a.vec_ok);
+        const int align[5] = {8, 8, 16, 16, 16};
+        split(h->S, common_head(addr, elt, align, 5), 4, &a.head, &a.ngroups, &a.vec_ok);
+        a.lds_reserve = h->lds_adam;
         a.lp = (int32_t)h->d.lp;
         a.b1 = (float)hp.beta1;
         a.b2 = (float)hp.beta2;
@@ -467,6 +523,7 @@ zero_status zero_adam_step(zero_shard_t h, const zero_adam_hparams* hp_in, void*
     h->good_steps = good_next;
     h->phase = kIdle;
     h->covered = 0;
+    h->slot_cursor = 0;
     if (out) *out = info;
     return ZERO_OK;
 }
