@@ -51,6 +51,37 @@ def measured_traffic(per_launch_elems: int):
     return t.get("hbm_bytes_per_launch")
 
 
+def copy_ceiling(torch, nbytes: int, reps: int):
+    """GB/s of the plain nontemporal copy kernel (read + write bytes / time),
+    the achievable-bandwidth line beside the roofline peak."""
+    import ctypes
+    lib_path = os.path.join(ROOT, "zero_dp_sharded_amd", "libhbmcopy.so")
+    if not os.path.exists(lib_path):
+        raise RuntimeError(f"{lib_path} missing: build with `python -m zero_dp_sharded_amd.build`")
+    lib = ctypes.CDLL(lib_path)
+    lib.hbm_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.hbm_copy.restype = ctypes.c_int
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    src.normal_()                  # realistic bit patterns: HBM power depends on data
+    stream = torch.cuda.current_stream()
+    times = []
+    for k in range(reps + 2):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        rc = lib.hbm_copy(dst.data_ptr(), src.data_ptr(), nbytes, stream.cuda_stream)
+        b.record(stream)
+        if rc != 0:
+            raise RuntimeError(f"hbm_copy failed with {rc}")
+        if k >= 2:
+            times.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in times)[len(times) // 2]
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(w, state_host, contribs_host, bucket_elems):
     import oracle
     hp = oracle.AdamHP(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
@@ -72,6 +103,8 @@ def main() -> int:
     ap.add_argument("--workload", default="128b")
     ap.add_argument("--cpu-sample", type=int, default=1 << 27,
                     help="shard elements the CPU oracle runs on (0 = skip)")
+    ap.add_argument("--only", choices=["copy"], default=None,
+                    help="run only the plain copy kernel (byte-counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -91,6 +124,12 @@ def main() -> int:
         return 2
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    copy_bytes = 8_000_000_000
+    copy_gbs = copy_ceiling(torch, copy_bytes, reps=10 if args.only is None else 3)
+    print(f"[bench] plain copy of {copy_bytes} bytes: {copy_gbs:.0f} GB/s", file=sys.stderr,
+          flush=True)
+    if args.only == "copy":
+        return 0
     w = synth.WORKLOADS[args.workload]
     S, R, cb = w.shard, w.R, w.bucket_elems
     lp_t = w.torch_lp
@@ -187,6 +226,7 @@ def main() -> int:
                    "storage": w.lp, "loss_scale": w.scale, "lr": w.lr,
                    "weight_decay": w.weight_decay},
         "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
+        "copy_ceiling_gbs": copy_gbs,
         "step_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernels_ms": {"adam": adam_avg, "reduce_all_buckets": red_avg,
                        "reduce_gbs": reduce_bytes / (red_avg * 1e-3) / 1e9},

@@ -15,6 +15,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libzeroshard.so")
 SOURCES = ["zero_kernels.hip", "zero_shard.cpp", "zero_state_bytes.cpp"]
+# benchmark helper: plain HBM copy (ceiling and counter calibration)
+COPY_LIB = os.path.join(HERE, "libhbmcopy.so")
+COPY_SOURCES = ["hbm_copy.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -29,11 +32,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    objdir = os.path.join(ROOT, "_build", "zeroshard")
-    os.makedirs(objdir, exist_ok=True)
+def _compile(sources, objdir, verbose):
     objs = []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -47,12 +48,23 @@ def build(verbose: bool = False) -> str:
         if verbose and err.strip():
             print(err, file=sys.stderr)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    return objs
+
+
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    objdir = os.path.join(ROOT, "_build", "zeroshard")
+    os.makedirs(objdir, exist_ok=True)
+    _link(_compile(SOURCES, objdir, verbose), LIB, verbose)
+    _link(_compile(COPY_SOURCES, objdir, verbose), COPY_LIB, verbose)
     return LIB
 
 
