@@ -156,3 +156,16 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(zs, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         zs.zero_abi_version()
+
+
+def test_init_rejects_too_many_buckets_before_device_work():
+    """C_B = 1 on a 2^31-element shard would need 2^32 partial slots: refused
+    during validation, before any device call (addresses are never touched)."""
+    d = zs.ZeroShardDesc(1 << 31, 1, 0, 1, zs.ZERO_FP16, 1 << 40, 2 << 40, 3 << 40, 4 << 40,
+                         5 << 40)
+    h = ctypes.c_void_p()
+    s = zs.lib().zero_shard_init(ctypes.byref(d), ctypes.byref(GOOD_HP), ctypes.byref(GOOD_LS),
+                                 ctypes.byref(h))
+    assert s == zs.ZERO_ERR_UNSUPPORTED
+    assert "bucket" in zs.zero_last_error()
+    assert h.value is None

@@ -1,0 +1,128 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py
+times (the workload's own shard, C_B and R through the C ABI).
+
+Per step:
+  - sampled elements (edges, both sides of every bucket boundary, the +inf
+    event, 65,536 random positions) of the stored gradient against the oracle
+    run on the same sampled contributions;
+  - the whole stored gradient bitwise against an independent torch fp32
+    reduce (sum in ascending r from +0, times 1/R, rounded to the 2-byte
+    format), a property that holds at any size;
+  - the norm against a torch fp64 sum of the unscaled squares of the stored
+    gradient;
+  - flags, skips, t and scale exactly against the oracle.
+After the last step: master, m, v and the 2-byte params at the sampled
+positions against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import zero_dp_sharded_amd as zs
+from gpu_common import (LP_CODE, f32, hp_of, log, lp_is_nan, ls_of, max_rel, oracle_hp, oracle_ls,
+                        u16, ulp_dist)
+from zero_dp_sharded_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+CHUNK = 1 << 27
+
+
+def sample_indices(w: synth.Workload, n_random: int = 65_536, seed: int = 1) -> np.ndarray:
+    S, cb = w.shard, w.bucket_elems
+    idx = {0, 1, 2, 3, 7, 8, 9, S - 1, S - 2, S - 3, S - 8, S - 9}
+    for b in range(0, S, cb):
+        idx.update({b - 1, b, b + 1})
+    i = synth.inject_index(S)
+    idx.update({i - 1, i, i + 1})
+    rng = np.random.default_rng(seed)
+    idx.update(rng.integers(0, S, size=n_random).tolist())
+    return np.array(sorted(x for x in idx if 0 <= x < S), dtype=np.int64)
+
+
+def torch_reduce_equal(bufs, grad, R, lp_t):
+    """Bitwise compare of the stored gradient with a torch fp32 reduce."""
+    inv_r = 1.0 / R
+    S = grad.numel()
+    for off in range(0, S, CHUNK):
+        end = min(S, off + CHUNK)
+        acc = torch.zeros(end - off, dtype=torch.float32, device=grad.device)
+        for b in bufs:
+            acc.add_(b[off:end].float())
+        ref = (acc * inv_r).to(lp_t)
+        got = grad[off:end]
+        same = (ref.view(torch.int16) == got.view(torch.int16)) | (torch.isnan(ref) & torch.isnan(got))
+        if not bool(same.all()):
+            bad = torch.nonzero(~same)[:4].flatten().tolist()
+            return False, off + bad[0] if bad else -1
+    return True, -1
+
+
+def torch_sumsq(grad, inv_scale):
+    s = torch.zeros((), dtype=torch.float64, device=grad.device)
+    for off in range(0, grad.numel(), CHUNK):
+        u = grad[off:off + CHUNK].float() * inv_scale
+        s += (u.double() ** 2).sum()
+    return float(s)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gpt2_1.5b", "7.5b_bf16", "13b_inf", "128b"])
+def test_full_size_sampled(name):
+    w = synth.WORKLOADS[name]
+    S, R, cb, lp_t = w.shard, w.R, w.bucket_elems, w.torch_lp
+    lp = LP_CODE[w.lp]
+    dev = torch.device("cuda", 0)
+    log(f"[fullsize] {w.name}: S={S} R={R} C_B={cb} steps={w.steps}")
+    idx = sample_indices(w)
+    idx_t = torch.from_numpy(idx).to(dev)
+
+    master, m, v = synth.init_state(w, dev, seed=0)
+    grad = torch.zeros(S, dtype=lp_t, device=dev)
+    param = master.to(lp_t)
+    bufs = synth.alloc_contribs(w, dev)
+    hp, ls = hp_of(w), ls_of(w)
+    ohp, ols = oracle_hp(hp), oracle_ls(ls)
+    ost = oracle.new_state(lp, f32(master[idx_t]), f32(m[idx_t]), f32(v[idx_t]), ohp, ols)
+    assert np.array_equal(u16(param[idx_t]), ost.param)
+    h = zs.zero_shard_init(master, m, v, grad, param, psi=w.psi, nd=w.nd, rank=w.rank,
+                           bucket_elems=cb, hp=hp, ls=ls)
+    try:
+        scale = ls.init_scale
+        for s in range(w.steps):
+            synth.fill_contribs(w, bufs, s, scale, seed=0)
+            cs = [u16(b[idx_t]) for b in bufs]
+            zs.reduce_buckets(h, bufs, S, cb)
+            chk = zs.zero_overflow_check(h)
+            ok, where = torch_reduce_equal(bufs, grad, R, lp_t)
+            assert ok, (name, s, "full reduce differs at", where)
+            oi = oracle.step(ost, cs, len(idx), ohp, ols)
+            gs = u16(grad[idx_t])
+            gn, on = lp_is_nan(gs, w.lp), lp_is_nan(ost.grad, w.lp)
+            assert np.array_equal(gn, on) and np.array_equal(gs[~gn], ost.grad[~on]), (name, s)
+            assert chk.overflow == oi.overflow, (name, s)
+            if not chk.overflow:
+                inv = float(np.float32(1.0 / chk.scale_used))
+                tn = np.sqrt(torch_sumsq(grad, inv))
+                assert chk.grad_norm == pytest.approx(tn, rel=1e-9), (name, s)
+            info = zs.zero_adam_step(h)
+            assert (info.overflow, info.skipped, info.step_t, info.scale_used, info.scale_next) == \
+                (oi.overflow, oi.skipped, oi.step_t, oi.scale_used, oi.scale_next), (name, s)
+            log(f"[fullsize] {name} step {s}: overflow={info.overflow} t={info.step_t} "
+                f"norm={chk.grad_norm:.6g} scale={info.scale_used}")
+            scale = info.scale_next
+        torch.cuda.synchronize()
+        assert max_rel(f32(master[idx_t]), ost.master) <= 1e-6
+        assert max_rel(f32(m[idx_t]), ost.m) <= 1e-6
+        assert max_rel(f32(v[idx_t]), ost.v) <= 1e-6
+        assert int(ulp_dist(u16(param[idx_t]), ost.param).max()) <= 1
+        bit = (np.array_equal(f32(master[idx_t]).view(np.uint32), ost.master.view(np.uint32))
+               and np.array_equal(u16(param[idx_t]), ost.param))
+        log(f"[fullsize] {name}: sampled state bitwise equal to the oracle: {bit}")
+        assert bit
+        if w.inject_step is not None:
+            assert ost.t == w.steps - 1
+    finally:
+        zs.zero_shard_destroy(h)
+        del master, m, v, grad, param, bufs
+        torch.cuda.empty_cache()

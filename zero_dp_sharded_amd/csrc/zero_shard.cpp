@@ -250,6 +250,18 @@ zero_status zero_shard_init(const zero_shard_desc* desc, const zero_adam_hparams
     st = check_ls(ls);
     if (st != ZERO_OK) return st;
 
+    // One fp64 partial per reduce workgroup of a step.  A bucket of len
+    // elements uses at most len/2048 + 2 workgroups (the element-wise path
+    // covers 2048 elements per workgroup, the vector path 4096 plus a ragged
+    // end), and the stand-alone scan needs no more.
+    const int64_t nbuckets = (S + d.bucket_elems - 1) / d.bucket_elems;
+    const int64_t nslots = S / zk::kScalarElemsPerBlock + 2 * nbuckets + 4;
+    if (nslots > (int64_t(1) << 25))
+        return fail(ZERO_ERR_UNSUPPORTED,
+                    "init: %lld buckets of %lld elements need %lld partial slots (limit 2^25); "
+                    "use a larger bucket_elems", (long long)nbuckets, (long long)d.bucket_elems,
+                    (long long)nslots);
+
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "init: hipGetDevice");
@@ -264,21 +276,8 @@ zero_status zero_shard_init(const zero_shard_desc* desc, const zero_adam_hparams
     h->t = hp->initial_step;
     h->scale = ls->init_scale;
     h->good_steps = 0;
-
-    // One fp64 partial per reduce workgroup of a step.  A bucket of len
-    // elements uses at most len/2048 + 2 workgroups (the element-wise path
-    // covers 2048 elements per workgroup, the vector path 4096 plus a ragged
-    // end), and the stand-alone scan needs no more.
-    const int64_t nbuckets = (S + d.bucket_elems - 1) / d.bucket_elems;
-    const int64_t nslots = S / zk::kScalarElemsPerBlock + 2 * nbuckets + 4;
-    if (nslots > (int64_t(1) << 25)) {
-        delete h;
-        return fail(ZERO_ERR_UNSUPPORTED,
-                    "init: %lld buckets of %lld elements need %lld partial slots (limit 2^25); "
-                    "use a larger bucket_elems", (long long)nbuckets, (long long)d.bucket_elems,
-                    (long long)nslots);
-    }
     h->nslots = nslots;
+
     const size_t ws_bytes = sizeof(double) * (size_t)(nslots + zk::kFoldMaxBlocks) +
                             sizeof(zk::CheckResult);
     e = hipMalloc(&h->ws, ws_bytes);
