@@ -2,8 +2,9 @@
 """Throughput of the owner-rank ZeRO-DP step on one MI355X.
 
 One step = every C_B bucket reduce of the owner's shard, the overflow check
-(with its one host synchronisation) and the fused Adam + cast, through the C
-ABI, on the 128B-parameter workload at Nd = 64: a 2.0e9-element shard, 4
+and the fused Adam + cast, through the C ABI (device-gated flow: the check's
+result stays on the GPU for Adam and the host waits only for its copy; the
+synchronous-check flow is timed beside it), on the 128B-parameter workload at Nd = 64: a 2.0e9-element shard, 4
 contributions, C_B = 2e8, fp16 storage, loss scale 4096, AdamW lr 6e-5, wd 0.1.
 Inputs are seeded synthetic tensors resident in HBM before timing starts; the
 same contribution batch feeds every step (each step still reads and writes
@@ -125,10 +126,10 @@ def main() -> int:
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     copy_bytes = 8_000_000_000
-    copy_gbs = copy_ceiling(torch, copy_bytes, reps=10 if args.only is None else 3)
-    print(f"[bench] plain copy of {copy_bytes} bytes: {copy_gbs:.0f} GB/s", file=sys.stderr,
-          flush=True)
     if args.only == "copy":
+        copy_gbs = copy_ceiling(torch, copy_bytes, reps=3)
+        print(f"[bench] plain copy of {copy_bytes} bytes: {copy_gbs:.0f} GB/s", file=sys.stderr,
+              flush=True)
         return 0
     w = synth.WORKLOADS[args.workload]
     S, R, cb = w.shard, w.R, w.bucket_elems
@@ -152,13 +153,24 @@ def main() -> int:
     ptrs = [b.data_ptr() for b in bufs]
     offs = [(off, min(cb, S - off)) for off in range(0, S, cb)]
 
-    def step(ev=None):
-        for k, (off, ln) in enumerate(offs):
-            if ev is not None:
-                ev["r"][k][0].record(stream)
+    def step(ev=None, flow="gated"):
+        # four timing events per step: around all bucket reduces and around
+        # the Adam enqueue (more events between kernels cost step time)
+        if ev is not None:
+            ev["r"][0].record(stream)
+        for off, ln in offs:
             zs.zero_bucket_reduce(h, [p + 2 * off for p in ptrs], off, ln, stream)
+        if ev is not None:
+            ev["r"][1].record(stream)
+        if flow == "gated":
+            # check, result copy and device-gated Adam in one enqueue; the
+            # host waits only for the result copy
             if ev is not None:
-                ev["r"][k][1].record(stream)
+                ev["a"][0].record(stream)
+            zs.zero_adam_step_gated(h, None, stream)
+            if ev is not None:
+                ev["a"][1].record(stream)
+            return zs.zero_step_resolve(h)
         info = zs.zero_overflow_check(h, stream)
         if ev is not None:
             ev["a"][0].record(stream)
@@ -173,22 +185,36 @@ def main() -> int:
     print(f"[bench] warmup {args.warmup} done", file=sys.stderr, flush=True)
 
     mk = lambda: torch.cuda.Event(enable_timing=True)
-    evs = [{"r": [(mk(), mk()) for _ in offs], "a": (mk(), mk())} for _ in range(args.steps)]
-    skipped = 0
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        info = step(evs[k])
-        skipped += info.overflow
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    adam_ms = [e["a"][0].elapsed_time(e["a"][1]) for e in evs]
-    red_ms = [sum(a.elapsed_time(b) for a, b in e["r"]) for e in evs]
-    adam_avg = sum(adam_ms) / len(adam_ms)
-    red_avg = sum(red_ms) / len(red_ms)
-    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step, adam {adam_avg:.3f} ms, "
-          f"reduce {red_avg:.3f} ms, skipped {skipped}", file=sys.stderr, flush=True)
+
+    def timed(flow):
+        evs = [{"r": (mk(), mk()), "a": (mk(), mk())} for _ in range(args.steps)]
+        skipped = 0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            info = step(evs[k], flow)
+            skipped += info.overflow
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms = (t1 - t0) * 1e3 / args.steps
+        adam = [e["a"][0].elapsed_time(e["a"][1]) for e in evs]
+        red = [e["r"][0].elapsed_time(e["r"][1]) for e in evs]
+        return ms, sum(adam) / len(adam), sum(red) / len(red), skipped
+
+    ms_step, adam_avg, red_avg, skipped = timed("gated")
+    print(f"[bench] timed {args.steps} gated steps: {ms_step:.3f} ms/step, adam (with check "
+          f"fold + copy) {adam_avg:.3f} ms, reduce {red_avg:.3f} ms, skipped {skipped}",
+          file=sys.stderr, flush=True)
+    ms_sync, adam_sync, red_sync, skipped_sync = timed("sync")
+    print(f"[bench] timed {args.steps} synchronous-check steps: {ms_sync:.3f} ms/step, adam "
+          f"{adam_sync:.3f} ms, reduce {red_sync:.3f} ms", file=sys.stderr, flush=True)
+
+    # The copy ceiling runs after the step timing: allocating and freeing its
+    # 16 GB before the shard arrays were allocated slowed the Adam pass by ~5%
+    # on MI355X (placement of the five streamed arrays).
+    copy_gbs = copy_ceiling(torch, copy_bytes, reps=10)
+    print(f"[bench] plain copy of {copy_bytes} bytes: {copy_gbs:.0f} GB/s", file=sys.stderr,
+          flush=True)
 
     adam_bytes = 28 * S                      # grad 2 + master/m/v 12 read; 12 + param 2 written
     reduce_bytes = (2 * R + 2) * S
@@ -228,12 +254,18 @@ def main() -> int:
         "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
         "copy_ceiling_gbs": copy_gbs,
         "step_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "kernels_ms": {"adam": adam_avg, "reduce_all_buckets": red_avg,
+        "kernels_ms": {"adam_incl_check_fold": adam_avg, "adam_sync_flow": adam_sync,
+                       "reduce_all_buckets": red_avg,
                        "reduce_gbs": reduce_bytes / (red_avg * 1e-3) / 1e9},
+        "flow": "device-gated check + Adam (zero_adam_step_gated / zero_step_resolve)",
+        "ms_per_step_sync_check_flow": ms_sync,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "adam_kernel<fp16, decoupled wd>",
-                     "algorithmic_bytes_per_launch": adam_bytes},
+                     "kernel": "adam_vec_kernel<fp16, decoupled wd>",
+                     "algorithmic_bytes_per_launch": adam_bytes,
+                     "launch_ms": adam_avg,
+                     "timing": "HIP events around the gated Adam enqueue (includes the "
+                               "two fold kernels and the 16-byte result copy)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -231,6 +231,32 @@ zero_status zero_overflow_check(zero_shard_t h, void* stream, zero_step_info* ou
 zero_status zero_adam_step(zero_shard_t h, const zero_adam_hparams* hp, void* stream,
                            zero_step_info* out);
 
+/*
+ * Device-gated check + Adam: the same step as zero_overflow_check followed by
+ * zero_adam_step, without the stream stall between them.  After the buckets
+ * of a step (or with none, scanning a caller-filled grad_shard), this
+ * enqueues the check, an asynchronous copy of its result to pinned host
+ * memory, and the Adam update for step t + 1; every Adam workgroup reads the
+ * check's device result first and returns at once when it reports a
+ * non-finite gradient, so a skipped step still changes no state.  The host
+ * then calls zero_step_resolve, which waits only for the result copy (not for
+ * the update) and commits t and the loss scale.  Callers that hold a stream
+ * of steps in flight keep the GPU busy across the decision.  hp as in
+ * zero_adam_step.
+ * Errors: STATE (dead handle, partial coverage, step already checked or
+ * pending), INVALID_ARG (hp out of range), HIP.
+ */
+zero_status zero_adam_step_gated(zero_shard_t h, const zero_adam_hparams* hp, void* stream);
+
+/*
+ * Finish a gated step: wait for its check result, fill *out (may be NULL) as
+ * zero_adam_step would, advance t when the step was applied and update the
+ * loss scale.  The update itself may still be running on the stream.  Until
+ * this call, every other step call on the handle returns ZERO_ERR_STATE.
+ * Errors: STATE (dead handle, no gated step pending), HIP.
+ */
+zero_status zero_step_resolve(zero_shard_t h, zero_step_info* out);
+
 /* Step counter, current loss scale and clean-step count (for checkpoints). */
 zero_status zero_shard_get_counters(zero_shard_t h, int64_t* step_t, double* scale,
                                     int64_t* good_steps);

@@ -77,12 +77,14 @@ class GpuRun:
 def run_gpu(w: synth.Workload, *, elems: Optional[int] = None, steps: Optional[int] = None,
             seed: int = 0, bucket_elems: Optional[int] = None, hp: Optional[zs.AdamHParams] = None,
             ls: Optional[zs.LossScaleCfg] = None, keep_contribs: bool = True,
-            offsets: Optional[dict] = None, hook=None) -> GpuRun:
+            offsets: Optional[dict] = None, hook=None, flow: str = "sync") -> GpuRun:
     """Run `steps` owner-rank steps of workload w (its first `elems` shard
     elements) through the C ABI on cuda:0.  offsets maps an array name
     ('master', 'm', 'v', 'grad', 'param', 'contrib') to an element offset of its
     base pointer inside a larger allocation (alignment tests).  hook(step,
-    bufs) may edit the contributions of a step before it runs."""
+    bufs) may edit the contributions of a step before it runs.  flow "sync"
+    uses zero_overflow_check + zero_adam_step, "gated" zero_adam_step_gated +
+    zero_step_resolve."""
     dev = torch.device("cuda", 0)
     S = w.shard if elems is None else elems
     steps = w.steps if steps is None else steps
@@ -122,10 +124,14 @@ def run_gpu(w: synth.Workload, *, elems: Optional[int] = None, steps: Optional[i
             if keep_contribs:
                 kept.append([u16(b) for b in bufs])
             zs.reduce_buckets(h, bufs, S, cb)
-            chk = zs.zero_overflow_check(h)
-            info = zs.zero_adam_step(h)
-            assert info.overflow == chk.overflow
-            assert info.grad_norm == chk.grad_norm or (np.isnan(info.grad_norm) and np.isnan(chk.grad_norm))
+            if flow == "gated":
+                zs.zero_adam_step_gated(h)
+                info = zs.zero_step_resolve(h)
+            else:
+                chk = zs.zero_overflow_check(h)
+                info = zs.zero_adam_step(h)
+                assert info.overflow == chk.overflow
+                assert info.grad_norm == chk.grad_norm or (np.isnan(info.grad_norm) and np.isnan(chk.grad_norm))
             infos.append(info)
             scale = info.scale_next
         torch.cuda.synchronize()

@@ -308,3 +308,62 @@ def test_abi_state_machine_errors_leave_state_unchanged():
         zs.zero_shard_destroy(h)
     assert L.zero_shard_destroy(h) == zs.ZERO_ERR_STATE
     assert L.zero_bucket_reduce(h, arr(0), R, 0, cb, None) == zs.ZERO_ERR_STATE
+
+
+@pytest.mark.parametrize("name,elems,cb", [("gpt2_1.5b", 300_007, 65_536), ("13b_inf", 120_013, 16_384),
+                                           ("7.5b_bf16", 90_001, 30_000)])
+def test_gated_flow_matches_oracle(name, elems, cb):
+    """The device-gated check + Adam gives the synchronous flow's results,
+    including the skipped overflow step of the 13B workload."""
+    w = W[name]
+    g = run_gpu(w, elems=elems, bucket_elems=cb, flow="gated")
+    st, oi = run_oracle(w, g, bucket_elems=cb)
+    assert compare(w, g, st, oi, f"gated {name}")["bitwise"]
+    s = run_gpu(w, elems=elems, bucket_elems=cb, flow="sync")
+    for k in ("master", "m", "v", "grad", "param"):
+        assert np.array_equal(getattr(g, k).view(np.uint8), getattr(s, k).view(np.uint8)), k
+    assert [(i.overflow, i.step_t, i.scale_next) for i in g.infos] == \
+        [(i.overflow, i.step_t, i.scale_next) for i in s.infos]
+
+
+def test_gated_skip_and_state_errors():
+    n, cb = 20_000, 8_192
+    h, t = _handle(n, cb=cb)
+    L = zs.lib()
+    R = 2
+    bufs = [torch.randn(n, device="cuda").half() for _ in range(R)]
+    bufs[1][n // 3] = float("inf")
+    info = zs.ZeroStepInfo()
+    try:
+        before = {k: v.clone() for k, v in t.items()}
+        # gated step with partial coverage is refused
+        zs.reduce_buckets(h, bufs, cb, cb)        # only the first bucket
+        assert L.zero_adam_step_gated(h, None, None) == zs.ZERO_ERR_STATE
+        for off in range(cb, n, cb):
+            ln = min(cb, n - off)
+            zs.zero_bucket_reduce(h, [b.data_ptr() + 2 * off for b in bufs], off, ln)
+        assert L.zero_step_resolve(h, ctypes.byref(info)) == zs.ZERO_ERR_STATE   # nothing pending
+        zs.zero_adam_step_gated(h)
+        # everything else is refused while the step is pending
+        arr = (ctypes.c_void_p * R)(*[b.data_ptr() for b in bufs])
+        assert L.zero_bucket_reduce(h, arr, R, 0, cb, None) == zs.ZERO_ERR_STATE
+        assert L.zero_overflow_check(h, None, ctypes.byref(info)) == zs.ZERO_ERR_STATE
+        assert L.zero_adam_step(h, None, None, ctypes.byref(info)) == zs.ZERO_ERR_STATE
+        assert L.zero_adam_step_gated(h, None, None) == zs.ZERO_ERR_STATE
+        assert L.zero_shard_set_counters(h, 0, 1.0, 0) == zs.ZERO_ERR_STATE
+        res = zs.zero_step_resolve(h)
+        assert res.overflow == 1 and res.skipped == 1 and res.step_t == 0
+        assert res.scale_next == 512.0
+        torch.cuda.synchronize()
+        for k in ("master", "m", "v", "param"):
+            assert torch.equal(before[k], t[k]), k
+        # a clean gated step after the skip applies t = 1
+        bufs[1][n // 3] = 0.5
+        zs.reduce_buckets(h, bufs, n, cb)
+        zs.zero_adam_step_gated(h)
+        res = zs.zero_step_resolve(h)
+        assert res.overflow == 0 and res.step_t == 1
+        torch.cuda.synchronize()
+        assert not torch.equal(before["master"], t["master"])
+    finally:
+        zs.zero_shard_destroy(h)

@@ -31,7 +31,8 @@ ZERO_MAX_CONTRIB = 64
 
 ABI_SYMBOLS = (
     "zero_state_bytes", "zero_state_bytes_ex", "zero_shard_init", "zero_bucket_reduce",
-    "zero_overflow_check", "zero_adam_step", "zero_shard_get_counters",
+    "zero_overflow_check", "zero_adam_step", "zero_adam_step_gated", "zero_step_resolve",
+    "zero_shard_get_counters",
     "zero_shard_set_counters", "zero_shard_destroy", "zero_status_str", "zero_last_error",
     "zero_abi_version",
 )
@@ -99,6 +100,8 @@ def lib() -> ctypes.CDLL:
         L.zero_overflow_check.argtypes = [_vp, _vp, ctypes.POINTER(ZeroStepInfo)]
         L.zero_adam_step.argtypes = [_vp, ctypes.POINTER(ZeroAdamHParams), _vp,
                                      ctypes.POINTER(ZeroStepInfo)]
+        L.zero_adam_step_gated.argtypes = [_vp, ctypes.POINTER(ZeroAdamHParams), _vp]
+        L.zero_step_resolve.argtypes = [_vp, ctypes.POINTER(ZeroStepInfo)]
         L.zero_shard_get_counters.argtypes = [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_f64),
                                               ctypes.POINTER(_i64)]
         L.zero_shard_set_counters.argtypes = [_vp, _i64, _f64, _i64]
@@ -111,6 +114,7 @@ def lib() -> ctypes.CDLL:
         L.zero_abi_version.argtypes = []
         for name in ("zero_state_bytes", "zero_state_bytes_ex", "zero_shard_init",
                      "zero_bucket_reduce", "zero_overflow_check", "zero_adam_step",
+                     "zero_adam_step_gated", "zero_step_resolve",
                      "zero_shard_get_counters", "zero_shard_set_counters", "zero_shard_destroy"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -281,6 +285,17 @@ def zero_adam_step(h: int, hp: Optional[AdamHParams] = None, stream=None) -> Ste
     hpc = ctypes.byref(hp.to_c()) if hp is not None else None
     _check(lib().zero_adam_step(h, hpc, _stream_ptr(stream), ctypes.byref(out)),
            "zero_adam_step")
+    return StepInfo.from_c(out)
+
+
+def zero_adam_step_gated(h: int, hp: Optional[AdamHParams] = None, stream=None) -> None:
+    hpc = ctypes.byref(hp.to_c()) if hp is not None else None
+    _check(lib().zero_adam_step_gated(h, hpc, _stream_ptr(stream)), "zero_adam_step_gated")
+
+
+def zero_step_resolve(h: int) -> StepInfo:
+    out = ZeroStepInfo()
+    _check(lib().zero_step_resolve(h, ctypes.byref(out)), "zero_step_resolve")
     return StepInfo.from_c(out)
 
 

@@ -12,20 +12,46 @@ constexpr int kMaxContrib = 64;
 // Reduce / scan: 256 lanes per workgroup, each lane two runs of 8 two-byte
 // elements (each load instruction of a wave covers 1 KiB contiguously);
 // residency capped at 4 workgroups (16 waves) per CU.
-constexpr int kRedBlock = 256;
-constexpr int kRedRuns = 2;
+// (The ZK_* macros exist only to build tuning variants; the defaults are the
+// measured optimum.)
+#ifndef ZK_RED_BLOCK
+#define ZK_RED_BLOCK 256
+#endif
+#ifndef ZK_RED_RUNS
+#define ZK_RED_RUNS 2
+#endif
+#ifndef ZK_RED_PER_CU
+#define ZK_RED_PER_CU 4
+#endif
+#ifndef ZK_ADAM_BLOCK
+#define ZK_ADAM_BLOCK 64
+#endif
+#ifndef ZK_ADAM_GROUPS
+#define ZK_ADAM_GROUPS 1
+#endif
+#ifndef ZK_ADAM_PER_CU
+#define ZK_ADAM_PER_CU 10
+#endif
+constexpr int kRedBlock = ZK_RED_BLOCK;
+constexpr int kRedRuns = ZK_RED_RUNS;
 constexpr int64_t kRedElemsPerBlock = (int64_t)kRedBlock * kRedRuns * 8;   // 4096
-constexpr int kRedPerCU = 4;
-// Adam: 128 lanes per workgroup, each lane two groups of 4 elements;
-// residency capped at 5 workgroups (10 waves) per CU.
-constexpr int kAdamBlock = 128;
-constexpr int kAdamGroups = 2;
-constexpr int64_t kAdamElemsPerBlock = (int64_t)kAdamBlock * kAdamGroups * 4;  // 1024
-constexpr int kAdamPerCU = 5;
+constexpr int kRedPerCU = ZK_RED_PER_CU;
+// Adam: one wave (64 lanes) per workgroup, each lane one group of 4 elements;
+// residency capped at 10 workgroups (10 waves) per CU.
+constexpr int kAdamBlock = ZK_ADAM_BLOCK;
+constexpr int kAdamGroups = ZK_ADAM_GROUPS;
+constexpr int64_t kAdamElemsPerBlock = (int64_t)kAdamBlock * kAdamGroups * 4;  // 256
+constexpr int kAdamPerCU = ZK_ADAM_PER_CU;
 // Element-wise kernels (unaligned heads and tails, or arrays without a common
 // alignment): 256 lanes, 8 elements per lane, lane-consecutive per step.
 constexpr int kScalarBlock = 256;
 constexpr int64_t kScalarElemsPerBlock = (int64_t)kScalarBlock * 8;
+// Work-items per launch stay below 2^31; larger bodies are split into
+// consecutive launches.
+#ifndef ZK_MAX_LAUNCH_ITEMS
+#define ZK_MAX_LAUNCH_ITEMS (int64_t(1) << 31)
+#endif
+constexpr int64_t kMaxLaunchItems = ZK_MAX_LAUNCH_ITEMS;
 // Fixed-order fold of the per-workgroup partials.
 constexpr int kFoldBlock = 256;
 constexpr int kFoldMaxBlocks = 1024;
@@ -94,6 +120,9 @@ struct AdamLaunch {
     int32_t wd_kind;
     uint32_t lds_reserve;
     float b1, b2, omb1, omb2, bc1, bc2, lr, eps, wd, inv_scale;
+    // device-gated launch: every workgroup returns at once when gate->sumsq
+    // is NaN (a non-finite stored gradient); nullptr = always apply
+    const CheckResult* gate;
 };
 
 // Partial slots a reduce / scan of this layout writes: one per workgroup of

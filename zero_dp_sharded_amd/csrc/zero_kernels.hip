@@ -171,10 +171,10 @@ __device__ __forceinline__ void reduce_s(const ReduceLaunch& L, int64_t e, int& 
     check_s<LP>(o, L.inv_scale, flag, ss);
 }
 
-// Vector body: workgroup b covers runs [b*512, b*512 + 512); lane l owns runs
-// b*512 + l and b*512 + 256 + l.  Element offsets past `head` are multiples of
-// 8, so contribution and output pointers advanced by `head` are 16-byte
-// aligned and are indexed in units of 8 elements.
+// Vector body: workgroup b covers runs [b*B*U, (b+1)*B*U) for B lanes and U
+// runs per lane; lane l owns runs b*B*U + u*B + l.  Element offsets past `head`
+// are multiples of 8, so contribution and output pointers advanced by `head`
+// are 16-byte aligned and are indexed in units of 8 elements.
 template <int LP, int RT>
 __global__ __launch_bounds__(kRedBlock) void reduce_vec_kernel(ReduceLaunch L)
 {
@@ -326,8 +326,18 @@ __device__ __forceinline__ void adam_e(float graw, float& p, float& m, float& v,
 
 // Vector body: groups of 4 elements past `head` (fp32 pointers advanced by
 // head are 16-byte aligned, 2-byte pointers 8-byte aligned).  Workgroup b
-// covers groups [b*256, b*256 + 256); lane l owns groups b*256 + l and
-// b*256 + 128 + l, and issues all eight loads before any arithmetic.
+// covers groups [b*B*G, (b+1)*B*G) for B lanes and G groups per lane; lane l
+// owns groups b*B*G + u*B + l, u < G, and issues all loads before any
+// arithmetic.
+// Device-side skip of a gated launch: the fold leaves NaN in the result when
+// any stored gradient is not finite.  The vector kernel reads the gate after
+// issuing its loads (a skipped step then costs the 14 load bytes per element
+// but writes nothing); the element-wise kernel reads it first.
+__device__ __forceinline__ bool gated_off(const AdamLaunch& a)
+{
+    return a.gate != nullptr && __builtin_isnan(a.gate->sumsq);
+}
+
 template <int LP, int WD>
 __global__ __launch_bounds__(kAdamBlock) void adam_vec_kernel(AdamLaunch a)
 {
@@ -350,6 +360,9 @@ __global__ __launch_bounds__(kAdamBlock) void adam_vec_kernel(AdamLaunch a)
             v[u] = ld_nt<f4>(vb, q);
         }
     }
+    // The gate is read after the loads are issued, so its latency overlaps
+    // them; on a skipped step the workgroup returns before any store.
+    if (gated_off(a)) return;
 #pragma unroll
     for (int u = 0; u < kAdamGroups; ++u) {
         const int64_t q = q0 + u * kAdamBlock;
@@ -376,6 +389,7 @@ template <int LP, int WD>
 __global__ __launch_bounds__(kScalarBlock) void adam_elem_kernel(AdamLaunch a, Ranges rg)
 {
     using T = typename Fmt<LP>::T;
+    if (gated_off(a)) return;
     const int64_t cnt = rg.count();
     for (int j = 0; j < (int)(kScalarElemsPerBlock / kScalarBlock); ++j) {
         const int64_t k = (int64_t)blockIdx.x * kScalarElemsPerBlock + j * kScalarBlock + threadIdx.x;
@@ -408,20 +422,36 @@ Ranges ranges_of(int64_t n, int64_t head, int64_t body, int32_t vec_ok)
 }
 
 template <int LP>
+hipError_t reduce_vec_launch(const ReduceLaunch& L, unsigned grid, hipStream_t s)
+{
+    const unsigned lds = L.lds_reserve;
+    switch (L.R) {
+    case 1: reduce_vec_kernel<LP, 1><<<grid, kRedBlock, lds, s>>>(L); break;
+    case 2: reduce_vec_kernel<LP, 2><<<grid, kRedBlock, lds, s>>>(L); break;
+    case 4: reduce_vec_kernel<LP, 4><<<grid, kRedBlock, lds, s>>>(L); break;
+    case 8: reduce_vec_kernel<LP, 8><<<grid, kRedBlock, lds, s>>>(L); break;
+    case 16: reduce_vec_kernel<LP, 16><<<grid, kRedBlock, lds, s>>>(L); break;
+    default: reduce_vec_kernel<LP, 0><<<grid, kRedBlock, lds, s>>>(L); break;
+    }
+    return hipGetLastError();
+}
+
+template <int LP>
 hipError_t reduce_dispatch(const ReduceLaunch& L, hipStream_t s)
 {
-    const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, (int64_t)kRedBlock * kRedRuns) : 0;
-    if (vblocks > 0) {
-        const unsigned grid = (unsigned)vblocks;
-        const unsigned lds = L.lds_reserve;
-        switch (L.R) {
-        case 1: reduce_vec_kernel<LP, 1><<<grid, kRedBlock, lds, s>>>(L); break;
-        case 2: reduce_vec_kernel<LP, 2><<<grid, kRedBlock, lds, s>>>(L); break;
-        case 4: reduce_vec_kernel<LP, 4><<<grid, kRedBlock, lds, s>>>(L); break;
-        case 8: reduce_vec_kernel<LP, 8><<<grid, kRedBlock, lds, s>>>(L); break;
-        case 16: reduce_vec_kernel<LP, 16><<<grid, kRedBlock, lds, s>>>(L); break;
-        default: reduce_vec_kernel<LP, 0><<<grid, kRedBlock, lds, s>>>(L); break;
-        }
+    const int64_t runs_per_block = (int64_t)kRedBlock * kRedRuns;
+    const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, runs_per_block) : 0;
+    // consecutive launches of at most kMaxLaunchItems work-items; each starts
+    // its runs and its partial slots where the previous one stopped
+    const int64_t max_blocks = kMaxLaunchItems / kRedBlock;
+    for (int64_t b0 = 0; b0 < vblocks; b0 += max_blocks) {
+        const int64_t nb = vblocks - b0 < max_blocks ? vblocks - b0 : max_blocks;
+        ReduceLaunch part = L;
+        part.head = L.head + 8 * runs_per_block * b0;
+        part.nvec = L.nvec - runs_per_block * b0;
+        part.slot_base = L.slot_base + b0;
+        hipError_t e = reduce_vec_launch<LP>(part, (unsigned)nb, s);
+        if (e != hipSuccess) return e;
     }
     const Ranges rg = ranges_of(L.n, L.head, 8 * L.nvec, L.vec_ok);
     const int64_t sblocks = ceil_div(rg.a_len + rg.b_len, kScalarElemsPerBlock);
@@ -433,9 +463,18 @@ hipError_t reduce_dispatch(const ReduceLaunch& L, hipStream_t s)
 template <int LP, int WD>
 hipError_t adam_dispatch(const AdamLaunch& a, hipStream_t s)
 {
-    const int64_t vblocks = a.vec_ok ? ceil_div(a.ngroups, (int64_t)kAdamBlock * kAdamGroups) : 0;
-    if (vblocks > 0)
-        adam_vec_kernel<LP, WD><<<(unsigned)vblocks, kAdamBlock, a.lds_reserve, s>>>(a);
+    const int64_t groups_per_block = (int64_t)kAdamBlock * kAdamGroups;
+    const int64_t vblocks = a.vec_ok ? ceil_div(a.ngroups, groups_per_block) : 0;
+    const int64_t max_blocks = kMaxLaunchItems / kAdamBlock;
+    for (int64_t b0 = 0; b0 < vblocks; b0 += max_blocks) {
+        const int64_t nb = vblocks - b0 < max_blocks ? vblocks - b0 : max_blocks;
+        AdamLaunch part = a;
+        part.head = a.head + 4 * groups_per_block * b0;
+        part.ngroups = a.ngroups - groups_per_block * b0;
+        adam_vec_kernel<LP, WD><<<(unsigned)nb, kAdamBlock, a.lds_reserve, s>>>(part);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const Ranges rg = ranges_of(a.n, a.head, 4 * a.ngroups, a.vec_ok);
     const int64_t sblocks = ceil_div(rg.a_len + rg.b_len, kScalarElemsPerBlock);
     if (sblocks > 0) adam_elem_kernel<LP, WD><<<(unsigned)sblocks, kScalarBlock, 0, s>>>(a, rg);
@@ -455,9 +494,19 @@ hipError_t adam_dispatch_wd(const AdamLaunch& a, hipStream_t s)
 template <int LP>
 hipError_t scan_dispatch(const ScanLaunch& L, hipStream_t s)
 {
-    const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, (int64_t)kRedBlock * kRedRuns) : 0;
-    if (vblocks > 0)
-        scan_vec_kernel<LP><<<(unsigned)vblocks, kRedBlock, L.lds_reserve, s>>>(L);
+    const int64_t runs_per_block = (int64_t)kRedBlock * kRedRuns;
+    const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, runs_per_block) : 0;
+    const int64_t max_blocks = kMaxLaunchItems / kRedBlock;
+    for (int64_t b0 = 0; b0 < vblocks; b0 += max_blocks) {
+        const int64_t nb = vblocks - b0 < max_blocks ? vblocks - b0 : max_blocks;
+        ScanLaunch part = L;
+        part.head = L.head + 8 * runs_per_block * b0;
+        part.nvec = L.nvec - runs_per_block * b0;
+        part.slot_base = L.slot_base + b0;
+        scan_vec_kernel<LP><<<(unsigned)nb, kRedBlock, L.lds_reserve, s>>>(part);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const Ranges rg = ranges_of(L.n, L.head, 8 * L.nvec, L.vec_ok);
     const int64_t sblocks = ceil_div(rg.a_len + rg.b_len, kScalarElemsPerBlock);
     if (sblocks > 0)

@@ -37,7 +37,7 @@ zero_status hip_fail(hipError_t e, const char* what)
     return fail(ZERO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-enum Phase { kIdle = 0, kReducing = 1, kChecked = 2 };
+enum Phase { kIdle = 0, kReducing = 1, kChecked = 2, kPending = 3 };
 
 }  // namespace
 
@@ -69,6 +69,10 @@ struct zero_shard_s {
     // dynamic LDS reserved per workgroup to cap residency per CU
     uint32_t lds_adam = 0;
     uint32_t lds_reduce = 0;
+    // gated steps: event after the result copy, and the speculative update
+    hipEvent_t result_ready = nullptr;
+    double pend_pw1 = 1.0, pend_pw2 = 1.0;
+    bool pend_same_betas = false;
 };
 
 namespace {
@@ -251,11 +255,13 @@ zero_status zero_shard_init(const zero_shard_desc* desc, const zero_adam_hparams
     if (st != ZERO_OK) return st;
 
     // One fp64 partial per reduce workgroup of a step.  A bucket of len
-    // elements uses at most len/2048 + 2 workgroups (the element-wise path
-    // covers 2048 elements per workgroup, the vector path 4096 plus a ragged
-    // end), and the stand-alone scan needs no more.
+    // elements uses at most len/per + 2 workgroups, per being the smaller of
+    // the element-wise and the vector kernels' elements per workgroup (plus a
+    // ragged end), and the stand-alone scan needs no more.
+    const int64_t per = zk::kScalarElemsPerBlock < zk::kRedElemsPerBlock
+                            ? zk::kScalarElemsPerBlock : zk::kRedElemsPerBlock;
     const int64_t nbuckets = (S + d.bucket_elems - 1) / d.bucket_elems;
-    const int64_t nslots = S / zk::kScalarElemsPerBlock + 2 * nbuckets + 4;
+    const int64_t nslots = S / per + 2 * nbuckets + 4;
     if (nslots > (int64_t(1) << 25))
         return fail(ZERO_ERR_UNSUPPORTED,
                     "init: %lld buckets of %lld elements need %lld partial slots (limit 2^25); "
@@ -309,6 +315,14 @@ zero_status zero_shard_init(const zero_shard_desc* desc, const zero_adam_hparams
         return fail(ZERO_ERR_OOM, "init: hipHostMalloc: %s", hipGetErrorString(e));
     }
     std::memset(h->host_result, 0, 64);
+    e = hipEventCreateWithFlags(&h->result_ready, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        (void)hipFree(h->ws);
+        (void)hipHostFree(h->host_result);
+        delete h;
+        (void)hipGetLastError();
+        return fail(ZERO_ERR_HIP, "init: hipEventCreate: %s", hipGetErrorString(e));
+    }
     {
         std::lock_guard<std::mutex> lk(g_live_mu);
         g_live.insert(h);
@@ -330,6 +344,7 @@ zero_status zero_shard_destroy(zero_shard_t h)
     (void)hipDeviceSynchronize();
     (void)hipFree(h->ws);
     (void)hipHostFree(h->host_result);
+    if (h->result_ready) (void)hipEventDestroy(h->result_ready);
     if (cur != h->device && cur >= 0) (void)hipSetDevice(cur);
     delete h;
     return ZERO_OK;
@@ -357,6 +372,8 @@ zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int3
                     (long long)bucket_len, (long long)h->d.bucket_elems);
     if (h->phase == kChecked)
         return fail(ZERO_ERR_STATE, "bucket_reduce: step already checked; call zero_adam_step");
+    if (h->phase == kPending)
+        return fail(ZERO_ERR_STATE, "bucket_reduce: a gated step is pending; call zero_step_resolve");
     const int64_t expect = h->phase == kIdle ? 0 : h->covered;
     if (bucket_off != expect)
         return fail(ZERO_ERR_STATE, "bucket_reduce: expected bucket at %lld, got %lld",
@@ -399,18 +416,13 @@ zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int3
     return ZERO_OK;
 }
 
-zero_status zero_overflow_check(zero_shard_t h, void* stream, zero_step_info* out)
+}  // extern "C"
+
+// Launch the check of the step on `s`: the stand-alone scan when no bucket was
+// reduced, the fixed-order fold of the partials, and the copy of the result to
+// pinned host memory.  Call only in phase kIdle or kReducing with full coverage.
+static zero_status launch_check(zero_shard_s* h, hipStream_t s, const char* who)
 {
-    if (!live(h)) return fail(ZERO_ERR_STATE, "overflow_check: not a live handle");
-    if (!out) return fail(ZERO_ERR_INVALID_ARG, "overflow_check: NULL out");
-    if (h->phase == kChecked) {
-        *out = h->check;
-        return ZERO_OK;
-    }
-    if (h->phase == kReducing && h->covered != h->S)
-        return fail(ZERO_ERR_STATE, "overflow_check: buckets cover [0, %lld) of [0, %lld)",
-                    (long long)h->covered, (long long)h->S);
-    hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (h->phase == kIdle) {
         zk::ScanLaunch L;
@@ -426,20 +438,23 @@ zero_status zero_overflow_check(zero_shard_t h, void* stream, zero_step_info* ou
         L.slot_base = 0;
         L.lds_reserve = h->lds_reduce;
         e = zk::launch_scan(L, s);
-        if (e != hipSuccess) return hip_fail(e, "overflow_check: scan launch");
+        if (e != hipSuccess) return hip_fail(e, who);
         h->slot_cursor = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok);
     }
     e = zk::launch_finalize(h->partial, h->slot_cursor, h->level1, h->result, s);
-    if (e != hipSuccess) return hip_fail(e, "overflow_check: finalize launch");
+    if (e != hipSuccess) return hip_fail(e, who);
     e = hipMemcpyAsync(h->host_result, h->result, sizeof(zk::CheckResult), hipMemcpyDeviceToHost, s);
-    if (e != hipSuccess) return hip_fail(e, "overflow_check: copy");
-    e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return hip_fail(e, "overflow_check: synchronize");
+    if (e != hipSuccess) return hip_fail(e, who);
+    return ZERO_OK;
+}
 
+// The step's result from the pinned copy: overflow when the total is NaN (a
+// non-finite stored gradient makes its workgroup partial NaN; finite values
+// alone never produce NaN).
+static zero_step_info read_check(zero_shard_s* h)
+{
     zero_step_info info;
     std::memset(&info, 0, sizeof(info));
-    // a non-finite stored gradient turns its workgroup partial, and so the
-    // total, into NaN; finite values alone never produce NaN
     const double total = h->host_result->sumsq;
     info.overflow = std::isnan(total) ? 1 : 0;
     info.skipped = info.overflow;
@@ -448,9 +463,110 @@ zero_status zero_overflow_check(zero_shard_t h, void* stream, zero_step_info* ou
     info.scale_used = h->scale;
     int64_t g;
     next_scale(h, info.overflow, &info.scale_next, &g);
-    h->check = info;
+    return info;
+}
+
+// Launch Adam for applied step t = h->t + 1 with hyper-parameters hp; gate is
+// the device result a gated launch reads (nullptr = apply unconditionally).
+// Returns the fp64 powers beta^t it used and whether they extend the cache.
+static zero_status launch_adam_step(zero_shard_s* h, const zero_adam_hparams& hp, hipStream_t s,
+                                    const zk::CheckResult* gate, double* pw1_out,
+                                    double* pw2_out, bool* same_betas_out, const char* who)
+{
+    const int64_t t = h->t + 1;
+    double pw1, pw2;
+    const bool same_betas = hp.beta1 == h->hp.beta1 && hp.beta2 == h->hp.beta2;
+    if (same_betas && h->pw_t == t - 1) {
+        pw1 = h->pw1 * (double)(float)hp.beta1;
+        pw2 = h->pw2 * (double)(float)hp.beta2;
+    } else {
+        pw1 = beta_pow(hp.beta1, t);
+        pw2 = beta_pow(hp.beta2, t);
+    }
+    zk::AdamLaunch a;
+    std::memset(&a, 0, sizeof(a));
+    a.grad = h->d.grad_shard;
+    a.master = h->d.master;
+    a.m = h->d.exp_avg;
+    a.v = h->d.exp_avg_sq;
+    a.param = h->d.param_shard;
+    a.n = h->S;
+    const uintptr_t addr[5] = {(uintptr_t)a.grad, (uintptr_t)a.param, (uintptr_t)a.master,
+                               (uintptr_t)a.m, (uintptr_t)a.v};
+    const int elt[5] = {2, 2, 4, 4, 4};
+    const int align[5] = {8, 8, 16, 16, 16};
+    split(h->S, common_head(addr, elt, align, 5), 4, &a.head, &a.ngroups, &a.vec_ok);
+    a.lds_reserve = h->lds_adam;
+    a.lp = (int32_t)h->d.lp;
+    a.b1 = (float)hp.beta1;
+    a.b2 = (float)hp.beta2;
+    a.omb1 = 1.0f - a.b1;
+    a.omb2 = 1.0f - a.b2;
+    a.bc1 = hp.bias_correction ? (float)(1.0 - pw1) : 1.0f;
+    a.bc2 = hp.bias_correction ? (float)(1.0 - pw2) : 1.0f;
+    a.lr = (float)hp.lr;
+    a.eps = (float)hp.eps;
+    a.wd = (float)hp.weight_decay;
+    a.inv_scale = (float)(1.0 / h->scale);
+    a.wd_kind = a.wd == 0.0f ? zk::kWdNone
+              : (hp.wd_mode == ZERO_WD_L2 ? zk::kWdL2 : zk::kWdDecoupled);
+    a.gate = gate;
+    hipError_t e = zk::launch_adam(a, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+    *pw1_out = pw1;
+    *pw2_out = pw2;
+    *same_betas_out = same_betas;
+    return ZERO_OK;
+}
+
+// Commit the outcome of a step: on success t advances (and the beta^t cache);
+// the loss scale follows the overflow flag; the handle returns to idle.
+static void commit_step(zero_shard_s* h, zero_step_info* info, double pw1, double pw2,
+                        bool same_betas)
+{
+    double scale_next;
+    int64_t good_next;
+    next_scale(h, info->overflow, &scale_next, &good_next);
+    if (!info->overflow) {
+        h->t += 1;
+        if (same_betas) {
+            h->pw1 = pw1;
+            h->pw2 = pw2;
+            h->pw_t = h->t;
+        }
+    }
+    info->step_t = h->t;
+    info->scale_next = scale_next;
+    h->scale = scale_next;
+    h->good_steps = good_next;
+    h->phase = kIdle;
+    h->covered = 0;
+    h->slot_cursor = 0;
+}
+
+extern "C" {
+
+zero_status zero_overflow_check(zero_shard_t h, void* stream, zero_step_info* out)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "overflow_check: not a live handle");
+    if (!out) return fail(ZERO_ERR_INVALID_ARG, "overflow_check: NULL out");
+    if (h->phase == kPending)
+        return fail(ZERO_ERR_STATE, "overflow_check: a gated step is pending; call zero_step_resolve");
+    if (h->phase == kChecked) {
+        *out = h->check;
+        return ZERO_OK;
+    }
+    if (h->phase == kReducing && h->covered != h->S)
+        return fail(ZERO_ERR_STATE, "overflow_check: buckets cover [0, %lld) of [0, %lld)",
+                    (long long)h->covered, (long long)h->S);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    zero_status st = launch_check(h, s, "overflow_check");
+    if (st != ZERO_OK) return st;
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "overflow_check: synchronize");
+    h->check = read_check(h);
     h->phase = kChecked;
-    *out = info;
+    *out = h->check;
     return ZERO_OK;
 }
 
@@ -466,63 +582,59 @@ zero_status zero_adam_step(zero_shard_t h, const zero_adam_hparams* hp_in, void*
     }
     const zero_adam_hparams& hp = hp_in ? *hp_in : h->hp;
     zero_step_info info = h->check;
-    double scale_next;
-    int64_t good_next;
-    next_scale(h, info.overflow, &scale_next, &good_next);
+    double pw1 = 1.0, pw2 = 1.0;
+    bool same = false;
     if (!info.overflow) {
-        const int64_t t = h->t + 1;
-        double pw1, pw2;
-        const bool same_betas = hp.beta1 == h->hp.beta1 && hp.beta2 == h->hp.beta2;
-        if (same_betas && h->pw_t == t - 1) {
-            pw1 = h->pw1 * (double)(float)hp.beta1;
-            pw2 = h->pw2 * (double)(float)hp.beta2;
-        } else {
-            pw1 = beta_pow(hp.beta1, t);
-            pw2 = beta_pow(hp.beta2, t);
-        }
-        zk::AdamLaunch a;
-        std::memset(&a, 0, sizeof(a));
-        a.grad = h->d.grad_shard;
-        a.master = h->d.master;
-        a.m = h->d.exp_avg;
-        a.v = h->d.exp_avg_sq;
-        a.param = h->d.param_shard;
-        a.n = h->S;
-        const uintptr_t addr[5] = {(uintptr_t)a.grad, (uintptr_t)a.param, (uintptr_t)a.master,
-                                   (uintptr_t)a.m, (uintptr_t)a.v};
-        const int elt[5] = {2, 2, 4, 4, 4};
-        const int align[5] = {8, 8, 16, 16, 16};
-        split(h->S, common_head(addr, elt, align, 5), 4, &a.head, &a.ngroups, &a.vec_ok);
-        a.lds_reserve = h->lds_adam;
-        a.lp = (int32_t)h->d.lp;
-        a.b1 = (float)hp.beta1;
-        a.b2 = (float)hp.beta2;
-        a.omb1 = 1.0f - a.b1;
-        a.omb2 = 1.0f - a.b2;
-        a.bc1 = hp.bias_correction ? (float)(1.0 - pw1) : 1.0f;
-        a.bc2 = hp.bias_correction ? (float)(1.0 - pw2) : 1.0f;
-        a.lr = (float)hp.lr;
-        a.eps = (float)hp.eps;
-        a.wd = (float)hp.weight_decay;
-        a.inv_scale = (float)(1.0 / h->scale);
-        a.wd_kind = a.wd == 0.0f ? zk::kWdNone
-                  : (hp.wd_mode == ZERO_WD_L2 ? zk::kWdL2 : zk::kWdDecoupled);
-        hipError_t e = zk::launch_adam(a, static_cast<hipStream_t>(stream));
-        if (e != hipSuccess) return hip_fail(e, "adam_step: launch");
-        h->t = t;
-        if (same_betas) {
-            h->pw1 = pw1;
-            h->pw2 = pw2;
-            h->pw_t = t;
-        }
-        info.step_t = t;
+        zero_status st = launch_adam_step(h, hp, static_cast<hipStream_t>(stream), nullptr, &pw1,
+                                          &pw2, &same, "adam_step: launch");
+        if (st != ZERO_OK) return st;
     }
-    info.scale_next = scale_next;
-    h->scale = scale_next;
-    h->good_steps = good_next;
-    h->phase = kIdle;
-    h->covered = 0;
-    h->slot_cursor = 0;
+    commit_step(h, &info, pw1, pw2, same);
+    if (out) *out = info;
+    return ZERO_OK;
+}
+
+zero_status zero_adam_step_gated(zero_shard_t h, const zero_adam_hparams* hp_in, void* stream)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "adam_step_gated: not a live handle");
+    if (h->phase == kChecked || h->phase == kPending)
+        return fail(ZERO_ERR_STATE, "adam_step_gated: step already checked or pending");
+    if (h->phase == kReducing && h->covered != h->S)
+        return fail(ZERO_ERR_STATE, "adam_step_gated: buckets cover [0, %lld) of [0, %lld)",
+                    (long long)h->covered, (long long)h->S);
+    if (hp_in) {
+        zero_status st = check_hparams(hp_in);
+        if (st != ZERO_OK) return st;
+    }
+    const zero_adam_hparams& hp = hp_in ? *hp_in : h->hp;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Phase before = h->phase;
+    const int64_t cursor_before = h->slot_cursor;
+    zero_status st = launch_check(h, s, "adam_step_gated: check");
+    if (st == ZERO_OK) {
+        hipError_t e = hipEventRecord(h->result_ready, s);
+        if (e != hipSuccess) st = hip_fail(e, "adam_step_gated: event");
+    }
+    if (st == ZERO_OK)
+        st = launch_adam_step(h, hp, s, h->result, &h->pend_pw1, &h->pend_pw2,
+                              &h->pend_same_betas, "adam_step_gated: launch");
+    if (st != ZERO_OK) {
+        h->phase = before;
+        h->slot_cursor = cursor_before;
+        return st;
+    }
+    h->phase = kPending;
+    return ZERO_OK;
+}
+
+zero_status zero_step_resolve(zero_shard_t h, zero_step_info* out)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "step_resolve: not a live handle");
+    if (h->phase != kPending) return fail(ZERO_ERR_STATE, "step_resolve: no gated step pending");
+    hipError_t e = hipEventSynchronize(h->result_ready);
+    if (e != hipSuccess) return hip_fail(e, "step_resolve: event");
+    zero_step_info info = read_check(h);
+    commit_step(h, &info, h->pend_pw1, h->pend_pw2, h->pend_same_betas);
     if (out) *out = info;
     return ZERO_OK;
 }
