@@ -18,6 +18,7 @@ a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -106,6 +107,10 @@ def main() -> int:
                     help="shard elements the CPU oracle runs on (0 = skip)")
     ap.add_argument("--only", choices=["copy"], default=None,
                     help="run only the plain copy kernel (byte-counter calibration)")
+    ap.add_argument("--mode", choices=["pos_g", "pos"], default="pos_g",
+                    help="pos_g: gradient partitioning (bucket reduces + check + Adam); "
+                         "pos: optimizer-state partitioning only (the owner's slice of an "
+                         "already all-reduced gradient: scan check + Adam)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -139,8 +144,13 @@ def main() -> int:
     master, m, v = synth.init_state(w, dev, seed=0)
     grad = torch.zeros(S, dtype=lp_t, device=dev)
     param = master.to(lp_t)
-    bufs = synth.alloc_contribs(w, dev)
-    synth.fill_contribs(w, bufs, 0, w.scale, seed=0)
+    if args.mode == "pos":
+        # the caller's slice of the all-reduced gradient: one seeded draw
+        bufs = []
+        synth.fill_contribs(dataclasses.replace(w, R=1), [grad], 0, w.scale, seed=0)
+    else:
+        bufs = synth.alloc_contribs(w, dev)
+        synth.fill_contribs(w, bufs, 0, w.scale, seed=0)
     torch.cuda.synchronize()
     print("[bench] inputs resident", file=sys.stderr, flush=True)
 
@@ -158,8 +168,9 @@ def main() -> int:
         # the Adam enqueue (more events between kernels cost step time)
         if ev is not None:
             ev["r"][0].record(stream)
-        for off, ln in offs:
-            zs.zero_bucket_reduce(h, [p + 2 * off for p in ptrs], off, ln, stream)
+        if args.mode == "pos_g":
+            for off, ln in offs:
+                zs.zero_bucket_reduce(h, [p + 2 * off for p in ptrs], off, ln, stream)
         if ev is not None:
             ev["r"][1].record(stream)
         if flow == "gated":
@@ -223,7 +234,7 @@ def main() -> int:
     traffic = measured_traffic(S)
 
     cpu = None
-    if args.cpu_sample > 0:
+    if args.cpu_sample > 0 and args.mode == "pos_g":
         n = min(args.cpu_sample, S)
         state_host = tuple(t[:n].cpu().numpy() for t in (master, m, v))
         contribs_host = [b[:n].view(torch.int16).cpu().numpy().view(np.uint16) for b in bufs]
@@ -247,8 +258,11 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded; same contribution batch every step)",
-        "config": {"workload": w.name, "psi": w.psi, "nd": w.nd, "rank": w.rank,
-                   "shard_elems": S, "contributions": R, "bucket_elems": cb,
+        "config": {"workload": w.name + (" -- P_os: scan check + Adam on the owner's slice of an "
+                                          "all-reduced gradient" if args.mode == "pos" else ""),
+                   "mode": args.mode, "psi": w.psi, "nd": w.nd, "rank": w.rank,
+                   "shard_elems": S, "contributions": R if args.mode == "pos_g" else 0,
+                   "bucket_elems": cb,
                    "storage": w.lp, "loss_scale": w.scale, "lr": w.lr,
                    "weight_decay": w.weight_decay},
         "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
@@ -256,7 +270,8 @@ def main() -> int:
         "step_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernels_ms": {"adam_incl_check_fold": adam_avg, "adam_sync_flow": adam_sync,
                        "reduce_all_buckets": red_avg,
-                       "reduce_gbs": reduce_bytes / (red_avg * 1e-3) / 1e9},
+                       "reduce_gbs": (reduce_bytes / (red_avg * 1e-3) / 1e9
+                                      if args.mode == "pos_g" else None)},
         "flow": "device-gated check + Adam (zero_adam_step_gated / zero_step_resolve)",
         "ms_per_step_sync_check_flow": ms_sync,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,

@@ -232,6 +232,21 @@ zero_status zero_adam_step(zero_shard_t h, const zero_adam_hparams* hp, void* st
                            zero_step_info* out);
 
 /*
+ * Install the step's global check result on every rank before zero_adam_step,
+ * for data parallelism across Nd processes: each rank runs
+ * zero_overflow_check on its own partition, the caller all-reduces the
+ * overflow flags (MAX) and the squared norms (SUM, from grad_norm^2) over the
+ * ranks, and passes the outcome here, so that all ranks skip or apply the
+ * step together ("ZeRO：大模型训练的内存优化革命" 3.1.1 and 3.1.2: every process
+ * updates only its partition, so the decision must be shared).  Phase must be
+ * CHECKED.  global_overflow must be 0 or 1 and not below this rank's own flag;
+ * global_grad_norm is reported as the step's norm.  *out (may be NULL) gets
+ * the merged result.  Errors: STATE (dead handle, not checked), INVALID_ARG.
+ */
+zero_status zero_overflow_merge(zero_shard_t h, int32_t global_overflow, double global_grad_norm,
+                                zero_step_info* out);
+
+/*
  * Device-gated check + Adam: the same step as zero_overflow_check followed by
  * zero_adam_step, without the stream stall between them.  After the buckets
  * of a step (or with none, scanning a caller-filled grad_shard), this

@@ -31,7 +31,8 @@ ZERO_MAX_CONTRIB = 64
 
 ABI_SYMBOLS = (
     "zero_state_bytes", "zero_state_bytes_ex", "zero_shard_init", "zero_bucket_reduce",
-    "zero_overflow_check", "zero_adam_step", "zero_adam_step_gated", "zero_step_resolve",
+    "zero_overflow_check", "zero_overflow_merge", "zero_adam_step", "zero_adam_step_gated",
+    "zero_step_resolve",
     "zero_shard_get_counters",
     "zero_shard_set_counters", "zero_shard_destroy", "zero_status_str", "zero_last_error",
     "zero_abi_version",
@@ -100,6 +101,7 @@ def lib() -> ctypes.CDLL:
         L.zero_overflow_check.argtypes = [_vp, _vp, ctypes.POINTER(ZeroStepInfo)]
         L.zero_adam_step.argtypes = [_vp, ctypes.POINTER(ZeroAdamHParams), _vp,
                                      ctypes.POINTER(ZeroStepInfo)]
+        L.zero_overflow_merge.argtypes = [_vp, _i32, _f64, ctypes.POINTER(ZeroStepInfo)]
         L.zero_adam_step_gated.argtypes = [_vp, ctypes.POINTER(ZeroAdamHParams), _vp]
         L.zero_step_resolve.argtypes = [_vp, ctypes.POINTER(ZeroStepInfo)]
         L.zero_shard_get_counters.argtypes = [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_f64),
@@ -114,7 +116,7 @@ def lib() -> ctypes.CDLL:
         L.zero_abi_version.argtypes = []
         for name in ("zero_state_bytes", "zero_state_bytes_ex", "zero_shard_init",
                      "zero_bucket_reduce", "zero_overflow_check", "zero_adam_step",
-                     "zero_adam_step_gated", "zero_step_resolve",
+                     "zero_overflow_merge", "zero_adam_step_gated", "zero_step_resolve",
                      "zero_shard_get_counters", "zero_shard_set_counters", "zero_shard_destroy"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -285,6 +287,13 @@ def zero_adam_step(h: int, hp: Optional[AdamHParams] = None, stream=None) -> Ste
     hpc = ctypes.byref(hp.to_c()) if hp is not None else None
     _check(lib().zero_adam_step(h, hpc, _stream_ptr(stream), ctypes.byref(out)),
            "zero_adam_step")
+    return StepInfo.from_c(out)
+
+
+def zero_overflow_merge(h: int, global_overflow: int, global_grad_norm: float) -> StepInfo:
+    out = ZeroStepInfo()
+    _check(lib().zero_overflow_merge(h, global_overflow, global_grad_norm, ctypes.byref(out)),
+           "zero_overflow_merge")
     return StepInfo.from_c(out)
 
 

@@ -594,6 +594,26 @@ zero_status zero_adam_step(zero_shard_t h, const zero_adam_hparams* hp_in, void*
     return ZERO_OK;
 }
 
+zero_status zero_overflow_merge(zero_shard_t h, int32_t global_overflow, double global_grad_norm,
+                                zero_step_info* out)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "overflow_merge: not a live handle");
+    if (h->phase != kChecked)
+        return fail(ZERO_ERR_STATE, "overflow_merge: zero_overflow_check has not completed this step");
+    if (global_overflow != 0 && global_overflow != 1)
+        return fail(ZERO_ERR_INVALID_ARG, "overflow_merge: global_overflow must be 0 or 1");
+    if (global_overflow < h->check.overflow)
+        return fail(ZERO_ERR_INVALID_ARG,
+                    "overflow_merge: this rank overflowed; the global flag cannot be 0");
+    h->check.overflow = global_overflow;
+    h->check.skipped = global_overflow;
+    h->check.grad_norm = global_grad_norm;
+    int64_t g;
+    next_scale(h, global_overflow, &h->check.scale_next, &g);
+    if (out) *out = h->check;
+    return ZERO_OK;
+}
+
 zero_status zero_adam_step_gated(zero_shard_t h, const zero_adam_hparams* hp_in, void* stream)
 {
     if (!live(h)) return fail(ZERO_ERR_STATE, "adam_step_gated: not a live handle");
