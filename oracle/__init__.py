@@ -33,7 +33,9 @@ from typing import Callable, List, Optional, Sequence
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liboracle.so")
+# ZERO_ORACLE_LIB points the pin tests at a deliberately broken copy of the
+# oracle (tests/test_oracle_mutations.py); normally unset.
+LIB_PATH = os.environ.get("ZERO_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 
 FP16 = 1
 BF16 = 2
