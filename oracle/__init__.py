@@ -39,6 +39,7 @@ LIB_PATH = os.environ.get("ZERO_ORACLE_LIB") or os.path.join(HERE, "liboracle.so
 
 FP16 = 1
 BF16 = 2
+FP32 = 3      # 4-byte storage of grads, contributions and params (b = 4)
 
 _lib = None
 
@@ -46,6 +47,7 @@ _u16p = ctypes.POINTER(ctypes.c_uint16)
 _f32p = ctypes.POINTER(ctypes.c_float)
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
 
 
 class _Bytes(ctypes.Structure):
@@ -86,11 +88,12 @@ def lib():
                                        ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
         L.oracle_take_shard_u16.argtypes = [_u16p, _i64, _i32, _i32, _u16p]
         L.oracle_take_shard_f32.argtypes = [_f32p, _i64, _i32, _i32, _f32p]
-        L.oracle_bucket_reduce.argtypes = [_i32, _i32, ctypes.POINTER(_u16p), _i64, _u16p]
-        L.oracle_flag_sumsq.argtypes = [_i32, _u16p, _i64, ctypes.c_float,
+        L.oracle_bucket_reduce.argtypes = [_i32, _i32, ctypes.POINTER(_vp), _i64, _vp]
+        L.oracle_flag_sumsq.argtypes = [_i32, _vp, _i64, ctypes.c_float,
                                         ctypes.POINTER(_i32), ctypes.POINTER(ctypes.c_double)]
         L.oracle_adam_scalars.argtypes = [ctypes.c_double] * 5 + [_i32, _i64, ctypes.c_double, _f32p]
-        L.oracle_adam_update.argtypes = [_i32, _i64, _u16p, _f32p, _f32p, _f32p, _u16p, _f32p, _i32]
+        L.oracle_adam_update.argtypes = [_i32, _i64, _vp, _f32p, _f32p, _f32p, _vp, _f32p, _i32]
+        L.oracle_sgd_update.argtypes = [_i32, _i64, _vp, _f32p, _f32p, _vp, _f32p]
         L.oracle_loss_scale_next.argtypes = [_i32, _i32, _i32, ctypes.c_double,
                                              ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]
         L.oracle_state_bytes.argtypes = [_i64, _i32, _i32, _i64, _i32, _i32, _i32,
@@ -107,6 +110,18 @@ def _p16(a: np.ndarray):
 def _p32(a: np.ndarray):
     assert a.dtype == np.float32 and a.flags.c_contiguous
     return a.ctypes.data_as(_f32p)
+
+
+def _store_dtype(lp: int):
+    return np.float32 if lp == FP32 else np.uint16
+
+
+def _pg(lp: int, a: Optional[np.ndarray]):
+    """Pointer to gradient-like storage: uint16 bits, or fp32 values for FP32."""
+    if a is None:
+        return None
+    assert a.dtype == _store_dtype(lp) and a.flags.c_contiguous, (a.dtype, lp)
+    return a.ctypes.data_as(_vp)
 
 
 # ---------------------------------------------------------------- 2-byte formats
@@ -150,20 +165,21 @@ def take_shard(flat: np.ndarray, nd: int, rank: int) -> np.ndarray:
 # ---------------------------------------------------------------- reduce (a2)
 
 def bucket_reduce(lp: int, contribs: Sequence[np.ndarray]) -> np.ndarray:
-    """Mean of R 2-byte contributions, fp32 accumulate in ascending order."""
-    cs = [np.ascontiguousarray(c, dtype=np.uint16) for c in contribs]
+    """Mean of R contributions, fp32 accumulate in ascending order."""
+    dt = _store_dtype(lp)
+    cs = [np.ascontiguousarray(c, dtype=dt) for c in contribs]
     n = cs[0].size
     assert all(c.size == n for c in cs)
-    arr = (_u16p * len(cs))(*[_p16(c) for c in cs])
-    out = np.empty(n, np.uint16)
-    lib().oracle_bucket_reduce(lp, len(cs), arr, n, _p16(out))
+    arr = (_vp * len(cs))(*[c.ctypes.data for c in cs])
+    out = np.empty(n, dt)
+    lib().oracle_bucket_reduce(lp, len(cs), arr, n, _pg(lp, out))
     return out
 
 
 def reduce_shard(lp: int, contribs: Sequence[np.ndarray], bucket_elems: int) -> np.ndarray:
     """Reduce a whole shard one C_B bucket at a time, buckets in ascending order."""
     n = contribs[0].size
-    out = np.empty(n, np.uint16)
+    out = np.empty(n, _store_dtype(lp))
     for off in range(0, n, bucket_elems):
         end = min(n, off + bucket_elems)
         out[off:end] = bucket_reduce(lp, [c[off:end] for c in contribs])
@@ -173,11 +189,11 @@ def reduce_shard(lp: int, contribs: Sequence[np.ndarray], bucket_elems: int) -> 
 # ---------------------------------------------------------------- flag / norm (a3)
 
 def flag_sumsq(lp: int, g: np.ndarray, scale: float, flag: int = 0, sumsq: float = 0.0):
-    g = np.ascontiguousarray(g, dtype=np.uint16)
+    g = np.ascontiguousarray(g, dtype=_store_dtype(lp))
     f = _i32(flag)
     s = ctypes.c_double(sumsq)
     inv = float(np.float32(1.0 / scale))
-    lib().oracle_flag_sumsq(lp, _p16(g), g.size, inv, ctypes.byref(f), ctypes.byref(s))
+    lib().oracle_flag_sumsq(lp, _pg(lp, g), g.size, inv, ctypes.byref(f), ctypes.byref(s))
     return f.value, s.value
 
 
@@ -211,15 +227,42 @@ def adam_scalars(hp: AdamHP, t: int, scale: float) -> np.ndarray:
 
 
 def adam_update(lp: int, grad: np.ndarray, master: np.ndarray, m: np.ndarray,
-                v: np.ndarray, param: np.ndarray, sc: np.ndarray, wd_mode: int = 0) -> None:
-    """In place: master, m, v (fp32) and param (2-byte bits)."""
+                v: np.ndarray, param: Optional[np.ndarray], sc: np.ndarray,
+                wd_mode: int = 0) -> None:
+    """In place: master, m, v (fp32) and param (2-byte bits; None with FP32
+    storage, where master is the parameter)."""
     n = master.size
-    for a in (grad, param):
-        assert a.size == n and a.dtype == np.uint16
+    assert grad.size == n and (param is None or param.size == n)
     for a in (master, m, v):
         assert a.size == n and a.dtype == np.float32
-    lib().oracle_adam_update(lp, n, _p16(grad), _p32(master), _p32(m), _p32(v),
-                             _p16(param), _p32(np.ascontiguousarray(sc, np.float32)), wd_mode)
+    lib().oracle_adam_update(lp, n, _pg(lp, grad), _p32(master), _p32(m), _p32(v),
+                             _pg(lp, param), _p32(np.ascontiguousarray(sc, np.float32)), wd_mode)
+
+
+@dataclass
+class SGDHP:
+    """Heavy-ball SGD with L2 weight decay; momentum 0 with no buffer = plain SGD."""
+    lr: float = 1e-2
+    momentum: float = 0.9
+    weight_decay: float = 0.0
+    initial_step: int = 0
+
+
+def sgd_scalars(hp: SGDHP, scale: float) -> np.ndarray:
+    return np.array([hp.lr, hp.momentum, hp.weight_decay, 1.0 / scale], dtype=np.float64) \
+        .astype(np.float32)
+
+
+def sgd_update(lp: int, grad: np.ndarray, master: np.ndarray, momentum: Optional[np.ndarray],
+               param: Optional[np.ndarray], sc: np.ndarray) -> None:
+    """In place: master (and the momentum buffer, and 2-byte param bits)."""
+    n = master.size
+    assert grad.size == n and master.dtype == np.float32
+    if momentum is not None:
+        assert momentum.size == n and momentum.dtype == np.float32
+    lib().oracle_sgd_update(lp, n, _pg(lp, grad), _p32(master),
+                            None if momentum is None else _p32(momentum), _pg(lp, param),
+                            _p32(np.ascontiguousarray(sc, np.float32)))
 
 
 def loss_scale_next(overflow: int, ls: LossScale, scale: float, good_steps: int):
@@ -244,39 +287,43 @@ class StepInfo:
 
 @dataclass
 class ShardState:
-    """The owner's shard: fp32 master / m / v and 2-byte grad / param bits."""
+    """The owner's shard: fp32 master / m / v and the gradient / param storage
+    (2-byte bits, or fp32 values with FP32 storage, where param is None and
+    master is the parameter).  For SGD, m is the momentum buffer (None for
+    plain SGD) and v is None."""
     lp: int
     master: np.ndarray
-    m: np.ndarray
-    v: np.ndarray
+    m: Optional[np.ndarray]
+    v: Optional[np.ndarray]
     grad: np.ndarray
-    param: np.ndarray
+    param: Optional[np.ndarray]
     t: int = 0
     scale: float = 1.0
     good_steps: int = 0
 
     def copy(self) -> "ShardState":
-        return ShardState(self.lp, self.master.copy(), self.m.copy(), self.v.copy(),
-                          self.grad.copy(), self.param.copy(), self.t, self.scale,
-                          self.good_steps)
+        c = lambda a: None if a is None else a.copy()
+        return ShardState(self.lp, self.master.copy(), c(self.m), c(self.v), self.grad.copy(),
+                          c(self.param), self.t, self.scale, self.good_steps)
 
 
-def new_state(lp: int, master: np.ndarray, m: np.ndarray, v: np.ndarray,
-              hp: AdamHP, ls: LossScale) -> ShardState:
+def new_state(lp: int, master: np.ndarray, m, v, hp, ls: LossScale) -> ShardState:
     n = master.size
-    st = ShardState(lp, np.array(master, np.float32), np.array(m, np.float32),
-                    np.array(v, np.float32), np.zeros(n, np.uint16), np.zeros(n, np.uint16),
+    st = ShardState(lp, np.array(master, np.float32),
+                    None if m is None else np.array(m, np.float32),
+                    None if v is None else np.array(v, np.float32),
+                    np.zeros(n, _store_dtype(lp)), None,
                     t=hp.initial_step, scale=float(ls.init_scale), good_steps=0)
-    st.param = f32_to_lp(lp, st.master)
+    if lp != FP32:
+        st.param = f32_to_lp(lp, st.master)
     return st
 
 
 def step(st: ShardState, contribs: Sequence[np.ndarray], bucket_elems: int,
-         hp: AdamHP, ls: LossScale, forced_flag: Optional[int] = None) -> StepInfo:
-    """One owner-rank step on the whole shard held in memory.
-
-    forced_flag lets a caller that evaluates a sample of a larger shard supply
-    the overflow decision taken over the full shard (chunked evaluation)."""
+         hp, ls: LossScale, forced_flag: Optional[int] = None) -> StepInfo:
+    """One owner-rank step on the whole shard held in memory; hp is an AdamHP
+    or an SGDHP.  forced_flag lets a caller that evaluates a sample of a larger
+    shard supply the overflow decision taken over the full shard."""
     st.grad = reduce_shard(st.lp, contribs, bucket_elems)
     flag, sumsq = flag_sumsq(st.lp, st.grad, st.scale)
     if forced_flag is not None:
@@ -287,8 +334,11 @@ def step(st: ShardState, contribs: Sequence[np.ndarray], bucket_elems: int,
     else:
         skipped = 0
         st.t += 1
-        sc = adam_scalars(hp, st.t, st.scale)
-        adam_update(st.lp, st.grad, st.master, st.m, st.v, st.param, sc, hp.wd_mode)
+        if isinstance(hp, SGDHP):
+            sgd_update(st.lp, st.grad, st.master, st.m, st.param, sgd_scalars(hp, st.scale))
+        else:
+            sc = adam_scalars(hp, st.t, st.scale)
+            adam_update(st.lp, st.grad, st.master, st.m, st.v, st.param, sc, hp.wd_mode)
     st.scale, st.good_steps = loss_scale_next(flag, ls, st.scale, st.good_steps)
     return StepInfo(flag, skipped, st.t, float(np.sqrt(sumsq)), scale_used, st.scale)
 

@@ -49,6 +49,7 @@
 
 #define ORACLE_FP16 1
 #define ORACLE_BF16 2
+#define ORACLE_FP32 3   /* 4-byte storage of grads and params (the pages' b = 4) */
 
 /* ------------------------------------------------------------------------ */
 /* 2-byte formats.  IEEE binary16 and bfloat16, round to nearest, ties to    */
@@ -134,6 +135,22 @@ static uint16_t f32_to_lp(int lp, float x)
     return lp == ORACLE_BF16 ? oracle_f32_to_bf16(x) : oracle_f32_to_f16(x);
 }
 
+/* Gradients, contributions and 2-byte params live as uint16 bit patterns;
+ * with 4-byte storage they are plain fp32 values. */
+static float load_g(int lp, const void* a, int64_t i)
+{
+    if (lp == ORACLE_FP32) return ((const float*)a)[i];
+    return lp_to_f32(lp, ((const uint16_t*)a)[i]);
+}
+
+static void store_g(int lp, void* a, int64_t i, float x)
+{
+    if (lp == ORACLE_FP32)
+        ((float*)a)[i] = x;
+    else
+        ((uint16_t*)a)[i] = f32_to_lp(lp, x);
+}
+
 void oracle_lp_to_f32_array(int lp, const uint16_t* in, int64_t n, float* out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = lp_to_f32(lp, in[i]);
@@ -190,15 +207,15 @@ void oracle_take_shard_f32(const float* flat, int64_t psi, int32_t nd,
 /* g = rne_lp(acc * (1/R)).                                                   */
 /* ------------------------------------------------------------------------ */
 
-void oracle_bucket_reduce(int lp, int32_t n_contrib, const uint16_t* const* contribs,
-                          int64_t n, uint16_t* out)
+void oracle_bucket_reduce(int lp, int32_t n_contrib, const void* const* contribs,
+                          int64_t n, void* out)
 {
     float inv_r = (float)(1.0 / (double)n_contrib);
     for (int64_t i = 0; i < n; ++i) {
         float acc = 0.0f;
         for (int32_t r = 0; r < n_contrib; ++r)
-            acc = acc + lp_to_f32(lp, contribs[r][i]);
-        out[i] = f32_to_lp(lp, acc * inv_r);
+            acc = acc + load_g(lp, contribs[r], i);
+        store_g(lp, out, i, acc * inv_r);
     }
 }
 
@@ -209,13 +226,13 @@ void oracle_bucket_reduce(int lp, int32_t n_contrib, const uint16_t* const* cont
 /* unscaled fp32 gradients in fp64.  Accumulates into *flag and *sumsq.       */
 /* ------------------------------------------------------------------------ */
 
-void oracle_flag_sumsq(int lp, const uint16_t* g, int64_t n, float inv_scale,
+void oracle_flag_sumsq(int lp, const void* g, int64_t n, float inv_scale,
                        int32_t* flag, double* sumsq)
 {
     int32_t f = *flag;
     double s = *sumsq;
     for (int64_t i = 0; i < n; ++i) {
-        float x = lp_to_f32(lp, g[i]);
+        float x = load_g(lp, g, i);
         if (!isfinite(x)) f = 1;
         float u = x * inv_scale;
         s += (double)u * (double)u;
@@ -268,8 +285,8 @@ void oracle_adam_scalars(double beta1, double beta2, double lr, double eps,
 /* wd_mode: 0 decoupled, 1 L2.  A zero weight decay adds no term.             */
 /* ------------------------------------------------------------------------ */
 
-void oracle_adam_update(int lp, int64_t n, const uint16_t* grad, float* master,
-                        float* exp_avg, float* exp_avg_sq, uint16_t* param,
+void oracle_adam_update(int lp, int64_t n, const void* grad, float* master,
+                        float* exp_avg, float* exp_avg_sq, void* param,
                         const float* sc, int32_t wd_mode)
 {
     float b1 = sc[0], b2 = sc[1], omb1 = sc[2], omb2 = sc[3];
@@ -277,7 +294,7 @@ void oracle_adam_update(int lp, int64_t n, const uint16_t* grad, float* master,
     float inv_scale = sc[9];
     for (int64_t i = 0; i < n; ++i) {
         float p = master[i];
-        float g = lp_to_f32(lp, grad[i]) * inv_scale;
+        float g = load_g(lp, grad, i) * inv_scale;
         if (wd_mode == 1 && wd != 0.0f)
             g = g + wd * p;
         float m = b1 * exp_avg[i] + omb1 * g;
@@ -291,7 +308,40 @@ void oracle_adam_update(int lp, int64_t n, const uint16_t* grad, float* master,
         master[i] = p;
         exp_avg[i] = m;
         exp_avg_sq[i] = v;
-        param[i] = f32_to_lp(lp, p);
+        if (param) store_g(lp, param, i, p);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* SGD on the owner's shard (the optimizers of the blog.vllbc.top page's      */
+/* extension group C: SGD with momentum, K = 4 bytes of state, and plain SGD, */
+/* K = 0).  The pages give no formula; textbook heavy-ball SGD, with the      */
+/* classic L2 weight decay folded into the gradient:                          */
+/*   g = f32(grad) * (1/scale)            [wd != 0: g = g + wd * p]           */
+/*   with momentum:  buf = mu*buf + g ;  d = buf                              */
+/*   plain SGD:      d = g                                                    */
+/*   p = p - lr*d ;  2-byte storage: param = rne_lp(p)                        */
+/* sc: [0] lr [1] mu [2] wd [3] 1/scale.  momentum == NULL: plain SGD.        */
+/* ------------------------------------------------------------------------ */
+
+void oracle_sgd_update(int lp, int64_t n, const void* grad, float* master, float* momentum,
+                       void* param, const float* sc)
+{
+    float lr = sc[0], mu = sc[1], wd = sc[2], inv_scale = sc[3];
+    for (int64_t i = 0; i < n; ++i) {
+        float p = master[i];
+        float g = load_g(lp, grad, i) * inv_scale;
+        if (wd != 0.0f)
+            g = g + wd * p;
+        float d = g;
+        if (momentum) {
+            float b = mu * momentum[i] + g;
+            momentum[i] = b;
+            d = b;
+        }
+        p = p - lr * d;
+        master[i] = p;
+        if (param) store_g(lp, param, i, p);
     }
 }
 

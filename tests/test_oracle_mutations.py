@@ -12,7 +12,8 @@ import pytest
 from conftest import ROOT
 
 SRC = os.path.join(ROOT, "oracle", "zero_oracle.c")
-PINS = ["tests/test_oracle_ledger.py", "tests/test_oracle_formats.py", "tests/test_oracle_step.py"]
+PINS = ["tests/test_oracle_ledger.py", "tests/test_oracle_formats.py", "tests/test_oracle_step.py",
+        "tests/test_oracle_sgd.py"]
 
 # (name, exact text in zero_oracle.c, replacement); each text occurs once
 MUTATIONS = [
@@ -39,9 +40,11 @@ MUTATIONS = [
     ("bias corrections swapped", "float m_hat = m / bc1;", "float m_hat = m / bc2;"),
     ("update sign", "p = p - lr * u;", "p = p + lr * u;"),
     ("decoupled decay sign", "u = u + wd * p;", "u = u - wd * p;"),
-    ("L2 decay sign", "g = g + wd * p;", "g = g - wd * p;"),
-    ("Adam ignores the loss scale", "float g = lp_to_f32(lp, grad[i]) * inv_scale;",
-     "float g = lp_to_f32(lp, grad[i]);"),
+    ("Adam L2 decay sign", "if (wd_mode == 1 && wd != 0.0f)\n            g = g + wd * p;",
+     "if (wd_mode == 1 && wd != 0.0f)\n            g = g - wd * p;"),
+    ("Adam ignores the loss scale",
+     "float g = load_g(lp, grad, i) * inv_scale;\n        if (wd_mode == 1",
+     "float g = load_g(lp, grad, i);\n        if (wd_mode == 1"),
     ("bias correction of step t-1", "for (int64_t k = 0; k < t; ++k) {",
      "for (int64_t k = 1; k < t; ++k) {"),
     ("1-beta1 from beta2", "out[2] = 1.0f - b1;", "out[2] = 1.0f - b2;"),
@@ -58,7 +61,20 @@ MUTATIONS = [
      "out->comm_bytes_stage[3] = 2.0 * P * b;"),
     ("bf16 decoded as fp16", "return lp == ORACLE_BF16 ? oracle_bf16_to_f32(v) : oracle_f16_to_f32(v);",
      "return lp == ORACLE_BF16 ? oracle_f16_to_f32(v) : oracle_f16_to_f32(v);"),
-    ("param cast from the momentum", "param[i] = f32_to_lp(lp, p);", "param[i] = f32_to_lp(lp, m);"),
+    ("param cast from the momentum", "exp_avg_sq[i] = v;\n        if (param) store_g(lp, param, i, p);",
+     "exp_avg_sq[i] = v;\n        if (param) store_g(lp, param, i, m);"),
+    ("SGD momentum ignores mu", "float b = mu * momentum[i] + g;", "float b = momentum[i] + g;"),
+    ("SGD steps along g, not the buffer", "d = b;", "d = g;"),
+    ("SGD decay sign", "if (wd != 0.0f)\n            g = g + wd * p;",
+     "if (wd != 0.0f)\n            g = g - wd * p;"),
+    ("SGD step sign", "p = p - lr * d;", "p = p + lr * d;"),
+    ("SGD ignores the loss scale",
+     "float g = load_g(lp, grad, i) * inv_scale;\n        if (wd != 0.0f)",
+     "float g = load_g(lp, grad, i);\n        if (wd != 0.0f)"),
+    ("fp32 storage read as 2-byte", "if (lp == ORACLE_FP32) return ((const float*)a)[i];",
+     "if (lp == 99) return ((const float*)a)[i];"),
+    ("fp32 storage written rounded to fp16", "    if (lp == ORACLE_FP32)\n        ((float*)a)[i] = x;",
+     "    if (lp == ORACLE_FP32)\n        ((float*)a)[i] = oracle_f16_to_f32(oracle_f32_to_f16(x));"),
 ]
 
 
