@@ -56,8 +56,12 @@ typedef enum {
     ZERO_ERR_UNSUPPORTED = 5  /* valid request this build does not implement  */
 } zero_status;
 
-/* 2-byte storage format of grads and params (IEEE binary16 or bfloat16). */
-typedef enum { ZERO_FP16 = 1, ZERO_BF16 = 2 } zero_lp_dtype;
+/* Storage format of grads, contributions and params: the 2-byte formats of
+ * mixed precision (IEEE binary16 or bfloat16; an fp32 master copy is updated
+ * and cast back), or ZERO_FP32, 4-byte storage (the pages' b = 4 case of the
+ * (2b+K) Psi ledger): fp32 grads and contributions, and `master` is the fp32
+ * parameter itself (param_shard must then be NULL). */
+typedef enum { ZERO_FP16 = 1, ZERO_BF16 = 2, ZERO_FP32 = 3 } zero_lp_dtype;
 
 /* Weight decay: decoupled (AdamW form, u += wd * p before p -= lr * u) or L2
  * (g += wd * p before the moments). */
@@ -68,12 +72,14 @@ typedef struct zero_shard_s* zero_shard_t; /* opaque */
 /*
  * The owner's shard.  Rank `rank` of `nd` owns elements [rank*S, (rank+1)*S) of
  * the flat Psi-element parameter space, S = ceil(psi / nd) (the last shard is
- * zero-padded).  All five arrays hold S elements, are caller-owned device
- * memory, must not overlap, and must outlive the handle:
- *   master, exp_avg, exp_avg_sq : fp32 master weights, first and second moments
- *   grad_shard                  : 2-byte reduced gradient (written by the reduce)
- *   param_shard                 : 2-byte params: the owner's slice of the
- *                                 parameter all-gather buffer (written by Adam)
+ * zero-padded).  All arrays hold S elements, are caller-owned device memory,
+ * must not overlap, and must outlive the handle:
+ *   master      : fp32 master weights (with ZERO_FP32 storage: the parameters)
+ *   exp_avg     : Adam first moment; SGD momentum buffer (NULL: plain SGD)
+ *   exp_avg_sq  : Adam second moment (NULL for SGD)
+ *   grad_shard  : reduced gradient in the storage format (written by the reduce)
+ *   param_shard : 2-byte params: the owner's slice of the parameter all-gather
+ *                 buffer (written by the update); NULL with ZERO_FP32 storage
  * bucket_elems is C_B: every bucket but the last of a step holds exactly C_B
  * elements.
  */
@@ -99,6 +105,22 @@ typedef struct {
     zero_wd_mode wd_mode;
     int64_t initial_step;
 } zero_adam_hparams;
+
+/* SGD, the K = 4 (with momentum) and K = 0 (plain) optimizers of the
+ * blog.vllbc.top page's (2b+K) Psi extension; the pages give no formula.
+ * Textbook heavy-ball SGD with L2 weight decay, per element (fp32, each
+ * operation rounded to nearest even, no fused multiply-add):
+ *     g = f32(grad) * fp32(1/scale)      [wd != 0: g = g + wd*p]
+ *     with a momentum buffer: buf = mu*buf + g ; p = p - lr*buf
+ *     plain:                  p = p - lr*g
+ *     2-byte storage:         param = rne_2byte(p)
+ * lr, mu, wd are the fp32 roundings of the values.  Ranges: lr >= 0,
+ * 0 <= momentum < 1 (0 without a buffer), weight_decay >= 0,
+ * initial_step >= 0. */
+typedef struct {
+    double lr, momentum, weight_decay;
+    int64_t initial_step;
+} zero_sgd_hparams;
 
 /* Loss scaling (not on the pages).  dynamic = 1: an overflowing step halves
  * the scale (not below min_scale); growth_interval clean steps in a row double
@@ -136,8 +158,8 @@ typedef struct {
 typedef struct {
     int64_t shard_elems;
     int64_t bytes_master, bytes_m, bytes_v, bytes_grad, bytes_param;
-    int64_t bytes_shard_total; /* = 16 * S for 2-byte grads and params */
-    int64_t bytes_staging;     /* = n_contrib * C_B * 2: one bucket of contributions */
+    int64_t bytes_shard_total; /* = 16 * S for an Adam shard of either storage */
+    int64_t bytes_staging;     /* = n_contrib * C_B * (2 or 4): one bucket of contributions */
     double per_rank_stage[4];
     double comm_bytes_stage[4];
     double comm_bytes_stage1_with_gather;
@@ -147,7 +169,9 @@ typedef struct {
 /*
  * Ledger for mixed-precision Adam (b = 2, K = 12).  Pure host arithmetic, no
  * device access.  psi >= 1, nd >= 1, n_contrib in [1, ZERO_MAX_CONTRIB],
- * bucket_elems >= 1, lp a zero_lp_dtype, out non-NULL.
+ * bucket_elems >= 1, lp a zero_lp_dtype, out non-NULL.  The allocation fields
+ * describe an Adam shard of storage format lp (with ZERO_FP32: 4-byte grads,
+ * no param_shard).
  */
 zero_status zero_state_bytes(int64_t psi, int32_t nd, int32_t n_contrib,
                              int64_t bucket_elems, zero_lp_dtype lp,
@@ -179,12 +203,25 @@ zero_status zero_shard_init(const zero_shard_desc* desc, const zero_adam_hparams
                             const zero_loss_scale_cfg* ls, zero_shard_t* out);
 
 /*
+ * Create a handle whose update rule is SGD (zero_sgd_step /
+ * zero_sgd_step_gated) instead of Adam.  desc as for zero_shard_init, with
+ * exp_avg the momentum buffer (NULL for plain SGD, which then needs
+ * momentum == 0) and exp_avg_sq NULL.  The bucket reduce, the check, the merge
+ * and zero_step_resolve are shared with Adam handles; the Adam step calls
+ * refuse an SGD handle and the SGD step calls an Adam handle (ZERO_ERR_STATE).
+ * Errors as zero_shard_init.
+ */
+zero_status zero_shard_init_sgd(const zero_shard_desc* desc, const zero_sgd_hparams* hp,
+                                const zero_loss_scale_cfg* ls, zero_shard_t* out);
+
+/*
  * Reduce one C_B bucket of the owner's shard from n_contrib contributions
  * ("ZeRO：大模型训练的内存优化革命" 3.1.2: gradients reduced on the owner).
  * contribs: host array of n_contrib device pointers, each to bucket_len
- * 2-byte gradients (contribution r, elements [bucket_off, bucket_off+len) of
- * the shard).  Per element: fp32 sum over r = 0..R-1 in that order starting
- * from +0, times fp32(1/R), rounded to the 2-byte format into
+ * gradients in the storage format (contribution r, elements
+ * [bucket_off, bucket_off+len) of the shard).  Per element: fp32 sum over
+ * r = 0..R-1 in that order starting from +0, times fp32(1/R), stored in the
+ * storage format (rounded to nearest even for the 2-byte formats) into
  * grad_shard[bucket_off + i].  The same pass records the overflow flag and the
  * squared norm of the unscaled values for zero_overflow_check.
  * Asynchronous on `stream`; contribution memory must stay valid until the
@@ -192,15 +229,15 @@ zero_status zero_shard_init(const zero_shard_desc* desc, const zero_adam_hparams
  * contiguous order starting at 0; bucket_len must equal bucket_elems except
  * for the last bucket, which ends at S.
  * Errors: INVALID_ARG (NULL, n_contrib outside [1, 64], bucket outside [0, S),
- * bucket_len < 1 or > bucket_elems, misaligned pointer), STATE (dead handle,
- * bucket not the next one, step already checked), HIP.
+ * bucket_len < 1 or > bucket_elems, pointer not aligned to its element size),
+ * STATE (dead handle, bucket not the next one, step already checked), HIP.
  */
 zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int32_t n_contrib,
                                int64_t bucket_off, int64_t bucket_len, void* stream);
 
 /*
  * Finish the overflow check of the step: OR of "not finite" over the stored
- * 2-byte gradient shard and its unscaled squared norm, summed over per-block
+ * gradient shard and its unscaled squared norm, summed over per-block
  * partials in a fixed order (bitwise reproducible).  If no bucket was reduced
  * this step, the stored grad_shard is scanned instead (for callers that fill
  * it themselves).  Synchronises `stream` and fills *out (skipped = overflow;
@@ -230,6 +267,23 @@ zero_status zero_overflow_check(zero_shard_t h, void* stream, zero_step_info* ou
  */
 zero_status zero_adam_step(zero_shard_t h, const zero_adam_hparams* hp, void* stream,
                            zero_step_info* out);
+
+/*
+ * The SGD update of a checked step, as zero_adam_step is for Adam: skipped on
+ * overflow, else t += 1 and the update of zero_sgd_hparams.  hp = NULL uses the
+ * values given at init; otherwise *hp is used for this step only.
+ * Errors: STATE (dead handle, not an SGD handle, no completed check this step),
+ * INVALID_ARG (hp out of range), HIP.
+ */
+zero_status zero_sgd_step(zero_shard_t h, const zero_sgd_hparams* hp, void* stream,
+                          zero_step_info* out);
+
+/*
+ * Device-gated check + SGD update, as zero_adam_step_gated is for Adam; finish
+ * with zero_step_resolve.  Errors: STATE (also: not an SGD handle), INVALID_ARG,
+ * HIP.
+ */
+zero_status zero_sgd_step_gated(zero_shard_t h, const zero_sgd_hparams* hp, void* stream);
 
 /*
  * Install the step's global check result on every rank before zero_adam_step,

@@ -404,7 +404,9 @@ void oracle_state_bytes(int64_t psi, int32_t nd, int32_t n_contrib, int64_t buck
     out->bytes_m = 4 * s;
     out->bytes_v = 4 * s;
     out->bytes_grad = (int64_t)lp_bytes * s;
-    out->bytes_param = (int64_t)lp_bytes * s;
+    /* with 4-byte storage the fp32 master is the parameter (the page's K = 8
+       fp32 Adam counts only m and v as optimizer state) */
+    out->bytes_param = lp_bytes == 4 ? 0 : (int64_t)lp_bytes * s;
     out->bytes_shard_total = out->bytes_master + out->bytes_m + out->bytes_v
                            + out->bytes_grad + out->bytes_param;
     out->bytes_staging = (int64_t)n_contrib * bucket_elems * lp_bytes;

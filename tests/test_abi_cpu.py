@@ -41,6 +41,7 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(zs.ZeroAdamHParams) == 56
     assert ctypes.sizeof(zs.ZeroLossScaleCfg) == 24
     assert ctypes.sizeof(zs.ZeroStepInfo) == 40
+    assert ctypes.sizeof(zs.ZeroSgdHParams) == 32
     assert ctypes.sizeof(zs.ZeroStateBytes) == 8 * 8 + 8 * 4 * 2 + 8 + 8 * 4 * 3
 
 
@@ -78,7 +79,7 @@ def test_state_bytes_rejects(args):
         zs.zero_state_bytes(*args, zs.ZERO_FP16)
     assert e.value.status == zs.ZERO_ERR_INVALID_ARG
     with pytest.raises(zs.ZeroError):
-        zs.zero_state_bytes(10, 4, 1, 1, 3)
+        zs.zero_state_bytes(10, 4, 1, 1, 7)
     with pytest.raises(zs.ZeroError):
         zs.zero_state_bytes_ex(10, 4, 1, 1, zs.ZERO_FP16, 3, 12)
 
@@ -169,3 +170,67 @@ def test_init_rejects_too_many_buckets_before_device_work():
     assert s == zs.ZERO_ERR_UNSUPPORTED
     assert "bucket" in zs.zero_last_error()
     assert h.value is None
+
+
+@pytest.mark.parametrize("psi,nd,R,cb", CASES[:4])
+def test_state_bytes_fp32_storage_equals_oracle(oracle, psi, nd, R, cb):
+    a = zs.zero_state_bytes(psi, nd, R, cb, zs.ZERO_FP32)
+    b = oracle.state_bytes(psi, nd, R, cb, lp_bytes=4)
+    assert a == b
+    assert a["bytes_param"] == 0 and a["bytes_grad"] == 4 * a["shard_elems"]
+    assert a["bytes_shard_total"] == 16 * a["shard_elems"]
+
+
+def _desc32(**over):
+    d = dict(lp=zs.ZERO_FP32, param_shard=0)
+    d.update(over)
+    return _desc(**d)
+
+
+GOOD_SGD = zs.ZeroSgdHParams(1e-2, 0.9, 0.0, 0)
+
+
+@pytest.mark.parametrize("over", [
+    dict(param_shard=0x80000),          # fp32 storage takes no 2-byte param
+    dict(grad_shard=0x60002),           # fp32 grads must be 4-byte aligned
+    dict(exp_avg_sq=0), dict(master=0),
+])
+def test_init_fp32_storage_rejects(over):
+    h = ctypes.c_void_p()
+    s = zs.lib().zero_shard_init(ctypes.byref(_desc32(**over)), ctypes.byref(GOOD_HP),
+                                 ctypes.byref(GOOD_LS), ctypes.byref(h))
+    assert s == zs.ZERO_ERR_INVALID_ARG, zs.zero_last_error()
+    assert h.value is None
+
+
+@pytest.mark.parametrize("desc_over,hp", [
+    (dict(exp_avg=0), zs.ZeroSgdHParams(1e-2, 0.9, 0.0, 0)),    # momentum without a buffer
+    (dict(), zs.ZeroSgdHParams(1e-2, 1.0, 0.0, 0)),            # momentum outside [0, 1)
+    (dict(), zs.ZeroSgdHParams(-1.0, 0.9, 0.0, 0)),
+    (dict(), zs.ZeroSgdHParams(float("nan"), 0.9, 0.0, 0)),
+    (dict(), zs.ZeroSgdHParams(1e-2, 0.9, -1.0, 0)),
+    (dict(), zs.ZeroSgdHParams(1e-2, 0.9, 0.0, -3)),
+    (dict(exp_avg_sq=0x40000), GOOD_SGD),                       # SGD takes no second moment
+    (dict(grad_shard=0x20001), GOOD_SGD),
+])
+def test_init_sgd_rejects(desc_over, hp):
+    d = dict(exp_avg_sq=0)
+    d.update(desc_over)
+    h = ctypes.c_void_p()
+    s = zs.lib().zero_shard_init_sgd(ctypes.byref(_desc(**d)), ctypes.byref(hp),
+                                     ctypes.byref(GOOD_LS), ctypes.byref(h))
+    assert s == zs.ZERO_ERR_INVALID_ARG, zs.zero_last_error()
+    assert h.value is None
+
+
+def test_sgd_entry_points_reject_dead_handles():
+    L = zs.lib()
+    bogus = ctypes.c_void_p(0xDEAD0)
+    info = zs.ZeroStepInfo()
+    assert L.zero_sgd_step(bogus, None, None, ctypes.byref(info)) == zs.ZERO_ERR_STATE
+    assert L.zero_sgd_step_gated(bogus, None, None) == zs.ZERO_ERR_STATE
+    h = ctypes.c_void_p()
+    assert L.zero_shard_init_sgd(None, ctypes.byref(GOOD_SGD), ctypes.byref(GOOD_LS),
+                                 ctypes.byref(h)) == zs.ZERO_ERR_INVALID_ARG
+    assert L.zero_shard_init_sgd(ctypes.byref(_desc(exp_avg_sq=0)), None, ctypes.byref(GOOD_LS),
+                                 ctypes.byref(h)) == zs.ZERO_ERR_INVALID_ARG

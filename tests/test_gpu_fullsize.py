@@ -6,13 +6,13 @@ Per step:
     event, 65,536 random positions) of the stored gradient against the oracle
     run on the same sampled contributions;
   - the whole stored gradient bitwise against an independent torch fp32
-    reduce (sum in ascending r from +0, times 1/R, rounded to the 2-byte
+    reduce (sum in ascending r from +0, times 1/R, rounded to the storage
     format), a property that holds at any size;
   - the norm against a torch fp64 sum of the unscaled squares of the stored
     gradient;
   - flags, skips, t and scale exactly against the oracle.
-After the last step: master, m, v and the 2-byte params at the sampled
-positions against the oracle.
+After the last step: master, m, v (SGD: the momentum buffer) and the 2-byte
+params at the sampled positions against the oracle.
 """
 import numpy as np
 import pytest
@@ -21,7 +21,7 @@ import torch
 import oracle
 import zero_dp_sharded_amd as zs
 from gpu_common import (LP_CODE, f32, hp_of, log, lp_is_nan, ls_of, max_rel, oracle_hp, oracle_ls,
-                        u16, ulp_dist)
+                        stored, u16, ulp_dist)
 from zero_dp_sharded_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -52,7 +52,8 @@ def torch_reduce_equal(bufs, grad, R, lp_t):
             acc.add_(b[off:end].float())
         ref = (acc * inv_r).to(lp_t)
         got = grad[off:end]
-        same = (ref.view(torch.int16) == got.view(torch.int16)) | (torch.isnan(ref) & torch.isnan(got))
+        bits = torch.int32 if lp_t == torch.float32 else torch.int16
+        same = (ref.view(bits) == got.view(bits)) | (torch.isnan(ref) & torch.isnan(got))
         if not bool(same.all()):
             bad = torch.nonzero(~same)[:4].flatten().tolist()
             return False, off + bad[0] if bad else -1
@@ -67,7 +68,12 @@ def torch_sumsq(grad, inv_scale):
     return float(s)
 
 
-@pytest.mark.parametrize("name", ["tiny", "gpt2_1.5b", "7.5b_bf16", "13b_inf", "128b"])
+def _bits(x: np.ndarray) -> np.ndarray:
+    return x.view(np.uint32) if x.dtype == np.float32 else x
+
+
+@pytest.mark.parametrize("name", ["tiny", "gpt2_1.5b", "7.5b_bf16", "13b_inf", "128b",
+                                  "c1_7.5b_sgdm", "c2_1.5b_sgd"])
 def test_full_size_sampled(name):
     w = synth.WORKLOADS[name]
     S, R, cb, lp_t = w.shard, w.R, w.bucket_elems, w.torch_lp
@@ -78,34 +84,45 @@ def test_full_size_sampled(name):
     idx_t = torch.from_numpy(idx).to(dev)
 
     master, m, v = synth.init_state(w, dev, seed=0)
+    m = m if w.has_m else None
+    v = v if w.has_v else None
     grad = torch.zeros(S, dtype=lp_t, device=dev)
-    param = master.to(lp_t)
+    param = None if lp_t == torch.float32 else master.to(lp_t)
     bufs = synth.alloc_contribs(w, dev)
     hp, ls = hp_of(w), ls_of(w)
     ohp, ols = oracle_hp(hp), oracle_ls(ls)
-    ost = oracle.new_state(lp, f32(master[idx_t]), f32(m[idx_t]), f32(v[idx_t]), ohp, ols)
-    assert np.array_equal(u16(param[idx_t]), ost.param)
-    h = zs.zero_shard_init(master, m, v, grad, param, psi=w.psi, nd=w.nd, rank=w.rank,
-                           bucket_elems=cb, hp=hp, ls=ls)
+    sample = lambda t: None if t is None else f32(t[idx_t])
+    ost = oracle.new_state(lp, f32(master[idx_t]), sample(m), sample(v), ohp, ols)
+    if param is not None:
+        assert np.array_equal(u16(param[idx_t]), ost.param)
+    if w.opt == "sgd":
+        h = zs.zero_shard_init_sgd(master, m, grad, param, psi=w.psi, nd=w.nd, rank=w.rank,
+                                   bucket_elems=cb, hp=hp, ls=ls)
+        step_fn = zs.zero_sgd_step
+    else:
+        h = zs.zero_shard_init(master, m, v, grad, param, psi=w.psi, nd=w.nd, rank=w.rank,
+                               bucket_elems=cb, hp=hp, ls=ls)
+        step_fn = zs.zero_adam_step
     try:
         scale = ls.init_scale
         for s in range(w.steps):
             synth.fill_contribs(w, bufs, s, scale, seed=0)
-            cs = [u16(b[idx_t]) for b in bufs]
+            cs = [stored(b[idx_t]) for b in bufs]
             zs.reduce_buckets(h, bufs, S, cb)
             chk = zs.zero_overflow_check(h)
             ok, where = torch_reduce_equal(bufs, grad, R, lp_t)
             assert ok, (name, s, "full reduce differs at", where)
             oi = oracle.step(ost, cs, len(idx), ohp, ols)
-            gs = u16(grad[idx_t])
+            gs = stored(grad[idx_t])
             gn, on = lp_is_nan(gs, w.lp), lp_is_nan(ost.grad, w.lp)
-            assert np.array_equal(gn, on) and np.array_equal(gs[~gn], ost.grad[~on]), (name, s)
+            assert np.array_equal(gn, on), (name, s)
+            assert np.array_equal(_bits(gs)[~gn], _bits(ost.grad)[~on]), (name, s)
             assert chk.overflow == oi.overflow, (name, s)
             if not chk.overflow:
                 inv = float(np.float32(1.0 / chk.scale_used))
                 tn = np.sqrt(torch_sumsq(grad, inv))
                 assert chk.grad_norm == pytest.approx(tn, rel=1e-9), (name, s)
-            info = zs.zero_adam_step(h)
+            info = step_fn(h)
             assert (info.overflow, info.skipped, info.step_t, info.scale_used, info.scale_next) == \
                 (oi.overflow, oi.skipped, oi.step_t, oi.scale_used, oi.scale_next), (name, s)
             log(f"[fullsize] {name} step {s}: overflow={info.overflow} t={info.step_t} "
@@ -113,11 +130,16 @@ def test_full_size_sampled(name):
             scale = info.scale_next
         torch.cuda.synchronize()
         assert max_rel(f32(master[idx_t]), ost.master) <= 1e-6
-        assert max_rel(f32(m[idx_t]), ost.m) <= 1e-6
-        assert max_rel(f32(v[idx_t]), ost.v) <= 1e-6
-        assert int(ulp_dist(u16(param[idx_t]), ost.param).max()) <= 1
-        bit = (np.array_equal(f32(master[idx_t]).view(np.uint32), ost.master.view(np.uint32))
-               and np.array_equal(u16(param[idx_t]), ost.param))
+        for a, b in ((m, ost.m), (v, ost.v)):
+            assert (a is None) == (b is None)
+            if a is not None:
+                assert max_rel(f32(a[idx_t]), b) <= 1e-6
+        bit = np.array_equal(f32(master[idx_t]).view(np.uint32), ost.master.view(np.uint32))
+        if param is not None:
+            assert int(ulp_dist(u16(param[idx_t]), ost.param).max()) <= 1
+            bit = bit and np.array_equal(u16(param[idx_t]), ost.param)
+        if m is not None:
+            bit = bit and np.array_equal(f32(m[idx_t]).view(np.uint32), ost.m.view(np.uint32))
         log(f"[fullsize] {name}: sampled state bitwise equal to the oracle: {bit}")
         assert bit
         if w.inject_step is not None:

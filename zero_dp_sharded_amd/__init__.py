@@ -25,14 +25,15 @@ ZERO_ERR_UNSUPPORTED = 5
 
 ZERO_FP16 = 1
 ZERO_BF16 = 2
+ZERO_FP32 = 3
 ZERO_WD_DECOUPLED = 0
 ZERO_WD_L2 = 1
 ZERO_MAX_CONTRIB = 64
 
 ABI_SYMBOLS = (
-    "zero_state_bytes", "zero_state_bytes_ex", "zero_shard_init", "zero_bucket_reduce",
-    "zero_overflow_check", "zero_overflow_merge", "zero_adam_step", "zero_adam_step_gated",
-    "zero_step_resolve",
+    "zero_state_bytes", "zero_state_bytes_ex", "zero_shard_init", "zero_shard_init_sgd",
+    "zero_bucket_reduce", "zero_overflow_check", "zero_overflow_merge", "zero_adam_step",
+    "zero_adam_step_gated", "zero_sgd_step", "zero_sgd_step_gated", "zero_step_resolve",
     "zero_shard_get_counters",
     "zero_shard_set_counters", "zero_shard_destroy", "zero_status_str", "zero_last_error",
     "zero_abi_version",
@@ -51,6 +52,10 @@ class ZeroAdamHParams(ctypes.Structure):
     _fields_ = [("lr", _f64), ("beta1", _f64), ("beta2", _f64), ("eps", _f64),
                 ("weight_decay", _f64), ("bias_correction", _i32), ("wd_mode", ctypes.c_int),
                 ("initial_step", _i64)]
+
+
+class ZeroSgdHParams(ctypes.Structure):
+    _fields_ = [("lr", _f64), ("momentum", _f64), ("weight_decay", _f64), ("initial_step", _i64)]
 
 
 class ZeroLossScaleCfg(ctypes.Structure):
@@ -97,6 +102,12 @@ def lib() -> ctypes.CDLL:
         L.zero_shard_init.argtypes = [ctypes.POINTER(ZeroShardDesc),
                                       ctypes.POINTER(ZeroAdamHParams),
                                       ctypes.POINTER(ZeroLossScaleCfg), ctypes.POINTER(_vp)]
+        L.zero_shard_init_sgd.argtypes = [ctypes.POINTER(ZeroShardDesc),
+                                          ctypes.POINTER(ZeroSgdHParams),
+                                          ctypes.POINTER(ZeroLossScaleCfg), ctypes.POINTER(_vp)]
+        L.zero_sgd_step.argtypes = [_vp, ctypes.POINTER(ZeroSgdHParams), _vp,
+                                    ctypes.POINTER(ZeroStepInfo)]
+        L.zero_sgd_step_gated.argtypes = [_vp, ctypes.POINTER(ZeroSgdHParams), _vp]
         L.zero_bucket_reduce.argtypes = [_vp, ctypes.POINTER(_vp), _i32, _i64, _i64, _vp]
         L.zero_overflow_check.argtypes = [_vp, _vp, ctypes.POINTER(ZeroStepInfo)]
         L.zero_adam_step.argtypes = [_vp, ctypes.POINTER(ZeroAdamHParams), _vp,
@@ -114,11 +125,9 @@ def lib() -> ctypes.CDLL:
         L.zero_last_error.argtypes = []
         L.zero_abi_version.restype = ctypes.c_int
         L.zero_abi_version.argtypes = []
-        for name in ("zero_state_bytes", "zero_state_bytes_ex", "zero_shard_init",
-                     "zero_bucket_reduce", "zero_overflow_check", "zero_adam_step",
-                     "zero_overflow_merge", "zero_adam_step_gated", "zero_step_resolve",
-                     "zero_shard_get_counters", "zero_shard_set_counters", "zero_shard_destroy"):
-            getattr(L, name).restype = ctypes.c_int
+        for name in ABI_SYMBOLS:
+            if name not in ("zero_status_str", "zero_last_error", "zero_abi_version"):
+                getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -160,6 +169,17 @@ class AdamHParams:
     def to_c(self) -> ZeroAdamHParams:
         return ZeroAdamHParams(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay,
                                self.bias_correction, self.wd_mode, self.initial_step)
+
+
+@dataclass
+class SGDHParams:
+    lr: float = 1e-2
+    momentum: float = 0.0
+    weight_decay: float = 0.0
+    initial_step: int = 0
+
+    def to_c(self) -> ZeroSgdHParams:
+        return ZeroSgdHParams(self.lr, self.momentum, self.weight_decay, self.initial_step)
 
 
 @dataclass
@@ -243,33 +263,62 @@ def _check_tensor(name, t, dtype, n):
         raise ValueError(f"{name}: must be contiguous with at least {n} elements")
 
 
-def zero_shard_init(master, exp_avg, exp_avg_sq, grad_shard, param_shard, *, psi: int,
-                    nd: int, rank: int, bucket_elems: int, hp: AdamHParams,
-                    ls: LossScaleCfg) -> int:
-    """Create a handle over caller-owned torch tensors; returns the handle."""
+def _lp_of(grad_shard):
     import torch
-    lp_t = grad_shard.dtype
-    lp = {torch.float16: ZERO_FP16, torch.bfloat16: ZERO_BF16}.get(lp_t)
+    lp = {torch.float16: ZERO_FP16, torch.bfloat16: ZERO_BF16,
+          torch.float32: ZERO_FP32}.get(grad_shard.dtype)
     if lp is None:
-        raise TypeError(f"grad_shard must be float16 or bfloat16, got {lp_t}")
+        raise TypeError(f"grad_shard must be float16, bfloat16 or float32, got {grad_shard.dtype}")
+    return lp
+
+
+def _desc_of(master, exp_avg, exp_avg_sq, grad_shard, param_shard, psi, nd, rank,
+             bucket_elems) -> ZeroShardDesc:
+    """Descriptor over torch tensors (None for an absent array).  fp32
+    grad_shard selects 4-byte storage, which takes no param_shard."""
+    import torch
+    lp = _lp_of(grad_shard)
     S = -(-psi // nd)
     for name, t, dt in (("master", master, torch.float32), ("exp_avg", exp_avg, torch.float32),
                         ("exp_avg_sq", exp_avg_sq, torch.float32),
-                        ("grad_shard", grad_shard, lp_t), ("param_shard", param_shard, lp_t)):
-        _check_tensor(name, t, dt, S)
-    desc = ZeroShardDesc(psi, nd, rank, bucket_elems, lp, master.data_ptr(),
-                         exp_avg.data_ptr(), exp_avg_sq.data_ptr(), grad_shard.data_ptr(),
-                         param_shard.data_ptr())
+                        ("grad_shard", grad_shard, grad_shard.dtype),
+                        ("param_shard", param_shard, grad_shard.dtype)):
+        if t is not None:
+            _check_tensor(name, t, dt, S)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    return ZeroShardDesc(psi, nd, rank, bucket_elems, lp, ptr(master), ptr(exp_avg),
+                         ptr(exp_avg_sq), ptr(grad_shard), ptr(param_shard))
+
+
+def zero_shard_init(master, exp_avg, exp_avg_sq, grad_shard, param_shard, *, psi: int,
+                    nd: int, rank: int, bucket_elems: int, hp: AdamHParams,
+                    ls: LossScaleCfg) -> int:
+    """Create an Adam handle over caller-owned torch tensors; returns the handle.
+    fp32 grad_shard: 4-byte storage, param_shard None."""
+    desc = _desc_of(master, exp_avg, exp_avg_sq, grad_shard, param_shard, psi, nd, rank,
+                    bucket_elems)
     h = _vp()
     _check(lib().zero_shard_init(ctypes.byref(desc), ctypes.byref(hp.to_c()),
                                  ctypes.byref(ls.to_c()), ctypes.byref(h)), "zero_shard_init")
     return h.value
 
 
+def zero_shard_init_sgd(master, momentum_buf, grad_shard, param_shard, *, psi: int, nd: int,
+                        rank: int, bucket_elems: int, hp: SGDHParams, ls: LossScaleCfg) -> int:
+    """Create an SGD handle; momentum_buf None for plain SGD."""
+    desc = _desc_of(master, momentum_buf, None, grad_shard, param_shard, psi, nd, rank,
+                    bucket_elems)
+    h = _vp()
+    _check(lib().zero_shard_init_sgd(ctypes.byref(desc), ctypes.byref(hp.to_c()),
+                                     ctypes.byref(ls.to_c()), ctypes.byref(h)),
+           "zero_shard_init_sgd")
+    return h.value
+
+
 def zero_bucket_reduce(h: int, contribs: Sequence, bucket_off: int, bucket_len: int,
                        stream=None) -> None:
     """contribs: R tensors (or device addresses), each holding this bucket's
-    bucket_len 2-byte gradients of one contribution."""
+    bucket_len gradients of one contribution in the storage format."""
     arr = (_vp * len(contribs))(*[_dptr(c) for c in contribs])
     _check(lib().zero_bucket_reduce(h, arr, len(contribs), bucket_off, bucket_len,
                                     _stream_ptr(stream)), "zero_bucket_reduce")
@@ -302,6 +351,18 @@ def zero_adam_step_gated(h: int, hp: Optional[AdamHParams] = None, stream=None) 
     _check(lib().zero_adam_step_gated(h, hpc, _stream_ptr(stream)), "zero_adam_step_gated")
 
 
+def zero_sgd_step(h: int, hp: Optional[SGDHParams] = None, stream=None) -> StepInfo:
+    out = ZeroStepInfo()
+    hpc = ctypes.byref(hp.to_c()) if hp is not None else None
+    _check(lib().zero_sgd_step(h, hpc, _stream_ptr(stream), ctypes.byref(out)), "zero_sgd_step")
+    return StepInfo.from_c(out)
+
+
+def zero_sgd_step_gated(h: int, hp: Optional[SGDHParams] = None, stream=None) -> None:
+    hpc = ctypes.byref(hp.to_c()) if hp is not None else None
+    _check(lib().zero_sgd_step_gated(h, hpc, _stream_ptr(stream)), "zero_sgd_step_gated")
+
+
 def zero_step_resolve(h: int) -> StepInfo:
     out = ZeroStepInfo()
     _check(lib().zero_step_resolve(h, ctypes.byref(out)), "zero_step_resolve")
@@ -325,10 +386,12 @@ def zero_shard_destroy(h: int) -> None:
 
 
 def reduce_buckets(h: int, contribs: Sequence, shard_elems: int, bucket_elems: int,
-                   stream=None) -> None:
+                   stream=None, esz: Optional[int] = None) -> None:
     """Submit every C_B bucket of a step in ascending order.  contribs are R
-    shard-sized tensors; bucket b passes the views [off, off + len)."""
-    esz = 2
+    shard-sized tensors (or addresses, with esz the bytes per element); bucket b
+    passes the views [off, off + len)."""
+    if esz is None:
+        esz = 2 if isinstance(contribs[0], int) else contribs[0].element_size()
     ptrs = [_dptr(c) for c in contribs]
     for off in range(0, shard_elems, bucket_elems):
         ln = min(bucket_elems, shard_elems - off)

@@ -60,6 +60,21 @@ def _link(objs, lib, verbose):
     os.replace(tmp, lib)
 
 
+def device_asm(src: str = "zero_kernels.hip") -> str:
+    """gfx950 assembly of one source under the build flags (for inspection and
+    for tests of what the compiler emitted)."""
+    objdir = os.path.join(ROOT, "_build", "zeroshard")
+    os.makedirs(objdir, exist_ok=True)
+    out = os.path.join(objdir, os.path.splitext(src)[0] + ".s")
+    cmd = [HIPCC, *FLAGS, "-x", "hip", "--cuda-device-only", "-S", os.path.join(CSRC, src),
+           "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")
+    with open(out, encoding="utf-8") as f:
+        return f.read()
+
+
 def build(verbose: bool = False) -> str:
     objdir = os.path.join(ROOT, "_build", "zeroshard")
     os.makedirs(objdir, exist_ok=True)

@@ -9,9 +9,9 @@ namespace zk {
 
 constexpr int kMaxContrib = 64;
 
-// Reduce / scan: 256 lanes per workgroup, each lane two runs of 8 two-byte
-// elements (each load instruction of a wave covers 1 KiB contiguously);
-// residency capped at 4 workgroups (16 waves) per CU.
+// Reduce / scan: 256 lanes per workgroup, each lane two 16-byte runs (8
+// two-byte or 4 fp32 elements; each load instruction of a wave covers 1 KiB
+// contiguously); residency capped at 4 workgroups (16 waves) per CU.
 // (The ZK_* macros exist only to build tuning variants; the defaults are the
 // measured optimum.)
 #ifndef ZK_RED_BLOCK
@@ -34,10 +34,11 @@ constexpr int kMaxContrib = 64;
 #endif
 constexpr int kRedBlock = ZK_RED_BLOCK;
 constexpr int kRedRuns = ZK_RED_RUNS;
-constexpr int64_t kRedElemsPerBlock = (int64_t)kRedBlock * kRedRuns * 8;   // 4096
+// elements one reduce workgroup covers with the narrowest run (fp32, 4 per run)
+constexpr int64_t kRedElemsPerBlockMin = (int64_t)kRedBlock * kRedRuns * 4;   // 2048
 constexpr int kRedPerCU = ZK_RED_PER_CU;
-// Adam: one wave (64 lanes) per workgroup, each lane one group of 4 elements;
-// residency capped at 10 workgroups (10 waves) per CU.
+// Adam and SGD: one wave (64 lanes) per workgroup, each lane one group of 4
+// elements; residency capped at 10 workgroups (10 waves) per CU.
 constexpr int kAdamBlock = ZK_ADAM_BLOCK;
 constexpr int kAdamGroups = ZK_ADAM_GROUPS;
 constexpr int64_t kAdamElemsPerBlock = (int64_t)kAdamBlock * kAdamGroups * 4;  // 256
@@ -61,9 +62,9 @@ struct ContribPtrs {
 };
 
 // One bucket of the reduce.  Elements [0, n) of the bucket; the vector body
-// starts at `head` and holds `nvec` runs of 8 elements that are 16-byte aligned
-// in every contribution and in `out`.  vec_ok = 0 selects the element-wise
-// path.  Workgroup b writes partial[slot_base + b]: the fp64 sum of the squared
+// starts at `head` and holds `nvec` 16-byte runs (8 two-byte or 4 fp32
+// elements) that are 16-byte aligned in every contribution and in `out`.
+// vec_ok = 0 selects the element-wise path.  Workgroup b writes partial[slot_base + b]: the fp64 sum of the squared
 // unscaled stored values of its elements, or NaN if any stored value is not
 // finite.
 struct ReduceLaunch {
@@ -73,7 +74,7 @@ struct ReduceLaunch {
     int64_t head;
     int64_t nvec;
     int32_t R;
-    int32_t lp;            // 1 fp16, 2 bf16
+    int32_t lp;            // 1 fp16, 2 bf16, 3 fp32
     int32_t vec_ok;
     float inv_r;
     float inv_scale;
@@ -94,6 +95,23 @@ struct ScanLaunch {
     double* partial;
     int64_t slot_base;
     uint32_t lds_reserve;
+};
+
+// SGD over n elements, laid out like AdamLaunch.  mom == nullptr: plain SGD.
+struct SgdLaunch {
+    const void* grad;
+    float* master;
+    float* mom;
+    void* param;
+    int64_t n;
+    int64_t head;
+    int64_t ngroups;
+    int32_t lp;
+    int32_t vec_ok;
+    int32_t has_wd;
+    uint32_t lds_reserve;
+    float lr, mu, wd, inv_scale;
+    const struct CheckResult* gate;
 };
 
 struct CheckResult {
@@ -125,9 +143,13 @@ struct AdamLaunch {
     const CheckResult* gate;
 };
 
+// Elements per 16-byte run of a storage format: 8 two-byte or 4 fp32 values.
+inline int run_width(int32_t lp) { return lp == 3 ? 4 : 8; }
+
 // Partial slots a reduce / scan of this layout writes: one per workgroup of
-// the vector kernel plus one per workgroup of the element-wise kernel.
-int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok);
+// the vector kernel plus one per workgroup of the element-wise kernel.  W is
+// the run width of the storage format.
+int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok, int W);
 
 hipError_t launch_reduce(const ReduceLaunch& L, hipStream_t s);
 hipError_t launch_scan(const ScanLaunch& L, hipStream_t s);
@@ -135,5 +157,6 @@ hipError_t launch_scan(const ScanLaunch& L, hipStream_t s);
 hipError_t launch_finalize(const double* partial, int64_t nslots, double* level1,
                            CheckResult* out, hipStream_t s);
 hipError_t launch_adam(const AdamLaunch& a, hipStream_t s);
+hipError_t launch_sgd(const SgdLaunch& a, hipStream_t s);
 
 }  // namespace zk

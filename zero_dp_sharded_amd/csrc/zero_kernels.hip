@@ -10,12 +10,17 @@
 //    (lane-consecutive 16-byte or 8-byte pieces);
 //  - nontemporal loads and stores (each byte is touched once per step);
 //  - a cap on resident workgroups per CU, set by reserving dynamic LDS the
-//    kernels never touch: with the 5 to 7 concurrent streams of these kernels,
-//    fewer resident waves (8 per CU for Adam, 16 for the reduce) sustain more
-//    HBM bandwidth than full occupancy.
+//    kernels never touch: with the 4 to 7 concurrent streams of these kernels,
+//    fewer resident waves (10 per CU for the update, 16 for the reduce)
+//    sustain more HBM bandwidth than full occupancy.
 // The only cross-lane work is the fixed-shape reduction of the overflow flag
 // and the squared gradient norm: wave butterfly, one LDS slot per wave, one
 // fp64 partial per workgroup, then a fixed-order two-level fold.
+//
+// Storage formats: fp16 and bf16 (2-byte grads and params beside the fp32
+// master copy) and fp32 (4-byte grads; the fp32 master is the parameter and
+// no low-precision copy is written).  A 16-byte run holds 8 two-byte or 4 fp32
+// elements.
 //
 // Floating point: built with -ffp-contract=off, correctly rounded fp32 divide
 // and square root, fp32 denormals kept, and packed-fp32 instructions disabled.
@@ -34,19 +39,41 @@ typedef __bf16 b4 __attribute__((ext_vector_type(4)));
 typedef float f8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Per storage format: element type T and its bit pattern type, the 16-byte run
+// VW of W elements with its fp32 image FW and bit view BW, the 4-element group
+// V4 of the update kernels, and the exponent mask that marks inf/NaN.
 template <int LP> struct Fmt;
 template <> struct Fmt<1> {            // IEEE binary16
     using T = _Float16;
-    using V8 = h8;
+    using Bits = unsigned short;
+    static constexpr int W = 8;
+    using VW = h8;
+    using FW = f8;
+    using BW = u16x8;
     using V4 = h4;
-    static constexpr unsigned short kExp = 0x7c00;
+    static constexpr Bits kExp = 0x7c00;
 };
 template <> struct Fmt<2> {            // bfloat16
     using T = __bf16;
-    using V8 = b8;
+    using Bits = unsigned short;
+    static constexpr int W = 8;
+    using VW = b8;
+    using FW = f8;
+    using BW = u16x8;
     using V4 = b4;
-    static constexpr unsigned short kExp = 0x7f80;
+    static constexpr Bits kExp = 0x7f80;
+};
+template <> struct Fmt<3> {            // IEEE binary32
+    using T = float;
+    using Bits = unsigned int;
+    static constexpr int W = 4;
+    using VW = f4;
+    using FW = f4;
+    using BW = u32x4;
+    using V4 = f4;
+    static constexpr Bits kExp = 0x7f800000u;
 };
 
 template <typename V>
@@ -67,18 +94,42 @@ __device__ __forceinline__ float load_s(const void* base, int64_t e)
     return static_cast<float>(static_cast<const typename Fmt<LP>::T*>(base)[e]);
 }
 
+// Base pointer advanced by `elems` elements of the storage format.
+template <int LP>
+__device__ __forceinline__ const void* adv(const void* p, int64_t elems)
+{
+    return static_cast<const char*>(p) + (int64_t)sizeof(typename Fmt<LP>::T) * elems;
+}
+
+template <int LP>
+__device__ __forceinline__ void* adv(void* p, int64_t elems)
+{
+    return static_cast<char*>(p) + (int64_t)sizeof(typename Fmt<LP>::T) * elems;
+}
+
+// An fp32 result held as a rounded fp32 value before it is narrowed.  Without
+// it the compiler may fuse the multiply that produced it with the conversion to
+// fp16 (v_fma_mixlo_f16 rounds the exact product once, straight to fp16), which
+// skips the fp32 rounding in between and differs in the last fp16 bit whenever
+// the fp32 product falls on an fp16 rounding tie.
+__device__ __forceinline__ float pin_f32(float x)
+{
+    asm("" : "+v"(x));
+    return x;
+}
+
 // ----------------------------------------------------------------- check
 
-// Overflow flag and squared unscaled norm of stored 2-byte values.
+// Overflow flag and squared unscaled norm of one stored run.
 template <int LP>
-__device__ __forceinline__ void check_v(typename Fmt<LP>::V8 o, float inv_scale, int& flag,
+__device__ __forceinline__ void check_v(typename Fmt<LP>::VW o, float inv_scale, int& flag,
                                         double& ss)
 {
     using F = Fmt<LP>;
-    const u16x8 bits = __builtin_bit_cast(u16x8, o);
-    const f8 of = __builtin_convertvector(o, f8);
+    const typename F::BW bits = __builtin_bit_cast(typename F::BW, o);
+    const typename F::FW of = __builtin_convertvector(o, typename F::FW);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < F::W; ++k) {
         flag |= (bits[k] & F::kExp) == F::kExp;
         const float u = of[k] * inv_scale;
         ss += (double)u * (double)u;
@@ -90,7 +141,7 @@ __device__ __forceinline__ void check_s(typename Fmt<LP>::T o, float inv_scale, 
                                         double& ss)
 {
     using F = Fmt<LP>;
-    const unsigned short bits = __builtin_bit_cast(unsigned short, o);
+    const typename F::Bits bits = __builtin_bit_cast(typename F::Bits, o);
     flag |= (bits & F::kExp) == F::kExp;
     const float u = static_cast<float>(o) * inv_scale;
     ss += (double)u * (double)u;
@@ -146,17 +197,19 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 
 // ----------------------------------------------------------------- reduce
 
-// Finish the 8-element run vi of the vector body (elements head + 8 vi ..):
-// acc holds the fp32 sum over r = 0..R-1 in order from +0; scale by
-// fp32(1/R), round to the 2-byte format, store, check.
+// Finish run vi of the vector body (elements head + W vi ..): acc holds the
+// fp32 sum over r = 0..R-1 in order from +0; scale by fp32(1/R), convert to
+// the storage format (round to nearest even), store, check.
 template <int LP>
-__device__ __forceinline__ void reduce_finish(const ReduceLaunch& L, int64_t vi, f8 acc, int& flag,
-                                              double& ss)
+__device__ __forceinline__ void reduce_finish(const ReduceLaunch& L, int64_t vi,
+                                              typename Fmt<LP>::FW acc, int& flag, double& ss)
 {
-    using V8 = typename Fmt<LP>::V8;
+    using VW = typename Fmt<LP>::VW;
     acc = acc * L.inv_r;
-    const V8 o = __builtin_convertvector(acc, V8);
-    st_nt<V8>(static_cast<char*>(L.out) + 2 * L.head, vi, o);
+#pragma unroll
+    for (int k = 0; k < Fmt<LP>::W; ++k) acc[k] = pin_f32(acc[k]);
+    const VW o = __builtin_convertvector(acc, VW);
+    st_nt<VW>(adv<LP>(L.out, L.head), vi, o);
     check_v<LP>(o, L.inv_scale, flag, ss);
 }
 
@@ -166,41 +219,41 @@ __device__ __forceinline__ void reduce_s(const ReduceLaunch& L, int64_t e, int& 
     using T = typename Fmt<LP>::T;
     float acc = 0.f;
     for (int r = 0; r < L.R; ++r) acc = acc + load_s<LP>(L.c.p[r], e);
-    const T o = static_cast<T>(acc * L.inv_r);
+    const T o = static_cast<T>(pin_f32(acc * L.inv_r));
     static_cast<T*>(L.out)[e] = o;
     check_s<LP>(o, L.inv_scale, flag, ss);
 }
 
 // Vector body: workgroup b covers runs [b*B*U, (b+1)*B*U) for B lanes and U
 // runs per lane; lane l owns runs b*B*U + u*B + l.  Element offsets past `head`
-// are multiples of 8, so contribution and output pointers advanced by `head`
-// are 16-byte aligned and are indexed in units of 8 elements.
+// are multiples of W, so contribution and output pointers advanced by `head`
+// are 16-byte aligned and are indexed in units of runs.
 template <int LP, int RT>
 __global__ __launch_bounds__(kRedBlock) void reduce_vec_kernel(ReduceLaunch L)
 {
-    using V8 = typename Fmt<LP>::V8;
+    using VW = typename Fmt<LP>::VW;
+    using FW = typename Fmt<LP>::FW;
     int flag = 0;
     double ss = 0.0;
     const int64_t v0 = (int64_t)blockIdx.x * (kRedBlock * kRedRuns) + threadIdx.x;
     if constexpr (RT > 0 && RT * kRedRuns <= 16) {
         // every load of both runs in flight before the arithmetic
-        V8 x[kRedRuns][RT];
+        VW x[kRedRuns][RT];
 #pragma unroll
         for (int u = 0; u < kRedRuns; ++u) {
             const int64_t vi = v0 + u * kRedBlock;
             if (vi < L.nvec) {
 #pragma unroll
-                for (int r = 0; r < RT; ++r)
-                    x[u][r] = ld_nt<V8>(static_cast<const char*>(L.c.p[r]) + 2 * L.head, vi);
+                for (int r = 0; r < RT; ++r) x[u][r] = ld_nt<VW>(adv<LP>(L.c.p[r], L.head), vi);
             }
         }
 #pragma unroll
         for (int u = 0; u < kRedRuns; ++u) {
             const int64_t vi = v0 + u * kRedBlock;
             if (vi < L.nvec) {
-                f8 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                FW acc = (FW)(0.f);
 #pragma unroll
-                for (int r = 0; r < RT; ++r) acc = acc + __builtin_convertvector(x[u][r], f8);
+                for (int r = 0; r < RT; ++r) acc = acc + __builtin_convertvector(x[u][r], FW);
                 reduce_finish<LP>(L, vi, acc, flag, ss);
             }
         }
@@ -208,25 +261,23 @@ __global__ __launch_bounds__(kRedBlock) void reduce_vec_kernel(ReduceLaunch L)
         for (int u = 0; u < kRedRuns; ++u) {
             const int64_t vi = v0 + u * kRedBlock;
             if (vi >= L.nvec) break;
-            f8 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            FW acc = (FW)(0.f);
             if constexpr (RT > 0) {
-                V8 x[RT];
+                VW x[RT];
 #pragma unroll
-                for (int r = 0; r < RT; ++r)
-                    x[r] = ld_nt<V8>(static_cast<const char*>(L.c.p[r]) + 2 * L.head, vi);
+                for (int r = 0; r < RT; ++r) x[r] = ld_nt<VW>(adv<LP>(L.c.p[r], L.head), vi);
 #pragma unroll
-                for (int r = 0; r < RT; ++r) acc = acc + __builtin_convertvector(x[r], f8);
+                for (int r = 0; r < RT; ++r) acc = acc + __builtin_convertvector(x[r], FW);
             } else {
                 for (int r0 = 0; r0 < L.R; r0 += 8) {
                     const int cnt = L.R - r0 < 8 ? L.R - r0 : 8;
-                    V8 x[8];
+                    VW x[8];
 #pragma unroll
                     for (int k = 0; k < 8; ++k)
-                        if (k < cnt)
-                            x[k] = ld_nt<V8>(static_cast<const char*>(L.c.p[r0 + k]) + 2 * L.head, vi);
+                        if (k < cnt) x[k] = ld_nt<VW>(adv<LP>(L.c.p[r0 + k], L.head), vi);
 #pragma unroll
                     for (int k = 0; k < 8; ++k)
-                        if (k < cnt) acc = acc + __builtin_convertvector(x[k], f8);
+                        if (k < cnt) acc = acc + __builtin_convertvector(x[k], FW);
                 }
             }
             reduce_finish<LP>(L, vi, acc, flag, ss);
@@ -253,15 +304,15 @@ __global__ __launch_bounds__(kScalarBlock) void reduce_elem_kernel(ReduceLaunch 
 template <int LP>
 __global__ __launch_bounds__(kRedBlock) void scan_vec_kernel(ScanLaunch L)
 {
-    using V8 = typename Fmt<LP>::V8;
+    using VW = typename Fmt<LP>::VW;
     int flag = 0;
     double ss = 0.0;
     const int64_t v0 = (int64_t)blockIdx.x * (kRedBlock * kRedRuns) + threadIdx.x;
-    V8 x[kRedRuns];
+    VW x[kRedRuns];
 #pragma unroll
     for (int u = 0; u < kRedRuns; ++u) {
         const int64_t vi = v0 + u * kRedBlock;
-        if (vi < L.nvec) x[u] = ld_nt<V8>(static_cast<const char*>(L.g) + 2 * L.head, vi);
+        if (vi < L.nvec) x[u] = ld_nt<VW>(adv<LP>(L.g, L.head), vi);
     }
 #pragma unroll
     for (int u = 0; u < kRedRuns; ++u)
@@ -305,6 +356,17 @@ __global__ __launch_bounds__(kFoldBlock) void fold_kernel(const double* in, int6
     }
 }
 
+// ----------------------------------------------------------------- update gate
+
+// Device-side skip of a gated launch: the fold leaves NaN in the result when
+// any stored gradient is not finite.  The vector kernels read the gate after
+// issuing their loads, so its latency overlaps them (a skipped step costs the
+// load bytes but writes nothing); the element-wise kernels read it first.
+__device__ __forceinline__ bool gated_off(const CheckResult* gate)
+{
+    return gate != nullptr && __builtin_isnan(gate->sumsq);
+}
+
 // ----------------------------------------------------------------- Adam
 
 // Textbook Adam on one element (Kingma & Ba 2015, Algorithm 1), in the order
@@ -328,22 +390,12 @@ __device__ __forceinline__ void adam_e(float graw, float& p, float& m, float& v,
 // head are 16-byte aligned, 2-byte pointers 8-byte aligned).  Workgroup b
 // covers groups [b*B*G, (b+1)*B*G) for B lanes and G groups per lane; lane l
 // owns groups b*B*G + u*B + l, u < G, and issues all loads before any
-// arithmetic.
-// Device-side skip of a gated launch: the fold leaves NaN in the result when
-// any stored gradient is not finite.  The vector kernel reads the gate after
-// issuing its loads (a skipped step then costs the 14 load bytes per element
-// but writes nothing); the element-wise kernel reads it first.
-__device__ __forceinline__ bool gated_off(const AdamLaunch& a)
-{
-    return a.gate != nullptr && __builtin_isnan(a.gate->sumsq);
-}
-
+// arithmetic.  With fp32 storage there is no 2-byte parameter to write.
 template <int LP, int WD>
 __global__ __launch_bounds__(kAdamBlock) void adam_vec_kernel(AdamLaunch a)
 {
     using V4 = typename Fmt<LP>::V4;
-    const void* gb = static_cast<const char*>(a.grad) + 2 * a.head;
-    void* qb = static_cast<char*>(a.param) + 2 * a.head;
+    const void* gb = adv<LP>(a.grad, a.head);
     float* pb = a.master + a.head;
     float* mb = a.m + a.head;
     float* vb = a.v + a.head;
@@ -360,9 +412,7 @@ __global__ __launch_bounds__(kAdamBlock) void adam_vec_kernel(AdamLaunch a)
             v[u] = ld_nt<f4>(vb, q);
         }
     }
-    // The gate is read after the loads are issued, so its latency overlaps
-    // them; on a skipped step the workgroup returns before any store.
-    if (gated_off(a)) return;
+    if (gated_off(a.gate)) return;
 #pragma unroll
     for (int u = 0; u < kAdamGroups; ++u) {
         const int64_t q = q0 + u * kAdamBlock;
@@ -380,7 +430,8 @@ __global__ __launch_bounds__(kAdamBlock) void adam_vec_kernel(AdamLaunch a)
             st_nt<f4>(pb, q, pp);
             st_nt<f4>(mb, q, mm);
             st_nt<f4>(vb, q, vv);
-            st_nt<V4>(qb, q, __builtin_convertvector(pp, V4));
+            if constexpr (LP != 3)
+                st_nt<V4>(adv<LP>(a.param, a.head), q, __builtin_convertvector(pp, V4));
         }
     }
 }
@@ -389,7 +440,7 @@ template <int LP, int WD>
 __global__ __launch_bounds__(kScalarBlock) void adam_elem_kernel(AdamLaunch a, Ranges rg)
 {
     using T = typename Fmt<LP>::T;
-    if (gated_off(a)) return;
+    if (gated_off(a.gate)) return;
     const int64_t cnt = rg.count();
     for (int j = 0; j < (int)(kScalarElemsPerBlock / kScalarBlock); ++j) {
         const int64_t k = (int64_t)blockIdx.x * kScalarElemsPerBlock + j * kScalarBlock + threadIdx.x;
@@ -400,10 +451,94 @@ __global__ __launch_bounds__(kScalarBlock) void adam_elem_kernel(AdamLaunch a, R
             a.master[e] = p;
             a.m[e] = m;
             a.v[e] = v;
-            static_cast<T*>(a.param)[e] = static_cast<T>(p);
+            if constexpr (LP != 3) static_cast<T*>(a.param)[e] = static_cast<T>(p);
         }
     }
 }
+
+// ----------------------------------------------------------------- SGD
+
+// Heavy-ball SGD with L2 weight decay on one element, in the order the public
+// header states; p and the momentum buffer b are updated in place.
+template <int MOM, int WD>
+__device__ __forceinline__ void sgd_e(float graw, float& p, float& b, const SgdLaunch& a)
+{
+    float g = graw * a.inv_scale;
+    if constexpr (WD) g = g + a.wd * p;
+    float d = g;
+    if constexpr (MOM) {
+        b = a.mu * b + g;
+        d = b;
+    }
+    p = p - a.lr * d;
+}
+
+// Same layout and load-first order as adam_vec_kernel.
+template <int LP, int MOM, int WD>
+__global__ __launch_bounds__(kAdamBlock) void sgd_vec_kernel(SgdLaunch a)
+{
+    using V4 = typename Fmt<LP>::V4;
+    const void* gb = adv<LP>(a.grad, a.head);
+    float* pb = a.master + a.head;
+    float* bb = MOM ? a.mom + a.head : nullptr;
+    const int64_t q0 = (int64_t)blockIdx.x * (kAdamBlock * kAdamGroups) + threadIdx.x;
+    V4 g[kAdamGroups];
+    f4 p[kAdamGroups], b[kAdamGroups];
+#pragma unroll
+    for (int u = 0; u < kAdamGroups; ++u) {
+        const int64_t q = q0 + u * kAdamBlock;
+        if (q < a.ngroups) {
+            g[u] = ld_nt<V4>(gb, q);
+            p[u] = ld_nt<f4>(pb, q);
+            if constexpr (MOM) b[u] = ld_nt<f4>(bb, q);
+        }
+    }
+    if (gated_off(a.gate)) return;
+#pragma unroll
+    for (int u = 0; u < kAdamGroups; ++u) {
+        const int64_t q = q0 + u * kAdamBlock;
+        if (q < a.ngroups) {
+            const f4 gf = __builtin_convertvector(g[u], f4);
+            f4 pp = p[u];
+            f4 buf = (f4)(0.f);
+            if constexpr (MOM) buf = b[u];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float pk = pp[k], bk = buf[k];
+                sgd_e<MOM, WD>(gf[k], pk, bk, a);
+                pp[k] = pk;
+                buf[k] = bk;
+            }
+            st_nt<f4>(pb, q, pp);
+            if constexpr (MOM) st_nt<f4>(bb, q, buf);
+            if constexpr (LP != 3)
+                st_nt<V4>(adv<LP>(a.param, a.head), q, __builtin_convertvector(pp, V4));
+        }
+    }
+}
+
+template <int LP, int MOM, int WD>
+__global__ __launch_bounds__(kScalarBlock) void sgd_elem_kernel(SgdLaunch a, Ranges rg)
+{
+    using T = typename Fmt<LP>::T;
+    if (gated_off(a.gate)) return;
+    const int64_t cnt = rg.count();
+    for (int j = 0; j < (int)(kScalarElemsPerBlock / kScalarBlock); ++j) {
+        const int64_t k = (int64_t)blockIdx.x * kScalarElemsPerBlock + j * kScalarBlock + threadIdx.x;
+        if (k < cnt) {
+            const int64_t e = rg.at(k);
+            float p = a.master[e];
+            float b = 0.f;
+            if constexpr (MOM) b = a.mom[e];
+            sgd_e<MOM, WD>(load_s<LP>(a.grad, e), p, b, a);
+            a.master[e] = p;
+            if constexpr (MOM) a.mom[e] = b;
+            if constexpr (LP != 3) static_cast<T*>(a.param)[e] = static_cast<T>(p);
+        }
+    }
+}
+
+// ----------------------------------------------------------------- launches
 
 // Element lists of a layout: head and tail of the vector path, or everything.
 Ranges ranges_of(int64_t n, int64_t head, int64_t body, int32_t vec_ok)
@@ -439,6 +574,7 @@ hipError_t reduce_vec_launch(const ReduceLaunch& L, unsigned grid, hipStream_t s
 template <int LP>
 hipError_t reduce_dispatch(const ReduceLaunch& L, hipStream_t s)
 {
+    constexpr int W = Fmt<LP>::W;
     const int64_t runs_per_block = (int64_t)kRedBlock * kRedRuns;
     const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, runs_per_block) : 0;
     // consecutive launches of at most kMaxLaunchItems work-items; each starts
@@ -447,16 +583,40 @@ hipError_t reduce_dispatch(const ReduceLaunch& L, hipStream_t s)
     for (int64_t b0 = 0; b0 < vblocks; b0 += max_blocks) {
         const int64_t nb = vblocks - b0 < max_blocks ? vblocks - b0 : max_blocks;
         ReduceLaunch part = L;
-        part.head = L.head + 8 * runs_per_block * b0;
+        part.head = L.head + W * runs_per_block * b0;
         part.nvec = L.nvec - runs_per_block * b0;
         part.slot_base = L.slot_base + b0;
         hipError_t e = reduce_vec_launch<LP>(part, (unsigned)nb, s);
         if (e != hipSuccess) return e;
     }
-    const Ranges rg = ranges_of(L.n, L.head, 8 * L.nvec, L.vec_ok);
+    const Ranges rg = ranges_of(L.n, L.head, W * L.nvec, L.vec_ok);
     const int64_t sblocks = ceil_div(rg.a_len + rg.b_len, kScalarElemsPerBlock);
     if (sblocks > 0)
         reduce_elem_kernel<LP><<<(unsigned)sblocks, kScalarBlock, 0, s>>>(L, rg, L.slot_base + vblocks);
+    return hipGetLastError();
+}
+
+template <int LP>
+hipError_t scan_dispatch(const ScanLaunch& L, hipStream_t s)
+{
+    constexpr int W = Fmt<LP>::W;
+    const int64_t runs_per_block = (int64_t)kRedBlock * kRedRuns;
+    const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, runs_per_block) : 0;
+    const int64_t max_blocks = kMaxLaunchItems / kRedBlock;
+    for (int64_t b0 = 0; b0 < vblocks; b0 += max_blocks) {
+        const int64_t nb = vblocks - b0 < max_blocks ? vblocks - b0 : max_blocks;
+        ScanLaunch part = L;
+        part.head = L.head + W * runs_per_block * b0;
+        part.nvec = L.nvec - runs_per_block * b0;
+        part.slot_base = L.slot_base + b0;
+        scan_vec_kernel<LP><<<(unsigned)nb, kRedBlock, L.lds_reserve, s>>>(part);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const Ranges rg = ranges_of(L.n, L.head, W * L.nvec, L.vec_ok);
+    const int64_t sblocks = ceil_div(rg.a_len + rg.b_len, kScalarElemsPerBlock);
+    if (sblocks > 0)
+        scan_elem_kernel<LP><<<(unsigned)sblocks, kScalarBlock, 0, s>>>(L, rg, L.slot_base + vblocks);
     return hipGetLastError();
 }
 
@@ -491,46 +651,62 @@ hipError_t adam_dispatch_wd(const AdamLaunch& a, hipStream_t s)
     }
 }
 
-template <int LP>
-hipError_t scan_dispatch(const ScanLaunch& L, hipStream_t s)
+template <int LP, int MOM, int WD>
+hipError_t sgd_dispatch(const SgdLaunch& a, hipStream_t s)
 {
-    const int64_t runs_per_block = (int64_t)kRedBlock * kRedRuns;
-    const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, runs_per_block) : 0;
-    const int64_t max_blocks = kMaxLaunchItems / kRedBlock;
+    const int64_t groups_per_block = (int64_t)kAdamBlock * kAdamGroups;
+    const int64_t vblocks = a.vec_ok ? ceil_div(a.ngroups, groups_per_block) : 0;
+    const int64_t max_blocks = kMaxLaunchItems / kAdamBlock;
     for (int64_t b0 = 0; b0 < vblocks; b0 += max_blocks) {
         const int64_t nb = vblocks - b0 < max_blocks ? vblocks - b0 : max_blocks;
-        ScanLaunch part = L;
-        part.head = L.head + 8 * runs_per_block * b0;
-        part.nvec = L.nvec - runs_per_block * b0;
-        part.slot_base = L.slot_base + b0;
-        scan_vec_kernel<LP><<<(unsigned)nb, kRedBlock, L.lds_reserve, s>>>(part);
+        SgdLaunch part = a;
+        part.head = a.head + 4 * groups_per_block * b0;
+        part.ngroups = a.ngroups - groups_per_block * b0;
+        sgd_vec_kernel<LP, MOM, WD><<<(unsigned)nb, kAdamBlock, a.lds_reserve, s>>>(part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const Ranges rg = ranges_of(L.n, L.head, 8 * L.nvec, L.vec_ok);
+    const Ranges rg = ranges_of(a.n, a.head, 4 * a.ngroups, a.vec_ok);
     const int64_t sblocks = ceil_div(rg.a_len + rg.b_len, kScalarElemsPerBlock);
     if (sblocks > 0)
-        scan_elem_kernel<LP><<<(unsigned)sblocks, kScalarBlock, 0, s>>>(L, rg, L.slot_base + vblocks);
+        sgd_elem_kernel<LP, MOM, WD><<<(unsigned)sblocks, kScalarBlock, 0, s>>>(a, rg);
     return hipGetLastError();
+}
+
+template <int LP>
+hipError_t sgd_dispatch_kind(const SgdLaunch& a, hipStream_t s)
+{
+    if (a.mom != nullptr)
+        return a.has_wd ? sgd_dispatch<LP, 1, 1>(a, s) : sgd_dispatch<LP, 1, 0>(a, s);
+    return a.has_wd ? sgd_dispatch<LP, 0, 1>(a, s) : sgd_dispatch<LP, 0, 0>(a, s);
 }
 
 }  // namespace
 
-int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok)
+int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok, int W)
 {
+    (void)head;
     const int64_t vblocks = vec_ok ? ceil_div(nvec, (int64_t)kRedBlock * kRedRuns) : 0;
-    const int64_t scalars = vec_ok ? n - 8 * nvec : n;
+    const int64_t scalars = vec_ok ? n - (int64_t)W * nvec : n;
     return vblocks + ceil_div(scalars, kScalarElemsPerBlock);
 }
 
 hipError_t launch_reduce(const ReduceLaunch& L, hipStream_t s)
 {
-    return L.lp == 2 ? reduce_dispatch<2>(L, s) : reduce_dispatch<1>(L, s);
+    switch (L.lp) {
+    case 2: return reduce_dispatch<2>(L, s);
+    case 3: return reduce_dispatch<3>(L, s);
+    default: return reduce_dispatch<1>(L, s);
+    }
 }
 
 hipError_t launch_scan(const ScanLaunch& L, hipStream_t s)
 {
-    return L.lp == 2 ? scan_dispatch<2>(L, s) : scan_dispatch<1>(L, s);
+    switch (L.lp) {
+    case 2: return scan_dispatch<2>(L, s);
+    case 3: return scan_dispatch<3>(L, s);
+    default: return scan_dispatch<1>(L, s);
+    }
 }
 
 hipError_t launch_finalize(const double* partial, int64_t nslots, double* level1,
@@ -547,7 +723,20 @@ hipError_t launch_finalize(const double* partial, int64_t nslots, double* level1
 
 hipError_t launch_adam(const AdamLaunch& a, hipStream_t s)
 {
-    return a.lp == 2 ? adam_dispatch_wd<2>(a, s) : adam_dispatch_wd<1>(a, s);
+    switch (a.lp) {
+    case 2: return adam_dispatch_wd<2>(a, s);
+    case 3: return adam_dispatch_wd<3>(a, s);
+    default: return adam_dispatch_wd<1>(a, s);
+    }
+}
+
+hipError_t launch_sgd(const SgdLaunch& a, hipStream_t s)
+{
+    switch (a.lp) {
+    case 2: return sgd_dispatch_kind<2>(a, s);
+    case 3: return sgd_dispatch_kind<3>(a, s);
+    default: return sgd_dispatch_kind<1>(a, s);
+    }
 }
 
 }  // namespace zk

@@ -38,6 +38,7 @@ zero_status hip_fail(hipError_t e, const char* what)
 }
 
 enum Phase { kIdle = 0, kReducing = 1, kChecked = 2, kPending = 3 };
+enum Opt { kOptAdam = 0, kOptSgd = 1 };
 
 }  // namespace
 
@@ -45,7 +46,10 @@ struct zero_shard_s {
     int device = -1;
     zero_shard_desc d{};
     int64_t S = 0;
-    zero_adam_hparams hp{};
+    Opt opt = kOptAdam;
+    int esz = 2;                  // bytes per stored gradient / param element
+    zero_adam_hparams hp{};       // Adam handles
+    zero_sgd_hparams sgd{};       // SGD handles
     zero_loss_scale_cfg ls{};
     // step state
     int64_t t = 0;
@@ -120,8 +124,24 @@ zero_status check_ls(const zero_loss_scale_cfg* ls)
     return ZERO_OK;
 }
 
-// Both 2-byte formats take two bytes per element.
-constexpr size_t kLpBytes = 2;
+zero_status check_sgd_hparams(const zero_sgd_hparams* hp, bool has_buffer)
+{
+    if (!hp) return fail(ZERO_ERR_INVALID_ARG, "sgd hparams: NULL");
+    if (!(std::isfinite(hp->lr) && hp->lr >= 0.0))
+        return fail(ZERO_ERR_INVALID_ARG, "sgd hparams: lr must be finite and >= 0");
+    if (!(hp->momentum >= 0.0 && hp->momentum < 1.0))
+        return fail(ZERO_ERR_INVALID_ARG, "sgd hparams: momentum must lie in [0, 1)");
+    if (hp->momentum != 0.0 && !has_buffer)
+        return fail(ZERO_ERR_INVALID_ARG, "sgd hparams: momentum != 0 needs a momentum buffer (exp_avg)");
+    if (!(std::isfinite(hp->weight_decay) && hp->weight_decay >= 0.0))
+        return fail(ZERO_ERR_INVALID_ARG, "sgd hparams: weight_decay must be finite and >= 0");
+    if (hp->initial_step < 0)
+        return fail(ZERO_ERR_INVALID_ARG, "sgd hparams: initial_step must be >= 0");
+    return ZERO_OK;
+}
+
+// Bytes per stored gradient / parameter element of a storage format.
+int lp_bytes(zero_lp_dtype lp) { return lp == ZERO_FP32 ? 4 : 2; }
 
 // Leading elements to peel so that every listed address, advanced by that many
 // elements of size elt[k], is aligned to align[k] bytes; -1 if none below 8
@@ -220,52 +240,61 @@ const char* zero_status_str(zero_status s)
     return "ZERO_ERR_UNKNOWN";
 }
 
-zero_status zero_shard_init(const zero_shard_desc* desc, const zero_adam_hparams* hp,
-                            const zero_loss_scale_cfg* ls, zero_shard_t* out)
+}  // extern "C"
+
+// Validation and creation shared by the Adam and the SGD handles.  `need_m` /
+// `need_v`: whether exp_avg / exp_avg_sq must be given (1), must be NULL (-1)
+// or may be either (0).  On success the handle holds desc, S, opt and the loss
+// scale; the caller stores its hyper-parameters and t.
+static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m, int need_v,
+                               const zero_loss_scale_cfg* ls, const char* who,
+                               zero_shard_s** out)
 {
-    if (!desc || !out) return fail(ZERO_ERR_INVALID_ARG, "init: NULL desc or out");
     const zero_shard_desc& d = *desc;
-    if (d.psi < 1) return fail(ZERO_ERR_INVALID_ARG, "init: psi must be >= 1");
-    if (d.nd < 1) return fail(ZERO_ERR_INVALID_ARG, "init: nd must be >= 1");
-    if (d.rank < 0 || d.rank >= d.nd) return fail(ZERO_ERR_INVALID_ARG, "init: rank outside [0, nd)");
-    if (d.bucket_elems < 1) return fail(ZERO_ERR_INVALID_ARG, "init: bucket_elems must be >= 1");
-    if (d.lp != ZERO_FP16 && d.lp != ZERO_BF16)
-        return fail(ZERO_ERR_INVALID_ARG, "init: unknown lp dtype %d", (int)d.lp);
-    if (!d.master || !d.exp_avg || !d.exp_avg_sq || !d.grad_shard || !d.param_shard)
-        return fail(ZERO_ERR_INVALID_ARG, "init: NULL shard array");
-    const uintptr_t a32[3] = {(uintptr_t)d.master, (uintptr_t)d.exp_avg, (uintptr_t)d.exp_avg_sq};
-    const uintptr_t a16[2] = {(uintptr_t)d.grad_shard, (uintptr_t)d.param_shard};
-    for (uintptr_t a : a32)
-        if (a & 3u) return fail(ZERO_ERR_INVALID_ARG, "init: fp32 array not 4-byte aligned");
-    for (uintptr_t a : a16)
-        if (a & 1u) return fail(ZERO_ERR_INVALID_ARG, "init: 2-byte array not 2-byte aligned");
+    if (d.psi < 1) return fail(ZERO_ERR_INVALID_ARG, "%s: psi must be >= 1", who);
+    if (d.nd < 1) return fail(ZERO_ERR_INVALID_ARG, "%s: nd must be >= 1", who);
+    if (d.rank < 0 || d.rank >= d.nd) return fail(ZERO_ERR_INVALID_ARG, "%s: rank outside [0, nd)", who);
+    if (d.bucket_elems < 1) return fail(ZERO_ERR_INVALID_ARG, "%s: bucket_elems must be >= 1", who);
+    if (d.lp != ZERO_FP16 && d.lp != ZERO_BF16 && d.lp != ZERO_FP32)
+        return fail(ZERO_ERR_INVALID_ARG, "%s: unknown lp dtype %d", who, (int)d.lp);
+    const bool fp32 = d.lp == ZERO_FP32;
+    if (!d.master || !d.grad_shard) return fail(ZERO_ERR_INVALID_ARG, "%s: NULL master or grad_shard", who);
+    if (fp32 && d.param_shard)
+        return fail(ZERO_ERR_INVALID_ARG, "%s: param_shard must be NULL with fp32 storage", who);
+    if (!fp32 && !d.param_shard) return fail(ZERO_ERR_INVALID_ARG, "%s: NULL param_shard", who);
+    if ((need_m > 0 && !d.exp_avg) || (need_v > 0 && !d.exp_avg_sq))
+        return fail(ZERO_ERR_INVALID_ARG, "%s: NULL optimizer state array", who);
+    if ((need_m < 0 && d.exp_avg) || (need_v < 0 && d.exp_avg_sq))
+        return fail(ZERO_ERR_INVALID_ARG, "%s: this optimizer takes no %s", who,
+                    need_m < 0 && d.exp_avg ? "exp_avg" : "exp_avg_sq");
+    const int esz = lp_bytes(d.lp);
     const int64_t S = (d.psi + d.nd - 1) / d.nd;
-    {
-        const uintptr_t all[5] = {a32[0], a32[1], a32[2], a16[0], a16[1]};
-        const size_t len[5] = {(size_t)S * 4, (size_t)S * 4, (size_t)S * 4,
-                               (size_t)S * kLpBytes, (size_t)S * kLpBytes};
-        for (int i = 0; i < 5; ++i)
-            for (int j = i + 1; j < 5; ++j)
-                if (overlaps(all[i], len[i], all[j], len[j]))
-                    return fail(ZERO_ERR_INVALID_ARG, "init: shard arrays %d and %d overlap", i, j);
-    }
-    zero_status st = check_hparams(hp);
-    if (st != ZERO_OK) return st;
-    st = check_ls(ls);
+    // every given array: address, element size, bytes
+    const void* arr[5] = {d.master, d.exp_avg, d.exp_avg_sq, d.grad_shard, d.param_shard};
+    const int el[5] = {4, 4, 4, esz, esz};
+    for (int i = 0; i < 5; ++i)
+        if (arr[i] && ((uintptr_t)arr[i] % (uintptr_t)el[i]) != 0)
+            return fail(ZERO_ERR_INVALID_ARG, "%s: shard array %d not %d-byte aligned", who, i, el[i]);
+    for (int i = 0; i < 5; ++i)
+        for (int j = i + 1; j < 5; ++j)
+            if (arr[i] && arr[j] &&
+                overlaps((uintptr_t)arr[i], (size_t)S * el[i], (uintptr_t)arr[j], (size_t)S * el[j]))
+                return fail(ZERO_ERR_INVALID_ARG, "%s: shard arrays %d and %d overlap", who, i, j);
+    zero_status st = check_ls(ls);
     if (st != ZERO_OK) return st;
 
     // One fp64 partial per reduce workgroup of a step.  A bucket of len
     // elements uses at most len/per + 2 workgroups, per being the smaller of
     // the element-wise and the vector kernels' elements per workgroup (plus a
     // ragged end), and the stand-alone scan needs no more.
-    const int64_t per = zk::kScalarElemsPerBlock < zk::kRedElemsPerBlock
-                            ? zk::kScalarElemsPerBlock : zk::kRedElemsPerBlock;
+    const int64_t per = zk::kScalarElemsPerBlock < zk::kRedElemsPerBlockMin
+                            ? zk::kScalarElemsPerBlock : zk::kRedElemsPerBlockMin;
     const int64_t nbuckets = (S + d.bucket_elems - 1) / d.bucket_elems;
     const int64_t nslots = S / per + 2 * nbuckets + 4;
     if (nslots > (int64_t(1) << 25))
         return fail(ZERO_ERR_UNSUPPORTED,
-                    "init: %lld buckets of %lld elements need %lld partial slots (limit 2^25); "
-                    "use a larger bucket_elems", (long long)nbuckets, (long long)d.bucket_elems,
+                    "%s: %lld buckets of %lld elements need %lld partial slots (limit 2^25); "
+                    "use a larger bucket_elems", who, (long long)nbuckets, (long long)d.bucket_elems,
                     (long long)nslots);
 
     int dev = -1;
@@ -277,9 +306,9 @@ zero_status zero_shard_init(const zero_shard_desc* desc, const zero_adam_hparams
     h->device = dev;
     h->d = d;
     h->S = S;
-    h->hp = *hp;
+    h->opt = opt;
+    h->esz = esz;
     h->ls = *ls;
-    h->t = hp->initial_step;
     h->scale = ls->init_scale;
     h->good_steps = 0;
     h->nslots = nslots;
@@ -323,10 +352,46 @@ zero_status zero_shard_init(const zero_shard_desc* desc, const zero_adam_hparams
         (void)hipGetLastError();
         return fail(ZERO_ERR_HIP, "init: hipEventCreate: %s", hipGetErrorString(e));
     }
-    {
-        std::lock_guard<std::mutex> lk(g_live_mu);
-        g_live.insert(h);
-    }
+    *out = h;
+    return ZERO_OK;
+}
+
+static void publish(zero_shard_s* h)
+{
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    g_live.insert(h);
+}
+
+extern "C" {
+
+zero_status zero_shard_init(const zero_shard_desc* desc, const zero_adam_hparams* hp,
+                            const zero_loss_scale_cfg* ls, zero_shard_t* out)
+{
+    if (!desc || !out) return fail(ZERO_ERR_INVALID_ARG, "init: NULL desc or out");
+    zero_status st = check_hparams(hp);
+    if (st != ZERO_OK) return st;
+    zero_shard_s* h = nullptr;
+    st = init_common(desc, kOptAdam, 1, 1, ls, "init", &h);
+    if (st != ZERO_OK) return st;
+    h->hp = *hp;
+    h->t = hp->initial_step;
+    publish(h);
+    *out = h;
+    return ZERO_OK;
+}
+
+zero_status zero_shard_init_sgd(const zero_shard_desc* desc, const zero_sgd_hparams* hp,
+                                const zero_loss_scale_cfg* ls, zero_shard_t* out)
+{
+    if (!desc || !out) return fail(ZERO_ERR_INVALID_ARG, "init_sgd: NULL desc or out");
+    zero_status st = check_sgd_hparams(hp, desc->exp_avg != nullptr);
+    if (st != ZERO_OK) return st;
+    zero_shard_s* h = nullptr;
+    st = init_common(desc, kOptSgd, 0, -1, ls, "init_sgd", &h);
+    if (st != ZERO_OK) return st;
+    h->sgd = *hp;
+    h->t = hp->initial_step;
+    publish(h);
     *out = h;
     return ZERO_OK;
 }
@@ -360,8 +425,9 @@ zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int3
                     ZERO_MAX_CONTRIB);
     for (int r = 0; r < n_contrib; ++r) {
         if (!contribs[r]) return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: contribution %d is NULL", r);
-        if ((uintptr_t)contribs[r] & 1u)
-            return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: contribution %d not 2-byte aligned", r);
+        if ((uintptr_t)contribs[r] % (uintptr_t)h->esz != 0)
+            return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: contribution %d not %d-byte aligned", r,
+                        h->esz);
     }
     if (bucket_len < 1) return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: bucket_len must be >= 1");
     if (bucket_off < 0 || bucket_off >= h->S || bucket_len > h->S - bucket_off)
@@ -388,16 +454,17 @@ zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int3
     for (int r = 0; r < n_contrib; ++r) {
         L.c.p[r] = contribs[r];
         addr[r] = (uintptr_t)contribs[r];
-        elt[r] = 2;
+        elt[r] = h->esz;
         align[r] = 16;
     }
-    char* out = static_cast<char*>(h->d.grad_shard) + bucket_off * 2;
+    char* out = static_cast<char*>(h->d.grad_shard) + bucket_off * h->esz;
     addr[n_contrib] = (uintptr_t)out;
-    elt[n_contrib] = 2;
+    elt[n_contrib] = h->esz;
     align[n_contrib] = 16;
     L.out = out;
     L.n = bucket_len;
-    split(bucket_len, common_head(addr, elt, align, n_contrib + 1), 8, &L.head, &L.nvec, &L.vec_ok);
+    const int W = zk::run_width(h->d.lp);
+    split(bucket_len, common_head(addr, elt, align, n_contrib + 1), W, &L.head, &L.nvec, &L.vec_ok);
     L.R = n_contrib;
     L.lp = (int32_t)h->d.lp;
     L.inv_r = (float)(1.0 / (double)n_contrib);
@@ -405,7 +472,7 @@ zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int3
     L.partial = h->partial;
     L.slot_base = h->phase == kIdle ? 0 : h->slot_cursor;
     L.lds_reserve = h->lds_reduce;
-    const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok);
+    const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W);
     if (L.slot_base + blocks > h->nslots)
         return fail(ZERO_ERR_UNSUPPORTED, "bucket_reduce: partial slots exhausted");
     hipError_t e = zk::launch_reduce(L, static_cast<hipStream_t>(stream));
@@ -428,10 +495,11 @@ static zero_status launch_check(zero_shard_s* h, hipStream_t s, const char* who)
         zk::ScanLaunch L;
         std::memset(&L, 0, sizeof(L));
         const uintptr_t a = (uintptr_t)h->d.grad_shard;
-        const int el = 2, al = 16;
+        const int el = h->esz, al = 16;
+        const int W = zk::run_width(h->d.lp);
         L.g = h->d.grad_shard;
         L.n = h->S;
-        split(h->S, common_head(&a, &el, &al, 1), 8, &L.head, &L.nvec, &L.vec_ok);
+        split(h->S, common_head(&a, &el, &al, 1), W, &L.head, &L.nvec, &L.vec_ok);
         L.lp = (int32_t)h->d.lp;
         L.inv_scale = (float)(1.0 / h->scale);
         L.partial = h->partial;
@@ -439,7 +507,7 @@ static zero_status launch_check(zero_shard_s* h, hipStream_t s, const char* who)
         L.lds_reserve = h->lds_reduce;
         e = zk::launch_scan(L, s);
         if (e != hipSuccess) return hip_fail(e, who);
-        h->slot_cursor = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok);
+        h->slot_cursor = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W);
     }
     e = zk::launch_finalize(h->partial, h->slot_cursor, h->level1, h->result, s);
     if (e != hipSuccess) return hip_fail(e, who);
@@ -491,11 +559,12 @@ static zero_status launch_adam_step(zero_shard_s* h, const zero_adam_hparams& hp
     a.v = h->d.exp_avg_sq;
     a.param = h->d.param_shard;
     a.n = h->S;
-    const uintptr_t addr[5] = {(uintptr_t)a.grad, (uintptr_t)a.param, (uintptr_t)a.master,
-                               (uintptr_t)a.m, (uintptr_t)a.v};
-    const int elt[5] = {2, 2, 4, 4, 4};
-    const int align[5] = {8, 8, 16, 16, 16};
-    split(h->S, common_head(addr, elt, align, 5), 4, &a.head, &a.ngroups, &a.vec_ok);
+    // groups of 4: 16-byte aligned in the fp32 arrays, 4*esz in the stored ones
+    const uintptr_t addr[5] = {(uintptr_t)a.master, (uintptr_t)a.m, (uintptr_t)a.v,
+                               (uintptr_t)a.grad, (uintptr_t)a.param};
+    const int elt[5] = {4, 4, 4, h->esz, h->esz};
+    const int align[5] = {16, 16, 16, 4 * h->esz, 4 * h->esz};
+    split(h->S, common_head(addr, elt, align, a.param ? 5 : 4), 4, &a.head, &a.ngroups, &a.vec_ok);
     a.lds_reserve = h->lds_adam;
     a.lp = (int32_t)h->d.lp;
     a.b1 = (float)hp.beta1;
@@ -516,6 +585,43 @@ static zero_status launch_adam_step(zero_shard_s* h, const zero_adam_hparams& hp
     *pw1_out = pw1;
     *pw2_out = pw2;
     *same_betas_out = same_betas;
+    return ZERO_OK;
+}
+
+// Launch SGD for applied step t + 1 with hyper-parameters hp; gate as in
+// launch_adam_step.
+static zero_status launch_sgd_step(zero_shard_s* h, const zero_sgd_hparams& hp, hipStream_t s,
+                                   const zk::CheckResult* gate, const char* who)
+{
+    zk::SgdLaunch a;
+    std::memset(&a, 0, sizeof(a));
+    a.grad = h->d.grad_shard;
+    a.master = h->d.master;
+    a.mom = h->d.exp_avg;
+    a.param = h->d.param_shard;
+    a.n = h->S;
+    uintptr_t addr[4];
+    int elt[4], align[4], cnt = 0;
+    const void* arr[4] = {a.master, a.mom, a.grad, a.param};
+    const int el[4] = {4, 4, h->esz, h->esz};
+    for (int k = 0; k < 4; ++k) {
+        if (!arr[k]) continue;
+        addr[cnt] = (uintptr_t)arr[k];
+        elt[cnt] = el[k];
+        align[cnt] = 4 * el[k];
+        ++cnt;
+    }
+    split(h->S, common_head(addr, elt, align, cnt), 4, &a.head, &a.ngroups, &a.vec_ok);
+    a.lds_reserve = h->lds_adam;
+    a.lp = (int32_t)h->d.lp;
+    a.lr = (float)hp.lr;
+    a.mu = (float)hp.momentum;
+    a.wd = (float)hp.weight_decay;
+    a.has_wd = a.wd != 0.0f;
+    a.inv_scale = (float)(1.0 / h->scale);
+    a.gate = gate;
+    hipError_t e = zk::launch_sgd(a, s);
+    if (e != hipSuccess) return hip_fail(e, who);
     return ZERO_OK;
 }
 
@@ -574,6 +680,7 @@ zero_status zero_adam_step(zero_shard_t h, const zero_adam_hparams* hp_in, void*
                            zero_step_info* out)
 {
     if (!live(h)) return fail(ZERO_ERR_STATE, "adam_step: not a live handle");
+    if (h->opt != kOptAdam) return fail(ZERO_ERR_STATE, "adam_step: handle was created for SGD");
     if (h->phase != kChecked)
         return fail(ZERO_ERR_STATE, "adam_step: zero_overflow_check has not completed this step");
     if (hp_in) {
@@ -617,6 +724,7 @@ zero_status zero_overflow_merge(zero_shard_t h, int32_t global_overflow, double 
 zero_status zero_adam_step_gated(zero_shard_t h, const zero_adam_hparams* hp_in, void* stream)
 {
     if (!live(h)) return fail(ZERO_ERR_STATE, "adam_step_gated: not a live handle");
+    if (h->opt != kOptAdam) return fail(ZERO_ERR_STATE, "adam_step_gated: handle was created for SGD");
     if (h->phase == kChecked || h->phase == kPending)
         return fail(ZERO_ERR_STATE, "adam_step_gated: step already checked or pending");
     if (h->phase == kReducing && h->covered != h->S)
@@ -643,6 +751,63 @@ zero_status zero_adam_step_gated(zero_shard_t h, const zero_adam_hparams* hp_in,
         h->slot_cursor = cursor_before;
         return st;
     }
+    h->phase = kPending;
+    return ZERO_OK;
+}
+
+zero_status zero_sgd_step(zero_shard_t h, const zero_sgd_hparams* hp_in, void* stream,
+                          zero_step_info* out)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "sgd_step: not a live handle");
+    if (h->opt != kOptSgd) return fail(ZERO_ERR_STATE, "sgd_step: handle was created for Adam");
+    if (h->phase != kChecked)
+        return fail(ZERO_ERR_STATE, "sgd_step: zero_overflow_check has not completed this step");
+    if (hp_in) {
+        zero_status st = check_sgd_hparams(hp_in, h->d.exp_avg != nullptr);
+        if (st != ZERO_OK) return st;
+    }
+    const zero_sgd_hparams& hp = hp_in ? *hp_in : h->sgd;
+    zero_step_info info = h->check;
+    if (!info.overflow) {
+        zero_status st = launch_sgd_step(h, hp, static_cast<hipStream_t>(stream), nullptr,
+                                         "sgd_step: launch");
+        if (st != ZERO_OK) return st;
+    }
+    commit_step(h, &info, 1.0, 1.0, false);
+    if (out) *out = info;
+    return ZERO_OK;
+}
+
+zero_status zero_sgd_step_gated(zero_shard_t h, const zero_sgd_hparams* hp_in, void* stream)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "sgd_step_gated: not a live handle");
+    if (h->opt != kOptSgd) return fail(ZERO_ERR_STATE, "sgd_step_gated: handle was created for Adam");
+    if (h->phase == kChecked || h->phase == kPending)
+        return fail(ZERO_ERR_STATE, "sgd_step_gated: step already checked or pending");
+    if (h->phase == kReducing && h->covered != h->S)
+        return fail(ZERO_ERR_STATE, "sgd_step_gated: buckets cover [0, %lld) of [0, %lld)",
+                    (long long)h->covered, (long long)h->S);
+    if (hp_in) {
+        zero_status st = check_sgd_hparams(hp_in, h->d.exp_avg != nullptr);
+        if (st != ZERO_OK) return st;
+    }
+    const zero_sgd_hparams& hp = hp_in ? *hp_in : h->sgd;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Phase before = h->phase;
+    const int64_t cursor_before = h->slot_cursor;
+    zero_status st = launch_check(h, s, "sgd_step_gated: check");
+    if (st == ZERO_OK) {
+        hipError_t e = hipEventRecord(h->result_ready, s);
+        if (e != hipSuccess) st = hip_fail(e, "sgd_step_gated: event");
+    }
+    if (st == ZERO_OK) st = launch_sgd_step(h, hp, s, h->result, "sgd_step_gated: launch");
+    if (st != ZERO_OK) {
+        h->phase = before;
+        h->slot_cursor = cursor_before;
+        return st;
+    }
+    h->pend_pw1 = h->pend_pw2 = 1.0;
+    h->pend_same_betas = false;
     h->phase = kPending;
     return ZERO_OK;
 }

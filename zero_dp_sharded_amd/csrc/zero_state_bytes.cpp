@@ -22,7 +22,7 @@ zero_status ledger(int64_t psi, int32_t nd, int32_t n_contrib, int64_t bucket_el
                    zero_lp_dtype lp, int32_t b_bytes, int32_t k_optim, zero_state_bytes_t* out)
 {
     if (!out || psi < 1 || nd < 1 || n_contrib < 1 || n_contrib > ZERO_MAX_CONTRIB ||
-        bucket_elems < 1 || (lp != ZERO_FP16 && lp != ZERO_BF16) ||
+        bucket_elems < 1 || (lp != ZERO_FP16 && lp != ZERO_BF16 && lp != ZERO_FP32) ||
         (b_bytes != 2 && b_bytes != 4) || k_optim < 0)
         return ZERO_ERR_INVALID_ARG;
     const int64_t shard = psi / nd + (psi % nd != 0 ? 1 : 0);
@@ -32,10 +32,13 @@ zero_status ledger(int64_t psi, int32_t nd, int32_t n_contrib, int64_t bucket_el
     r.bytes_master = shard * 4;
     r.bytes_m = shard * 4;
     r.bytes_v = shard * 4;
-    r.bytes_grad = shard * 2;
-    r.bytes_param = shard * 2;
+    // Adam shard of this storage format: 4-byte storage keeps the parameter in
+    // the fp32 master itself (no 2-byte copy)
+    const int64_t esz = lp == ZERO_FP32 ? 4 : 2;
+    r.bytes_grad = shard * esz;
+    r.bytes_param = lp == ZERO_FP32 ? 0 : shard * 2;
     r.bytes_shard_total = r.bytes_master + r.bytes_m + r.bytes_v + r.bytes_grad + r.bytes_param;
-    r.bytes_staging = (int64_t)n_contrib * bucket_elems * 2;
+    r.bytes_staging = (int64_t)n_contrib * bucket_elems * esz;
 
     const double P = (double)psi;
     const double N = (double)nd;

@@ -9,7 +9,8 @@ the same values by copying them to the host.
 
 Workloads follow the pages' model sizes (GPT-2 1.5B, 7.5B, 13B, 128B; the
 "AI论文陪读·ZeRO" section 01 and the blog.vllbc.top ZeRO/DeepSpeed worked
-examples and Table 1), with synthetic values in place of real gradients:
+examples and Table 1; the fp32 SGD cases of that page's extension group C),
+with synthetic values in place of real gradients:
 gradients N(0, 1e-3) per contribution times the loss scale, master weights
 N(0, 0.02).  N(0, s) means standard deviation s.
 """
@@ -29,7 +30,7 @@ class Workload:
     rank: int
     R: int
     bucket_elems: int
-    lp: str                   # "fp16" or "bf16"
+    lp: str                   # "fp16", "bf16" or "fp32" (4-byte storage)
     scale: float
     dynamic: int
     lr: float
@@ -44,6 +45,8 @@ class Workload:
     beta1: float = 0.9
     beta2: float = 0.999
     eps: float = 1e-8
+    opt: str = "adam"                     # "adam" or "sgd"
+    momentum: float = 0.0                 # SGD: > 0 keeps a momentum buffer
 
     @property
     def shard(self) -> int:
@@ -55,7 +58,16 @@ class Workload:
 
     @property
     def torch_lp(self):
-        return torch.float16 if self.lp == "fp16" else torch.bfloat16
+        return {"fp16": torch.float16, "bf16": torch.bfloat16, "fp32": torch.float32}[self.lp]
+
+    @property
+    def has_m(self) -> bool:
+        """Whether the shard keeps a first-moment / momentum array."""
+        return self.opt == "adam" or self.momentum > 0.0
+
+    @property
+    def has_v(self) -> bool:
+        return self.opt == "adam"
 
 
 WORKLOADS = {
@@ -78,6 +90,17 @@ WORKLOADS = {
     "128b": Workload("128B, Nd=64, shard 2.0e9, R=4, C_B 200M, fp16, scale 4096",
                      psi=128_000_000_000, nd=64, rank=0, R=4, bucket_elems=200_000_000,
                      lp="fp16", scale=4096.0, dynamic=1, lr=6e-5, weight_decay=0.1, steps=5),
+    # extension group C of the blog.vllbc.top page: fp32 storage (b = 4)
+    "c1_7.5b_sgdm": Workload("C1: 7.5B, Nd=64, shard 117,187,500, R=8, C_B 50M, fp32 SGD with "
+                             "momentum 0.9, static scale 1",
+                             psi=7_500_000_000, nd=64, rank=0, R=8, bucket_elems=50_000_000,
+                             lp="fp32", scale=1.0, dynamic=0, lr=1e-2, weight_decay=1e-4,
+                             steps=10, opt="sgd", momentum=0.9),
+    "c2_1.5b_sgd": Workload("C2: GPT-2 1.5B, Nd=8, shard 187.5M, R=8, C_B 50M, fp32 plain SGD, "
+                            "static scale 1",
+                            psi=1_500_000_000, nd=8, rank=0, R=8, bucket_elems=50_000_000,
+                            lp="fp32", scale=1.0, dynamic=0, lr=1e-2, weight_decay=0.0,
+                            steps=10, opt="sgd"),
 }
 
 
@@ -164,7 +187,8 @@ def contribution_seed(seed: int, step: int, r: int) -> int:
 def fill_contribs(w: Workload, bufs: List[torch.Tensor], step: int, scale: float,
                   seed: int = 0) -> None:
     """Fill the R contribution buffers of `step` (0-based) with
-    rne_lp(N(0, grad_std) * scale); at the workload's inject step,
+    N(0, grad_std) * scale rounded to the buffers' dtype; at the workload's
+    inject step,
     contribution 0 gets +inf at element n/2 + 1 of its n elements."""
     for r, b in enumerate(bufs):
         _fill_normal(b, w.grad_std * scale, contribution_seed(seed, step, r))
