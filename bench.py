@@ -14,6 +14,10 @@ Prints one JSON line: params/s of the shard (Adam-updated parameters per
 second), the step time, the dominant kernel's achieved HBM bandwidth against
 the 8 TB/s peak (HIP events on the launch stream), and the CPU oracle timed on
 a bounded sample of the same workload.
+
+--workload picks another shape, among them the fp32-storage SGD cases of the
+blog.vllbc.top page's extension group C (c1_7.5b_sgdm: SGD with momentum;
+c2_1.5b_sgd: plain SGD); the update kernel is then the SGD one.
 """
 from __future__ import annotations
 
@@ -29,7 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, AMD public spec
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_adam_128b.json")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "zero_dp_sharded_amd", "csrc", "zero_kernels.hip")
 
 
@@ -38,11 +42,11 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(per_launch_elems: int):
-    """HBM bytes per Adam launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
+def measured_traffic(workload: str, per_launch_elems: int):
+    """HBM bytes per update launch from the committed rocprofv3 counter summary
+    of this workload, if it was taken on the current kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(PROFILES, f"traffic_{workload}.json")) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -84,13 +88,27 @@ def copy_ceiling(torch, nbytes: int, reps: int):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def update_bytes_per_elem(w) -> int:
+    """Algorithmic HBM bytes of the update per shard element: the stored
+    gradient read, each fp32 state array (master, then m / momentum and v where
+    the optimizer keeps them) read and written, and the 2-byte parameter
+    written (absent with fp32 storage, where the master is the parameter)."""
+    esz = 4 if w.lp == "fp32" else 2
+    fp32_arrays = 1 + int(w.has_m) + int(w.has_v)
+    return esz + 8 * fp32_arrays + (0 if w.lp == "fp32" else 2)
+
+
 def cpu_baseline(w, state_host, contribs_host, bucket_elems):
     import oracle
-    hp = oracle.AdamHP(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
-                       weight_decay=w.weight_decay)
+    if w.opt == "sgd":
+        hp = oracle.SGDHP(lr=w.lr, momentum=w.momentum, weight_decay=w.weight_decay)
+    else:
+        hp = oracle.AdamHP(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                           weight_decay=w.weight_decay)
     ls = oracle.LossScale(init_scale=w.scale, dynamic=w.dynamic)
     master, m, v = state_host
-    st = oracle.new_state(oracle.FP16 if w.lp == "fp16" else oracle.BF16, master, m, v, hp, ls)
+    lp = {"fp16": oracle.FP16, "bf16": oracle.BF16, "fp32": oracle.FP32}[w.lp]
+    st = oracle.new_state(lp, master, m, v, hp, ls)
     t0 = time.perf_counter()
     oracle.step(st, contribs_host, bucket_elems, hp, ls)
     dt = time.perf_counter() - t0
@@ -142,8 +160,12 @@ def main() -> int:
     print(f"[bench] workload {w.name}: S={S} R={R} C_B={cb}", file=sys.stderr, flush=True)
 
     master, m, v = synth.init_state(w, dev, seed=0)
+    m = m if w.has_m else None
+    v = v if w.has_v else None
     grad = torch.zeros(S, dtype=lp_t, device=dev)
-    param = master.to(lp_t)
+    param = None if w.lp == "fp32" else master.to(lp_t)
+    esz = grad.element_size()
+    sgd = w.opt == "sgd"
     if args.mode == "pos":
         # the caller's slice of the all-reduced gradient: one seeded draw
         bufs = []
@@ -154,11 +176,18 @@ def main() -> int:
     torch.cuda.synchronize()
     print("[bench] inputs resident", file=sys.stderr, flush=True)
 
-    hp = zs.AdamHParams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
-                        weight_decay=w.weight_decay)
     ls = zs.LossScaleCfg(init_scale=w.scale, dynamic=w.dynamic)
-    h = zs.zero_shard_init(master, m, v, grad, param, psi=w.psi, nd=w.nd, rank=w.rank,
-                           bucket_elems=cb, hp=hp, ls=ls)
+    if sgd:
+        hp = zs.SGDHParams(lr=w.lr, momentum=w.momentum, weight_decay=w.weight_decay)
+        h = zs.zero_shard_init_sgd(master, m, grad, param, psi=w.psi, nd=w.nd, rank=w.rank,
+                                   bucket_elems=cb, hp=hp, ls=ls)
+        update_gated, update_sync = zs.zero_sgd_step_gated, zs.zero_sgd_step
+    else:
+        hp = zs.AdamHParams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                            weight_decay=w.weight_decay)
+        h = zs.zero_shard_init(master, m, v, grad, param, psi=w.psi, nd=w.nd, rank=w.rank,
+                               bucket_elems=cb, hp=hp, ls=ls)
+        update_gated, update_sync = zs.zero_adam_step_gated, zs.zero_adam_step
     stream = torch.cuda.current_stream()
     ptrs = [b.data_ptr() for b in bufs]
     offs = [(off, min(cb, S - off)) for off in range(0, S, cb)]
@@ -170,7 +199,7 @@ def main() -> int:
             ev["r"][0].record(stream)
         if args.mode == "pos_g":
             for off, ln in offs:
-                zs.zero_bucket_reduce(h, [p + 2 * off for p in ptrs], off, ln, stream)
+                zs.zero_bucket_reduce(h, [p + esz * off for p in ptrs], off, ln, stream)
         if ev is not None:
             ev["r"][1].record(stream)
         if flow == "gated":
@@ -178,14 +207,14 @@ def main() -> int:
             # host waits only for the result copy
             if ev is not None:
                 ev["a"][0].record(stream)
-            zs.zero_adam_step_gated(h, None, stream)
+            update_gated(h, None, stream)
             if ev is not None:
                 ev["a"][1].record(stream)
             return zs.zero_step_resolve(h)
         info = zs.zero_overflow_check(h, stream)
         if ev is not None:
             ev["a"][0].record(stream)
-        zs.zero_adam_step(h, None, stream)
+        update_sync(h, None, stream)
         if ev is not None:
             ev["a"][1].record(stream)
         return info
@@ -227,26 +256,31 @@ def main() -> int:
     print(f"[bench] plain copy of {copy_bytes} bytes: {copy_gbs:.0f} GB/s", file=sys.stderr,
           flush=True)
 
-    adam_bytes = 28 * S                      # grad 2 + master/m/v 12 read; 12 + param 2 written
-    reduce_bytes = (2 * R + 2) * S
+    adam_bytes = update_bytes_per_elem(w) * S
+    reduce_bytes = (R + 1) * esz * S           # R contributions read, the stored gradient written
     achieved = adam_bytes / (adam_avg * 1e-3) / 1e9
     step_bytes = adam_bytes + reduce_bytes
-    traffic = measured_traffic(S)
+    traffic = measured_traffic(args.workload, S)
 
     cpu = None
     if args.cpu_sample > 0 and args.mode == "pos_g":
         n = min(args.cpu_sample, S)
-        state_host = tuple(t[:n].cpu().numpy() for t in (master, m, v))
-        contribs_host = [b[:n].view(torch.int16).cpu().numpy().view(np.uint16) for b in bufs]
+        state_host = tuple(None if t is None else t[:n].cpu().numpy() for t in (master, m, v))
+        if w.lp == "fp32":
+            contribs_host = [b[:n].cpu().numpy() for b in bufs]
+        else:
+            contribs_host = [b[:n].view(torch.int16).cpu().numpy().view(np.uint16) for b in bufs]
         rate, dt = cpu_baseline(w, state_host, contribs_host, cb)
         cpu = {"value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
-               "sample": f"one full step (reduce of {R} contributions, flag/norm, Adam) on the "
+               "sample": f"one full step (reduce of {R} contributions, flag/norm, "
+                         f"{'SGD' if sgd else 'Adam'}) on the "
                          f"first {n} elements of the same shard; {dt:.1f} s single-threaded"}
         del state_host, contribs_host
     zs.zero_shard_destroy(h)
 
     out = {
-        "metric": "Adam-updated params/sec per rank shard + achieved HBM GB/s vs MI355X peak",
+        "metric": ("SGD" if sgd else "Adam") + "-updated params/sec per rank shard + achieved "
+                  "HBM GB/s vs MI355X peak",
         "value": S / (ms_step * 1e-3),
         "unit": "params/s",
         "n_gpus": 1,
@@ -263,8 +297,9 @@ def main() -> int:
                    "mode": args.mode, "psi": w.psi, "nd": w.nd, "rank": w.rank,
                    "shard_elems": S, "contributions": R if args.mode == "pos_g" else 0,
                    "bucket_elems": cb,
-                   "storage": w.lp, "loss_scale": w.scale, "lr": w.lr,
-                   "weight_decay": w.weight_decay},
+                   "storage": w.lp, "optimizer": (f"sgd(momentum={w.momentum})" if sgd
+                                                   else "adamw"),
+                   "loss_scale": w.scale, "lr": w.lr, "weight_decay": w.weight_decay},
         "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
         "copy_ceiling_gbs": copy_gbs,
         "step_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -272,11 +307,13 @@ def main() -> int:
                        "reduce_all_buckets": red_avg,
                        "reduce_gbs": (reduce_bytes / (red_avg * 1e-3) / 1e9
                                       if args.mode == "pos_g" else None)},
-        "flow": "device-gated check + Adam (zero_adam_step_gated / zero_step_resolve)",
+        "flow": ("device-gated check + update (zero_sgd_step_gated / zero_step_resolve)" if sgd
+                 else "device-gated check + Adam (zero_adam_step_gated / zero_step_resolve)"),
         "ms_per_step_sync_check_flow": ms_sync,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "adam_vec_kernel<fp16, decoupled wd>",
+                     "kernel": (f"sgd_vec_kernel<{w.lp}, momentum={int(w.has_m)}>" if sgd
+                                else f"adam_vec_kernel<{w.lp}, decoupled wd>"),
                      "algorithmic_bytes_per_launch": adam_bytes,
                      "launch_ms": adam_avg,
                      "timing": "HIP events around the gated Adam enqueue (includes the "

@@ -191,7 +191,7 @@ zero_status zero_state_bytes_ex(int64_t psi, int32_t nd, int32_t n_contrib,
 /*
  * Create a handle bound to the current device.  Copies *desc, *hp and *ls.
  * Allocates a device workspace for the check's per-workgroup partials, 8 bytes
- * per 2048 shard elements plus 16 bytes per bucket plus 8 KiB (7.8 MB for a
+ * per 1024 shard elements plus 16 bytes per bucket plus 8 KiB (15.6 MB for a
  * 2e9-element shard), and 64 bytes of pinned host memory; touches none of the
  * caller's arrays.
  * Errors: INVALID_ARG (NULL argument or pointer in desc, psi < 1, nd < 1, rank

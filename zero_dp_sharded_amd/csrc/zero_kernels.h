@@ -11,7 +11,9 @@ constexpr int kMaxContrib = 64;
 
 // Reduce / scan: 256 lanes per workgroup, each lane two 16-byte runs (8
 // two-byte or 4 fp32 elements; each load instruction of a wave covers 1 KiB
-// contiguously); residency capped at 4 workgroups (16 waves) per CU.
+// contiguously), one run when a reduce has 8 or more contributions (its loads
+// already keep enough bytes in flight); residency capped at 4 workgroups (16
+// waves) per CU.
 // (The ZK_* macros exist only to build tuning variants; the defaults are the
 // measured optimum.)
 #ifndef ZK_RED_BLOCK
@@ -19,6 +21,9 @@ constexpr int kMaxContrib = 64;
 #endif
 #ifndef ZK_RED_RUNS
 #define ZK_RED_RUNS 2
+#endif
+#ifndef ZK_RED_RUNS_MANY
+#define ZK_RED_RUNS_MANY 1
 #endif
 #ifndef ZK_RED_PER_CU
 #define ZK_RED_PER_CU 4
@@ -32,17 +37,43 @@ constexpr int kMaxContrib = 64;
 #ifndef ZK_ADAM_PER_CU
 #define ZK_ADAM_PER_CU 10
 #endif
+#ifndef ZK_SGD_MOM_GROUPS
+#define ZK_SGD_MOM_GROUPS 1
+#endif
+#ifndef ZK_SGD_MOM_PER_CU
+#define ZK_SGD_MOM_PER_CU 16
+#endif
+#ifndef ZK_SGD_PLAIN_GROUPS
+#define ZK_SGD_PLAIN_GROUPS 1
+#endif
+#ifndef ZK_SGD_PLAIN_PER_CU
+#define ZK_SGD_PLAIN_PER_CU 24
+#endif
 constexpr int kRedBlock = ZK_RED_BLOCK;
 constexpr int kRedRuns = ZK_RED_RUNS;
-// elements one reduce workgroup covers with the narrowest run (fp32, 4 per run)
-constexpr int64_t kRedElemsPerBlockMin = (int64_t)kRedBlock * kRedRuns * 4;   // 2048
+constexpr int kRedRunsMany = ZK_RED_RUNS_MANY;   // runs per lane when R >= 8
+constexpr int kRedManyR = 8;
+// Runs per lane of a reduce with R contributions (a scan uses kRedRuns).
+inline int red_runs(int R) { return R >= kRedManyR ? kRedRunsMany : kRedRuns; }
+// elements one reduce or scan workgroup covers at the least (fp32, 4 per run)
+constexpr int64_t kRedElemsPerBlockMin =
+    (int64_t)kRedBlock * (kRedRuns < kRedRunsMany ? kRedRuns : kRedRunsMany) * 4;
 constexpr int kRedPerCU = ZK_RED_PER_CU;
-// Adam and SGD: one wave (64 lanes) per workgroup, each lane one group of 4
-// elements; residency capped at 10 workgroups (10 waves) per CU.
+// Adam: one wave (64 lanes) per workgroup, each lane one group of 4 elements;
+// residency capped at 10 workgroups (10 waves) per CU.
 constexpr int kAdamBlock = ZK_ADAM_BLOCK;
 constexpr int kAdamGroups = ZK_ADAM_GROUPS;
 constexpr int64_t kAdamElemsPerBlock = (int64_t)kAdamBlock * kAdamGroups * 4;  // 256
 constexpr int kAdamPerCU = ZK_ADAM_PER_CU;
+// SGD: one wave per workgroup, one group of 4 per lane like Adam, but it
+// streams fewer arrays (3 with a momentum buffer, 2 without), so it keeps more
+// waves resident to hold enough bytes in flight: 16 per CU with momentum, 24
+// without (measured on MI355X; 10 per CU left plain SGD at 64% of peak).
+constexpr int kSgdBlock = 64;
+constexpr int kSgdMomGroups = ZK_SGD_MOM_GROUPS;
+constexpr int kSgdMomPerCU = ZK_SGD_MOM_PER_CU;
+constexpr int kSgdPlainGroups = ZK_SGD_PLAIN_GROUPS;
+constexpr int kSgdPlainPerCU = ZK_SGD_PLAIN_PER_CU;
 // Element-wise kernels (unaligned heads and tails, or arrays without a common
 // alignment): 256 lanes, 8 elements per lane, lane-consecutive per step.
 constexpr int kScalarBlock = 256;
@@ -148,8 +179,9 @@ inline int run_width(int32_t lp) { return lp == 3 ? 4 : 8; }
 
 // Partial slots a reduce / scan of this layout writes: one per workgroup of
 // the vector kernel plus one per workgroup of the element-wise kernel.  W is
-// the run width of the storage format.
-int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok, int W);
+// the run width of the storage format, U the runs per lane (red_runs(R) for a
+// reduce, kRedRuns for a scan).
+int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok, int W, int U);
 
 hipError_t launch_reduce(const ReduceLaunch& L, hipStream_t s);
 hipError_t launch_scan(const ScanLaunch& L, hipStream_t s);

@@ -205,9 +205,9 @@ __device__ __forceinline__ void reduce_finish(const ReduceLaunch& L, int64_t vi,
                                               typename Fmt<LP>::FW acc, int& flag, double& ss)
 {
     using VW = typename Fmt<LP>::VW;
+    // (no pin_f32 here: hipcc converts the vector with plain conversions, which
+    // a codegen test checks, and the pin costs about 3% of the reduce)
     acc = acc * L.inv_r;
-#pragma unroll
-    for (int k = 0; k < Fmt<LP>::W; ++k) acc[k] = pin_f32(acc[k]);
     const VW o = __builtin_convertvector(acc, VW);
     st_nt<VW>(adv<LP>(L.out, L.head), vi, o);
     check_v<LP>(o, L.inv_scale, flag, ss);
@@ -228,19 +228,19 @@ __device__ __forceinline__ void reduce_s(const ReduceLaunch& L, int64_t e, int& 
 // runs per lane; lane l owns runs b*B*U + u*B + l.  Element offsets past `head`
 // are multiples of W, so contribution and output pointers advanced by `head`
 // are 16-byte aligned and are indexed in units of runs.
-template <int LP, int RT>
+template <int LP, int RT, int U>
 __global__ __launch_bounds__(kRedBlock) void reduce_vec_kernel(ReduceLaunch L)
 {
     using VW = typename Fmt<LP>::VW;
     using FW = typename Fmt<LP>::FW;
     int flag = 0;
     double ss = 0.0;
-    const int64_t v0 = (int64_t)blockIdx.x * (kRedBlock * kRedRuns) + threadIdx.x;
-    if constexpr (RT > 0 && RT * kRedRuns <= 16) {
-        // every load of both runs in flight before the arithmetic
-        VW x[kRedRuns][RT];
+    const int64_t v0 = (int64_t)blockIdx.x * (kRedBlock * U) + threadIdx.x;
+    if constexpr (RT > 0 && RT * U <= 16) {
+        // every load of all U runs in flight before the arithmetic
+        VW x[U][RT];
 #pragma unroll
-        for (int u = 0; u < kRedRuns; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int64_t vi = v0 + u * kRedBlock;
             if (vi < L.nvec) {
 #pragma unroll
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kRedBlock) void reduce_vec_kernel(ReduceLaunch L)
             }
         }
 #pragma unroll
-        for (int u = 0; u < kRedRuns; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int64_t vi = v0 + u * kRedBlock;
             if (vi < L.nvec) {
                 FW acc = (FW)(0.f);
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kRedBlock) void reduce_vec_kernel(ReduceLaunch L)
             }
         }
     } else {
-        for (int u = 0; u < kRedRuns; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int64_t vi = v0 + u * kRedBlock;
             if (vi >= L.nvec) break;
             FW acc = (FW)(0.f);
@@ -473,20 +473,20 @@ __device__ __forceinline__ void sgd_e(float graw, float& p, float& b, const SgdL
     p = p - a.lr * d;
 }
 
-// Same layout and load-first order as adam_vec_kernel.
-template <int LP, int MOM, int WD>
-__global__ __launch_bounds__(kAdamBlock) void sgd_vec_kernel(SgdLaunch a)
+// Same layout and load-first order as adam_vec_kernel, with G groups per lane.
+template <int LP, int MOM, int WD, int G>
+__global__ __launch_bounds__(kSgdBlock) void sgd_vec_kernel(SgdLaunch a)
 {
     using V4 = typename Fmt<LP>::V4;
     const void* gb = adv<LP>(a.grad, a.head);
     float* pb = a.master + a.head;
     float* bb = MOM ? a.mom + a.head : nullptr;
-    const int64_t q0 = (int64_t)blockIdx.x * (kAdamBlock * kAdamGroups) + threadIdx.x;
-    V4 g[kAdamGroups];
-    f4 p[kAdamGroups], b[kAdamGroups];
+    const int64_t q0 = (int64_t)blockIdx.x * (kSgdBlock * G) + threadIdx.x;
+    V4 g[G];
+    f4 p[G], b[G];
 #pragma unroll
-    for (int u = 0; u < kAdamGroups; ++u) {
-        const int64_t q = q0 + u * kAdamBlock;
+    for (int u = 0; u < G; ++u) {
+        const int64_t q = q0 + u * kSgdBlock;
         if (q < a.ngroups) {
             g[u] = ld_nt<V4>(gb, q);
             p[u] = ld_nt<f4>(pb, q);
@@ -495,8 +495,8 @@ __global__ __launch_bounds__(kAdamBlock) void sgd_vec_kernel(SgdLaunch a)
     }
     if (gated_off(a.gate)) return;
 #pragma unroll
-    for (int u = 0; u < kAdamGroups; ++u) {
-        const int64_t q = q0 + u * kAdamBlock;
+    for (int u = 0; u < G; ++u) {
+        const int64_t q = q0 + u * kSgdBlock;
         if (q < a.ngroups) {
             const f4 gf = __builtin_convertvector(g[u], f4);
             f4 pp = p[u];
@@ -556,17 +556,24 @@ Ranges ranges_of(int64_t n, int64_t head, int64_t body, int32_t vec_ok)
     return rg;
 }
 
+// U must equal red_runs(L.R): the dispatch sizes the grid with it.
 template <int LP>
 hipError_t reduce_vec_launch(const ReduceLaunch& L, unsigned grid, hipStream_t s)
 {
+    constexpr int A = kRedRuns, B = kRedRunsMany;
     const unsigned lds = L.lds_reserve;
     switch (L.R) {
-    case 1: reduce_vec_kernel<LP, 1><<<grid, kRedBlock, lds, s>>>(L); break;
-    case 2: reduce_vec_kernel<LP, 2><<<grid, kRedBlock, lds, s>>>(L); break;
-    case 4: reduce_vec_kernel<LP, 4><<<grid, kRedBlock, lds, s>>>(L); break;
-    case 8: reduce_vec_kernel<LP, 8><<<grid, kRedBlock, lds, s>>>(L); break;
-    case 16: reduce_vec_kernel<LP, 16><<<grid, kRedBlock, lds, s>>>(L); break;
-    default: reduce_vec_kernel<LP, 0><<<grid, kRedBlock, lds, s>>>(L); break;
+    case 1: reduce_vec_kernel<LP, 1, A><<<grid, kRedBlock, lds, s>>>(L); break;
+    case 2: reduce_vec_kernel<LP, 2, A><<<grid, kRedBlock, lds, s>>>(L); break;
+    case 4: reduce_vec_kernel<LP, 4, A><<<grid, kRedBlock, lds, s>>>(L); break;
+    case 8: reduce_vec_kernel<LP, 8, B><<<grid, kRedBlock, lds, s>>>(L); break;
+    case 16: reduce_vec_kernel<LP, 16, B><<<grid, kRedBlock, lds, s>>>(L); break;
+    default:
+        if (L.R >= kRedManyR)
+            reduce_vec_kernel<LP, 0, B><<<grid, kRedBlock, lds, s>>>(L);
+        else
+            reduce_vec_kernel<LP, 0, A><<<grid, kRedBlock, lds, s>>>(L);
+        break;
     }
     return hipGetLastError();
 }
@@ -575,7 +582,7 @@ template <int LP>
 hipError_t reduce_dispatch(const ReduceLaunch& L, hipStream_t s)
 {
     constexpr int W = Fmt<LP>::W;
-    const int64_t runs_per_block = (int64_t)kRedBlock * kRedRuns;
+    const int64_t runs_per_block = (int64_t)kRedBlock * red_runs(L.R);
     const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, runs_per_block) : 0;
     // consecutive launches of at most kMaxLaunchItems work-items; each starts
     // its runs and its partial slots where the previous one stopped
@@ -654,15 +661,16 @@ hipError_t adam_dispatch_wd(const AdamLaunch& a, hipStream_t s)
 template <int LP, int MOM, int WD>
 hipError_t sgd_dispatch(const SgdLaunch& a, hipStream_t s)
 {
-    const int64_t groups_per_block = (int64_t)kAdamBlock * kAdamGroups;
+    constexpr int G = MOM ? kSgdMomGroups : kSgdPlainGroups;
+    const int64_t groups_per_block = (int64_t)kSgdBlock * G;
     const int64_t vblocks = a.vec_ok ? ceil_div(a.ngroups, groups_per_block) : 0;
-    const int64_t max_blocks = kMaxLaunchItems / kAdamBlock;
+    const int64_t max_blocks = kMaxLaunchItems / kSgdBlock;
     for (int64_t b0 = 0; b0 < vblocks; b0 += max_blocks) {
         const int64_t nb = vblocks - b0 < max_blocks ? vblocks - b0 : max_blocks;
         SgdLaunch part = a;
         part.head = a.head + 4 * groups_per_block * b0;
         part.ngroups = a.ngroups - groups_per_block * b0;
-        sgd_vec_kernel<LP, MOM, WD><<<(unsigned)nb, kAdamBlock, a.lds_reserve, s>>>(part);
+        sgd_vec_kernel<LP, MOM, WD, G><<<(unsigned)nb, kSgdBlock, a.lds_reserve, s>>>(part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -683,10 +691,10 @@ hipError_t sgd_dispatch_kind(const SgdLaunch& a, hipStream_t s)
 
 }  // namespace
 
-int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok, int W)
+int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok, int W, int U)
 {
     (void)head;
-    const int64_t vblocks = vec_ok ? ceil_div(nvec, (int64_t)kRedBlock * kRedRuns) : 0;
+    const int64_t vblocks = vec_ok ? ceil_div(nvec, (int64_t)kRedBlock * U) : 0;
     const int64_t scalars = vec_ok ? n - (int64_t)W * nvec : n;
     return vblocks + ceil_div(scalars, kScalarElemsPerBlock);
 }

@@ -72,6 +72,8 @@ struct zero_shard_s {
     zk::CheckResult* host_result = nullptr;
     // dynamic LDS reserved per workgroup to cap residency per CU
     uint32_t lds_adam = 0;
+    uint32_t lds_sgd_mom = 0;
+    uint32_t lds_sgd_plain = 0;
     uint32_t lds_reduce = 0;
     // gated steps: event after the result copy, and the speculative update
     hipEvent_t result_ready = nullptr;
@@ -335,6 +337,8 @@ static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m,
         lds_blk = 64 * 1024;
     (void)hipGetLastError();
     h->lds_adam = lds_reserve_for(lds_cu, lds_blk, zk::kAdamPerCU);
+    h->lds_sgd_mom = lds_reserve_for(lds_cu, lds_blk, zk::kSgdMomPerCU);
+    h->lds_sgd_plain = lds_reserve_for(lds_cu, lds_blk, zk::kSgdPlainPerCU);
     h->lds_reduce = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCU);
     e = hipHostMalloc(reinterpret_cast<void**>(&h->host_result), 64, hipHostMallocDefault);
     if (e != hipSuccess) {
@@ -472,7 +476,7 @@ zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int3
     L.partial = h->partial;
     L.slot_base = h->phase == kIdle ? 0 : h->slot_cursor;
     L.lds_reserve = h->lds_reduce;
-    const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W);
+    const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::red_runs(L.R));
     if (L.slot_base + blocks > h->nslots)
         return fail(ZERO_ERR_UNSUPPORTED, "bucket_reduce: partial slots exhausted");
     hipError_t e = zk::launch_reduce(L, static_cast<hipStream_t>(stream));
@@ -507,7 +511,7 @@ static zero_status launch_check(zero_shard_s* h, hipStream_t s, const char* who)
         L.lds_reserve = h->lds_reduce;
         e = zk::launch_scan(L, s);
         if (e != hipSuccess) return hip_fail(e, who);
-        h->slot_cursor = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W);
+        h->slot_cursor = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::kRedRuns);
     }
     e = zk::launch_finalize(h->partial, h->slot_cursor, h->level1, h->result, s);
     if (e != hipSuccess) return hip_fail(e, who);
@@ -612,7 +616,7 @@ static zero_status launch_sgd_step(zero_shard_s* h, const zero_sgd_hparams& hp, 
         ++cnt;
     }
     split(h->S, common_head(addr, elt, align, cnt), 4, &a.head, &a.ngroups, &a.vec_ok);
-    a.lds_reserve = h->lds_adam;
+    a.lds_reserve = a.mom ? h->lds_sgd_mom : h->lds_sgd_plain;
     a.lp = (int32_t)h->d.lp;
     a.lr = (float)hp.lr;
     a.mu = (float)hp.momentum;

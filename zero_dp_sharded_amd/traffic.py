@@ -4,8 +4,9 @@
             and total duration per kernel), headed by the command that made it.
   traffic : two --pmc runs of bench.py (FETCH_SIZE, then WRITE_SIZE), each
             holding the plain copy kernel of known size and the step's kernels
-            -> HBM bytes per launch of each kernel, the counters scaled by what
-            they read for the copy (bytes moved / counter bytes), as JSON.
+            -> HBM bytes per launch of the update kernel (Adam or SGD) and of
+            the reduce, the counters scaled by what they read for the copy
+            (bytes moved / counter bytes), as JSON.
 
 The JSON carries a hash of the kernel source; bench.py uses its byte count
 only while the source is unchanged.
@@ -78,7 +79,8 @@ def traffic(args) -> int:
                                 "fetch_kib": cf, "write_kib": cw,
                                 "fetch_factor": ffac, "write_factor": wfac},
            "kernels": {}}
-    for label, needle, algo in (("adam", "adam_vec_kernel", 28 * args.elems),
+    for label, needle, algo in (("update", args.update_kernel,
+                                 args.update_bytes_per_elem * args.elems),
                                 ("reduce", "reduce_vec_kernel", None)):
         try:
             f, nf = _match(fetch, needle)
@@ -89,7 +91,8 @@ def traffic(args) -> int:
         out["kernels"][label] = {"fetch_kib_per_launch": f, "write_kib_per_launch": w,
                                  "dispatches": [nf, nw], "hbm_bytes_per_launch": b,
                                  "algorithmic_bytes_per_launch": algo}
-    out["hbm_bytes_per_launch"] = out["kernels"].get("adam", {}).get("hbm_bytes_per_launch")
+    out["update_kernel"] = args.update_kernel
+    out["hbm_bytes_per_launch"] = out["kernels"].get("update", {}).get("hbm_bytes_per_launch")
     with open(args.out, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
@@ -129,7 +132,12 @@ def main() -> int:
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
-    t.add_argument("--elems", type=int, required=True)
+    t.add_argument("--elems", type=int, required=True,
+                   help="shard elements one update launch processes")
+    t.add_argument("--update-kernel", default="adam_vec_kernel",
+                   help="name fragment of the update kernel (adam_vec_kernel, sgd_vec_kernel)")
+    t.add_argument("--update-bytes-per-elem", type=int, default=28,
+                   help="algorithmic bytes of the update per element")
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
     t.add_argument("--out", required=True)
