@@ -94,6 +94,8 @@ def lib():
         L.oracle_adam_scalars.argtypes = [ctypes.c_double] * 5 + [_i32, _i64, ctypes.c_double, _f32p]
         L.oracle_adam_update.argtypes = [_i32, _i64, _vp, _f32p, _f32p, _f32p, _vp, _f32p, _i32]
         L.oracle_sgd_update.argtypes = [_i32, _i64, _vp, _f32p, _f32p, _vp, _f32p]
+        L.oracle_clip_coef.argtypes = [ctypes.c_double, ctypes.c_double]
+        L.oracle_clip_coef.restype = ctypes.c_float
         L.oracle_loss_scale_next.argtypes = [_i32, _i32, _i32, ctypes.c_double,
                                              ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]
         L.oracle_state_bytes.argtypes = [_i64, _i32, _i32, _i64, _i32, _i32, _i32,
@@ -219,10 +221,18 @@ class LossScale:
     min_scale: float = 1.0
 
 
-def adam_scalars(hp: AdamHP, t: int, scale: float) -> np.ndarray:
-    out = np.empty(10, np.float32)
+def clip_coef(sumsq: float, max_norm: float) -> float:
+    """Global-norm clipping coefficient min(1, max_norm / (sqrt(sumsq) + 1e-6))
+    in fp64, rounded to fp32; 1 when max_norm <= 0 (textbook clipping; the
+    pages are silent)."""
+    return float(lib().oracle_clip_coef(sumsq, max_norm))
+
+
+def adam_scalars(hp: AdamHP, t: int, scale: float, coef: float = 1.0) -> np.ndarray:
+    out = np.empty(11, np.float32)
     lib().oracle_adam_scalars(hp.beta1, hp.beta2, hp.lr, hp.eps, hp.weight_decay,
                               hp.bias_correction, t, scale, _p32(out))
+    out[10] = np.float32(coef)
     return out
 
 
@@ -248,9 +258,9 @@ class SGDHP:
     initial_step: int = 0
 
 
-def sgd_scalars(hp: SGDHP, scale: float) -> np.ndarray:
-    return np.array([hp.lr, hp.momentum, hp.weight_decay, 1.0 / scale], dtype=np.float64) \
-        .astype(np.float32)
+def sgd_scalars(hp: SGDHP, scale: float, coef: float = 1.0) -> np.ndarray:
+    return np.array([hp.lr, hp.momentum, hp.weight_decay, 1.0 / scale, coef],
+                    dtype=np.float64).astype(np.float32)
 
 
 def sgd_update(lp: int, grad: np.ndarray, master: np.ndarray, momentum: Optional[np.ndarray],
@@ -320,14 +330,21 @@ def new_state(lp: int, master: np.ndarray, m, v, hp, ls: LossScale) -> ShardStat
 
 
 def step(st: ShardState, contribs: Sequence[np.ndarray], bucket_elems: int,
-         hp, ls: LossScale, forced_flag: Optional[int] = None) -> StepInfo:
+         hp, ls: LossScale, forced_flag: Optional[int] = None, max_norm: float = 0.0,
+         clip_sumsq: Optional[float] = None) -> StepInfo:
     """One owner-rank step on the whole shard held in memory; hp is an AdamHP
     or an SGDHP.  forced_flag lets a caller that evaluates a sample of a larger
-    shard supply the overflow decision taken over the full shard."""
+    shard supply the overflow decision taken over the full shard, and
+    clip_sumsq the squared norm the clipping coefficient is taken from (default:
+    this shard's).  max_norm > 0 clips the unscaled gradient to that global
+    norm."""
     st.grad = reduce_shard(st.lp, contribs, bucket_elems)
     flag, sumsq = flag_sumsq(st.lp, st.grad, st.scale)
     if forced_flag is not None:
         flag = int(forced_flag)
+    coef = 1.0
+    if not flag:
+        coef = clip_coef(sumsq if clip_sumsq is None else clip_sumsq, max_norm)
     scale_used = st.scale
     if flag:
         skipped = 1
@@ -335,9 +352,10 @@ def step(st: ShardState, contribs: Sequence[np.ndarray], bucket_elems: int,
         skipped = 0
         st.t += 1
         if isinstance(hp, SGDHP):
-            sgd_update(st.lp, st.grad, st.master, st.m, st.param, sgd_scalars(hp, st.scale))
+            sgd_update(st.lp, st.grad, st.master, st.m, st.param,
+                       sgd_scalars(hp, st.scale, coef))
         else:
-            sc = adam_scalars(hp, st.t, st.scale)
+            sc = adam_scalars(hp, st.t, st.scale, coef)
             adam_update(st.lp, st.grad, st.master, st.m, st.v, st.param, sc, hp.wd_mode)
     st.scale, st.good_steps = loss_scale_next(flag, ls, st.scale, st.good_steps)
     return StepInfo(flag, skipped, st.t, float(np.sqrt(sumsq)), scale_used, st.scale)

@@ -242,9 +242,26 @@ void oracle_flag_sumsq(int lp, const void* g, int64_t n, float inv_scale,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Global-norm clipping coefficient (the pages are silent; the textbook rule, */
+/* as in PyTorch's clip_grad_norm_): with norm = sqrt(sumsq) of the unscaled  */
+/* gradient and a limit max_norm > 0, coef = min(1, max_norm/(norm + 1e-6)),  */
+/* computed in fp64 and rounded to fp32; max_norm <= 0 disables clipping      */
+/* (coef = 1).  The update multiplies the unscaled gradient by coef.          */
+/* ------------------------------------------------------------------------ */
+
+float oracle_clip_coef(double sumsq, double max_norm)
+{
+    if (!(max_norm > 0.0)) return 1.0f;
+    double norm = sqrt(sumsq);
+    double c = max_norm / (norm + 1e-6);
+    return c < 1.0 ? (float)c : 1.0f;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Host scalars of one applied Adam step (t counts applied steps, t >= 1).   */
 /* out: [0] beta1 [1] beta2 [2] 1-beta1 [3] 1-beta2 [4] bias corr. 1          */
 /*      [5] bias corr. 2 [6] lr [7] eps [8] weight decay [9] 1/scale          */
+/*      [10] clipping coefficient (set to 1 here; the caller may replace it)  */
 /* beta^t is the product of t copies of the fp32-rounded beta, in fp64.       */
 /* ------------------------------------------------------------------------ */
 
@@ -268,6 +285,7 @@ void oracle_adam_scalars(double beta1, double beta2, double lr, double eps,
     out[7] = (float)eps;
     out[8] = (float)weight_decay;
     out[9] = (float)(1.0 / loss_scale);
+    out[10] = 1.0f;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -277,7 +295,8 @@ void oracle_adam_scalars(double beta1, double beta2, double lr, double eps,
 /* the local fp32 parameter shard and optimizer state; [P4] "Where Did All    */
 /* the Memory Go?": the update runs on fp32 weights, then casts to fp16.      */
 /* Textbook Adam (Kingma & Ba 2015, Algorithm 1) per element:                 */
-/*   g  = f32(grad) * (1/scale)          [L2 mode: g += wd * p]               */
+/*   g  = f32(grad) * (1/scale) ; g = g * coef  [clipping]                   */
+/*                                        [L2 mode: g += wd * p]              */
 /*   m  = b1*m + (1-b1)*g                                                     */
 /*   v  = b2*v + (1-b2)*(g*g)                                                 */
 /*   u  = (m/bc1) / (sqrt(v/bc2) + eps)  [decoupled mode: u += wd * p]        */
@@ -291,10 +310,12 @@ void oracle_adam_update(int lp, int64_t n, const void* grad, float* master,
 {
     float b1 = sc[0], b2 = sc[1], omb1 = sc[2], omb2 = sc[3];
     float bc1 = sc[4], bc2 = sc[5], lr = sc[6], eps = sc[7], wd = sc[8];
-    float inv_scale = sc[9];
+    float inv_scale = sc[9], coef = sc[10];
     for (int64_t i = 0; i < n; ++i) {
         float p = master[i];
         float g = load_g(lp, grad, i) * inv_scale;
+        if (coef != 1.0f)
+            g = g * coef;
         if (wd_mode == 1 && wd != 0.0f)
             g = g + wd * p;
         float m = b1 * exp_avg[i] + omb1 * g;
@@ -317,20 +338,24 @@ void oracle_adam_update(int lp, int64_t n, const void* grad, float* master,
 /* extension group C: SGD with momentum, K = 4 bytes of state, and plain SGD, */
 /* K = 0).  The pages give no formula; textbook heavy-ball SGD, with the      */
 /* classic L2 weight decay folded into the gradient:                          */
-/*   g = f32(grad) * (1/scale)            [wd != 0: g = g + wd * p]           */
+/*   g = f32(grad) * (1/scale) ; g = g * coef   [clipping]                   */
+/*                                        [wd != 0: g = g + wd * p]           */
 /*   with momentum:  buf = mu*buf + g ;  d = buf                              */
 /*   plain SGD:      d = g                                                    */
 /*   p = p - lr*d ;  2-byte storage: param = rne_lp(p)                        */
-/* sc: [0] lr [1] mu [2] wd [3] 1/scale.  momentum == NULL: plain SGD.        */
+/* sc: [0] lr [1] mu [2] wd [3] 1/scale [4] clipping coefficient.            */
+/* momentum == NULL: plain SGD.                                               */
 /* ------------------------------------------------------------------------ */
 
 void oracle_sgd_update(int lp, int64_t n, const void* grad, float* master, float* momentum,
                        void* param, const float* sc)
 {
-    float lr = sc[0], mu = sc[1], wd = sc[2], inv_scale = sc[3];
+    float lr = sc[0], mu = sc[1], wd = sc[2], inv_scale = sc[3], coef = sc[4];
     for (int64_t i = 0; i < n; ++i) {
         float p = master[i];
         float g = load_g(lp, grad, i) * inv_scale;
+        if (coef != 1.0f)
+            g = g * coef;
         if (wd != 0.0f)
             g = g + wd * p;
         float d = g;

@@ -13,7 +13,7 @@ from conftest import ROOT
 
 SRC = os.path.join(ROOT, "oracle", "zero_oracle.c")
 PINS = ["tests/test_oracle_ledger.py", "tests/test_oracle_formats.py", "tests/test_oracle_step.py",
-        "tests/test_oracle_sgd.py"]
+        "tests/test_oracle_sgd.py", "tests/test_oracle_clip.py"]
 
 # (name, exact text in zero_oracle.c, replacement); each text occurs once
 MUTATIONS = [
@@ -43,8 +43,8 @@ MUTATIONS = [
     ("Adam L2 decay sign", "if (wd_mode == 1 && wd != 0.0f)\n            g = g + wd * p;",
      "if (wd_mode == 1 && wd != 0.0f)\n            g = g - wd * p;"),
     ("Adam ignores the loss scale",
-     "float g = load_g(lp, grad, i) * inv_scale;\n        if (wd_mode == 1",
-     "float g = load_g(lp, grad, i);\n        if (wd_mode == 1"),
+     "float g = load_g(lp, grad, i) * inv_scale;\n        if (coef != 1.0f)\n            g = g * coef;\n        if (wd_mode == 1",
+     "float g = load_g(lp, grad, i);\n        if (coef != 1.0f)\n            g = g * coef;\n        if (wd_mode == 1"),
     ("bias correction of step t-1", "for (int64_t k = 0; k < t; ++k) {",
      "for (int64_t k = 1; k < t; ++k) {"),
     ("1-beta1 from beta2", "out[2] = 1.0f - b1;", "out[2] = 1.0f - b2;"),
@@ -69,8 +69,13 @@ MUTATIONS = [
      "if (wd != 0.0f)\n            g = g - wd * p;"),
     ("SGD step sign", "p = p - lr * d;", "p = p + lr * d;"),
     ("SGD ignores the loss scale",
-     "float g = load_g(lp, grad, i) * inv_scale;\n        if (wd != 0.0f)",
-     "float g = load_g(lp, grad, i);\n        if (wd != 0.0f)"),
+     "float g = load_g(lp, grad, i) * inv_scale;\n        if (coef != 1.0f)\n            g = g * coef;\n        if (wd != 0.0f)",
+     "float g = load_g(lp, grad, i);\n        if (coef != 1.0f)\n            g = g * coef;\n        if (wd != 0.0f)"),
+    ("clip not clamped at 1", "return c < 1.0 ? (float)c : 1.0f;", "return (float)c;"),
+    ("clip norm without the root", "double norm = sqrt(sumsq);", "double norm = sumsq;"),
+    ("clip drops the 1e-6", "double c = max_norm / (norm + 1e-6);", "double c = max_norm / norm;"),
+    ("Adam ignores the clip", "g = g * coef;\n        if (wd_mode == 1", "g = g * 1.0f;\n        if (wd_mode == 1"),
+    ("SGD clips twice", "g = g * coef;\n        if (wd != 0.0f)", "g = g * coef * coef;\n        if (wd != 0.0f)"),
     ("fp32 storage read as 2-byte", "if (lp == ORACLE_FP32) return ((const float*)a)[i];",
      "if (lp == 99) return ((const float*)a)[i];"),
     ("fp32 storage written rounded to fp16", "    if (lp == ORACLE_FP32)\n        ((float*)a)[i] = x;",
