@@ -2,10 +2,13 @@
 """Throughput of the owner-rank ZeRO-DP step on one MI355X.
 
 One step = every C_B bucket reduce of the owner's shard, the overflow check
-and the fused Adam + cast, through the C ABI (device-gated flow: the check's
-result stays on the GPU for Adam and the host waits only for its copy; the
-synchronous-check flow is timed beside it), on the 128B-parameter workload at Nd = 64: a 2.0e9-element shard, 4
-contributions, C_B = 2e8, fp16 storage, loss scale 4096, AdamW lr 6e-5, wd 0.1.
+and the fused Adam + cast, through the C ABI, on the 128B-parameter workload at
+Nd = 64: a 2.0e9-element shard, 4 contributions, C_B = 2e8, fp16 storage, loss
+scale 4096, AdamW lr 6e-5, wd 0.1.  Four flows run the same step and are all
+timed: device-resident steps enqueued back to back (the reported value by
+default: the decision and the counters stay on the GPU, no host round trip),
+the same step captured in a HIP graph and replayed, the device-gated check
+(the host waits for a 16-byte result copy per step) and the synchronous check.
 Inputs are seeded synthetic tensors resident in HBM before timing starts; the
 same contribution batch feeds every step (each step still reads and writes
 every byte).
@@ -125,6 +128,11 @@ def main() -> int:
                     help="shard elements the CPU oracle runs on (0 = skip)")
     ap.add_argument("--only", choices=["copy"], default=None,
                     help="run only the plain copy kernel (byte-counter calibration)")
+    ap.add_argument("--flow", choices=["gated", "sync", "device", "graph"], default="device",
+                    help="flow whose step time is the reported value: device-gated check "
+                         "(gated), synchronous check (sync), device-resident steps enqueued "
+                         "back to back (device), or one device-resident step captured in a "
+                         "HIP graph and replayed (graph); all four are timed")
     ap.add_argument("--mode", choices=["pos_g", "pos"], default="pos_g",
                     help="pos_g: gradient partitioning (bucket reduces + check + Adam); "
                          "pos: optimizer-state partitioning only (the owner's slice of an "
@@ -249,6 +257,38 @@ def main() -> int:
     print(f"[bench] timed {args.steps} synchronous-check steps: {ms_sync:.3f} ms/step, adam "
           f"{adam_sync:.3f} ms, reduce {red_sync:.3f} ms", file=sys.stderr, flush=True)
 
+    def timed_device(use_graph):
+        # device-resident flow: no host synchronisation inside the timed steps
+        contrib = bufs if args.mode == "pos_g" else None
+        zs.zero_device_begin(h, stream)
+        graph = None
+        if use_graph:
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                zs.zero_step_device(h, contrib)     # the capture stream is current here
+            run = graph.replay
+        else:
+            run = lambda: zs.zero_step_device(h, contrib, stream)
+        for _ in range(max(1, args.warmup)):
+            run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            run()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        zs.zero_device_end(h, stream)
+        del graph
+        return ms
+
+    ms_device = timed_device(False)
+    ms_graph = timed_device(True)
+    print(f"[bench] timed {args.steps} device-resident steps: {ms_device:.3f} ms/step; "
+          f"graph replays: {ms_graph:.3f} ms/step", file=sys.stderr, flush=True)
+    by_flow = {"gated": ms_step, "sync": ms_sync, "device": ms_device, "graph": ms_graph}
+    ms_step = by_flow[args.flow]
+
     # The copy ceiling runs after the step timing: allocating and freeing its
     # 16 GB before the shard arrays were allocated slowed the Adam pass by ~5%
     # on MI355X (placement of the five streamed arrays).
@@ -307,17 +347,16 @@ def main() -> int:
                        "reduce_all_buckets": red_avg,
                        "reduce_gbs": (reduce_bytes / (red_avg * 1e-3) / 1e9
                                       if args.mode == "pos_g" else None)},
-        "flow": ("device-gated check + update (zero_sgd_step_gated / zero_step_resolve)" if sgd
-                 else "device-gated check + Adam (zero_adam_step_gated / zero_step_resolve)"),
-        "ms_per_step_sync_check_flow": ms_sync,
+        "flow": args.flow,
+        "ms_per_step_by_flow": by_flow,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": (f"sgd_vec_kernel<{w.lp}, momentum={int(w.has_m)}>" if sgd
                                 else f"adam_vec_kernel<{w.lp}, decoupled wd>"),
                      "algorithmic_bytes_per_launch": adam_bytes,
                      "launch_ms": adam_avg,
-                     "timing": "HIP events around the gated Adam enqueue (includes the "
-                               "two fold kernels and the 16-byte result copy)"},
+                     "timing": "HIP events around the Adam enqueue of the device-gated flow "
+                               "(includes the fold kernels and the 16-byte result copy)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

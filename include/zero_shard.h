@@ -21,6 +21,10 @@
  *     zero_bucket_reduce   x nbuckets  (ascending, contiguous, covering [0, S))
  *     zero_overflow_check            (synchronises the stream once)
  *     zero_adam_step                 (skipped when the check found inf/nan)
+ * or the device-gated form (zero_adam_step_gated + zero_step_resolve), or the
+ * device-resident form, whose whole step is one enqueue that a caller may
+ * capture in a HIP graph (zero_device_begin, zero_step_device per step,
+ * zero_device_end).
  *
  * Conventions for every function:
  *  - Returns a zero_status.  Arguments are validated before anything is
@@ -190,10 +194,10 @@ zero_status zero_state_bytes_ex(int64_t psi, int32_t nd, int32_t n_contrib,
 
 /*
  * Create a handle bound to the current device.  Copies *desc, *hp and *ls.
- * Allocates a device workspace for the check's per-workgroup partials, 8 bytes
- * per 1024 shard elements plus 16 bytes per bucket plus 8 KiB (15.6 MB for a
- * 2e9-element shard), and 64 bytes of pinned host memory; touches none of the
- * caller's arrays.
+ * Allocates a device workspace for the check's per-workgroup partials and the
+ * device-resident step state, 8 bytes per 1024 shard elements plus 16 bytes
+ * per bucket plus 8.2 KiB (15.6 MB for a 2e9-element shard), and 256 bytes of
+ * pinned host memory; touches none of the caller's arrays.
  * Errors: INVALID_ARG (NULL argument or pointer in desc, psi < 1, nd < 1, rank
  * outside [0, nd), bucket_elems < 1, unknown lp, misaligned or overlapping
  * arrays, hp or ls out of range), UNSUPPORTED (buckets so small that the
@@ -286,6 +290,21 @@ zero_status zero_sgd_step(zero_shard_t h, const zero_sgd_hparams* hp, void* stre
 zero_status zero_sgd_step_gated(zero_shard_t h, const zero_sgd_hparams* hp, void* stream);
 
 /*
+ * Global-norm clipping (not on the pages; the textbook rule, as PyTorch's
+ * clip_grad_norm_): with max_grad_norm > 0, every later step multiplies the
+ * unscaled gradient by coef = min(1, max_grad_norm / (norm + 1e-6)), norm the
+ * step's gradient norm (grad_norm of zero_step_info), coef computed in fp64
+ * and rounded to fp32, before weight decay and the moments:
+ *     g = f32(grad) * fp32(1/scale) ;  g = g * coef ;  ...
+ * A coefficient of 1 leaves the update bitwise unchanged.  The check computes
+ * coef on the device from its own norm; after zero_overflow_merge it comes from
+ * the merged global norm.  max_grad_norm = 0 turns clipping off (the default).
+ * Errors: STATE (dead handle, a step in progress, device-resident flow
+ * active), INVALID_ARG (negative or not finite).
+ */
+zero_status zero_shard_set_clip(zero_shard_t h, double max_grad_norm);
+
+/*
  * Install the step's global check result on every rank before zero_adam_step,
  * for data parallelism across Nd processes: each rank runs
  * zero_overflow_check on its own partition, the caller all-reduces the
@@ -325,6 +344,41 @@ zero_status zero_adam_step_gated(zero_shard_t h, const zero_adam_hparams* hp, vo
  * Errors: STATE (dead handle, no gated step pending), HIP.
  */
 zero_status zero_step_resolve(zero_shard_t h, zero_step_info* out);
+
+/*
+ * Device-resident flow, for shards whose step is short enough that launches
+ * and host round trips dominate.  zero_device_begin copies t, the loss scale
+ * and the clean-step count into device memory (one kernel on `stream`); from
+ * then on each zero_step_device enqueues a whole step on `stream`, with no
+ * host synchronisation and no host-side state change:
+ *   - the reduce of every C_B bucket of the shard from n_contrib contributions
+ *     (contribs: host array of device pointers, each to S elements of the
+ *     storage format; element i of contribution r is its value for shard
+ *     element i), or, with contribs = NULL and n_contrib = 0, the scan of a
+ *     caller-filled grad_shard;
+ *   - the fixed-order fold (norm, overflow, clipping coefficient);
+ *   - a one-lane kernel that decides the step exactly as the host flows do
+ *     (skip on overflow; otherwise t += 1 and the bias corrections of step t;
+ *     the loss-scale rule) and advances the device copy of the counters;
+ *   - the update (Adam or SGD with the init hyper-parameters), which reads
+ *     the decision and the step's scalars from device memory and writes
+ *     nothing on a skipped step.
+ * Because every launch argument is fixed for fixed contribution pointers,
+ * the enqueue of zero_step_device may be captured in a HIP graph and
+ * replayed; each replay is one step.  The loss scale the next step's
+ * gradients must carry is only known on the device (or after
+ * zero_device_end).  zero_device_end synchronises `stream`, copies the
+ * counters back to the handle and leaves the flow; *out (may be NULL) gets the
+ * last step's result (step_t and scale_next are the current values; with no
+ * step run, overflow = 0 and grad_norm = 0).  While the flow is active every
+ * other step, check, merge, counter and clipping call returns ZERO_ERR_STATE.
+ * Errors: STATE (dead handle, flow not / already active, a step in progress),
+ * INVALID_ARG (contribution pointers as for zero_bucket_reduce), HIP.
+ */
+zero_status zero_device_begin(zero_shard_t h, void* stream);
+zero_status zero_step_device(zero_shard_t h, const void* const* contribs, int32_t n_contrib,
+                             void* stream);
+zero_status zero_device_end(zero_shard_t h, void* stream, zero_step_info* out);
 
 /* Step counter, current loss scale and clean-step count (for checkpoints). */
 zero_status zero_shard_get_counters(zero_shard_t h, int64_t* step_t, double* scale,

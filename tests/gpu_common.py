@@ -88,14 +88,19 @@ class GpuRun:
 def run_gpu(w: synth.Workload, *, elems: Optional[int] = None, steps: Optional[int] = None,
             seed: int = 0, bucket_elems: Optional[int] = None, hp=None,
             ls: Optional[zs.LossScaleCfg] = None, keep_contribs: bool = True,
-            offsets: Optional[dict] = None, hook=None, flow: str = "sync") -> GpuRun:
+            offsets: Optional[dict] = None, hook=None, flow: str = "sync",
+            max_norm: float = 0.0, scale_of=None) -> GpuRun:
     """Run `steps` owner-rank steps of workload w (its first `elems` shard
     elements) through the C ABI on cuda:0.  offsets maps an array name
     ('master', 'm', 'v', 'grad', 'param', 'contrib') to an element offset of its
     base pointer inside a larger allocation (alignment tests).  hook(step,
     bufs) may edit the contributions of a step before it runs.  flow "sync"
     uses zero_overflow_check + the step call, "gated" the gated step call +
-    zero_step_resolve.  The workload's opt picks Adam or SGD."""
+    zero_step_resolve, "device" one zero_step_device per step between
+    zero_device_begin and zero_device_end (ended after every step to read its
+    result), "device_run" the same without ending between steps (only the last
+    step's result is read; the others are None).  The workload's opt picks Adam
+    or SGD; max_norm > 0 turns on global-norm clipping."""
     dev = torch.device("cuda", 0)
     S = w.shard if elems is None else elems
     steps = w.steps if steps is None else steps
@@ -145,13 +150,30 @@ def run_gpu(w: synth.Workload, *, elems: Optional[int] = None, steps: Optional[i
     gated_fn = zs.zero_sgd_step_gated if sgd else zs.zero_adam_step_gated
     infos, kept = [], []
     try:
+        if max_norm:
+            zs.zero_shard_set_clip(h, max_norm)
         scale = ls.init_scale
+        if flow == "device_run":
+            zs.zero_device_begin(h)
         for s in range(steps):
+            if flow == "device_run" and scale_of is not None:
+                scale = scale_of(s)
             synth.fill_contribs(w, bufs, s, scale, seed)
             if hook is not None:
                 hook(s, bufs)
             if keep_contribs:
                 kept.append([stored(b) for b in bufs])
+            if flow == "device":
+                zs.zero_device_begin(h)
+                zs.zero_step_device(h, bufs)
+                info = zs.zero_device_end(h)
+                infos.append(info)
+                scale = info.scale_next
+                continue
+            if flow == "device_run":
+                zs.zero_step_device(h, bufs)
+                infos.append(zs.zero_device_end(h) if s == steps - 1 else None)
+                continue
             zs.reduce_buckets(h, bufs, S, cb)
             if flow == "gated":
                 gated_fn(h)
@@ -172,13 +194,13 @@ def run_gpu(w: synth.Workload, *, elems: Optional[int] = None, steps: Optional[i
 
 
 def run_oracle(w: synth.Workload, g: GpuRun, *, bucket_elems: Optional[int] = None,
-               hp=None, ls: Optional[zs.LossScaleCfg] = None):
+               hp=None, ls: Optional[zs.LossScaleCfg] = None, max_norm: float = 0.0):
     lp = LP_CODE[w.lp]
     cb = w.bucket_elems if bucket_elems is None else bucket_elems
     ohp = oracle_hp(hp or hp_of(w))
     ols = oracle_ls(ls or ls_of(w))
     st = oracle.new_state(lp, g.master0, g.m0, g.v0, ohp, ols)
-    infos = [oracle.step(st, cs, cb, ohp, ols) for cs in g.contribs]
+    infos = [oracle.step(st, cs, cb, ohp, ols, max_norm=max_norm) for cs in g.contribs]
     return st, infos
 
 
@@ -210,6 +232,8 @@ def compare(w: synth.Workload, g: GpuRun, st, oinfos, tag: str = "") -> dict:
     """Assert the parity rules; return the observed worst errors."""
     assert len(g.infos) == len(oinfos)
     for k, (a, b) in enumerate(zip(g.infos, oinfos)):
+        if a is None:                    # a device-resident step whose result was not read
+            continue
         assert a.overflow == b.overflow, (tag, k, a, b)
         assert a.skipped == b.skipped, (tag, k)
         assert a.step_t == b.step_t, (tag, k, a.step_t, b.step_t)

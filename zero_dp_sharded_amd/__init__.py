@@ -34,6 +34,7 @@ ABI_SYMBOLS = (
     "zero_state_bytes", "zero_state_bytes_ex", "zero_shard_init", "zero_shard_init_sgd",
     "zero_bucket_reduce", "zero_overflow_check", "zero_overflow_merge", "zero_adam_step",
     "zero_adam_step_gated", "zero_sgd_step", "zero_sgd_step_gated", "zero_step_resolve",
+    "zero_shard_set_clip", "zero_device_begin", "zero_step_device", "zero_device_end",
     "zero_shard_get_counters",
     "zero_shard_set_counters", "zero_shard_destroy", "zero_status_str", "zero_last_error",
     "zero_abi_version",
@@ -115,6 +116,10 @@ def lib() -> ctypes.CDLL:
         L.zero_overflow_merge.argtypes = [_vp, _i32, _f64, ctypes.POINTER(ZeroStepInfo)]
         L.zero_adam_step_gated.argtypes = [_vp, ctypes.POINTER(ZeroAdamHParams), _vp]
         L.zero_step_resolve.argtypes = [_vp, ctypes.POINTER(ZeroStepInfo)]
+        L.zero_shard_set_clip.argtypes = [_vp, _f64]
+        L.zero_device_begin.argtypes = [_vp, _vp]
+        L.zero_step_device.argtypes = [_vp, ctypes.POINTER(_vp), _i32, _vp]
+        L.zero_device_end.argtypes = [_vp, _vp, ctypes.POINTER(ZeroStepInfo)]
         L.zero_shard_get_counters.argtypes = [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_f64),
                                               ctypes.POINTER(_i64)]
         L.zero_shard_set_counters.argtypes = [_vp, _i64, _f64, _i64]
@@ -366,6 +371,31 @@ def zero_sgd_step_gated(h: int, hp: Optional[SGDHParams] = None, stream=None) ->
 def zero_step_resolve(h: int) -> StepInfo:
     out = ZeroStepInfo()
     _check(lib().zero_step_resolve(h, ctypes.byref(out)), "zero_step_resolve")
+    return StepInfo.from_c(out)
+
+
+def zero_shard_set_clip(h: int, max_grad_norm: float) -> None:
+    _check(lib().zero_shard_set_clip(h, max_grad_norm), "zero_shard_set_clip")
+
+
+def zero_device_begin(h: int, stream=None) -> None:
+    _check(lib().zero_device_begin(h, _stream_ptr(stream)), "zero_device_begin")
+
+
+def zero_step_device(h: int, contribs: Optional[Sequence] = None, stream=None) -> None:
+    """Enqueue one whole device-resident step; contribs are R shard-sized
+    tensors (or device addresses), None to scan a caller-filled grad_shard.
+    Capturable in a graph."""
+    if contribs is None:
+        arr, n = None, 0
+    else:
+        arr, n = (_vp * len(contribs))(*[_dptr(c) for c in contribs]), len(contribs)
+    _check(lib().zero_step_device(h, arr, n, _stream_ptr(stream)), "zero_step_device")
+
+
+def zero_device_end(h: int, stream=None) -> StepInfo:
+    out = ZeroStepInfo()
+    _check(lib().zero_device_end(h, _stream_ptr(stream), ctypes.byref(out)), "zero_device_end")
     return StepInfo.from_c(out)
 
 

@@ -87,17 +87,55 @@ constexpr int64_t kMaxLaunchItems = ZK_MAX_LAUNCH_ITEMS;
 // Fixed-order fold of the per-workgroup partials.
 constexpr int kFoldBlock = 256;
 constexpr int kFoldMaxBlocks = 1024;
+// At most this many partials are summed by one workgroup in one launch.
+constexpr int64_t kFoldOneLevel = 4096;
 
 struct ContribPtrs {
     const void* p[kMaxContrib];
 };
 
+// Result of a step's check, written by the last fold launch.
+struct CheckResult {
+    double sumsq;          // squared unscaled norm; NaN when a stored value was not finite
+    float clip;            // global-norm clipping coefficient (1 when off or on overflow)
+    float pad;
+};
+
+// Step state kept in device memory by the device-resident flow, so that a
+// whole step (reduce, check, decision, update) runs without the host and can
+// be captured in a graph.  The prepare kernel reads the check, decides, and
+// advances the counters; the reduce reads inv_scale, the update upd_*.
+struct DevState {
+    double scale;          // loss scale the next step's gradients carry
+    double pw1, pw2;       // products of the fp32-rounded betas over applied steps
+    int64_t t;             // applied steps
+    int64_t good;          // clean steps since the scale last changed
+    int64_t steps_run;     // device steps prepared since the state was loaded
+    double last_sumsq;     // the last step's check result (NaN: overflow)
+    double last_scale;     // the loss scale the last step's gradients carried
+    float inv_scale;       // fp32(1/scale) for the current step's check
+    float upd_inv_scale;   // the same for the update of the step just decided
+    float bc1, bc2;        // bias corrections of that update
+    int32_t skip;          // 1: that update writes nothing
+    int32_t pad;
+};
+
+// Constants of the prepare kernel (per handle).
+struct PrepareArgs {
+    double b1, b2;         // fp32-rounded betas, as fp64 factors
+    double min_scale;
+    int32_t bias_correction;
+    int32_t dynamic;
+    int64_t growth_interval;
+};
+
 // One bucket of the reduce.  Elements [0, n) of the bucket; the vector body
 // starts at `head` and holds `nvec` 16-byte runs (8 two-byte or 4 fp32
 // elements) that are 16-byte aligned in every contribution and in `out`.
-// vec_ok = 0 selects the element-wise path.  Workgroup b writes partial[slot_base + b]: the fp64 sum of the squared
-// unscaled stored values of its elements, or NaN if any stored value is not
-// finite.
+// vec_ok = 0 selects the element-wise path.  Workgroup b writes
+// partial[slot_base + b]: the fp64 sum of the squared unscaled stored values
+// of its elements, or NaN if any stored value is not finite.  The unscale
+// factor is inv_scale, or dev->inv_scale when dev is set.
 struct ReduceLaunch {
     ContribPtrs c;
     void* out;
@@ -112,6 +150,7 @@ struct ReduceLaunch {
     double* partial;
     int64_t slot_base;
     uint32_t lds_reserve;  // dynamic LDS that caps workgroups per CU
+    const DevState* dev;
 };
 
 // Stand-alone check of a stored gradient shard (no reduce this step).
@@ -126,28 +165,18 @@ struct ScanLaunch {
     double* partial;
     int64_t slot_base;
     uint32_t lds_reserve;
+    const DevState* dev;
 };
 
-// SGD over n elements, laid out like AdamLaunch.  mom == nullptr: plain SGD.
-struct SgdLaunch {
-    const void* grad;
-    float* master;
-    float* mom;
-    void* param;
-    int64_t n;
-    int64_t head;
-    int64_t ngroups;
-    int32_t lp;
-    int32_t vec_ok;
-    int32_t has_wd;
-    uint32_t lds_reserve;
-    float lr, mu, wd, inv_scale;
-    const struct CheckResult* gate;
-};
-
-struct CheckResult {
-    double sumsq;          // NaN when a stored value was not finite
-    double pad;
+// Where an update takes its per-step values.  Host flows pass inv_scale (and
+// the bias corrections) as arguments; res, when set, supplies the clipping
+// coefficient (else `clip`), and with gate = 1 its NaN sum skips the update;
+// dev, when set, supplies inv_scale, the bias corrections and the skip.
+struct StepSource {
+    const CheckResult* res;
+    const DevState* dev;
+    int32_t gate;
+    float clip;
 };
 
 enum WdKind { kWdNone = 0, kWdDecoupled = 1, kWdL2 = 2 };
@@ -169,9 +198,24 @@ struct AdamLaunch {
     int32_t wd_kind;
     uint32_t lds_reserve;
     float b1, b2, omb1, omb2, bc1, bc2, lr, eps, wd, inv_scale;
-    // device-gated launch: every workgroup returns at once when gate->sumsq
-    // is NaN (a non-finite stored gradient); nullptr = always apply
-    const CheckResult* gate;
+    StepSource src;
+};
+
+// SGD over n elements, laid out like AdamLaunch.  mom == nullptr: plain SGD.
+struct SgdLaunch {
+    const void* grad;
+    float* master;
+    float* mom;
+    void* param;
+    int64_t n;
+    int64_t head;
+    int64_t ngroups;
+    int32_t lp;
+    int32_t vec_ok;
+    int32_t has_wd;
+    uint32_t lds_reserve;
+    float lr, mu, wd, inv_scale;
+    StepSource src;
 };
 
 // Elements per 16-byte run of a storage format: 8 two-byte or 4 fp32 values.
@@ -185,9 +229,16 @@ int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok, int
 
 hipError_t launch_reduce(const ReduceLaunch& L, hipStream_t s);
 hipError_t launch_scan(const ScanLaunch& L, hipStream_t s);
-// Sum partial[0, nslots) in a fixed order into out->sumsq (two launches).
+// Sum partial[0, nslots) in a fixed order into out->sumsq (one launch for up
+// to kFoldOneLevel partials, else two) and set out->clip = min(1, max_norm /
+// (sqrt(sumsq) + 1e-6)) in fp64, rounded to fp32 (1 when max_norm <= 0 or the
+// sum is NaN).  dev set (device-resident flow): the same last lane then
+// decides the step and advances the device state with pa.
 hipError_t launch_finalize(const double* partial, int64_t nslots, double* level1,
-                           CheckResult* out, hipStream_t s);
+                           CheckResult* out, double max_norm, DevState* dev,
+                           const PrepareArgs& pa, hipStream_t s);
+// Device-resident flow: write the state.
+hipError_t launch_load_state(DevState* d, const DevState& init, hipStream_t s);
 hipError_t launch_adam(const AdamLaunch& a, hipStream_t s);
 hipError_t launch_sgd(const SgdLaunch& a, hipStream_t s);
 

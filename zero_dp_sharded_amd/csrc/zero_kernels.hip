@@ -202,7 +202,8 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 // the storage format (round to nearest even), store, check.
 template <int LP>
 __device__ __forceinline__ void reduce_finish(const ReduceLaunch& L, int64_t vi,
-                                              typename Fmt<LP>::FW acc, int& flag, double& ss)
+                                              typename Fmt<LP>::FW acc, float inv_scale, int& flag,
+                                              double& ss)
 {
     using VW = typename Fmt<LP>::VW;
     // (no pin_f32 here: hipcc converts the vector with plain conversions, which
@@ -210,18 +211,25 @@ __device__ __forceinline__ void reduce_finish(const ReduceLaunch& L, int64_t vi,
     acc = acc * L.inv_r;
     const VW o = __builtin_convertvector(acc, VW);
     st_nt<VW>(adv<LP>(L.out, L.head), vi, o);
-    check_v<LP>(o, L.inv_scale, flag, ss);
+    check_v<LP>(o, inv_scale, flag, ss);
 }
 
 template <int LP>
-__device__ __forceinline__ void reduce_s(const ReduceLaunch& L, int64_t e, int& flag, double& ss)
+__device__ __forceinline__ void reduce_s(const ReduceLaunch& L, int64_t e, float inv_scale, int& flag,
+                                         double& ss)
 {
     using T = typename Fmt<LP>::T;
     float acc = 0.f;
     for (int r = 0; r < L.R; ++r) acc = acc + load_s<LP>(L.c.p[r], e);
     const T o = static_cast<T>(pin_f32(acc * L.inv_r));
     static_cast<T*>(L.out)[e] = o;
-    check_s<LP>(o, L.inv_scale, flag, ss);
+    check_s<LP>(o, inv_scale, flag, ss);
+}
+
+// The unscale factor of a check: the launch argument, or the device state's.
+__device__ __forceinline__ float check_inv_scale(float arg, const DevState* dev)
+{
+    return dev != nullptr ? dev->inv_scale : arg;
 }
 
 // Vector body: workgroup b covers runs [b*B*U, (b+1)*B*U) for B lanes and U
@@ -235,6 +243,7 @@ __global__ __launch_bounds__(kRedBlock) void reduce_vec_kernel(ReduceLaunch L)
     using FW = typename Fmt<LP>::FW;
     int flag = 0;
     double ss = 0.0;
+    const float inv_scale = check_inv_scale(L.inv_scale, L.dev);
     const int64_t v0 = (int64_t)blockIdx.x * (kRedBlock * U) + threadIdx.x;
     if constexpr (RT > 0 && RT * U <= 16) {
         // every load of all U runs in flight before the arithmetic
@@ -254,7 +263,7 @@ __global__ __launch_bounds__(kRedBlock) void reduce_vec_kernel(ReduceLaunch L)
                 FW acc = (FW)(0.f);
 #pragma unroll
                 for (int r = 0; r < RT; ++r) acc = acc + __builtin_convertvector(x[u][r], FW);
-                reduce_finish<LP>(L, vi, acc, flag, ss);
+                reduce_finish<LP>(L, vi, acc, inv_scale, flag, ss);
             }
         }
     } else {
@@ -280,7 +289,7 @@ __global__ __launch_bounds__(kRedBlock) void reduce_vec_kernel(ReduceLaunch L)
                         if (k < cnt) acc = acc + __builtin_convertvector(x[k], FW);
                 }
             }
-            reduce_finish<LP>(L, vi, acc, flag, ss);
+            reduce_finish<LP>(L, vi, acc, inv_scale, flag, ss);
         }
     }
     block_partial<kRedBlock>(L.partial + L.slot_base + blockIdx.x, flag, ss);
@@ -292,11 +301,12 @@ __global__ __launch_bounds__(kScalarBlock) void reduce_elem_kernel(ReduceLaunch 
 {
     int flag = 0;
     double ss = 0.0;
+    const float inv_scale = check_inv_scale(L.inv_scale, L.dev);
     const int64_t cnt = rg.count();
 #pragma unroll 2
     for (int j = 0; j < (int)(kScalarElemsPerBlock / kScalarBlock); ++j) {
         const int64_t k = (int64_t)blockIdx.x * kScalarElemsPerBlock + j * kScalarBlock + threadIdx.x;
-        if (k < cnt) reduce_s<LP>(L, rg.at(k), flag, ss);
+        if (k < cnt) reduce_s<LP>(L, rg.at(k), inv_scale, flag, ss);
     }
     block_partial<kScalarBlock>(L.partial + slot + blockIdx.x, flag, ss);
 }
@@ -307,6 +317,7 @@ __global__ __launch_bounds__(kRedBlock) void scan_vec_kernel(ScanLaunch L)
     using VW = typename Fmt<LP>::VW;
     int flag = 0;
     double ss = 0.0;
+    const float inv_scale = check_inv_scale(L.inv_scale, L.dev);
     const int64_t v0 = (int64_t)blockIdx.x * (kRedBlock * kRedRuns) + threadIdx.x;
     VW x[kRedRuns];
 #pragma unroll
@@ -316,7 +327,7 @@ __global__ __launch_bounds__(kRedBlock) void scan_vec_kernel(ScanLaunch L)
     }
 #pragma unroll
     for (int u = 0; u < kRedRuns; ++u)
-        if (v0 + u * kRedBlock < L.nvec) check_v<LP>(x[u], L.inv_scale, flag, ss);
+        if (v0 + u * kRedBlock < L.nvec) check_v<LP>(x[u], inv_scale, flag, ss);
     block_partial<kRedBlock>(L.partial + L.slot_base + blockIdx.x, flag, ss);
 }
 
@@ -327,17 +338,61 @@ __global__ __launch_bounds__(kScalarBlock) void scan_elem_kernel(ScanLaunch L, R
     using T = typename Fmt<LP>::T;
     int flag = 0;
     double ss = 0.0;
+    const float inv_scale = check_inv_scale(L.inv_scale, L.dev);
     const int64_t cnt = rg.count();
     for (int j = 0; j < (int)(kScalarElemsPerBlock / kScalarBlock); ++j) {
         const int64_t k = (int64_t)blockIdx.x * kScalarElemsPerBlock + j * kScalarBlock + threadIdx.x;
-        if (k < cnt) check_s<LP>(static_cast<const T*>(L.g)[rg.at(k)], L.inv_scale, flag, ss);
+        if (k < cnt) check_s<LP>(static_cast<const T*>(L.g)[rg.at(k)], inv_scale, flag, ss);
     }
     block_partial<kScalarBlock>(L.partial + slot + blockIdx.x, flag, ss);
 }
 
-// Workgroup b sums in[b*chunk, min(n, (b+1)*chunk)) with a fixed shape.
+// Decide the checked step in device memory, as the host flows do: overflow
+// when the check's sum is NaN; an applied step advances t and the fp64 beta
+// powers and sets the bias corrections of its update; the loss scale halves on
+// overflow (not below min_scale) and doubles after growth_interval clean
+// steps.  The update reads upd_inv_scale (this step's), the next check
+// inv_scale (the next step's).  One lane runs it.
+__device__ void prepare_step(DevState* d, double ss, const PrepareArgs& a)
+{
+    const bool overflow = __builtin_isnan(ss);
+    DevState s = *d;
+    s.last_sumsq = ss;
+    s.last_scale = s.scale;
+    s.upd_inv_scale = s.inv_scale;
+    s.skip = overflow ? 1 : 0;
+    if (!overflow) {
+        s.t += 1;
+        s.pw1 = s.pw1 * a.b1;
+        s.pw2 = s.pw2 * a.b2;
+        s.bc1 = a.bias_correction ? (float)(1.0 - s.pw1) : 1.0f;
+        s.bc2 = a.bias_correction ? (float)(1.0 - s.pw2) : 1.0f;
+    }
+    if (a.dynamic) {
+        if (overflow) {
+            double sc = s.scale / 2.0;
+            s.scale = sc < a.min_scale ? a.min_scale : sc;
+            s.good = 0;
+        } else {
+            s.good += 1;
+            if (s.good == a.growth_interval) {
+                s.scale = s.scale * 2.0;
+                s.good = 0;
+            }
+        }
+    }
+    s.inv_scale = (float)(1.0 / s.scale);
+    s.steps_run += 1;
+    *d = s;
+}
+
+// Workgroup b sums in[b*chunk, min(n, (b+1)*chunk)) with a fixed shape into
+// out[b]; the last level (res set, one workgroup) writes the check result and
+// the clipping coefficient instead, and with dev set also decides the step.
 __global__ __launch_bounds__(kFoldBlock) void fold_kernel(const double* in, int64_t n, int64_t chunk,
-                                                          double* out)
+                                                          double* out, CheckResult* res,
+                                                          double max_norm, DevState* dev,
+                                                          PrepareArgs pa)
 {
     const int64_t lo = (int64_t)blockIdx.x * chunk;
     const int64_t hi = lo + chunk < n ? lo + chunk : n;
@@ -352,19 +407,52 @@ __global__ __launch_bounds__(kFoldBlock) void fold_kernel(const double* in, int6
         double t = sh[0];
 #pragma unroll
         for (int k = 1; k < kFoldBlock / 64; ++k) t += sh[k];
-        out[blockIdx.x] = t;
+        if (res == nullptr) {
+            out[blockIdx.x] = t;
+        } else {
+            // textbook global-norm clipping: min(1, max_norm / (norm + 1e-6)) in
+            // fp64; a NaN sum (overflow) fails the comparison and gives 1
+            float coef = 1.0f;
+            if (max_norm > 0.0) {
+                const double c = max_norm / (sqrt(t) + 1e-6);
+                if (c < 1.0) coef = (float)c;
+            }
+            res->sumsq = t;
+            res->clip = coef;
+            res->pad = 0.0f;
+            if (dev != nullptr) prepare_step(dev, t, pa);
+        }
     }
 }
 
-// ----------------------------------------------------------------- update gate
+// ----------------------------------------------------------------- update scalars
 
-// Device-side skip of a gated launch: the fold leaves NaN in the result when
-// any stored gradient is not finite.  The vector kernels read the gate after
-// issuing their loads, so its latency overlaps them (a skipped step costs the
-// load bytes but writes nothing); the element-wise kernels read it first.
-__device__ __forceinline__ bool gated_off(const CheckResult* gate)
+// Per-step values of an update: from the launch (host flows) or from device
+// memory (the check result's clipping coefficient and NaN gate; the device
+// state's scale, bias corrections and decision).  The vector kernels read them
+// after issuing their loads, so their latency overlaps the loads (a skipped
+// step costs the load bytes but writes nothing); the element-wise kernels read
+// them first.
+struct StepVals {
+    float inv_scale, bc1, bc2, clip;
+    bool skip;
+};
+
+__device__ __forceinline__ StepVals step_vals(const StepSource& src, float inv_scale, float bc1,
+                                              float bc2)
 {
-    return gate != nullptr && __builtin_isnan(gate->sumsq);
+    StepVals v{inv_scale, bc1, bc2, src.clip, false};
+    if (src.res != nullptr) {
+        v.clip = src.res->clip;
+        if (src.gate) v.skip = __builtin_isnan(src.res->sumsq);
+    }
+    if (src.dev != nullptr) {
+        v.inv_scale = src.dev->upd_inv_scale;
+        v.bc1 = src.dev->bc1;
+        v.bc2 = src.dev->bc2;
+        v.skip = src.dev->skip != 0;
+    }
+    return v;
 }
 
 // ----------------------------------------------------------------- Adam
@@ -373,14 +461,15 @@ __device__ __forceinline__ bool gated_off(const CheckResult* gate)
 // the public header states; p, m, v are updated in place.
 template <int WD>
 __device__ __forceinline__ void adam_e(float graw, float& p, float& m, float& v,
-                                       const AdamLaunch& a)
+                                       const AdamLaunch& a, const StepVals& sv)
 {
-    float g = graw * a.inv_scale;
+    float g = graw * sv.inv_scale;
+    g = g * sv.clip;                       // exact when the coefficient is 1
     if constexpr (WD == kWdL2) g = g + a.wd * p;
     m = a.b1 * m + a.omb1 * g;
     v = a.b2 * v + a.omb2 * (g * g);
-    const float mh = m / a.bc1;
-    const float vh = v / a.bc2;
+    const float mh = m / sv.bc1;
+    const float vh = v / sv.bc2;
     float u = mh / (sqrtf(vh) + a.eps);
     if constexpr (WD == kWdDecoupled) u = u + a.wd * p;
     p = p - a.lr * u;
@@ -412,7 +501,8 @@ __global__ __launch_bounds__(kAdamBlock) void adam_vec_kernel(AdamLaunch a)
             v[u] = ld_nt<f4>(vb, q);
         }
     }
-    if (gated_off(a.gate)) return;
+    const StepVals sv = step_vals(a.src, a.inv_scale, a.bc1, a.bc2);
+    if (sv.skip) return;
 #pragma unroll
     for (int u = 0; u < kAdamGroups; ++u) {
         const int64_t q = q0 + u * kAdamBlock;
@@ -422,7 +512,7 @@ __global__ __launch_bounds__(kAdamBlock) void adam_vec_kernel(AdamLaunch a)
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 float pk = pp[k], mk = mm[k], vk = vv[k];
-                adam_e<WD>(gf[k], pk, mk, vk, a);
+                adam_e<WD>(gf[k], pk, mk, vk, a, sv);
                 pp[k] = pk;
                 mm[k] = mk;
                 vv[k] = vk;
@@ -440,14 +530,15 @@ template <int LP, int WD>
 __global__ __launch_bounds__(kScalarBlock) void adam_elem_kernel(AdamLaunch a, Ranges rg)
 {
     using T = typename Fmt<LP>::T;
-    if (gated_off(a.gate)) return;
+    const StepVals sv = step_vals(a.src, a.inv_scale, a.bc1, a.bc2);
+    if (sv.skip) return;
     const int64_t cnt = rg.count();
     for (int j = 0; j < (int)(kScalarElemsPerBlock / kScalarBlock); ++j) {
         const int64_t k = (int64_t)blockIdx.x * kScalarElemsPerBlock + j * kScalarBlock + threadIdx.x;
         if (k < cnt) {
             const int64_t e = rg.at(k);
             float p = a.master[e], m = a.m[e], v = a.v[e];
-            adam_e<WD>(load_s<LP>(a.grad, e), p, m, v, a);
+            adam_e<WD>(load_s<LP>(a.grad, e), p, m, v, a, sv);
             a.master[e] = p;
             a.m[e] = m;
             a.v[e] = v;
@@ -461,9 +552,11 @@ __global__ __launch_bounds__(kScalarBlock) void adam_elem_kernel(AdamLaunch a, R
 // Heavy-ball SGD with L2 weight decay on one element, in the order the public
 // header states; p and the momentum buffer b are updated in place.
 template <int MOM, int WD>
-__device__ __forceinline__ void sgd_e(float graw, float& p, float& b, const SgdLaunch& a)
+__device__ __forceinline__ void sgd_e(float graw, float& p, float& b, const SgdLaunch& a,
+                                      const StepVals& sv)
 {
-    float g = graw * a.inv_scale;
+    float g = graw * sv.inv_scale;
+    g = g * sv.clip;                       // exact when the coefficient is 1
     if constexpr (WD) g = g + a.wd * p;
     float d = g;
     if constexpr (MOM) {
@@ -493,7 +586,8 @@ __global__ __launch_bounds__(kSgdBlock) void sgd_vec_kernel(SgdLaunch a)
             if constexpr (MOM) b[u] = ld_nt<f4>(bb, q);
         }
     }
-    if (gated_off(a.gate)) return;
+    const StepVals sv = step_vals(a.src, a.inv_scale, 1.0f, 1.0f);
+    if (sv.skip) return;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
         const int64_t q = q0 + u * kSgdBlock;
@@ -505,7 +599,7 @@ __global__ __launch_bounds__(kSgdBlock) void sgd_vec_kernel(SgdLaunch a)
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 float pk = pp[k], bk = buf[k];
-                sgd_e<MOM, WD>(gf[k], pk, bk, a);
+                sgd_e<MOM, WD>(gf[k], pk, bk, a, sv);
                 pp[k] = pk;
                 buf[k] = bk;
             }
@@ -521,7 +615,8 @@ template <int LP, int MOM, int WD>
 __global__ __launch_bounds__(kScalarBlock) void sgd_elem_kernel(SgdLaunch a, Ranges rg)
 {
     using T = typename Fmt<LP>::T;
-    if (gated_off(a.gate)) return;
+    const StepVals sv = step_vals(a.src, a.inv_scale, 1.0f, 1.0f);
+    if (sv.skip) return;
     const int64_t cnt = rg.count();
     for (int j = 0; j < (int)(kScalarElemsPerBlock / kScalarBlock); ++j) {
         const int64_t k = (int64_t)blockIdx.x * kScalarElemsPerBlock + j * kScalarBlock + threadIdx.x;
@@ -530,12 +625,19 @@ __global__ __launch_bounds__(kScalarBlock) void sgd_elem_kernel(SgdLaunch a, Ran
             float p = a.master[e];
             float b = 0.f;
             if constexpr (MOM) b = a.mom[e];
-            sgd_e<MOM, WD>(load_s<LP>(a.grad, e), p, b, a);
+            sgd_e<MOM, WD>(load_s<LP>(a.grad, e), p, b, a, sv);
             a.master[e] = p;
             if constexpr (MOM) a.mom[e] = b;
             if constexpr (LP != 3) static_cast<T*>(a.param)[e] = static_cast<T>(p);
         }
     }
+}
+
+// ----------------------------------------------------------------- device-resident step
+
+__global__ __launch_bounds__(64) void load_state_kernel(DevState* d, DevState init)
+{
+    if (threadIdx.x == 0) *d = init;
 }
 
 // ----------------------------------------------------------------- launches
@@ -718,16 +820,32 @@ hipError_t launch_scan(const ScanLaunch& L, hipStream_t s)
 }
 
 hipError_t launch_finalize(const double* partial, int64_t nslots, double* level1,
-                           CheckResult* out, hipStream_t s)
+                           CheckResult* out, double max_norm, DevState* dev,
+                           const PrepareArgs& pa, hipStream_t s)
 {
+    const PrepareArgs none{};
+    if (nslots <= kFoldOneLevel) {
+        // few partials: one workgroup sums them all (one launch less)
+        fold_kernel<<<1, kFoldBlock, 0, s>>>(partial, nslots, nslots, nullptr, out, max_norm, dev,
+                                             pa);
+        return hipGetLastError();
+    }
     int64_t g1 = ceil_div(nslots, 1024);
-    if (g1 < 1) g1 = 1;
     if (g1 > kFoldMaxBlocks) g1 = kFoldMaxBlocks;
     const int64_t chunk = ceil_div(nslots, g1);
-    fold_kernel<<<(unsigned)g1, kFoldBlock, 0, s>>>(partial, nslots, chunk, level1);
-    fold_kernel<<<1, kFoldBlock, 0, s>>>(level1, g1, g1, &out->sumsq);
+    fold_kernel<<<(unsigned)g1, kFoldBlock, 0, s>>>(partial, nslots, chunk, level1, nullptr, 0.0,
+                                                    nullptr, none);
+    fold_kernel<<<1, kFoldBlock, 0, s>>>(level1, g1, g1, nullptr, out, max_norm, dev, pa);
     return hipGetLastError();
 }
+
+hipError_t launch_load_state(DevState* d, const DevState& init, hipStream_t s)
+{
+    load_state_kernel<<<1, 64, 0, s>>>(d, init);
+    return hipGetLastError();
+}
+
+
 
 hipError_t launch_adam(const AdamLaunch& a, hipStream_t s)
 {

@@ -79,6 +79,14 @@ struct zero_shard_s {
     hipEvent_t result_ready = nullptr;
     double pend_pw1 = 1.0, pend_pw2 = 1.0;
     bool pend_same_betas = false;
+    // global-norm clipping limit (0: off); a merged step's coefficient
+    double max_norm = 0.0;
+    bool merged = false;
+    float merge_clip = 1.0f;
+    // device-resident flow: the step state in device memory, its pinned copy
+    zk::DevState* dev = nullptr;
+    zk::DevState* host_dev = nullptr;
+    bool device_mode = false;
 };
 
 namespace {
@@ -316,7 +324,7 @@ static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m,
     h->nslots = nslots;
 
     const size_t ws_bytes = sizeof(double) * (size_t)(nslots + zk::kFoldMaxBlocks) +
-                            sizeof(zk::CheckResult);
+                            sizeof(zk::CheckResult) + sizeof(zk::DevState);
     e = hipMalloc(&h->ws, ws_bytes);
     if (e != hipSuccess) {
         delete h;
@@ -327,6 +335,7 @@ static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m,
     h->partial = static_cast<double*>(h->ws);
     h->level1 = h->partial + nslots;
     h->result = reinterpret_cast<zk::CheckResult*>(h->level1 + zk::kFoldMaxBlocks);
+    h->dev = reinterpret_cast<zk::DevState*>(h->result + 1);
 
     int lds_cu = 0, lds_blk = 0;
     if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
@@ -340,14 +349,16 @@ static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m,
     h->lds_sgd_mom = lds_reserve_for(lds_cu, lds_blk, zk::kSgdMomPerCU);
     h->lds_sgd_plain = lds_reserve_for(lds_cu, lds_blk, zk::kSgdPlainPerCU);
     h->lds_reduce = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCU);
-    e = hipHostMalloc(reinterpret_cast<void**>(&h->host_result), 64, hipHostMallocDefault);
+    static_assert(sizeof(zk::CheckResult) <= 64 && sizeof(zk::DevState) <= 192, "pinned layout");
+    e = hipHostMalloc(reinterpret_cast<void**>(&h->host_result), 256, hipHostMallocDefault);
     if (e != hipSuccess) {
         (void)hipFree(h->ws);
         delete h;
         (void)hipGetLastError();
         return fail(ZERO_ERR_OOM, "init: hipHostMalloc: %s", hipGetErrorString(e));
     }
-    std::memset(h->host_result, 0, 64);
+    std::memset(h->host_result, 0, 256);
+    h->host_dev = reinterpret_cast<zk::DevState*>(reinterpret_cast<char*>(h->host_result) + 64);
     e = hipEventCreateWithFlags(&h->result_ready, hipEventDisableTiming);
     if (e != hipSuccess) {
         (void)hipFree(h->ws);
@@ -357,6 +368,66 @@ static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m,
         return fail(ZERO_ERR_HIP, "init: hipEventCreate: %s", hipGetErrorString(e));
     }
     *out = h;
+    return ZERO_OK;
+}
+
+// Validate R contribution pointers of a handle's storage format.
+static zero_status check_contribs(const zero_shard_s* h, const void* const* contribs,
+                                  int32_t n_contrib, const char* who)
+{
+    if (!contribs) return fail(ZERO_ERR_INVALID_ARG, "%s: NULL contribs", who);
+    if (n_contrib < 1 || n_contrib > ZERO_MAX_CONTRIB)
+        return fail(ZERO_ERR_INVALID_ARG, "%s: n_contrib %d outside [1, %d]", who, n_contrib,
+                    ZERO_MAX_CONTRIB);
+    for (int r = 0; r < n_contrib; ++r) {
+        if (!contribs[r]) return fail(ZERO_ERR_INVALID_ARG, "%s: contribution %d is NULL", who, r);
+        if ((uintptr_t)contribs[r] % (uintptr_t)h->esz != 0)
+            return fail(ZERO_ERR_INVALID_ARG, "%s: contribution %d not %d-byte aligned", who, r,
+                        h->esz);
+    }
+    return ZERO_OK;
+}
+
+// Launch the reduce of the bucket [off, off + len) of the shard from the
+// contributions' bucket pointers, writing partial slots from slot_base on;
+// dev set: the unscale factor comes from the device state.
+static zero_status enqueue_reduce(zero_shard_s* h, const void* const* ptrs, int32_t n_contrib,
+                                  int64_t off, int64_t len, int64_t slot_base,
+                                  const zk::DevState* dev, hipStream_t s, int64_t* blocks_out,
+                                  const char* who)
+{
+    zk::ReduceLaunch L;
+    std::memset(&L, 0, sizeof(L));
+    uintptr_t addr[ZERO_MAX_CONTRIB + 1];
+    int elt[ZERO_MAX_CONTRIB + 1], align[ZERO_MAX_CONTRIB + 1];
+    for (int r = 0; r < n_contrib; ++r) {
+        L.c.p[r] = ptrs[r];
+        addr[r] = (uintptr_t)ptrs[r];
+        elt[r] = h->esz;
+        align[r] = 16;
+    }
+    char* out = static_cast<char*>(h->d.grad_shard) + off * h->esz;
+    addr[n_contrib] = (uintptr_t)out;
+    elt[n_contrib] = h->esz;
+    align[n_contrib] = 16;
+    L.out = out;
+    L.n = len;
+    const int W = zk::run_width(h->d.lp);
+    split(len, common_head(addr, elt, align, n_contrib + 1), W, &L.head, &L.nvec, &L.vec_ok);
+    L.R = n_contrib;
+    L.lp = (int32_t)h->d.lp;
+    L.inv_r = (float)(1.0 / (double)n_contrib);
+    L.inv_scale = (float)(1.0 / h->scale);
+    L.partial = h->partial;
+    L.slot_base = slot_base;
+    L.lds_reserve = h->lds_reduce;
+    L.dev = dev;
+    const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::red_runs(L.R));
+    if (L.slot_base + blocks > h->nslots)
+        return fail(ZERO_ERR_UNSUPPORTED, "%s: partial slots exhausted", who);
+    hipError_t e = zk::launch_reduce(L, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+    *blocks_out = blocks;
     return ZERO_OK;
 }
 
@@ -423,16 +494,10 @@ zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int3
                                int64_t bucket_off, int64_t bucket_len, void* stream)
 {
     if (!live(h)) return fail(ZERO_ERR_STATE, "bucket_reduce: not a live handle");
-    if (!contribs) return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: NULL contribs");
-    if (n_contrib < 1 || n_contrib > ZERO_MAX_CONTRIB)
-        return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: n_contrib %d outside [1, %d]", n_contrib,
-                    ZERO_MAX_CONTRIB);
-    for (int r = 0; r < n_contrib; ++r) {
-        if (!contribs[r]) return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: contribution %d is NULL", r);
-        if ((uintptr_t)contribs[r] % (uintptr_t)h->esz != 0)
-            return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: contribution %d not %d-byte aligned", r,
-                        h->esz);
-    }
+    if (h->device_mode)
+        return fail(ZERO_ERR_STATE, "bucket_reduce: device-resident flow active; call zero_device_end");
+    zero_status cst = check_contribs(h, contribs, n_contrib, "bucket_reduce");
+    if (cst != ZERO_OK) return cst;
     if (bucket_len < 1) return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: bucket_len must be >= 1");
     if (bucket_off < 0 || bucket_off >= h->S || bucket_len > h->S - bucket_off)
         return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: bucket [%lld, +%lld) outside [0, %lld)",
@@ -451,69 +516,57 @@ zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int3
     if (bucket_off + bucket_len < h->S && bucket_len != h->d.bucket_elems)
         return fail(ZERO_ERR_STATE, "bucket_reduce: only the last bucket may be shorter than C_B");
 
-    zk::ReduceLaunch L;
-    std::memset(&L, 0, sizeof(L));
-    uintptr_t addr[ZERO_MAX_CONTRIB + 1];
-    int elt[ZERO_MAX_CONTRIB + 1], align[ZERO_MAX_CONTRIB + 1];
-    for (int r = 0; r < n_contrib; ++r) {
-        L.c.p[r] = contribs[r];
-        addr[r] = (uintptr_t)contribs[r];
-        elt[r] = h->esz;
-        align[r] = 16;
-    }
-    char* out = static_cast<char*>(h->d.grad_shard) + bucket_off * h->esz;
-    addr[n_contrib] = (uintptr_t)out;
-    elt[n_contrib] = h->esz;
-    align[n_contrib] = 16;
-    L.out = out;
-    L.n = bucket_len;
-    const int W = zk::run_width(h->d.lp);
-    split(bucket_len, common_head(addr, elt, align, n_contrib + 1), W, &L.head, &L.nvec, &L.vec_ok);
-    L.R = n_contrib;
-    L.lp = (int32_t)h->d.lp;
-    L.inv_r = (float)(1.0 / (double)n_contrib);
-    L.inv_scale = (float)(1.0 / h->scale);
-    L.partial = h->partial;
-    L.slot_base = h->phase == kIdle ? 0 : h->slot_cursor;
-    L.lds_reserve = h->lds_reduce;
-    const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::red_runs(L.R));
-    if (L.slot_base + blocks > h->nslots)
-        return fail(ZERO_ERR_UNSUPPORTED, "bucket_reduce: partial slots exhausted");
-    hipError_t e = zk::launch_reduce(L, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "bucket_reduce: launch");
+    int64_t blocks = 0;
+    const int64_t slot_base = h->phase == kIdle ? 0 : h->slot_cursor;
+    zero_status st = enqueue_reduce(h, contribs, n_contrib, bucket_off, bucket_len, slot_base, nullptr,
+                                    static_cast<hipStream_t>(stream), &blocks, "bucket_reduce");
+    if (st != ZERO_OK) return st;
     h->covered = bucket_off + bucket_len;
-    h->slot_cursor = L.slot_base + blocks;
+    h->slot_cursor = slot_base + blocks;
     h->phase = kReducing;
     return ZERO_OK;
 }
 
 }  // extern "C"
 
+// Launch the stand-alone scan of the stored grad_shard (no bucket reduced this
+// step) into partial slots from 0; returns the slots written.
+static zero_status enqueue_scan(zero_shard_s* h, const zk::DevState* dev, hipStream_t s,
+                                int64_t* slots, const char* who)
+{
+    zk::ScanLaunch L;
+    std::memset(&L, 0, sizeof(L));
+    const uintptr_t a = (uintptr_t)h->d.grad_shard;
+    const int el = h->esz, al = 16;
+    const int W = zk::run_width(h->d.lp);
+    L.g = h->d.grad_shard;
+    L.n = h->S;
+    split(h->S, common_head(&a, &el, &al, 1), W, &L.head, &L.nvec, &L.vec_ok);
+    L.lp = (int32_t)h->d.lp;
+    L.inv_scale = (float)(1.0 / h->scale);
+    L.partial = h->partial;
+    L.slot_base = 0;
+    L.lds_reserve = h->lds_reduce;
+    L.dev = dev;
+    hipError_t e = zk::launch_scan(L, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+    *slots = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::kRedRuns);
+    return ZERO_OK;
+}
+
 // Launch the check of the step on `s`: the stand-alone scan when no bucket was
-// reduced, the fixed-order fold of the partials, and the copy of the result to
-// pinned host memory.  Call only in phase kIdle or kReducing with full coverage.
+// reduced, the fixed-order fold of the partials (with the clipping
+// coefficient), and the copy of the result to pinned host memory.  Call only
+// in phase kIdle or kReducing with full coverage.
 static zero_status launch_check(zero_shard_s* h, hipStream_t s, const char* who)
 {
-    hipError_t e;
     if (h->phase == kIdle) {
-        zk::ScanLaunch L;
-        std::memset(&L, 0, sizeof(L));
-        const uintptr_t a = (uintptr_t)h->d.grad_shard;
-        const int el = h->esz, al = 16;
-        const int W = zk::run_width(h->d.lp);
-        L.g = h->d.grad_shard;
-        L.n = h->S;
-        split(h->S, common_head(&a, &el, &al, 1), W, &L.head, &L.nvec, &L.vec_ok);
-        L.lp = (int32_t)h->d.lp;
-        L.inv_scale = (float)(1.0 / h->scale);
-        L.partial = h->partial;
-        L.slot_base = 0;
-        L.lds_reserve = h->lds_reduce;
-        e = zk::launch_scan(L, s);
-        if (e != hipSuccess) return hip_fail(e, who);
-        h->slot_cursor = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::kRedRuns);
+        zero_status st = enqueue_scan(h, nullptr, s, &h->slot_cursor, who);
+        if (st != ZERO_OK) return st;
     }
-    e = zk::launch_finalize(h->partial, h->slot_cursor, h->level1, h->result, s);
+    const zk::PrepareArgs none{};
+    hipError_t e = zk::launch_finalize(h->partial, h->slot_cursor, h->level1, h->result, h->max_norm,
+                                       nullptr, none, s);
     if (e != hipSuccess) return hip_fail(e, who);
     e = hipMemcpyAsync(h->host_result, h->result, sizeof(zk::CheckResult), hipMemcpyDeviceToHost, s);
     if (e != hipSuccess) return hip_fail(e, who);
@@ -538,11 +591,41 @@ static zero_step_info read_check(zero_shard_s* h)
     return info;
 }
 
-// Launch Adam for applied step t = h->t + 1 with hyper-parameters hp; gate is
-// the device result a gated launch reads (nullptr = apply unconditionally).
+// Where the update of each flow takes its per-step values.  Synchronous check:
+// the clipping coefficient from the device result (the host-computed one after
+// a merge); gated: also skip on the result's NaN; device-resident: everything
+// from the device state.
+static zk::StepSource source_sync(const zero_shard_s* h)
+{
+    zk::StepSource src{};
+    src.res = h->merged ? nullptr : h->result;
+    src.clip = h->merged ? h->merge_clip : 1.0f;
+    return src;
+}
+
+static zk::StepSource source_gated(const zero_shard_s* h)
+{
+    zk::StepSource src{};
+    src.res = h->result;
+    src.gate = 1;
+    src.clip = 1.0f;
+    return src;
+}
+
+static zk::StepSource source_device(const zero_shard_s* h)
+{
+    zk::StepSource src{};
+    src.res = h->result;
+    src.dev = h->dev;
+    src.clip = 1.0f;
+    return src;
+}
+
+// Launch Adam for applied step t = h->t + 1 with hyper-parameters hp; src says
+// where the kernels take the per-step values (see source_*).
 // Returns the fp64 powers beta^t it used and whether they extend the cache.
 static zero_status launch_adam_step(zero_shard_s* h, const zero_adam_hparams& hp, hipStream_t s,
-                                    const zk::CheckResult* gate, double* pw1_out,
+                                    const zk::StepSource& src, double* pw1_out,
                                     double* pw2_out, bool* same_betas_out, const char* who)
 {
     const int64_t t = h->t + 1;
@@ -583,7 +666,7 @@ static zero_status launch_adam_step(zero_shard_s* h, const zero_adam_hparams& hp
     a.inv_scale = (float)(1.0 / h->scale);
     a.wd_kind = a.wd == 0.0f ? zk::kWdNone
               : (hp.wd_mode == ZERO_WD_L2 ? zk::kWdL2 : zk::kWdDecoupled);
-    a.gate = gate;
+    a.src = src;
     hipError_t e = zk::launch_adam(a, s);
     if (e != hipSuccess) return hip_fail(e, who);
     *pw1_out = pw1;
@@ -592,10 +675,10 @@ static zero_status launch_adam_step(zero_shard_s* h, const zero_adam_hparams& hp
     return ZERO_OK;
 }
 
-// Launch SGD for applied step t + 1 with hyper-parameters hp; gate as in
+// Launch SGD for applied step t + 1 with hyper-parameters hp; src as in
 // launch_adam_step.
 static zero_status launch_sgd_step(zero_shard_s* h, const zero_sgd_hparams& hp, hipStream_t s,
-                                   const zk::CheckResult* gate, const char* who)
+                                   const zk::StepSource& src, const char* who)
 {
     zk::SgdLaunch a;
     std::memset(&a, 0, sizeof(a));
@@ -623,7 +706,7 @@ static zero_status launch_sgd_step(zero_shard_s* h, const zero_sgd_hparams& hp, 
     a.wd = (float)hp.weight_decay;
     a.has_wd = a.wd != 0.0f;
     a.inv_scale = (float)(1.0 / h->scale);
-    a.gate = gate;
+    a.src = src;
     hipError_t e = zk::launch_sgd(a, s);
     if (e != hipSuccess) return hip_fail(e, who);
     return ZERO_OK;
@@ -652,6 +735,7 @@ static void commit_step(zero_shard_s* h, zero_step_info* info, double pw1, doubl
     h->phase = kIdle;
     h->covered = 0;
     h->slot_cursor = 0;
+    h->merged = false;
 }
 
 extern "C" {
@@ -659,6 +743,8 @@ extern "C" {
 zero_status zero_overflow_check(zero_shard_t h, void* stream, zero_step_info* out)
 {
     if (!live(h)) return fail(ZERO_ERR_STATE, "overflow_check: not a live handle");
+    if (h->device_mode)
+        return fail(ZERO_ERR_STATE, "%s: device-resident flow active; call zero_device_end", "overflow_check");
     if (!out) return fail(ZERO_ERR_INVALID_ARG, "overflow_check: NULL out");
     if (h->phase == kPending)
         return fail(ZERO_ERR_STATE, "overflow_check: a gated step is pending; call zero_step_resolve");
@@ -696,8 +782,8 @@ zero_status zero_adam_step(zero_shard_t h, const zero_adam_hparams* hp_in, void*
     double pw1 = 1.0, pw2 = 1.0;
     bool same = false;
     if (!info.overflow) {
-        zero_status st = launch_adam_step(h, hp, static_cast<hipStream_t>(stream), nullptr, &pw1,
-                                          &pw2, &same, "adam_step: launch");
+        zero_status st = launch_adam_step(h, hp, static_cast<hipStream_t>(stream), source_sync(h),
+                                          &pw1, &pw2, &same, "adam_step: launch");
         if (st != ZERO_OK) return st;
     }
     commit_step(h, &info, pw1, pw2, same);
@@ -719,6 +805,13 @@ zero_status zero_overflow_merge(zero_shard_t h, int32_t global_overflow, double 
     h->check.overflow = global_overflow;
     h->check.skipped = global_overflow;
     h->check.grad_norm = global_grad_norm;
+    // the clipping coefficient of the global norm, by the rule the fold applies
+    h->merged = true;
+    h->merge_clip = 1.0f;
+    if (h->max_norm > 0.0 && !global_overflow) {
+        const double c = h->max_norm / (global_grad_norm + 1e-6);
+        if (c < 1.0) h->merge_clip = (float)c;
+    }
     int64_t g;
     next_scale(h, global_overflow, &h->check.scale_next, &g);
     if (out) *out = h->check;
@@ -728,6 +821,8 @@ zero_status zero_overflow_merge(zero_shard_t h, int32_t global_overflow, double 
 zero_status zero_adam_step_gated(zero_shard_t h, const zero_adam_hparams* hp_in, void* stream)
 {
     if (!live(h)) return fail(ZERO_ERR_STATE, "adam_step_gated: not a live handle");
+    if (h->device_mode)
+        return fail(ZERO_ERR_STATE, "%s: device-resident flow active; call zero_device_end", "adam_step_gated");
     if (h->opt != kOptAdam) return fail(ZERO_ERR_STATE, "adam_step_gated: handle was created for SGD");
     if (h->phase == kChecked || h->phase == kPending)
         return fail(ZERO_ERR_STATE, "adam_step_gated: step already checked or pending");
@@ -748,7 +843,7 @@ zero_status zero_adam_step_gated(zero_shard_t h, const zero_adam_hparams* hp_in,
         if (e != hipSuccess) st = hip_fail(e, "adam_step_gated: event");
     }
     if (st == ZERO_OK)
-        st = launch_adam_step(h, hp, s, h->result, &h->pend_pw1, &h->pend_pw2,
+        st = launch_adam_step(h, hp, s, source_gated(h), &h->pend_pw1, &h->pend_pw2,
                               &h->pend_same_betas, "adam_step_gated: launch");
     if (st != ZERO_OK) {
         h->phase = before;
@@ -773,7 +868,7 @@ zero_status zero_sgd_step(zero_shard_t h, const zero_sgd_hparams* hp_in, void* s
     const zero_sgd_hparams& hp = hp_in ? *hp_in : h->sgd;
     zero_step_info info = h->check;
     if (!info.overflow) {
-        zero_status st = launch_sgd_step(h, hp, static_cast<hipStream_t>(stream), nullptr,
+        zero_status st = launch_sgd_step(h, hp, static_cast<hipStream_t>(stream), source_sync(h),
                                          "sgd_step: launch");
         if (st != ZERO_OK) return st;
     }
@@ -785,6 +880,8 @@ zero_status zero_sgd_step(zero_shard_t h, const zero_sgd_hparams* hp_in, void* s
 zero_status zero_sgd_step_gated(zero_shard_t h, const zero_sgd_hparams* hp_in, void* stream)
 {
     if (!live(h)) return fail(ZERO_ERR_STATE, "sgd_step_gated: not a live handle");
+    if (h->device_mode)
+        return fail(ZERO_ERR_STATE, "%s: device-resident flow active; call zero_device_end", "sgd_step_gated");
     if (h->opt != kOptSgd) return fail(ZERO_ERR_STATE, "sgd_step_gated: handle was created for Adam");
     if (h->phase == kChecked || h->phase == kPending)
         return fail(ZERO_ERR_STATE, "sgd_step_gated: step already checked or pending");
@@ -804,7 +901,7 @@ zero_status zero_sgd_step_gated(zero_shard_t h, const zero_sgd_hparams* hp_in, v
         hipError_t e = hipEventRecord(h->result_ready, s);
         if (e != hipSuccess) st = hip_fail(e, "sgd_step_gated: event");
     }
-    if (st == ZERO_OK) st = launch_sgd_step(h, hp, s, h->result, "sgd_step_gated: launch");
+    if (st == ZERO_OK) st = launch_sgd_step(h, hp, s, source_gated(h), "sgd_step_gated: launch");
     if (st != ZERO_OK) {
         h->phase = before;
         h->slot_cursor = cursor_before;
@@ -832,6 +929,8 @@ zero_status zero_shard_get_counters(zero_shard_t h, int64_t* step_t, double* sca
                                     int64_t* good_steps)
 {
     if (!live(h)) return fail(ZERO_ERR_STATE, "get_counters: not a live handle");
+    if (h->device_mode)
+        return fail(ZERO_ERR_STATE, "%s: device-resident flow active; call zero_device_end", "get_counters");
     if (!step_t || !scale || !good_steps) return fail(ZERO_ERR_INVALID_ARG, "get_counters: NULL");
     *step_t = h->t;
     *scale = h->scale;
@@ -843,6 +942,8 @@ zero_status zero_shard_set_counters(zero_shard_t h, int64_t step_t, double scale
                                     int64_t good_steps)
 {
     if (!live(h)) return fail(ZERO_ERR_STATE, "set_counters: not a live handle");
+    if (h->device_mode)
+        return fail(ZERO_ERR_STATE, "%s: device-resident flow active; call zero_device_end", "set_counters");
     if (step_t < 0 || !finite_pos(scale) || good_steps < 0)
         return fail(ZERO_ERR_INVALID_ARG, "set_counters: values out of range");
     if (h->phase != kIdle) return fail(ZERO_ERR_STATE, "set_counters: a step is in progress");
@@ -850,6 +951,121 @@ zero_status zero_shard_set_counters(zero_shard_t h, int64_t step_t, double scale
     h->scale = scale;
     h->good_steps = good_steps;
     h->pw_t = -1;
+    return ZERO_OK;
+}
+
+zero_status zero_shard_set_clip(zero_shard_t h, double max_grad_norm)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "set_clip: not a live handle");
+    if (h->device_mode)
+        return fail(ZERO_ERR_STATE, "set_clip: device-resident flow active; call zero_device_end");
+    if (h->phase != kIdle) return fail(ZERO_ERR_STATE, "set_clip: a step is in progress");
+    if (!(std::isfinite(max_grad_norm) && max_grad_norm >= 0.0))
+        return fail(ZERO_ERR_INVALID_ARG, "set_clip: max_grad_norm must be finite and >= 0");
+    h->max_norm = max_grad_norm;
+    return ZERO_OK;
+}
+
+zero_status zero_device_begin(zero_shard_t h, void* stream)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "device_begin: not a live handle");
+    if (h->device_mode) return fail(ZERO_ERR_STATE, "device_begin: already active");
+    if (h->phase != kIdle) return fail(ZERO_ERR_STATE, "device_begin: a step is in progress");
+    zk::DevState init;
+    std::memset(&init, 0, sizeof(init));
+    init.scale = h->scale;
+    init.pw1 = h->opt == kOptAdam ? beta_pow(h->hp.beta1, h->t) : 1.0;
+    init.pw2 = h->opt == kOptAdam ? beta_pow(h->hp.beta2, h->t) : 1.0;
+    init.t = h->t;
+    init.good = h->good_steps;
+    init.inv_scale = (float)(1.0 / h->scale);
+    init.upd_inv_scale = init.inv_scale;
+    init.bc1 = init.bc2 = 1.0f;
+    hipError_t e = zk::launch_load_state(h->dev, init, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "device_begin: launch");
+    h->device_mode = true;
+    return ZERO_OK;
+}
+
+zero_status zero_step_device(zero_shard_t h, const void* const* contribs, int32_t n_contrib,
+                             void* stream)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "step_device: not a live handle");
+    if (!h->device_mode) return fail(ZERO_ERR_STATE, "step_device: call zero_device_begin first");
+    const bool scan = n_contrib == 0 && contribs == nullptr;
+    if (!scan) {
+        zero_status st = check_contribs(h, contribs, n_contrib, "step_device");
+        if (st != ZERO_OK) return st;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int64_t slots = 0;
+    if (scan) {
+        zero_status st = enqueue_scan(h, h->dev, s, &slots, "step_device: scan");
+        if (st != ZERO_OK) return st;
+    } else {
+        const void* ptrs[ZERO_MAX_CONTRIB];
+        for (int64_t off = 0; off < h->S; off += h->d.bucket_elems) {
+            const int64_t len = h->S - off < h->d.bucket_elems ? h->S - off : h->d.bucket_elems;
+            for (int r = 0; r < n_contrib; ++r)
+                ptrs[r] = static_cast<const char*>(contribs[r]) + off * h->esz;
+            int64_t blocks = 0;
+            zero_status st = enqueue_reduce(h, ptrs, n_contrib, off, len, slots, h->dev, s, &blocks,
+                                            "step_device: reduce");
+            if (st != ZERO_OK) return st;
+            slots += blocks;
+        }
+    }
+    zk::PrepareArgs pa;
+    std::memset(&pa, 0, sizeof(pa));
+    if (h->opt == kOptAdam) {
+        pa.b1 = (double)(float)h->hp.beta1;
+        pa.b2 = (double)(float)h->hp.beta2;
+        pa.bias_correction = h->hp.bias_correction;
+    }
+    pa.min_scale = h->ls.min_scale;
+    pa.dynamic = h->ls.dynamic;
+    pa.growth_interval = h->ls.growth_interval;
+    hipError_t e = zk::launch_finalize(h->partial, slots, h->level1, h->result, h->max_norm, h->dev,
+                                       pa, s);
+    if (e != hipSuccess) return hip_fail(e, "step_device: fold");
+    double pw1, pw2;
+    bool same;
+    zero_status st = h->opt == kOptAdam
+        ? launch_adam_step(h, h->hp, s, source_device(h), &pw1, &pw2, &same, "step_device: update")
+        : launch_sgd_step(h, h->sgd, s, source_device(h), "step_device: update");
+    return st;
+}
+
+zero_status zero_device_end(zero_shard_t h, void* stream, zero_step_info* out)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "device_end: not a live handle");
+    if (!h->device_mode) return fail(ZERO_ERR_STATE, "device_end: the device flow is not active");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(h->host_dev, h->dev, sizeof(zk::DevState), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "device_end: state copy");
+    const zk::DevState st = *h->host_dev;
+    h->t = st.t;
+    h->scale = st.scale;
+    h->good_steps = st.good;
+    if (h->opt == kOptAdam) {
+        h->pw1 = st.pw1;
+        h->pw2 = st.pw2;
+        h->pw_t = st.t;
+    }
+    h->device_mode = false;
+    zero_step_info info;
+    std::memset(&info, 0, sizeof(info));
+    info.step_t = h->t;
+    info.scale_next = h->scale;
+    info.scale_used = h->scale;
+    if (st.steps_run > 0) {
+        info.overflow = std::isnan(st.last_sumsq) ? 1 : 0;
+        info.skipped = info.overflow;
+        info.grad_norm = std::sqrt(st.last_sumsq);
+        info.scale_used = st.last_scale;
+    }
+    if (out) *out = info;
     return ZERO_OK;
 }
 
