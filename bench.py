@@ -101,6 +101,20 @@ def update_bytes_per_elem(w) -> int:
     return esz + 8 * fp32_arrays + (0 if w.lp == "fp32" else 2)
 
 
+def host_info() -> dict:
+    """CPU model and the cores this process may run on (the oracle uses one)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(w, state_host, contribs_host, bucket_elems):
     import oracle
     if w.opt == "sgd":
@@ -314,7 +328,8 @@ def main() -> int:
         cpu = {"value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
                "sample": f"one full step (reduce of {R} contributions, flag/norm, "
                          f"{'SGD' if sgd else 'Adam'}) on the "
-                         f"first {n} elements of the same shard; {dt:.1f} s single-threaded"}
+                         f"first {n} elements of the same shard; {dt:.1f} s single-threaded",
+               "host": host_info()}
         del state_host, contribs_host
     zs.zero_shard_destroy(h)
 
