@@ -122,6 +122,19 @@ def test_device_flow_equals_sync_bitwise(name, clip):
             assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), (name, clip, k, "run")
 
 
+@pytest.mark.parametrize("name", ["adam_fp16", "sgdm_fp32"])
+def test_device_flow_misaligned(name):
+    """Arrays at odd element offsets (peeled heads and tails, and the
+    element-wise fallback) in the device-resident flow, against the oracle."""
+    w = _w(CASES[name], steps=3)
+    hp = _hp(name, w)
+    for o in (dict(master=1, m=3, v=2, grad=1, param=3, contrib=2), dict(grad=1, contrib=1)):
+        g = run_gpu(w, elems=70_001, bucket_elems=20_000, hp=hp, offsets=o, flow="device",
+                    max_norm=0.3 * _typical_norm(w, 70_001))
+        st, oi = run_oracle(w, g, bucket_elems=20_000, hp=hp, max_norm=0.3 * _typical_norm(w, 70_001))
+        compare(w, g, st, oi, f"device misaligned {name} {o}")
+
+
 def test_device_flow_scan_of_caller_filled_gradient():
     """contribs = None: the device step scans grad_shard (the P_os case)."""
     dev = torch.device("cuda", 0)

@@ -72,14 +72,18 @@ def _bits(x: np.ndarray) -> np.ndarray:
     return x.view(np.uint32) if x.dtype == np.float32 else x
 
 
-@pytest.mark.parametrize("name", ["tiny", "gpt2_1.5b", "7.5b_bf16", "13b_inf", "128b",
-                                  "c1_7.5b_sgdm", "c2_1.5b_sgd"])
-def test_full_size_sampled(name):
+@pytest.mark.parametrize("name,flow", [
+    ("tiny", "sync"), ("gpt2_1.5b", "sync"), ("7.5b_bf16", "sync"), ("13b_inf", "sync"),
+    ("128b", "sync"), ("c1_7.5b_sgdm", "sync"), ("c2_1.5b_sgd", "sync"),
+    # the device-resident flow bench.py times, at full size
+    ("gpt2_1.5b", "device"), ("13b_inf", "device"), ("128b", "device"),
+])
+def test_full_size_sampled(name, flow):
     w = synth.WORKLOADS[name]
     S, R, cb, lp_t = w.shard, w.R, w.bucket_elems, w.torch_lp
     lp = LP_CODE[w.lp]
     dev = torch.device("cuda", 0)
-    log(f"[fullsize] {w.name}: S={S} R={R} C_B={cb} steps={w.steps}")
+    log(f"[fullsize] {w.name}: S={S} R={R} C_B={cb} steps={w.steps} flow={flow}")
     idx = sample_indices(w)
     idx_t = torch.from_numpy(idx).to(dev)
 
@@ -108,8 +112,13 @@ def test_full_size_sampled(name):
         for s in range(w.steps):
             synth.fill_contribs(w, bufs, s, scale, seed=0)
             cs = [stored(b[idx_t]) for b in bufs]
-            zs.reduce_buckets(h, bufs, S, cb)
-            chk = zs.zero_overflow_check(h)
+            if flow == "device":
+                zs.zero_device_begin(h)
+                zs.zero_step_device(h, bufs)
+                chk = zs.zero_device_end(h)
+            else:
+                zs.reduce_buckets(h, bufs, S, cb)
+                chk = zs.zero_overflow_check(h)
             ok, where = torch_reduce_equal(bufs, grad, R, lp_t)
             assert ok, (name, s, "full reduce differs at", where)
             oi = oracle.step(ost, cs, len(idx), ohp, ols)
@@ -122,7 +131,7 @@ def test_full_size_sampled(name):
                 inv = float(np.float32(1.0 / chk.scale_used))
                 tn = np.sqrt(torch_sumsq(grad, inv))
                 assert chk.grad_norm == pytest.approx(tn, rel=1e-9), (name, s)
-            info = step_fn(h)
+            info = chk if flow == "device" else step_fn(h)
             assert (info.overflow, info.skipped, info.step_t, info.scale_used, info.scale_next) == \
                 (oi.overflow, oi.skipped, oi.step_t, oi.scale_used, oi.scale_next), (name, s)
             log(f"[fullsize] {name} step {s}: overflow={info.overflow} t={info.step_t} "
