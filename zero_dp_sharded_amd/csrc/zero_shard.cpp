@@ -629,9 +629,12 @@ static zero_status launch_adam_step(zero_shard_s* h, const zero_adam_hparams& hp
                                     double* pw2_out, bool* same_betas_out, const char* who)
 {
     const int64_t t = h->t + 1;
-    double pw1, pw2;
+    double pw1 = 1.0, pw2 = 1.0;
     const bool same_betas = hp.beta1 == h->hp.beta1 && hp.beta2 == h->hp.beta2;
-    if (same_betas && h->pw_t == t - 1) {
+    if (src.dev != nullptr) {
+        // the device-resident flow takes t and the bias corrections from the
+        // device state; the host copies are stale and unused
+    } else if (same_betas && h->pw_t == t - 1) {
         pw1 = h->pw1 * (double)(float)hp.beta1;
         pw2 = h->pw2 * (double)(float)hp.beta2;
     } else {
