@@ -114,7 +114,8 @@ typedef struct {
  * blog.vllbc.top page's (2b+K) Psi extension; the pages give no formula.
  * Textbook heavy-ball SGD with L2 weight decay, per element (fp32, each
  * operation rounded to nearest even, no fused multiply-add):
- *     g = f32(grad) * fp32(1/scale)      [wd != 0: g = g + wd*p]
+ *     g = f32(grad) * fp32(1/scale) ;  g = g * coef   [clipping, else 1]
+ *                                        [wd != 0: g = g + wd*p]
  *     with a momentum buffer: buf = mu*buf + g ; p = p - lr*buf
  *     plain:                  p = p - lr*g
  *     2-byte storage:         param = rne_2byte(p)
@@ -234,7 +235,8 @@ zero_status zero_shard_init_sgd(const zero_shard_desc* desc, const zero_sgd_hpar
  * for the last bucket, which ends at S.
  * Errors: INVALID_ARG (NULL, n_contrib outside [1, 64], bucket outside [0, S),
  * bucket_len < 1 or > bucket_elems, pointer not aligned to its element size),
- * STATE (dead handle, bucket not the next one, step already checked), HIP.
+ * STATE (dead handle, bucket not the next one, step already checked,
+ * device-resident flow active), HIP.
  */
 zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int32_t n_contrib,
                                int64_t bucket_off, int64_t bucket_len, void* stream);
@@ -244,11 +246,12 @@ zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int3
  * gradient shard and its unscaled squared norm, summed over per-block
  * partials in a fixed order (bitwise reproducible).  If no bucket was reduced
  * this step, the stored grad_shard is scanned instead (for callers that fill
- * it themselves).  Synchronises `stream` and fills *out (skipped = overflow;
- * step_t is the count before this step).  Calling it again before
- * zero_adam_step returns the same result.
+ * it themselves).  With clipping on, the same fold computes the step's
+ * clipping coefficient.  Synchronises `stream` and fills *out (skipped =
+ * overflow; step_t is the count before this step).  Calling it again before
+ * the step call returns the same result.
  * Errors: INVALID_ARG (NULL out), STATE (dead handle, buckets cover only part
- * of the shard), HIP.
+ * of the shard, device-resident flow active), HIP.
  */
 zero_status zero_overflow_check(zero_shard_t h, void* stream, zero_step_info* out);
 
@@ -257,17 +260,18 @@ zero_status zero_overflow_check(zero_shard_t h, void* stream, zero_step_info* ou
  * launched, the states are unchanged, t is unchanged, and with dynamic scaling
  * the scale halves.  Otherwise t += 1 and, per element (fp32, every operation
  * rounded to nearest even, no fused multiply-add):
- *     g = f32(grad) * fp32(1/scale)            [L2 mode: g = g + wd*p]
+ *     g = f32(grad) * fp32(1/scale) ;  g = g * coef   [coef: clipping, else 1]
+ *                                              [L2 mode: g = g + wd*p]
  *     m = b1*m + (1-b1)*g ;  v = b2*v + (1-b2)*(g*g)
  *     u = (m/bc1) / (sqrt(v/bc2) + eps)         [decoupled: u = u + wd*p]
- *     p = p - lr*u ;  param = rne_2byte(p)
+ *     p = p - lr*u ;  param = rne_2byte(p)      [no param with fp32 storage]
  * with b1, b2, lr, eps, wd the fp32 roundings of the hyper-parameters,
  * bc_k = fp32(1 - b_k^t) (b_k^t a product of t fp64 factors; 1 when bias
  * correction is off).  hp = NULL uses the values given at init; otherwise *hp
  * is used for this step only (its initial_step is ignored).  Asynchronous on
  * `stream`; *out (may be NULL) gets the step's result.
- * Errors: STATE (dead handle, no completed check this step), INVALID_ARG (hp out
- * of range), HIP.
+ * Errors: STATE (dead handle, an SGD handle, no completed check this step),
+ * INVALID_ARG (hp out of range), HIP.
  */
 zero_status zero_adam_step(zero_shard_t h, const zero_adam_hparams* hp, void* stream,
                            zero_step_info* out);
@@ -331,8 +335,9 @@ zero_status zero_overflow_merge(zero_shard_t h, int32_t global_overflow, double 
  * the update) and commits t and the loss scale.  Callers that hold a stream
  * of steps in flight keep the GPU busy across the decision.  hp as in
  * zero_adam_step.
- * Errors: STATE (dead handle, partial coverage, step already checked or
- * pending), INVALID_ARG (hp out of range), HIP.
+ * Errors: STATE (dead handle, an SGD handle, partial coverage, step already
+ * checked or pending, device-resident flow active), INVALID_ARG (hp out of
+ * range), HIP.
  */
 zero_status zero_adam_step_gated(zero_shard_t h, const zero_adam_hparams* hp, void* stream);
 
@@ -380,11 +385,13 @@ zero_status zero_step_device(zero_shard_t h, const void* const* contribs, int32_
                              void* stream);
 zero_status zero_device_end(zero_shard_t h, void* stream, zero_step_info* out);
 
-/* Step counter, current loss scale and clean-step count (for checkpoints). */
+/* Step counter, current loss scale and clean-step count (for checkpoints).
+ * STATE while the device-resident flow is active (the values live on the
+ * device until zero_device_end). */
 zero_status zero_shard_get_counters(zero_shard_t h, int64_t* step_t, double* scale,
                                     int64_t* good_steps);
-/* Restore them between steps (phase must be idle).  step_t >= 0, scale > 0,
- * good_steps >= 0. */
+/* Restore them between steps (phase must be idle, device-resident flow not
+ * active).  step_t >= 0, scale > 0, good_steps >= 0. */
 zero_status zero_shard_set_counters(zero_shard_t h, int64_t step_t, double scale,
                                     int64_t good_steps);
 

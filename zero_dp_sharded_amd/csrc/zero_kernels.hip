@@ -10,12 +10,14 @@
 //    (lane-consecutive 16-byte or 8-byte pieces);
 //  - nontemporal loads and stores (each byte is touched once per step);
 //  - a cap on resident workgroups per CU, set by reserving dynamic LDS the
-//    kernels never touch: with the 4 to 7 concurrent streams of these kernels,
-//    fewer resident waves (10 per CU for the update, 16 for the reduce)
-//    sustain more HBM bandwidth than full occupancy.
+//    kernels never touch: with the 3 to 9 concurrent streams of these kernels,
+//    fewer resident waves (10 per CU for Adam, 16 or 24 for SGD, 16 for the
+//    reduce) sustain more HBM bandwidth than full occupancy.
 // The only cross-lane work is the fixed-shape reduction of the overflow flag
 // and the squared gradient norm: wave butterfly, one LDS slot per wave, one
-// fp64 partial per workgroup, then a fixed-order two-level fold.
+// fp64 partial per workgroup, then a fixed-order fold of one or two levels
+// whose last lane also computes the clipping coefficient and, in the
+// device-resident flow, decides the step.
 //
 // Storage formats: fp16 and bf16 (2-byte grads and params beside the fp32
 // master copy) and fp32 (4-byte grads; the fp32 master is the parameter and
