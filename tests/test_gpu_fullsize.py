@@ -157,3 +157,58 @@ def test_full_size_sampled(name, flow):
         zs.zero_shard_destroy(h)
         del master, m, v, grad, param, bufs
         torch.cuda.empty_cache()
+
+
+def test_shard_beyond_2pow31_elements():
+    """A 2^31 + 1001-element shard (64-bit element indices throughout): two
+    steps, the second with +inf planted past index 2^31; sampled elements on
+    both sides of 2^31 against the oracle, the whole stored gradient against a
+    torch reduce."""
+    S = (1 << 31) + 1001
+    w = synth.Workload("2^31+1001-element shard, R=2, fp16", psi=S, nd=1, rank=0, R=2,
+                       bucket_elems=1 << 30, lp="fp16", scale=256.0, dynamic=1, lr=1e-3,
+                       weight_decay=0.01, steps=2)
+    dev = torch.device("cuda", 0)
+    log(f"[fullsize] {w.name}")
+    idx = np.array(sorted({0, 1, (1 << 30) - 1, 1 << 30, (1 << 31) - 2, (1 << 31) - 1, 1 << 31,
+                           (1 << 31) + 1, (1 << 31) + 7, S - 9, S - 2, S - 1}), dtype=np.int64)
+    rng = np.random.default_rng(3)
+    idx = np.unique(np.concatenate([idx, rng.integers(0, S, 4096)]))
+    idx_t = torch.from_numpy(idx).to(dev)
+    master, m, v = synth.init_state(w, dev, seed=0)
+    grad = torch.zeros(S, dtype=torch.float16, device=dev)
+    param = master.to(torch.float16)
+    bufs = synth.alloc_contribs(w, dev)
+    hp, ls = hp_of(w), ls_of(w)
+    ohp, ols = oracle_hp(hp), oracle_ls(ls)
+    ost = oracle.new_state(oracle.FP16, f32(master[idx_t]), f32(m[idx_t]), f32(v[idx_t]), ohp, ols)
+    h = zs.zero_shard_init(master, m, v, grad, param, psi=S, nd=1, rank=0,
+                           bucket_elems=w.bucket_elems, hp=hp, ls=ls)
+    try:
+        scale = w.scale
+        for s in range(2):
+            synth.fill_contribs(w, bufs, s, scale, seed=0)
+            if s == 1:
+                bufs[1][(1 << 31) + 7] = float("inf")
+            cs = [u16(b[idx_t]) for b in bufs]
+            zs.reduce_buckets(h, bufs, S, w.bucket_elems)
+            chk = zs.zero_overflow_check(h)
+            ok, where = torch_reduce_equal(bufs, grad, 2, torch.float16)
+            assert ok, ("reduce differs at", where)
+            oi = oracle.step(ost, cs, len(idx), ohp, ols)
+            assert chk.overflow == oi.overflow == s
+            gs = u16(grad[idx_t])
+            gn = lp_is_nan(gs, "fp16")
+            assert np.array_equal(gn, lp_is_nan(ost.grad, "fp16"))
+            assert np.array_equal(gs[~gn], ost.grad[~gn])
+            info = zs.zero_adam_step(h)
+            assert (info.step_t, info.scale_next) == (oi.step_t, oi.scale_next)
+            scale = info.scale_next
+        torch.cuda.synchronize()
+        assert np.array_equal(f32(master[idx_t]).view(np.uint32), ost.master.view(np.uint32))
+        assert np.array_equal(u16(param[idx_t]), ost.param)
+        assert ost.t == 1 and scale == 128.0
+    finally:
+        zs.zero_shard_destroy(h)
+        del master, m, v, grad, param, bufs
+        torch.cuda.empty_cache()
