@@ -155,7 +155,7 @@ def main() -> int:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the owner-rank step on one GPU only; "
-              "multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+              "multi-GPU runs are not supported (use --gpus 1).", file=sys.stderr)
         return 2
 
     import numpy as np

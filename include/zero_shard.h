@@ -57,7 +57,7 @@ typedef enum {
     ZERO_ERR_STATE = 2,       /* call out of order, bad coverage, dead handle */
     ZERO_ERR_HIP = 3,         /* the HIP runtime reported an error            */
     ZERO_ERR_OOM = 4,         /* workspace allocation failed                  */
-    ZERO_ERR_UNSUPPORTED = 5  /* valid request this build does not implement  */
+    ZERO_ERR_UNSUPPORTED = 5  /* valid request the library does not implement */
 } zero_status;
 
 /* Storage format of grads, contributions and params: the 2-byte formats of
@@ -151,7 +151,7 @@ typedef struct {
     double scale_next;
 } zero_step_info;
 
-/* Per-rank ledger.  Allocation of this build's shard, and the analytic per-rank
+/* Per-rank ledger.  Allocation of this library's shard, and the analytic per-rank
  * model-state bytes of stages 0..3 with their components (params, grads,
  * optimizer state) and the per-step communication volume in bytes, from the
  * blog.vllbc.top ZeRO/DeepSpeed page (stage formulas, Table 1, worked examples,
@@ -186,7 +186,7 @@ zero_status zero_state_bytes(int64_t psi, int32_t nd, int32_t n_contrib,
  * Same ledger with the parameter byte width b (2 or 4) and optimizer multiplier
  * K (12 mixed-precision Adam, 8 fp32 Adam, 4 SGD with momentum, 0 SGD) of the
  * page's (2b+K) Psi extension (its group C examples).  Allocation fields still
- * describe this build's Adam shard.
+ * describe this library's Adam shard.
  */
 zero_status zero_state_bytes_ex(int64_t psi, int32_t nd, int32_t n_contrib,
                                 int64_t bucket_elems, zero_lp_dtype lp,

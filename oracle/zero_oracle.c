@@ -403,7 +403,7 @@ void oracle_loss_scale_next(int32_t overflow, int32_t dynamic, int32_t growth_in
 /*   Stage 3 = (2b+K) Psi/Nd               (+ parameters partitioned)         */
 /* [P3] communication ledger: 2 Psi elements per rank per step for stages     */
 /* 0-2, 3 Psi for stage 3 (b bytes each); stage 1 with the step-end gather    */
-/* counts 3 Psi.  Allocated bytes of this build's shard: master, m, v in fp32 */
+/* counts 3 Psi.  Allocated bytes of the library's shard: master, m, v in fp32 */
 /* and grad, param in the 2-byte format = (12 + 2*lp) * S.                    */
 /* ------------------------------------------------------------------------ */
 
