@@ -21,7 +21,7 @@ from gpu_common import f32, u16
 pytestmark = pytest.mark.gpu
 
 
-def _run_pos(psi, nd, steps, inject=None, seed=3, lr=1e-3, wd=0.01, scale=1024.0):
+def _run_pos(psi, nd, steps, inject=None, seed=3, lr=1e-3, wd=0.01, scale=1024.0, max_norm=0.0):
     """Simulate nd P_os ranks; returns the all-gather buffer, fp32 states, infos
     per step (rank 0's) and the per-step full gradients (host bits)."""
     dev = torch.device("cuda", 0)
@@ -43,6 +43,9 @@ def _run_pos(psi, nd, steps, inject=None, seed=3, lr=1e-3, wd=0.01, scale=1024.0
           for r in range(nd)]
     infos, grads = [], []
     try:
+        for h in hs:
+            if max_norm:
+                zs.zero_shard_set_clip(h, max_norm)
         cur = scale
         for s in range(steps):
             g = torch.randn(psi, generator=gen, device=dev) * (1e-3 * cur)
@@ -130,3 +133,29 @@ def test_merge_argument_checks():
         assert zs.zero_adam_step(h).skipped == 1
     finally:
         zs.zero_shard_destroy(h)
+
+
+def test_pos_clipping_uses_the_merged_global_norm():
+    """With clipping on, every rank clips with the coefficient of the merged
+    global norm: the concatenated slices match the oracle's unsharded clipped
+    update (the coefficient comes from the host after the merge, so the bar is
+    the fp32 tolerance), as does a single rank clipping with its own norm."""
+    psi, nd, steps = 600_011, 4, 3
+    max_norm = 0.2                       # well below the typical norm (~0.8 here)
+    got = _run_pos(psi, nd, steps, max_norm=max_norm)
+    hp = oracle.AdamHP(lr=1e-3, weight_decay=0.01)
+    ls = oracle.LossScale(init_scale=1024.0)
+    st = oracle.new_state(oracle.FP16, got["master0"], np.zeros(psi), np.zeros(psi), hp, ls)
+    for s, g in enumerate(got["grads"]):
+        flag, ss = oracle.flag_sumsq(oracle.FP16, g, st.scale)
+        assert got["infos"][s][1].grad_norm == pytest.approx(np.sqrt(ss), rel=1e-9)
+        assert oracle.clip_coef(ss, max_norm) < 1.0
+        st.t += 1
+        oracle.adam_update(oracle.FP16, g, st.master, st.m, st.v, st.param,
+                           oracle.adam_scalars(hp, st.t, st.scale, oracle.clip_coef(ss, max_norm)))
+    rel = np.max(np.abs(got["master"].astype(np.float64) - st.master) /
+                 np.maximum(np.abs(st.master), 1.2e-38))
+    assert rel <= 1e-6
+    one = _run_pos(psi, 1, steps, max_norm=max_norm)       # one rank: its own norm is global
+    assert np.max(np.abs(one["master"].astype(np.float64) - st.master) /
+                  np.maximum(np.abs(st.master), 1.2e-38)) <= 1e-6
