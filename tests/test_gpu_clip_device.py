@@ -216,7 +216,7 @@ def test_device_flow_state_machine():
         zs.zero_shard_destroy(h)
 
 
-@pytest.mark.parametrize("name", ["adam_fp16", "sgdm_fp32"])
+@pytest.mark.parametrize("name", ["adam_fp16", "sgdm_fp32", "adam_bf16_l2", "sgd_fp32"])
 def test_graph_captured_step_replays(name):
     """One zero_step_device captured in a CUDA graph, replayed 6 times with the
     contributions refilled eagerly (and an overflow planted before replay 3)
@@ -287,3 +287,52 @@ def test_graph_captured_step_replays(name):
     finally:
         zs.zero_shard_destroy(ha)
         zs.zero_shard_destroy(hb)
+
+
+@pytest.mark.parametrize("name", ["adam_fp16", "sgdm_fp32"])
+def test_device_flow_after_counter_restore(name):
+    """Counters restored with zero_shard_set_counters (t = 7, scale 64, 3 clean
+    steps, as after a checkpoint): the device-resident flow starts from them
+    (bias corrections of steps 8, 9, ...) exactly as the synchronous flow does."""
+    w = _w(CASES[name], steps=3, dynamic=1, scale=64.0)
+    dev = torch.device("cuda", 0)
+    elems, cb = 90_001, 30_000
+    hp = _hp(name, w)
+    bufs = synth.alloc_contribs(w, dev, elems=elems)
+    out = {}
+    for flow in ("sync", "device"):
+        master0, m0, v0 = synth.init_state(w, dev, 0, elems=elems)
+        master = master0.clone()
+        m = m0.clone() if w.has_m else None
+        v = v0.clone() if w.has_v else None
+        grad = torch.zeros(elems, dtype=w.torch_lp, device=dev)
+        param = None if w.lp == "fp32" else master0.to(w.torch_lp)
+        if w.opt == "sgd":
+            h = zs.zero_shard_init_sgd(master, m, grad, param, psi=elems, nd=1, rank=0,
+                                       bucket_elems=cb, hp=hp, ls=ls_of(w))
+        else:
+            h = zs.zero_shard_init(master, m, v, grad, param, psi=elems, nd=1, rank=0,
+                                   bucket_elems=cb, hp=hp, ls=ls_of(w))
+        try:
+            zs.zero_shard_set_counters(h, 7, 64.0, 3)
+            infos = []
+            for s in range(w.steps):
+                synth.fill_contribs(w, bufs, s, 64.0, seed=0)
+                if flow == "sync":
+                    zs.reduce_buckets(h, bufs, elems, cb)
+                    zs.zero_overflow_check(h)
+                    infos.append(zs.zero_sgd_step(h) if w.opt == "sgd" else zs.zero_adam_step(h))
+                else:
+                    zs.zero_device_begin(h)
+                    zs.zero_step_device(h, bufs)
+                    infos.append(zs.zero_device_end(h))
+            torch.cuda.synchronize()
+            out[flow] = (infos, f32(master), None if m is None else f32(m))
+            assert zs.zero_shard_get_counters(h) == (10, 64.0, 6)
+        finally:
+            zs.zero_shard_destroy(h)
+    (ia, ma, mma), (ib, mb, mmb) = out["sync"], out["device"]
+    assert [(i.step_t, i.scale_next) for i in ia] == [(i.step_t, i.scale_next) for i in ib]
+    assert np.array_equal(ma.view(np.uint32), mb.view(np.uint32))
+    if mma is not None:
+        assert np.array_equal(mma.view(np.uint32), mmb.view(np.uint32))
