@@ -185,8 +185,12 @@ zero_status zero_state_bytes(int64_t psi, int32_t nd, int32_t n_contrib,
 /*
  * Same ledger with the parameter byte width b (2 or 4) and optimizer multiplier
  * K (12 mixed-precision Adam, 8 fp32 Adam, 4 SGD with momentum, 0 SGD) of the
- * page's (2b+K) Psi extension (its group C examples).  Allocation fields still
- * describe this library's Adam shard.
+ * page's (2b+K) Psi extension (its group C examples).  The allocation fields
+ * describe the shard a handle of storage lp and optimizer K holds: the fp32
+ * master, fp32 optimizer arrays for K - 4 bytes (2-byte storage, where K counts
+ * the master copy) or K bytes (ZERO_FP32 storage, where the master is the
+ * parameter), the stored gradient and the 2-byte parameter.  With b matching lp
+ * and Nd dividing psi, bytes_shard_total equals per_rank_stage[3].
  */
 zero_status zero_state_bytes_ex(int64_t psi, int32_t nd, int32_t n_contrib,
                                 int64_t bucket_elems, zero_lp_dtype lp,

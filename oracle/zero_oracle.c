@@ -425,12 +425,17 @@ void oracle_state_bytes(int64_t psi, int32_t nd, int32_t n_contrib, int64_t buck
     double P = (double)psi, N = (double)nd, b = (double)param_bytes, K = (double)k_optim;
     memset(out, 0, sizeof(*out));
     out->shard_elems = s;
+    /* The shard the library allocates for storage lp_bytes and optimizer
+       state K.  With 2-byte storage K counts the fp32 master copy (12 = 4
+       master + 8 Adam moments); with 4-byte storage the fp32 master is the
+       parameter and K counts only the optimizer's own arrays (8 Adam, 4 SGD
+       momentum, 0 plain SGD; the page's extension group C).  The optimizer's
+       arrays are fp32: a first one when they take 4 bytes, a second at 8. */
+    int64_t opt = lp_bytes == 4 ? k_optim : k_optim - 4;
     out->bytes_master = 4 * s;
-    out->bytes_m = 4 * s;
-    out->bytes_v = 4 * s;
+    out->bytes_m = opt >= 4 ? 4 * s : 0;
+    out->bytes_v = opt >= 8 ? 4 * s : 0;
     out->bytes_grad = (int64_t)lp_bytes * s;
-    /* with 4-byte storage the fp32 master is the parameter (the page's K = 8
-       fp32 Adam counts only m and v as optimizer state) */
     out->bytes_param = lp_bytes == 4 ? 0 : (int64_t)lp_bytes * s;
     out->bytes_shard_total = out->bytes_master + out->bytes_m + out->bytes_v
                            + out->bytes_grad + out->bytes_param;

@@ -58,11 +58,12 @@ def test_state_bytes_equals_oracle(oracle, psi, nd, R, cb):
     assert a == b
 
 
-@pytest.mark.parametrize("b,K", [(2, 12), (4, 8), (4, 4), (4, 0)])
-def test_state_bytes_ex_equals_oracle(oracle, b, K):
+@pytest.mark.parametrize("b,K", [(2, 12), (4, 8), (4, 4), (4, 0), (2, 8), (2, 4)])
+@pytest.mark.parametrize("lp,lp_bytes", [(zs.ZERO_BF16, 2), (zs.ZERO_FP32, 4)])
+def test_state_bytes_ex_equals_oracle(oracle, b, K, lp, lp_bytes):
     for psi, nd, R, cb in CASES:
-        a = zs.zero_state_bytes_ex(psi, nd, R, cb, zs.ZERO_BF16, b, K)
-        o = oracle.state_bytes(psi, nd, R, cb, param_bytes=b, k_optim=K)
+        a = zs.zero_state_bytes_ex(psi, nd, R, cb, lp, b, K)
+        o = oracle.state_bytes(psi, nd, R, cb, lp_bytes=lp_bytes, param_bytes=b, k_optim=K)
         assert a == o
 
 

@@ -132,3 +132,19 @@ def test_allocation_and_staging(oracle):
 ])
 def test_display_rule(oracle, val, shown):
     assert oracle.display_gb(val) == shown
+
+
+@pytest.mark.parametrize("psi,nd,lp_bytes,b,K", [
+    (7_500_000_000, 64, 2, 2, 12),     # example A: mixed-precision Adam
+    (128_000_000_000, 64, 2, 2, 12),   # example B
+    (7_500_000_000, 64, 4, 4, 4),      # C1: fp32 SGD with momentum
+    (1_500_000_000, 8, 4, 4, 0),       # C2: fp32 plain SGD
+    (1_500_000_000, 8, 4, 4, 8),       # fp32 Adam
+    (1_500_000_000, 8, 2, 2, 8),       # mixed-precision SGD with momentum (master + buffer)
+])
+def test_allocation_equals_stage3_bytes(oracle, psi, nd, lp_bytes, b, K):
+    """The shard one rank allocates is the Stage-3 per-rank share (2b+K)Psi/Nd
+    of the page's ledger, for every storage/optimizer pair of its examples."""
+    d = oracle.state_bytes(psi, nd, 1, 1, lp_bytes=lp_bytes, param_bytes=b, k_optim=K)
+    assert psi % nd == 0
+    assert d["bytes_shard_total"] == d["per_rank_stage"][3] == (2 * b + K) * psi // nd

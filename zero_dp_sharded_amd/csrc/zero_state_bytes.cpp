@@ -29,12 +29,16 @@ zero_status ledger(int64_t psi, int32_t nd, int32_t n_contrib, int64_t bucket_el
     zero_state_bytes_t r;
     std::memset(&r, 0, sizeof(r));
     r.shard_elems = shard;
-    r.bytes_master = shard * 4;
-    r.bytes_m = shard * 4;
-    r.bytes_v = shard * 4;
-    // Adam shard of this storage format: 4-byte storage keeps the parameter in
-    // the fp32 master itself (no 2-byte copy)
+    // The shard a handle allocates: the fp32 master (with 4-byte storage it is
+    // the parameter itself, and no 2-byte copy exists), the optimizer's fp32
+    // arrays, the stored gradient and the 2-byte parameter.  K counts the
+    // master copy with 2-byte storage (12 = 4 + 8 Adam) and only the
+    // optimizer's arrays with 4-byte storage (8 Adam, 4 SGD momentum, 0 SGD).
     const int64_t esz = lp == ZERO_FP32 ? 4 : 2;
+    const int64_t opt = lp == ZERO_FP32 ? k_optim : k_optim - 4;
+    r.bytes_master = shard * 4;
+    r.bytes_m = opt >= 4 ? shard * 4 : 0;
+    r.bytes_v = opt >= 8 ? shard * 4 : 0;
     r.bytes_grad = shard * esz;
     r.bytes_param = lp == ZERO_FP32 ? 0 : shard * 2;
     r.bytes_shard_total = r.bytes_master + r.bytes_m + r.bytes_v + r.bytes_grad + r.bytes_param;
