@@ -1,0 +1,46 @@
+"""bench.py's host-side contract, without a GPU: more than one GPU is refused
+with a message, the algorithmic byte counts match the kernels' definitions,
+and the traffic lookup only accepts counters taken on the current kernels."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from conftest import ROOT
+
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+from zero_dp_sharded_amd import synth  # noqa: E402
+
+
+@pytest.mark.parametrize("args,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}),
+                                      ([], {"WORLD_SIZE": "4"})])
+def test_more_than_one_gpu_is_refused(args, env):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                       env=dict(os.environ, **env), capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_update_bytes_per_element():
+    W = synth.WORKLOADS
+    assert bench.update_bytes_per_elem(W["128b"]) == 28        # 2 + 12 read, 12 + 2 written
+    assert bench.update_bytes_per_elem(W["7.5b_bf16"]) == 28
+    assert bench.update_bytes_per_elem(W["c1_7.5b_sgdm"]) == 20  # 4 + 8 read, 8 written
+    assert bench.update_bytes_per_elem(W["c2_1.5b_sgd"]) == 12   # 4 + 4 read, 4 written
+
+
+def test_traffic_only_from_counters_of_the_current_kernels(tmp_path, monkeypatch):
+    assert bench.measured_traffic("no_such_workload", 1) is None
+    d = {"kernel_source_sha256_16": bench.kernel_source_hash(), "elems_per_launch": 10,
+         "hbm_bytes_per_launch": 123.0}
+    (tmp_path / "traffic_w.json").write_text(json.dumps(d))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.measured_traffic("w", 10) == 123.0
+    assert bench.measured_traffic("w", 11) is None              # another shard size
+    d["kernel_source_sha256_16"] = "0" * 16
+    (tmp_path / "traffic_w.json").write_text(json.dumps(d))
+    assert bench.measured_traffic("w", 10) is None              # stale kernels
