@@ -741,6 +741,46 @@ static void commit_step(zero_shard_s* h, zero_step_info* info, double pw1, doubl
     h->merged = false;
 }
 
+// Checks shared by the gated step calls of both optimizers.
+static zero_status gated_preconditions(zero_shard_s* h, Opt opt, const char* who)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "%s: not a live handle", who);
+    if (h->device_mode)
+        return fail(ZERO_ERR_STATE, "%s: device-resident flow active; call zero_device_end", who);
+    if (h->opt != opt)
+        return fail(ZERO_ERR_STATE, "%s: handle was created for %s", who,
+                    h->opt == kOptAdam ? "Adam" : "SGD");
+    if (h->phase == kChecked || h->phase == kPending)
+        return fail(ZERO_ERR_STATE, "%s: step already checked or pending", who);
+    if (h->phase == kReducing && h->covered != h->S)
+        return fail(ZERO_ERR_STATE, "%s: buckets cover [0, %lld) of [0, %lld)", who,
+                    (long long)h->covered, (long long)h->S);
+    return ZERO_OK;
+}
+
+// Enqueue a gated step: the check, its result copy and the event the resolve
+// waits on, then the update (launch_update), which skips itself on overflow.
+// On an error the handle returns to the phase it was in.
+template <typename F>
+static zero_status enqueue_gated(zero_shard_s* h, hipStream_t s, const char* who, F launch_update)
+{
+    const Phase before = h->phase;
+    const int64_t cursor_before = h->slot_cursor;
+    zero_status st = launch_check(h, s, who);
+    if (st == ZERO_OK) {
+        hipError_t e = hipEventRecord(h->result_ready, s);
+        if (e != hipSuccess) st = hip_fail(e, who);
+    }
+    if (st == ZERO_OK) st = launch_update(s);
+    if (st != ZERO_OK) {
+        h->phase = before;
+        h->slot_cursor = cursor_before;
+        return st;
+    }
+    h->phase = kPending;
+    return ZERO_OK;
+}
+
 extern "C" {
 
 zero_status zero_overflow_check(zero_shard_t h, void* stream, zero_step_info* out)
@@ -823,38 +863,15 @@ zero_status zero_overflow_merge(zero_shard_t h, int32_t global_overflow, double 
 
 zero_status zero_adam_step_gated(zero_shard_t h, const zero_adam_hparams* hp_in, void* stream)
 {
-    if (!live(h)) return fail(ZERO_ERR_STATE, "adam_step_gated: not a live handle");
-    if (h->device_mode)
-        return fail(ZERO_ERR_STATE, "%s: device-resident flow active; call zero_device_end", "adam_step_gated");
-    if (h->opt != kOptAdam) return fail(ZERO_ERR_STATE, "adam_step_gated: handle was created for SGD");
-    if (h->phase == kChecked || h->phase == kPending)
-        return fail(ZERO_ERR_STATE, "adam_step_gated: step already checked or pending");
-    if (h->phase == kReducing && h->covered != h->S)
-        return fail(ZERO_ERR_STATE, "adam_step_gated: buckets cover [0, %lld) of [0, %lld)",
-                    (long long)h->covered, (long long)h->S);
-    if (hp_in) {
-        zero_status st = check_hparams(hp_in);
-        if (st != ZERO_OK) return st;
-    }
+    const char* who = "adam_step_gated";
+    zero_status st = gated_preconditions(h, kOptAdam, who);
+    if (st != ZERO_OK) return st;
+    if (hp_in && (st = check_hparams(hp_in)) != ZERO_OK) return st;
     const zero_adam_hparams& hp = hp_in ? *hp_in : h->hp;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const Phase before = h->phase;
-    const int64_t cursor_before = h->slot_cursor;
-    zero_status st = launch_check(h, s, "adam_step_gated: check");
-    if (st == ZERO_OK) {
-        hipError_t e = hipEventRecord(h->result_ready, s);
-        if (e != hipSuccess) st = hip_fail(e, "adam_step_gated: event");
-    }
-    if (st == ZERO_OK)
-        st = launch_adam_step(h, hp, s, source_gated(h), &h->pend_pw1, &h->pend_pw2,
-                              &h->pend_same_betas, "adam_step_gated: launch");
-    if (st != ZERO_OK) {
-        h->phase = before;
-        h->slot_cursor = cursor_before;
-        return st;
-    }
-    h->phase = kPending;
-    return ZERO_OK;
+    return enqueue_gated(h, static_cast<hipStream_t>(stream), who, [&](hipStream_t s) {
+        return launch_adam_step(h, hp, s, source_gated(h), &h->pend_pw1, &h->pend_pw2,
+                                &h->pend_same_betas, "adam_step_gated: launch");
+    });
 }
 
 zero_status zero_sgd_step(zero_shard_t h, const zero_sgd_hparams* hp_in, void* stream,
@@ -882,38 +899,16 @@ zero_status zero_sgd_step(zero_shard_t h, const zero_sgd_hparams* hp_in, void* s
 
 zero_status zero_sgd_step_gated(zero_shard_t h, const zero_sgd_hparams* hp_in, void* stream)
 {
-    if (!live(h)) return fail(ZERO_ERR_STATE, "sgd_step_gated: not a live handle");
-    if (h->device_mode)
-        return fail(ZERO_ERR_STATE, "%s: device-resident flow active; call zero_device_end", "sgd_step_gated");
-    if (h->opt != kOptSgd) return fail(ZERO_ERR_STATE, "sgd_step_gated: handle was created for Adam");
-    if (h->phase == kChecked || h->phase == kPending)
-        return fail(ZERO_ERR_STATE, "sgd_step_gated: step already checked or pending");
-    if (h->phase == kReducing && h->covered != h->S)
-        return fail(ZERO_ERR_STATE, "sgd_step_gated: buckets cover [0, %lld) of [0, %lld)",
-                    (long long)h->covered, (long long)h->S);
-    if (hp_in) {
-        zero_status st = check_sgd_hparams(hp_in, h->d.exp_avg != nullptr);
-        if (st != ZERO_OK) return st;
-    }
+    const char* who = "sgd_step_gated";
+    zero_status st = gated_preconditions(h, kOptSgd, who);
+    if (st != ZERO_OK) return st;
+    if (hp_in && (st = check_sgd_hparams(hp_in, h->d.exp_avg != nullptr)) != ZERO_OK) return st;
     const zero_sgd_hparams& hp = hp_in ? *hp_in : h->sgd;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const Phase before = h->phase;
-    const int64_t cursor_before = h->slot_cursor;
-    zero_status st = launch_check(h, s, "sgd_step_gated: check");
-    if (st == ZERO_OK) {
-        hipError_t e = hipEventRecord(h->result_ready, s);
-        if (e != hipSuccess) st = hip_fail(e, "sgd_step_gated: event");
-    }
-    if (st == ZERO_OK) st = launch_sgd_step(h, hp, s, source_gated(h), "sgd_step_gated: launch");
-    if (st != ZERO_OK) {
-        h->phase = before;
-        h->slot_cursor = cursor_before;
-        return st;
-    }
-    h->pend_pw1 = h->pend_pw2 = 1.0;
-    h->pend_same_betas = false;
-    h->phase = kPending;
-    return ZERO_OK;
+    return enqueue_gated(h, static_cast<hipStream_t>(stream), who, [&](hipStream_t s) {
+        h->pend_pw1 = h->pend_pw2 = 1.0;
+        h->pend_same_betas = false;
+        return launch_sgd_step(h, hp, s, source_gated(h), "sgd_step_gated: launch");
+    });
 }
 
 zero_status zero_step_resolve(zero_shard_t h, zero_step_info* out)
