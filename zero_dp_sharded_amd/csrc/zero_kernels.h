@@ -12,8 +12,9 @@ constexpr int kMaxContrib = 64;
 // Reduce / scan: 256 lanes per workgroup, each lane two 16-byte runs (8
 // two-byte or 4 fp32 elements; each load instruction of a wave covers 1 KiB
 // contiguously), one run when a reduce has 8 or more contributions (its loads
-// already keep enough bytes in flight); residency capped at 4 workgroups (16
-// waves) per CU.
+// already keep enough bytes in flight).  Residency is capped by the number of
+// streams: 4 workgroups (16 waves) per CU below 8 contributions, 3 from 8 and
+// 2 from 16, which keeps about 96-128 KiB of loads in flight per CU.
 // (The ZK_* macros exist only to build tuning variants; the defaults are the
 // measured optimum.)
 #ifndef ZK_RED_BLOCK
@@ -27,6 +28,12 @@ constexpr int kMaxContrib = 64;
 #endif
 #ifndef ZK_RED_PER_CU
 #define ZK_RED_PER_CU 4
+#endif
+#ifndef ZK_RED_PER_CU_MANY
+#define ZK_RED_PER_CU_MANY 3
+#endif
+#ifndef ZK_RED_PER_CU_WIDE
+#define ZK_RED_PER_CU_WIDE 2
 #endif
 #ifndef ZK_ADAM_BLOCK
 #define ZK_ADAM_BLOCK 64
@@ -59,6 +66,9 @@ inline int red_runs(int R) { return R >= kRedManyR ? kRedRunsMany : kRedRuns; }
 constexpr int64_t kRedElemsPerBlockMin =
     (int64_t)kRedBlock * (kRedRuns < kRedRunsMany ? kRedRuns : kRedRunsMany) * 4;
 constexpr int kRedPerCU = ZK_RED_PER_CU;
+constexpr int kRedPerCUMany = ZK_RED_PER_CU_MANY;   // residency when 8 <= R < 16
+constexpr int kRedPerCUWide = ZK_RED_PER_CU_WIDE;   // residency when R >= 16
+constexpr int kRedWideR = 16;
 // Adam: one wave (64 lanes) per workgroup, each lane one group of 4 elements;
 // residency capped at 10 workgroups (10 waves) per CU.
 constexpr int kAdamBlock = ZK_ADAM_BLOCK;

@@ -75,6 +75,8 @@ struct zero_shard_s {
     uint32_t lds_sgd_mom = 0;
     uint32_t lds_sgd_plain = 0;
     uint32_t lds_reduce = 0;
+    uint32_t lds_reduce_many = 0;   // reduces of 8 <= R < 16 contributions
+    uint32_t lds_reduce_wide = 0;   // reduces of R >= 16 contributions
     // gated steps: event after the result copy, and the speculative update
     hipEvent_t result_ready = nullptr;
     double pend_pw1 = 1.0, pend_pw2 = 1.0;
@@ -349,6 +351,8 @@ static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m,
     h->lds_sgd_mom = lds_reserve_for(lds_cu, lds_blk, zk::kSgdMomPerCU);
     h->lds_sgd_plain = lds_reserve_for(lds_cu, lds_blk, zk::kSgdPlainPerCU);
     h->lds_reduce = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCU);
+    h->lds_reduce_many = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCUMany);
+    h->lds_reduce_wide = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCUWide);
     static_assert(sizeof(zk::CheckResult) <= 64 && sizeof(zk::DevState) <= 192, "pinned layout");
     e = hipHostMalloc(reinterpret_cast<void**>(&h->host_result), 256, hipHostMallocDefault);
     if (e != hipSuccess) {
@@ -420,7 +424,9 @@ static zero_status enqueue_reduce(zero_shard_s* h, const void* const* ptrs, int3
     L.inv_scale = (float)(1.0 / h->scale);
     L.partial = h->partial;
     L.slot_base = slot_base;
-    L.lds_reserve = h->lds_reduce;
+    L.lds_reserve = n_contrib >= zk::kRedWideR   ? h->lds_reduce_wide
+                    : n_contrib >= zk::kRedManyR ? h->lds_reduce_many
+                                                 : h->lds_reduce;
     L.dev = dev;
     const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::red_runs(L.R));
     if (L.slot_base + blocks > h->nslots)
