@@ -9,31 +9,42 @@ namespace zk {
 
 constexpr int kMaxContrib = 64;
 
-// Reduce / scan: 256 lanes per workgroup, each lane two 16-byte runs (8
-// two-byte or 4 fp32 elements; each load instruction of a wave covers 1 KiB
-// contiguously), one run when a reduce has 8 or more contributions (its loads
-// already keep enough bytes in flight).  Residency is capped by the number of
-// streams: 4 workgroups (16 waves) per CU below 8 contributions, 3 from 8 and
-// 2 from 16, which keeps about 96-128 KiB of loads in flight per CU.
+// Reduce / scan: 256 lanes per workgroup, each lane a few 16-byte runs (a run
+// is 8 two-byte or 4 fp32 elements; each load instruction of a wave covers
+// 1 KiB contiguously).  Runs per lane and resident workgroups per CU are set
+// so that a CU keeps about 96-144 KiB of loads in flight:
+//   reduce, R < 8:   3 runs, 3 workgroups per CU (2 runs for buckets too small
+//                    to fill the chip, where more workgroups finish sooner);
+//   reduce, R >= 8:  1 run, 3 workgroups per CU (2 from R = 16);
+//   scan (1 stream): 4 runs, 8 workgroups per CU.
 // (The ZK_* macros exist only to build tuning variants; the defaults are the
 // measured optimum.)
 #ifndef ZK_RED_BLOCK
 #define ZK_RED_BLOCK 256
 #endif
 #ifndef ZK_RED_RUNS
-#define ZK_RED_RUNS 2
+#define ZK_RED_RUNS 3
+#endif
+#ifndef ZK_RED_RUNS_SMALL
+#define ZK_RED_RUNS_SMALL 2
 #endif
 #ifndef ZK_RED_RUNS_MANY
 #define ZK_RED_RUNS_MANY 1
 #endif
 #ifndef ZK_RED_PER_CU
-#define ZK_RED_PER_CU 4
+#define ZK_RED_PER_CU 3
 #endif
 #ifndef ZK_RED_PER_CU_MANY
 #define ZK_RED_PER_CU_MANY 3
 #endif
 #ifndef ZK_RED_PER_CU_WIDE
 #define ZK_RED_PER_CU_WIDE 2
+#endif
+#ifndef ZK_SCAN_RUNS
+#define ZK_SCAN_RUNS 4
+#endif
+#ifndef ZK_SCAN_PER_CU
+#define ZK_SCAN_PER_CU 8
 #endif
 #ifndef ZK_ADAM_BLOCK
 #define ZK_ADAM_BLOCK 64
@@ -60,11 +71,23 @@ constexpr int kRedBlock = ZK_RED_BLOCK;
 constexpr int kRedRuns = ZK_RED_RUNS;
 constexpr int kRedRunsMany = ZK_RED_RUNS_MANY;   // runs per lane when R >= 8
 constexpr int kRedManyR = 8;
-// Runs per lane of a reduce with R contributions (a scan uses kRedRuns).
-inline int red_runs(int R) { return R >= kRedManyR ? kRedRunsMany : kRedRuns; }
+constexpr int kRedRunsSmall = ZK_RED_RUNS_SMALL;   // R < 8, bucket below kRedSmallNvec runs
+// runs of one full residency of kRedRuns workgroups on 256 CUs
+constexpr int64_t kRedSmallNvec = (int64_t)256 * ZK_RED_PER_CU * ZK_RED_BLOCK * ZK_RED_RUNS;
+// Runs per lane of the reduce of a bucket of nvec runs with R contributions.
+inline int red_runs(int R, int64_t nvec)
+{
+    if (R >= kRedManyR) return kRedRunsMany;
+    return nvec < kRedSmallNvec ? kRedRunsSmall : kRedRuns;
+}
+// The stand-alone scan reads a single stream, so it takes its own runs per
+// lane and residency.
+constexpr int kScanRuns = ZK_SCAN_RUNS;
+constexpr int kScanPerCU = ZK_SCAN_PER_CU;
+constexpr int kMin2(int a, int b) { return a < b ? a : b; }
+constexpr int kMinRuns = kMin2(kMin2(kRedRuns, kRedRunsSmall), kMin2(kRedRunsMany, kScanRuns));
 // elements one reduce or scan workgroup covers at the least (fp32, 4 per run)
-constexpr int64_t kRedElemsPerBlockMin =
-    (int64_t)kRedBlock * (kRedRuns < kRedRunsMany ? kRedRuns : kRedRunsMany) * 4;
+constexpr int64_t kRedElemsPerBlockMin = (int64_t)kRedBlock * kMinRuns * 4;
 constexpr int kRedPerCU = ZK_RED_PER_CU;
 constexpr int kRedPerCUMany = ZK_RED_PER_CU_MANY;   // residency when 8 <= R < 16
 constexpr int kRedPerCUWide = ZK_RED_PER_CU_WIDE;   // residency when R >= 16
@@ -233,8 +256,8 @@ inline int run_width(int32_t lp) { return lp == 3 ? 4 : 8; }
 
 // Partial slots a reduce / scan of this layout writes: one per workgroup of
 // the vector kernel plus one per workgroup of the element-wise kernel.  W is
-// the run width of the storage format, U the runs per lane (red_runs(R) for a
-// reduce, kRedRuns for a scan).
+// the run width of the storage format, U the runs per lane (red_runs(R, nvec)
+// for a reduce, kScanRuns for a scan).
 int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok, int W, int U);
 
 hipError_t launch_reduce(const ReduceLaunch& L, hipStream_t s);

@@ -320,15 +320,15 @@ __global__ __launch_bounds__(kRedBlock) void scan_vec_kernel(ScanLaunch L)
     int flag = 0;
     double ss = 0.0;
     const float inv_scale = check_inv_scale(L.inv_scale, L.dev);
-    const int64_t v0 = (int64_t)blockIdx.x * (kRedBlock * kRedRuns) + threadIdx.x;
-    VW x[kRedRuns];
+    const int64_t v0 = (int64_t)blockIdx.x * (kRedBlock * kScanRuns) + threadIdx.x;
+    VW x[kScanRuns];
 #pragma unroll
-    for (int u = 0; u < kRedRuns; ++u) {
+    for (int u = 0; u < kScanRuns; ++u) {
         const int64_t vi = v0 + u * kRedBlock;
         if (vi < L.nvec) x[u] = ld_nt<VW>(adv<LP>(L.g, L.head), vi);
     }
 #pragma unroll
-    for (int u = 0; u < kRedRuns; ++u)
+    for (int u = 0; u < kScanRuns; ++u)
         if (v0 + u * kRedBlock < L.nvec) check_v<LP>(x[u], inv_scale, flag, ss);
     block_partial<kRedBlock>(L.partial + L.slot_base + blockIdx.x, flag, ss);
 }
@@ -660,23 +660,39 @@ Ranges ranges_of(int64_t n, int64_t head, int64_t body, int32_t vec_ok)
     return rg;
 }
 
-// U must equal red_runs(L.R): the dispatch sizes the grid with it.
-template <int LP>
-hipError_t reduce_vec_launch(const ReduceLaunch& L, unsigned grid, hipStream_t s)
+template <int LP, int RT, int U>
+void reduce_vec_go(const ReduceLaunch& L, unsigned grid, hipStream_t s)
 {
-    constexpr int A = kRedRuns, B = kRedRunsMany;
-    const unsigned lds = L.lds_reserve;
+    reduce_vec_kernel<LP, RT, U><<<grid, kRedBlock, L.lds_reserve, s>>>(L);
+}
+
+// Below 8 contributions, the runs per lane U is kRedRuns or kRedRunsSmall;
+// from 8 on it is kRedRunsMany.  U must be the one the dispatch sized the grid
+// with (red_runs of the whole bucket).
+template <int LP, int RT>
+void reduce_vec_few(const ReduceLaunch& L, unsigned grid, int U, hipStream_t s)
+{
+    if (U == kRedRunsSmall)
+        reduce_vec_go<LP, RT, kRedRunsSmall>(L, grid, s);
+    else
+        reduce_vec_go<LP, RT, kRedRuns>(L, grid, s);
+}
+
+template <int LP>
+hipError_t reduce_vec_launch(const ReduceLaunch& L, unsigned grid, int U, hipStream_t s)
+{
+    constexpr int B = kRedRunsMany;
     switch (L.R) {
-    case 1: reduce_vec_kernel<LP, 1, A><<<grid, kRedBlock, lds, s>>>(L); break;
-    case 2: reduce_vec_kernel<LP, 2, A><<<grid, kRedBlock, lds, s>>>(L); break;
-    case 4: reduce_vec_kernel<LP, 4, A><<<grid, kRedBlock, lds, s>>>(L); break;
-    case 8: reduce_vec_kernel<LP, 8, B><<<grid, kRedBlock, lds, s>>>(L); break;
-    case 16: reduce_vec_kernel<LP, 16, B><<<grid, kRedBlock, lds, s>>>(L); break;
+    case 1: reduce_vec_few<LP, 1>(L, grid, U, s); break;
+    case 2: reduce_vec_few<LP, 2>(L, grid, U, s); break;
+    case 4: reduce_vec_few<LP, 4>(L, grid, U, s); break;
+    case 8: reduce_vec_go<LP, 8, B>(L, grid, s); break;
+    case 16: reduce_vec_go<LP, 16, B>(L, grid, s); break;
     default:
         if (L.R >= kRedManyR)
-            reduce_vec_kernel<LP, 0, B><<<grid, kRedBlock, lds, s>>>(L);
+            reduce_vec_go<LP, 0, B>(L, grid, s);
         else
-            reduce_vec_kernel<LP, 0, A><<<grid, kRedBlock, lds, s>>>(L);
+            reduce_vec_few<LP, 0>(L, grid, U, s);
         break;
     }
     return hipGetLastError();
@@ -686,7 +702,8 @@ template <int LP>
 hipError_t reduce_dispatch(const ReduceLaunch& L, hipStream_t s)
 {
     constexpr int W = Fmt<LP>::W;
-    const int64_t runs_per_block = (int64_t)kRedBlock * red_runs(L.R);
+    const int U = red_runs(L.R, L.nvec);
+    const int64_t runs_per_block = (int64_t)kRedBlock * U;
     const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, runs_per_block) : 0;
     // consecutive launches of at most kMaxLaunchItems work-items; each starts
     // its runs and its partial slots where the previous one stopped
@@ -697,7 +714,7 @@ hipError_t reduce_dispatch(const ReduceLaunch& L, hipStream_t s)
         part.head = L.head + W * runs_per_block * b0;
         part.nvec = L.nvec - runs_per_block * b0;
         part.slot_base = L.slot_base + b0;
-        hipError_t e = reduce_vec_launch<LP>(part, (unsigned)nb, s);
+        hipError_t e = reduce_vec_launch<LP>(part, (unsigned)nb, U, s);
         if (e != hipSuccess) return e;
     }
     const Ranges rg = ranges_of(L.n, L.head, W * L.nvec, L.vec_ok);
@@ -711,7 +728,7 @@ template <int LP>
 hipError_t scan_dispatch(const ScanLaunch& L, hipStream_t s)
 {
     constexpr int W = Fmt<LP>::W;
-    const int64_t runs_per_block = (int64_t)kRedBlock * kRedRuns;
+    const int64_t runs_per_block = (int64_t)kRedBlock * kScanRuns;
     const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, runs_per_block) : 0;
     const int64_t max_blocks = kMaxLaunchItems / kRedBlock;
     for (int64_t b0 = 0; b0 < vblocks; b0 += max_blocks) {

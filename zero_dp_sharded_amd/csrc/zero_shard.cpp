@@ -77,6 +77,7 @@ struct zero_shard_s {
     uint32_t lds_reduce = 0;
     uint32_t lds_reduce_many = 0;   // reduces of 8 <= R < 16 contributions
     uint32_t lds_reduce_wide = 0;   // reduces of R >= 16 contributions
+    uint32_t lds_scan = 0;
     // gated steps: event after the result copy, and the speculative update
     hipEvent_t result_ready = nullptr;
     double pend_pw1 = 1.0, pend_pw2 = 1.0;
@@ -353,6 +354,7 @@ static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m,
     h->lds_reduce = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCU);
     h->lds_reduce_many = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCUMany);
     h->lds_reduce_wide = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCUWide);
+    h->lds_scan = lds_reserve_for(lds_cu, lds_blk, zk::kScanPerCU);
     static_assert(sizeof(zk::CheckResult) <= 64 && sizeof(zk::DevState) <= 192, "pinned layout");
     e = hipHostMalloc(reinterpret_cast<void**>(&h->host_result), 256, hipHostMallocDefault);
     if (e != hipSuccess) {
@@ -428,7 +430,7 @@ static zero_status enqueue_reduce(zero_shard_s* h, const void* const* ptrs, int3
                     : n_contrib >= zk::kRedManyR ? h->lds_reduce_many
                                                  : h->lds_reduce;
     L.dev = dev;
-    const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::red_runs(L.R));
+    const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::red_runs(L.R, L.nvec));
     if (L.slot_base + blocks > h->nslots)
         return fail(ZERO_ERR_UNSUPPORTED, "%s: partial slots exhausted", who);
     hipError_t e = zk::launch_reduce(L, s);
@@ -552,11 +554,11 @@ static zero_status enqueue_scan(zero_shard_s* h, const zk::DevState* dev, hipStr
     L.inv_scale = (float)(1.0 / h->scale);
     L.partial = h->partial;
     L.slot_base = 0;
-    L.lds_reserve = h->lds_reduce;
+    L.lds_reserve = h->lds_scan;
     L.dev = dev;
     hipError_t e = zk::launch_scan(L, s);
     if (e != hipSuccess) return hip_fail(e, who);
-    *slots = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::kRedRuns);
+    *slots = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::kScanRuns);
     return ZERO_OK;
 }
 
