@@ -365,10 +365,10 @@ zero_status zero_step_resolve(zero_shard_t h, zero_step_info* out);
  *     storage format; element i of contribution r is its value for shard
  *     element i), or, with contribs = NULL and n_contrib = 0, the scan of a
  *     caller-filled grad_shard;
- *   - the fixed-order fold (norm, overflow, clipping coefficient);
- *   - a one-lane kernel that decides the step exactly as the host flows do
- *     (skip on overflow; otherwise t += 1 and the bias corrections of step t;
- *     the loss-scale rule) and advances the device copy of the counters;
+ *   - the fixed-order fold (norm, overflow, clipping coefficient), whose last
+ *     lane then decides the step exactly as the host flows do (skip on
+ *     overflow; otherwise t += 1 and the bias corrections of step t; the
+ *     loss-scale rule) and advances the device copy of the counters;
  *   - the update (Adam or SGD with the init hyper-parameters), which reads
  *     the decision and the step's scalars from device memory and writes
  *     nothing on a skipped step.
