@@ -236,15 +236,20 @@ zero_status zero_shard_init_sgd(const zero_shard_desc* desc, const zero_sgd_hpar
  * Asynchronous on `stream`; contribution memory must stay valid until the
  * kernel has run.  Buckets of one step must be submitted in ascending,
  * contiguous order starting at 0; bucket_len must equal bucket_elems except
- * for the last bucket, which ends at S.
+ * for the last bucket, which ends at S.  A contribution may be the bucket's
+ * own slice of grad_shard (&grad_shard[bucket_off], an in-place reduce: each
+ * element is read before it is written); otherwise contributions must not
+ * overlap grad_shard, and none may overlap master, exp_avg, exp_avg_sq or
+ * param_shard.
  * Performance: contributions whose base addresses lie exactly 512 MiB, 1 GiB
  * or 2 GiB apart hit the same DRAM banks in step and were measured 10-15%
  * slower on MI355X than ones at unrelated distances; a skew of 2-8 KiB
  * between them avoids it.
  * Errors: INVALID_ARG (NULL, n_contrib outside [1, 64], bucket outside [0, S),
- * bucket_len < 1 or > bucket_elems, pointer not aligned to its element size),
- * STATE (dead handle, bucket not the next one, step already checked,
- * device-resident flow active), HIP.
+ * bucket_len < 1 or > bucket_elems, pointer not aligned to its element size,
+ * a contribution overlapping a shard array as above), STATE (dead handle,
+ * bucket not the next one, step already checked, device-resident flow
+ * active), HIP.
  */
 zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int32_t n_contrib,
                                int64_t bucket_off, int64_t bucket_len, void* stream);
@@ -367,8 +372,9 @@ zero_status zero_step_resolve(zero_shard_t h, zero_step_info* out);
  *   - the reduce of every C_B bucket of the shard from n_contrib contributions
  *     (contribs: host array of device pointers, each to S elements of the
  *     storage format; element i of contribution r is its value for shard
- *     element i), or, with contribs = NULL and n_contrib = 0, the scan of a
- *     caller-filled grad_shard;
+ *     element i; a contribution may be grad_shard itself, none may overlap
+ *     it otherwise or overlap another shard array), or, with contribs = NULL
+ *     and n_contrib = 0, the scan of a caller-filled grad_shard;
  *   - the fixed-order fold (norm, overflow, clipping coefficient), whose last
  *     lane then decides the step exactly as the host flows do (skip on
  *     overflow; otherwise t += 1 and the bias corrections of step t; the

@@ -275,6 +275,14 @@ def test_abi_state_machine_errors_leave_state_unchanged():
         assert L.zero_bucket_reduce(h, None, R, 0, cb, None) == zs.ZERO_ERR_INVALID_ARG
         odd = (ctypes.c_void_p * R)(*[b.data_ptr() + 1 for b in bufs])
         assert L.zero_bucket_reduce(h, odd, R, 0, cb, None) == zs.ZERO_ERR_INVALID_ARG
+        # a contribution over a shard array, or over grad_shard other than as
+        # the bucket's own slice
+        for name, shift in (("master", 0), ("m", 4 * 7), ("v", 0), ("param", 2 * (n - 1)),
+                            ("grad", 2), ("grad", 2 * cb)):
+            over = (ctypes.c_void_p * R)(*([t[name].data_ptr() + shift] +
+                                           [b.data_ptr() for b in bufs[1:]]))
+            assert L.zero_bucket_reduce(h, over, R, 0, cb, None) == zs.ZERO_ERR_INVALID_ARG, name
+            assert "overlaps" in zs.zero_last_error(), name
         assert L.zero_overflow_check(h, None, None) == zs.ZERO_ERR_INVALID_ARG
         # a valid first bucket, then errors mid-step
         assert L.zero_bucket_reduce(h, arr(0), R, 0, cb, None) == zs.ZERO_OK
@@ -308,6 +316,59 @@ def test_abi_state_machine_errors_leave_state_unchanged():
         zs.zero_shard_destroy(h)
     assert L.zero_shard_destroy(h) == zs.ZERO_ERR_STATE
     assert L.zero_bucket_reduce(h, arr(0), R, 0, cb, None) == zs.ZERO_ERR_STATE
+
+
+@pytest.mark.parametrize("flow", ["sync", "device"])
+def test_in_place_reduce(flow):
+    """Contribution 0 is grad_shard itself (a reduce in place of the first
+    contribution's buffer): bucket by bucket in the synchronous flow, the
+    whole shard in one device-resident step; bitwise equal to the oracle fed
+    the original contributions."""
+    n, cb, R = 100_003, 30_000, 4
+    h, t = _handle(n, cb=cb)
+    master0 = f32(t["master"]).copy()
+    gen = torch.Generator(device="cuda").manual_seed(21)
+    bufs = [(torch.randn(n, generator=gen, device="cuda") * 4.0).half() for _ in range(R)]
+    cs = [u16(b) for b in bufs]
+    t["grad"].copy_(bufs[0])
+    srcs = [t["grad"]] + bufs[1:]
+    log(f"in-place reduce, {flow} flow")
+    try:
+        if flow == "sync":
+            zs.reduce_buckets(h, srcs, n, cb)
+            zs.zero_overflow_check(h)
+            info = zs.zero_adam_step(h)
+        else:
+            zs.zero_device_begin(h)
+            zs.zero_step_device(h, srcs)
+            info = zs.zero_device_end(h)
+        torch.cuda.synchronize()
+    finally:
+        zs.zero_shard_destroy(h)
+    ohp, ols = oracle.AdamHP(lr=1e-3), oracle.LossScale(init_scale=1024.0)
+    st = oracle.new_state(oracle.FP16, master0, np.zeros(n), np.zeros(n), ohp, ols)
+    oi = oracle.step(st, cs, cb, ohp, ols)
+    assert info.overflow == oi.overflow == 0 and info.step_t == 1
+    assert np.array_equal(u16(t["grad"]), st.grad)
+    assert np.array_equal(f32(t["master"]).view(np.uint32), st.master.view(np.uint32))
+    assert np.array_equal(u16(t["param"]), st.param)
+
+
+def test_device_step_refuses_overlapping_contribution():
+    n, cb, R = 20_000, 8_192, 4
+    h, t = _handle(n, cb=cb)
+    bufs = [torch.randn(n, device="cuda").half() for _ in range(R)]
+    L = zs.lib()
+    try:
+        zs.zero_device_begin(h)
+        for name, shift in (("master", 0), ("grad", 2)):
+            ptrs = (ctypes.c_void_p * R)(*([t[name].data_ptr() + shift] +
+                                           [b.data_ptr() for b in bufs[1:]]))
+            assert L.zero_step_device(h, ptrs, R, None) == zs.ZERO_ERR_INVALID_ARG, name
+        info = zs.zero_device_end(h)
+        assert info.step_t == 0
+    finally:
+        zs.zero_shard_destroy(h)
 
 
 @pytest.mark.parametrize("name,elems,cb", [("gpt2_1.5b", 300_007, 65_536), ("13b_inf", 120_013, 16_384),

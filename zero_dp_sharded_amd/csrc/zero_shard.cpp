@@ -394,6 +394,34 @@ static zero_status check_contribs(const zero_shard_s* h, const void* const* cont
     return ZERO_OK;
 }
 
+// Contributions covering len elements for the shard elements [off, off + len)
+// may be that very slice of grad_shard (an in-place reduce: each lane loads its
+// elements before it stores them) but must not otherwise overlap grad_shard,
+// and must not overlap master, exp_avg, exp_avg_sq or param_shard.
+static zero_status check_contrib_overlap(const zero_shard_s* h, const void* const* contribs,
+                                         int32_t n_contrib, int64_t off, int64_t len,
+                                         const char* who)
+{
+    const size_t nb = (size_t)len * (size_t)h->esz;
+    const uintptr_t own = (uintptr_t)h->d.grad_shard + (uintptr_t)off * (uintptr_t)h->esz;
+    const void* state[4] = {h->d.master, h->d.exp_avg, h->d.exp_avg_sq, h->d.param_shard};
+    const size_t state_bytes[4] = {(size_t)h->S * 4, (size_t)h->S * 4, (size_t)h->S * 4,
+                                   (size_t)h->S * (size_t)h->esz};
+    for (int r = 0; r < n_contrib; ++r) {
+        const uintptr_t a = (uintptr_t)contribs[r];
+        for (int k = 0; k < 4; ++k)
+            if (state[k] && overlaps(a, nb, (uintptr_t)state[k], state_bytes[k]))
+                return fail(ZERO_ERR_INVALID_ARG, "%s: contribution %d overlaps shard array %d",
+                            who, r, k == 3 ? 4 : k);
+        if (a != own &&
+            overlaps(a, nb, (uintptr_t)h->d.grad_shard, (size_t)h->S * (size_t)h->esz))
+            return fail(ZERO_ERR_INVALID_ARG,
+                        "%s: contribution %d overlaps grad_shard other than as its own slice", who,
+                        r);
+    }
+    return ZERO_OK;
+}
+
 // Launch the reduce of the bucket [off, off + len) of the shard from the
 // contributions' bucket pointers, writing partial slots from slot_base on;
 // dev set: the unscale factor comes from the device state.
@@ -513,6 +541,8 @@ zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int3
     if (bucket_len > h->d.bucket_elems)
         return fail(ZERO_ERR_INVALID_ARG, "bucket_reduce: bucket_len %lld exceeds C_B %lld",
                     (long long)bucket_len, (long long)h->d.bucket_elems);
+    cst = check_contrib_overlap(h, contribs, n_contrib, bucket_off, bucket_len, "bucket_reduce");
+    if (cst != ZERO_OK) return cst;
     if (h->phase == kChecked)
         return fail(ZERO_ERR_STATE, "bucket_reduce: step already checked; call zero_adam_step");
     if (h->phase == kPending)
@@ -1001,6 +1031,7 @@ zero_status zero_step_device(zero_shard_t h, const void* const* contribs, int32_
     const bool scan = n_contrib == 0 && contribs == nullptr;
     if (!scan) {
         zero_status st = check_contribs(h, contribs, n_contrib, "step_device");
+        if (st == ZERO_OK) st = check_contrib_overlap(h, contribs, n_contrib, 0, h->S, "step_device");
         if (st != ZERO_OK) return st;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
