@@ -34,7 +34,11 @@
  *  - "Device pointer" means memory of the device that was current when the
  *    handle was created.  Any 2-byte-aligned address is accepted for 2-byte
  *    arrays and any 4-byte-aligned address for fp32 arrays; the kernels peel
- *    unaligned heads and tails.
+ *    unaligned heads and tails.  Before any launch the library asks the HIP
+ *    runtime about every array and contribution and refuses (INVALID_ARG)
+ *    pageable host memory, another device's memory, and a range that runs
+ *    past the end of its allocation; this is best effort (the runtime sees
+ *    allocations, not the caller's tensors inside them), not a guarantee.
  *  - A handle is not thread-safe.  Separate handles are independent.
  *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  */

@@ -354,6 +354,64 @@ def test_in_place_reduce(flow):
     assert np.array_equal(u16(t["param"]), st.param)
 
 
+def _hip():
+    h = ctypes.CDLL("libamdhip64.so")
+    h.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+    h.hipFree.argtypes = [ctypes.c_void_p]
+    return h
+
+
+def test_host_memory_and_short_allocations_refused():
+    """Arrays the runtime reports as pageable host memory, or that run past the
+    end of their allocation, are refused before anything is launched.  Each
+    case is tried first at zero_shard_init, which launches nothing, and only
+    then as a contribution."""
+    n = (1 << 19) + 1                    # 4n bytes = 2 MiB + 4
+    L = zs.lib()
+    hip = _hip()
+    dev = torch.device("cuda", 0)
+    host = torch.zeros(n, dtype=torch.float32)                 # pageable host memory
+    raw = ctypes.c_void_p()
+    assert hip.hipMalloc(ctypes.byref(raw), 1 << 21) == 0      # 2 MiB: one fp32 element short
+    try:
+        m = torch.zeros(n, device=dev)
+        v = torch.zeros(n, device=dev)
+        grad = torch.zeros(n, dtype=torch.float16, device=dev)
+        param = torch.zeros(n, dtype=torch.float16, device=dev)
+        hp, ls = zs.AdamHParams(lr=1e-3).to_c(), zs.LossScaleCfg(init_scale=1.0).to_c()
+        for master_ptr, what in ((host.data_ptr(), "not device-accessible"), (raw.value, "past the end")):
+            d = zs.ZeroShardDesc(n * 4, 4, 0, n, zs.ZERO_FP16, master_ptr, m.data_ptr(),
+                                 v.data_ptr(), grad.data_ptr(), param.data_ptr())
+            out = ctypes.c_void_p()
+            st = L.zero_shard_init(ctypes.byref(d), ctypes.byref(hp), ctypes.byref(ls),
+                                   ctypes.byref(out))
+            if st == zs.ZERO_OK:
+                zs.zero_shard_destroy(out.value)
+            assert st == zs.ZERO_ERR_INVALID_ARG and what in zs.zero_last_error(), what
+        # the same checks guard the contributions
+        h, t = _handle(n, cb=n)
+        try:
+            good = [torch.zeros(n, dtype=torch.float16, device=dev) for _ in range(3)]
+            host16 = torch.zeros(n, dtype=torch.float16)
+            # n fp16 elements from raw + 1 MiB end 2 bytes past the 2 MiB allocation
+            for bad, what in ((host16.data_ptr(), "not device-accessible"),
+                              (raw.value + (1 << 20), "past the end")):
+                ptrs = (ctypes.c_void_p * 4)(bad, *[g.data_ptr() for g in good])
+                assert L.zero_bucket_reduce(h, ptrs, 4, 0, n, None) == zs.ZERO_ERR_INVALID_ARG
+                assert what in zs.zero_last_error(), what
+            with pytest.raises(ValueError):
+                zs.zero_bucket_reduce(h, [host16] + good, 0, n)
+            # nothing was launched or recorded: a valid step still runs
+            zs.reduce_buckets(h, good + [good[0]], n, n)
+            assert zs.zero_overflow_check(h).overflow == 0
+            assert zs.zero_adam_step(h).step_t == 1
+        finally:
+            zs.zero_shard_destroy(h)
+    finally:
+        torch.cuda.synchronize()
+        hip.hipFree(raw)
+
+
 def test_device_step_refuses_overlapping_contribution():
     n, cb, R = 20_000, 8_192, 4
     h, t = _handle(n, cb=cb)

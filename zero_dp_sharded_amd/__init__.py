@@ -226,9 +226,11 @@ def _stream_ptr(stream) -> Optional[int]:
 
 
 def _dptr(x) -> int:
-    """Device address of a tensor (or an int address)."""
+    """Device address of a GPU tensor (or an int address, passed through)."""
     if isinstance(x, int):
         return x
+    if x.device.type != "cuda":
+        raise ValueError(f"expected a GPU tensor, got one on {x.device}")
     return x.data_ptr()
 
 

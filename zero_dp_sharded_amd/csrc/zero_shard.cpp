@@ -90,6 +90,9 @@ struct zero_shard_s {
     zk::DevState* dev = nullptr;
     zk::DevState* host_dev = nullptr;
     bool device_mode = false;
+    // the contribution set zero_step_device last validated
+    const void* dev_checked[ZERO_MAX_CONTRIB] = {};
+    int32_t dev_checked_n = 0;
 };
 
 namespace {
@@ -232,6 +235,42 @@ bool overlaps(uintptr_t a, size_t na, uintptr_t b, size_t nb)
     return a < b + nb && b < a + na;
 }
 
+// Whether [p, p + nbytes) may be handed to the kernels of device `dev`: the
+// runtime must not report it as unregistered host memory or as another
+// device's memory, and where it knows the allocation's extent the range must
+// end inside it.  Best effort: memory the runtime cannot classify (for
+// example, ranges mapped through the virtual-memory API) is accepted.
+bool device_range_ok(const void* p, size_t nbytes, int dev, char* why, size_t why_len)
+{
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;
+    }
+    if (a.type == hipMemoryTypeUnregistered) {
+        snprintf(why, why_len, "is not device-accessible memory (pageable host memory?)");
+        return false;
+    }
+    if (a.type == hipMemoryTypeDevice) {
+        if (a.device != dev) {
+            snprintf(why, why_len, "is memory of device %d, the handle's is %d", a.device, dev);
+            return false;
+        }
+        hipDeviceptr_t base = nullptr;
+        size_t size = 0;
+        if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) == hipSuccess) {
+            if ((uintptr_t)p + nbytes > (uintptr_t)base + size) {
+                snprintf(why, why_len, "runs %zu bytes past the end of its allocation",
+                         (size_t)((uintptr_t)p + nbytes - ((uintptr_t)base + size)));
+                return false;
+            }
+        } else {
+            (void)hipGetLastError();
+        }
+    }
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -313,6 +352,12 @@ static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m,
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "init: hipGetDevice");
+    for (int i = 0; i < 5; ++i) {
+        char why[160];
+        if (arr[i] && !device_range_ok(arr[i], (size_t)S * el[i], dev, why, sizeof(why)))
+            return fail(ZERO_ERR_INVALID_ARG, "%s: shard array %d (%lld elements) %s", who, i,
+                        (long long)S, why);
+    }
 
     zero_shard_s* h = new (std::nothrow) zero_shard_s();
     if (!h) return fail(ZERO_ERR_OOM, "init: host allocation failed");
@@ -395,9 +440,11 @@ static zero_status check_contribs(const zero_shard_s* h, const void* const* cont
 }
 
 // Contributions covering len elements for the shard elements [off, off + len)
-// may be that very slice of grad_shard (an in-place reduce: each lane loads its
-// elements before it stores them) but must not otherwise overlap grad_shard,
-// and must not overlap master, exp_avg, exp_avg_sq or param_shard.
+// must be device-accessible memory of the handle's device (as far as the
+// runtime can tell); they may be that very slice of grad_shard (an in-place
+// reduce: each lane loads its elements before it stores them) but must not
+// otherwise overlap grad_shard, and must not overlap master, exp_avg,
+// exp_avg_sq or param_shard.
 static zero_status check_contrib_overlap(const zero_shard_s* h, const void* const* contribs,
                                          int32_t n_contrib, int64_t off, int64_t len,
                                          const char* who)
@@ -409,6 +456,10 @@ static zero_status check_contrib_overlap(const zero_shard_s* h, const void* cons
                                    (size_t)h->S * (size_t)h->esz};
     for (int r = 0; r < n_contrib; ++r) {
         const uintptr_t a = (uintptr_t)contribs[r];
+        char why[160];
+        if (!device_range_ok(contribs[r], nb, h->device, why, sizeof(why)))
+            return fail(ZERO_ERR_INVALID_ARG, "%s: contribution %d (%lld elements) %s", who, r,
+                        (long long)len, why);
         for (int k = 0; k < 4; ++k)
             if (state[k] && overlaps(a, nb, (uintptr_t)state[k], state_bytes[k]))
                 return fail(ZERO_ERR_INVALID_ARG, "%s: contribution %d overlaps shard array %d",
@@ -1019,6 +1070,7 @@ zero_status zero_device_begin(zero_shard_t h, void* stream)
     init.bc1 = init.bc2 = 1.0f;
     hipError_t e = zk::launch_load_state(h->dev, init, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "device_begin: launch");
+    h->dev_checked_n = 0;
     h->device_mode = true;
     return ZERO_OK;
 }
@@ -1031,8 +1083,16 @@ zero_status zero_step_device(zero_shard_t h, const void* const* contribs, int32_
     const bool scan = n_contrib == 0 && contribs == nullptr;
     if (!scan) {
         zero_status st = check_contribs(h, contribs, n_contrib, "step_device");
-        if (st == ZERO_OK) st = check_contrib_overlap(h, contribs, n_contrib, 0, h->S, "step_device");
         if (st != ZERO_OK) return st;
+        // a launch-bound step repeats the same pointers: validate a new set once
+        bool same = n_contrib == h->dev_checked_n;
+        for (int r = 0; same && r < n_contrib; ++r) same = contribs[r] == h->dev_checked[r];
+        if (!same) {
+            st = check_contrib_overlap(h, contribs, n_contrib, 0, h->S, "step_device");
+            if (st != ZERO_OK) return st;
+            for (int r = 0; r < n_contrib; ++r) h->dev_checked[r] = contribs[r];
+            h->dev_checked_n = n_contrib;
+        }
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     int64_t slots = 0;
