@@ -39,6 +39,9 @@
  *    pageable host memory, another device's memory, and a range that runs
  *    past the end of its allocation; this is best effort (the runtime sees
  *    allocations, not the caller's tensors inside them), not a guarantee.
+ *  - Every call that enqueues work must be made with the handle's device
+ *    current (else ZERO_ERR_STATE) and, for a non-NULL stream, with a stream
+ *    of that device (else ZERO_ERR_INVALID_ARG).
  *  - A handle is not thread-safe.  Separate handles are independent.
  *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  */

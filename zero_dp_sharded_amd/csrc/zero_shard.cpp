@@ -108,6 +108,28 @@ bool live(zero_shard_t h)
 
 bool finite_pos(double x) { return std::isfinite(x) && x > 0.0; }
 
+// Calls that launch work must run with the handle's device current and, for a
+// non-default stream, on a stream of that device; otherwise the kernels would
+// reach this device's arrays from another GPU.
+zero_status check_device(const zero_shard_s* h, void* stream, const char* who)
+{
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, who);
+    if (cur != h->device)
+        return fail(ZERO_ERR_STATE, "%s: the handle belongs to device %d but device %d is current",
+                    who, h->device, cur);
+    if (stream) {
+        int sd = -1;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sd) != hipSuccess)
+            (void)hipGetLastError();
+        else if (sd != h->device)
+            return fail(ZERO_ERR_INVALID_ARG, "%s: the stream belongs to device %d, the handle to %d",
+                        who, sd, h->device);
+    }
+    return ZERO_OK;
+}
+
 zero_status check_hparams(const zero_adam_hparams* hp)
 {
     if (!hp) return fail(ZERO_ERR_INVALID_ARG, "adam hparams: NULL");
@@ -581,6 +603,7 @@ zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int3
                                int64_t bucket_off, int64_t bucket_len, void* stream)
 {
     if (!live(h)) return fail(ZERO_ERR_STATE, "bucket_reduce: not a live handle");
+    if (zero_status ds = check_device(h, stream, "bucket_reduce")) return ds;
     if (h->device_mode)
         return fail(ZERO_ERR_STATE, "bucket_reduce: device-resident flow active; call zero_device_end");
     zero_status cst = check_contribs(h, contribs, n_contrib, "bucket_reduce");
@@ -875,6 +898,7 @@ extern "C" {
 zero_status zero_overflow_check(zero_shard_t h, void* stream, zero_step_info* out)
 {
     if (!live(h)) return fail(ZERO_ERR_STATE, "overflow_check: not a live handle");
+    if (zero_status ds = check_device(h, stream, "overflow_check")) return ds;
     if (h->device_mode)
         return fail(ZERO_ERR_STATE, "%s: device-resident flow active; call zero_device_end", "overflow_check");
     if (!out) return fail(ZERO_ERR_INVALID_ARG, "overflow_check: NULL out");
@@ -902,6 +926,7 @@ zero_status zero_adam_step(zero_shard_t h, const zero_adam_hparams* hp_in, void*
                            zero_step_info* out)
 {
     if (!live(h)) return fail(ZERO_ERR_STATE, "adam_step: not a live handle");
+    if (zero_status ds = check_device(h, stream, "adam_step")) return ds;
     if (h->opt != kOptAdam) return fail(ZERO_ERR_STATE, "adam_step: handle was created for SGD");
     if (h->phase != kChecked)
         return fail(ZERO_ERR_STATE, "adam_step: zero_overflow_check has not completed this step");
@@ -954,6 +979,7 @@ zero_status zero_adam_step_gated(zero_shard_t h, const zero_adam_hparams* hp_in,
 {
     const char* who = "adam_step_gated";
     zero_status st = gated_preconditions(h, kOptAdam, who);
+    if (st == ZERO_OK) st = check_device(h, stream, who);
     if (st != ZERO_OK) return st;
     if (hp_in && (st = check_hparams(hp_in)) != ZERO_OK) return st;
     const zero_adam_hparams& hp = hp_in ? *hp_in : h->hp;
@@ -967,6 +993,7 @@ zero_status zero_sgd_step(zero_shard_t h, const zero_sgd_hparams* hp_in, void* s
                           zero_step_info* out)
 {
     if (!live(h)) return fail(ZERO_ERR_STATE, "sgd_step: not a live handle");
+    if (zero_status ds = check_device(h, stream, "sgd_step")) return ds;
     if (h->opt != kOptSgd) return fail(ZERO_ERR_STATE, "sgd_step: handle was created for Adam");
     if (h->phase != kChecked)
         return fail(ZERO_ERR_STATE, "sgd_step: zero_overflow_check has not completed this step");
@@ -990,6 +1017,7 @@ zero_status zero_sgd_step_gated(zero_shard_t h, const zero_sgd_hparams* hp_in, v
 {
     const char* who = "sgd_step_gated";
     zero_status st = gated_preconditions(h, kOptSgd, who);
+    if (st == ZERO_OK) st = check_device(h, stream, who);
     if (st != ZERO_OK) return st;
     if (hp_in && (st = check_sgd_hparams(hp_in, h->d.exp_avg != nullptr)) != ZERO_OK) return st;
     const zero_sgd_hparams& hp = hp_in ? *hp_in : h->sgd;
@@ -1056,6 +1084,7 @@ zero_status zero_shard_set_clip(zero_shard_t h, double max_grad_norm)
 zero_status zero_device_begin(zero_shard_t h, void* stream)
 {
     if (!live(h)) return fail(ZERO_ERR_STATE, "device_begin: not a live handle");
+    if (zero_status ds = check_device(h, stream, "device_begin")) return ds;
     if (h->device_mode) return fail(ZERO_ERR_STATE, "device_begin: already active");
     if (h->phase != kIdle) return fail(ZERO_ERR_STATE, "device_begin: a step is in progress");
     zk::DevState init;
@@ -1079,6 +1108,7 @@ zero_status zero_step_device(zero_shard_t h, const void* const* contribs, int32_
                              void* stream)
 {
     if (!live(h)) return fail(ZERO_ERR_STATE, "step_device: not a live handle");
+    if (zero_status ds = check_device(h, stream, "step_device")) return ds;
     if (!h->device_mode) return fail(ZERO_ERR_STATE, "step_device: call zero_device_begin first");
     const bool scan = n_contrib == 0 && contribs == nullptr;
     if (!scan) {
@@ -1136,6 +1166,7 @@ zero_status zero_step_device(zero_shard_t h, const void* const* contribs, int32_
 zero_status zero_device_end(zero_shard_t h, void* stream, zero_step_info* out)
 {
     if (!live(h)) return fail(ZERO_ERR_STATE, "device_end: not a live handle");
+    if (zero_status ds = check_device(h, stream, "device_end")) return ds;
     if (!h->device_mode) return fail(ZERO_ERR_STATE, "device_end: the device flow is not active");
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipMemcpyAsync(h->host_dev, h->dev, sizeof(zk::DevState), hipMemcpyDeviceToHost, s);
