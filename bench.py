@@ -26,7 +26,6 @@ from __future__ import annotations
 
 import argparse
 import dataclasses
-import hashlib
 import json
 import os
 import sys
@@ -37,12 +36,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, AMD public spec
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "zero_dp_sharded_amd", "csrc", "zero_kernels.hip")
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_code_hash() -> str:
+    from zero_dp_sharded_amd.traffic import kernel_code_hash as h
+    return h()
 
 
 def measured_traffic(workload: str, per_launch_elems: int):
@@ -53,7 +51,7 @@ def measured_traffic(workload: str, per_launch_elems: int):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_code_sha256_16") != kernel_code_hash():
         return None
     if t.get("elems_per_launch") != per_launch_elems:
         return None

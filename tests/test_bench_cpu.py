@@ -35,12 +35,21 @@ def test_update_bytes_per_element():
 
 def test_traffic_only_from_counters_of_the_current_kernels(tmp_path, monkeypatch):
     assert bench.measured_traffic("no_such_workload", 1) is None
-    d = {"kernel_source_sha256_16": bench.kernel_source_hash(), "elems_per_launch": 10,
+    d = {"kernel_code_sha256_16": bench.kernel_code_hash(), "elems_per_launch": 10,
          "hbm_bytes_per_launch": 123.0}
     (tmp_path / "traffic_w.json").write_text(json.dumps(d))
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     assert bench.measured_traffic("w", 10) == 123.0
     assert bench.measured_traffic("w", 11) is None              # another shard size
-    d["kernel_source_sha256_16"] = "0" * 16
+    d["kernel_code_sha256_16"] = "0" * 16
     (tmp_path / "traffic_w.json").write_text(json.dumps(d))
     assert bench.measured_traffic("w", 10) is None              # stale kernels
+
+
+def test_kernel_code_hash_ignores_comments_only():
+    from zero_dp_sharded_amd.traffic import kernel_code_hash
+    src = "int f(int x)\n{\n    return x * 3;   // triple\n}\n"
+    assert kernel_code_hash([src]) == kernel_code_hash(["/* note */ int f(int x) { return x * 3; }"])
+    assert kernel_code_hash([src]) != kernel_code_hash([src.replace("3", "4")])
+    assert kernel_code_hash([src, "a"]) != kernel_code_hash([src + "a"])      # file boundaries count
+    assert len(kernel_code_hash()) == 16

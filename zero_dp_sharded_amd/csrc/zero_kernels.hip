@@ -10,9 +10,11 @@
 //    (lane-consecutive 16-byte or 8-byte pieces);
 //  - nontemporal loads and stores (each byte is touched once per step);
 //  - a cap on resident workgroups per CU, set by reserving dynamic LDS the
-//    kernels never touch: with the 3 to 9 concurrent streams of these kernels,
-//    fewer resident waves (10 per CU for Adam, 16 or 24 for SGD, 16 for the
-//    reduce) sustain more HBM bandwidth than full occupancy.
+//    kernels never touch: with the 3 to 17 concurrent streams of the update
+//    and reduce kernels, fewer resident waves (10 per CU for Adam, 16 or 24
+//    for SGD, 12 or 8 for the reduce) sustain more HBM bandwidth than full
+//    occupancy; the one-stream scan keeps 32 waves with 4 runs per lane.  The
+//    measured optimum keeps roughly 96-144 KiB of loads in flight per CU.
 // The only cross-lane work is the fixed-shape reduction of the overflow flag
 // and the squared gradient norm: wave butterfly, one LDS slot per wave, one
 // fp64 partial per workgroup, then a fixed-order fold of one or two levels

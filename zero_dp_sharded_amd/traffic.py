@@ -8,8 +8,9 @@
             the reduce, the counters scaled by what they read for the copy
             (bytes moved / counter bytes), as JSON.
 
-The JSON carries a hash of the kernel source; bench.py uses its byte count
-only while the source is unchanged.
+The JSON carries a hash of the kernels' code (zero_kernels.hip and the shapes
+in zero_kernels.h, comments and whitespace left out); bench.py uses its byte
+count only while that code is unchanged.
 """
 from __future__ import annotations
 
@@ -19,11 +20,13 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SRC = os.path.join(ROOT, "zero_dp_sharded_amd", "csrc", "zero_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "zero_dp_sharded_amd", "csrc", name)
+                  for name in ("zero_kernels.hip", "zero_kernels.h")]
 COPY_BYTES = 8_000_000_000      # bytes read and bytes written by bench.py's copy
 
 
@@ -61,9 +64,27 @@ def _match(d, needle):
     return sum(vals) / len(vals), len(vals)
 
 
-def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed (the
+    kernel sources hold no comment markers inside string literals)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_code_hash(texts=None) -> str:
+    """First 16 hex digits of the SHA-256 of the kernels' code, by default of
+    the files in KERNEL_SOURCES."""
+    if texts is None:
+        texts = []
+        for path in KERNEL_SOURCES:
+            with open(path) as f:
+                texts.append(f.read())
+    h = hashlib.sha256()
+    for t in texts:
+        h.update(code_only(t).encode())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
 
 
 def traffic(args) -> int:
@@ -74,7 +95,7 @@ def traffic(args) -> int:
     ffac = COPY_BYTES / (cf * 1024.0)
     wfac = COPY_BYTES / (cw * 1024.0)
     out = {"command_fetch": args.cmd_fetch, "command_write": args.cmd_write,
-           "kernel_source_sha256_16": kernel_hash(), "elems_per_launch": args.elems,
+           "kernel_code_sha256_16": kernel_code_hash(), "elems_per_launch": args.elems,
            "copy_calibration": {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
                                 "fetch_kib": cf, "write_kib": cw,
                                 "fetch_factor": ffac, "write_factor": wfac},
