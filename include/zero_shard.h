@@ -207,8 +207,9 @@ zero_status zero_state_bytes_ex(int64_t psi, int32_t nd, int32_t n_contrib,
 /*
  * Create a handle bound to the current device.  Copies *desc, *hp and *ls.
  * Allocates a device workspace for the check's per-workgroup partials and the
- * device-resident step state, 8 bytes per 1024 shard elements plus 16 bytes
- * per bucket plus 8.2 KiB (15.6 MB for a 2e9-element shard), and 256 bytes of
+ * device-resident step state, 8 bytes per 512 shard elements (per 256 with
+ * ZERO_FP32 storage) plus 16 bytes per bucket plus 8.2 KiB (31.3 MB for a
+ * 2e9-element 2-byte shard), and 256 bytes of
  * pinned host memory; touches none of the caller's arrays.
  * Errors: INVALID_ARG (NULL argument or pointer in desc, psi < 1, nd < 1, rank
  * outside [0, nd), bucket_elems < 1, unknown lp, misaligned or overlapping

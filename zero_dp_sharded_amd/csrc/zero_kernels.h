@@ -9,18 +9,23 @@ namespace zk {
 
 constexpr int kMaxContrib = 64;
 
-// Reduce / scan: 256 lanes per workgroup, each lane a few 16-byte runs (a run
-// is 8 two-byte or 4 fp32 elements; each load instruction of a wave covers
-// 1 KiB contiguously).  Runs per lane and resident workgroups per CU are set
-// so that a CU keeps about 96-144 KiB of loads in flight:
-//   reduce, R < 8:   3 runs, 3 workgroups per CU (2 runs for buckets too small
-//                    to fill the chip, where more workgroups finish sooner);
-//   reduce, R >= 8:  1 run, 3 workgroups per CU (2 from R = 16);
-//   scan (1 stream): 4 runs, 8 workgroups per CU.
+// Reduce / scan: each lane a few 16-byte runs (a run is 8 two-byte or 4 fp32
+// elements; each load instruction of a wave covers 1 KiB contiguously).
+// Workgroup size, runs per lane and resident workgroups per CU, as measured
+// best on MI355X (roughly 80-144 KiB of loads in flight per CU):
+//   reduce, R < 8:   256 lanes, 3 runs, 3 workgroups per CU (2 runs for
+//                    buckets too small to fill the chip, where more
+//                    workgroups finish sooner);
+//   reduce, R >= 8:  64 lanes (one wave), 1 run, 10 workgroups per CU
+//                    (6 from R = 16);
+//   scan (1 stream): 256 lanes, 4 runs, 8 workgroups per CU.
 // (The ZK_* macros exist only to build tuning variants; the defaults are the
 // measured optimum.)
 #ifndef ZK_RED_BLOCK
 #define ZK_RED_BLOCK 256
+#endif
+#ifndef ZK_RED_BLOCK_MANY
+#define ZK_RED_BLOCK_MANY 64
 #endif
 #ifndef ZK_RED_RUNS
 #define ZK_RED_RUNS 3
@@ -35,10 +40,10 @@ constexpr int kMaxContrib = 64;
 #define ZK_RED_PER_CU 3
 #endif
 #ifndef ZK_RED_PER_CU_MANY
-#define ZK_RED_PER_CU_MANY 3
+#define ZK_RED_PER_CU_MANY 10
 #endif
 #ifndef ZK_RED_PER_CU_WIDE
-#define ZK_RED_PER_CU_WIDE 2
+#define ZK_RED_PER_CU_WIDE 6
 #endif
 #ifndef ZK_SCAN_RUNS
 #define ZK_SCAN_RUNS 4
@@ -67,10 +72,13 @@ constexpr int kMaxContrib = 64;
 #ifndef ZK_SGD_PLAIN_PER_CU
 #define ZK_SGD_PLAIN_PER_CU 24
 #endif
-constexpr int kRedBlock = ZK_RED_BLOCK;
+constexpr int kRedBlock = ZK_RED_BLOCK;           // reduce (R < 8) and scan
+constexpr int kRedBlockMany = ZK_RED_BLOCK_MANY;  // reduce, R >= 8
 constexpr int kRedRuns = ZK_RED_RUNS;
 constexpr int kRedRunsMany = ZK_RED_RUNS_MANY;   // runs per lane when R >= 8
 constexpr int kRedManyR = 8;
+// Lanes per workgroup of the reduce with R contributions.
+inline int red_block(int R) { return R >= kRedManyR ? kRedBlockMany : kRedBlock; }
 constexpr int kRedRunsSmall = ZK_RED_RUNS_SMALL;   // R < 8, bucket below kRedSmallNvec runs
 // runs of one full residency of kRedRuns workgroups on 256 CUs
 constexpr int64_t kRedSmallNvec = (int64_t)256 * ZK_RED_PER_CU * ZK_RED_BLOCK * ZK_RED_RUNS;
@@ -85,9 +93,10 @@ inline int red_runs(int R, int64_t nvec)
 constexpr int kScanRuns = ZK_SCAN_RUNS;
 constexpr int kScanPerCU = ZK_SCAN_PER_CU;
 constexpr int kMin2(int a, int b) { return a < b ? a : b; }
-constexpr int kMinRuns = kMin2(kMin2(kRedRuns, kRedRunsSmall), kMin2(kRedRunsMany, kScanRuns));
-// elements one reduce or scan workgroup covers at the least (fp32, 4 per run)
-constexpr int64_t kRedElemsPerBlockMin = (int64_t)kRedBlock * kMinRuns * 4;
+// runs one vector reduce or scan workgroup covers at the least
+constexpr int64_t kRunsPerBlockMin =
+    kMin2(kMin2(kRedBlock * kMin2(kRedRuns, kRedRunsSmall), kRedBlockMany * kRedRunsMany),
+          kRedBlock * kScanRuns);
 constexpr int kRedPerCU = ZK_RED_PER_CU;
 constexpr int kRedPerCUMany = ZK_RED_PER_CU_MANY;   // residency when 8 <= R < 16
 constexpr int kRedPerCUWide = ZK_RED_PER_CU_WIDE;   // residency when R >= 16
@@ -256,9 +265,11 @@ inline int run_width(int32_t lp) { return lp == 3 ? 4 : 8; }
 
 // Partial slots a reduce / scan of this layout writes: one per workgroup of
 // the vector kernel plus one per workgroup of the element-wise kernel.  W is
-// the run width of the storage format, U the runs per lane (red_runs(R, nvec)
-// for a reduce, kScanRuns for a scan).
-int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok, int W, int U);
+// the run width of the storage format, U the runs per lane and BS the lanes
+// per workgroup (red_runs(R, nvec) and red_block(R) for a reduce, kScanRuns
+// and kRedBlock for a scan).
+int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok, int W, int U,
+                      int BS);
 
 hipError_t launch_reduce(const ReduceLaunch& L, hipStream_t s);
 hipError_t launch_scan(const ScanLaunch& L, hipStream_t s);

@@ -236,25 +236,25 @@ __device__ __forceinline__ float check_inv_scale(float arg, const DevState* dev)
     return dev != nullptr ? dev->inv_scale : arg;
 }
 
-// Vector body: workgroup b covers runs [b*B*U, (b+1)*B*U) for B lanes and U
-// runs per lane; lane l owns runs b*B*U + u*B + l.  Element offsets past `head`
+// Vector body: workgroup b covers runs [b*BS*U, (b+1)*BS*U) for BS lanes and
+// U runs per lane; lane l owns runs b*BS*U + u*BS + l.  Element offsets past `head`
 // are multiples of W, so contribution and output pointers advanced by `head`
 // are 16-byte aligned and are indexed in units of runs.
-template <int LP, int RT, int U>
-__global__ __launch_bounds__(kRedBlock) void reduce_vec_kernel(ReduceLaunch L)
+template <int LP, int RT, int U, int BS>
+__global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
 {
     using VW = typename Fmt<LP>::VW;
     using FW = typename Fmt<LP>::FW;
     int flag = 0;
     double ss = 0.0;
     const float inv_scale = check_inv_scale(L.inv_scale, L.dev);
-    const int64_t v0 = (int64_t)blockIdx.x * (kRedBlock * U) + threadIdx.x;
+    const int64_t v0 = (int64_t)blockIdx.x * (BS * U) + threadIdx.x;
     if constexpr (RT > 0 && RT * U <= 16) {
         // every load of all U runs in flight before the arithmetic
         VW x[U][RT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t vi = v0 + u * kRedBlock;
+            const int64_t vi = v0 + u * BS;
             if (vi < L.nvec) {
 #pragma unroll
                 for (int r = 0; r < RT; ++r) x[u][r] = ld_nt<VW>(adv<LP>(L.c.p[r], L.head), vi);
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kRedBlock) void reduce_vec_kernel(ReduceLaunch L)
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t vi = v0 + u * kRedBlock;
+            const int64_t vi = v0 + u * BS;
             if (vi < L.nvec) {
                 FW acc = (FW)(0.f);
 #pragma unroll
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(kRedBlock) void reduce_vec_kernel(ReduceLaunch L)
         }
     } else {
         for (int u = 0; u < U; ++u) {
-            const int64_t vi = v0 + u * kRedBlock;
+            const int64_t vi = v0 + u * BS;
             if (vi >= L.nvec) break;
             FW acc = (FW)(0.f);
             if constexpr (RT > 0) {
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(kRedBlock) void reduce_vec_kernel(ReduceLaunch L)
             reduce_finish<LP>(L, vi, acc, inv_scale, flag, ss);
         }
     }
-    block_partial<kRedBlock>(L.partial + L.slot_base + blockIdx.x, flag, ss);
+    block_partial<BS>(L.partial + L.slot_base + blockIdx.x, flag, ss);
 }
 
 template <int LP>
@@ -662,37 +662,38 @@ Ranges ranges_of(int64_t n, int64_t head, int64_t body, int32_t vec_ok)
     return rg;
 }
 
-template <int LP, int RT, int U>
+template <int LP, int RT, int U, int BS>
 void reduce_vec_go(const ReduceLaunch& L, unsigned grid, hipStream_t s)
 {
-    reduce_vec_kernel<LP, RT, U><<<grid, kRedBlock, L.lds_reserve, s>>>(L);
+    reduce_vec_kernel<LP, RT, U, BS><<<grid, BS, L.lds_reserve, s>>>(L);
 }
 
-// Below 8 contributions, the runs per lane U is kRedRuns or kRedRunsSmall;
-// from 8 on it is kRedRunsMany.  U must be the one the dispatch sized the grid
-// with (red_runs of the whole bucket).
+// Below 8 contributions the workgroup has kRedBlock lanes and the runs per
+// lane U is kRedRuns or kRedRunsSmall; from 8 on it has kRedBlockMany lanes
+// and U is kRedRunsMany.  U must be the one the dispatch sized the grid with
+// (red_runs of the whole bucket).
 template <int LP, int RT>
 void reduce_vec_few(const ReduceLaunch& L, unsigned grid, int U, hipStream_t s)
 {
     if (U == kRedRunsSmall)
-        reduce_vec_go<LP, RT, kRedRunsSmall>(L, grid, s);
+        reduce_vec_go<LP, RT, kRedRunsSmall, kRedBlock>(L, grid, s);
     else
-        reduce_vec_go<LP, RT, kRedRuns>(L, grid, s);
+        reduce_vec_go<LP, RT, kRedRuns, kRedBlock>(L, grid, s);
 }
 
 template <int LP>
 hipError_t reduce_vec_launch(const ReduceLaunch& L, unsigned grid, int U, hipStream_t s)
 {
-    constexpr int B = kRedRunsMany;
+    constexpr int B = kRedRunsMany, BM = kRedBlockMany;
     switch (L.R) {
     case 1: reduce_vec_few<LP, 1>(L, grid, U, s); break;
     case 2: reduce_vec_few<LP, 2>(L, grid, U, s); break;
     case 4: reduce_vec_few<LP, 4>(L, grid, U, s); break;
-    case 8: reduce_vec_go<LP, 8, B>(L, grid, s); break;
-    case 16: reduce_vec_go<LP, 16, B>(L, grid, s); break;
+    case 8: reduce_vec_go<LP, 8, B, BM>(L, grid, s); break;
+    case 16: reduce_vec_go<LP, 16, B, BM>(L, grid, s); break;
     default:
         if (L.R >= kRedManyR)
-            reduce_vec_go<LP, 0, B>(L, grid, s);
+            reduce_vec_go<LP, 0, B, BM>(L, grid, s);
         else
             reduce_vec_few<LP, 0>(L, grid, U, s);
         break;
@@ -705,11 +706,12 @@ hipError_t reduce_dispatch(const ReduceLaunch& L, hipStream_t s)
 {
     constexpr int W = Fmt<LP>::W;
     const int U = red_runs(L.R, L.nvec);
-    const int64_t runs_per_block = (int64_t)kRedBlock * U;
+    const int BS = red_block(L.R);
+    const int64_t runs_per_block = (int64_t)BS * U;
     const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, runs_per_block) : 0;
     // consecutive launches of at most kMaxLaunchItems work-items; each starts
     // its runs and its partial slots where the previous one stopped
-    const int64_t max_blocks = kMaxLaunchItems / kRedBlock;
+    const int64_t max_blocks = kMaxLaunchItems / BS;
     for (int64_t b0 = 0; b0 < vblocks; b0 += max_blocks) {
         const int64_t nb = vblocks - b0 < max_blocks ? vblocks - b0 : max_blocks;
         ReduceLaunch part = L;
@@ -814,10 +816,11 @@ hipError_t sgd_dispatch_kind(const SgdLaunch& a, hipStream_t s)
 
 }  // namespace
 
-int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok, int W, int U)
+int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok, int W, int U,
+                      int BS)
 {
     (void)head;
-    const int64_t vblocks = vec_ok ? ceil_div(nvec, (int64_t)kRedBlock * U) : 0;
+    const int64_t vblocks = vec_ok ? ceil_div(nvec, (int64_t)BS * U) : 0;
     const int64_t scalars = vec_ok ? n - (int64_t)W * nvec : n;
     return vblocks + ceil_div(scalars, kScalarElemsPerBlock);
 }

@@ -361,8 +361,8 @@ static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m,
     // elements uses at most len/per + 2 workgroups, per being the smaller of
     // the element-wise and the vector kernels' elements per workgroup (plus a
     // ragged end), and the stand-alone scan needs no more.
-    const int64_t per = zk::kScalarElemsPerBlock < zk::kRedElemsPerBlockMin
-                            ? zk::kScalarElemsPerBlock : zk::kRedElemsPerBlockMin;
+    const int64_t vper = zk::kRunsPerBlockMin * zk::run_width(d.lp);
+    const int64_t per = zk::kScalarElemsPerBlock < vper ? zk::kScalarElemsPerBlock : vper;
     const int64_t nbuckets = (S + d.bucket_elems - 1) / d.bucket_elems;
     const int64_t nslots = S / per + 2 * nbuckets + 4;
     if (nslots > (int64_t(1) << 25))
@@ -531,7 +531,8 @@ static zero_status enqueue_reduce(zero_shard_s* h, const void* const* ptrs, int3
                     : n_contrib >= zk::kRedManyR ? h->lds_reduce_many
                                                  : h->lds_reduce;
     L.dev = dev;
-    const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::red_runs(L.R, L.nvec));
+    const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::red_runs(L.R, L.nvec),
+                                             zk::red_block(L.R));
     if (L.slot_base + blocks > h->nslots)
         return fail(ZERO_ERR_UNSUPPORTED, "%s: partial slots exhausted", who);
     hipError_t e = zk::launch_reduce(L, s);
@@ -662,7 +663,7 @@ static zero_status enqueue_scan(zero_shard_s* h, const zk::DevState* dev, hipStr
     L.dev = dev;
     hipError_t e = zk::launch_scan(L, s);
     if (e != hipSuccess) return hip_fail(e, who);
-    *slots = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::kScanRuns);
+    *slots = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::kScanRuns, zk::kRedBlock);
     return ZERO_OK;
 }
 
