@@ -4,8 +4,8 @@ element against the oracle.
 Below 8 contributions a bucket reduce gives each lane 3 runs of 16 bytes once
 the bucket holds at least 589,824 runs (256 CUs x 3 workgroups x 256 lanes x
 3 runs: 4,718,592 two-byte or 2,359,296 fp32 elements) and 2 runs below that;
-from 8 contributions it gives 1 run.  The stand-alone scan gives each lane 4
-runs.  Each case below puts one bucket exactly at that threshold and one just
+from 8 contributions it gives 1 run on one-wave workgroups.  The stand-alone
+scan gives each lane 4 runs.  Each case below puts one bucket exactly at that threshold and one just
 under it (with a ragged element-wise tail) into the same step, with every
 contribution-count class and storage format, and with base pointers off the
 16-byte grid.
