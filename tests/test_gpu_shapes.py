@@ -2,9 +2,9 @@
 element against the oracle.
 
 Below 8 contributions a bucket reduce gives each lane 3 runs of 16 bytes once
-the bucket holds at least 589,824 runs (256 CUs x 3 workgroups x 256 lanes x
-3 runs: 4,718,592 two-byte or 2,359,296 fp32 elements) and 2 runs below that;
-from 8 contributions it gives 1 run on one-wave workgroups.  The stand-alone
+the bucket holds at least 491,520 runs (256 CUs x 10 workgroups x 64 lanes x
+3 runs: 3,932,160 two-byte or 1,966,080 fp32 elements) and 2 runs below that;
+from 8 contributions it gives 1 run.  The stand-alone
 scan gives each lane 4 runs.  Each case below puts one bucket exactly at that threshold and one just
 under it (with a ragged element-wise tail) into the same step, with every
 contribution-count class and storage format, and with base pointers off the
@@ -24,7 +24,7 @@ from zero_dp_sharded_amd import synth
 pytestmark = pytest.mark.gpu
 
 W = synth.WORKLOADS
-THRESHOLD_RUNS = 256 * 3 * 256 * 3
+THRESHOLD_RUNS = 256 * 10 * 64 * 3
 
 
 def _two_buckets(run_width: int):

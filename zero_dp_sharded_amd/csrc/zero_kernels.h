@@ -13,16 +13,15 @@ constexpr int kMaxContrib = 64;
 // elements; each load instruction of a wave covers 1 KiB contiguously).
 // Workgroup size, runs per lane and resident workgroups per CU, as measured
 // best on MI355X (roughly 80-144 KiB of loads in flight per CU):
-//   reduce, R < 8:   256 lanes, 3 runs, 3 workgroups per CU (2 runs for
-//                    buckets too small to fill the chip, where more
+//   reduce, R < 8:   64 lanes (one wave), 3 runs, 10 workgroups per CU (2 runs
+//                    for buckets too small to fill the chip, where more
 //                    workgroups finish sooner);
-//   reduce, R >= 8:  64 lanes (one wave), 1 run, 10 workgroups per CU
-//                    (6 from R = 16);
+//   reduce, R >= 8:  64 lanes, 1 run, 10 workgroups per CU (6 from R = 16);
 //   scan (1 stream): 256 lanes, 4 runs, 8 workgroups per CU.
 // (The ZK_* macros exist only to build tuning variants; the defaults are the
 // measured optimum.)
 #ifndef ZK_RED_BLOCK
-#define ZK_RED_BLOCK 256
+#define ZK_RED_BLOCK 64
 #endif
 #ifndef ZK_RED_BLOCK_MANY
 #define ZK_RED_BLOCK_MANY 64
@@ -37,13 +36,16 @@ constexpr int kMaxContrib = 64;
 #define ZK_RED_RUNS_MANY 1
 #endif
 #ifndef ZK_RED_PER_CU
-#define ZK_RED_PER_CU 3
+#define ZK_RED_PER_CU 10
 #endif
 #ifndef ZK_RED_PER_CU_MANY
 #define ZK_RED_PER_CU_MANY 10
 #endif
 #ifndef ZK_RED_PER_CU_WIDE
 #define ZK_RED_PER_CU_WIDE 6
+#endif
+#ifndef ZK_SCAN_BLOCK
+#define ZK_SCAN_BLOCK 256
 #endif
 #ifndef ZK_SCAN_RUNS
 #define ZK_SCAN_RUNS 4
@@ -72,7 +74,7 @@ constexpr int kMaxContrib = 64;
 #ifndef ZK_SGD_PLAIN_PER_CU
 #define ZK_SGD_PLAIN_PER_CU 24
 #endif
-constexpr int kRedBlock = ZK_RED_BLOCK;           // reduce (R < 8) and scan
+constexpr int kRedBlock = ZK_RED_BLOCK;           // reduce, R < 8
 constexpr int kRedBlockMany = ZK_RED_BLOCK_MANY;  // reduce, R >= 8
 constexpr int kRedRuns = ZK_RED_RUNS;
 constexpr int kRedRunsMany = ZK_RED_RUNS_MANY;   // runs per lane when R >= 8
@@ -90,13 +92,14 @@ inline int red_runs(int R, int64_t nvec)
 }
 // The stand-alone scan reads a single stream, so it takes its own runs per
 // lane and residency.
+constexpr int kScanBlock = ZK_SCAN_BLOCK;
 constexpr int kScanRuns = ZK_SCAN_RUNS;
 constexpr int kScanPerCU = ZK_SCAN_PER_CU;
 constexpr int kMin2(int a, int b) { return a < b ? a : b; }
 // runs one vector reduce or scan workgroup covers at the least
 constexpr int64_t kRunsPerBlockMin =
     kMin2(kMin2(kRedBlock * kMin2(kRedRuns, kRedRunsSmall), kRedBlockMany * kRedRunsMany),
-          kRedBlock * kScanRuns);
+          kScanBlock * kScanRuns);
 constexpr int kRedPerCU = ZK_RED_PER_CU;
 constexpr int kRedPerCUMany = ZK_RED_PER_CU_MANY;   // residency when 8 <= R < 16
 constexpr int kRedPerCUWide = ZK_RED_PER_CU_WIDE;   // residency when R >= 16
@@ -267,7 +270,7 @@ inline int run_width(int32_t lp) { return lp == 3 ? 4 : 8; }
 // the vector kernel plus one per workgroup of the element-wise kernel.  W is
 // the run width of the storage format, U the runs per lane and BS the lanes
 // per workgroup (red_runs(R, nvec) and red_block(R) for a reduce, kScanRuns
-// and kRedBlock for a scan).
+// and kScanBlock for a scan).
 int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok, int W, int U,
                       int BS);
 

@@ -316,23 +316,23 @@ __global__ __launch_bounds__(kScalarBlock) void reduce_elem_kernel(ReduceLaunch 
 }
 
 template <int LP>
-__global__ __launch_bounds__(kRedBlock) void scan_vec_kernel(ScanLaunch L)
+__global__ __launch_bounds__(kScanBlock) void scan_vec_kernel(ScanLaunch L)
 {
     using VW = typename Fmt<LP>::VW;
     int flag = 0;
     double ss = 0.0;
     const float inv_scale = check_inv_scale(L.inv_scale, L.dev);
-    const int64_t v0 = (int64_t)blockIdx.x * (kRedBlock * kScanRuns) + threadIdx.x;
+    const int64_t v0 = (int64_t)blockIdx.x * (kScanBlock * kScanRuns) + threadIdx.x;
     VW x[kScanRuns];
 #pragma unroll
     for (int u = 0; u < kScanRuns; ++u) {
-        const int64_t vi = v0 + u * kRedBlock;
+        const int64_t vi = v0 + u * kScanBlock;
         if (vi < L.nvec) x[u] = ld_nt<VW>(adv<LP>(L.g, L.head), vi);
     }
 #pragma unroll
     for (int u = 0; u < kScanRuns; ++u)
-        if (v0 + u * kRedBlock < L.nvec) check_v<LP>(x[u], inv_scale, flag, ss);
-    block_partial<kRedBlock>(L.partial + L.slot_base + blockIdx.x, flag, ss);
+        if (v0 + u * kScanBlock < L.nvec) check_v<LP>(x[u], inv_scale, flag, ss);
+    block_partial<kScanBlock>(L.partial + L.slot_base + blockIdx.x, flag, ss);
 }
 
 template <int LP>
@@ -732,16 +732,16 @@ template <int LP>
 hipError_t scan_dispatch(const ScanLaunch& L, hipStream_t s)
 {
     constexpr int W = Fmt<LP>::W;
-    const int64_t runs_per_block = (int64_t)kRedBlock * kScanRuns;
+    const int64_t runs_per_block = (int64_t)kScanBlock * kScanRuns;
     const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, runs_per_block) : 0;
-    const int64_t max_blocks = kMaxLaunchItems / kRedBlock;
+    const int64_t max_blocks = kMaxLaunchItems / kScanBlock;
     for (int64_t b0 = 0; b0 < vblocks; b0 += max_blocks) {
         const int64_t nb = vblocks - b0 < max_blocks ? vblocks - b0 : max_blocks;
         ScanLaunch part = L;
         part.head = L.head + W * runs_per_block * b0;
         part.nvec = L.nvec - runs_per_block * b0;
         part.slot_base = L.slot_base + b0;
-        scan_vec_kernel<LP><<<(unsigned)nb, kRedBlock, L.lds_reserve, s>>>(part);
+        scan_vec_kernel<LP><<<(unsigned)nb, kScanBlock, L.lds_reserve, s>>>(part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

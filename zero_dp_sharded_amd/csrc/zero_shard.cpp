@@ -663,7 +663,7 @@ static zero_status enqueue_scan(zero_shard_s* h, const zk::DevState* dev, hipStr
     L.dev = dev;
     hipError_t e = zk::launch_scan(L, s);
     if (e != hipSuccess) return hip_fail(e, who);
-    *slots = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::kScanRuns, zk::kRedBlock);
+    *slots = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::kScanRuns, zk::kScanBlock);
     return ZERO_OK;
 }
 
