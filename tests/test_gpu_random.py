@@ -1,8 +1,9 @@
 """Seeded random configurations against the oracle: shard size, contribution
 count, bucket size, storage format, optimizer, flow, clipping, array offsets
-and an overflow step drawn at random (fixed seed, so every run checks the same
-48 cases), each a few steps at sizes the oracle finishes in well under a
-second.  Catches interactions the targeted tests do not enumerate."""
+and an overflow step drawn at random (fixed seeds, so every run checks the same
+48 small cases and 12 large ones), each a few steps at sizes the oracle
+finishes in about a second.  Catches interactions the targeted tests do not
+enumerate."""
 import dataclasses
 
 import numpy as np
@@ -18,12 +19,18 @@ BASES = {"fp16": synth.WORKLOADS["gpt2_1.5b"], "bf16": synth.WORKLOADS["7.5b_bf1
          "fp32": synth.WORKLOADS["c1_7.5b_sgdm"]}
 
 
-def _case(k: int):
-    rng = np.random.default_rng(1000 + k)
+SMALL = [1, 5, 63, 64, 65, 1000, 4099, 65_537, 131_071, 250_000]
+# shards whose buckets can reach the size at which the reduce gives each lane 3
+# runs (491,520 runs: 3,932,160 two-byte or 1,966,080 fp32 elements)
+LARGE = [1_966_081, 3_932_167, 4_500_001, 6_000_007]
+
+
+def _case(k: int, sizes=SMALL, seed0: int = 1000, steps: int = 3, r_hi: int = 21):
+    rng = np.random.default_rng(seed0 + k)
     lp = ["fp16", "bf16", "fp32"][rng.integers(3)]
     opt = ["adam", "sgd_m", "sgd"][rng.integers(3)]
-    elems = int(rng.choice([1, 5, 63, 64, 65, 1000, 4099, 65_537, 131_071, 250_000]))
-    R = int(rng.integers(1, 21))
+    elems = int(rng.choice(sizes))
+    R = int(rng.integers(1, r_hi))
     cb = int(max(1, min(elems, rng.integers(1, elems + 1) if rng.random() < 0.5 else elems)))
     flow = ["sync", "gated", "device"][rng.integers(3)]
     clip = bool(rng.random() < 0.3)
@@ -31,16 +38,16 @@ def _case(k: int):
     names = ["master", "m", "v", "grad", "param", "contrib"]
     offsets = {n: int(rng.integers(0, 8)) for n in names} if rng.random() < 0.5 else {}
     w = dataclasses.replace(
-        BASES[lp], name=f"random case {k}", R=R, steps=3, lp=lp, inject_step=inject,
+        BASES[lp], name=f"random case {k}", R=R, steps=steps, lp=lp,
+        inject_step=None if inject is None else min(inject, steps - 1),
         opt="adam" if opt == "adam" else "sgd", momentum=0.9 if opt == "sgd_m" else 0.0,
         scale=float(2 ** int(rng.integers(0, 12))), dynamic=int(rng.integers(0, 2)),
         weight_decay=float(rng.choice([0.0, 0.01])))
     return w, elems, cb, flow, clip, offsets
 
 
-@pytest.mark.parametrize("k", range(48))
-def test_random_case(k):
-    w, elems, cb, flow, clip, offsets = _case(k)
+def _run_case(k, case):
+    w, elems, cb, flow, clip, offsets = case
     hp = hp_of(w)
     if w.opt == "adam" and k % 4 == 1:
         hp = dataclasses.replace(hp, wd_mode=zs.ZERO_WD_L2)
@@ -57,3 +64,15 @@ def test_random_case(k):
         assert errs["bitwise"], (k, errs)
     if w.inject_step is not None:
         assert g.infos[w.inject_step].overflow == 1
+
+
+@pytest.mark.parametrize("k", range(48))
+def test_random_case(k):
+    _run_case(k, _case(k))
+
+
+@pytest.mark.parametrize("k", range(12))
+def test_random_large_case(k):
+    """Shards of 2-6M elements, where a bucket of up to the whole shard takes
+    3 runs per lane below 8 contributions; 2 steps each."""
+    _run_case(100 + k, _case(k, LARGE, seed0=2000, steps=2, r_hi=8 if k % 3 else 21))
