@@ -290,6 +290,73 @@ def test_graph_captured_step_replays(name):
 
 
 @pytest.mark.parametrize("name", ["adam_fp16", "sgdm_fp32"])
+def test_graph_holding_several_steps(name):
+    """Three zero_step_device calls captured in one CUDA graph: each replay runs
+    three steps whose counters, bias corrections and loss scale evolve on the
+    device.  Two replays equal six eager device-resident steps after every
+    third step, bitwise, and the oracle's six steps on the same contributions."""
+    w = _w(CASES[name], steps=6, dynamic=1, scale=64.0)
+    dev = torch.device("cuda", 0)
+    elems, cb, K = 70_001, 25_000, 3
+    hp = _hp(name, w)
+
+    def make():
+        master0, m0, v0 = synth.init_state(w, dev, 0, elems=elems)
+        master = master0.clone()
+        m = m0.clone() if w.has_m else None
+        v = v0.clone() if w.has_v else None
+        grad = torch.zeros(elems, dtype=w.torch_lp, device=dev)
+        param = None if w.lp == "fp32" else master0.to(w.torch_lp)
+        if w.opt == "sgd":
+            h = zs.zero_shard_init_sgd(master, m, grad, param, psi=elems * w.nd, nd=w.nd, rank=0,
+                                       bucket_elems=cb, hp=hp, ls=ls_of(w))
+        else:
+            h = zs.zero_shard_init(master, m, v, grad, param, psi=elems * w.nd, nd=w.nd, rank=0,
+                                   bucket_elems=cb, hp=hp, ls=ls_of(w))
+        return h, dict(master=master, m=m, v=v, param=param, master0=master0, m0=m0, v0=v0)
+
+    bufs = synth.alloc_contribs(w, dev, elems=elems)
+    synth.fill_contribs(w, bufs, 0, w.scale, seed=0)
+    ha, A = make()
+    hb, B = make()
+    ohp, ols = oracle_hp(hp), oracle_ls(ls_of(w))
+    ost = oracle.new_state(LP_CODE[w.lp], f32(A["master0"]), f32(A["m0"]) if w.has_m else None,
+                           f32(A["v0"]) if w.has_v else None, ohp, ols)
+    cs = [stored(b) for b in bufs]
+    log(f"[graph x{K}] {name}")
+    try:
+        zs.zero_device_begin(ha)
+        zs.zero_device_begin(hb)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(K):
+                zs.zero_step_device(hb, bufs)
+        torch.cuda.synchronize()
+        for rep in range(w.steps // K):
+            for _ in range(K):
+                zs.zero_step_device(ha, bufs)
+                oracle.step(ost, cs, cb, ohp, ols)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for k in ("master", "m", "v", "param"):
+                if A[k] is not None:
+                    view = torch.int32 if A[k].dtype == torch.float32 else torch.int16
+                    assert torch.equal(A[k].view(view), B[k].view(view)), (name, rep, k)
+        ia, ib = zs.zero_device_end(ha), zs.zero_device_end(hb)
+        assert (ia.step_t, ia.scale_next) == (ib.step_t, ib.scale_next) == (w.steps, w.scale)
+        assert ost.t == w.steps
+        assert np.array_equal(f32(B["master"]).view(np.uint32), ost.master.view(np.uint32))
+        if B["param"] is not None:
+            assert np.array_equal(stored(B["param"]), ost.param)
+        del graph
+    finally:
+        zs.zero_shard_destroy(ha)
+        zs.zero_shard_destroy(hb)
+
+
+@pytest.mark.parametrize("name", ["adam_fp16", "sgdm_fp32"])
 def test_device_flow_after_counter_restore(name):
     """Counters restored with zero_shard_set_counters (t = 7, scale 64, 3 clean
     steps, as after a checkpoint): the device-resident flow starts from them
