@@ -65,14 +65,21 @@ def test_contribution_counts(R):
     assert compare(w, g, st, oi, f"R={R}")["bitwise"]
 
 
-@pytest.mark.parametrize("over", [
+HP_VARIANTS = [
     dict(weight_decay=0.1, wd_mode=0), dict(weight_decay=0.1, wd_mode=1),
     dict(bias_correction=0), dict(beta1=0.0), dict(lr=0.0), dict(initial_step=5),
     dict(beta1=0.5, beta2=0.75, eps=1e-3),
-])
-def test_hparam_variants(over):
+]
+
+
+@pytest.mark.parametrize("flow", ["sync", "gated", "device"])
+@pytest.mark.parametrize("over", HP_VARIANTS)
+def test_hparam_variants(over, flow):
+    """Each hyper-parameter variant in the synchronous, device-gated and
+    device-resident flows (the last computes the step count and the bias
+    corrections on the device)."""
     w = W["gpt2_1.5b"]
     hp = hp_of(w, **over)
-    g = run_gpu(w, elems=50_001, steps=4, bucket_elems=20_000, hp=hp)
+    g = run_gpu(w, elems=50_001, steps=4, bucket_elems=20_000, hp=hp, flow=flow)
     st, oi = run_oracle(w, g, bucket_elems=20_000, hp=hp)
-    assert compare(w, g, st, oi, str(over))["bitwise"]
+    assert compare(w, g, st, oi, f"{over} {flow}")["bitwise"]
