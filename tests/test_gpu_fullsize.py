@@ -76,7 +76,8 @@ def _bits(x: np.ndarray) -> np.ndarray:
     ("tiny", "sync"), ("gpt2_1.5b", "sync"), ("7.5b_bf16", "sync"), ("13b_inf", "sync"),
     ("128b", "sync"), ("c1_7.5b_sgdm", "sync"), ("c2_1.5b_sgd", "sync"),
     # the device-resident flow bench.py times, at full size
-    ("gpt2_1.5b", "device"), ("13b_inf", "device"), ("128b", "device"),
+    ("gpt2_1.5b", "device"), ("7.5b_bf16", "device"), ("13b_inf", "device"), ("128b", "device"),
+    ("c1_7.5b_sgdm", "device"), ("c2_1.5b_sgd", "device"),
 ])
 def test_full_size_sampled(name, flow):
     w = synth.WORKLOADS[name]
