@@ -16,7 +16,8 @@ constexpr int kMaxContrib = 64;
 //   reduce, R < 8:   64 lanes (one wave), 3 runs, 10 workgroups per CU (2 runs
 //                    for buckets too small to fill the chip, where more
 //                    workgroups finish sooner);
-//   reduce, R >= 8:  64 lanes, 1 run, 10 workgroups per CU (6 from R = 16);
+//   reduce, R >= 8:  64 lanes, 1 run, 12 workgroups per CU with 2-byte storage
+//                    and 10 with fp32 (6 from R = 16);
 //   scan (1 stream): 256 lanes, 4 runs, 8 workgroups per CU.
 // (The ZK_* macros exist only to build tuning variants; the defaults are the
 // measured optimum.)
@@ -40,6 +41,9 @@ constexpr int kMaxContrib = 64;
 #endif
 #ifndef ZK_RED_PER_CU_MANY
 #define ZK_RED_PER_CU_MANY 10
+#endif
+#ifndef ZK_RED_PER_CU_MANY_2B
+#define ZK_RED_PER_CU_MANY_2B 12
 #endif
 #ifndef ZK_RED_PER_CU_WIDE
 #define ZK_RED_PER_CU_WIDE 6
@@ -101,7 +105,8 @@ constexpr int64_t kRunsPerBlockMin =
     kMin2(kMin2(kRedBlock * kMin2(kRedRuns, kRedRunsSmall), kRedBlockMany * kRedRunsMany),
           kScanBlock * kScanRuns);
 constexpr int kRedPerCU = ZK_RED_PER_CU;
-constexpr int kRedPerCUMany = ZK_RED_PER_CU_MANY;   // residency when 8 <= R < 16
+constexpr int kRedPerCUMany = ZK_RED_PER_CU_MANY;   // residency when 8 <= R < 16, fp32
+constexpr int kRedPerCUMany2B = ZK_RED_PER_CU_MANY_2B;   // the same, 2-byte storage
 constexpr int kRedPerCUWide = ZK_RED_PER_CU_WIDE;   // residency when R >= 16
 constexpr int kRedWideR = 16;
 // Adam: one wave (64 lanes) per workgroup, each lane one group of 4 elements;

@@ -419,7 +419,8 @@ static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m,
     h->lds_sgd_mom = lds_reserve_for(lds_cu, lds_blk, zk::kSgdMomPerCU);
     h->lds_sgd_plain = lds_reserve_for(lds_cu, lds_blk, zk::kSgdPlainPerCU);
     h->lds_reduce = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCU);
-    h->lds_reduce_many = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCUMany);
+    h->lds_reduce_many = lds_reserve_for(
+        lds_cu, lds_blk, d.lp == ZERO_FP32 ? zk::kRedPerCUMany : zk::kRedPerCUMany2B);
     h->lds_reduce_wide = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCUWide);
     h->lds_scan = lds_reserve_for(lds_cu, lds_blk, zk::kScanPerCU);
     static_assert(sizeof(zk::CheckResult) <= 64 && sizeof(zk::DevState) <= 192, "pinned layout");
