@@ -1,6 +1,8 @@
-"""Build tests/native/abi_example: a C++ program that uses libzeroshard.so
-through its C header with plain HIP memory, streams and the HIP graph API,
-checked against the oracle (test infrastructure, linked in from oracle/)."""
+"""Build the native test programs, C++ users of libzeroshard.so through its C
+header with plain HIP memory, streams and the HIP graph API:
+  abi_example  : every flow checked against the oracle (test infrastructure,
+                 linked in from oracle/);
+  step_latency : microseconds per device-resident step, direct and in graphs."""
 import os
 import shutil
 import subprocess
@@ -9,6 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(os.path.dirname(HERE))
 OUT = os.path.join(HERE, "abi_example")
+LATENCY = os.path.join(HERE, "step_latency")
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
 
@@ -28,6 +31,13 @@ def build(verbose: bool = False) -> str:
         [HIPCC, main_obj, oracle_obj, f"-L{os.path.join(ROOT, 'zero_dp_sharded_amd')}",
          "-lzeroshard", "-lm", "-Wl,-rpath,$ORIGIN/../../zero_dp_sharded_amd", "-o", OUT + ".tmp"],
     ]
+    lat_obj = os.path.join(objdir, "step_latency.o")
+    cmds += [
+        [HIPCC, "-O2", "-std=c++17", "-Wall", f"-I{os.path.join(ROOT, 'include')}", "-c",
+         os.path.join(HERE, "step_latency.cpp"), "-o", lat_obj],
+        [HIPCC, lat_obj, f"-L{os.path.join(ROOT, 'zero_dp_sharded_amd')}", "-lzeroshard",
+         "-Wl,-rpath,$ORIGIN/../../zero_dp_sharded_amd", "-o", LATENCY + ".tmp"],
+    ]
     for cmd in cmds:
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -35,6 +45,7 @@ def build(verbose: bool = False) -> str:
         if r.returncode != 0:
             raise RuntimeError(f"{cmd[0]} failed:\n{r.stderr}")
     os.replace(OUT + ".tmp", OUT)
+    os.replace(LATENCY + ".tmp", LATENCY)
     return OUT
 
 
