@@ -45,7 +45,10 @@ def kernel_code_hash() -> str:
 
 def measured_traffic(workload: str, per_launch_elems: int):
     """HBM bytes per update launch from the committed rocprofv3 counter summary
-    of this workload, if it was taken on the current kernel source; else None."""
+    of this workload, if it was taken on the current kernel source and the
+    in-tree library is the one loaded (not a ZERO_SHARD_LIB variant); else None."""
+    if os.environ.get("ZERO_SHARD_LIB"):
+        return None
     try:
         with open(os.path.join(PROFILES, f"traffic_{workload}.json")) as f:
             t = json.load(f)

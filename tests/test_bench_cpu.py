@@ -53,3 +53,12 @@ def test_kernel_code_hash_ignores_comments_only():
     assert kernel_code_hash([src]) != kernel_code_hash([src.replace("3", "4")])
     assert kernel_code_hash([src, "a"]) != kernel_code_hash([src + "a"])      # file boundaries count
     assert len(kernel_code_hash()) == 16
+
+
+def test_variant_builds_and_traffic_of_variants(monkeypatch):
+    from zero_dp_sharded_amd import build as B
+    with pytest.raises(ValueError):
+        B.build_variant({"NOT_A_SHAPE": 1}, "/nonexistent")      # refused before compiling
+    assert bench.measured_traffic("128b", 2_000_000_000) is not None
+    monkeypatch.setenv("ZERO_SHARD_LIB", "/some/variant/libzeroshard.so")
+    assert bench.measured_traffic("128b", 2_000_000_000) is None  # counters are the in-tree build's

@@ -14,7 +14,8 @@ from dataclasses import dataclass
 from typing import Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libzeroshard.so")
+# ZERO_SHARD_LIB: another build of the library (a tuning variant, see build.py)
+LIB_PATH = os.environ.get("ZERO_SHARD_LIB") or os.path.join(HERE, "libzeroshard.so")
 
 ZERO_OK = 0
 ZERO_ERR_INVALID_ARG = 1

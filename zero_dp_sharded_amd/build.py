@@ -4,6 +4,14 @@ Floating-point flags: no contraction into fused multiply-adds, correctly
 rounded fp32 divide and square root, fp32 denormals kept, and no packed-fp32
 instructions.  hipcc's host pass warns that it does not know the packed-fp32
 feature; the warning is harmless.
+
+    python -m zero_dp_sharded_amd.build [-v]
+    python -m zero_dp_sharded_amd.build --variant OUT_DIR NAME=VALUE ...
+
+The second form builds a tuning variant (the ZK_* shape macros of
+csrc/zero_kernels.h overridden) into OUT_DIR and leaves the in-tree library
+alone; point ZERO_SHARD_LIB at OUT_DIR/libzeroshard.so to run the tests or
+bench.py against it.
 """
 import os
 import shutil
@@ -32,12 +40,12 @@ FLAGS = [
 ]
 
 
-def _compile(sources, objdir, verbose):
+def _compile(sources, objdir, verbose, extra=()):
     objs = []
     for src in sources:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -83,5 +91,25 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_variant(defines: dict, out_dir: str, verbose: bool = False) -> str:
+    """libzeroshard.so with shape macros overridden ({"ZK_RED_PER_CU": 3, ...})
+    into out_dir, for A/B measurements."""
+    for name in defines:
+        if not name.startswith("ZK_"):
+            raise ValueError(f"{name}: only the ZK_* shape macros may be overridden")
+    out_dir = os.path.abspath(out_dir)
+    objdir = os.path.join(out_dir, "obj")
+    os.makedirs(objdir, exist_ok=True)
+    extra = [f"-D{k}={v}" for k, v in defines.items()]
+    lib = os.path.join(out_dir, "libzeroshard.so")
+    _link(_compile(SOURCES, objdir, verbose, extra), lib, verbose)
+    return lib
+
+
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
+    args = [a for a in sys.argv[1:] if a != "-v"]
+    if args and args[0] == "--variant":
+        defs = dict(a.split("=", 1) for a in args[2:])
+        print(build_variant(defs, args[1], verbose="-v" in sys.argv))
+    else:
+        build(verbose="-v" in sys.argv)
