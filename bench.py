@@ -116,7 +116,7 @@ def host_info() -> dict:
     return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0))}
 
 
-def cpu_baseline(w, state_host, contribs_host, bucket_elems):
+def _oracle_setup(w):
     import oracle
     if w.opt == "sgd":
         hp = oracle.SGDHP(lr=w.lr, momentum=w.momentum, weight_decay=w.weight_decay)
@@ -124,13 +124,60 @@ def cpu_baseline(w, state_host, contribs_host, bucket_elems):
         hp = oracle.AdamHP(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                            weight_decay=w.weight_decay)
     ls = oracle.LossScale(init_scale=w.scale, dynamic=w.dynamic)
-    master, m, v = state_host
     lp = {"fp16": oracle.FP16, "bf16": oracle.BF16, "fp32": oracle.FP32}[w.lp]
+    return oracle, hp, ls, lp
+
+
+def cpu_baseline(w, state_host, contribs_host, bucket_elems):
+    """The oracle's step on the whole sample, on one core: (params/s, seconds,
+    the oracle's state after the step)."""
+    oracle, hp, ls, lp = _oracle_setup(w)
+    master, m, v = state_host
     st = oracle.new_state(lp, master, m, v, hp, ls)
     t0 = time.perf_counter()
     oracle.step(st, contribs_host, bucket_elems, hp, ls)
     dt = time.perf_counter() - t0
-    return master.size / dt, dt
+    return master.size / dt, dt, st
+
+
+def cpu_baseline_threads(w, state_host, contribs_host, bucket_elems, threads):
+    """The same oracle step with the sample cut into `threads` contiguous
+    chunks, one thread each (the oracle's C calls release the GIL).  Each chunk
+    is a shard of its own, so the concatenated result equals the one-core
+    result whenever no chunk overflows (no workload here plants an overflow in
+    the timed step).  Returns (params/s, seconds, concatenated master)."""
+    import threading
+
+    import numpy as np
+    oracle, hp, ls, lp = _oracle_setup(w)
+    master, m, v = state_host
+    n = master.size
+    bounds = [n * k // threads for k in range(threads + 1)]
+    parts = [slice(bounds[k], bounds[k + 1]) for k in range(threads) if bounds[k + 1] > bounds[k]]
+    states = [oracle.new_state(lp, master[sl], None if m is None else m[sl],
+                               None if v is None else v[sl], hp, ls) for sl in parts]
+    chunks = [[c[sl] for c in contribs_host] for sl in parts]
+    gate = threading.Barrier(len(parts) + 1)
+    errors = []
+
+    def work(k):
+        gate.wait()
+        try:
+            oracle.step(states[k], chunks[k], bucket_elems, hp, ls)
+        except Exception as e:   # reported after the join
+            errors.append(e)
+
+    pool = [threading.Thread(target=work, args=(k,)) for k in range(len(parts))]
+    for t in pool:
+        t.start()
+    gate.wait()
+    t0 = time.perf_counter()
+    for t in pool:
+        t.join()
+    dt = time.perf_counter() - t0
+    if errors:
+        raise errors[0]
+    return n / dt, dt, np.concatenate([s.master for s in states])
 
 
 def main() -> int:
@@ -329,12 +376,21 @@ def main() -> int:
             contribs_host = [b[:n].cpu().numpy() for b in bufs]
         else:
             contribs_host = [b[:n].view(torch.int16).cpu().numpy().view(np.uint16) for b in bufs]
-        rate, dt = cpu_baseline(w, state_host, contribs_host, cb)
+        rate, dt, st1 = cpu_baseline(w, state_host, contribs_host, cb)
+        threads = min(len(os.sched_getaffinity(0)), 16)
+        prate, pdt, pmaster = cpu_baseline_threads(w, state_host, contribs_host, cb, threads)
         cpu = {"value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
                "sample": f"one full step (reduce of {R} contributions, flag/norm, "
                          f"{'SGD' if sgd else 'Adam'}) on the "
                          f"first {n} elements of the same shard; {dt:.1f} s single-threaded",
-               "host": host_info()}
+               "host": host_info(),
+               "all_cores": {"value": prate, "unit": "params/s", "cores": threads,
+                             "seconds": pdt,
+                             "equals_one_core": bool(np.array_equal(
+                                 pmaster.view(np.uint32), st1.master.view(np.uint32))),
+                             "how": "the same sample in contiguous chunks, one thread per "
+                                    "chunk, each an oracle step of its own"}}
+        del st1, pmaster
         del state_host, contribs_host
     zs.zero_shard_destroy(h)
 

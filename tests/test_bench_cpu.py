@@ -62,3 +62,32 @@ def test_variant_builds_and_traffic_of_variants(monkeypatch):
     assert bench.measured_traffic("128b", 2_000_000_000) is not None
     monkeypatch.setenv("ZERO_SHARD_LIB", "/some/variant/libzeroshard.so")
     assert bench.measured_traffic("128b", 2_000_000_000) is None  # counters are the in-tree build's
+
+
+@pytest.mark.parametrize("wname,threads", [("128b", 3), ("7.5b_bf16", 4), ("c1_7.5b_sgdm", 5),
+                                           ("c2_1.5b_sgd", 2)])
+def test_threaded_oracle_timing_equals_one_core(wname, threads):
+    """The all-cores CPU baseline runs the oracle on contiguous chunks of the
+    sample; with no overflow that is the one-core step, bitwise."""
+    import numpy as np
+    w = synth.WORKLOADS[wname]
+    n, cb = 40_003, 8_192
+    rng = np.random.default_rng(5)
+    master = rng.normal(0, 0.02, n).astype(np.float32)
+    m = rng.normal(0, 1e-4, n).astype(np.float32) if w.has_m else None
+    v = np.abs(rng.normal(0, 1e-8, n)).astype(np.float32) if w.has_v else None
+    R = w.R
+    g = rng.normal(0, 1e-3, (R, n)) * w.scale
+    if w.lp == "fp32":
+        contribs = [row.astype(np.float32) for row in g]
+    elif w.lp == "fp16":
+        contribs = [row.astype(np.float16).view(np.uint16) for row in g]
+    else:
+        import torch
+        contribs = [torch.from_numpy(row.astype(np.float32)).to(torch.bfloat16)
+                    .view(torch.int16).numpy().view(np.uint16) for row in g]
+    rate, dt, st = bench.cpu_baseline(w, (master, m, v), contribs, cb)
+    prate, pdt, pmaster = bench.cpu_baseline_threads(w, (master, m, v), contribs, cb, threads)
+    assert rate > 0 and prate > 0
+    assert np.array_equal(pmaster.view(np.uint32), st.master.view(np.uint32))
+    assert not np.array_equal(st.master, master)                 # the step did update

@@ -40,3 +40,5 @@ def test_bench_json_line():
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["cores"] >= 1 and c["value"] > 0
     assert isinstance(c["unit"], str) and isinstance(c["sample"], str)
+    a = c["all_cores"]
+    assert a["cores"] >= 1 and a["value"] > 0 and a["equals_one_core"] is True
