@@ -394,6 +394,11 @@ zero_status zero_step_resolve(zero_shard_t h, zero_step_info* out);
  *   - the update (Adam or SGD with the init hyper-parameters), which reads
  *     the decision and the step's scalars from device memory and writes
  *     nothing on a skipped step.
+ * When the step has at most 256 per-workgroup partials and the update covers
+ * the shard in one vector launch (every array 16-byte aligned, S a multiple of
+ * 4), the update itself folds the partials in the same fixed order and takes
+ * the same decision, and its last workgroup advances the counters: one launch
+ * fewer, bitwise the same results (see zero_shard_inline_folds).
  * Because every launch argument is fixed for fixed contribution pointers,
  * the enqueue of zero_step_device may be captured in a HIP graph and
  * replayed; each replay is one step.  The loss scale the next step's
@@ -410,6 +415,11 @@ zero_status zero_device_begin(zero_shard_t h, void* stream);
 zero_status zero_step_device(zero_shard_t h, const void* const* contribs, int32_t n_contrib,
                              void* stream);
 zero_status zero_device_end(zero_shard_t h, void* stream, zero_step_info* out);
+
+/* Diagnostic: *count = the zero_step_device calls on this handle, since init,
+ * that enqueued the fold inside the update instead of a fold launch.
+ * Errors: STATE (dead handle), INVALID_ARG (count NULL). */
+zero_status zero_shard_inline_folds(zero_shard_t h, int64_t* count);
 
 /* Step counter, current loss scale and clean-step count (for checkpoints).
  * STATE while the device-resident flow is active (the values live on the

@@ -89,7 +89,7 @@ def run_gpu(w: synth.Workload, *, elems: Optional[int] = None, steps: Optional[i
             seed: int = 0, bucket_elems: Optional[int] = None, hp=None,
             ls: Optional[zs.LossScaleCfg] = None, keep_contribs: bool = True,
             offsets: Optional[dict] = None, hook=None, flow: str = "sync",
-            max_norm: float = 0.0, scale_of=None) -> GpuRun:
+            max_norm: float = 0.0, scale_of=None, inline_folds: Optional[list] = None) -> GpuRun:
     """Run `steps` owner-rank steps of workload w (its first `elems` shard
     elements) through the C ABI on cuda:0.  offsets maps an array name
     ('master', 'm', 'v', 'grad', 'param', 'contrib') to an element offset of its
@@ -100,7 +100,9 @@ def run_gpu(w: synth.Workload, *, elems: Optional[int] = None, steps: Optional[i
     zero_device_begin and zero_device_end (ended after every step to read its
     result), "device_run" the same without ending between steps (only the last
     step's result is read; the others are None).  The workload's opt picks Adam
-    or SGD; max_norm > 0 turns on global-norm clipping."""
+    or SGD; max_norm > 0 turns on global-norm clipping.  inline_folds, when
+    given, receives the handle's count of device steps whose update folded the
+    partials itself."""
     dev = torch.device("cuda", 0)
     S = w.shard if elems is None else elems
     steps = w.steps if steps is None else steps
@@ -186,6 +188,8 @@ def run_gpu(w: synth.Workload, *, elems: Optional[int] = None, steps: Optional[i
             infos.append(info)
             scale = info.scale_next
         torch.cuda.synchronize()
+        if inline_folds is not None:
+            inline_folds.append(zs.zero_shard_inline_folds(h))
     finally:
         zs.zero_shard_destroy(h)
     opt = lambda t: None if t is None else f32(t)

@@ -36,7 +36,7 @@ ABI_SYMBOLS = (
     "zero_bucket_reduce", "zero_overflow_check", "zero_overflow_merge", "zero_adam_step",
     "zero_adam_step_gated", "zero_sgd_step", "zero_sgd_step_gated", "zero_step_resolve",
     "zero_shard_set_clip", "zero_device_begin", "zero_step_device", "zero_device_end",
-    "zero_shard_get_counters",
+    "zero_shard_inline_folds", "zero_shard_get_counters",
     "zero_shard_set_counters", "zero_shard_destroy", "zero_status_str", "zero_last_error",
     "zero_abi_version",
 )
@@ -121,6 +121,7 @@ def lib() -> ctypes.CDLL:
         L.zero_device_begin.argtypes = [_vp, _vp]
         L.zero_step_device.argtypes = [_vp, ctypes.POINTER(_vp), _i32, _vp]
         L.zero_device_end.argtypes = [_vp, _vp, ctypes.POINTER(ZeroStepInfo)]
+        L.zero_shard_inline_folds.argtypes = [_vp, ctypes.POINTER(_i64)]
         L.zero_shard_get_counters.argtypes = [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_f64),
                                               ctypes.POINTER(_i64)]
         L.zero_shard_set_counters.argtypes = [_vp, _i64, _f64, _i64]
@@ -394,6 +395,14 @@ def zero_step_device(h: int, contribs: Optional[Sequence] = None, stream=None) -
     else:
         arr, n = (_vp * len(contribs))(*[_dptr(c) for c in contribs]), len(contribs)
     _check(lib().zero_step_device(h, arr, n, _stream_ptr(stream)), "zero_step_device")
+
+
+def zero_shard_inline_folds(h: int) -> int:
+    """Device-resident steps of this handle whose update folded the partials
+    itself (no fold launch)."""
+    n = _i64()
+    _check(lib().zero_shard_inline_folds(h, ctypes.byref(n)), "zero_shard_inline_folds")
+    return n.value
 
 
 def zero_device_end(h: int, stream=None) -> StepInfo:

@@ -201,6 +201,7 @@ struct ReduceLaunch {
     int64_t slot_base;
     uint32_t lds_reserve;  // dynamic LDS that caps workgroups per CU
     const DevState* dev;
+    DevState* snapshot;    // set: workgroup 0 copies *dev there (see InlineFold)
 };
 
 // Stand-alone check of a stored gradient shard (no reduce this step).
@@ -216,17 +217,41 @@ struct ScanLaunch {
     int64_t slot_base;
     uint32_t lds_reserve;
     const DevState* dev;
+    DevState* snapshot;
+};
+
+// The fold inside the update, for a device-resident step with few partials:
+// every update workgroup sums the partials itself, in the fold kernel's order
+// (so bitwise its sum), and takes the clipping coefficient and the decision
+// from that sum and the step's starting state exactly as the fold's last lane
+// would.  It reads that state from `snapshot`, the copy the step's reduce (or
+// scan) launches made of `dev`, so workgroup 0 can write the advanced state to
+// `dev` (and the check result) while the others still read: no counter, no
+// atomics.  This saves the fold's launch on launch-bound shards.  The update
+// must run as one vector launch with no element-wise part.
+constexpr int kInlineFoldMax = 256;
+struct InlineFold {
+    const double* partial;     // nullptr: off
+    int32_t n;                 // partials, at most kInlineFoldMax
+    int32_t pad;
+    const DevState* snapshot;
+    DevState* dev;
+    CheckResult* res;
+    double max_norm;
+    PrepareArgs pa;
 };
 
 // Where an update takes its per-step values.  Host flows pass inv_scale (and
 // the bias corrections) as arguments; res, when set, supplies the clipping
 // coefficient (else `clip`), and with gate = 1 its NaN sum skips the update;
-// dev, when set, supplies inv_scale, the bias corrections and the skip.
+// dev, when set, supplies inv_scale, the bias corrections and the skip; fold,
+// when set, replaces the fold kernel (see InlineFold).
 struct StepSource {
     const CheckResult* res;
     const DevState* dev;
     int32_t gate;
     float clip;
+    InlineFold fold;
 };
 
 enum WdKind { kWdNone = 0, kWdDecoupled = 1, kWdL2 = 2 };
@@ -291,6 +316,13 @@ hipError_t launch_finalize(const double* partial, int64_t nslots, double* level1
                            const PrepareArgs& pa, hipStream_t s);
 // Device-resident flow: write the state.
 hipError_t launch_load_state(DevState* d, const DevState& init, hipStream_t s);
+// Whether an update of ngroups groups of 4 with `lanes` lanes and `groups`
+// groups per lane runs as one launch (the inline fold needs that).
+inline bool one_launch(int64_t ngroups, int lanes, int groups)
+{
+    const int64_t blocks = (ngroups + (int64_t)lanes * groups - 1) / ((int64_t)lanes * groups);
+    return blocks * lanes <= kMaxLaunchItems;
+}
 hipError_t launch_adam(const AdamLaunch& a, hipStream_t s);
 hipError_t launch_sgd(const SgdLaunch& a, hipStream_t s);
 

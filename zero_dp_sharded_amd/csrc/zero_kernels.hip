@@ -230,6 +230,14 @@ __device__ __forceinline__ void reduce_s(const ReduceLaunch& L, int64_t e, float
     check_s<LP>(o, inv_scale, flag, ss);
 }
 
+// Device-resident steps: workgroup 0 of each reduce or scan launch copies the
+// step's starting state for an inline-fold update (see InlineFold; the copies
+// are identical, and nothing reads the snapshot before the update).
+__device__ __forceinline__ void snapshot_state(const DevState* dev, DevState* snap)
+{
+    if (snap != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *snap = *dev;
+}
+
 // The unscale factor of a check: the launch argument, or the device state's.
 __device__ __forceinline__ float check_inv_scale(float arg, const DevState* dev)
 {
@@ -240,7 +248,7 @@ __device__ __forceinline__ float check_inv_scale(float arg, const DevState* dev)
 // U runs per lane; lane l owns runs b*BS*U + u*BS + l.  Element offsets past `head`
 // are multiples of W, so contribution and output pointers advanced by `head`
 // are 16-byte aligned and are indexed in units of runs.
-template <int LP, int RT, int U, int BS>
+template <int LP, int RT, int U, int BS, int SNAP>
 __global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
 {
     using VW = typename Fmt<LP>::VW;
@@ -296,6 +304,7 @@ __global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
             reduce_finish<LP>(L, vi, acc, inv_scale, flag, ss);
         }
     }
+    if constexpr (SNAP) snapshot_state(L.dev, L.snapshot);
     block_partial<BS>(L.partial + L.slot_base + blockIdx.x, flag, ss);
 }
 
@@ -312,10 +321,11 @@ __global__ __launch_bounds__(kScalarBlock) void reduce_elem_kernel(ReduceLaunch 
         const int64_t k = (int64_t)blockIdx.x * kScalarElemsPerBlock + j * kScalarBlock + threadIdx.x;
         if (k < cnt) reduce_s<LP>(L, rg.at(k), inv_scale, flag, ss);
     }
+    snapshot_state(L.dev, L.snapshot);
     block_partial<kScalarBlock>(L.partial + slot + blockIdx.x, flag, ss);
 }
 
-template <int LP>
+template <int LP, int SNAP>
 __global__ __launch_bounds__(kScanBlock) void scan_vec_kernel(ScanLaunch L)
 {
     using VW = typename Fmt<LP>::VW;
@@ -332,6 +342,7 @@ __global__ __launch_bounds__(kScanBlock) void scan_vec_kernel(ScanLaunch L)
 #pragma unroll
     for (int u = 0; u < kScanRuns; ++u)
         if (v0 + u * kScanBlock < L.nvec) check_v<LP>(x[u], inv_scale, flag, ss);
+    if constexpr (SNAP) snapshot_state(L.dev, L.snapshot);
     block_partial<kScanBlock>(L.partial + L.slot_base + blockIdx.x, flag, ss);
 }
 
@@ -348,6 +359,7 @@ __global__ __launch_bounds__(kScalarBlock) void scan_elem_kernel(ScanLaunch L, R
         const int64_t k = (int64_t)blockIdx.x * kScalarElemsPerBlock + j * kScalarBlock + threadIdx.x;
         if (k < cnt) check_s<LP>(static_cast<const T*>(L.g)[rg.at(k)], inv_scale, flag, ss);
     }
+    snapshot_state(L.dev, L.snapshot);
     block_partial<kScalarBlock>(L.partial + slot + blockIdx.x, flag, ss);
 }
 
@@ -390,6 +402,19 @@ __device__ void prepare_step(DevState* d, double ss, const PrepareArgs& a)
     *d = s;
 }
 
+// Textbook global-norm clipping coefficient min(1, max_norm / (norm + 1e-6)),
+// in fp64 and rounded to fp32; 1 when clipping is off, and for a NaN sum
+// (overflow), which fails the comparison.
+__device__ __forceinline__ float clip_coef(double sumsq, double max_norm)
+{
+    float coef = 1.0f;
+    if (max_norm > 0.0) {
+        const double c = max_norm / (sqrt(sumsq) + 1e-6);
+        if (c < 1.0) coef = (float)c;
+    }
+    return coef;
+}
+
 // Workgroup b sums in[b*chunk, min(n, (b+1)*chunk)) with a fixed shape into
 // out[b]; the last level (res set, one workgroup) writes the check result and
 // the clipping coefficient instead, and with dev set also decides the step.
@@ -414,15 +439,8 @@ __global__ __launch_bounds__(kFoldBlock) void fold_kernel(const double* in, int6
         if (res == nullptr) {
             out[blockIdx.x] = t;
         } else {
-            // textbook global-norm clipping: min(1, max_norm / (norm + 1e-6)) in
-            // fp64; a NaN sum (overflow) fails the comparison and gives 1
-            float coef = 1.0f;
-            if (max_norm > 0.0) {
-                const double c = max_norm / (sqrt(t) + 1e-6);
-                if (c < 1.0) coef = (float)c;
-            }
             res->sumsq = t;
-            res->clip = coef;
+            res->clip = clip_coef(t, max_norm);
             res->pad = 0.0f;
             if (dev != nullptr) prepare_step(dev, t, pa);
         }
@@ -459,6 +477,59 @@ __device__ __forceinline__ StepVals step_vals(const StepSource& src, float inv_s
     return v;
 }
 
+// The inline fold (InlineFold): the one-workgroup fold of at most 256
+// partials, reproduced by one wave.  Lane l stands for the fold's lanes l,
+// l+64, l+128 and l+192, each of which holds at most one partial (0.0 + p);
+// the four 64-lane butterflies are the fold's four waves, and their totals add
+// in wave order, so the sum is bitwise the fold kernel's.  Every lane ends
+// with the same value.
+__device__ __forceinline__ double fold_small(const double* p, int n)
+{
+    double w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = (int)(threadIdx.x & 63) + 64 * k;   // every wave sums them all
+        double s = 0.0;
+        if (i < n) s += p[i];
+        w[k] = s;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] += __shfl_xor(w[k], off, 64);
+    }
+    return ((w[0] + w[1]) + w[2]) + w[3];
+}
+
+// The step as the fold's last lane decides it, computed by every workgroup
+// from the snapshot of the state the step started with.
+struct InlineDecision {
+    DevState next;
+    double sumsq;
+    float clip;
+};
+
+__device__ __forceinline__ StepVals step_vals_inline(const InlineFold& f, InlineDecision& d)
+{
+    d.sumsq = fold_small(f.partial, f.n);
+    d.next = *f.snapshot;
+    prepare_step(&d.next, d.sumsq, f.pa);
+    d.clip = clip_coef(d.sumsq, f.max_norm);
+    return StepVals{d.next.upd_inv_scale, d.next.bc1, d.next.bc2, d.clip, d.next.skip != 0};
+}
+
+// Workgroup 0 writes the advanced state and the check result; no workgroup of
+// the update reads either.
+__device__ __forceinline__ void inline_commit(const InlineFold& f, const InlineDecision& d)
+{
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *f.dev = d.next;
+        f.res->sumsq = d.sumsq;
+        f.res->clip = d.clip;
+        f.res->pad = 0.0f;
+    }
+}
+
 // ----------------------------------------------------------------- Adam
 
 // Textbook Adam on one element (Kingma & Ba 2015, Algorithm 1), in the order
@@ -484,7 +555,8 @@ __device__ __forceinline__ void adam_e(float graw, float& p, float& m, float& v,
 // covers groups [b*B*G, (b+1)*B*G) for B lanes and G groups per lane; lane l
 // owns groups b*B*G + u*B + l, u < G, and issues all loads before any
 // arithmetic.  With fp32 storage there is no 2-byte parameter to write.
-template <int LP, int WD>
+// INL = 1: the step's values come from the inline fold (a.src.fold).
+template <int LP, int WD, int INL>
 __global__ __launch_bounds__(kAdamBlock) void adam_vec_kernel(AdamLaunch a)
 {
     using V4 = typename Fmt<LP>::V4;
@@ -505,12 +577,18 @@ __global__ __launch_bounds__(kAdamBlock) void adam_vec_kernel(AdamLaunch a)
             v[u] = ld_nt<f4>(vb, q);
         }
     }
-    const StepVals sv = step_vals(a.src, a.inv_scale, a.bc1, a.bc2);
-    if (sv.skip) return;
+    StepVals sv;
+    InlineDecision dec;
+    if constexpr (INL) {
+        sv = step_vals_inline(a.src.fold, dec);
+    } else {
+        sv = step_vals(a.src, a.inv_scale, a.bc1, a.bc2);
+        if (sv.skip) return;
+    }
 #pragma unroll
     for (int u = 0; u < kAdamGroups; ++u) {
         const int64_t q = q0 + u * kAdamBlock;
-        if (q < a.ngroups) {
+        if (q < a.ngroups && !(INL && sv.skip)) {
             const f4 gf = __builtin_convertvector(g[u], f4);
             f4 pp = p[u], mm = m[u], vv = v[u];
 #pragma unroll
@@ -528,6 +606,7 @@ __global__ __launch_bounds__(kAdamBlock) void adam_vec_kernel(AdamLaunch a)
                 st_nt<V4>(adv<LP>(a.param, a.head), q, __builtin_convertvector(pp, V4));
         }
     }
+    if constexpr (INL) inline_commit(a.src.fold, dec);
 }
 
 template <int LP, int WD>
@@ -570,8 +649,9 @@ __device__ __forceinline__ void sgd_e(float graw, float& p, float& b, const SgdL
     p = p - a.lr * d;
 }
 
-// Same layout and load-first order as adam_vec_kernel, with G groups per lane.
-template <int LP, int MOM, int WD, int G>
+// Same layout and load-first order as adam_vec_kernel, with G groups per lane;
+// INL as there.
+template <int LP, int MOM, int WD, int G, int INL>
 __global__ __launch_bounds__(kSgdBlock) void sgd_vec_kernel(SgdLaunch a)
 {
     using V4 = typename Fmt<LP>::V4;
@@ -590,12 +670,18 @@ __global__ __launch_bounds__(kSgdBlock) void sgd_vec_kernel(SgdLaunch a)
             if constexpr (MOM) b[u] = ld_nt<f4>(bb, q);
         }
     }
-    const StepVals sv = step_vals(a.src, a.inv_scale, 1.0f, 1.0f);
-    if (sv.skip) return;
+    StepVals sv;
+    InlineDecision dec;
+    if constexpr (INL) {
+        sv = step_vals_inline(a.src.fold, dec);
+    } else {
+        sv = step_vals(a.src, a.inv_scale, 1.0f, 1.0f);
+        if (sv.skip) return;
+    }
 #pragma unroll
     for (int u = 0; u < G; ++u) {
         const int64_t q = q0 + u * kSgdBlock;
-        if (q < a.ngroups) {
+        if (q < a.ngroups && !(INL && sv.skip)) {
             const f4 gf = __builtin_convertvector(g[u], f4);
             f4 pp = p[u];
             f4 buf = (f4)(0.f);
@@ -613,6 +699,7 @@ __global__ __launch_bounds__(kSgdBlock) void sgd_vec_kernel(SgdLaunch a)
                 st_nt<V4>(adv<LP>(a.param, a.head), q, __builtin_convertvector(pp, V4));
         }
     }
+    if constexpr (INL) inline_commit(a.src.fold, dec);
 }
 
 template <int LP, int MOM, int WD>
@@ -662,10 +749,15 @@ Ranges ranges_of(int64_t n, int64_t head, int64_t body, int32_t vec_ok)
     return rg;
 }
 
+// SNAP = 1 (a snapshot target is set) only for the small steps of the inline
+// fold, so the reduce of every other step keeps the plain kernel.
 template <int LP, int RT, int U, int BS>
 void reduce_vec_go(const ReduceLaunch& L, unsigned grid, hipStream_t s)
 {
-    reduce_vec_kernel<LP, RT, U, BS><<<grid, BS, L.lds_reserve, s>>>(L);
+    if (L.snapshot != nullptr)
+        reduce_vec_kernel<LP, RT, U, BS, 1><<<grid, BS, L.lds_reserve, s>>>(L);
+    else
+        reduce_vec_kernel<LP, RT, U, BS, 0><<<grid, BS, L.lds_reserve, s>>>(L);
 }
 
 // Below 8 contributions the workgroup has kRedBlock lanes and the runs per
@@ -741,7 +833,10 @@ hipError_t scan_dispatch(const ScanLaunch& L, hipStream_t s)
         part.head = L.head + W * runs_per_block * b0;
         part.nvec = L.nvec - runs_per_block * b0;
         part.slot_base = L.slot_base + b0;
-        scan_vec_kernel<LP><<<(unsigned)nb, kScanBlock, L.lds_reserve, s>>>(part);
+        if (L.snapshot != nullptr)
+            scan_vec_kernel<LP, 1><<<(unsigned)nb, kScanBlock, L.lds_reserve, s>>>(part);
+        else
+            scan_vec_kernel<LP, 0><<<(unsigned)nb, kScanBlock, L.lds_reserve, s>>>(part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -757,13 +852,22 @@ hipError_t adam_dispatch(const AdamLaunch& a, hipStream_t s)
 {
     const int64_t groups_per_block = (int64_t)kAdamBlock * kAdamGroups;
     const int64_t vblocks = a.vec_ok ? ceil_div(a.ngroups, groups_per_block) : 0;
+    if (a.src.fold.partial != nullptr) {
+        // the inline fold: one vector launch over the whole array
+        if (!a.vec_ok || a.head != 0 || 4 * a.ngroups != a.n || vblocks < 1 ||
+            !one_launch(a.ngroups, kAdamBlock, kAdamGroups) || a.src.fold.n < 1 ||
+            a.src.fold.n > kInlineFoldMax)
+            return hipErrorInvalidValue;
+        adam_vec_kernel<LP, WD, 1><<<(unsigned)vblocks, kAdamBlock, a.lds_reserve, s>>>(a);
+        return hipGetLastError();
+    }
     const int64_t max_blocks = kMaxLaunchItems / kAdamBlock;
     for (int64_t b0 = 0; b0 < vblocks; b0 += max_blocks) {
         const int64_t nb = vblocks - b0 < max_blocks ? vblocks - b0 : max_blocks;
         AdamLaunch part = a;
         part.head = a.head + 4 * groups_per_block * b0;
         part.ngroups = a.ngroups - groups_per_block * b0;
-        adam_vec_kernel<LP, WD><<<(unsigned)nb, kAdamBlock, a.lds_reserve, s>>>(part);
+        adam_vec_kernel<LP, WD, 0><<<(unsigned)nb, kAdamBlock, a.lds_reserve, s>>>(part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -789,13 +893,21 @@ hipError_t sgd_dispatch(const SgdLaunch& a, hipStream_t s)
     constexpr int G = MOM ? kSgdMomGroups : kSgdPlainGroups;
     const int64_t groups_per_block = (int64_t)kSgdBlock * G;
     const int64_t vblocks = a.vec_ok ? ceil_div(a.ngroups, groups_per_block) : 0;
+    if (a.src.fold.partial != nullptr) {
+        if (!a.vec_ok || a.head != 0 || 4 * a.ngroups != a.n || vblocks < 1 ||
+            !one_launch(a.ngroups, kSgdBlock, G) || a.src.fold.n < 1 ||
+            a.src.fold.n > kInlineFoldMax)
+            return hipErrorInvalidValue;
+        sgd_vec_kernel<LP, MOM, WD, G, 1><<<(unsigned)vblocks, kSgdBlock, a.lds_reserve, s>>>(a);
+        return hipGetLastError();
+    }
     const int64_t max_blocks = kMaxLaunchItems / kSgdBlock;
     for (int64_t b0 = 0; b0 < vblocks; b0 += max_blocks) {
         const int64_t nb = vblocks - b0 < max_blocks ? vblocks - b0 : max_blocks;
         SgdLaunch part = a;
         part.head = a.head + 4 * groups_per_block * b0;
         part.ngroups = a.ngroups - groups_per_block * b0;
-        sgd_vec_kernel<LP, MOM, WD, G><<<(unsigned)nb, kSgdBlock, a.lds_reserve, s>>>(part);
+        sgd_vec_kernel<LP, MOM, WD, G, 0><<<(unsigned)nb, kSgdBlock, a.lds_reserve, s>>>(part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

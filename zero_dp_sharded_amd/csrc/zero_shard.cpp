@@ -90,6 +90,10 @@ struct zero_shard_s {
     zk::DevState* dev = nullptr;
     zk::DevState* host_dev = nullptr;
     bool device_mode = false;
+    // the step's starting state as the reduce copies it for an inline-fold
+    // update (device memory), and the device steps enqueued with that fold
+    zk::DevState* dev_snapshot = nullptr;
+    int64_t inline_folds = 0;
     // the contribution set zero_step_device last validated
     const void* dev_checked[ZERO_MAX_CONTRIB] = {};
     int32_t dev_checked_n = 0;
@@ -394,7 +398,7 @@ static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m,
     h->nslots = nslots;
 
     const size_t ws_bytes = sizeof(double) * (size_t)(nslots + zk::kFoldMaxBlocks) +
-                            sizeof(zk::CheckResult) + sizeof(zk::DevState);
+                            sizeof(zk::CheckResult) + 2 * sizeof(zk::DevState);
     e = hipMalloc(&h->ws, ws_bytes);
     if (e != hipSuccess) {
         delete h;
@@ -406,6 +410,7 @@ static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m,
     h->level1 = h->partial + nslots;
     h->result = reinterpret_cast<zk::CheckResult*>(h->level1 + zk::kFoldMaxBlocks);
     h->dev = reinterpret_cast<zk::DevState*>(h->result + 1);
+    h->dev_snapshot = h->dev + 1;
 
     int lds_cu = 0, lds_blk = 0;
     if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
@@ -498,11 +503,14 @@ static zero_status check_contrib_overlap(const zero_shard_s* h, const void* cons
 
 // Launch the reduce of the bucket [off, off + len) of the shard from the
 // contributions' bucket pointers, writing partial slots from slot_base on;
-// dev set: the unscale factor comes from the device state.
+// dev set: the unscale factor comes from the device state; snapshot set: the
+// launch also copies the device state there (inline-fold steps).  With
+// launch = false only *blocks_out (the partial slots it would write) is set.
 static zero_status enqueue_reduce(zero_shard_s* h, const void* const* ptrs, int32_t n_contrib,
                                   int64_t off, int64_t len, int64_t slot_base,
                                   const zk::DevState* dev, hipStream_t s, int64_t* blocks_out,
-                                  const char* who)
+                                  const char* who, zk::DevState* snapshot = nullptr,
+                                  bool launch = true)
 {
     zk::ReduceLaunch L;
     std::memset(&L, 0, sizeof(L));
@@ -532,10 +540,15 @@ static zero_status enqueue_reduce(zero_shard_s* h, const void* const* ptrs, int3
                     : n_contrib >= zk::kRedManyR ? h->lds_reduce_many
                                                  : h->lds_reduce;
     L.dev = dev;
+    L.snapshot = snapshot;
     const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::red_runs(L.R, L.nvec),
                                              zk::red_block(L.R));
     if (L.slot_base + blocks > h->nslots)
         return fail(ZERO_ERR_UNSUPPORTED, "%s: partial slots exhausted", who);
+    if (!launch) {
+        *blocks_out = blocks;
+        return ZERO_OK;
+    }
     hipError_t e = zk::launch_reduce(L, s);
     if (e != hipSuccess) return hip_fail(e, who);
     *blocks_out = blocks;
@@ -644,9 +657,11 @@ zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int3
 }  // extern "C"
 
 // Launch the stand-alone scan of the stored grad_shard (no bucket reduced this
-// step) into partial slots from 0; returns the slots written.
+// step) into partial slots from 0; returns the slots written.  snapshot and
+// launch as for enqueue_reduce.
 static zero_status enqueue_scan(zero_shard_s* h, const zk::DevState* dev, hipStream_t s,
-                                int64_t* slots, const char* who)
+                                int64_t* slots, const char* who,
+                                zk::DevState* snapshot = nullptr, bool launch = true)
 {
     zk::ScanLaunch L;
     std::memset(&L, 0, sizeof(L));
@@ -662,9 +677,11 @@ static zero_status enqueue_scan(zero_shard_s* h, const zk::DevState* dev, hipStr
     L.slot_base = 0;
     L.lds_reserve = h->lds_scan;
     L.dev = dev;
+    L.snapshot = snapshot;
+    *slots = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::kScanRuns, zk::kScanBlock);
+    if (!launch) return ZERO_OK;
     hipError_t e = zk::launch_scan(L, s);
     if (e != hipSuccess) return hip_fail(e, who);
-    *slots = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::kScanRuns, zk::kScanBlock);
     return ZERO_OK;
 }
 
@@ -735,6 +752,41 @@ static zk::StepSource source_device(const zero_shard_s* h)
     return src;
 }
 
+// Layout of the update over the shard: groups of 4 elements, 16-byte aligned
+// in the fp32 arrays and 4*esz in the stored ones, after a common scalar head
+// (see split); the arrays present are those of the handle's optimizer.
+static void update_layout(const zero_shard_s* h, int64_t* head, int64_t* ngroups, int32_t* vec_ok)
+{
+    uintptr_t addr[5];
+    int elt[5], align[5], cnt = 0;
+    const void* arr[5] = {h->d.master, h->d.exp_avg, h->opt == kOptAdam ? h->d.exp_avg_sq : nullptr,
+                          h->d.grad_shard, h->d.param_shard};
+    const int el[5] = {4, 4, 4, h->esz, h->esz};
+    for (int k = 0; k < 5; ++k) {
+        if (!arr[k]) continue;
+        addr[cnt] = (uintptr_t)arr[k];
+        elt[cnt] = el[k];
+        align[cnt] = 4 * el[k];
+        ++cnt;
+    }
+    split(h->S, common_head(addr, elt, align, cnt), 4, head, ngroups, vec_ok);
+}
+
+// Whether a device-resident step with `slots` partials folds them inside the
+// update: few enough partials, and an update that is one vector launch over
+// the whole shard (no element-wise head or tail).
+static bool inline_fold_ok(const zero_shard_s* h, int64_t slots)
+{
+    if (slots < 1 || slots > zk::kInlineFoldMax) return false;
+    int64_t head, ngroups;
+    int32_t vec_ok;
+    update_layout(h, &head, &ngroups, &vec_ok);
+    if (!vec_ok || head != 0 || 4 * ngroups != h->S) return false;
+    if (h->opt == kOptAdam) return zk::one_launch(ngroups, zk::kAdamBlock, zk::kAdamGroups);
+    return zk::one_launch(ngroups, zk::kSgdBlock,
+                          h->d.exp_avg ? zk::kSgdMomGroups : zk::kSgdPlainGroups);
+}
+
 // Launch Adam for applied step t = h->t + 1 with hyper-parameters hp; src says
 // where the kernels take the per-step values (see source_*).
 // Returns the fp64 powers beta^t it used and whether they extend the cache.
@@ -763,12 +815,7 @@ static zero_status launch_adam_step(zero_shard_s* h, const zero_adam_hparams& hp
     a.v = h->d.exp_avg_sq;
     a.param = h->d.param_shard;
     a.n = h->S;
-    // groups of 4: 16-byte aligned in the fp32 arrays, 4*esz in the stored ones
-    const uintptr_t addr[5] = {(uintptr_t)a.master, (uintptr_t)a.m, (uintptr_t)a.v,
-                               (uintptr_t)a.grad, (uintptr_t)a.param};
-    const int elt[5] = {4, 4, 4, h->esz, h->esz};
-    const int align[5] = {16, 16, 16, 4 * h->esz, 4 * h->esz};
-    split(h->S, common_head(addr, elt, align, a.param ? 5 : 4), 4, &a.head, &a.ngroups, &a.vec_ok);
+    update_layout(h, &a.head, &a.ngroups, &a.vec_ok);
     a.lds_reserve = h->lds_adam;
     a.lp = (int32_t)h->d.lp;
     a.b1 = (float)hp.beta1;
@@ -804,18 +851,7 @@ static zero_status launch_sgd_step(zero_shard_s* h, const zero_sgd_hparams& hp, 
     a.mom = h->d.exp_avg;
     a.param = h->d.param_shard;
     a.n = h->S;
-    uintptr_t addr[4];
-    int elt[4], align[4], cnt = 0;
-    const void* arr[4] = {a.master, a.mom, a.grad, a.param};
-    const int el[4] = {4, 4, h->esz, h->esz};
-    for (int k = 0; k < 4; ++k) {
-        if (!arr[k]) continue;
-        addr[cnt] = (uintptr_t)arr[k];
-        elt[cnt] = el[k];
-        align[cnt] = 4 * el[k];
-        ++cnt;
-    }
-    split(h->S, common_head(addr, elt, align, cnt), 4, &a.head, &a.ngroups, &a.vec_ok);
+    update_layout(h, &a.head, &a.ngroups, &a.vec_ok);
     a.lds_reserve = a.mom ? h->lds_sgd_mom : h->lds_sgd_plain;
     a.lp = (int32_t)h->d.lp;
     a.lr = (float)hp.lr;
@@ -1127,23 +1163,30 @@ zero_status zero_step_device(zero_shard_t h, const void* const* contribs, int32_
         }
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    int64_t slots = 0;
-    if (scan) {
-        zero_status st = enqueue_scan(h, h->dev, s, &slots, "step_device: scan");
-        if (st != ZERO_OK) return st;
-    } else {
+    // the reduce (or scan) launches: first counted, so that a step with few
+    // partials can snapshot the state for an update that folds them itself
+    auto enqueue_check = [&](bool launch, zk::DevState* snapshot, int64_t* slots) -> zero_status {
+        *slots = 0;
+        if (scan) return enqueue_scan(h, h->dev, s, slots, "step_device: scan", snapshot, launch);
         const void* ptrs[ZERO_MAX_CONTRIB];
         for (int64_t off = 0; off < h->S; off += h->d.bucket_elems) {
             const int64_t len = h->S - off < h->d.bucket_elems ? h->S - off : h->d.bucket_elems;
             for (int r = 0; r < n_contrib; ++r)
                 ptrs[r] = static_cast<const char*>(contribs[r]) + off * h->esz;
             int64_t blocks = 0;
-            zero_status st = enqueue_reduce(h, ptrs, n_contrib, off, len, slots, h->dev, s, &blocks,
-                                            "step_device: reduce");
+            zero_status st = enqueue_reduce(h, ptrs, n_contrib, off, len, *slots, h->dev, s,
+                                            &blocks, "step_device: reduce", snapshot, launch);
             if (st != ZERO_OK) return st;
-            slots += blocks;
+            *slots += blocks;
         }
-    }
+        return ZERO_OK;
+    };
+    int64_t slots = 0;
+    zero_status cst = enqueue_check(false, nullptr, &slots);
+    if (cst != ZERO_OK) return cst;
+    const bool fold_inline = inline_fold_ok(h, slots);
+    cst = enqueue_check(true, fold_inline ? h->dev_snapshot : nullptr, &slots);
+    if (cst != ZERO_OK) return cst;
     zk::PrepareArgs pa;
     std::memset(&pa, 0, sizeof(pa));
     if (h->opt == kOptAdam) {
@@ -1154,15 +1197,36 @@ zero_status zero_step_device(zero_shard_t h, const void* const* contribs, int32_
     pa.min_scale = h->ls.min_scale;
     pa.dynamic = h->ls.dynamic;
     pa.growth_interval = h->ls.growth_interval;
-    hipError_t e = zk::launch_finalize(h->partial, slots, h->level1, h->result, h->max_norm, h->dev,
-                                       pa, s);
-    if (e != hipSuccess) return hip_fail(e, "step_device: fold");
+    zk::StepSource src = source_device(h);
+    if (fold_inline) {
+        // the update folds the partials and decides the step itself
+        src.fold.partial = h->partial;
+        src.fold.n = (int32_t)slots;
+        src.fold.snapshot = h->dev_snapshot;
+        src.fold.dev = h->dev;
+        src.fold.res = h->result;
+        src.fold.max_norm = h->max_norm;
+        src.fold.pa = pa;
+    } else {
+        hipError_t e = zk::launch_finalize(h->partial, slots, h->level1, h->result, h->max_norm,
+                                           h->dev, pa, s);
+        if (e != hipSuccess) return hip_fail(e, "step_device: fold");
+    }
     double pw1, pw2;
     bool same;
     zero_status st = h->opt == kOptAdam
-        ? launch_adam_step(h, h->hp, s, source_device(h), &pw1, &pw2, &same, "step_device: update")
-        : launch_sgd_step(h, h->sgd, s, source_device(h), "step_device: update");
+        ? launch_adam_step(h, h->hp, s, src, &pw1, &pw2, &same, "step_device: update")
+        : launch_sgd_step(h, h->sgd, s, src, "step_device: update");
+    if (st == ZERO_OK && src.fold.partial != nullptr) h->inline_folds += 1;
     return st;
+}
+
+zero_status zero_shard_inline_folds(zero_shard_t h, int64_t* count)
+{
+    if (!live(h)) return fail(ZERO_ERR_STATE, "inline_folds: not a live handle");
+    if (!count) return fail(ZERO_ERR_INVALID_ARG, "inline_folds: count is NULL");
+    *count = h->inline_folds;
+    return ZERO_OK;
 }
 
 zero_status zero_device_end(zero_shard_t h, void* stream, zero_step_info* out)
