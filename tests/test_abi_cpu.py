@@ -150,6 +150,10 @@ def test_null_and_dead_handles():
     assert L.zero_bucket_reduce(bogus, arr, 1, 0, 1, None) == zs.ZERO_ERR_STATE
     assert L.zero_overflow_check(bogus, None, ctypes.byref(info)) == zs.ZERO_ERR_STATE
     assert L.zero_adam_step(bogus, None, None, ctypes.byref(info)) == zs.ZERO_ERR_STATE
+    n = ctypes.c_int64(-1)
+    assert L.zero_shard_inline_folds(bogus, ctypes.byref(n)) == zs.ZERO_ERR_STATE
+    assert L.zero_shard_inline_folds(None, ctypes.byref(n)) == zs.ZERO_ERR_STATE
+    assert n.value == -1                                   # untouched on error
     assert L.zero_shard_destroy(bogus) == zs.ZERO_ERR_STATE
 
 
