@@ -208,3 +208,19 @@ def test_inline_fold_graph_replays(name):
     finally:
         zs.zero_shard_destroy(ha)
         zs.zero_shard_destroy(hb)
+
+
+def test_inline_folds_needs_a_count_pointer():
+    w = W["tiny"]
+    dev = torch.device("cuda", 0)
+    n = 4096
+    master0, m0, v0 = synth.init_state(w, dev, 0, elems=n)
+    grad = torch.zeros(n, dtype=torch.float16, device=dev)
+    param = master0.to(torch.float16)
+    h = zs.zero_shard_init(master0, m0, v0, grad, param, psi=n * w.nd, nd=w.nd, rank=0,
+                           bucket_elems=n, hp=hp_of(w), ls=ls_of(w))
+    try:
+        assert zs.lib().zero_shard_inline_folds(h, None) == zs.ZERO_ERR_INVALID_ARG
+        assert zs.zero_shard_inline_folds(h) == 0
+    finally:
+        zs.zero_shard_destroy(h)

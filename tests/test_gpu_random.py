@@ -76,3 +76,35 @@ def test_random_large_case(k):
     """Shards of 2-6M elements, where a bucket of up to the whole shard takes
     3 runs per lane below 8 contributions; 2 steps each."""
     _run_case(100 + k, _case(k, LARGE, seed0=2000, steps=2, r_hi=8 if k % 3 else 21))
+
+
+INLINE_SIZES = [8, 64, 1024, 4096, 32_768, 65_536]
+
+
+@pytest.mark.parametrize("k", range(24))
+def test_random_inline_fold_case(k):
+    """Device-resident steps on aligned shards of 8-65,536 elements, where the
+    update usually folds the partials itself: any storage format, optimizer,
+    contribution count, bucket size, clipping and overflow step.  A single
+    bucket of a multiple of 8 elements has at most 256 partials in every
+    format, so there the inline fold must have run on every step."""
+    w, elems, cb, _, clip, _ = _case(k, INLINE_SIZES, seed0=3000, steps=3)
+    if k % 2 == 0:
+        cb = elems
+    hp = hp_of(w)
+    norm = w.grad_std / np.sqrt(w.R) * np.sqrt(elems)
+    max_norm = 0.5 * norm if clip else 0.0
+    log(f"[random inline {k}] lp={w.lp} opt={w.opt} mom={w.momentum} elems={elems} R={w.R} "
+        f"cb={cb} clip={clip} inject={w.inject_step} scale={w.scale} dynamic={w.dynamic}")
+    n = []
+    g = run_gpu(w, elems=elems, bucket_elems=cb, hp=hp, flow="device", max_norm=max_norm,
+                inline_folds=n)
+    st, oi = run_oracle(w, g, bucket_elems=cb, hp=hp, max_norm=max_norm)
+    errs = compare(w, g, st, oi, f"random inline {k}")
+    log(f"[random inline {k}] inline steps {n[0]} of {w.steps}")
+    if not clip:
+        assert errs["bitwise"], (k, errs)
+    if w.inject_step is not None:
+        assert g.infos[w.inject_step].overflow == 1
+    if cb == elems:
+        assert n == [w.steps], (k, n)
