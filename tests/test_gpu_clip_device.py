@@ -135,10 +135,13 @@ def test_device_flow_misaligned(name):
         compare(w, g, st, oi, f"device misaligned {name} {o}")
 
 
-def test_device_flow_scan_of_caller_filled_gradient():
-    """contribs = None: the device step scans grad_shard (the P_os case)."""
+@pytest.mark.parametrize("n,inline", [(300_007, 0), (300_000, 1), (2_097_152, 1)])
+def test_device_flow_scan_of_caller_filled_gradient(n, inline):
+    """contribs = None: the device step scans grad_shard (the P_os case).  An
+    aligned shard of at most 256 scan workgroups (2,097,152 elements: exactly
+    256) folds the partials inside the update; 300,007 elements leave the
+    update a scalar tail and take the fold launch."""
     dev = torch.device("cuda", 0)
-    n = 300_007
     gen = torch.Generator(device=dev).manual_seed(5)
     master = torch.randn(n, generator=gen, device=dev) * 0.02
     m, v = torch.zeros(n, device=dev), torch.zeros(n, device=dev)
@@ -153,6 +156,7 @@ def test_device_flow_scan_of_caller_filled_gradient():
         zs.zero_device_begin(h)
         zs.zero_step_device(h, None)
         info = zs.zero_device_end(h)
+        assert zs.zero_shard_inline_folds(h) == inline
     finally:
         zs.zero_shard_destroy(h)
     ohp = oracle.AdamHP(lr=1e-3, weight_decay=0.01)
