@@ -19,7 +19,9 @@
 // and the squared gradient norm: wave butterfly, one LDS slot per wave, one
 // fp64 partial per workgroup, then a fixed-order fold of one or two levels
 // whose last lane also computes the clipping coefficient and, in the
-// device-resident flow, decides the step.
+// device-resident flow, decides the step.  A device-resident step of at most
+// 256 partials has no fold launch: every update workgroup repeats the fold in
+// the same order and takes the same decision (see InlineFold).
 //
 // Storage formats: fp16 and bf16 (2-byte grads and params beside the fp32
 // master copy) and fp32 (4-byte grads; the fp32 master is the parameter and
