@@ -116,6 +116,37 @@ def host_info() -> dict:
     return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0))}
 
 
+def sample_parity(gpu, st, n, counters) -> dict:
+    """One step of the benchmarked flow against the oracle's step from the same
+    state, counters and contributions, on the first n shard elements: the
+    stored gradient and the 2-byte params bitwise, the fp32 arrays bitwise and
+    by max relative error (the parity bar is 1e-6)."""
+    import numpy as np
+    out = {"elements": n, "from_step": int(counters[0]), "loss_scale": counters[1]}
+    out["grad_bitwise"] = bool(np.array_equal(gpu["grad"].view(np.uint8), st.grad.view(np.uint8)))
+    rel = 0.0
+    same = True
+    for k, o in (("master", st.master), ("m", st.m), ("v", st.v)):
+        g = gpu[k]
+        if g is None:
+            continue
+        same &= bool(np.array_equal(g.view(np.uint32), o.view(np.uint32)))
+        o64 = o.astype(np.float64)
+        rel = max(rel, float(np.max(np.abs(g.astype(np.float64) - o64)
+                                    / np.maximum(np.abs(o64), 1.1754944e-38))))
+    out["fp32_state_bitwise"] = same
+    out["fp32_state_max_rel"] = rel
+    if gpu["param"] is not None:
+        out["param_bitwise"] = bool(np.array_equal(gpu["param"], st.param))
+    return out
+
+
+def env_info(torch) -> dict:
+    props = torch.cuda.get_device_properties(0)
+    return {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+            "device": props.name, "arch": getattr(props, "gcnArchName", None)}
+
+
 def _oracle_setup(w):
     import oracle
     if w.opt == "sgd":
@@ -128,19 +159,27 @@ def _oracle_setup(w):
     return oracle, hp, ls, lp
 
 
-def cpu_baseline(w, state_host, contribs_host, bucket_elems):
+def _counters(st, counters):
+    """Start an oracle state at the library's step count, loss scale and
+    clean-step count (None: the workload's initial values)."""
+    if counters is not None:
+        st.t, st.scale, st.good_steps = counters
+    return st
+
+
+def cpu_baseline(w, state_host, contribs_host, bucket_elems, counters=None):
     """The oracle's step on the whole sample, on one core: (params/s, seconds,
     the oracle's state after the step)."""
     oracle, hp, ls, lp = _oracle_setup(w)
     master, m, v = state_host
-    st = oracle.new_state(lp, master, m, v, hp, ls)
+    st = _counters(oracle.new_state(lp, master, m, v, hp, ls), counters)
     t0 = time.perf_counter()
     oracle.step(st, contribs_host, bucket_elems, hp, ls)
     dt = time.perf_counter() - t0
     return master.size / dt, dt, st
 
 
-def cpu_baseline_threads(w, state_host, contribs_host, bucket_elems, threads):
+def cpu_baseline_threads(w, state_host, contribs_host, bucket_elems, threads, counters=None):
     """The same oracle step with the sample cut into `threads` contiguous
     chunks, one thread each (the oracle's C calls release the GIL).  Each chunk
     is a shard of its own, so the concatenated result equals the one-core
@@ -154,8 +193,9 @@ def cpu_baseline_threads(w, state_host, contribs_host, bucket_elems, threads):
     n = master.size
     bounds = [n * k // threads for k in range(threads + 1)]
     parts = [slice(bounds[k], bounds[k + 1]) for k in range(threads) if bounds[k + 1] > bounds[k]]
-    states = [oracle.new_state(lp, master[sl], None if m is None else m[sl],
-                               None if v is None else v[sl], hp, ls) for sl in parts]
+    states = [_counters(oracle.new_state(lp, master[sl], None if m is None else m[sl],
+                                         None if v is None else v[sl], hp, ls), counters)
+              for sl in parts]
     chunks = [[c[sl] for c in contribs_host] for sl in parts]
     gate = threading.Barrier(len(parts) + 1)
     errors = []
@@ -369,16 +409,30 @@ def main() -> int:
     traffic = measured_traffic(args.workload, S)
 
     cpu = None
+    parity = None
     if args.cpu_sample > 0 and args.mode == "pos_g":
         n = min(args.cpu_sample, S)
-        state_host = tuple(None if t is None else t[:n].cpu().numpy() for t in (master, m, v))
-        if w.lp == "fp32":
-            contribs_host = [b[:n].cpu().numpy() for b in bufs]
-        else:
-            contribs_host = [b[:n].view(torch.int16).cpu().numpy().view(np.uint16) for b in bufs]
-        rate, dt, st1 = cpu_baseline(w, state_host, contribs_host, cb)
+        host = lambda t: None if t is None else t[:n].cpu().numpy()
+        bits = lambda t: (t[:n].cpu().numpy() if t.dtype == torch.float32
+                          else t[:n].view(torch.int16).cpu().numpy().view(np.uint16))
+        state_host = tuple(host(t) for t in (master, m, v))
+        contribs_host = [bits(b) for b in bufs]
+        counters = zs.zero_shard_get_counters(h)
+        # one more step of the reported (device-resident) flow on the same
+        # inputs: its first n elements are checked against the oracle's step
+        zs.zero_device_begin(h, stream)
+        zs.zero_step_device(h, bufs, stream)
+        zs.zero_device_end(h, stream)
+        gpu_after = {"grad": bits(grad), "master": host(master), "m": host(m), "v": host(v),
+                     "param": None if param is None else bits(param)}
+        rate, dt, st1 = cpu_baseline(w, state_host, contribs_host, cb, counters)
+        parity = sample_parity(gpu_after, st1, n, counters)
+        del gpu_after
+        print(f"[bench] parity of one more step on {n} elements: {parity}", file=sys.stderr,
+              flush=True)
         threads = min(len(os.sched_getaffinity(0)), 16)
-        prate, pdt, pmaster = cpu_baseline_threads(w, state_host, contribs_host, cb, threads)
+        prate, pdt, pmaster = cpu_baseline_threads(w, state_host, contribs_host, cb, threads,
+                                                   counters)
         cpu = {"value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
                "sample": f"one full step (reduce of {R} contributions, flag/norm, "
                          f"{'SGD' if sgd else 'Adam'}) on the "
@@ -434,6 +488,8 @@ def main() -> int:
                      "timing": "HIP events around the update enqueue of the synchronous-check "
                                "flow, on the launch stream (the update kernel alone)"},
         "cpu_baseline": cpu,
+        "parity_sample": parity,
+        "env": env_info(torch),
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -91,3 +91,27 @@ def test_threaded_oracle_timing_equals_one_core(wname, threads):
     assert rate > 0 and prate > 0
     assert np.array_equal(pmaster.view(np.uint32), st.master.view(np.uint32))
     assert not np.array_equal(st.master, master)                 # the step did update
+
+
+def test_sample_parity_reports_bitwise_and_relative_error():
+    import numpy as np
+    from types import SimpleNamespace
+    rng = np.random.default_rng(1)
+    n = 1000
+    st = SimpleNamespace(grad=rng.integers(0, 2**16, n, dtype=np.uint16),
+                         master=rng.normal(0, 0.02, n).astype(np.float32),
+                         m=rng.normal(0, 1e-4, n).astype(np.float32),
+                         v=np.abs(rng.normal(0, 1e-8, n)).astype(np.float32),
+                         param=rng.integers(0, 2**16, n, dtype=np.uint16))
+    gpu = {k: getattr(st, k).copy() for k in ("grad", "master", "m", "v", "param")}
+    p = bench.sample_parity(gpu, st, n, (7, 4096.0, 7))
+    assert p["grad_bitwise"] and p["fp32_state_bitwise"] and p["param_bitwise"]
+    assert p["fp32_state_max_rel"] == 0.0 and p["from_step"] == 7
+    gpu["v"][3] = np.nextafter(gpu["v"][3], np.float32(1))      # one ulp off
+    gpu["grad"][5] ^= 1
+    p = bench.sample_parity(gpu, st, n, (7, 4096.0, 7))
+    assert not p["fp32_state_bitwise"] and not p["grad_bitwise"] and p["param_bitwise"]
+    assert 0.0 < p["fp32_state_max_rel"] < 1e-6
+    gpu["m"] = None                                              # SGD without momentum
+    gpu["v"] = None
+    assert bench.sample_parity(gpu, st, n, (7, 4096.0, 7))["fp32_state_bitwise"]

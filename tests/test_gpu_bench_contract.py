@@ -42,3 +42,8 @@ def test_bench_json_line():
     assert isinstance(c["unit"], str) and isinstance(c["sample"], str)
     a = c["all_cores"]
     assert a["cores"] >= 1 and a["value"] > 0 and a["equals_one_core"] is True
+    p = d["parity_sample"]
+    assert p["elements"] == 65536 and p["from_step"] > 0
+    assert p["grad_bitwise"] and p["fp32_state_bitwise"] and p["param_bitwise"]
+    assert p["fp32_state_max_rel"] == 0.0
+    assert d["env"]["arch"].startswith("gfx950")
