@@ -427,8 +427,19 @@ __global__ __launch_bounds__(kFoldBlock) void fold_kernel(const double* in, int6
 {
     const int64_t lo = (int64_t)blockIdx.x * chunk;
     const int64_t hi = lo + chunk < n ? lo + chunk : n;
+    // lane l adds in[lo + l], in[lo + l + 256], ... in that order; eight loads
+    // are issued before their adds, so the lane waits for memory once per
+    // eight partials, not once per partial
     double s = 0.0;
-    for (int64_t i = lo + threadIdx.x; i < hi; i += kFoldBlock) s += in[i];
+    int64_t i = lo + threadIdx.x;
+    for (; i + 7 * kFoldBlock < hi; i += 8 * kFoldBlock) {
+        double x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = in[i + k * kFoldBlock];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s += x[k];
+    }
+    for (; i < hi; i += kFoldBlock) s += in[i];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
     __shared__ double sh[kFoldBlock / 64];
@@ -487,13 +498,18 @@ __device__ __forceinline__ StepVals step_vals(const StepSource& src, float inv_s
 // with the same value.
 __device__ __forceinline__ double fold_small(const double* p, int n)
 {
-    double w[4];
+    // all four loads issued together (a lane past n loads p[0] and keeps 0.0)
+    double x[4], w[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int i = (int)(threadIdx.x & 63) + 64 * k;   // every wave sums them all
-        double s = 0.0;
-        if (i < n) s += p[i];
-        w[k] = s;
+        x[k] = p[i < n ? i : 0];
+    }
+    __builtin_amdgcn_sched_barrier(0);     // keep the four loads ahead of every use
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = (int)(threadIdx.x & 63) + 64 * k;
+        w[k] = i < n ? 0.0 + x[k] : 0.0;
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -513,8 +529,8 @@ struct InlineDecision {
 
 __device__ __forceinline__ StepVals step_vals_inline(const InlineFold& f, InlineDecision& d)
 {
+    d.next = *f.snapshot;                  // loaded while the partials are in flight
     d.sumsq = fold_small(f.partial, f.n);
-    d.next = *f.snapshot;
     prepare_step(&d.next, d.sumsq, f.pa);
     d.clip = clip_coef(d.sumsq, f.max_norm);
     return StepVals{d.next.upd_inv_scale, d.next.bc1, d.next.bc2, d.clip, d.next.skip != 0};
