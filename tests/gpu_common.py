@@ -10,6 +10,7 @@ within relative 1e-5.  With fp32 storage there is no 2-byte param.
 from __future__ import annotations
 
 import dataclasses
+import os
 import sys
 from typing import List, Optional
 
@@ -21,6 +22,18 @@ import zero_dp_sharded_amd as zs
 from zero_dp_sharded_amd import synth
 
 LP_CODE = {"fp16": oracle.FP16, "bf16": oracle.BF16, "fp32": oracle.FP32}
+
+# Which steps fold their partials inside the update depends on the launch
+# shapes a build was compiled with; a variant build loaded through
+# ZERO_SHARD_LIB (tuning shapes, or every launch split after 1024 work-items)
+# may take the fold launch where the in-tree build does not.  Tests assert the
+# inline-fold counts only for the in-tree library; parity holds for every build.
+IN_TREE_BUILD = not os.environ.get("ZERO_SHARD_LIB")
+
+
+def expect_inline_folds(got, expected, tag=""):
+    if IN_TREE_BUILD:
+        assert got == expected, (tag, got, expected)
 
 
 def log(*a):

@@ -21,8 +21,8 @@ import torch
 
 import oracle
 import zero_dp_sharded_amd as zs
-from gpu_common import (LP_CODE, compare, f32, hp_of, log, ls_of, oracle_hp, oracle_ls, run_gpu,
-                        run_oracle, stored)
+from gpu_common import (LP_CODE, compare, expect_inline_folds, f32, hp_of, log, ls_of, oracle_hp,
+                        oracle_ls, run_gpu, run_oracle, stored)
 from zero_dp_sharded_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -75,7 +75,8 @@ def test_inline_fold_equals_sync_and_oracle(name, clip):
                 inline_folds=n_sync)
     b = run_gpu(w, elems=elems, bucket_elems=cb, flow="device", max_norm=max_norm,
                 inline_folds=n_dev)
-    assert n_sync == [0] and n_dev == [w.steps], (n_sync, n_dev)
+    assert n_sync == [0]
+    expect_inline_folds(n_dev, [w.steps], name)
     assert [i.overflow for i in b.infos] == [0, 1, 0, 0, 0]
     _same(a, b, f"{name} clip={clip}")
     st, oi = run_oracle(w, b, bucket_elems=cb, max_norm=max_norm)
@@ -94,7 +95,7 @@ def test_inline_fold_uninterrupted_steps(name):
     n = []
     c = run_gpu(w, elems=elems, bucket_elems=cb, flow="device_run",
                 scale_of=lambda s: scales[s], inline_folds=n)
-    assert n == [w.steps]
+    expect_inline_folds(n, [w.steps], name)
     last, ref = c.infos[-1], a.infos[-1]
     assert (last.overflow, last.step_t, last.scale_used, last.scale_next, last.grad_norm) == \
         (ref.overflow, ref.step_t, ref.scale_used, ref.scale_next, ref.grad_norm)
@@ -196,8 +197,8 @@ def test_inline_fold_graph_replays(name):
             log(f"[inline graph] replay {rep}: oracle t={ost.t} scale={ost.scale}")
             scale = ost.scale
         ia, ib = zs.zero_device_end(ha), zs.zero_device_end(hb)
-        assert zs.zero_shard_inline_folds(ha) == w.steps
-        assert zs.zero_shard_inline_folds(hb) == K        # captured once, replayed twice
+        expect_inline_folds(zs.zero_shard_inline_folds(ha), w.steps, name)
+        expect_inline_folds(zs.zero_shard_inline_folds(hb), K, name)   # captured once, replayed twice
         assert (ia.overflow, ia.step_t, ia.scale_next) == (ib.overflow, ib.step_t, ib.scale_next)
         assert ia.overflow == 1 and np.isnan(ia.grad_norm) and np.isnan(ib.grad_norm)
         # three overflowing steps in the second batch: t stays at 3, the scale
