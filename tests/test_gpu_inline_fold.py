@@ -1,5 +1,5 @@
 """GPU parity of the fold inside the update, the device-resident step of small
-shards.  When a step has at most 256 per-workgroup partials and the update is
+shards.  When a step has at most 512 per-workgroup partials and the update is
 one vector launch over the whole shard, every update workgroup folds the
 partials itself in the fold kernel's order and decides the step, and the last
 one to finish advances the device counters.  The results must be bitwise
@@ -34,12 +34,15 @@ def _w(base, **over):
     return dataclasses.replace(base, **over)
 
 
-# name -> (workload, shard elements, C_B): each exactly 256 partials
+# name -> (workload, shard elements, C_B): 256 partials (one partial per fold
+# lane) or 512 (two per lane, the limit)
 CASES = {
     "adam_fp16_r4": (_w(W["tiny"], steps=5), 262_144, 65_536),        # 4 x 64
+    "adam_fp16_r4_512": (_w(W["tiny"], steps=5), 524_288, 524_288),   # 512
     "adam_bf16_r8": (_w(W["7.5b_bf16"], steps=5), 131_072, 65_536),   # 2 x 128
     "adam_fp16_r16": (_w(W["13b_inf"], steps=5, inject_step=None), 131_072, 131_072),  # 256
     "sgdm_fp32_r8": (_w(W["c1_7.5b_sgdm"], steps=5), 65_536, 65_536),  # 256
+    "sgdm_fp32_r8_512": (_w(W["c1_7.5b_sgdm"], steps=5), 131_072, 32_768),  # 4 x 128
     "sgd_fp32_r8": (_w(W["c2_1.5b_sgd"], steps=5), 65_536, 32_768),    # 2 x 128
 }
 
@@ -106,7 +109,7 @@ def test_inline_fold_uninterrupted_steps(name):
 
 
 @pytest.mark.parametrize("elems,cb,why", [
-    (263_168, 263_168, "257 partials"),              # 32,896 runs / 128 per workgroup
+    (525_312, 525_312, "513 partials"),              # 65,664 runs / 128 per workgroup
     (200_002, 200_002, "update with a scalar tail"),  # 197 partials, S not a multiple of 4
 ])
 def test_past_the_limits_takes_the_fold_launch(elems, cb, why):
@@ -134,7 +137,7 @@ def test_misaligned_update_takes_the_fold_launch():
     _same(a, b, "misaligned master")
 
 
-@pytest.mark.parametrize("name", ["adam_fp16_r4", "sgdm_fp32_r8"])
+@pytest.mark.parametrize("name", ["adam_fp16_r4", "sgdm_fp32_r8", "adam_fp16_r4_512"])
 def test_inline_fold_graph_replays(name):
     """Three inline-fold steps captured in one CUDA graph, replayed twice with
     eager refills of the contributions between replays (an overflow planted

@@ -229,7 +229,7 @@ struct ScanLaunch {
 // `dev` (and the check result) while the others still read: no counter, no
 // atomics.  This saves the fold's launch on launch-bound shards.  The update
 // must run as one vector launch with no element-wise part.
-constexpr int kInlineFoldMax = 256;
+constexpr int kInlineFoldMax = 512;
 struct InlineFold {
     const double* partial;     // nullptr: off
     int32_t n;                 // partials, at most kInlineFoldMax

@@ -20,7 +20,7 @@
 // fp64 partial per workgroup, then a fixed-order fold of one or two levels
 // whose last lane also computes the clipping coefficient and, in the
 // device-resident flow, decides the step.  A device-resident step of at most
-// 256 partials has no fold launch: every update workgroup repeats the fold in
+// 512 partials has no fold launch: every update workgroup repeats the fold in
 // the same order and takes the same decision (see InlineFold).
 //
 // Storage formats: fp16 and bf16 (2-byte grads and params beside the fp32
@@ -490,26 +490,36 @@ __device__ __forceinline__ StepVals step_vals(const StepSource& src, float inv_s
     return v;
 }
 
-// The inline fold (InlineFold): the one-workgroup fold of at most 256
+// The inline fold (InlineFold): the one-workgroup fold of at most 512
 // partials, reproduced by one wave.  Lane l stands for the fold's lanes l,
-// l+64, l+128 and l+192, each of which holds at most one partial (0.0 + p);
-// the four 64-lane butterflies are the fold's four waves, and their totals add
-// in wave order, so the sum is bitwise the fold kernel's.  Every lane ends
-// with the same value.
-__device__ __forceinline__ double fold_small(const double* p, int n)
+// l+64, l+128 and l+192; fold lane j adds the partials j, j+256 (T = 2 when
+// there are more than 256) to 0.0 in that order, the four 64-lane butterflies
+// are the fold's four waves, and their totals add in wave order, so the sum is
+// bitwise the fold kernel's.  Every lane ends with the same value.  (Up to 1024
+// partials, T = 4, the redundant loads cost what the fold launch saves.)
+template <int T>
+__device__ __forceinline__ double fold_small_t(const double* p, int n)
 {
-    // all four loads issued together (a lane past n loads p[0] and keeps 0.0)
-    double x[4], w[4];
+    // all 4T loads issued together (a slot past n loads p[0] and adds nothing)
+    double x[4][T], w[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int i = (int)(threadIdx.x & 63) + 64 * k;   // every wave sums them all
-        x[k] = p[i < n ? i : 0];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int i = (int)(threadIdx.x & 63) + 64 * k + 256 * t;   // every wave sums them all
+            x[k][t] = p[i < n ? i : 0];
+        }
     }
-    __builtin_amdgcn_sched_barrier(0);     // keep the four loads ahead of every use
+    __builtin_amdgcn_sched_barrier(0);     // keep the loads ahead of every use
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int i = (int)(threadIdx.x & 63) + 64 * k;
-        w[k] = i < n ? 0.0 + x[k] : 0.0;
+        double s = 0.0;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int i = (int)(threadIdx.x & 63) + 64 * k + 256 * t;
+            if (i < n) s += x[k][t];
+        }
+        w[k] = s;
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -517,6 +527,11 @@ __device__ __forceinline__ double fold_small(const double* p, int n)
         for (int k = 0; k < 4; ++k) w[k] += __shfl_xor(w[k], off, 64);
     }
     return ((w[0] + w[1]) + w[2]) + w[3];
+}
+
+__device__ __forceinline__ double fold_small(const double* p, int n)
+{
+    return n <= 256 ? fold_small_t<1>(p, n) : fold_small_t<2>(p, n);
 }
 
 // The step as the fold's last lane decides it, computed by every workgroup
