@@ -7,8 +7,9 @@ Nd = 64: a 2.0e9-element shard, 4 contributions, C_B = 2e8, fp16 storage, loss
 scale 4096, AdamW lr 6e-5, wd 0.1.  Four flows run the same step and are all
 timed: device-resident steps enqueued back to back (the reported value by
 default: the decision and the counters stay on the GPU, no host round trip),
-the same step captured in a HIP graph and replayed, the device-gated check
-(the host waits for a 16-byte result copy per step) and the synchronous check.
+the same steps captured in a HIP graph (up to 10 per graph) and replayed, the
+device-gated check (the host waits for a 16-byte result copy per step) and the
+synchronous check.
 Inputs are seeded synthetic tensors resident in HBM before timing starts; the
 same contribution batch feeds every step (each step still reads and writes
 every byte).
@@ -233,8 +234,8 @@ def main() -> int:
     ap.add_argument("--flow", choices=["gated", "sync", "device", "graph"], default="device",
                     help="flow whose step time is the reported value: device-gated check "
                          "(gated), synchronous check (sync), device-resident steps enqueued "
-                         "back to back (device), or one device-resident step captured in a "
-                         "HIP graph and replayed (graph); all four are timed")
+                         "back to back (device), or device-resident steps captured in a HIP "
+                         "graph (up to 10 per graph) and replayed (graph); all four are timed")
     ap.add_argument("--mode", choices=["pos_g", "pos"], default="pos_g",
                     help="pos_g: gradient partitioning (bucket reduces + check + Adam); "
                          "pos: optimizer-state partitioning only (the owner's slice of an "
@@ -360,23 +361,29 @@ def main() -> int:
           f"{adam_sync:.3f} ms, reduce {red_sync:.3f} ms", file=sys.stderr, flush=True)
 
     def timed_device(use_graph):
-        # device-resident flow: no host synchronisation inside the timed steps
+        # device-resident flow: no host synchronisation inside the timed steps.
+        # The graph holds g consecutive steps, g the largest divisor of K up to
+        # 10, and is replayed K / g times: exactly K steps, with the graph
+        # launch cost spread over g of them as a training loop would.
         contrib = bufs if args.mode == "pos_g" else None
         zs.zero_device_begin(h, stream)
         graph = None
+        per_run = 1
         if use_graph:
+            per_run = max(d for d in range(1, min(10, args.steps) + 1) if args.steps % d == 0)
             torch.cuda.synchronize()
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
-                zs.zero_step_device(h, contrib)     # the capture stream is current here
+                for _ in range(per_run):
+                    zs.zero_step_device(h, contrib)     # the capture stream is current here
             run = graph.replay
         else:
             run = lambda: zs.zero_step_device(h, contrib, stream)
-        for _ in range(max(1, args.warmup)):
+        for _ in range(max(1, args.warmup // per_run)):
             run()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(args.steps // per_run):
             run()
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / args.steps
