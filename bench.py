@@ -432,7 +432,15 @@ def main() -> int:
         zs.zero_device_end(h, stream)
         gpu_after = {"grad": bits(grad), "master": host(master), "m": host(m), "v": host(v),
                      "param": None if param is None else bits(param)}
-        rate, dt, st1 = cpu_baseline(w, state_host, contribs_host, cb, counters)
+        # the one-core leg runs pinned to one core (this thread only; restored
+        # before the all-cores leg starts its threads)
+        affinity = os.sched_getaffinity(0)
+        pinned = min(affinity)
+        os.sched_setaffinity(0, {pinned})
+        try:
+            rate, dt, st1 = cpu_baseline(w, state_host, contribs_host, cb, counters)
+        finally:
+            os.sched_setaffinity(0, affinity)
         parity = sample_parity(gpu_after, st1, n, counters)
         del gpu_after
         print(f"[bench] parity of one more step on {n} elements: {parity}", file=sys.stderr,
@@ -443,7 +451,8 @@ def main() -> int:
         cpu = {"value": rate, "unit": "params/s", "cores": 1, "kind": "oracle",
                "sample": f"one full step (reduce of {R} contributions, flag/norm, "
                          f"{'SGD' if sgd else 'Adam'}) on the "
-                         f"first {n} elements of the same shard; {dt:.1f} s single-threaded",
+                         f"first {n} elements of the same shard; {dt:.1f} s single-threaded, "
+                         f"pinned to core {pinned}",
                "host": host_info(),
                "all_cores": {"value": prate, "unit": "params/s", "cores": threads,
                              "seconds": pdt,
