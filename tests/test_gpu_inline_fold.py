@@ -1,8 +1,8 @@
 """GPU parity of the fold inside the update, the device-resident step of small
 shards.  When a step has at most 512 per-workgroup partials and the update is
 one vector launch over the whole shard, every update workgroup folds the
-partials itself in the fold kernel's order and decides the step, and the last
-one to finish advances the device counters.  The results must be bitwise
+partials itself in the fold kernel's order and decides the step from the state
+snapshot the step's reduce took, and workgroup 0 advances the device counters.  The results must be bitwise
 those of the synchronous flow (fold kernel, host decision) and match the
 oracle, through skipped steps, loss-scale changes and clipping; shapes just
 past the limits must take the fold launch instead; and graph replays of such
@@ -88,9 +88,9 @@ def test_inline_fold_equals_sync_and_oracle(name, clip):
 
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_inline_fold_uninterrupted_steps(name):
-    """Five steps on the device alone (the counter of finished workgroups must
-    return to zero after every step): the last step's result and the final
-    state equal the synchronous flow's."""
+    """Five steps on the device alone (each step's snapshot must be the state
+    the previous step left): the last step's result and the final state equal
+    the synchronous flow's."""
     base, elems, cb = CASES[name]
     w = _w(base, inject_step=2, dynamic=1, scale=64.0)
     a = run_gpu(w, elems=elems, bucket_elems=cb, flow="sync")
