@@ -51,6 +51,14 @@ MUTATIONS = [
     ("flag misses inf", "if (!isfinite(x)) f = 1;", "if (isnan(x)) f = 1;"),
     ("norm not unscaled", "float u = x * inv_scale;", "float u = x;"),
     ("scale not halved", "double s = *scale / 2.0;", "double s = *scale;"),
+    ("scale not floored at min_scale", "*scale = s < min_scale ? min_scale : s;", "*scale = s;"),
+    ("scale grows one clean step late", "if (*good_steps == growth_interval)",
+     "if (*good_steps > growth_interval)"),
+    ("clean count kept after growth", "*scale = *scale * 2.0;\n            *good_steps = 0;",
+     "*scale = *scale * 2.0;"),
+    ("clean count kept after overflow", "        *good_steps = 0;\n    } else {",
+     "    } else {"),
+    ("static scale still halves", "    if (!dynamic) return;\n", ""),
     ("partition floors", "    int64_t s = (psi + nd - 1) / nd;\n    int64_t b = (int64_t)rank * s;",
      "    int64_t s = psi / nd;\n    int64_t b = (int64_t)rank * s;"),
     ("stage 2 drops b/Nd", "out->per_rank_stage[2] = b * P + ((b + K) * P) / N;",

@@ -346,6 +346,31 @@ def test_scale_growth_and_floor(oracle):
     assert oracle.loss_scale_next(1, st, 1.0, 0) == (1.0, 0)
 
 
+def test_scale_clean_count_restarts(oracle):
+    """The loss-scale reading (halve on overflow down to min_scale, double
+    after growth_interval clean steps) counts clean steps since the scale last
+    changed: the count restarts after a growth and after an overflow.
+    Hand-computed for interval 2 from 8.0: clean, overflow, then four clean
+    steps (two growths), two overflows, one clean step."""
+    ls = oracle.LossScale(init_scale=8.0, dynamic=1, growth_interval=2, min_scale=1.0)
+    s, g = 8.0, 0
+    scales, goods = [], []
+    for f in (0, 1, 0, 0, 0, 0, 1, 1, 0):
+        s, g = oracle.loss_scale_next(f, ls, s, g)
+        scales.append(s)
+        goods.append(g)
+    assert scales == [8.0, 4.0, 4.0, 8.0, 8.0, 16.0, 8.0, 4.0, 4.0]
+    assert goods == [1, 0, 1, 0, 1, 0, 0, 0, 1]
+
+
+def test_static_scale_never_changes(oracle):
+    """A static loss scale (the 7.5B workload's) stays put on an overflow and on
+    clean steps, above the floor too, and the clean count is left alone."""
+    st = oracle.LossScale(init_scale=8.0, dynamic=0, growth_interval=1, min_scale=1.0)
+    assert oracle.loss_scale_next(1, st, 8.0, 3) == (8.0, 3)
+    assert oracle.loss_scale_next(0, st, 8.0, 3) == (8.0, 3)
+
+
 def test_shard_concat_equals_unsharded(oracle):
     """The pages' invariant: partitioning over Nd ranks changes only where the
     states live; concatenating the Nd owner updates equals the Nd = 1 update."""
