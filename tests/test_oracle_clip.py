@@ -136,6 +136,31 @@ def test_adamw_clip_trajectory_matches_torch(oracle, max_norm):
     assert np.allclose(st.master, want, rtol=1e-5, atol=1e-8)
 
 
+@pytest.mark.parametrize("max_norm", [0.0, 0.05, 1e9])
+def test_adam_l2_clip_trajectory_matches_torch(oracle, max_norm):
+    """L2 weight decay (wd_mode 1) adds wd * p to the gradient after clipping,
+    as torch.optim.Adam's weight_decay does to a gradient that
+    clip_grad_norm_ has already scaled (float64, CPU)."""
+    rng = np.random.default_rng(13)
+    n, steps = 2003, 5
+    lr, b1, b2, eps, wd = 1e-2, 0.9, 0.999, 1e-8, 0.1
+    p0 = (rng.standard_normal(n) * 0.1).astype(np.float32)
+    grads = [(rng.standard_normal(n) * 0.01).astype(np.float32) for _ in range(steps)]
+    hp = oracle.AdamHP(lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd, wd_mode=1)
+    z = np.zeros(n)
+    st = _step_oracle(oracle, hp, FP32, p0, z, z, grads, max_norm)
+    f = lambda x: float(np.float32(x))
+    p = torch.tensor(p0.astype(np.float64), requires_grad=True)
+    opt = torch.optim.Adam([p], lr=f(lr), betas=(f(b1), f(b2)), eps=f(eps), weight_decay=f(wd))
+    for g in grads:
+        p.grad = torch.tensor(g.astype(np.float64))
+        if max_norm > 0:
+            torch.nn.utils.clip_grad_norm_([p], max_norm)
+        opt.step()
+    want = p.detach().numpy()
+    assert np.allclose(st.master, want, rtol=1e-5, atol=1e-8)
+
+
 def test_clipping_leaves_constant_gradient_adam_unchanged(oracle):
     """Adam with eps -> 0 sees g and c*g (c > 0) alike, so a clipped constant
     gradient gives the unclipped trajectory up to rounding."""

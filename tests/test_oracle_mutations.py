@@ -51,6 +51,13 @@ MUTATIONS = [
     ("flag misses inf", "if (!isfinite(x)) f = 1;", "if (isnan(x)) f = 1;"),
     ("norm not unscaled", "float u = x * inv_scale;", "float u = x;"),
     ("scale not halved", "double s = *scale / 2.0;", "double s = *scale;"),
+    ("norm summed in fp32", "s += (double)u * (double)u;", "s = (double)((float)s + u * u);"),
+    ("L2 decay before clipping",
+     "if (coef != 1.0f)\n            g = g * coef;\n        if (wd_mode == 1 && wd != 0.0f)\n            g = g + wd * p;",
+     "if (wd_mode == 1 && wd != 0.0f)\n            g = g + wd * p;\n        if (coef != 1.0f)\n            g = g * coef;"),
+    ("bias correction applied when off", "out[4] = bias_correction ? (float)(1.0 - pw1) : 1.0f;",
+     "out[4] = (float)(1.0 - pw1);"),
+    ("variance corrected by bc1", "float v_hat = v / bc2;", "float v_hat = v / bc1;"),
     ("scale not floored at min_scale", "*scale = s < min_scale ? min_scale : s;", "*scale = s;"),
     ("scale grows one clean step late", "if (*good_steps == growth_interval)",
      "if (*good_steps > growth_interval)"),
