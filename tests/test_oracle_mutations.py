@@ -51,6 +51,12 @@ MUTATIONS = [
     ("flag misses inf", "if (!isfinite(x)) f = 1;", "if (isnan(x)) f = 1;"),
     ("norm not unscaled", "float u = x * inv_scale;", "float u = x;"),
     ("scale not halved", "double s = *scale / 2.0;", "double s = *scale;"),
+    ("reduce divides by R", "store_g(lp, out, i, acc * inv_r);",
+     "store_g(lp, out, i, acc / (float)n_contrib);"),
+    ("fp16 NaN narrowed to inf", "(f ? (0x200u | (f >> 13)) : 0u)", "0u"),
+    ("bf16 NaN rounded like a number",
+     "    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu))\n        return (uint16_t)((u >> 16) | 0x40u);\n",
+     ""),
     ("norm summed in fp32", "s += (double)u * (double)u;", "s = (double)((float)s + u * u);"),
     ("L2 decay before clipping",
      "if (coef != 1.0f)\n            g = g * coef;\n        if (wd_mode == 1 && wd != 0.0f)\n            g = g + wd * p;",

@@ -13,7 +13,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-FP16, BF16 = 1, 2
+FP16, BF16, FP32 = 1, 2, 3
 
 
 def f16_bits(x):
@@ -47,6 +47,24 @@ def test_reduce_exact_integer_sums(oracle):
             inv = np.float32(1.0 / R)
             want = (ints.sum(axis=0).astype(np.float32) * inv).astype(np.float16).view(np.uint16)
             assert np.array_equal(got, want)
+
+
+def test_reduce_scales_by_fp32_reciprocal(oracle):
+    """The mean is the fp32 sum times fp32(1/R) (one fp32 rounding), not the sum
+    divided by R; the two differ in the last fp32 bit for some sums when R is not
+    a power of two.  fp32 storage keeps that bit.  Integer contributions make
+    every partial sum exact, and sum * fp32(1/R) is exact in fp64, so rounding
+    it once to fp32 gives the expected value."""
+    rng = np.random.default_rng(3)
+    for R in (3, 5, 6, 7):
+        ints = rng.integers(-1000, 1000, size=(R, 4099))
+        cs = [c.astype(np.float32) for c in ints]
+        got = oracle.bucket_reduce(FP32, cs)
+        sums = ints.sum(axis=0).astype(np.float64)
+        want = (sums * np.float64(np.float32(1.0 / R))).astype(np.float32)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), R
+        divided = (sums / R).astype(np.float32)
+        assert np.any(want != divided), R          # the pin tells the two apart
 
 
 def test_reduce_brute_force_fractions(oracle):
