@@ -57,6 +57,11 @@ MUTATIONS = [
     ("bf16 NaN rounded like a number",
      "    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu))\n        return (uint16_t)((u >> 16) | 0x40u);\n",
      ""),
+    ("fp16 subnormal loses its sign", "return sign ? -mag : mag;", "return mag;"),
+    ("fp16 exponent rebias off by one", "((e + 112u) << 23)", "((e + 111u) << 23)"),
+    ("SGD stores the gradient as the buffer", "momentum[i] = b;", "momentum[i] = g;"),
+    ("SGD momentum scales the gradient too", "float b = mu * momentum[i] + g;",
+     "float b = mu * (momentum[i] + g);"),
     ("norm summed in fp32", "s += (double)u * (double)u;", "s = (double)((float)s + u * u);"),
     ("L2 decay before clipping",
      "if (coef != 1.0f)\n            g = g * coef;\n        if (wd_mode == 1 && wd != 0.0f)\n            g = g + wd * p;",
