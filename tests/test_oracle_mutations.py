@@ -62,6 +62,13 @@ MUTATIONS = [
     ("SGD stores the gradient as the buffer", "momentum[i] = b;", "momentum[i] = g;"),
     ("SGD momentum scales the gradient too", "float b = mu * momentum[i] + g;",
      "float b = mu * (momentum[i] + g);"),
+    ("stage 0 counts one 2-byte copy", "out->per_rank_stage[0] = (2.0 * b + K) * P;",
+     "out->per_rank_stage[0] = (b + K) * P;"),
+    ("gradients partitioned from stage 1", "out->comp_grads[st] = st < 2 ? b * P : (b * P) / N;",
+     "out->comp_grads[st] = st < 1 ? b * P : (b * P) / N;"),
+    ("staging ignores the contribution count",
+     "out->bytes_staging = (int64_t)n_contrib * bucket_elems * lp_bytes;",
+     "out->bytes_staging = bucket_elems * lp_bytes;"),
     ("norm summed in fp32", "s += (double)u * (double)u;", "s = (double)((float)s + u * u);"),
     ("L2 decay before clipping",
      "if (coef != 1.0f)\n            g = g * coef;\n        if (wd_mode == 1 && wd != 0.0f)\n            g = g + wd * p;",
