@@ -13,9 +13,10 @@ pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def test_bench_json_line():
+@pytest.mark.parametrize("flow", ["device", "graph"])
+def test_bench_json_line(flow):
     cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--steps", "3",
-           "--warmup", "1", "--cpu-sample", "65536"]
+           "--warmup", "1", "--cpu-sample", "65536", "--flow", flow]
     print("running", " ".join(cmd), flush=True)
     out = subprocess.run(cmd, capture_output=True, text=True, timeout=240, cwd=ROOT)
     assert out.returncode == 0, out.stderr[-2000:]
@@ -29,6 +30,7 @@ def test_bench_json_line():
                      ("cpu_baseline", dict)):
         assert isinstance(d[key], typ), (key, d.get(key))
     assert "vs_baseline" in d and d["vs_baseline"] is None
+    assert d["flow"] == flow and d["ms_per_step"] == d["ms_per_step_by_flow"][flow]
     assert (d["n_gpus"], d["steps"], d["warmup"]) == (1, 3, 1)
     assert d["higher_is_better"] is True and d["scaling"] in ("weak", "strong")
     assert d["value"] > 0 and d["ms_per_step"] > 0
