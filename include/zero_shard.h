@@ -112,7 +112,8 @@ typedef struct {
 } zero_shard_desc;
 
 /* Textbook Adam (Kingma & Ba 2015, Algorithm 1); the pages give no formula.
- * Ranges: lr >= 0, 0 <= beta1 < 1, 0 <= beta2 < 1, eps > 0, weight_decay >= 0,
+ * Ranges: lr >= 0, 0 <= beta1 < 1, 0 <= beta2 < 1 (also after rounding to
+ * fp32: a beta within 3e-8 of 1 is refused), eps > 0, weight_decay >= 0,
  * initial_step >= 0 (number of steps already applied). */
 typedef struct {
     double lr, beta1, beta2, eps, weight_decay;
@@ -141,7 +142,11 @@ typedef struct {
 /* Loss scaling (not on the pages).  dynamic = 1: an overflowing step halves
  * the scale (not below min_scale); growth_interval clean steps in a row double
  * it.  dynamic = 0: the scale stays at init_scale; an overflowing step is still
- * skipped.  init_scale > 0, min_scale > 0, growth_interval >= 1. */
+ * skipped.  The check unscales first: a step overflows when any unscaled
+ * gradient f32(grad) * fp32(1/scale) is not finite, which includes a finite
+ * stored value that a scale below 1 unscales past the fp32 range.
+ * init_scale > 0 and min_scale > 0, each with a finite, non-zero fp32
+ * reciprocal (about 3e-39 < scale < 1.4e45); growth_interval >= 1. */
 typedef struct {
     double init_scale;
     int32_t dynamic;
@@ -267,8 +272,8 @@ zero_status zero_bucket_reduce(zero_shard_t h, const void* const* contribs, int3
                                int64_t bucket_off, int64_t bucket_len, void* stream);
 
 /*
- * Finish the overflow check of the step: OR of "not finite" over the stored
- * gradient shard and its unscaled squared norm, summed over per-block
+ * Finish the overflow check of the step: OR of "not finite" over the unscaled
+ * gradient shard (f32(grad) * fp32(1/scale)) and its squared norm, summed over per-block
  * partials in a fixed order (bitwise reproducible).  If no bucket was reduced
  * this step, the stored grad_shard is scanned instead (for callers that fill
  * it themselves).  With clipping on, the same fold computes the step's
@@ -342,8 +347,11 @@ zero_status zero_shard_set_clip(zero_shard_t h, double max_grad_norm);
  * step together ("ZeRO：大模型训练的内存优化革命" 3.1.1 and 3.1.2: every process
  * updates only its partition, so the decision must be shared).  Phase must be
  * CHECKED.  global_overflow must be 0 or 1 and not below this rank's own flag;
- * global_grad_norm is reported as the step's norm.  *out (may be NULL) gets
- * the merged result.  Errors: STATE (dead handle, not checked), INVALID_ARG.
+ * global_grad_norm is reported as the step's norm and, with clipping on, sets
+ * the coefficient.  With global_overflow = 0 it must be finite and not below
+ * this rank's own norm (relative slack 1e-9); with 1 it is only reported.
+ * *out (may be NULL) gets the merged result.  Errors: STATE (dead handle, not
+ * checked), INVALID_ARG (the handle is left unchanged).
  */
 zero_status zero_overflow_merge(zero_shard_t h, int32_t global_overflow, double global_grad_norm,
                                 zero_step_info* out);
@@ -427,7 +435,8 @@ zero_status zero_shard_inline_folds(zero_shard_t h, int64_t* count);
 zero_status zero_shard_get_counters(zero_shard_t h, int64_t* step_t, double* scale,
                                     int64_t* good_steps);
 /* Restore them between steps (phase must be idle, device-resident flow not
- * active).  step_t >= 0, scale > 0, good_steps >= 0. */
+ * active).  step_t >= 0, good_steps >= 0, scale as init_scale of
+ * zero_loss_scale_cfg. */
 zero_status zero_shard_set_counters(zero_shard_t h, int64_t step_t, double scale,
                                     int64_t good_steps);
 

@@ -229,6 +229,10 @@ def clip_coef(sumsq: float, max_norm: float) -> float:
 
 
 def adam_scalars(hp: AdamHP, t: int, scale: float, coef: float = 1.0) -> np.ndarray:
+    # the update uses the fp32 roundings of the betas; one that rounds to 1
+    # leaves a zero bias correction (Adam needs beta < 1)
+    if not (np.float32(hp.beta1) < 1 and np.float32(hp.beta2) < 1):
+        raise ValueError("betas must stay below 1 after rounding to fp32")
     out = np.empty(11, np.float32)
     lib().oracle_adam_scalars(hp.beta1, hp.beta2, hp.lr, hp.eps, hp.weight_decay,
                               hp.bias_correction, t, scale, _p32(out))

@@ -33,8 +33,9 @@
  *  - The reduce is the mean over the R contributions actually reduced, summed
  *    in fp32 in ascending contribution order starting from +0.0f.
  *  - The reduced gradient shard is stored in the 2-byte format (16 Psi/Nd
- *    ledger); overflow is any non-finite stored value; a step with overflow is
- *    skipped and, with dynamic scaling, halves the loss scale.
+ *    ledger); overflow is any non-finite stored or unscaled value; a step
+ *    with overflow is skipped and, with dynamic scaling, halves the loss
+ *    scale.
  *  - Weight decay is decoupled (AdamW form, scaled by lr) unless L2 mode is set.
  *  - Floating point: fp32 arithmetic as the pages fix for the optimizer state
  *    ("fp32 momentum, variance and parameter copy"); every operation rounds to
@@ -221,9 +222,12 @@ void oracle_bucket_reduce(int lp, int32_t n_contrib, const void* const* contribs
 
 /* ------------------------------------------------------------------------ */
 /* Unscale, overflow check and squared gradient norm over a stored shard.    */
-/* The pages are silent on loss scaling; reading: the flag is set when any    */
-/* stored 2-byte gradient is not finite, and sumsq adds the squares of the    */
-/* unscaled fp32 gradients in fp64.  Accumulates into *flag and *sumsq.       */
+/* The pages are silent on loss scaling; reading: the step unscales first and */
+/* then checks for inf/nan, so the flag is set when an unscaled fp32 value    */
+/* u = x * (1/scale) is not finite.  That covers every non-finite stored x    */
+/* (inf or NaN times any factor is inf or NaN) and also a finite x that       */
+/* unscales to inf under a scale below 1.  sumsq adds u*u in fp64.            */
+/* Accumulates into *flag and *sumsq.                                         */
 /* ------------------------------------------------------------------------ */
 
 void oracle_flag_sumsq(int lp, const void* g, int64_t n, float inv_scale,
@@ -233,8 +237,8 @@ void oracle_flag_sumsq(int lp, const void* g, int64_t n, float inv_scale,
     double s = *sumsq;
     for (int64_t i = 0; i < n; ++i) {
         float x = load_g(lp, g, i);
-        if (!isfinite(x)) f = 1;
         float u = x * inv_scale;
+        if (!isfinite(u)) f = 1;
         s += (double)u * (double)u;
     }
     *flag = f;

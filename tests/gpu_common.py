@@ -102,7 +102,8 @@ def run_gpu(w: synth.Workload, *, elems: Optional[int] = None, steps: Optional[i
             seed: int = 0, bucket_elems: Optional[int] = None, hp=None,
             ls: Optional[zs.LossScaleCfg] = None, keep_contribs: bool = True,
             offsets: Optional[dict] = None, hook=None, flow: str = "sync",
-            max_norm: float = 0.0, scale_of=None, inline_folds: Optional[list] = None) -> GpuRun:
+            max_norm: float = 0.0, scale_of=None, inline_folds: Optional[list] = None,
+            init_hook=None) -> GpuRun:
     """Run `steps` owner-rank steps of workload w (its first `elems` shard
     elements) through the C ABI on cuda:0.  offsets maps an array name
     ('master', 'm', 'v', 'grad', 'param', 'contrib') to an element offset of its
@@ -115,7 +116,9 @@ def run_gpu(w: synth.Workload, *, elems: Optional[int] = None, steps: Optional[i
     step's result is read; the others are None).  The workload's opt picks Adam
     or SGD; max_norm > 0 turns on global-norm clipping.  inline_folds, when
     given, receives the handle's count of device steps whose update folded the
-    partials itself."""
+    partials itself.  init_hook(master0, m0, v0) may edit the initial fp32
+    state (m0 / v0 None where the optimizer keeps no such array) before it is
+    copied into the shard; the 2-byte param starts as its rounding."""
     dev = torch.device("cuda", 0)
     S = w.shard if elems is None else elems
     steps = w.steps if steps is None else steps
@@ -135,6 +138,8 @@ def run_gpu(w: synth.Workload, *, elems: Optional[int] = None, steps: Optional[i
         m0 = None
     if not w.has_v:
         v0 = None
+    if init_hook is not None:
+        init_hook(master0, m0, v0)
     master = alloc("master", torch.float32)
     master.copy_(master0)
     m = v = None
@@ -238,11 +243,17 @@ def lp_is_nan(bits: np.ndarray, lp: str) -> np.ndarray:
 
 
 def max_rel(a: np.ndarray, b: np.ndarray) -> float:
+    """Largest |a - b| / max(|b|, FLT_MIN); equal values (infinities of one
+    sign included) and NaN against NaN count 0, any other non-finite pair inf."""
     if a.size == 0:
         return 0.0
     a64, b64 = a.astype(np.float64), b.astype(np.float64)
     den = np.maximum(np.abs(b64), np.finfo(np.float32).tiny)
-    return float(np.max(np.abs(a64 - b64) / den))
+    with np.errstate(invalid="ignore", over="ignore"):
+        err = np.abs(a64 - b64) / den
+    err = np.where((a64 == b64) | (np.isnan(a64) & np.isnan(b64)), 0.0, err)
+    err = np.where(np.isnan(err), np.inf, err)
+    return float(np.max(err))
 
 
 def compare(w: synth.Workload, g: GpuRun, st, oinfos, tag: str = "") -> dict:

@@ -113,7 +113,9 @@ def test_init_rejects_bad_desc_before_device_work(over):
 @pytest.mark.parametrize("field,val", [("lr", -1.0), ("lr", float("nan")), ("beta1", 1.0),
                                        ("beta2", -0.1), ("eps", 0.0), ("eps", 1e-50),
                                        ("weight_decay", -0.1), ("bias_correction", 2),
-                                       ("wd_mode", 5), ("initial_step", -1)])
+                                       ("wd_mode", 5), ("initial_step", -1),
+                                       # below 1 in fp64 but 1.0 after rounding to fp32
+                                       ("beta1", 0.99999999), ("beta2", 1.0 - 1e-9)])
 def test_init_rejects_bad_hparams(field, val):
     hp = zs.ZeroAdamHParams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 0, 0)
     setattr(hp, field, val)
@@ -124,7 +126,11 @@ def test_init_rejects_bad_hparams(field, val):
 
 
 @pytest.mark.parametrize("field,val", [("init_scale", 0.0), ("init_scale", float("inf")),
-                                       ("dynamic", 2), ("growth_interval", 0), ("min_scale", -1.0)])
+                                       ("init_scale", float("nan")),
+                                       ("dynamic", 2), ("growth_interval", 0), ("min_scale", -1.0),
+                                       # fp32(1/scale) would be inf, or 0
+                                       ("init_scale", 1e-40), ("min_scale", 2e-39),
+                                       ("init_scale", 2e45), ("min_scale", 1e46)])
 def test_init_rejects_bad_loss_scale(field, val):
     ls = zs.ZeroLossScaleCfg(1024.0, 1, 1000, 1.0)
     setattr(ls, field, val)
@@ -239,3 +245,44 @@ def test_sgd_entry_points_reject_dead_handles():
                                  ctypes.byref(h)) == zs.ZERO_ERR_INVALID_ARG
     assert L.zero_shard_init_sgd(ctypes.byref(_desc(exp_avg_sq=0)), None, ctypes.byref(GOOD_LS),
                                  ctypes.byref(h)) == zs.ZERO_ERR_INVALID_ARG
+
+
+def test_init_accepts_scales_at_the_fp32_reciprocal_limits():
+    """3e-39 and 1.4e45 keep a finite, non-zero fp32 reciprocal: the loss-scale
+    check passes them, and init goes on to the device queries (which fail here
+    without a GPU, with another status than INVALID_ARG for the scale)."""
+    for init, mn in ((3e-39, 3e-39), (1.4e45, 1.0)):
+        ls = zs.ZeroLossScaleCfg(init, 1, 1000, mn)
+        h = ctypes.c_void_p()
+        s = zs.lib().zero_shard_init(ctypes.byref(_desc()), ctypes.byref(GOOD_HP),
+                                     ctypes.byref(ls), ctypes.byref(h))
+        assert "loss scale" not in zs.zero_last_error(), (init, s, zs.zero_last_error())
+
+
+def test_binding_refuses_bad_contribution_tensors():
+    """The binding checks each contribution tensor against the handle's storage
+    dtype and the elements the call reads, before any address crosses the ABI
+    (the library's own range check sees whole allocations, not tensors)."""
+    import torch
+    h = 0x5EED0
+    zs._handles[h] = (torch.float16, 1000)
+    try:
+        good = torch.zeros(1000, dtype=torch.float16)
+        cases = [
+            (lambda: zs.zero_bucket_reduce(h, [torch.zeros(100, dtype=torch.float32)], 0, 100),
+             TypeError),
+            (lambda: zs.zero_bucket_reduce(h, [good[:50]], 0, 100), ValueError),
+            (lambda: zs.zero_bucket_reduce(h, [good[::2]], 0, 100), ValueError),
+            (lambda: zs.zero_step_device(h, [good, good[:999]]), ValueError),
+            (lambda: zs.zero_step_device(h, [good.to(torch.bfloat16)]), TypeError),
+            (lambda: zs.reduce_buckets(h, [good[:999]], 1000, 100), ValueError),
+        ]
+        for call, err in cases:
+            with pytest.raises(err):
+                call()
+        # the right dtype, shape and size passes the binding's checks and
+        # fails only at the device test (a CPU tensor here)
+        with pytest.raises(ValueError, match="GPU"):
+            zs.zero_bucket_reduce(h, [good[:100]], 0, 100)
+    finally:
+        zs._handles.pop(h, None)

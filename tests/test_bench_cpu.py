@@ -55,11 +55,15 @@ def test_kernel_code_hash_ignores_comments_only():
     assert len(kernel_code_hash()) == 16
 
 
-def test_variant_builds_and_traffic_of_variants(monkeypatch):
+def test_variant_builds_and_traffic_of_variants(monkeypatch, tmp_path):
     from zero_dp_sharded_amd import build as B
     with pytest.raises(ValueError):
         B.build_variant({"NOT_A_SHAPE": 1}, "/nonexistent")      # refused before compiling
-    assert bench.measured_traffic("128b", 2_000_000_000) is not None
+    d = {"kernel_code_sha256_16": bench.kernel_code_hash(), "elems_per_launch": 2_000_000_000,
+         "hbm_bytes_per_launch": 5.6e10}
+    (tmp_path / "traffic_128b.json").write_text(json.dumps(d))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.measured_traffic("128b", 2_000_000_000) == 5.6e10
     monkeypatch.setenv("ZERO_SHARD_LIB", "/some/variant/libzeroshard.so")
     assert bench.measured_traffic("128b", 2_000_000_000) is None  # counters are the in-tree build's
 

@@ -135,6 +135,40 @@ def test_merge_argument_checks():
         zs.zero_shard_destroy(h)
 
 
+def test_merge_refuses_bad_global_norms():
+    """An applied step takes the global norm for its clipping coefficient, so a
+    clean merge refuses a norm that is NaN, infinite, negative or below this
+    rank's own norm (INVALID_ARG, the handle unchanged); an overflowing merge
+    only reports it."""
+    n = 4096
+    dev = torch.device("cuda", 0)
+    t = [torch.zeros(n, device=dev) for _ in range(3)]
+    g = torch.full((n,), 0.5, dtype=torch.float16, device=dev)
+    p = torch.zeros(n, dtype=torch.float16, device=dev)
+    h = zs.zero_shard_init(*t, g, p, psi=n, nd=1, rank=0, bucket_elems=n,
+                           hp=zs.AdamHParams(), ls=zs.LossScaleCfg(init_scale=1.0))
+    try:
+        zs.zero_shard_set_clip(h, 1.0)
+        chk = zs.zero_overflow_check(h)
+        own = chk.grad_norm
+        assert chk.overflow == 0 and own == pytest.approx(32.0)     # sqrt(4096 * 0.25)
+        for bad in (float("nan"), float("inf"), -1.0, 0.5 * own, own * (1 - 1e-6)):
+            with pytest.raises(zs.ZeroError) as e:
+                zs.zero_overflow_merge(h, 0, bad)
+            assert e.value.status == zs.ZERO_ERR_INVALID_ARG, bad
+            assert zs.zero_overflow_check(h).grad_norm == own          # handle unchanged
+        info = zs.zero_overflow_merge(h, 0, own * 2.0)
+        assert info.overflow == 0 and info.grad_norm == own * 2.0
+        assert zs.zero_adam_step(h).step_t == 1
+        # an overflowing global step: the norm is only reported
+        zs.zero_overflow_check(h)
+        info = zs.zero_overflow_merge(h, 1, float("nan"))
+        assert info.overflow == 1 and np.isnan(info.grad_norm)
+        assert zs.zero_adam_step(h).skipped == 1
+    finally:
+        zs.zero_shard_destroy(h)
+
+
 def test_pos_clipping_uses_the_merged_global_norm():
     """With clipping on, every rank clips with the coefficient of the merged
     global norm: the concatenated slices match the oracle's unsharded clipped

@@ -48,8 +48,11 @@ MUTATIONS = [
     ("bias correction of step t-1", "for (int64_t k = 0; k < t; ++k) {",
      "for (int64_t k = 1; k < t; ++k) {"),
     ("1-beta1 from beta2", "out[2] = 1.0f - b1;", "out[2] = 1.0f - b2;"),
-    ("flag misses inf", "if (!isfinite(x)) f = 1;", "if (isnan(x)) f = 1;"),
+    ("flag misses inf", "if (!isfinite(u)) f = 1;", "if (isnan(u)) f = 1;"),
     ("norm not unscaled", "float u = x * inv_scale;", "float u = x;"),
+    ("flag tests the stored value, not the unscaled one",
+     "float u = x * inv_scale;\n        if (!isfinite(u)) f = 1;",
+     "float u = x * inv_scale;\n        if (!isfinite(x)) f = 1;"),
     ("scale not halved", "double s = *scale / 2.0;", "double s = *scale;"),
     ("reduce divides by R", "store_g(lp, out, i, acc * inv_r);",
      "store_g(lp, out, i, acc / (float)n_contrib);"),

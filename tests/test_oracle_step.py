@@ -150,6 +150,62 @@ def test_flag_and_norm(oracle):
     assert oracle.flag_sumsq(BF16, b, 1.0)[0] == 1
 
 
+def test_flag_on_unscaled_overflow(oracle):
+    """The check runs on the unscaled values: with a loss scale below 1 a finite
+    stored gradient can unscale past the fp32 range, and that is an overflow.
+    bf16 0x7EFF is 0x1.FEp126, twice it is 0x1.FEp127 (below FLT_MAX, finite);
+    bf16 0x7F00 is 2^127, twice it is 2^128 (inf)."""
+    b = np.full(8, 0x3F80, np.uint16)
+    b[3] = 0x7EFF
+    f, s = oracle.flag_sumsq(BF16, b, 0.5)
+    assert f == 0
+    big = 2.0 * float(np.array([0x7EFF << 16], np.uint32).view(np.float32)[0])
+    assert big == float.fromhex("0x1.FEp127")
+    assert s == 7 * 4.0 + big * big
+    b[3] = 0x7F00
+    assert oracle.flag_sumsq(BF16, b, 0.5)[0] == 1
+    # fp32 storage: 1e38 unscaled by 4 is 4e38 > FLT_MAX
+    x = np.array([1.0, 1e38, -2.0], np.float32)
+    assert oracle.flag_sumsq(FP32, x, 0.25)[0] == 1
+    assert oracle.flag_sumsq(FP32, x, 1.0)[0] == 0
+    # fp16: 65504 * 2^120 > FLT_MAX, 65504 * 2^100 is not
+    h = f16_bits([65504.0, 1.0])
+    assert oracle.flag_sumsq(FP16, h, 2.0 ** -120)[0] == 1
+    assert oracle.flag_sumsq(FP16, h, 2.0 ** -100)[0] == 0
+
+
+def test_unscaled_overflow_skips_the_step(oracle):
+    """A whole step whose only fault is a finite gradient that unscales to inf:
+    skipped, state bitwise unchanged, t unchanged, the scale halved."""
+    hp = oracle.AdamHP(lr=1e-3)
+    ls = oracle.LossScale(init_scale=0.5, dynamic=1, min_scale=0.125)
+    rng = np.random.default_rng(11)
+    n = 64
+    master = rng.standard_normal(n).astype(np.float32) * 0.02
+    st = oracle.new_state(BF16, master, np.zeros(n, np.float32), np.zeros(n, np.float32), hp, ls)
+    before = st.copy()
+    c0 = oracle.f32_to_lp(BF16, rng.standard_normal(n).astype(np.float32) * 1e-3)
+    c0[17] = oracle.f32_to_lp(BF16, np.array([3e38], np.float32))[0]
+    info = oracle.step(st, [c0], n, hp, ls)
+    assert (info.overflow, info.skipped, info.step_t) == (1, 1, 0)
+    assert (info.scale_used, info.scale_next) == (0.5, 0.25)
+    assert not np.isfinite(info.grad_norm)
+    for a, b in ((st.master, before.master), (st.m, before.m), (st.v, before.v)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(st.param, before.param)
+    # the same gradient at scale 1 is an ordinary step
+    st2 = oracle.new_state(BF16, master, np.zeros(n, np.float32), np.zeros(n, np.float32), hp,
+                           oracle.LossScale(init_scale=1.0))
+    info2 = oracle.step(st2, [c0], n, hp, oracle.LossScale(init_scale=1.0))
+    assert (info2.overflow, info2.step_t) == (0, 1) and np.isfinite(info2.grad_norm)
+    # two such contributions overflow the fp32 accumulator itself (6e38): the
+    # stored mean is inf, an overflow at any scale
+    st3 = oracle.new_state(BF16, master, np.zeros(n, np.float32), np.zeros(n, np.float32), hp,
+                           oracle.LossScale(init_scale=1.0))
+    info3 = oracle.step(st3, [c0, c0.copy()], n, hp, oracle.LossScale(init_scale=1.0))
+    assert st3.grad[17] == 0x7F80 and info3.overflow == 1
+
+
 # ------------------------------------------------------------------ Adam
 
 def _adam_once(oracle, g_bits, master, m, v, hp, t, scale=1.0, lp=FP16):

@@ -236,6 +236,28 @@ def _dptr(x) -> int:
     return x.data_ptr()
 
 
+# Storage dtype and shard size of each live handle made through this binding,
+# so contribution tensors can be checked before their addresses cross the ABI
+# (the library sees only allocations, not the tensors inside them).
+_handles = {}
+
+
+def _contrib_ptrs(h: int, contribs: Sequence, n_elems: int, who: str) -> list:
+    """Addresses of contribution tensors (ints pass through unchecked); each
+    tensor must be a contiguous GPU tensor of the handle's storage dtype with
+    at least n_elems elements."""
+    meta = _handles.get(h)
+    out = []
+    for r, c in enumerate(contribs):
+        if isinstance(c, int):
+            out.append(c)
+            continue
+        if meta is not None:
+            _check_tensor(f"{who}: contribution {r}", c, meta[0], n_elems)
+        out.append(_dptr(c))
+    return out
+
+
 def _ledger(out: ZeroStateBytes) -> dict:
     d = {}
     for name, _ in ZeroStateBytes._fields_:
@@ -264,12 +286,12 @@ def _check_tensor(name, t, dtype, n):
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name}: expected a torch tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name}: must live on the GPU, got {t.device}")
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
     if not t.is_contiguous() or t.numel() < n:
         raise ValueError(f"{name}: must be contiguous with at least {n} elements")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must live on the GPU, got {t.device}")
 
 
 def _lp_of(grad_shard):
@@ -309,6 +331,7 @@ def zero_shard_init(master, exp_avg, exp_avg_sq, grad_shard, param_shard, *, psi
     h = _vp()
     _check(lib().zero_shard_init(ctypes.byref(desc), ctypes.byref(hp.to_c()),
                                  ctypes.byref(ls.to_c()), ctypes.byref(h)), "zero_shard_init")
+    _handles[h.value] = (grad_shard.dtype, -(-psi // nd))
     return h.value
 
 
@@ -321,6 +344,7 @@ def zero_shard_init_sgd(master, momentum_buf, grad_shard, param_shard, *, psi: i
     _check(lib().zero_shard_init_sgd(ctypes.byref(desc), ctypes.byref(hp.to_c()),
                                      ctypes.byref(ls.to_c()), ctypes.byref(h)),
            "zero_shard_init_sgd")
+    _handles[h.value] = (grad_shard.dtype, -(-psi // nd))
     return h.value
 
 
@@ -328,7 +352,8 @@ def zero_bucket_reduce(h: int, contribs: Sequence, bucket_off: int, bucket_len: 
                        stream=None) -> None:
     """contribs: R tensors (or device addresses), each holding this bucket's
     bucket_len gradients of one contribution in the storage format."""
-    arr = (_vp * len(contribs))(*[_dptr(c) for c in contribs])
+    ptrs = _contrib_ptrs(h, contribs, bucket_len, "zero_bucket_reduce")
+    arr = (_vp * len(ptrs))(*ptrs)
     _check(lib().zero_bucket_reduce(h, arr, len(contribs), bucket_off, bucket_len,
                                     _stream_ptr(stream)), "zero_bucket_reduce")
 
@@ -393,7 +418,9 @@ def zero_step_device(h: int, contribs: Optional[Sequence] = None, stream=None) -
     if contribs is None:
         arr, n = None, 0
     else:
-        arr, n = (_vp * len(contribs))(*[_dptr(c) for c in contribs]), len(contribs)
+        meta = _handles.get(h)
+        ptrs = _contrib_ptrs(h, contribs, meta[1] if meta else 0, "zero_step_device")
+        arr, n = (_vp * len(ptrs))(*ptrs), len(ptrs)
     _check(lib().zero_step_device(h, arr, n, _stream_ptr(stream)), "zero_step_device")
 
 
@@ -425,16 +452,19 @@ def zero_shard_set_counters(h: int, step_t: int, scale: float, good_steps: int) 
 
 def zero_shard_destroy(h: int) -> None:
     _check(lib().zero_shard_destroy(h), "zero_shard_destroy")
+    _handles.pop(h, None)
 
 
 def reduce_buckets(h: int, contribs: Sequence, shard_elems: int, bucket_elems: int,
                    stream=None, esz: Optional[int] = None) -> None:
     """Submit every C_B bucket of a step in ascending order.  contribs are R
-    shard-sized tensors (or addresses, with esz the bytes per element); bucket b
-    passes the views [off, off + len)."""
+    shard-sized tensors (or addresses); bucket b passes the views
+    [off, off + len).  esz, the bytes per element, defaults to the handle's
+    storage format (2 for an address whose handle this binding did not make)."""
+    meta = _handles.get(h)
     if esz is None:
-        esz = 2 if isinstance(contribs[0], int) else contribs[0].element_size()
-    ptrs = [_dptr(c) for c in contribs]
+        esz = meta[0].itemsize if meta is not None else 2
+    ptrs = _contrib_ptrs(h, contribs, shard_elems, "reduce_buckets")
     for off in range(0, shard_elems, bucket_elems):
         ln = min(bucket_elems, shard_elems - off)
         zero_bucket_reduce(h, [p + off * esz for p in ptrs], off, ln, stream)

@@ -146,7 +146,7 @@ struct ContribPtrs {
 
 // Result of a step's check, written by the last fold launch.
 struct CheckResult {
-    double sumsq;          // squared unscaled norm; NaN when a stored value was not finite
+    double sumsq;          // squared unscaled norm; NaN when an unscaled value was not finite
     float clip;            // global-norm clipping coefficient (1 when off or on overflow)
     float pad;
 };
@@ -184,7 +184,7 @@ struct PrepareArgs {
 // elements) that are 16-byte aligned in every contribution and in `out`.
 // vec_ok = 0 selects the element-wise path.  Workgroup b writes
 // partial[slot_base + b]: the fp64 sum of the squared unscaled stored values
-// of its elements, or NaN if any stored value is not finite.  The unscale
+// of its elements, or NaN if any unscaled value is not finite.  The unscale
 // factor is inv_scale, or dev->inv_scale when dev is set.
 struct ReduceLaunch {
     ContribPtrs c;

@@ -44,42 +44,30 @@ typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef __bf16 b4 __attribute__((ext_vector_type(4)));
 typedef float f8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Per storage format: element type T and its bit pattern type, the 16-byte run
-// VW of W elements with its fp32 image FW and bit view BW, the 4-element group
-// V4 of the update kernels, and the exponent mask that marks inf/NaN.
+// Per storage format: element type T, the 16-byte run VW of W elements with
+// its fp32 image FW, and the 4-element group V4 of the update kernels.
 template <int LP> struct Fmt;
 template <> struct Fmt<1> {            // IEEE binary16
     using T = _Float16;
-    using Bits = unsigned short;
     static constexpr int W = 8;
     using VW = h8;
     using FW = f8;
-    using BW = u16x8;
     using V4 = h4;
-    static constexpr Bits kExp = 0x7c00;
 };
 template <> struct Fmt<2> {            // bfloat16
     using T = __bf16;
-    using Bits = unsigned short;
     static constexpr int W = 8;
     using VW = b8;
     using FW = f8;
-    using BW = u16x8;
     using V4 = b4;
-    static constexpr Bits kExp = 0x7f80;
 };
 template <> struct Fmt<3> {            // IEEE binary32
     using T = float;
-    using Bits = unsigned int;
     static constexpr int W = 4;
     using VW = f4;
     using FW = f4;
-    using BW = u32x4;
     using V4 = f4;
-    static constexpr Bits kExp = 0x7f800000u;
 };
 
 template <typename V>
@@ -126,31 +114,32 @@ __device__ __forceinline__ float pin_f32(float x)
 
 // ----------------------------------------------------------------- check
 
+// The check runs on the unscaled value u = f32(stored) * fp32(1/scale): the
+// flag marks a u that is not finite.  A stored inf or NaN always gives one,
+// and so does a finite stored value that unscales past the fp32 range under a
+// loss scale below 1.
+__device__ __forceinline__ void check_u(float u, int& flag, double& ss)
+{
+    flag |= (__builtin_bit_cast(unsigned int, u) & 0x7f800000u) == 0x7f800000u;
+    ss += (double)u * (double)u;
+}
+
 // Overflow flag and squared unscaled norm of one stored run.
 template <int LP>
 __device__ __forceinline__ void check_v(typename Fmt<LP>::VW o, float inv_scale, int& flag,
                                         double& ss)
 {
     using F = Fmt<LP>;
-    const typename F::BW bits = __builtin_bit_cast(typename F::BW, o);
     const typename F::FW of = __builtin_convertvector(o, typename F::FW);
 #pragma unroll
-    for (int k = 0; k < F::W; ++k) {
-        flag |= (bits[k] & F::kExp) == F::kExp;
-        const float u = of[k] * inv_scale;
-        ss += (double)u * (double)u;
-    }
+    for (int k = 0; k < F::W; ++k) check_u(of[k] * inv_scale, flag, ss);
 }
 
 template <int LP>
 __device__ __forceinline__ void check_s(typename Fmt<LP>::T o, float inv_scale, int& flag,
                                         double& ss)
 {
-    using F = Fmt<LP>;
-    const typename F::Bits bits = __builtin_bit_cast(typename F::Bits, o);
-    flag |= (bits & F::kExp) == F::kExp;
-    const float u = static_cast<float>(o) * inv_scale;
-    ss += (double)u * (double)u;
+    check_u(static_cast<float>(o) * inv_scale, flag, ss);
 }
 
 // One fp64 partial per workgroup: the sum of its lanes' squares, or NaN when
@@ -366,14 +355,14 @@ __global__ __launch_bounds__(kScalarBlock) void scan_elem_kernel(ScanLaunch L, R
 }
 
 // Decide the checked step in device memory, as the host flows do: overflow
-// when the check's sum is NaN; an applied step advances t and the fp64 beta
+// when the check's sum is not finite (a flagged partial is NaN); an applied step advances t and the fp64 beta
 // powers and sets the bias corrections of its update; the loss scale halves on
 // overflow (not below min_scale) and doubles after growth_interval clean
 // steps.  The update reads upd_inv_scale (this step's), the next check
 // inv_scale (the next step's).  One lane runs it.
 __device__ void prepare_step(DevState* d, double ss, const PrepareArgs& a)
 {
-    const bool overflow = __builtin_isnan(ss);
+    const bool overflow = !__builtin_isfinite(ss);
     DevState s = *d;
     s.last_sumsq = ss;
     s.last_scale = s.scale;
@@ -405,12 +394,12 @@ __device__ void prepare_step(DevState* d, double ss, const PrepareArgs& a)
 }
 
 // Textbook global-norm clipping coefficient min(1, max_norm / (norm + 1e-6)),
-// in fp64 and rounded to fp32; 1 when clipping is off, and for a NaN sum
-// (overflow), which fails the comparison.
+// in fp64 and rounded to fp32; 1 when clipping is off or the sum is not
+// finite (overflow: the step is skipped).
 __device__ __forceinline__ float clip_coef(double sumsq, double max_norm)
 {
     float coef = 1.0f;
-    if (max_norm > 0.0) {
+    if (max_norm > 0.0 && __builtin_isfinite(sumsq)) {
         const double c = max_norm / (sqrt(sumsq) + 1e-6);
         if (c < 1.0) coef = (float)c;
     }
@@ -479,7 +468,7 @@ __device__ __forceinline__ StepVals step_vals(const StepSource& src, float inv_s
     StepVals v{inv_scale, bc1, bc2, src.clip, false};
     if (src.res != nullptr) {
         v.clip = src.res->clip;
-        if (src.gate) v.skip = __builtin_isnan(src.res->sumsq);
+        if (src.gate) v.skip = !__builtin_isfinite(src.res->sumsq);
     }
     if (src.dev != nullptr) {
         v.inv_scale = src.dev->upd_inv_scale;

@@ -112,6 +112,15 @@ bool live(zero_shard_t h)
 
 bool finite_pos(double x) { return std::isfinite(x) && x > 0.0; }
 
+// A loss scale the kernels can unscale by: finite, positive, and with an fp32
+// reciprocal that is neither 0 nor inf.
+bool scale_ok(double s)
+{
+    if (!finite_pos(s)) return false;
+    const float inv = (float)(1.0 / s);
+    return std::isfinite(inv) && inv > 0.0f;
+}
+
 // Calls that launch work must run with the handle's device current and, for a
 // non-default stream, on a stream of that device; otherwise the kernels would
 // reach this device's arrays from another GPU.
@@ -141,6 +150,10 @@ zero_status check_hparams(const zero_adam_hparams* hp)
         return fail(ZERO_ERR_INVALID_ARG, "adam hparams: lr must be finite and >= 0");
     if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
         return fail(ZERO_ERR_INVALID_ARG, "adam hparams: betas must lie in [0, 1)");
+    // the kernels use the fp32 roundings; a beta within 3e-8 of 1 rounds to 1,
+    // its bias correction 1 - beta^t to 0, and the update to NaN
+    if (!((float)hp->beta1 < 1.0f) || !((float)hp->beta2 < 1.0f))
+        return fail(ZERO_ERR_INVALID_ARG, "adam hparams: betas must stay below 1 in fp32");
     if (!finite_pos(hp->eps) || (float)hp->eps <= 0.0f)
         return fail(ZERO_ERR_INVALID_ARG, "adam hparams: eps must be > 0 in fp32");
     if (!(std::isfinite(hp->weight_decay) && hp->weight_decay >= 0.0))
@@ -157,8 +170,10 @@ zero_status check_hparams(const zero_adam_hparams* hp)
 zero_status check_ls(const zero_loss_scale_cfg* ls)
 {
     if (!ls) return fail(ZERO_ERR_INVALID_ARG, "loss scale: NULL");
-    if (!finite_pos(ls->init_scale) || !finite_pos(ls->min_scale))
-        return fail(ZERO_ERR_INVALID_ARG, "loss scale: init_scale and min_scale must be finite and > 0");
+    if (!scale_ok(ls->init_scale) || !scale_ok(ls->min_scale))
+        return fail(ZERO_ERR_INVALID_ARG,
+                    "loss scale: init_scale and min_scale must be finite and > 0 with a finite, "
+                    "non-zero fp32 reciprocal");
     if (ls->dynamic != 0 && ls->dynamic != 1)
         return fail(ZERO_ERR_INVALID_ARG, "loss scale: dynamic must be 0 or 1");
     if (ls->growth_interval < 1)
@@ -704,15 +719,15 @@ static zero_status launch_check(zero_shard_s* h, hipStream_t s, const char* who)
     return ZERO_OK;
 }
 
-// The step's result from the pinned copy: overflow when the total is NaN (a
-// non-finite stored gradient makes its workgroup partial NaN; finite values
-// alone never produce NaN).
+// The step's result from the pinned copy: overflow when the total is not
+// finite (a non-finite unscaled gradient makes its workgroup partial NaN; the
+// fp64 squares of finite fp32 values cannot sum to inf).
 static zero_step_info read_check(zero_shard_s* h)
 {
     zero_step_info info;
     std::memset(&info, 0, sizeof(info));
     const double total = h->host_result->sumsq;
-    info.overflow = std::isnan(total) ? 1 : 0;
+    info.overflow = std::isfinite(total) ? 0 : 1;
     info.skipped = info.overflow;
     info.step_t = h->t;
     info.grad_norm = std::sqrt(total);
@@ -997,6 +1012,15 @@ zero_status zero_overflow_merge(zero_shard_t h, int32_t global_overflow, double 
     if (global_overflow < h->check.overflow)
         return fail(ZERO_ERR_INVALID_ARG,
                     "overflow_merge: this rank overflowed; the global flag cannot be 0");
+    // an applied step takes its clipping coefficient from the global norm,
+    // which sums this rank's squares with the others': finite, >= 0 and not
+    // below this rank's own norm (to a relative 1e-9, the rounding of the sum)
+    if (!global_overflow &&
+        !(std::isfinite(global_grad_norm) && global_grad_norm >= 0.0 &&
+          global_grad_norm >= h->check.grad_norm * (1.0 - 1e-9)))
+        return fail(ZERO_ERR_INVALID_ARG,
+                    "overflow_merge: global_grad_norm %g must be finite and not below this "
+                    "rank's norm %g", global_grad_norm, h->check.grad_norm);
     h->check.overflow = global_overflow;
     h->check.skipped = global_overflow;
     h->check.grad_norm = global_grad_norm;
@@ -1097,7 +1121,7 @@ zero_status zero_shard_set_counters(zero_shard_t h, int64_t step_t, double scale
     if (!live(h)) return fail(ZERO_ERR_STATE, "set_counters: not a live handle");
     if (h->device_mode)
         return fail(ZERO_ERR_STATE, "%s: device-resident flow active; call zero_device_end", "set_counters");
-    if (step_t < 0 || !finite_pos(scale) || good_steps < 0)
+    if (step_t < 0 || !scale_ok(scale) || good_steps < 0)
         return fail(ZERO_ERR_INVALID_ARG, "set_counters: values out of range");
     if (h->phase != kIdle) return fail(ZERO_ERR_STATE, "set_counters: a step is in progress");
     h->t = step_t;
@@ -1254,7 +1278,7 @@ zero_status zero_device_end(zero_shard_t h, void* stream, zero_step_info* out)
     info.scale_next = h->scale;
     info.scale_used = h->scale;
     if (st.steps_run > 0) {
-        info.overflow = std::isnan(st.last_sumsq) ? 1 : 0;
+        info.overflow = std::isfinite(st.last_sumsq) ? 0 : 1;
         info.skipped = info.overflow;
         info.grad_norm = std::sqrt(st.last_sumsq);
         info.scale_used = st.last_scale;
