@@ -424,6 +424,38 @@ zero_status zero_step_device(zero_shard_t h, const void* const* contribs, int32_
                              void* stream);
 zero_status zero_device_end(zero_shard_t h, void* stream, zero_step_info* out);
 
+/*
+ * For callers that cannot allocate device memory (code that may not call
+ * hipMalloc: serving loops and harnesses that forbid allocation): one whole
+ * synchronous Adam step on a shard with no handle and no allocation.  The
+ * result equals that of a handle created over the same desc, hp and ls, with
+ * its counters set to *step_t, *scale and *good_steps and its clipping limit
+ * to max_grad_norm, running zero_bucket_reduce over every C_B bucket (or, with
+ * contribs = NULL and n_contrib = 0, the scan of a caller-filled grad_shard),
+ * zero_overflow_check and zero_adam_step.  contribs as for zero_step_device
+ * (n_contrib device pointers, each to S elements).  *step_t, *scale and
+ * *good_steps are the counters before the step (as zero_shard_get_counters
+ * returns them) and are updated in place; hp->initial_step and
+ * ls->init_scale are not used.  *out (may be NULL) gets the step's result.
+ * The check's partials, its fold and its result live in a 4 MiB static array
+ * of device memory, one per GPU, held until the process ends: a shard whose
+ * check needs more than 523,232 partial slots is refused (about 267M 2-byte
+ * elements with 8 or more contributions, up to 800M with fewer and buckets of
+ * at least 3.9M elements, 134M fp32 elements with 8 or more).  Every call on a GPU shares that GPU's array, so calls that
+ * overlap on one GPU (other threads, or other streams before this call's
+ * update has run) race; calls in order on one stream do not.  Synchronises
+ * `stream` once (for the check); the update stays asynchronous on it.
+ * Errors: INVALID_ARG (as zero_shard_init and zero_step_device, counters out
+ * of range, max_grad_norm negative or not finite, a shard too large for the
+ * scratch), STATE (another device current than the stream's), UNSUPPORTED
+ * (device ordinal 64 or above), HIP.
+ */
+zero_status zero_adam_step_noalloc(const zero_shard_desc* desc, const zero_adam_hparams* hp,
+                                   const zero_loss_scale_cfg* ls, double max_grad_norm,
+                                   const void* const* contribs, int32_t n_contrib,
+                                   int64_t* step_t, double* scale, int64_t* good_steps,
+                                   void* stream, zero_step_info* out);
+
 /* Diagnostic: *count = the zero_step_device calls on this handle, since init,
  * that enqueued the fold inside the update instead of a fold launch.
  * Errors: STATE (dead handle), INVALID_ARG (count NULL). */

@@ -36,7 +36,7 @@ ABI_SYMBOLS = (
     "zero_bucket_reduce", "zero_overflow_check", "zero_overflow_merge", "zero_adam_step",
     "zero_adam_step_gated", "zero_sgd_step", "zero_sgd_step_gated", "zero_step_resolve",
     "zero_shard_set_clip", "zero_device_begin", "zero_step_device", "zero_device_end",
-    "zero_shard_inline_folds", "zero_shard_get_counters",
+    "zero_shard_inline_folds", "zero_adam_step_noalloc", "zero_shard_get_counters",
     "zero_shard_set_counters", "zero_shard_destroy", "zero_status_str", "zero_last_error",
     "zero_abi_version",
 )
@@ -122,6 +122,11 @@ def lib() -> ctypes.CDLL:
         L.zero_step_device.argtypes = [_vp, ctypes.POINTER(_vp), _i32, _vp]
         L.zero_device_end.argtypes = [_vp, _vp, ctypes.POINTER(ZeroStepInfo)]
         L.zero_shard_inline_folds.argtypes = [_vp, ctypes.POINTER(_i64)]
+        L.zero_adam_step_noalloc.argtypes = [
+            ctypes.POINTER(ZeroShardDesc), ctypes.POINTER(ZeroAdamHParams),
+            ctypes.POINTER(ZeroLossScaleCfg), _f64, ctypes.POINTER(_vp), _i32,
+            ctypes.POINTER(_i64), ctypes.POINTER(_f64), ctypes.POINTER(_i64), _vp,
+            ctypes.POINTER(ZeroStepInfo)]
         L.zero_shard_get_counters.argtypes = [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_f64),
                                               ctypes.POINTER(_i64)]
         L.zero_shard_set_counters.argtypes = [_vp, _i64, _f64, _i64]
@@ -436,6 +441,35 @@ def zero_device_end(h: int, stream=None) -> StepInfo:
     out = ZeroStepInfo()
     _check(lib().zero_device_end(h, _stream_ptr(stream), ctypes.byref(out)), "zero_device_end")
     return StepInfo.from_c(out)
+
+
+def zero_adam_step_noalloc(master, exp_avg, exp_avg_sq, grad_shard, param_shard, *, psi: int,
+                           nd: int, rank: int, bucket_elems: int, hp: AdamHParams,
+                           ls: LossScaleCfg, counters, contribs: Optional[Sequence] = None,
+                           max_grad_norm: float = 0.0, stream=None):
+    """One whole synchronous Adam step with no handle and no device allocation
+    (the check's scratch is the library's static array).  counters = (step_t,
+    scale, good_steps) before the step; returns (StepInfo, counters after)."""
+    desc = _desc_of(master, exp_avg, exp_avg_sq, grad_shard, param_shard, psi, nd, rank,
+                    bucket_elems)
+    S = -(-psi // nd)
+    if contribs is None:
+        arr, n = None, 0
+    else:
+        ptrs = []
+        for r, c in enumerate(contribs):
+            if not isinstance(c, int):
+                _check_tensor(f"zero_adam_step_noalloc: contribution {r}", c, grad_shard.dtype, S)
+            ptrs.append(_dptr(c))
+        arr, n = (_vp * len(ptrs))(*ptrs), len(ptrs)
+    t, sc, g = _i64(counters[0]), _f64(counters[1]), _i64(counters[2])
+    out = ZeroStepInfo()
+    _check(lib().zero_adam_step_noalloc(ctypes.byref(desc), ctypes.byref(hp.to_c()),
+                                        ctypes.byref(ls.to_c()), max_grad_norm, arr, n,
+                                        ctypes.byref(t), ctypes.byref(sc), ctypes.byref(g),
+                                        _stream_ptr(stream), ctypes.byref(out)),
+           "zero_adam_step_noalloc")
+    return StepInfo.from_c(out), (t.value, sc.value, g.value)
 
 
 def zero_shard_get_counters(h: int):

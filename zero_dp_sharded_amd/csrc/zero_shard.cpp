@@ -335,15 +335,12 @@ const char* zero_status_str(zero_status s)
 
 }  // extern "C"
 
-// Validation and creation shared by the Adam and the SGD handles.  `need_m` /
+// Host checks of a shard descriptor (no device access).  `need_m` /
 // `need_v`: whether exp_avg / exp_avg_sq must be given (1), must be NULL (-1)
-// or may be either (0).  On success the handle holds desc, S, opt and the loss
-// scale; the caller stores its hyper-parameters and t.
-static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m, int need_v,
-                               const zero_loss_scale_cfg* ls, const char* who,
-                               zero_shard_s** out)
+// or may be either (0).  Sets *S_out.
+static zero_status check_desc(const zero_shard_desc& d, int need_m, int need_v, const char* who,
+                              int64_t* S_out)
 {
-    const zero_shard_desc& d = *desc;
     if (d.psi < 1) return fail(ZERO_ERR_INVALID_ARG, "%s: psi must be >= 1", who);
     if (d.nd < 1) return fail(ZERO_ERR_INVALID_ARG, "%s: nd must be >= 1", who);
     if (d.rank < 0 || d.rank >= d.nd) return fail(ZERO_ERR_INVALID_ARG, "%s: rank outside [0, nd)", who);
@@ -373,7 +370,62 @@ static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m,
             if (arr[i] && arr[j] &&
                 overlaps((uintptr_t)arr[i], (size_t)S * el[i], (uintptr_t)arr[j], (size_t)S * el[j]))
                 return fail(ZERO_ERR_INVALID_ARG, "%s: shard arrays %d and %d overlap", who, i, j);
-    zero_status st = check_ls(ls);
+    *S_out = S;
+    return ZERO_OK;
+}
+
+// The runtime's view of the shard arrays (see device_range_ok).
+static zero_status check_desc_ranges(const zero_shard_desc& d, int64_t S, int dev, const char* who)
+{
+    const int esz = lp_bytes(d.lp);
+    const void* arr[5] = {d.master, d.exp_avg, d.exp_avg_sq, d.grad_shard, d.param_shard};
+    const int el[5] = {4, 4, 4, esz, esz};
+    for (int i = 0; i < 5; ++i) {
+        char why[160];
+        if (arr[i] && !device_range_ok(arr[i], (size_t)S * el[i], dev, why, sizeof(why)))
+            return fail(ZERO_ERR_INVALID_ARG, "%s: shard array %d (%lld elements) %s", who, i,
+                        (long long)S, why);
+    }
+    return ZERO_OK;
+}
+
+// LDS per CU and the largest dynamic LDS of one workgroup on device `dev`.
+static void query_lds(int dev, int* lds_cu, int* lds_blk)
+{
+    if (hipDeviceGetAttribute(lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess || *lds_cu <= 0)
+        *lds_cu = 160 * 1024;
+    if (hipDeviceGetAttribute(lds_blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess || *lds_blk <= 0)
+        *lds_blk = 64 * 1024;
+    (void)hipGetLastError();
+}
+
+// The dynamic LDS each kernel reserves to cap its workgroups per CU.
+static void set_lds_reserves(zero_shard_s* h, int lds_cu, int lds_blk)
+{
+    h->lds_adam = lds_reserve_for(lds_cu, lds_blk, zk::kAdamPerCU);
+    h->lds_sgd_mom = lds_reserve_for(lds_cu, lds_blk, zk::kSgdMomPerCU);
+    h->lds_sgd_plain = lds_reserve_for(lds_cu, lds_blk, zk::kSgdPlainPerCU);
+    h->lds_reduce = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCU);
+    h->lds_reduce_many = lds_reserve_for(
+        lds_cu, lds_blk, h->d.lp == ZERO_FP32 ? zk::kRedPerCUMany : zk::kRedPerCUMany2B);
+    h->lds_reduce_wide = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCUWide);
+    h->lds_scan = lds_reserve_for(lds_cu, lds_blk, zk::kScanPerCU);
+}
+
+// Validation and creation shared by the Adam and the SGD handles (need_m /
+// need_v as for check_desc).  On success the handle holds desc, S, opt and the
+// loss scale; the caller stores its hyper-parameters and t.
+static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m, int need_v,
+                               const zero_loss_scale_cfg* ls, const char* who,
+                               zero_shard_s** out)
+{
+    const zero_shard_desc& d = *desc;
+    int64_t S = 0;
+    zero_status st = check_desc(d, need_m, need_v, who, &S);
+    if (st != ZERO_OK) return st;
+    st = check_ls(ls);
     if (st != ZERO_OK) return st;
 
     // One fp64 partial per reduce workgroup of a step.  A bucket of len
@@ -393,12 +445,8 @@ static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m,
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "init: hipGetDevice");
-    for (int i = 0; i < 5; ++i) {
-        char why[160];
-        if (arr[i] && !device_range_ok(arr[i], (size_t)S * el[i], dev, why, sizeof(why)))
-            return fail(ZERO_ERR_INVALID_ARG, "%s: shard array %d (%lld elements) %s", who, i,
-                        (long long)S, why);
-    }
+    st = check_desc_ranges(d, S, dev, who);
+    if (st != ZERO_OK) return st;
 
     zero_shard_s* h = new (std::nothrow) zero_shard_s();
     if (!h) return fail(ZERO_ERR_OOM, "init: host allocation failed");
@@ -406,7 +454,7 @@ static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m,
     h->d = d;
     h->S = S;
     h->opt = opt;
-    h->esz = esz;
+    h->esz = lp_bytes(d.lp);
     h->ls = *ls;
     h->scale = ls->init_scale;
     h->good_steps = 0;
@@ -428,21 +476,8 @@ static zero_status init_common(const zero_shard_desc* desc, Opt opt, int need_m,
     h->dev_snapshot = h->dev + 1;
 
     int lds_cu = 0, lds_blk = 0;
-    if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
-            hipSuccess || lds_cu <= 0)
-        lds_cu = 160 * 1024;
-    if (hipDeviceGetAttribute(&lds_blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
-            hipSuccess || lds_blk <= 0)
-        lds_blk = 64 * 1024;
-    (void)hipGetLastError();
-    h->lds_adam = lds_reserve_for(lds_cu, lds_blk, zk::kAdamPerCU);
-    h->lds_sgd_mom = lds_reserve_for(lds_cu, lds_blk, zk::kSgdMomPerCU);
-    h->lds_sgd_plain = lds_reserve_for(lds_cu, lds_blk, zk::kSgdPlainPerCU);
-    h->lds_reduce = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCU);
-    h->lds_reduce_many = lds_reserve_for(
-        lds_cu, lds_blk, d.lp == ZERO_FP32 ? zk::kRedPerCUMany : zk::kRedPerCUMany2B);
-    h->lds_reduce_wide = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCUWide);
-    h->lds_scan = lds_reserve_for(lds_cu, lds_blk, zk::kScanPerCU);
+    query_lds(dev, &lds_cu, &lds_blk);
+    set_lds_reserves(h, lds_cu, lds_blk);
     static_assert(sizeof(zk::CheckResult) <= 64 && sizeof(zk::DevState) <= 192, "pinned layout");
     e = hipHostMalloc(reinterpret_cast<void**>(&h->host_result), 256, hipHostMallocDefault);
     if (e != hipSuccess) {
@@ -1283,6 +1318,162 @@ zero_status zero_device_end(zero_shard_t h, void* stream, zero_step_info* out)
         info.grad_norm = std::sqrt(st.last_sumsq);
         info.scale_used = st.last_scale;
     }
+    if (out) *out = info;
+    return ZERO_OK;
+}
+
+}  // extern "C"
+
+// ----------------------------------------------------------------- no allocation
+
+// Scratch of zero_adam_step_noalloc: the check result (first 256 bytes), the
+// fold's first level, then the per-workgroup partials.  Every GPU the library
+// runs on holds one copy until the process ends.  Nothing in it must start at
+// zero: each launch writes every slot it later reads.
+constexpr size_t kNoallocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) double scratch[kNoallocScratchBytes / sizeof(double)];
+
+namespace {
+
+constexpr int kNoallocMaxDevices = 64;
+constexpr int64_t kNoallocHead = 256 / sizeof(double);
+constexpr int64_t kNoallocMaxSlots =
+    (int64_t)(kNoallocScratchBytes / sizeof(double)) - kNoallocHead - zk::kFoldMaxBlocks;
+static_assert(sizeof(zk::CheckResult) <= 256, "check result fits the scratch head");
+
+struct NoallocDevice {
+    double* ptr = nullptr;   // device address of this device's scratch
+    int lds_cu = 0, lds_blk = 0;
+};
+std::mutex g_noalloc_mu;
+NoallocDevice g_noalloc[kNoallocMaxDevices];
+
+// Once per device, with that device current: the device address of its copy
+// of `scratch` (host code must never pass the array's own name to a kernel:
+// on the host it names a host-side stand-in) and its LDS limits.
+zero_status noalloc_device(int dev, NoallocDevice* out, const char* who)
+{
+    if (dev < 0 || dev >= kNoallocMaxDevices)
+        return fail(ZERO_ERR_UNSUPPORTED, "%s: device %d beyond the %d this entry point serves",
+                    who, dev, kNoallocMaxDevices);
+    std::lock_guard<std::mutex> lk(g_noalloc_mu);
+    NoallocDevice& d = g_noalloc[dev];
+    if (d.ptr == nullptr) {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                            "adam_step_noalloc: hipGetSymbolAddress of the scratch");
+        }
+        query_lds(dev, &d.lds_cu, &d.lds_blk);
+        d.ptr = static_cast<double*>(p);
+    }
+    *out = d;
+    return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+zero_status zero_adam_step_noalloc(const zero_shard_desc* desc, const zero_adam_hparams* hp,
+                                   const zero_loss_scale_cfg* ls, double max_grad_norm,
+                                   const void* const* contribs, int32_t n_contrib,
+                                   int64_t* step_t, double* scale, int64_t* good_steps,
+                                   void* stream, zero_step_info* out)
+{
+    const char* who = "adam_step_noalloc";
+    if (!desc || !step_t || !scale || !good_steps)
+        return fail(ZERO_ERR_INVALID_ARG, "%s: NULL desc or counter", who);
+    zero_status st = check_hparams(hp);
+    if (st != ZERO_OK) return st;
+    int64_t S = 0;
+    if ((st = check_desc(*desc, 1, 1, who, &S)) != ZERO_OK) return st;
+    if ((st = check_ls(ls)) != ZERO_OK) return st;
+    if (*step_t < 0 || !scale_ok(*scale) || *good_steps < 0)
+        return fail(ZERO_ERR_INVALID_ARG, "%s: counters out of range", who);
+    if (!(std::isfinite(max_grad_norm) && max_grad_norm >= 0.0))
+        return fail(ZERO_ERR_INVALID_ARG, "%s: max_grad_norm must be finite and >= 0", who);
+    const bool scan = contribs == nullptr && n_contrib == 0;
+
+    // the step's state lives on this stack frame: no handle, no allocation
+    zero_shard_s h;
+    h.d = *desc;
+    h.S = S;
+    h.opt = kOptAdam;
+    h.esz = lp_bytes(desc->lp);
+    h.hp = *hp;
+    h.ls = *ls;
+    h.t = *step_t;
+    h.scale = *scale;
+    h.good_steps = *good_steps;
+    h.pw_t = -1;
+    h.max_norm = max_grad_norm;
+    if (!scan && (st = check_contribs(&h, contribs, n_contrib, who)) != ZERO_OK) return st;
+    hipError_t e = hipGetDevice(&h.device);
+    if (e != hipSuccess) return hip_fail(e, who);
+    if ((st = check_device(&h, stream, who)) != ZERO_OK) return st;
+
+    // the partial slots of the step's reduce (or scan) launches, counted
+    // before anything is launched, against what the scratch holds
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto enqueue_check = [&](bool launch, int64_t* slots) -> zero_status {
+        *slots = 0;
+        if (scan) return enqueue_scan(&h, nullptr, s, slots, who, nullptr, launch);
+        const void* ptrs[ZERO_MAX_CONTRIB];
+        for (int64_t off = 0; off < S; off += desc->bucket_elems) {
+            const int64_t len = S - off < desc->bucket_elems ? S - off : desc->bucket_elems;
+            for (int r = 0; r < n_contrib; ++r)
+                ptrs[r] = static_cast<const char*>(contribs[r]) + off * h.esz;
+            int64_t blocks = 0;
+            zero_status rs = enqueue_reduce(&h, ptrs, n_contrib, off, len, *slots, nullptr, s,
+                                            &blocks, who, nullptr, launch);
+            if (rs != ZERO_OK) return rs;
+            *slots += blocks;
+        }
+        return ZERO_OK;
+    };
+    int64_t slots = 0;
+    h.nslots = INT64_MAX;
+    if ((st = enqueue_check(false, &slots)) != ZERO_OK) return st;
+    if (slots > kNoallocMaxSlots)
+        return fail(ZERO_ERR_INVALID_ARG,
+                    "%s: this shard's check needs %lld partial slots, the %zu-byte static "
+                    "scratch holds %lld; use a handle (zero_shard_init) for larger shards",
+                    who, (long long)slots, kNoallocScratchBytes, (long long)kNoallocMaxSlots);
+    if ((st = check_desc_ranges(*desc, S, h.device, who)) != ZERO_OK) return st;
+    if (!scan && (st = check_contrib_overlap(&h, contribs, n_contrib, 0, S, who)) != ZERO_OK)
+        return st;
+
+    NoallocDevice nd;
+    if ((st = noalloc_device(h.device, &nd, who)) != ZERO_OK) return st;
+    set_lds_reserves(&h, nd.lds_cu, nd.lds_blk);
+    h.result = reinterpret_cast<zk::CheckResult*>(nd.ptr);
+    h.level1 = nd.ptr + kNoallocHead;
+    h.partial = h.level1 + zk::kFoldMaxBlocks;
+    h.nslots = kNoallocMaxSlots;
+
+    if ((st = enqueue_check(true, &slots)) != ZERO_OK) return st;
+    const zk::PrepareArgs none{};
+    e = zk::launch_finalize(h.partial, slots, h.level1, h.result, h.max_norm, nullptr, none, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+    zk::CheckResult res;
+    e = hipMemcpyAsync(&res, h.result, sizeof(res), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, who);
+    h.host_result = &res;
+    zero_step_info info = read_check(&h);
+    double pw1 = 1.0, pw2 = 1.0;
+    bool same = false;
+    if (!info.overflow) {
+        st = launch_adam_step(&h, *hp, s, source_sync(&h), &pw1, &pw2, &same, who);
+        if (st != ZERO_OK) return st;
+    }
+    commit_step(&h, &info, pw1, pw2, same);
+    *step_t = h.t;
+    *scale = h.scale;
+    *good_steps = h.good_steps;
     if (out) *out = info;
     return ZERO_OK;
 }
