@@ -333,19 +333,29 @@ def new_state(lp: int, master: np.ndarray, m, v, hp, ls: LossScale) -> ShardStat
     return st
 
 
+def bucket_flag_sumsq(lp: int, g: np.ndarray, scale: float, bucket_elems: int):
+    """Overflow flag and squared unscaled norm of a shard's stored gradient:
+    one fp64 sum per C_B bucket (its squares added in element order), the
+    bucket sums added in bucket order.  (The pages fix no order; this one lets
+    a chunked evaluation, one bucket per chunk, reproduce it bitwise.)"""
+    flag, sumsq = 0, 0.0
+    for off in range(0, g.size, bucket_elems):
+        f, s = flag_sumsq(lp, g[off:off + bucket_elems], scale)
+        flag |= f
+        sumsq += s
+    return flag, sumsq
+
+
 def step(st: ShardState, contribs: Sequence[np.ndarray], bucket_elems: int,
-         hp, ls: LossScale, forced_flag: Optional[int] = None, max_norm: float = 0.0,
+         hp, ls: LossScale, max_norm: float = 0.0,
          clip_sumsq: Optional[float] = None) -> StepInfo:
     """One owner-rank step on the whole shard held in memory; hp is an AdamHP
-    or an SGDHP.  forced_flag lets a caller that evaluates a sample of a larger
-    shard supply the overflow decision taken over the full shard, and
-    clip_sumsq the squared norm the clipping coefficient is taken from (default:
-    this shard's).  max_norm > 0 clips the unscaled gradient to that global
+    or an SGDHP.  clip_sumsq is the squared norm the clipping coefficient is
+    taken from (default: this shard's; a global norm over several shards
+    otherwise).  max_norm > 0 clips the unscaled gradient to that global
     norm."""
     st.grad = reduce_shard(st.lp, contribs, bucket_elems)
-    flag, sumsq = flag_sumsq(st.lp, st.grad, st.scale)
-    if forced_flag is not None:
-        flag = int(forced_flag)
+    flag, sumsq = bucket_flag_sumsq(st.lp, st.grad, st.scale, bucket_elems)
     coef = 1.0
     if not flag:
         coef = clip_coef(sumsq if clip_sumsq is None else clip_sumsq, max_norm)
@@ -363,6 +373,107 @@ def step(st: ShardState, contribs: Sequence[np.ndarray], bucket_elems: int,
             adam_update(st.lp, st.grad, st.master, st.m, st.v, st.param, sc, hp.wd_mode)
     st.scale, st.good_steps = loss_scale_next(flag, ls, st.scale, st.good_steps)
     return StepInfo(flag, skipped, st.t, float(np.sqrt(sumsq)), scale_used, st.scale)
+
+
+# ---------------------------------------------------------------- chunked evaluation
+
+@dataclass
+class ChunkStep:
+    """The decision of one step of a chunked run: its overflow flag, squared
+    norm, the loss scale its gradients carried, the applied-step count t the
+    update uses (unchanged by a skip) and the clipping coefficient."""
+    overflow: int
+    sumsq: float
+    scale: float
+    t: int
+    coef: float
+
+
+class ChunkedRun:
+    """k steps over a shard too large to hold whole, one C_B bucket (chunk) at
+    a time, with the results of the whole-shard steps, bitwise.  Everything
+    but the overflow decision and the norm is per element, so:
+
+      pass 1 (scan_step, once per step, in step order): reduce every chunk of
+        the step's contributions, take the flag and the squared norm over all
+        chunks, decide the step (skip, t, clipping coefficient) and the next
+        loss scale;
+      pass 2 (evolve, once per chunk, any chunk order): apply the recorded
+        steps to the chunk's state, given its reduced gradient of each step.
+
+    A step's contributions depend on the loss scale, which depends on the
+    flags of the steps before it, so pass 1 must see the steps in order.
+    hp: an AdamHP or an SGDHP."""
+
+    def __init__(self, lp: int, n: int, bucket_elems: int, hp, ls: LossScale,
+                 max_norm: float = 0.0, threads: int = 1):
+        self.lp, self.n, self.bucket_elems = lp, n, bucket_elems
+        self.hp, self.ls, self.max_norm, self.threads = hp, ls, max_norm, max(1, threads)
+        self.t = hp.initial_step
+        self.scale = float(ls.init_scale)
+        self.good_steps = 0
+        self.steps: List[ChunkStep] = []
+
+    def chunks(self):
+        cb = self.bucket_elems
+        return [(off, min(cb, self.n - off)) for off in range(0, self.n, cb)]
+
+    def scan_step(self, contribs_of: Callable[[int, int], Sequence[np.ndarray]],
+                  grads_out: Optional[np.ndarray] = None) -> StepInfo:
+        """Pass 1 of the next step.  contribs_of(off, n) returns the R
+        contributions of shard elements [off, off + n) (stored values, drawn
+        with the current self.scale); it is called in chunk order from this
+        thread.  Chunks are reduced on worker threads; their flags and sums
+        combine in chunk order.  grads_out (n elements) receives the reduced
+        gradient."""
+        from collections import deque
+        from concurrent.futures import ThreadPoolExecutor
+
+        def work(cs):
+            g = bucket_reduce(self.lp, cs)
+            return g, flag_sumsq(self.lp, g, self.scale)
+
+        flag, sumsq = 0, 0.0
+
+        def finish(off, n, fut):
+            nonlocal flag, sumsq
+            g, (f, s) = fut.result()
+            flag |= f
+            sumsq += s
+            if grads_out is not None:
+                grads_out[off:off + n] = g
+
+        with ThreadPoolExecutor(self.threads) as ex:
+            pending = deque()
+            for off, n in self.chunks():
+                pending.append((off, n, ex.submit(work, contribs_of(off, n))))
+                while len(pending) > self.threads:
+                    finish(*pending.popleft())
+            while pending:
+                finish(*pending.popleft())
+        scale_used = self.scale
+        coef = 1.0
+        if not flag:
+            self.t += 1
+            coef = clip_coef(sumsq, self.max_norm)
+        self.steps.append(ChunkStep(flag, sumsq, scale_used, self.t, coef))
+        self.scale, self.good_steps = loss_scale_next(flag, self.ls, self.scale, self.good_steps)
+        return StepInfo(flag, flag, self.t, float(np.sqrt(sumsq)), scale_used, self.scale)
+
+    def evolve(self, master: np.ndarray, m: Optional[np.ndarray], v: Optional[np.ndarray],
+               param: Optional[np.ndarray], grad_of: Callable[[int], np.ndarray]) -> None:
+        """Pass 2 for one chunk: apply every recorded step, in order, to the
+        chunk's state (in place; m / v / param None where absent).
+        grad_of(s) returns the chunk's reduced gradient of step s."""
+        for s, rec in enumerate(self.steps):
+            if rec.overflow:
+                continue
+            g = grad_of(s)
+            if isinstance(self.hp, SGDHP):
+                sgd_update(self.lp, g, master, m, param, sgd_scalars(self.hp, rec.scale, rec.coef))
+            else:
+                adam_update(self.lp, g, master, m, v, param,
+                            adam_scalars(self.hp, rec.t, rec.scale, rec.coef), self.hp.wd_mode)
 
 
 def run_steps(st: ShardState, contribs_for_step: Callable[[int, float], Sequence[np.ndarray]],
