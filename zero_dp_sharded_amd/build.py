@@ -26,6 +26,10 @@ SOURCES = ["zero_kernels.hip", "zero_shard.cpp", "zero_state_bytes.cpp"]
 # benchmark helper: plain HBM copy (ceiling and counter calibration)
 COPY_LIB = os.path.join(HERE, "libhbmcopy.so")
 COPY_SOURCES = ["hbm_copy.hip"]
+# test build: every launch split after 1024 work-items, so the consecutive-
+# launch path that only shards beyond 8.6e9 elements reach runs in the tests
+SPLIT_LAUNCH_DIR = os.path.join(HERE, "variants", "split_launch")
+SPLIT_LAUNCH_DEFINES = {"ZK_MAX_LAUNCH_ITEMS": 1024}
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -88,17 +92,22 @@ def build(verbose: bool = False) -> str:
     os.makedirs(objdir, exist_ok=True)
     _link(_compile(SOURCES, objdir, verbose), LIB, verbose)
     _link(_compile(COPY_SOURCES, objdir, verbose), COPY_LIB, verbose)
+    build_variant(SPLIT_LAUNCH_DEFINES, SPLIT_LAUNCH_DIR, verbose,
+                  objdir=os.path.join(ROOT, "_build", "split_launch"))
     return LIB
 
 
-def build_variant(defines: dict, out_dir: str, verbose: bool = False) -> str:
+def build_variant(defines: dict, out_dir: str, verbose: bool = False,
+                  objdir: str = None) -> str:
     """libzeroshard.so with shape macros overridden ({"ZK_RED_PER_CU": 3, ...})
-    into out_dir, for A/B measurements."""
+    into out_dir (objects in objdir, default out_dir/obj), for A/B
+    measurements and the split-launch test build."""
     for name in defines:
         if not name.startswith("ZK_"):
             raise ValueError(f"{name}: only the ZK_* shape macros may be overridden")
     out_dir = os.path.abspath(out_dir)
-    objdir = os.path.join(out_dir, "obj")
+    objdir = objdir or os.path.join(out_dir, "obj")
+    os.makedirs(out_dir, exist_ok=True)
     os.makedirs(objdir, exist_ok=True)
     extra = [f"-D{k}={v}" for k, v in defines.items()]
     lib = os.path.join(out_dir, "libzeroshard.so")
