@@ -112,6 +112,18 @@ bool live(zero_shard_t h)
 
 bool finite_pos(double x) { return std::isfinite(x) && x > 0.0; }
 
+// A caller's enum field through its 32-bit representation: a value outside the
+// enumerators is then an ordinary integer to refuse, not an out-of-range enum
+// load (undefined in C++).  Fields are read this way until validated.
+template <typename E>
+int32_t enum_value(const E& e)
+{
+    static_assert(sizeof(E) == sizeof(int32_t), "32-bit enum");
+    int32_t v;
+    std::memcpy(&v, &e, sizeof(v));
+    return v;
+}
+
 // A loss scale the kernels can unscale by: finite, positive, and with an fp32
 // reciprocal that is neither 0 nor inf.
 bool scale_ok(double s)
@@ -160,8 +172,9 @@ zero_status check_hparams(const zero_adam_hparams* hp)
         return fail(ZERO_ERR_INVALID_ARG, "adam hparams: weight_decay must be finite and >= 0");
     if (hp->bias_correction != 0 && hp->bias_correction != 1)
         return fail(ZERO_ERR_INVALID_ARG, "adam hparams: bias_correction must be 0 or 1");
-    if (hp->wd_mode != ZERO_WD_DECOUPLED && hp->wd_mode != ZERO_WD_L2)
-        return fail(ZERO_ERR_INVALID_ARG, "adam hparams: unknown wd_mode %d", (int)hp->wd_mode);
+    const int32_t wd_mode = enum_value(hp->wd_mode);
+    if (wd_mode != ZERO_WD_DECOUPLED && wd_mode != ZERO_WD_L2)
+        return fail(ZERO_ERR_INVALID_ARG, "adam hparams: unknown wd_mode %d", (int)wd_mode);
     if (hp->initial_step < 0)
         return fail(ZERO_ERR_INVALID_ARG, "adam hparams: initial_step must be >= 0");
     return ZERO_OK;
@@ -345,8 +358,9 @@ static zero_status check_desc(const zero_shard_desc& d, int need_m, int need_v, 
     if (d.nd < 1) return fail(ZERO_ERR_INVALID_ARG, "%s: nd must be >= 1", who);
     if (d.rank < 0 || d.rank >= d.nd) return fail(ZERO_ERR_INVALID_ARG, "%s: rank outside [0, nd)", who);
     if (d.bucket_elems < 1) return fail(ZERO_ERR_INVALID_ARG, "%s: bucket_elems must be >= 1", who);
-    if (d.lp != ZERO_FP16 && d.lp != ZERO_BF16 && d.lp != ZERO_FP32)
-        return fail(ZERO_ERR_INVALID_ARG, "%s: unknown lp dtype %d", who, (int)d.lp);
+    const int32_t lp = enum_value(d.lp);
+    if (lp != ZERO_FP16 && lp != ZERO_BF16 && lp != ZERO_FP32)
+        return fail(ZERO_ERR_INVALID_ARG, "%s: unknown lp dtype %d", who, (int)lp);
     const bool fp32 = d.lp == ZERO_FP32;
     if (!d.master || !d.grad_shard) return fail(ZERO_ERR_INVALID_ARG, "%s: NULL master or grad_shard", who);
     if (fp32 && d.param_shard)

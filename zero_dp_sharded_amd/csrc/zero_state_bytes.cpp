@@ -18,8 +18,19 @@
 
 namespace {
 
+// The caller's enum argument through its 32-bit representation: a value
+// outside the enumerators is then an ordinary integer to refuse, not an
+// out-of-range enum load (undefined in C++).
+int32_t enum_value(const zero_lp_dtype& e)
+{
+    static_assert(sizeof(zero_lp_dtype) == sizeof(int32_t), "32-bit enum");
+    int32_t v;
+    std::memcpy(&v, &e, sizeof(v));
+    return v;
+}
+
 zero_status ledger(int64_t psi, int32_t nd, int32_t n_contrib, int64_t bucket_elems,
-                   zero_lp_dtype lp, int32_t b_bytes, int32_t k_optim, zero_state_bytes_t* out)
+                   int32_t lp, int32_t b_bytes, int32_t k_optim, zero_state_bytes_t* out)
 {
     if (!out || psi < 1 || nd < 1 || n_contrib < 1 || n_contrib > ZERO_MAX_CONTRIB ||
         bucket_elems < 1 || (lp != ZERO_FP16 && lp != ZERO_BF16 && lp != ZERO_FP32) ||
@@ -74,7 +85,7 @@ extern "C" zero_status zero_state_bytes(int64_t psi, int32_t nd, int32_t n_contr
                                         int64_t bucket_elems, zero_lp_dtype lp,
                                         zero_state_bytes_t* out)
 {
-    return ledger(psi, nd, n_contrib, bucket_elems, lp, 2, 12, out);
+    return ledger(psi, nd, n_contrib, bucket_elems, enum_value(lp), 2, 12, out);
 }
 
 extern "C" zero_status zero_state_bytes_ex(int64_t psi, int32_t nd, int32_t n_contrib,
@@ -82,5 +93,5 @@ extern "C" zero_status zero_state_bytes_ex(int64_t psi, int32_t nd, int32_t n_co
                                            int32_t param_bytes, int32_t k_optim,
                                            zero_state_bytes_t* out)
 {
-    return ledger(psi, nd, n_contrib, bucket_elems, lp, param_bytes, k_optim, out);
+    return ledger(psi, nd, n_contrib, bucket_elems, enum_value(lp), param_bytes, k_optim, out);
 }
