@@ -8,11 +8,10 @@ oracle, through skipped steps, loss-scale changes and clipping; shapes just
 past the limits must take the fold launch instead; and graph replays of such
 steps must equal eager ones after every replay.
 
-The partial counts below follow the reduce's shape for buckets too small to
-fill the chip: one-wave workgroups with 2 runs of 16 bytes per lane below 8
-contributions and 1 run from 8 on (1024, 512 or 256 elements per workgroup
-for 2-byte storage with R < 8, 2-byte storage with R >= 8 and fp32 storage
-with R = 8)."""
+The partial counts below follow the reduce's shape for shards of at most
+8,388,608 elements: 256-lane workgroups with one run of 16 bytes per lane, so
+2048 elements per workgroup with 2-byte storage and 1024 with fp32 storage,
+for any contribution count."""
 import dataclasses
 
 import numpy as np
@@ -37,13 +36,13 @@ def _w(base, **over):
 # name -> (workload, shard elements, C_B): 256 partials (one partial per fold
 # lane) or 512 (two per lane, the limit)
 CASES = {
-    "adam_fp16_r4": (_w(W["tiny"], steps=5), 262_144, 65_536),        # 4 x 64
-    "adam_fp16_r4_512": (_w(W["tiny"], steps=5), 524_288, 524_288),   # 512
-    "adam_bf16_r8": (_w(W["7.5b_bf16"], steps=5), 131_072, 65_536),   # 2 x 128
-    "adam_fp16_r16": (_w(W["13b_inf"], steps=5, inject_step=None), 131_072, 131_072),  # 256
-    "sgdm_fp32_r8": (_w(W["c1_7.5b_sgdm"], steps=5), 65_536, 65_536),  # 256
-    "sgdm_fp32_r8_512": (_w(W["c1_7.5b_sgdm"], steps=5), 131_072, 32_768),  # 4 x 128
-    "sgd_fp32_r8": (_w(W["c2_1.5b_sgd"], steps=5), 65_536, 32_768),    # 2 x 128
+    "adam_fp16_r4": (_w(W["tiny"], steps=5), 524_288, 131_072),       # 4 x 64
+    "adam_fp16_r4_512": (_w(W["tiny"], steps=5), 1_048_576, 1_048_576),   # 512
+    "adam_bf16_r8": (_w(W["7.5b_bf16"], steps=5), 524_288, 262_144),  # 2 x 128
+    "adam_fp16_r16": (_w(W["13b_inf"], steps=5, inject_step=None), 524_288, 524_288),  # 256
+    "sgdm_fp32_r8": (_w(W["c1_7.5b_sgdm"], steps=5), 262_144, 262_144),  # 256
+    "sgdm_fp32_r8_512": (_w(W["c1_7.5b_sgdm"], steps=5), 524_288, 131_072),  # 4 x 128
+    "sgd_fp32_r8": (_w(W["c2_1.5b_sgd"], steps=5), 262_144, 131_072),  # 2 x 128
 }
 
 
@@ -109,8 +108,8 @@ def test_inline_fold_uninterrupted_steps(name):
 
 
 @pytest.mark.parametrize("elems,cb,why", [
-    (525_312, 525_312, "513 partials"),              # 65,664 runs / 128 per workgroup
-    (200_002, 200_002, "update with a scalar tail"),  # 197 partials, S not a multiple of 4
+    (1_050_624, 1_050_624, "513 partials"),          # 131,328 runs / 256 per workgroup
+    (200_002, 200_002, "update with a scalar tail"),  # 98 partials, S not a multiple of 4
 ])
 def test_past_the_limits_takes_the_fold_launch(elems, cb, why):
     """Shapes just past the inline fold's limits use the fold launch and still

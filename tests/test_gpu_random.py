@@ -20,9 +20,11 @@ BASES = {"fp16": synth.WORKLOADS["gpt2_1.5b"], "bf16": synth.WORKLOADS["7.5b_bf1
 
 
 SMALL = [1, 5, 63, 64, 65, 1000, 4099, 65_537, 131_071, 250_000]
-# shards whose buckets can reach the size at which the reduce gives each lane 3
-# runs (491,520 runs: 3,932,160 two-byte or 1,966,080 fp32 elements)
-LARGE = [1_966_081, 3_932_167, 4_500_001, 6_000_007]
+# shards past the 8,388,608 elements below which every kernel takes its
+# cache-resident 256-lane shape, whose buckets can reach the size at which the
+# reduce gives each lane 3 runs (491,520 runs: 3,932,160 two-byte or 1,966,080
+# fp32 elements)
+LARGE = [8_388_609, 8_500_001, 9_000_007, 10_000_019]
 
 
 def _case(k: int, sizes=SMALL, seed0: int = 1000, steps: int = 3, r_hi: int = 21):
@@ -73,8 +75,9 @@ def test_random_case(k):
 
 @pytest.mark.parametrize("k", range(12))
 def test_random_large_case(k):
-    """Shards of 2-6M elements, where a bucket of up to the whole shard takes
-    3 runs per lane below 8 contributions; 2 steps each."""
+    """Shards of 8.4-10M elements (the streaming shapes), where a bucket of up
+    to the whole shard takes 3 runs per lane below 8 contributions; 2 steps
+    each."""
     _run_case(100 + k, _case(k, LARGE, seed0=2000, steps=2, r_hi=8 if k % 3 else 21))
 
 

@@ -1,14 +1,17 @@
 """GPU parity at the sizes where the streaming kernels change shape, element by
 element against the oracle.
 
-Below 8 contributions a bucket reduce gives each lane 3 runs of 16 bytes once
-the bucket holds at least 491,520 runs (256 CUs x 10 workgroups x 64 lanes x
-3 runs: 3,932,160 two-byte or 1,966,080 fp32 elements) and 2 runs below that;
-from 8 contributions it gives 1 run.  The stand-alone
-scan gives each lane 4 runs.  Each case below puts one bucket exactly at that threshold and one just
-under it (with a ragged element-wise tail) into the same step, with every
+In a shard of more than 8,388,608 elements (smaller shards run every kernel in
+their cache-resident 256-lane shape), a bucket reduce below 8 contributions
+gives each lane 3 runs of 16 bytes once the bucket holds at least 491,520 runs
+(256 CUs x 10 workgroups x 64 lanes x 3 runs: 3,932,160 two-byte or 1,966,080
+fp32 elements) and 2 runs below that; from 8 contributions it gives 1 run.
+The stand-alone scan gives each lane 4 runs.  Each case below fills a shard
+past 8,388,608 elements with buckets exactly at that threshold and ends it
+with one just under it (with a ragged element-wise tail), with every
 contribution-count class and storage format, and with base pointers off the
-16-byte grid.
+16-byte grid.  The last case steps shards just at and just past the
+small-shard limit.
 """
 import dataclasses
 
@@ -25,13 +28,16 @@ pytestmark = pytest.mark.gpu
 
 W = synth.WORKLOADS
 THRESHOLD_RUNS = 256 * 10 * 64 * 3
+SMALL_SHARD = 1 << 23               # shards up to this size take the 256-lane shape
 
 
 def _two_buckets(run_width: int):
-    """(shard elements, bucket elements): bucket 0 has exactly THRESHOLD_RUNS
-    runs, bucket 1 one run fewer plus a ragged tail of run_width - 1."""
+    """(shard elements, bucket elements): buckets of exactly THRESHOLD_RUNS
+    runs until the shard passes SMALL_SHARD, then one of a run fewer plus a
+    ragged tail of run_width - 1."""
     cb = THRESHOLD_RUNS * run_width
-    return 2 * cb - 1, cb
+    full = SMALL_SHARD // cb + 1
+    return full * cb + cb - 1, cb
 
 
 @pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 7, 8])
@@ -69,7 +75,8 @@ def test_reduce_threshold_misaligned():
     the threshold, bucket 1's one run short of it, with a 1-element tail."""
     w = dataclasses.replace(W["gpt2_1.5b"], R=4, steps=2)
     cb = THRESHOLD_RUNS * 8 + 8
-    S = cb + THRESHOLD_RUNS * 8 - 2
+    S = 2 * cb + THRESHOLD_RUNS * 8 - 2
+    assert S > SMALL_SHARD
     offs = dict(master=3, m=3, v=3, grad=3, param=3, contrib=3)
     log(f"shapes misaligned S={S} cb={cb}")
     g = run_gpu(w, elems=S, bucket_elems=cb, offsets=offs)
@@ -111,3 +118,16 @@ def test_scan_multi_block_with_planted_inf():
         assert np.isfinite(f32(master)).all()
     finally:
         zs.zero_shard_destroy(h)
+
+
+@pytest.mark.parametrize("S", [SMALL_SHARD, SMALL_SHARD + 4, SMALL_SHARD + 1])
+@pytest.mark.parametrize("flow", ["sync", "device"])
+def test_small_shard_limit(S, flow):
+    """Shards at the small-shard limit (256-lane cached shape) and just past it
+    (the streaming shapes; +1 also with an element-wise tail): bitwise against
+    the oracle in the synchronous and device-resident flows."""
+    w = dataclasses.replace(W["gpt2_1.5b"], R=4, steps=2)
+    log(f"shapes small-shard limit S={S} flow={flow}")
+    g = run_gpu(w, elems=S, bucket_elems=3_000_000, flow=flow)
+    st, oi = run_oracle(w, g, bucket_elems=3_000_000)
+    assert compare(w, g, st, oi, f"S={S} {flow}")["bitwise"]

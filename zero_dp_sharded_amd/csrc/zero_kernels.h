@@ -83,17 +83,9 @@ constexpr int kRedBlockMany = ZK_RED_BLOCK_MANY;  // reduce, R >= 8
 constexpr int kRedRuns = ZK_RED_RUNS;
 constexpr int kRedRunsMany = ZK_RED_RUNS_MANY;   // runs per lane when R >= 8
 constexpr int kRedManyR = 8;
-// Lanes per workgroup of the reduce with R contributions.
-inline int red_block(int R) { return R >= kRedManyR ? kRedBlockMany : kRedBlock; }
 constexpr int kRedRunsSmall = ZK_RED_RUNS_SMALL;   // R < 8, bucket below kRedSmallNvec runs
 // runs of one full residency of kRedRuns workgroups on 256 CUs
 constexpr int64_t kRedSmallNvec = (int64_t)256 * ZK_RED_PER_CU * ZK_RED_BLOCK * ZK_RED_RUNS;
-// Runs per lane of the reduce of a bucket of nvec runs with R contributions.
-inline int red_runs(int R, int64_t nvec)
-{
-    if (R >= kRedManyR) return kRedRunsMany;
-    return nvec < kRedSmallNvec ? kRedRunsSmall : kRedRuns;
-}
 // The stand-alone scan reads a single stream, so it takes its own runs per
 // lane and residency.
 constexpr int kScanBlock = ZK_SCAN_BLOCK;
@@ -124,6 +116,42 @@ constexpr int kSgdMomGroups = ZK_SGD_MOM_GROUPS;
 constexpr int kSgdMomPerCU = ZK_SGD_MOM_PER_CU;
 constexpr int kSgdPlainGroups = ZK_SGD_PLAIN_GROUPS;
 constexpr int kSgdPlainPerCU = ZK_SGD_PLAIN_PER_CU;
+// Small shards (at most kSmallElems elements) keep their step's data in the
+// caches (the 256 MiB Infinity Cache holds 8M elements' worth of an fp16 Adam
+// step), and their steps are bound by launch and memory latency rather than by
+// HBM bandwidth.  Every bucket reduce and the update of such a shard run
+// 256-lane workgroups with one run or group per lane and plain (cached) loads
+// and stores: the update then reads the gradient the reduce just stored from
+// cache.  Measured on MI355X (device-resident fp16 Adam steps, R = 4, back to
+// back): 7.45 -> 7.3 us at 262,144 elements, 13.4 -> 10.6 us at 1M, 33.4 ->
+// 27.7 us at 4M, 59.1 -> 45.9 us at 8M; at 16M the streaming shapes below win.
+#ifndef ZK_SMALL_ELEMS
+#define ZK_SMALL_ELEMS (int64_t(1) << 23)
+#endif
+constexpr int64_t kSmallElems = ZK_SMALL_ELEMS;
+constexpr int kSmallBlock = 256;
+inline bool shard_small(int64_t S) { return S <= kSmallElems; }
+// Lanes per workgroup and runs per lane of a bucket reduce (nvec runs, R
+// contributions) of a small shard or not.
+inline int red_block(int R, bool small)
+{
+    if (small) return kSmallBlock;
+    return R >= kRedManyR ? kRedBlockMany : kRedBlock;
+}
+inline int red_runs(int R, int64_t nvec, bool small)
+{
+    if (small) return 1;
+    if (R >= kRedManyR) return kRedRunsMany;
+    return nvec < kRedSmallNvec ? kRedRunsSmall : kRedRuns;
+}
+// Update of an S-element shard: lanes per workgroup and groups per lane.
+inline int adam_lanes(int64_t S) { return shard_small(S) ? kSmallBlock : kAdamBlock; }
+inline int adam_groups(int64_t S) { return shard_small(S) ? 1 : kAdamGroups; }
+inline int sgd_lanes(int64_t S) { return shard_small(S) ? kSmallBlock : kSgdBlock; }
+inline int sgd_groups(int64_t S, bool mom)
+{
+    return shard_small(S) ? 1 : (mom ? kSgdMomGroups : kSgdPlainGroups);
+}
 // Element-wise kernels (unaligned heads and tails, or arrays without a common
 // alignment): 256 lanes, 8 elements per lane, lane-consecutive per step.
 constexpr int kScalarBlock = 256;
@@ -200,6 +228,7 @@ struct ReduceLaunch {
     double* partial;
     int64_t slot_base;
     uint32_t lds_reserve;  // dynamic LDS that caps workgroups per CU
+    int32_t small;         // 1: a bucket of a small shard (see shard_small)
     const DevState* dev;
     DevState* snapshot;    // set: workgroup 0 copies *dev there (see InlineFold)
 };

@@ -14,7 +14,10 @@
 //    and reduce kernels, fewer resident waves (10 per CU for Adam, 16 or 24
 //    for SGD, 12 or 8 for the reduce) sustain more HBM bandwidth than full
 //    occupancy; the one-stream scan keeps 32 waves with 4 runs per lane.  The
-//    measured optimum keeps roughly 96-144 KiB of loads in flight per CU.
+//    measured optimum keeps roughly 96-144 KiB of loads in flight per CU;
+//  - shards of at most 8M elements, whose step fits the caches, instead run
+//    256-lane workgroups with one run or group per lane and plain (cached)
+//    loads and stores in every bucket reduce and in the update.
 // The only cross-lane work is the fixed-shape reduction of the overflow flag
 // and the squared gradient norm: wave butterfly, one LDS slot per wave, one
 // fp64 partial per workgroup, then a fixed-order fold of one or two levels
@@ -80,6 +83,22 @@ template <typename V>
 __device__ __forceinline__ void st_nt(void* base, int64_t idx, V x)
 {
     __builtin_nontemporal_store(x, static_cast<V*>(base) + idx);
+}
+
+// Vector load / store: nontemporal (NT = 1, large shards: each byte is touched
+// once per step) or plain (NT = 0, small cache-resident shards).
+template <typename V, int NT>
+__device__ __forceinline__ V ld_v(const void* base, int64_t idx)
+{
+    if constexpr (NT) return ld_nt<V>(base, idx);
+    else return static_cast<const V*>(base)[idx];
+}
+
+template <typename V, int NT>
+__device__ __forceinline__ void st_v(void* base, int64_t idx, V x)
+{
+    if constexpr (NT) st_nt<V>(base, idx, x);
+    else static_cast<V*>(base)[idx] = x;
 }
 
 template <int LP>
@@ -195,7 +214,7 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 // Finish run vi of the vector body (elements head + W vi ..): acc holds the
 // fp32 sum over r = 0..R-1 in order from +0; scale by fp32(1/R), convert to
 // the storage format (round to nearest even), store, check.
-template <int LP>
+template <int LP, int NT>
 __device__ __forceinline__ void reduce_finish(const ReduceLaunch& L, int64_t vi,
                                               typename Fmt<LP>::FW acc, float inv_scale, int& flag,
                                               double& ss)
@@ -205,7 +224,7 @@ __device__ __forceinline__ void reduce_finish(const ReduceLaunch& L, int64_t vi,
     // a codegen test checks, and the pin costs about 3% of the reduce)
     acc = acc * L.inv_r;
     const VW o = __builtin_convertvector(acc, VW);
-    st_nt<VW>(adv<LP>(L.out, L.head), vi, o);
+    st_v<VW, NT>(adv<LP>(L.out, L.head), vi, o);
     check_v<LP>(o, inv_scale, flag, ss);
 }
 
@@ -228,7 +247,6 @@ __device__ __forceinline__ void snapshot_state(const DevState* dev, DevState* sn
 {
     if (snap != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *snap = *dev;
 }
-
 // The unscale factor of a check: the launch argument, or the device state's.
 __device__ __forceinline__ float check_inv_scale(float arg, const DevState* dev)
 {
@@ -238,8 +256,9 @@ __device__ __forceinline__ float check_inv_scale(float arg, const DevState* dev)
 // Vector body: workgroup b covers runs [b*BS*U, (b+1)*BS*U) for BS lanes and
 // U runs per lane; lane l owns runs b*BS*U + u*BS + l.  Element offsets past `head`
 // are multiples of W, so contribution and output pointers advanced by `head`
-// are 16-byte aligned and are indexed in units of runs.
-template <int LP, int RT, int U, int BS, int SNAP>
+// are 16-byte aligned and are indexed in units of runs.  NT: nontemporal
+// loads and stores (large buckets) or plain ones (small buckets).
+template <int LP, int RT, int U, int BS, int SNAP, int NT>
 __global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
 {
     using VW = typename Fmt<LP>::VW;
@@ -256,7 +275,7 @@ __global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
             const int64_t vi = v0 + u * BS;
             if (vi < L.nvec) {
 #pragma unroll
-                for (int r = 0; r < RT; ++r) x[u][r] = ld_nt<VW>(adv<LP>(L.c.p[r], L.head), vi);
+                for (int r = 0; r < RT; ++r) x[u][r] = ld_v<VW, NT>(adv<LP>(L.c.p[r], L.head), vi);
             }
         }
 #pragma unroll
@@ -266,7 +285,7 @@ __global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
                 FW acc = (FW)(0.f);
 #pragma unroll
                 for (int r = 0; r < RT; ++r) acc = acc + __builtin_convertvector(x[u][r], FW);
-                reduce_finish<LP>(L, vi, acc, inv_scale, flag, ss);
+                reduce_finish<LP, NT>(L, vi, acc, inv_scale, flag, ss);
             }
         }
     } else {
@@ -277,7 +296,7 @@ __global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
             if constexpr (RT > 0) {
                 VW x[RT];
 #pragma unroll
-                for (int r = 0; r < RT; ++r) x[r] = ld_nt<VW>(adv<LP>(L.c.p[r], L.head), vi);
+                for (int r = 0; r < RT; ++r) x[r] = ld_v<VW, NT>(adv<LP>(L.c.p[r], L.head), vi);
 #pragma unroll
                 for (int r = 0; r < RT; ++r) acc = acc + __builtin_convertvector(x[r], FW);
             } else {
@@ -286,13 +305,13 @@ __global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
                     VW x[8];
 #pragma unroll
                     for (int k = 0; k < 8; ++k)
-                        if (k < cnt) x[k] = ld_nt<VW>(adv<LP>(L.c.p[r0 + k], L.head), vi);
+                        if (k < cnt) x[k] = ld_v<VW, NT>(adv<LP>(L.c.p[r0 + k], L.head), vi);
 #pragma unroll
                     for (int k = 0; k < 8; ++k)
                         if (k < cnt) acc = acc + __builtin_convertvector(x[k], FW);
                 }
             }
-            reduce_finish<LP>(L, vi, acc, inv_scale, flag, ss);
+            reduce_finish<LP, NT>(L, vi, acc, inv_scale, flag, ss);
         }
     }
     if constexpr (SNAP) snapshot_state(L.dev, L.snapshot);
@@ -577,26 +596,27 @@ __device__ __forceinline__ void adam_e(float graw, float& p, float& m, float& v,
 // covers groups [b*B*G, (b+1)*B*G) for B lanes and G groups per lane; lane l
 // owns groups b*B*G + u*B + l, u < G, and issues all loads before any
 // arithmetic.  With fp32 storage there is no 2-byte parameter to write.
-// INL = 1: the step's values come from the inline fold (a.src.fold).
-template <int LP, int WD, int INL>
-__global__ __launch_bounds__(kAdamBlock) void adam_vec_kernel(AdamLaunch a)
+// INL = 1: the step's values come from the inline fold (a.src.fold).  NT as
+// for the reduce (plain loads and stores for small shards).
+template <int LP, int WD, int INL, int B, int G, int NT>
+__global__ __launch_bounds__(B) void adam_vec_kernel(AdamLaunch a)
 {
     using V4 = typename Fmt<LP>::V4;
     const void* gb = adv<LP>(a.grad, a.head);
     float* pb = a.master + a.head;
     float* mb = a.m + a.head;
     float* vb = a.v + a.head;
-    const int64_t q0 = (int64_t)blockIdx.x * (kAdamBlock * kAdamGroups) + threadIdx.x;
-    V4 g[kAdamGroups];
-    f4 p[kAdamGroups], m[kAdamGroups], v[kAdamGroups];
+    const int64_t q0 = (int64_t)blockIdx.x * (B * G) + threadIdx.x;
+    V4 g[G];
+    f4 p[G], m[G], v[G];
 #pragma unroll
-    for (int u = 0; u < kAdamGroups; ++u) {
-        const int64_t q = q0 + u * kAdamBlock;
+    for (int u = 0; u < G; ++u) {
+        const int64_t q = q0 + u * B;
         if (q < a.ngroups) {
-            g[u] = ld_nt<V4>(gb, q);
-            p[u] = ld_nt<f4>(pb, q);
-            m[u] = ld_nt<f4>(mb, q);
-            v[u] = ld_nt<f4>(vb, q);
+            g[u] = ld_v<V4, NT>(gb, q);
+            p[u] = ld_v<f4, NT>(pb, q);
+            m[u] = ld_v<f4, NT>(mb, q);
+            v[u] = ld_v<f4, NT>(vb, q);
         }
     }
     StepVals sv;
@@ -608,8 +628,8 @@ __global__ __launch_bounds__(kAdamBlock) void adam_vec_kernel(AdamLaunch a)
         if (sv.skip) return;
     }
 #pragma unroll
-    for (int u = 0; u < kAdamGroups; ++u) {
-        const int64_t q = q0 + u * kAdamBlock;
+    for (int u = 0; u < G; ++u) {
+        const int64_t q = q0 + u * B;
         if (q < a.ngroups && !(INL && sv.skip)) {
             const f4 gf = __builtin_convertvector(g[u], f4);
             f4 pp = p[u], mm = m[u], vv = v[u];
@@ -621,11 +641,11 @@ __global__ __launch_bounds__(kAdamBlock) void adam_vec_kernel(AdamLaunch a)
                 mm[k] = mk;
                 vv[k] = vk;
             }
-            st_nt<f4>(pb, q, pp);
-            st_nt<f4>(mb, q, mm);
-            st_nt<f4>(vb, q, vv);
+            st_v<f4, NT>(pb, q, pp);
+            st_v<f4, NT>(mb, q, mm);
+            st_v<f4, NT>(vb, q, vv);
             if constexpr (LP != 3)
-                st_nt<V4>(adv<LP>(a.param, a.head), q, __builtin_convertvector(pp, V4));
+                st_v<V4, NT>(adv<LP>(a.param, a.head), q, __builtin_convertvector(pp, V4));
         }
     }
     if constexpr (INL) inline_commit(a.src.fold, dec);
@@ -671,25 +691,25 @@ __device__ __forceinline__ void sgd_e(float graw, float& p, float& b, const SgdL
     p = p - a.lr * d;
 }
 
-// Same layout and load-first order as adam_vec_kernel, with G groups per lane;
-// INL as there.
-template <int LP, int MOM, int WD, int G, int INL>
-__global__ __launch_bounds__(kSgdBlock) void sgd_vec_kernel(SgdLaunch a)
+// Same layout and load-first order as adam_vec_kernel, with B lanes and G
+// groups per lane; INL and NT as there.
+template <int LP, int MOM, int WD, int G, int INL, int B, int NT>
+__global__ __launch_bounds__(B) void sgd_vec_kernel(SgdLaunch a)
 {
     using V4 = typename Fmt<LP>::V4;
     const void* gb = adv<LP>(a.grad, a.head);
     float* pb = a.master + a.head;
     float* bb = MOM ? a.mom + a.head : nullptr;
-    const int64_t q0 = (int64_t)blockIdx.x * (kSgdBlock * G) + threadIdx.x;
+    const int64_t q0 = (int64_t)blockIdx.x * (B * G) + threadIdx.x;
     V4 g[G];
     f4 p[G], b[G];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-        const int64_t q = q0 + u * kSgdBlock;
+        const int64_t q = q0 + u * B;
         if (q < a.ngroups) {
-            g[u] = ld_nt<V4>(gb, q);
-            p[u] = ld_nt<f4>(pb, q);
-            if constexpr (MOM) b[u] = ld_nt<f4>(bb, q);
+            g[u] = ld_v<V4, NT>(gb, q);
+            p[u] = ld_v<f4, NT>(pb, q);
+            if constexpr (MOM) b[u] = ld_v<f4, NT>(bb, q);
         }
     }
     StepVals sv;
@@ -702,7 +722,7 @@ __global__ __launch_bounds__(kSgdBlock) void sgd_vec_kernel(SgdLaunch a)
     }
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-        const int64_t q = q0 + u * kSgdBlock;
+        const int64_t q = q0 + u * B;
         if (q < a.ngroups && !(INL && sv.skip)) {
             const f4 gf = __builtin_convertvector(g[u], f4);
             f4 pp = p[u];
@@ -715,10 +735,10 @@ __global__ __launch_bounds__(kSgdBlock) void sgd_vec_kernel(SgdLaunch a)
                 pp[k] = pk;
                 buf[k] = bk;
             }
-            st_nt<f4>(pb, q, pp);
-            if constexpr (MOM) st_nt<f4>(bb, q, buf);
+            st_v<f4, NT>(pb, q, pp);
+            if constexpr (MOM) st_v<f4, NT>(bb, q, buf);
             if constexpr (LP != 3)
-                st_nt<V4>(adv<LP>(a.param, a.head), q, __builtin_convertvector(pp, V4));
+                st_v<V4, NT>(adv<LP>(a.param, a.head), q, __builtin_convertvector(pp, V4));
         }
     }
     if constexpr (INL) inline_commit(a.src.fold, dec);
@@ -773,19 +793,20 @@ Ranges ranges_of(int64_t n, int64_t head, int64_t body, int32_t vec_ok)
 
 // SNAP = 1 (a snapshot target is set) only for the small steps of the inline
 // fold, so the reduce of every other step keeps the plain kernel.
-template <int LP, int RT, int U, int BS>
+template <int LP, int RT, int U, int BS, int NT = 1>
 void reduce_vec_go(const ReduceLaunch& L, unsigned grid, hipStream_t s)
 {
     if (L.snapshot != nullptr)
-        reduce_vec_kernel<LP, RT, U, BS, 1><<<grid, BS, L.lds_reserve, s>>>(L);
+        reduce_vec_kernel<LP, RT, U, BS, 1, NT><<<grid, BS, L.lds_reserve, s>>>(L);
     else
-        reduce_vec_kernel<LP, RT, U, BS, 0><<<grid, BS, L.lds_reserve, s>>>(L);
+        reduce_vec_kernel<LP, RT, U, BS, 0, NT><<<grid, BS, L.lds_reserve, s>>>(L);
 }
 
 // Below 8 contributions the workgroup has kRedBlock lanes and the runs per
 // lane U is kRedRuns or kRedRunsSmall; from 8 on it has kRedBlockMany lanes
-// and U is kRedRunsMany.  U must be the one the dispatch sized the grid with
-// (red_runs of the whole bucket).
+// and U is kRedRunsMany; a bucket of a small shard (shard_small) takes
+// kSmallBlock lanes, one run each, plain loads and stores.  U and BS must be the ones the
+// dispatch sized the grid with (red_runs / red_block of the whole bucket).
 template <int LP, int RT>
 void reduce_vec_few(const ReduceLaunch& L, unsigned grid, int U, hipStream_t s)
 {
@@ -795,10 +816,28 @@ void reduce_vec_few(const ReduceLaunch& L, unsigned grid, int U, hipStream_t s)
         reduce_vec_go<LP, RT, kRedRuns, kRedBlock>(L, grid, s);
 }
 
+template <int LP, int RT>
+void reduce_vec_small(const ReduceLaunch& L, unsigned grid, hipStream_t s)
+{
+    reduce_vec_go<LP, RT, 1, kSmallBlock, 0>(L, grid, s);
+}
+
 template <int LP>
-hipError_t reduce_vec_launch(const ReduceLaunch& L, unsigned grid, int U, hipStream_t s)
+hipError_t reduce_vec_launch(const ReduceLaunch& L, unsigned grid, int U, bool small,
+                             hipStream_t s)
 {
     constexpr int B = kRedRunsMany, BM = kRedBlockMany;
+    if (small) {
+        switch (L.R) {
+        case 1: reduce_vec_small<LP, 1>(L, grid, s); break;
+        case 2: reduce_vec_small<LP, 2>(L, grid, s); break;
+        case 4: reduce_vec_small<LP, 4>(L, grid, s); break;
+        case 8: reduce_vec_small<LP, 8>(L, grid, s); break;
+        case 16: reduce_vec_small<LP, 16>(L, grid, s); break;
+        default: reduce_vec_small<LP, 0>(L, grid, s); break;
+        }
+        return hipGetLastError();
+    }
     switch (L.R) {
     case 1: reduce_vec_few<LP, 1>(L, grid, U, s); break;
     case 2: reduce_vec_few<LP, 2>(L, grid, U, s); break;
@@ -819,8 +858,9 @@ template <int LP>
 hipError_t reduce_dispatch(const ReduceLaunch& L, hipStream_t s)
 {
     constexpr int W = Fmt<LP>::W;
-    const int U = red_runs(L.R, L.nvec);
-    const int BS = red_block(L.R);
+    const bool small = L.small != 0;
+    const int U = red_runs(L.R, L.nvec, small);
+    const int BS = red_block(L.R, small);
     const int64_t runs_per_block = (int64_t)BS * U;
     const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, runs_per_block) : 0;
     // consecutive launches of at most kMaxLaunchItems work-items; each starts
@@ -832,7 +872,7 @@ hipError_t reduce_dispatch(const ReduceLaunch& L, hipStream_t s)
         part.head = L.head + W * runs_per_block * b0;
         part.nvec = L.nvec - runs_per_block * b0;
         part.slot_base = L.slot_base + b0;
-        hipError_t e = reduce_vec_launch<LP>(part, (unsigned)nb, U, s);
+        hipError_t e = reduce_vec_launch<LP>(part, (unsigned)nb, U, small, s);
         if (e != hipSuccess) return e;
     }
     const Ranges rg = ranges_of(L.n, L.head, W * L.nvec, L.vec_ok);
@@ -869,30 +909,44 @@ hipError_t scan_dispatch(const ScanLaunch& L, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int LP, int WD>
-hipError_t adam_dispatch(const AdamLaunch& a, hipStream_t s)
+// The vector launches of an update of B lanes and G groups per lane: the
+// inline-fold launch (one over the whole array) or consecutive launches of at
+// most kMaxLaunchItems work-items.
+template <int LP, int WD, int B, int G, int NT>
+hipError_t adam_vec_launches(const AdamLaunch& a, int64_t vblocks, hipStream_t s)
 {
-    const int64_t groups_per_block = (int64_t)kAdamBlock * kAdamGroups;
-    const int64_t vblocks = a.vec_ok ? ceil_div(a.ngroups, groups_per_block) : 0;
+    constexpr int64_t groups_per_block = (int64_t)B * G;
     if (a.src.fold.partial != nullptr) {
-        // the inline fold: one vector launch over the whole array
-        if (!a.vec_ok || a.head != 0 || 4 * a.ngroups != a.n || vblocks < 1 ||
-            !one_launch(a.ngroups, kAdamBlock, kAdamGroups) || a.src.fold.n < 1 ||
-            a.src.fold.n > kInlineFoldMax)
-            return hipErrorInvalidValue;
-        adam_vec_kernel<LP, WD, 1><<<(unsigned)vblocks, kAdamBlock, a.lds_reserve, s>>>(a);
+        adam_vec_kernel<LP, WD, 1, B, G, NT><<<(unsigned)vblocks, B, a.lds_reserve, s>>>(a);
         return hipGetLastError();
     }
-    const int64_t max_blocks = kMaxLaunchItems / kAdamBlock;
+    const int64_t max_blocks = kMaxLaunchItems / B;
     for (int64_t b0 = 0; b0 < vblocks; b0 += max_blocks) {
         const int64_t nb = vblocks - b0 < max_blocks ? vblocks - b0 : max_blocks;
         AdamLaunch part = a;
         part.head = a.head + 4 * groups_per_block * b0;
         part.ngroups = a.ngroups - groups_per_block * b0;
-        adam_vec_kernel<LP, WD, 0><<<(unsigned)nb, kAdamBlock, a.lds_reserve, s>>>(part);
+        adam_vec_kernel<LP, WD, 0, B, G, NT><<<(unsigned)nb, B, a.lds_reserve, s>>>(part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    return hipSuccess;
+}
+
+template <int LP, int WD>
+hipError_t adam_dispatch(const AdamLaunch& a, hipStream_t s)
+{
+    const bool small = shard_small(a.n);
+    const int lanes = adam_lanes(a.n), groups = adam_groups(a.n);
+    const int64_t vblocks = a.vec_ok ? ceil_div(a.ngroups, (int64_t)lanes * groups) : 0;
+    if (a.src.fold.partial != nullptr &&
+        (!a.vec_ok || a.head != 0 || 4 * a.ngroups != a.n || vblocks < 1 ||
+         !one_launch(a.ngroups, lanes, groups) || a.src.fold.n < 1 ||
+         a.src.fold.n > kInlineFoldMax))
+        return hipErrorInvalidValue;          // the inline fold needs one vector launch
+    hipError_t e = small ? adam_vec_launches<LP, WD, kSmallBlock, 1, 0>(a, vblocks, s)
+                         : adam_vec_launches<LP, WD, kAdamBlock, kAdamGroups, 1>(a, vblocks, s);
+    if (e != hipSuccess || a.src.fold.partial != nullptr) return e;
     const Ranges rg = ranges_of(a.n, a.head, 4 * a.ngroups, a.vec_ok);
     const int64_t sblocks = ceil_div(rg.a_len + rg.b_len, kScalarElemsPerBlock);
     if (sblocks > 0) adam_elem_kernel<LP, WD><<<(unsigned)sblocks, kScalarBlock, 0, s>>>(a, rg);
@@ -909,30 +963,42 @@ hipError_t adam_dispatch_wd(const AdamLaunch& a, hipStream_t s)
     }
 }
 
-template <int LP, int MOM, int WD>
-hipError_t sgd_dispatch(const SgdLaunch& a, hipStream_t s)
+template <int LP, int MOM, int WD, int B, int G, int NT>
+hipError_t sgd_vec_launches(const SgdLaunch& a, int64_t vblocks, hipStream_t s)
 {
-    constexpr int G = MOM ? kSgdMomGroups : kSgdPlainGroups;
-    const int64_t groups_per_block = (int64_t)kSgdBlock * G;
-    const int64_t vblocks = a.vec_ok ? ceil_div(a.ngroups, groups_per_block) : 0;
+    constexpr int64_t groups_per_block = (int64_t)B * G;
     if (a.src.fold.partial != nullptr) {
-        if (!a.vec_ok || a.head != 0 || 4 * a.ngroups != a.n || vblocks < 1 ||
-            !one_launch(a.ngroups, kSgdBlock, G) || a.src.fold.n < 1 ||
-            a.src.fold.n > kInlineFoldMax)
-            return hipErrorInvalidValue;
-        sgd_vec_kernel<LP, MOM, WD, G, 1><<<(unsigned)vblocks, kSgdBlock, a.lds_reserve, s>>>(a);
+        sgd_vec_kernel<LP, MOM, WD, G, 1, B, NT><<<(unsigned)vblocks, B, a.lds_reserve, s>>>(a);
         return hipGetLastError();
     }
-    const int64_t max_blocks = kMaxLaunchItems / kSgdBlock;
+    const int64_t max_blocks = kMaxLaunchItems / B;
     for (int64_t b0 = 0; b0 < vblocks; b0 += max_blocks) {
         const int64_t nb = vblocks - b0 < max_blocks ? vblocks - b0 : max_blocks;
         SgdLaunch part = a;
         part.head = a.head + 4 * groups_per_block * b0;
         part.ngroups = a.ngroups - groups_per_block * b0;
-        sgd_vec_kernel<LP, MOM, WD, G, 0><<<(unsigned)nb, kSgdBlock, a.lds_reserve, s>>>(part);
+        sgd_vec_kernel<LP, MOM, WD, G, 0, B, NT><<<(unsigned)nb, B, a.lds_reserve, s>>>(part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    return hipSuccess;
+}
+
+template <int LP, int MOM, int WD>
+hipError_t sgd_dispatch(const SgdLaunch& a, hipStream_t s)
+{
+    constexpr int G = MOM ? kSgdMomGroups : kSgdPlainGroups;
+    const bool small = shard_small(a.n);
+    const int lanes = sgd_lanes(a.n), groups = sgd_groups(a.n, MOM);
+    const int64_t vblocks = a.vec_ok ? ceil_div(a.ngroups, (int64_t)lanes * groups) : 0;
+    if (a.src.fold.partial != nullptr &&
+        (!a.vec_ok || a.head != 0 || 4 * a.ngroups != a.n || vblocks < 1 ||
+         !one_launch(a.ngroups, lanes, groups) || a.src.fold.n < 1 ||
+         a.src.fold.n > kInlineFoldMax))
+        return hipErrorInvalidValue;          // the inline fold needs one vector launch
+    hipError_t e = small ? sgd_vec_launches<LP, MOM, WD, kSmallBlock, 1, 0>(a, vblocks, s)
+                         : sgd_vec_launches<LP, MOM, WD, kSgdBlock, G, 1>(a, vblocks, s);
+    if (e != hipSuccess || a.src.fold.partial != nullptr) return e;
     const Ranges rg = ranges_of(a.n, a.head, 4 * a.ngroups, a.vec_ok);
     const int64_t sblocks = ceil_div(rg.a_len + rg.b_len, kScalarElemsPerBlock);
     if (sblocks > 0)

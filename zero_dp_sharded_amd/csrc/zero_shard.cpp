@@ -605,8 +605,10 @@ static zero_status enqueue_reduce(zero_shard_s* h, const void* const* ptrs, int3
                                                  : h->lds_reduce;
     L.dev = dev;
     L.snapshot = snapshot;
-    const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W, zk::red_runs(L.R, L.nvec),
-                                             zk::red_block(L.R));
+    L.small = zk::shard_small(h->S) ? 1 : 0;
+    const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W,
+                                             zk::red_runs(L.R, L.nvec, L.small != 0),
+                                             zk::red_block(L.R, L.small != 0));
     if (L.slot_base + blocks > h->nslots)
         return fail(ZERO_ERR_UNSUPPORTED, "%s: partial slots exhausted", who);
     if (!launch) {
@@ -846,9 +848,9 @@ static bool inline_fold_ok(const zero_shard_s* h, int64_t slots)
     int32_t vec_ok;
     update_layout(h, &head, &ngroups, &vec_ok);
     if (!vec_ok || head != 0 || 4 * ngroups != h->S) return false;
-    if (h->opt == kOptAdam) return zk::one_launch(ngroups, zk::kAdamBlock, zk::kAdamGroups);
-    return zk::one_launch(ngroups, zk::kSgdBlock,
-                          h->d.exp_avg ? zk::kSgdMomGroups : zk::kSgdPlainGroups);
+    if (h->opt == kOptAdam)
+        return zk::one_launch(ngroups, zk::adam_lanes(h->S), zk::adam_groups(h->S));
+    return zk::one_launch(ngroups, zk::sgd_lanes(h->S), zk::sgd_groups(h->S, h->d.exp_avg != nullptr));
 }
 
 // Launch Adam for applied step t = h->t + 1 with hyper-parameters hp; src says
