@@ -489,6 +489,9 @@ def main() -> int:
         "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
         "copy_ceiling_gbs": copy_gbs,
         "step_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        # the step against the plain copy measured on the same box in the same
+        # run: separates the machine's HBM from the kernels' share of it
+        "step_frac_of_copy_ceiling": step_bytes / (ms_step * 1e-3) / 1e9 / copy_gbs,
         "kernels_ms": {"update_gated_flow_incl_check": adam_avg, "update_sync_flow": adam_sync,
                        "reduce_all_buckets": red_avg,
                        "reduce_gbs": (reduce_bytes / (red_avg * 1e-3) / 1e9

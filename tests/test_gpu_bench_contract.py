@@ -34,6 +34,8 @@ def test_bench_json_line(flow):
     assert (d["n_gpus"], d["steps"], d["warmup"]) == (1, 3, 1)
     assert d["higher_is_better"] is True and d["scaling"] in ("weak", "strong")
     assert d["value"] > 0 and d["ms_per_step"] > 0
+    assert abs(d["step_frac_of_copy_ceiling"] -
+               d["step_hbm_gbs"] / d["copy_ceiling_gbs"]) < 1e-9
     assert isinstance(d["config"]["workload"], str)
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
