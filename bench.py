@@ -227,7 +227,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="128b")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 27,
+    ap.add_argument("--cpu-sample", type=int, default=1 << 29,
                     help="shard elements the CPU oracle runs on (0 = skip)")
     ap.add_argument("--only", choices=["copy"], default=None,
                     help="run only the plain copy kernel (byte-counter calibration)")
