@@ -451,6 +451,33 @@ class ChunkedRun:
                     finish(*pending.popleft())
             while pending:
                 finish(*pending.popleft())
+        return self._decide(flag, sumsq)
+
+    def check_step(self, stored_of: Callable[[int, int], np.ndarray]) -> StepInfo:
+        """Pass 1 of the next step when the gradient is already stored (the P_os
+        case: the owner's slice of an all-reduced gradient, no reduce).
+        stored_of(off, n) returns the stored gradient of shard elements
+        [off, off + n); flags and sums combine in chunk order as in
+        scan_step."""
+        from collections import deque
+        from concurrent.futures import ThreadPoolExecutor
+
+        flag, sumsq = 0, 0.0
+        with ThreadPoolExecutor(self.threads) as ex:
+            pending = deque()
+            for off, n in self.chunks():
+                pending.append(ex.submit(flag_sumsq, self.lp, stored_of(off, n), self.scale))
+                while len(pending) > self.threads:
+                    f, s = pending.popleft().result()
+                    flag |= f
+                    sumsq += s
+            while pending:
+                f, s = pending.popleft().result()
+                flag |= f
+                sumsq += s
+        return self._decide(flag, sumsq)
+
+    def _decide(self, flag: int, sumsq: float) -> StepInfo:
         scale_used = self.scale
         coef = 1.0
         if not flag:

@@ -14,6 +14,7 @@ oracle's order).  Partitioning changes where the states live, not the math of
 a step (the blog.vllbc.top ZeRO/DeepSpeed page), so the owner's full shard
 must match the unsharded definition element for element.
 """
+import dataclasses
 import os
 import time
 from concurrent.futures import ThreadPoolExecutor
@@ -24,7 +25,7 @@ import torch
 
 import oracle
 import zero_dp_sharded_amd as zs
-from gpu_common import LP_CODE, hp_of, ls_of, oracle_hp, oracle_ls
+from gpu_common import LP_CODE, hp_of, ls_of, oracle_hp, oracle_ls, ulp_dist
 from zero_dp_sharded_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -63,6 +64,16 @@ def mismatches(a, b):
     return int(np.count_nonzero(bad))
 
 
+def worst_errors(a, b):
+    """(max relative error with FLT_MIN floor, max 2-byte ulp distance) of a
+    chunk; fp32 arrays give the first, 2-byte bit patterns the second."""
+    if a.dtype == np.float32:
+        a64, b64 = a.astype(np.float64), b.astype(np.float64)
+        den = np.maximum(np.abs(b64), np.finfo(np.float32).tiny)
+        return float(np.max(np.abs(a64 - b64) / den)) if a.size else 0.0
+    return int(ulp_dist(a, b).max()) if a.size else 0
+
+
 def par_mismatches(a, b):
     n = a.size
     parts = [(k * n // THREADS, (k + 1) * n // THREADS) for k in range(THREADS)]
@@ -73,6 +84,28 @@ def par_mismatches(a, b):
 @pytest.mark.parametrize("name", ["tiny", "gpt2_1.5b", "7.5b_bf16", "13b_inf", "128b",
                                   "c1_7.5b_sgdm", "c2_1.5b_sgd"])
 def test_full_shard_device_flow(name, capsys):
+    _full_shard(name, capsys)
+
+
+def test_full_shard_clipped_device_flow(capsys):
+    """The GPT-2 workload with global-norm clipping to half its typical norm:
+    the coefficient comes from the device's fixed-order fold and the oracle's
+    bucket-ordered sum, so the state is held to the fp32 tolerance (max
+    relative error 1e-6, 1 ulp on params); the stored gradients stay bitwise."""
+    w = synth.WORKLOADS["gpt2_1.5b"]
+    typical = w.grad_std / np.sqrt(w.R) * np.sqrt(w.shard)
+    _full_shard("gpt2_1.5b", capsys, max_norm=0.5 * typical)
+
+
+def test_full_shard_pos_scan_device_flow(capsys):
+    """P_os on the 128B shard (the owner's slice of an already all-reduced
+    gradient): each step the caller fills grad_shard, the device-resident step
+    scans it (contribs = NULL) and updates; every element of the final state
+    against the oracle's stored-gradient chunked evaluation."""
+    _full_shard("128b", capsys, pos=True)
+
+
+def _full_shard(name, capsys, max_norm=0.0, pos=False):
     w = synth.WORKLOADS[name]
     S, R, cb, lp_t = w.shard, w.R, w.bucket_elems, w.torch_lp
     lp = LP_CODE[w.lp]
@@ -83,17 +116,19 @@ def test_full_shard_device_flow(name, capsys):
         with capsys.disabled():
             print(f"[fullshard {name} {time.time() - t0:6.1f}s] {msg}", flush=True)
 
-    log(f"{w.name}: S={S} R={R} C_B={cb} steps={w.steps}, oracle on {THREADS} threads")
+    log(f"{w.name}: S={S} R={R} C_B={cb} steps={w.steps} max_norm={max_norm:.4g} pos={pos}, "
+        f"oracle on {THREADS} threads")
     master, m, v = synth.init_state(w, dev, seed=0)
     m = m if w.has_m else None
     v = v if w.has_v else None
     grad = torch.zeros(S, dtype=lp_t, device=dev)
     param = None if lp_t == torch.float32 else master.to(lp_t)
-    bufs = synth.alloc_contribs(w, dev)
+    bufs = [] if pos else synth.alloc_contribs(w, dev)
     host0 = {k: None if t is None else d2h(t) for k, t in
              (("master", master), ("m", m), ("v", v), ("param", param))}
     hp, ls = hp_of(w), ls_of(w)
-    run = oracle.ChunkedRun(lp, S, cb, oracle_hp(hp), oracle_ls(ls), threads=THREADS)
+    run = oracle.ChunkedRun(lp, S, cb, oracle_hp(hp), oracle_ls(ls), max_norm=max_norm,
+                            threads=THREADS)
     grads = [np.empty(S, _host_dtype(grad)) for _ in range(w.steps)]
     gpu_grad = np.empty(S, _host_dtype(grad))
     if w.opt == "sgd":
@@ -103,15 +138,24 @@ def test_full_shard_device_flow(name, capsys):
         h = zs.zero_shard_init(master, m, v, grad, param, psi=w.psi, nd=w.nd, rank=w.rank,
                                bucket_elems=cb, hp=hp, ls=ls)
     try:
+        if max_norm:
+            zs.zero_shard_set_clip(h, max_norm)
         zs.zero_device_begin(h)
         infos = []
         for s in range(w.steps):
-            # the step's contributions carry the scale the oracle's decisions so
-            # far leave (the device decides the same scale on its own)
-            synth.fill_contribs(w, bufs, s, run.scale, seed=0)
-            zs.zero_step_device(h, bufs)
-            infos.append(run.scan_step(lambda off, n: [d2h(b[off:off + n]) for b in bufs],
-                                       grads_out=grads[s]))
+            # the step's contributions (P_os: the gradient itself) carry the
+            # scale the oracle's decisions so far leave (the device decides the
+            # same scale on its own)
+            if pos:
+                synth.fill_contribs(dataclasses.replace(w, R=1), [grad], s, run.scale, seed=0)
+                zs.zero_step_device(h, None)
+                d2h(grad, grads[s])
+                infos.append(run.check_step(lambda off, n: grads[s][off:off + n]))
+            else:
+                synth.fill_contribs(w, bufs, s, run.scale, seed=0)
+                zs.zero_step_device(h, bufs)
+                infos.append(run.scan_step(lambda off, n: [d2h(b[off:off + n]) for b in bufs],
+                                           grads_out=grads[s]))
             torch.cuda.synchronize()
             bad = par_mismatches(d2h(grad, gpu_grad), grads[s])
             log(f"step {s}: overflow={infos[-1].overflow} t={infos[-1].step_t} "
@@ -144,10 +188,17 @@ def test_full_shard_device_flow(name, capsys):
         parts = {k: host0[k][sl].copy() for k in keys}
         run.evolve(parts["master"], parts.get("m"), parts.get("v"), parts.get("param"),
                    lambda s: grads[s][sl])
-        return {k: mismatches(parts[k], final[k][sl]) for k in keys}
+        return {k: (mismatches(parts[k], final[k][sl]), worst_errors(final[k][sl], parts[k]))
+                for k in keys}
 
     with ThreadPoolExecutor(THREADS) as ex:
         results = list(ex.map(chunk, run.chunks()))
-    total = {k: sum(r[k] for r in results) for k in keys}
-    log(f"final state mismatches over {S} elements: {total}")
-    assert all(v == 0 for v in total.values()), total
+    total = {k: sum(r[k][0] for r in results) for k in keys}
+    worst = {k: max(r[k][1] for r in results) for k in keys}
+    log(f"final state mismatches over {S} elements: {total}; worst errors {worst}")
+    if max_norm:
+        # the fp32 tolerance: the clipping coefficient comes from two fp64 orders
+        for k in keys:
+            assert worst[k] <= (1 if k == "param" else 1e-6), (k, worst[k])
+    else:
+        assert all(v == 0 for v in total.values()), total

@@ -161,3 +161,50 @@ def test_chunked_norm_order_is_the_bucket_order(oracle):
     assert f == 0 and s == acc
     u = oracle.lp_to_f32(FP16, g).astype(np.float64) / 4.0
     assert s == pytest.approx(math.fsum(u * u), rel=1e-13)
+
+
+@pytest.mark.parametrize("lp,max_norm", [(FP16, 0.0), (BF16, 0.0), (FP16, 0.3)])
+def test_chunked_check_of_stored_gradient(oracle, lp, max_norm):
+    """The stored-gradient form (no reduce: the owner's slice of an all-reduced
+    gradient) chunked, against the same steps written out with the oracle's
+    primitives on the whole shard: flag and squared norm per bucket
+    (bucket_flag_sumsq), the decision, the update.  A planted inf in one step
+    is skipped."""
+    n, cb, steps = 100_003, 16_384, 4
+    hp = oracle.AdamHP(lr=1e-3, weight_decay=0.01)
+    ls = oracle.LossScale(init_scale=1024.0)
+    rng = np.random.default_rng(9)
+    master0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    grads = []
+    for s in range(steps):
+        x = (rng.standard_normal(n) * 1e-3 * 1024.0).astype(np.float32)
+        if s == 2:
+            x[n - 5] = np.inf
+        grads.append(oracle.f32_to_lp(lp, x))
+    # whole shard, by hand
+    st = oracle.new_state(lp, master0, np.zeros(n, np.float32), np.zeros(n, np.float32), hp, ls)
+    flags = []
+    for g in grads:
+        flag, ss = oracle.bucket_flag_sumsq(lp, g, st.scale, cb)
+        flags.append(flag)
+        if not flag:
+            st.t += 1
+            sc = oracle.adam_scalars(hp, st.t, st.scale, oracle.clip_coef(ss, max_norm))
+            oracle.adam_update(lp, g, st.master, st.m, st.v, st.param, sc, hp.wd_mode)
+        st.scale, st.good_steps = oracle.loss_scale_next(flag, ls, st.scale, st.good_steps)
+    assert flags == [0, 0, 1, 0]
+    # chunked
+    run = oracle.ChunkedRun(lp, n, cb, hp, ls, max_norm=max_norm, threads=3)
+    for g in grads:
+        run.check_step(lambda off, k: g[off:off + k])
+    master, m, v = master0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    param = oracle.f32_to_lp(lp, master0)
+    for off, k in reversed(run.chunks()):
+        sl = slice(off, off + k)
+        parts = [master[sl].copy(), m[sl].copy(), v[sl].copy(), param[sl].copy()]
+        run.evolve(*parts, lambda s: grads[s][sl])
+        master[sl], m[sl], v[sl], param[sl] = parts
+    for a, b in ((master, st.master), (m, st.m), (v, st.v)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(param, st.param)
+    assert (run.t, run.scale, run.good_steps) == (st.t, st.scale, st.good_steps)
