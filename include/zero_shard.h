@@ -441,9 +441,10 @@ zero_status zero_device_end(zero_shard_t h, void* stream, zero_step_info* out);
  * of device memory, one per GPU, held until the process ends: a shard whose
  * check needs more than 523,232 partial slots is refused (about 267M 2-byte
  * elements with 8 or more contributions, up to 800M with fewer and buckets of
- * at least 3.9M elements, 134M fp32 elements with 8 or more).  Every call on a GPU shares that GPU's array, so calls that
- * overlap on one GPU (other threads, or other streams before this call's
- * update has run) race; calls in order on one stream do not.  Synchronises
+ * at least 3.9M elements, 134M fp32 elements with 8 or more).  Every call on
+ * a GPU shares that GPU's array, so calls that overlap on one GPU (other
+ * threads, or other streams before this call's update has run) race; calls in
+ * order on one stream do not.  Synchronises
  * `stream` once (for the check); the update stays asynchronous on it.
  * Errors: INVALID_ARG (as zero_shard_init and zero_step_device, counters out
  * of range, max_grad_norm negative or not finite, a shard too large for the

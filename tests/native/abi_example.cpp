@@ -1,11 +1,14 @@
 // A native user of libzeroshard.so: plain HIP memory and streams, no torch,
-// no Python.  Runs steps of an fp16 Adam shard through the C ABI in three
+// no Python.  Runs steps of an fp16 Adam shard through the C ABI in four
 // ways and checks every one against the oracle (linked in from oracle/, test
 // infrastructure), bitwise:
 //   1. the synchronous check flow (bucket reduces, check, Adam);
 //   2. the device-resident flow, one zero_step_device per step;
 //   3. the device-resident step captured once with the HIP graph API
-//      (hipStreamBeginCapture / hipGraphInstantiate) and replayed per step.
+//      (hipStreamBeginCapture / hipGraphInstantiate) and replayed per step;
+//   4. the allocation-free step (zero_adam_step_noalloc: no handle, the
+//      counters carried by the caller), the form for callers that cannot
+//      allocate device memory.
 // Exit status 0 and a last line "abi_example ok" on success.
 #include <hip/hip_runtime.h>
 
@@ -179,20 +182,22 @@ int main()
     CHECK_HIP(hipMalloc(&param, S * 2));
     for (int r = 0; r < R; ++r) CHECK_HIP(hipMalloc(&contrib[r], S * 2));
 
-    for (int mode = 0; mode < 3; ++mode) {
+    for (int mode = 0; mode < 4; ++mode) {
         CHECK_HIP(hipMemcpy(master, init.master.data(), S * 4, hipMemcpyHostToDevice));
         CHECK_HIP(hipMemcpy(m, init.m.data(), S * 4, hipMemcpyHostToDevice));
         CHECK_HIP(hipMemcpy(v, init.v.data(), S * 4, hipMemcpyHostToDevice));
         CHECK_HIP(hipMemcpy(param, init.param.data(), S * 2, hipMemcpyHostToDevice));
         zero_shard_desc d{S, 1, 0, CB, ZERO_FP16, master, m, v, grad, param};
         zero_shard_t h = nullptr;
-        CHECK_Z(zero_shard_init(&d, &hp, &ls, &h));
+        if (mode < 3) CHECK_Z(zero_shard_init(&d, &hp, &ls, &h));
+        int64_t t = 0, good = 0;          // the counters the allocation-free step carries
+        double scale = kScale;
         const void* cp[R];
         for (int r = 0; r < R; ++r) cp[r] = contrib[r];
         hipGraphExec_t exec = nullptr;
         hipGraph_t graph = nullptr;
         zero_step_info info;
-        if (mode >= 1) CHECK_Z(zero_device_begin(h, stream));
+        if (mode == 1 || mode == 2) CHECK_Z(zero_device_begin(h, stream));
         for (int s = 0; s < kSteps; ++s) {
             for (int r = 0; r < R; ++r)
                 CHECK_HIP(hipMemcpyAsync(contrib[r], steps[s][r].data(), S * 2, hipMemcpyHostToDevice,
@@ -209,6 +214,9 @@ int main()
                 CHECK_Z(zero_adam_step(h, nullptr, stream, &info));
             } else if (mode == 1) {
                 CHECK_Z(zero_step_device(h, cp, R, stream));
+            } else if (mode == 3) {
+                CHECK_Z(zero_adam_step_noalloc(&d, &hp, &ls, 0.0, cp, R, &t, &scale, &good, stream,
+                                               &info));
             } else {
                 if (exec == nullptr) {
                     // capture the whole step once; every replay is one step
@@ -221,7 +229,12 @@ int main()
             }
             CHECK_HIP(hipStreamSynchronize(stream));
         }
-        if (mode >= 1) CHECK_Z(zero_device_end(h, stream, &info));
+        if (mode == 1 || mode == 2) CHECK_Z(zero_device_end(h, stream, &info));
+        if (mode == 3 && (t != kSteps || scale != kScale || good != kSteps)) {
+            std::fprintf(stderr, "allocation-free step: counters %lld %g %lld\n", (long long)t,
+                         scale, (long long)good);
+            ++failures;
+        }
         if (exec) CHECK_HIP(hipGraphExecDestroy(exec));
         if (graph) CHECK_HIP(hipGraphDestroy(graph));
         if (info.overflow != 0 || info.step_t != kSteps) {
@@ -238,7 +251,8 @@ int main()
         CHECK_HIP(hipMemcpy(got.m.data(), m, S * 4, hipMemcpyDeviceToHost));
         CHECK_HIP(hipMemcpy(got.v.data(), v, S * 4, hipMemcpyDeviceToHost));
         CHECK_HIP(hipMemcpy(got.param.data(), param, S * 2, hipMemcpyDeviceToHost));
-        const char* names[3] = {"synchronous flow", "device-resident flow", "graph replays"};
+        const char* names[4] = {"synchronous flow", "device-resident flow", "graph replays",
+                                "allocation-free step"};
         char what[96];
         std::snprintf(what, sizeof(what), "%s: master", names[mode]);
         expect_equal(what, got.master.data(), ref.master.data(), S * 4);
@@ -248,7 +262,7 @@ int main()
         expect_equal(what, got.v.data(), ref.v.data(), S * 4);
         std::snprintf(what, sizeof(what), "%s: param", names[mode]);
         expect_equal(what, got.param.data(), ref.param.data(), S * 2);
-        CHECK_Z(zero_shard_destroy(h));
+        if (h) CHECK_Z(zero_shard_destroy(h));
         std::printf("%s: %d steps, bitwise equal to the oracle: %s\n", names[mode], kSteps,
                     failures ? "no" : "yes");
     }

@@ -286,3 +286,48 @@ def test_binding_refuses_bad_contribution_tensors():
             zs.zero_bucket_reduce(h, [good[:100]], 0, 100)
     finally:
         zs._handles.pop(h, None)
+
+
+def _noalloc(desc=None, hp=None, ls=None, max_norm=0.0, counters=(0, 1024.0, 0)):
+    t, sc, g = ctypes.c_int64(counters[0]), ctypes.c_double(counters[1]), \
+        ctypes.c_int64(counters[2])
+    return zs.lib().zero_adam_step_noalloc(
+        None if desc is False else ctypes.byref(desc or _desc()),
+        None if hp is False else ctypes.byref(hp or GOOD_HP),
+        None if ls is False else ctypes.byref(ls or GOOD_LS),
+        max_norm, None, 0, ctypes.byref(t), ctypes.byref(sc), ctypes.byref(g), None, None), \
+        (t.value, sc.value, g.value)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(desc=False), dict(hp=False), dict(ls=False),
+    dict(desc=_desc(psi=0)), dict(desc=_desc(rank=4)), dict(desc=_desc(lp=7)),
+    dict(desc=_desc(master=0)), dict(desc=_desc(grad_shard=0x60001)),
+    dict(hp=zs.ZeroAdamHParams(1e-3, 1.0, 0.999, 1e-8, 0.0, 1, 0, 0)),
+    dict(ls=zs.ZeroLossScaleCfg(0.0, 1, 1000, 1.0)),
+    dict(counters=(-1, 1024.0, 0)), dict(counters=(0, 0.0, 0)),
+    dict(counters=(0, float("inf"), 0)), dict(counters=(0, 1e-40, 0)),
+    dict(counters=(0, 1024.0, -1)),
+    dict(max_norm=-1.0), dict(max_norm=float("nan")), dict(max_norm=float("inf")),
+], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
+def test_noalloc_rejects_bad_arguments_before_device_work(kw):
+    """The allocation-free step validates its desc, hyper-parameters, loss-scale
+    configuration, counters and clipping limit before it touches a device (the
+    same rules as zero_shard_init and zero_shard_set_counters), and leaves the
+    caller's counters untouched when it refuses."""
+    counters = kw.get("counters", (0, 1024.0, 0))
+    s, after = _noalloc(**kw)
+    assert s == zs.ZERO_ERR_INVALID_ARG, (s, zs.zero_last_error())
+    assert zs.zero_last_error()
+    assert after == counters
+
+
+def test_noalloc_null_counters():
+    L = zs.lib()
+    t, sc = ctypes.c_int64(0), ctypes.c_double(1.0)
+    for args in ((None, ctypes.byref(sc), ctypes.byref(t)),
+                 (ctypes.byref(t), None, ctypes.byref(t)),
+                 (ctypes.byref(t), ctypes.byref(sc), None)):
+        assert L.zero_adam_step_noalloc(ctypes.byref(_desc()), ctypes.byref(GOOD_HP),
+                                        ctypes.byref(GOOD_LS), 0.0, None, 0, *args, None,
+                                        None) == zs.ZERO_ERR_INVALID_ARG

@@ -1,7 +1,8 @@
 """The C ABI used natively (plain HIP memory and streams, the HIP graph API, no
 torch): tests/native/abi_example runs fp16 Adam steps through the synchronous
-flow, the device-resident flow and graph replays of a captured
-device-resident step, and checks each against the oracle bitwise;
+flow, the device-resident flow, graph replays of a captured device-resident
+step and the allocation-free step, and checks each against the oracle
+bitwise;
 tests/native/step_latency times device-resident steps enqueued directly and
 replayed from graphs of one and ten steps."""
 import os
@@ -26,7 +27,7 @@ def test_native_abi_example():
     assert r.returncode == 0, r.stderr
     lines = r.stdout.strip().splitlines()
     assert lines[-1] == "abi_example ok"
-    assert sum("bitwise equal to the oracle: yes" in ln for ln in lines) == 3
+    assert sum("bitwise equal to the oracle: yes" in ln for ln in lines) == 4
 
 
 LATENCY = os.path.join(ROOT, "tests", "native", "step_latency")
