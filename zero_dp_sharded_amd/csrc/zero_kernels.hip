@@ -162,7 +162,7 @@ __device__ __forceinline__ void check_s(typename Fmt<LP>::T o, float inv_scale, 
 }
 
 // One fp64 partial per workgroup: the sum of its lanes' squares, or NaN when
-// any lane saw a non-finite stored value.  Fixed reduction shape, so the
+// any lane saw a non-finite unscaled value.  Fixed reduction shape, so the
 // value is bitwise reproducible.
 template <int BS>
 __device__ __forceinline__ void block_partial(double* slot, int flag, double ss)
