@@ -3,12 +3,13 @@
 // the known-size reference that calibrates the rocprofv3 byte counters.  Not
 // part of the owner-rank step.
 //
-// Shape: the fastest plain copy measured on MI355X (8 GB of random bits,
-// nontemporal loads and stores): one-wave workgroups, each lane four 16-byte
-// vectors (all four loads issued before the stores), residency capped at 16
-// workgroups per CU by reserving dynamic LDS the kernel never touches.  It
-// moved 6.62 TB/s, against 6.45 TB/s for one vector per lane on 256-lane
-// workgroups at full occupancy.
+// Shape: the fastest plain copy measured on MI355X (8e9 bytes of random bits,
+// nontemporal loads and stores, interleaved sweeps on one box): one-wave
+// workgroups, each lane one 16-byte vector, residency capped at 32 workgroups
+// per CU by reserving dynamic LDS the kernel never touches.  It moved
+// 6.66-6.70 TB/s, against 6.57-6.61 TB/s for four vectors per lane at 16 per
+// CU, 6.45-6.53 TB/s at 24 per CU and 6.45 TB/s for 256-lane workgroups at 8
+// per CU.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -18,8 +19,8 @@ namespace {
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 64;
-constexpr int kRuns = 4;
-constexpr int kPerCU = 16;
+constexpr int kRuns = 1;
+constexpr int kPerCU = 32;
 
 __global__ __launch_bounds__(kBlock) void hbm_copy_kernel(const f4* __restrict__ src,
                                                           f4* __restrict__ dst, int64_t n16)
@@ -41,12 +42,12 @@ __global__ __launch_bounds__(kBlock) void hbm_copy_kernel(const f4* __restrict__
 }  // namespace
 
 // Copy `bytes` bytes (a multiple of 16, both pointers 16-byte aligned, at most
-// 2^36 bytes) from src to dst on `stream`, on the current device.  Returns 0
-// on success, 1 on a bad argument, 2 on a HIP error.
+// 2^34 bytes, so at most 2^30 work-items) from src to dst on `stream`, on the
+// current device.  Returns 0 on success, 1 on a bad argument, 2 on a HIP error.
 extern "C" int hbm_copy(void* dst, const void* src, int64_t bytes, void* stream)
 {
     if (!dst || !src || bytes <= 0 || (bytes & 15) || ((uintptr_t)dst & 15) ||
-        ((uintptr_t)src & 15) || bytes > (int64_t(1) << 36))
+        ((uintptr_t)src & 15) || bytes > (int64_t(1) << 34))
         return 1;
     int dev = 0, lds_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
