@@ -119,3 +119,21 @@ def test_sample_parity_reports_bitwise_and_relative_error():
     gpu["m"] = None                                              # SGD without momentum
     gpu["v"] = None
     assert bench.sample_parity(gpu, st, n, (7, 4096.0, 7))["fp32_state_bitwise"]
+
+
+def test_copy_helper_refuses_bad_arguments_before_device_work():
+    """bench.py's copy kernel (its bandwidth ceiling and counter calibration)
+    refuses NULL pointers, sizes that are not a positive multiple of 16 or
+    exceed 2^34 bytes (at most 2^30 work-items), and misaligned pointers,
+    returning 1 before any HIP call."""
+    import ctypes
+    path = os.path.join(ROOT, "zero_dp_sharded_amd", "libhbmcopy.so")
+    if not os.path.exists(path):
+        pytest.skip("libhbmcopy.so is not built")
+    lib = ctypes.CDLL(path)
+    lib.hbm_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.hbm_copy.restype = ctypes.c_int
+    a, b = 0x10000, 0x20000
+    for dst, src, n in ((None, b, 16), (a, None, 16), (a, b, 0), (a, b, -16), (a, b, 24),
+                        (a + 8, b, 16), (a, b + 4, 16), (a, b, (1 << 34) + 16)):
+        assert lib.hbm_copy(dst, src, n, None) == 1, (dst, src, n)
