@@ -91,11 +91,19 @@ constexpr int64_t kRedSmallNvec = (int64_t)256 * ZK_RED_PER_CU * ZK_RED_BLOCK * 
 constexpr int kScanBlock = ZK_SCAN_BLOCK;
 constexpr int kScanRuns = ZK_SCAN_RUNS;
 constexpr int kScanPerCU = ZK_SCAN_PER_CU;
+// A bucket whose contributions and output share an address phase only modulo
+// 8 or 4 bytes, not 16, moves each 16-byte run as `pieces` (2 or 4) aligned
+// pieces: one-wave workgroups, kRedPieceRunsFew runs per lane below 8
+// contributions (so that enough bytes are in flight), one from 8 and on the
+// buckets of small shards.
+constexpr int kRedPieceBlock = 64;
+constexpr int kRedPieceRunsFew = 3;
 constexpr int kMin2(int a, int b) { return a < b ? a : b; }
 // runs one vector reduce or scan workgroup covers at the least
 constexpr int64_t kRunsPerBlockMin =
-    kMin2(kMin2(kRedBlock * kMin2(kRedRuns, kRedRunsSmall), kRedBlockMany * kRedRunsMany),
-          kScanBlock * kScanRuns);
+    kMin2(kMin2(kMin2(kRedBlock * kMin2(kRedRuns, kRedRunsSmall), kRedBlockMany * kRedRunsMany),
+                kScanBlock * kScanRuns),
+          kRedPieceBlock);
 constexpr int kRedPerCU = ZK_RED_PER_CU;
 constexpr int kRedPerCUMany = ZK_RED_PER_CU_MANY;   // residency when 8 <= R < 16, fp32
 constexpr int kRedPerCUMany2B = ZK_RED_PER_CU_MANY_2B;   // the same, 2-byte storage
@@ -132,14 +140,16 @@ constexpr int64_t kSmallElems = ZK_SMALL_ELEMS;
 constexpr int kSmallBlock = 256;
 inline bool shard_small(int64_t S) { return S <= kSmallElems; }
 // Lanes per workgroup and runs per lane of a bucket reduce (nvec runs, R
-// contributions) of a small shard or not.
-inline int red_block(int R, bool small)
+// contributions) of a small shard or not, in whole runs (pieces = 1) or pieces.
+inline int red_block(int R, bool small, int pieces = 1)
 {
+    if (pieces > 1) return kRedPieceBlock;
     if (small) return kSmallBlock;
     return R >= kRedManyR ? kRedBlockMany : kRedBlock;
 }
-inline int red_runs(int R, int64_t nvec, bool small)
+inline int red_runs(int R, int64_t nvec, bool small, int pieces = 1)
 {
+    if (pieces > 1) return small || R >= kRedManyR ? 1 : kRedPieceRunsFew;
     if (small) return 1;
     if (R >= kRedManyR) return kRedRunsMany;
     return nvec < kRedSmallNvec ? kRedRunsSmall : kRedRuns;
@@ -209,8 +219,10 @@ struct PrepareArgs {
 
 // One bucket of the reduce.  Elements [0, n) of the bucket; the vector body
 // starts at `head` and holds `nvec` 16-byte runs (8 two-byte or 4 fp32
-// elements) that are 16-byte aligned in every contribution and in `out`.
-// vec_ok = 0 selects the element-wise path.  Workgroup b writes
+// elements) that are 16-byte aligned in every contribution and in `out`
+// (pieces = 1), or only 16/pieces-byte aligned (pieces = 2 or 4: each run is
+// moved as that many aligned pieces).  vec_ok = 0 selects the element-wise
+// path.  Workgroup b writes
 // partial[slot_base + b]: the fp64 sum of the squared unscaled stored values
 // of its elements, or NaN if any unscaled value is not finite.  The unscale
 // factor is inv_scale, or dev->inv_scale when dev is set.
@@ -229,6 +241,7 @@ struct ReduceLaunch {
     int64_t slot_base;
     uint32_t lds_reserve;  // dynamic LDS that caps workgroups per CU
     int32_t small;         // 1: a bucket of a small shard (see shard_small)
+    int32_t pieces;        // 1, 2 or 4 aligned pieces per run (see kRedPieceBlock)
     const DevState* dev;
     DevState* snapshot;    // set: workgroup 0 copies *dev there (see InlineFold)
 };

@@ -47,6 +47,9 @@ typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef __bf16 b4 __attribute__((ext_vector_type(4)));
 typedef float f8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 
 // Per storage format: element type T, the 16-byte run VW of W elements with
 // its fp32 image FW, and the 4-element group V4 of the update kernels.
@@ -72,6 +75,16 @@ template <> struct Fmt<3> {            // IEEE binary32
     using FW = f4;
     using V4 = f4;
 };
+
+// One of H aligned pieces of a 16-byte run: N = W / H elements of storage
+// type P (a scalar when N = 1) and their fp32 image F.
+template <int LP, int H> struct Piece;
+template <> struct Piece<1, 2> { static constexpr int N = 4; using P = h4; using F = f4; };
+template <> struct Piece<1, 4> { static constexpr int N = 2; using P = h2; using F = f2; };
+template <> struct Piece<2, 2> { static constexpr int N = 4; using P = b4; using F = f4; };
+template <> struct Piece<2, 4> { static constexpr int N = 2; using P = b2; using F = f2; };
+template <> struct Piece<3, 2> { static constexpr int N = 2; using P = f2; using F = f2; };
+template <> struct Piece<3, 4> { static constexpr int N = 1; using P = float; using F = float; };
 
 template <typename V>
 __device__ __forceinline__ V ld_nt(const void* base, int64_t idx)
@@ -312,6 +325,99 @@ __global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
                 }
             }
             reduce_finish<LP, NT>(L, vi, acc, inv_scale, flag, ss);
+        }
+    }
+    if constexpr (SNAP) snapshot_state(L.dev, L.snapshot);
+    block_partial<BS>(L.partial + L.slot_base + blockIdx.x, flag, ss);
+}
+
+// fp32 image of a piece, and a piece rounded (to nearest even) from its fp32
+// image; element k of an fp32 image.  N = 1 pieces are scalars.
+template <int N, typename F, typename P>
+__device__ __forceinline__ F widen(P x)
+{
+    if constexpr (N == 1) return static_cast<F>(x);
+    else return __builtin_convertvector(x, F);
+}
+
+template <int N, typename P, typename F>
+__device__ __forceinline__ P narrow(F x)
+{
+    if constexpr (N == 1) {
+        return static_cast<P>(pin_f32(x));
+    } else {
+#pragma unroll
+        for (int k = 0; k < N; ++k) x[k] = pin_f32(x[k]);
+        return __builtin_convertvector(x, P);
+    }
+}
+
+template <int N, typename F>
+__device__ __forceinline__ float elem(const F& x, int k)
+{
+    if constexpr (N == 1) return x;
+    else return x[k];
+}
+
+// Vector body of a bucket whose contributions and output share an address
+// phase only modulo 16/H bytes (H = 2: 8 bytes, H = 4: 4 bytes): the same runs
+// as reduce_vec_kernel, U per lane on kRedPieceBlock lanes, each moved as H
+// aligned pieces of N = W/H elements.  Workgroup b covers runs
+// [b*BS*U, (b+1)*BS*U), that is pieces [b*BS*U*H, (b+1)*BS*U*H); lane l owns
+// pieces b*BS*U*H + j*BS + l, j < U*H, so each load instruction of a wave
+// covers BS*16/H contiguous bytes.  The contributions are loaded K at a time
+// (8 with one run per lane, 4 with more: 128-192 bytes per lane), every piece
+// of them in flight before the arithmetic, and added in ascending r from +0:
+// each element's result is the vector kernel's.
+template <int LP, int H, int U, int SNAP, int NT>
+__global__ __launch_bounds__(kRedPieceBlock) void reduce_piece_kernel(ReduceLaunch L)
+{
+    using Pc = Piece<LP, H>;
+    using P = typename Pc::P;
+    using F = typename Pc::F;
+    constexpr int N = Pc::N, BS = kRedPieceBlock, J = U * H, K = U == 1 ? 8 : 4;
+    int flag = 0;
+    double ss = 0.0;
+    const float inv_scale = check_inv_scale(L.inv_scale, L.dev);
+    const int64_t npieces = L.nvec * H;
+    const int64_t q0 = (int64_t)blockIdx.x * (BS * J) + threadIdx.x;
+    F acc[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) acc[j] = (F)(0.f);
+    for (int r0 = 0; r0 < L.R; r0 += K) {
+        const int cnt = L.R - r0 < K ? L.R - r0 : K;
+        P x[K][J];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if (k < cnt) {
+                const void* base = adv<LP>(L.c.p[r0 + k], L.head);
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    const int64_t q = q0 + j * BS;
+                    if (q < npieces) x[k][j] = ld_v<P, NT>(base, q);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if (k < cnt) {
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    const int64_t q = q0 + j * BS;
+                    if (q < npieces) acc[j] = acc[j] + widen<N, F>(x[k][j]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int64_t q = q0 + j * BS;
+        if (q < npieces) {
+            const P o = narrow<N, P>(acc[j] * L.inv_r);
+            st_v<P, NT>(adv<LP>(L.out, L.head), q, o);
+            const F of = widen<N, F>(o);
+#pragma unroll
+            for (int k = 0; k < N; ++k) check_u(elem<N>(of, k) * inv_scale, flag, ss);
         }
     }
     if constexpr (SNAP) snapshot_state(L.dev, L.snapshot);
@@ -854,13 +960,46 @@ hipError_t reduce_vec_launch(const ReduceLaunch& L, unsigned grid, int U, bool s
     return hipGetLastError();
 }
 
+// The piece kernel of a bucket (L.pieces = 2 or 4) with U runs per lane (the
+// count red_runs gave the host): nontemporal for the buckets of large shards,
+// plain for small ones, as the vector kernels.
+template <int LP, int H, int U>
+void reduce_piece_go(const ReduceLaunch& L, unsigned grid, hipStream_t s)
+{
+    const bool nt = L.small == 0;
+    if (L.snapshot != nullptr) {
+        if (nt)
+            reduce_piece_kernel<LP, H, U, 1, 1><<<grid, kRedPieceBlock, L.lds_reserve, s>>>(L);
+        else
+            reduce_piece_kernel<LP, H, U, 1, 0><<<grid, kRedPieceBlock, L.lds_reserve, s>>>(L);
+    } else {
+        if (nt)
+            reduce_piece_kernel<LP, H, U, 0, 1><<<grid, kRedPieceBlock, L.lds_reserve, s>>>(L);
+        else
+            reduce_piece_kernel<LP, H, U, 0, 0><<<grid, kRedPieceBlock, L.lds_reserve, s>>>(L);
+    }
+}
+
+template <int LP>
+hipError_t reduce_piece_launch(const ReduceLaunch& L, unsigned grid, int U, hipStream_t s)
+{
+    if (L.pieces == 2) {
+        if (U == kRedPieceRunsFew) reduce_piece_go<LP, 2, kRedPieceRunsFew>(L, grid, s);
+        else reduce_piece_go<LP, 2, 1>(L, grid, s);
+    } else {
+        if (U == kRedPieceRunsFew) reduce_piece_go<LP, 4, kRedPieceRunsFew>(L, grid, s);
+        else reduce_piece_go<LP, 4, 1>(L, grid, s);
+    }
+    return hipGetLastError();
+}
+
 template <int LP>
 hipError_t reduce_dispatch(const ReduceLaunch& L, hipStream_t s)
 {
     constexpr int W = Fmt<LP>::W;
     const bool small = L.small != 0;
-    const int U = red_runs(L.R, L.nvec, small);
-    const int BS = red_block(L.R, small);
+    const int U = red_runs(L.R, L.nvec, small, L.pieces);
+    const int BS = red_block(L.R, small, L.pieces);
     const int64_t runs_per_block = (int64_t)BS * U;
     const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, runs_per_block) : 0;
     // consecutive launches of at most kMaxLaunchItems work-items; each starts
@@ -872,7 +1011,8 @@ hipError_t reduce_dispatch(const ReduceLaunch& L, hipStream_t s)
         part.head = L.head + W * runs_per_block * b0;
         part.nvec = L.nvec - runs_per_block * b0;
         part.slot_base = L.slot_base + b0;
-        hipError_t e = reduce_vec_launch<LP>(part, (unsigned)nb, U, small, s);
+        hipError_t e = L.pieces > 1 ? reduce_piece_launch<LP>(part, (unsigned)nb, U, s)
+                                    : reduce_vec_launch<LP>(part, (unsigned)nb, U, small, s);
         if (e != hipSuccess) return e;
     }
     const Ranges rg = ranges_of(L.n, L.head, W * L.nvec, L.vec_ok);

@@ -593,7 +593,17 @@ static zero_status enqueue_reduce(zero_shard_s* h, const void* const* ptrs, int3
     L.out = out;
     L.n = len;
     const int W = zk::run_width(h->d.lp);
-    split(len, common_head(addr, elt, align, n_contrib + 1), W, &L.head, &L.nvec, &L.vec_ok);
+    // whole 16-byte runs when every array shares its address phase modulo 16;
+    // else pieces of 8 or 4 bytes when they share it modulo that; else the
+    // element-wise kernel
+    int64_t head = common_head(addr, elt, align, n_contrib + 1);
+    L.pieces = 1;
+    for (int a = 8; head < 0 && a >= 4; a /= 2) {
+        for (int k = 0; k <= n_contrib; ++k) align[k] = a;
+        head = common_head(addr, elt, align, n_contrib + 1);
+        if (head >= 0) L.pieces = 16 / a;
+    }
+    split(len, head, W, &L.head, &L.nvec, &L.vec_ok);
     L.R = n_contrib;
     L.lp = (int32_t)h->d.lp;
     L.inv_r = (float)(1.0 / (double)n_contrib);
@@ -607,8 +617,8 @@ static zero_status enqueue_reduce(zero_shard_s* h, const void* const* ptrs, int3
     L.snapshot = snapshot;
     L.small = zk::shard_small(h->S) ? 1 : 0;
     const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W,
-                                             zk::red_runs(L.R, L.nvec, L.small != 0),
-                                             zk::red_block(L.R, L.small != 0));
+                                             zk::red_runs(L.R, L.nvec, L.small != 0, L.pieces),
+                                             zk::red_block(L.R, L.small != 0, L.pieces));
     if (L.slot_base + blocks > h->nslots)
         return fail(ZERO_ERR_UNSUPPORTED, "%s: partial slots exhausted", who);
     if (!launch) {
