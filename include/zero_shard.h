@@ -38,12 +38,11 @@
  *    16-byte boundary differ in element count (for example a param slice one
  *    element off the master's phase) leave no common vector layout, and the
  *    update then runs element-wise, measured 12-23% slower for an offset
- *    2-byte array on MI355X.  A bucket reduce whose contributions and output
- *    share their phase modulo 8 or 4 bytes (not 16) moves its runs as aligned
- *    8- or 4-byte pieces, measured 5-15% slower than aligned contributions;
- *    2-byte arrays whose phases differ modulo 4 bytes reduce element-wise,
- *    about 3x slower.  Before any launch the library asks the HIP
- *    runtime about every array and contribution and refuses (INVALID_ARG)
+ *    2-byte array on MI355X.  A bucket reduce whose contributions do not
+ *    share the output's phase modulo 16 bytes cuts each contribution's runs
+ *    out of aligned 16-byte loads (any phase, 2-byte or fp32), measured 4-10%
+ *    slower than aligned contributions.  Before any launch the library asks
+ *    the HIP runtime about every array and contribution and refuses (INVALID_ARG)
  *    pageable host memory, another device's memory, and a range that runs
  *    past the end of its allocation; this is best effort (the runtime sees
  *    allocations, not the caller's tensors inside them), not a guarantee.

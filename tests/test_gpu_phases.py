@@ -1,17 +1,20 @@
 """Bucket reduces whose contributions do not share one 16-byte address phase.
 
 When every contribution and the output share their address phase modulo 16
-bytes the reduce moves whole 16-byte runs; when they share it only modulo 8
-or 4 bytes it moves each run as 2 or 4 aligned pieces (reduce_piece_kernel);
-otherwise it falls back to the element-wise kernel.  Each case places the R
-contributions at their own byte offsets from a 16-byte boundary (as a caller
-gets when it carves them back to back from one buffer of a shard whose size
-is not a multiple of 8 elements), runs several steps in the synchronous,
-gated and device-resident flows, and compares every step's flag, norm and
-stored gradient and the final state with the oracle, bitwise.  Buckets of an
-odd size start at a different phase each, so the layout changes from bucket
-to bucket; one shard is above the small-shard limit (nontemporal pieces), one
-small enough for the device-resident step to fold its partials inline."""
+bytes the reduce moves whole aligned 16-byte runs; otherwise the shift kernel
+keeps the output runs aligned and cuts each contribution's runs out of the two
+aligned 16-byte words around them (reduce_shift_kernel), with a scalar head
+long enough to cover the largest phase and one whole run kept after the body.
+Each case places the R contributions at their own byte offsets from a 16-byte
+boundary (as a caller gets when it carves them back to back from one buffer of
+a shard whose size is not a multiple of 8), runs several steps in the
+synchronous, gated and device-resident flows, and compares every step's flag,
+norm and stored gradient and the final state with the oracle, bitwise.
+Buckets of an odd size start at a different phase each, so the layout changes
+from bucket to bucket; one shard is above the small-shard limit (nontemporal
+kernels with one and three runs per lane), one small enough for the
+device-resident step to fold its partials inline, and a sweep of tiny buckets
+covers the bodies of zero and one run."""
 import dataclasses
 
 import numpy as np
@@ -31,9 +34,13 @@ STEPS = 3
 
 # byte offsets of the contributions from a 16-byte boundary, and of grad_shard
 PHASES = {
-    "8-byte pieces": ([0, 8, 8, 0], 0),
-    "4-byte pieces": ([4, 8, 12, 0, 4], 8),
-    "2-byte phases: element-wise": ([0, 2, 6], 0),
+    "8-byte phases": ([0, 8, 8, 0], 0),
+    "4-byte phases": ([4, 8, 12, 0, 4], 8),
+    "2-byte phases": ([0, 2, 6], 0),
+    # output at 6 mod 16: head 5, then a phase of 6 elements moves it to 13
+    "2-byte phases, output off": ([14, 2, 6, 0], 6),
+    # nine contributions: one full batch of eight and one more
+    "nine contributions": ([2, 4, 6, 8, 10, 12, 14, 0, 2], 4),
 }
 
 
@@ -91,7 +98,7 @@ def _run(lp, S, cb, offs, goff, flow, seed=0):
     g = GpuRun(infos, kept, *host0, f32(st["master"]), f32(st["m"]), f32(st["v"]),
                stored(st["grad"]), None if st["param"] is None else u16(st["param"]))
     tag = f"{lp} S={S} cb={cb} offs={offs} grad+{goff} {flow}"
-    log(f"[pieces] {tag}")
+    log(f"[phases] {tag}")
     assert compare(w, g, ost, oinfos, tag)["bitwise"], tag
 
 
@@ -106,18 +113,36 @@ def test_contributions_at_distinct_phases(phase, lp, flow):
     _run(lp, 50_021, 10_007, offs, goff, flow)
 
 
+def _fp32_offsets(offs, goff):
+    return [o - o % 4 for o in offs], goff - goff % 4
+
+
 @pytest.mark.parametrize("lp", ["fp16", "fp32"])
-def test_pieces_above_the_small_shard_limit(lp):
-    """Nontemporal piece kernels: a shard past 8,388,608 elements, buckets of
-    an odd size, 8-byte and 4-byte phase sets, with one run per lane (8
-    contributions) and three (fewer)."""
+def test_shift_above_the_small_shard_limit(lp):
+    """Nontemporal shift kernels: a shard past 8,388,608 elements, buckets of
+    an odd size, 8-, 4- and 2-byte phase sets, with one run per lane (8 or
+    more contributions) and three (fewer)."""
     for offs, goff in (([0, 8, 0, 8, 8, 0, 0, 8], 0), ([4, 0, 12], 8), ([0, 8, 8, 0], 8),
-                       ([12, 4, 4, 8, 0, 4, 8, 12, 0], 0)):
+                       ([12, 4, 4, 8, 0, 4, 8, 12, 0], 0), ([2, 0, 14, 6], 10),
+                       ([6, 2, 0, 14, 12, 10, 8, 4], 2)):
+        if lp == "fp32":
+            offs, goff = _fp32_offsets(offs, goff)
         _run(lp, 8_400_017, 2_100_001, offs, goff, "device")
 
 
-def test_pieces_with_the_inline_fold():
+def test_shift_with_the_inline_fold():
     """A one-bucket device-resident step small enough to fold its partials in
-    the update (aligned update arrays), its reduce in 8-byte pieces."""
+    the update (aligned update arrays), its reduce in the shift kernel."""
     _run("fp16", 65_536, 65_536, [0, 8, 8], 0, "device")
     _run("bf16", 131_072, 131_072, [8, 0], 8, "device")
+    _run("fp16", 65_536, 65_536, [2, 14, 0, 6], 0, "device")
+
+
+@pytest.mark.parametrize("lp", ["bf16", "fp32"])
+def test_shift_tiny_buckets(lp):
+    """Buckets of 1 to 41 elements at 2-byte (fp32: 4-byte) phases: vector
+    bodies of zero, one and a few runs after heads of up to 15 elements, and
+    the head clipped to a bucket shorter than it."""
+    offs, goff = ([2, 12, 6], 6) if lp != "fp32" else ([4, 12, 8], 4)
+    for cb in (1, 2, 3, 7, 13, 16, 21, 24, 29, 31, 32, 37, 41):
+        _run(lp, 97, cb, offs, goff, "sync")

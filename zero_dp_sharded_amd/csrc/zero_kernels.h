@@ -18,6 +18,9 @@ constexpr int kMaxContrib = 64;
 //                    workgroups finish sooner);
 //   reduce, R >= 8:  64 lanes, 1 run, 12 workgroups per CU with 2-byte storage
 //                    and 10 with fp32 (6 from R = 16);
+//   shift reduce (contributions off the output's 16-byte phase): 64 lanes,
+//                    2 runs and 14 workgroups per CU below R = 8; 1 run and 16
+//                    (2-byte storage) or 12 (fp32) workgroups per CU from R = 8;
 //   scan (1 stream): 256 lanes, 4 runs, 8 workgroups per CU.
 // (The ZK_* macros exist only to build tuning variants; the defaults are the
 // measured optimum.)
@@ -47,6 +50,21 @@ constexpr int kMaxContrib = 64;
 #endif
 #ifndef ZK_RED_PER_CU_WIDE
 #define ZK_RED_PER_CU_WIDE 6
+#endif
+#ifndef ZK_RED_SHIFT_RUNS
+#define ZK_RED_SHIFT_RUNS 2
+#endif
+#ifndef ZK_RED_SHIFT_PER_CU
+#define ZK_RED_SHIFT_PER_CU 14
+#endif
+#ifndef ZK_RED_SHIFT_PER_CU_MANY
+#define ZK_RED_SHIFT_PER_CU_MANY 12
+#endif
+#ifndef ZK_RED_SHIFT_PER_CU_MANY_2B
+#define ZK_RED_SHIFT_PER_CU_MANY_2B 16
+#endif
+#ifndef ZK_RED_SHIFT_GROUP
+#define ZK_RED_SHIFT_GROUP 32
 #endif
 #ifndef ZK_SCAN_BLOCK
 #define ZK_SCAN_BLOCK 256
@@ -84,6 +102,19 @@ constexpr int kRedRuns = ZK_RED_RUNS;
 constexpr int kRedRunsMany = ZK_RED_RUNS_MANY;   // runs per lane when R >= 8
 constexpr int kRedManyR = 8;
 constexpr int kRedRunsSmall = ZK_RED_RUNS_SMALL;   // R < 8, bucket below kRedSmallNvec runs
+// runs per lane of the shift kernel below 8 contributions (its registers hold
+// two words per run and contribution in flight)
+constexpr int kRedShiftRuns = ZK_RED_SHIFT_RUNS;
+// The shift kernel hands each XCD kRedShiftGroup consecutive workgroups' runs
+// at a time, so that the word a wave's last lane reads past its runs is
+// usually read by a wave of the same XCD (same L2) as well (0: plain order).
+constexpr int kRedShiftGroup = ZK_RED_SHIFT_GROUP;
+// Resident shift-kernel workgroups per CU below 8 contributions, and from 8
+// with fp32 and with 2-byte storage: more than the vector kernel's, whose
+// loads it matches, to cover its extra exchange and shift instructions.
+constexpr int kRedShiftPerCU = ZK_RED_SHIFT_PER_CU;
+constexpr int kRedShiftPerCUMany = ZK_RED_SHIFT_PER_CU_MANY;
+constexpr int kRedShiftPerCUMany2B = ZK_RED_SHIFT_PER_CU_MANY_2B;
 // runs of one full residency of kRedRuns workgroups on 256 CUs
 constexpr int64_t kRedSmallNvec = (int64_t)256 * ZK_RED_PER_CU * ZK_RED_BLOCK * ZK_RED_RUNS;
 // The stand-alone scan reads a single stream, so it takes its own runs per
@@ -91,19 +122,11 @@ constexpr int64_t kRedSmallNvec = (int64_t)256 * ZK_RED_PER_CU * ZK_RED_BLOCK * 
 constexpr int kScanBlock = ZK_SCAN_BLOCK;
 constexpr int kScanRuns = ZK_SCAN_RUNS;
 constexpr int kScanPerCU = ZK_SCAN_PER_CU;
-// A bucket whose contributions and output share an address phase only modulo
-// 8 or 4 bytes, not 16, moves each 16-byte run as `pieces` (2 or 4) aligned
-// pieces: one-wave workgroups, kRedPieceRunsFew runs per lane below 8
-// contributions (so that enough bytes are in flight), one from 8 and on the
-// buckets of small shards.
-constexpr int kRedPieceBlock = 64;
-constexpr int kRedPieceRunsFew = 3;
 constexpr int kMin2(int a, int b) { return a < b ? a : b; }
 // runs one vector reduce or scan workgroup covers at the least
 constexpr int64_t kRunsPerBlockMin =
-    kMin2(kMin2(kMin2(kRedBlock * kMin2(kRedRuns, kRedRunsSmall), kRedBlockMany * kRedRunsMany),
-                kScanBlock * kScanRuns),
-          kRedPieceBlock);
+    kMin2(kMin2(kRedBlock * kMin2(kRedRuns, kRedRunsSmall), kRedBlockMany * kRedRunsMany),
+          kScanBlock * kScanRuns);
 constexpr int kRedPerCU = ZK_RED_PER_CU;
 constexpr int kRedPerCUMany = ZK_RED_PER_CU_MANY;   // residency when 8 <= R < 16, fp32
 constexpr int kRedPerCUMany2B = ZK_RED_PER_CU_MANY_2B;   // the same, 2-byte storage
@@ -140,18 +163,17 @@ constexpr int64_t kSmallElems = ZK_SMALL_ELEMS;
 constexpr int kSmallBlock = 256;
 inline bool shard_small(int64_t S) { return S <= kSmallElems; }
 // Lanes per workgroup and runs per lane of a bucket reduce (nvec runs, R
-// contributions) of a small shard or not, in whole runs (pieces = 1) or pieces.
-inline int red_block(int R, bool small, int pieces = 1)
+// contributions) of a small shard or not, in the vector or the shift kernel.
+inline int red_block(int R, bool small)
 {
-    if (pieces > 1) return kRedPieceBlock;
     if (small) return kSmallBlock;
     return R >= kRedManyR ? kRedBlockMany : kRedBlock;
 }
-inline int red_runs(int R, int64_t nvec, bool small, int pieces = 1)
+inline int red_runs(int R, int64_t nvec, bool small, bool shift = false)
 {
-    if (pieces > 1) return small || R >= kRedManyR ? 1 : kRedPieceRunsFew;
     if (small) return 1;
     if (R >= kRedManyR) return kRedRunsMany;
+    if (shift) return kRedShiftRuns;
     return nvec < kRedSmallNvec ? kRedRunsSmall : kRedRuns;
 }
 // Update of an S-element shard: lanes per workgroup and groups per lane.
@@ -219,10 +241,11 @@ struct PrepareArgs {
 
 // One bucket of the reduce.  Elements [0, n) of the bucket; the vector body
 // starts at `head` and holds `nvec` 16-byte runs (8 two-byte or 4 fp32
-// elements) that are 16-byte aligned in every contribution and in `out`
-// (pieces = 1), or only 16/pieces-byte aligned (pieces = 2 or 4: each run is
-// moved as that many aligned pieces).  vec_ok = 0 selects the element-wise
-// path.  Workgroup b writes
+// elements) that are 16-byte aligned in `out` and, with shift = 0, in every
+// contribution.  shift = 1: each contribution keeps its own address phase
+// modulo 16 bytes (the shift kernel cuts its runs out of aligned words), and
+// head >= that phase in elements, with at least one whole run after the body.
+// vec_ok = 0 selects the element-wise path.  Workgroup b writes
 // partial[slot_base + b]: the fp64 sum of the squared unscaled stored values
 // of its elements, or NaN if any unscaled value is not finite.  The unscale
 // factor is inv_scale, or dev->inv_scale when dev is set.
@@ -241,7 +264,7 @@ struct ReduceLaunch {
     int64_t slot_base;
     uint32_t lds_reserve;  // dynamic LDS that caps workgroups per CU
     int32_t small;         // 1: a bucket of a small shard (see shard_small)
-    int32_t pieces;        // 1, 2 or 4 aligned pieces per run (see kRedPieceBlock)
+    int32_t shift;         // 1: contributions off the output's 16-byte phase (see above)
     const DevState* dev;
     DevState* snapshot;    // set: workgroup 0 copies *dev there (see InlineFold)
 };

@@ -7,7 +7,8 @@
 //    in flight then sweep each array as one narrow front, which keeps DRAM
 //    row locality; grid-stride launches lost about 15 points of bandwidth;
 //  - every load and store instruction of a wave covers one contiguous span
-//    (lane-consecutive 16-byte or 8-byte pieces);
+//    (lane-consecutive 16-byte runs, or the 8-byte groups of four 2-byte
+//    values of the update);
 //  - nontemporal loads and stores (each byte is touched once per step);
 //  - a cap on resident workgroups per CU, set by reserving dynamic LDS the
 //    kernels never touch: with the 3 to 17 concurrent streams of the update
@@ -76,15 +77,8 @@ template <> struct Fmt<3> {            // IEEE binary32
     using V4 = f4;
 };
 
-// One of H aligned pieces of a 16-byte run: N = W / H elements of storage
-// type P (a scalar when N = 1) and their fp32 image F.
-template <int LP, int H> struct Piece;
-template <> struct Piece<1, 2> { static constexpr int N = 4; using P = h4; using F = f4; };
-template <> struct Piece<1, 4> { static constexpr int N = 2; using P = h2; using F = f2; };
-template <> struct Piece<2, 2> { static constexpr int N = 4; using P = b4; using F = f4; };
-template <> struct Piece<2, 4> { static constexpr int N = 2; using P = b2; using F = f2; };
-template <> struct Piece<3, 2> { static constexpr int N = 2; using P = f2; using F = f2; };
-template <> struct Piece<3, 4> { static constexpr int N = 1; using P = float; using F = float; };
+// A 16-byte run as four raw dwords.
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 
 template <typename V>
 __device__ __forceinline__ V ld_nt(const void* base, int64_t idx)
@@ -331,97 +325,146 @@ __global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
     block_partial<BS>(L.partial + L.slot_base + blockIdx.x, flag, ss);
 }
 
-// fp32 image of a piece, and a piece rounded (to nearest even) from its fp32
-// image; element k of an fp32 image.  N = 1 pieces are scalars.
-template <int N, typename F, typename P>
-__device__ __forceinline__ F widen(P x)
+// The 16 bytes at byte offset 4*D + b (b = 0 or, for 2-byte data, 2) of the
+// 32-byte window lo:hi, lo at the lower address: the five dwords from dword D
+// on, and for 2-byte data a byte funnel shift of each pair (v_alignbyte_b32
+// takes the high dword first).
+template <int LP, int D>
+__device__ __forceinline__ u4 cut16(u4 lo, u4 hi, uint32_t b)
 {
-    if constexpr (N == 1) return static_cast<F>(x);
-    else return __builtin_convertvector(x, F);
-}
-
-template <int N, typename P, typename F>
-__device__ __forceinline__ P narrow(F x)
-{
-    if constexpr (N == 1) {
-        return static_cast<P>(pin_f32(x));
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    if constexpr (LP == 3) {
+        (void)b;
+        return u4{w[D], w[D + 1], w[D + 2], w[D + 3]};
     } else {
-#pragma unroll
-        for (int k = 0; k < N; ++k) x[k] = pin_f32(x[k]);
-        return __builtin_convertvector(x, P);
+        return u4{__builtin_amdgcn_alignbyte(w[D + 1], w[D], b),
+                  __builtin_amdgcn_alignbyte(w[D + 2], w[D + 1], b),
+                  __builtin_amdgcn_alignbyte(w[D + 3], w[D + 2], b),
+                  __builtin_amdgcn_alignbyte(w[D + 4], w[D + 3], b)};
     }
 }
 
-template <int N, typename F>
-__device__ __forceinline__ float elem(const F& x, int k)
+// Lane i's value of x from lane i + 1 of its wave (DPP wave_shl:1); lane 63,
+// which has no such lane, keeps `old`.
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t old, uint32_t x)
 {
-    if constexpr (N == 1) return x;
-    else return x[k];
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, 0x130, 0xf, 0xf, false);
 }
 
-// Vector body of a bucket whose contributions and output share an address
-// phase only modulo 16/H bytes (H = 2: 8 bytes, H = 4: 4 bytes): the same runs
-// as reduce_vec_kernel, U per lane on kRedPieceBlock lanes, each moved as H
-// aligned pieces of N = W/H elements.  Workgroup b covers runs
-// [b*BS*U, (b+1)*BS*U), that is pieces [b*BS*U*H, (b+1)*BS*U*H); lane l owns
-// pieces b*BS*U*H + j*BS + l, j < U*H, so each load instruction of a wave
-// covers BS*16/H contiguous bytes.  The contributions are loaded K at a time
-// (8 with one run per lane, 4 with more: 128-192 bytes per lane), every piece
-// of them in flight before the arithmetic, and added in ascending r from +0:
-// each element's result is the vector kernel's.
-template <int LP, int H, int U, int SNAP, int NT>
-__global__ __launch_bounds__(kRedPieceBlock) void reduce_piece_kernel(ReduceLaunch L)
+// acc[u] += the fp32 image of the run cut at dword D from lo[u] and the word
+// after it: the next lane's lo[u]; for lane 63, lane 0's lo[u + 1], or nx at
+// the last run.  Only the dwords the cut reads are exchanged.
+template <int LP, int U, int D>
+__device__ __forceinline__ void add_cut(typename Fmt<LP>::FW (&acc)[U], const u4 (&lo)[U],
+                                        const u4& nx, uint32_t b)
 {
-    using Pc = Piece<LP, H>;
-    using P = typename Pc::P;
-    using F = typename Pc::F;
-    constexpr int N = Pc::N, BS = kRedPieceBlock, J = U * H, K = U == 1 ? 8 : 4;
+    using VW = typename Fmt<LP>::VW;
+    using FW = typename Fmt<LP>::FW;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        u4 hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t old =
+                u == U - 1 ? nx[e] : __builtin_amdgcn_readlane(lo[u + 1 < U ? u + 1 : u][e], 0);
+            hi[e] = from_next_lane(old, lo[u][e]);
+        }
+        // lanes past the body add what they hold: their sums are never stored
+        acc[u] = acc[u] + __builtin_convertvector(__builtin_bit_cast(VW, cut16<LP, D>(lo[u], hi, b)), FW);
+    }
+}
+
+// The block of runs (and partial slot) workgroup b of n takes in the shift
+// kernel.  Workgroups are dealt round-robin to the 8 XCDs; within each full
+// set of 8 * kRedShiftGroup workgroups this hands XCD x (workgroups b = x mod 8)
+// the kRedShiftGroup consecutive blocks x * kRedShiftGroup + (0 ..), so all
+// XCDs still sweep one narrow front while neighbouring blocks mostly share an
+// L2.  A bijection on [0, n): the last, partial set keeps the plain order.
+__device__ __forceinline__ unsigned shift_block(unsigned b, unsigned n)
+{
+    if constexpr (kRedShiftGroup <= 1) {
+        (void)n;
+        return b;
+    } else {
+        constexpr unsigned set = 8u * kRedShiftGroup;
+        const unsigned s0 = b - b % set;
+        if (s0 + set > n) return b;
+        const unsigned j = b - s0;
+        return s0 + (j % 8u) * kRedShiftGroup + j / 8u;
+    }
+}
+
+// Vector body of a bucket whose contributions do not all share the output's
+// address phase modulo 16 bytes (for example contributions carved back to back
+// from one buffer when the shard size is not a multiple of 8).  The output
+// runs are 16-byte aligned from `head`, with the workgroups, runs per lane and
+// partial slots of reduce_vec_kernel.  Contribution r's run vi starts
+// s_r = (its address at head) mod 16 bytes past a 16-byte boundary, inside the
+// aligned words vi and vi + 1 from base_r, and is cut out of them at the
+// wave-uniform offset s_r (a uniform branch on its dword part).  Each lane
+// loads word vi, also for vi = nvec (the word after the body, which the run
+// before it needs), and takes word vi + 1 from the next lane; lane 63 of a wave
+// takes it from lane 0's next run, or at its last run loads it.  So every word
+// crosses the memory path once, as in the aligned kernel, plus one word per
+// wave.  The host keeps head >= s_r / esz for every r and one whole run after
+// the body, so every word lies inside the bucket.  Contributions are taken K at
+// a time with every load in flight before the arithmetic and added in
+// ascending r from +0: each element's result is the vector kernel's.
+template <int LP, int U, int BS, int SNAP, int NT>
+__global__ __launch_bounds__(BS) void reduce_shift_kernel(ReduceLaunch L)
+{
+    using FW = typename Fmt<LP>::FW;
+    constexpr int K = U == 1 ? 8 : 4;
+    static_assert(U == 1 || BS == 64, "runs of one lane chain across one wave only");
     int flag = 0;
     double ss = 0.0;
     const float inv_scale = check_inv_scale(L.inv_scale, L.dev);
-    const int64_t npieces = L.nvec * H;
-    const int64_t q0 = (int64_t)blockIdx.x * (BS * J) + threadIdx.x;
-    F acc[J];
+    const unsigned blk = shift_block(blockIdx.x, gridDim.x);
+    const int64_t v0 = (int64_t)blk * (BS * U) + threadIdx.x;
+    const bool last_lane = (threadIdx.x & 63) == 63;
+    FW acc[U];
 #pragma unroll
-    for (int j = 0; j < J; ++j) acc[j] = (F)(0.f);
+    for (int u = 0; u < U; ++u) acc[u] = (FW)(0.f);
     for (int r0 = 0; r0 < L.R; r0 += K) {
         const int cnt = L.R - r0 < K ? L.R - r0 : K;
-        P x[K][J];
+        u4 lo[K][U], nx[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            if (k < cnt) {
-                const void* base = adv<LP>(L.c.p[r0 + k], L.head);
+            nx[k] = u4{0u, 0u, 0u, 0u};
 #pragma unroll
-                for (int j = 0; j < J; ++j) {
-                    const int64_t q = q0 + j * BS;
-                    if (q < npieces) x[k][j] = ld_v<P, NT>(base, q);
+            for (int u = 0; u < U; ++u) lo[k][u] = u4{0u, 0u, 0u, 0u};
+            if (k < cnt) {
+                const char* p = static_cast<const char*>(adv<LP>(L.c.p[r0 + k], L.head));
+                const void* base = p - ((uintptr_t)p & 15u);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t vi = v0 + u * BS;
+                    if (vi <= L.nvec) lo[k][u] = ld_v<u4, NT>(base, vi);
+                    if (u == U - 1 && last_lane && vi < L.nvec) nx[k] = ld_v<u4, NT>(base, vi + 1);
                 }
             }
         }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             if (k < cnt) {
-#pragma unroll
-                for (int j = 0; j < J; ++j) {
-                    const int64_t q = q0 + j * BS;
-                    if (q < npieces) acc[j] = acc[j] + widen<N, F>(x[k][j]);
+                const uint32_t sh = (uint32_t)(uintptr_t)adv<LP>(L.c.p[r0 + k], L.head) & 15u;
+                const uint32_t b = sh & 3u;
+                switch (sh >> 2) {
+                case 0: add_cut<LP, U, 0>(acc, lo[k], nx[k], b); break;
+                case 1: add_cut<LP, U, 1>(acc, lo[k], nx[k], b); break;
+                case 2: add_cut<LP, U, 2>(acc, lo[k], nx[k], b); break;
+                default: add_cut<LP, U, 3>(acc, lo[k], nx[k], b); break;
                 }
             }
         }
     }
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int64_t q = q0 + j * BS;
-        if (q < npieces) {
-            const P o = narrow<N, P>(acc[j] * L.inv_r);
-            st_v<P, NT>(adv<LP>(L.out, L.head), q, o);
-            const F of = widen<N, F>(o);
-#pragma unroll
-            for (int k = 0; k < N; ++k) check_u(elem<N>(of, k) * inv_scale, flag, ss);
-        }
+    for (int u = 0; u < U; ++u) {
+        const int64_t vi = v0 + u * BS;
+        if (vi < L.nvec) reduce_finish<LP, NT>(L, vi, acc[u], inv_scale, flag, ss);
     }
     if constexpr (SNAP) snapshot_state(L.dev, L.snapshot);
-    block_partial<BS>(L.partial + L.slot_base + blockIdx.x, flag, ss);
+    block_partial<BS>(L.partial + L.slot_base + blk, flag, ss);
 }
 
 template <int LP>
@@ -960,36 +1003,28 @@ hipError_t reduce_vec_launch(const ReduceLaunch& L, unsigned grid, int U, bool s
     return hipGetLastError();
 }
 
-// The piece kernel of a bucket (L.pieces = 2 or 4) with U runs per lane (the
-// count red_runs gave the host): nontemporal for the buckets of large shards,
-// plain for small ones, as the vector kernels.
-template <int LP, int H, int U>
-void reduce_piece_go(const ReduceLaunch& L, unsigned grid, hipStream_t s)
+// The shift kernel of a bucket (L.shift = 1): the vector kernel's workgroups,
+// with kRedShiftRuns runs per lane below 8 contributions on large shards.
+template <int LP, int U, int BS, int NT>
+void reduce_shift_go(const ReduceLaunch& L, unsigned grid, hipStream_t s)
 {
-    const bool nt = L.small == 0;
-    if (L.snapshot != nullptr) {
-        if (nt)
-            reduce_piece_kernel<LP, H, U, 1, 1><<<grid, kRedPieceBlock, L.lds_reserve, s>>>(L);
-        else
-            reduce_piece_kernel<LP, H, U, 1, 0><<<grid, kRedPieceBlock, L.lds_reserve, s>>>(L);
-    } else {
-        if (nt)
-            reduce_piece_kernel<LP, H, U, 0, 1><<<grid, kRedPieceBlock, L.lds_reserve, s>>>(L);
-        else
-            reduce_piece_kernel<LP, H, U, 0, 0><<<grid, kRedPieceBlock, L.lds_reserve, s>>>(L);
-    }
+    if (L.snapshot != nullptr)
+        reduce_shift_kernel<LP, U, BS, 1, NT><<<grid, BS, L.lds_reserve, s>>>(L);
+    else
+        reduce_shift_kernel<LP, U, BS, 0, NT><<<grid, BS, L.lds_reserve, s>>>(L);
 }
 
 template <int LP>
-hipError_t reduce_piece_launch(const ReduceLaunch& L, unsigned grid, int U, hipStream_t s)
+hipError_t reduce_shift_launch(const ReduceLaunch& L, unsigned grid, int U, bool small,
+                               hipStream_t s)
 {
-    if (L.pieces == 2) {
-        if (U == kRedPieceRunsFew) reduce_piece_go<LP, 2, kRedPieceRunsFew>(L, grid, s);
-        else reduce_piece_go<LP, 2, 1>(L, grid, s);
-    } else {
-        if (U == kRedPieceRunsFew) reduce_piece_go<LP, 4, kRedPieceRunsFew>(L, grid, s);
-        else reduce_piece_go<LP, 4, 1>(L, grid, s);
-    }
+    (void)U;
+    if (small)
+        reduce_shift_go<LP, 1, kSmallBlock, 0>(L, grid, s);
+    else if (L.R >= kRedManyR)
+        reduce_shift_go<LP, kRedRunsMany, kRedBlockMany, 1>(L, grid, s);
+    else
+        reduce_shift_go<LP, kRedShiftRuns, kRedBlock, 1>(L, grid, s);
     return hipGetLastError();
 }
 
@@ -998,8 +1033,8 @@ hipError_t reduce_dispatch(const ReduceLaunch& L, hipStream_t s)
 {
     constexpr int W = Fmt<LP>::W;
     const bool small = L.small != 0;
-    const int U = red_runs(L.R, L.nvec, small, L.pieces);
-    const int BS = red_block(L.R, small, L.pieces);
+    const int U = red_runs(L.R, L.nvec, small, L.shift != 0);
+    const int BS = red_block(L.R, small);
     const int64_t runs_per_block = (int64_t)BS * U;
     const int64_t vblocks = L.vec_ok ? ceil_div(L.nvec, runs_per_block) : 0;
     // consecutive launches of at most kMaxLaunchItems work-items; each starts
@@ -1011,8 +1046,8 @@ hipError_t reduce_dispatch(const ReduceLaunch& L, hipStream_t s)
         part.head = L.head + W * runs_per_block * b0;
         part.nvec = L.nvec - runs_per_block * b0;
         part.slot_base = L.slot_base + b0;
-        hipError_t e = L.pieces > 1 ? reduce_piece_launch<LP>(part, (unsigned)nb, U, s)
-                                    : reduce_vec_launch<LP>(part, (unsigned)nb, U, small, s);
+        hipError_t e = L.shift ? reduce_shift_launch<LP>(part, (unsigned)nb, U, small, s)
+                                : reduce_vec_launch<LP>(part, (unsigned)nb, U, small, s);
         if (e != hipSuccess) return e;
     }
     const Ranges rg = ranges_of(L.n, L.head, W * L.nvec, L.vec_ok);

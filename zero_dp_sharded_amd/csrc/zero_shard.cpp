@@ -77,6 +77,8 @@ struct zero_shard_s {
     uint32_t lds_reduce = 0;
     uint32_t lds_reduce_many = 0;   // reduces of 8 <= R < 16 contributions
     uint32_t lds_reduce_wide = 0;   // reduces of R >= 16 contributions
+    uint32_t lds_shift = 0;         // shift-kernel reduces of R < 8 contributions
+    uint32_t lds_shift_many = 0;    // and of R >= 8
     uint32_t lds_scan = 0;
     // gated steps: event after the result copy, and the speculative update
     hipEvent_t result_ready = nullptr;
@@ -425,6 +427,9 @@ static void set_lds_reserves(zero_shard_s* h, int lds_cu, int lds_blk)
     h->lds_reduce_many = lds_reserve_for(
         lds_cu, lds_blk, h->d.lp == ZERO_FP32 ? zk::kRedPerCUMany : zk::kRedPerCUMany2B);
     h->lds_reduce_wide = lds_reserve_for(lds_cu, lds_blk, zk::kRedPerCUWide);
+    h->lds_shift = lds_reserve_for(lds_cu, lds_blk, zk::kRedShiftPerCU);
+    h->lds_shift_many = lds_reserve_for(
+        lds_cu, lds_blk, h->d.lp == ZERO_FP32 ? zk::kRedShiftPerCUMany : zk::kRedShiftPerCUMany2B);
     h->lds_scan = lds_reserve_for(lds_cu, lds_blk, zk::kScanPerCU);
 }
 
@@ -594,31 +599,45 @@ static zero_status enqueue_reduce(zero_shard_s* h, const void* const* ptrs, int3
     L.n = len;
     const int W = zk::run_width(h->d.lp);
     // whole 16-byte runs when every array shares its address phase modulo 16;
-    // else pieces of 8 or 4 bytes when they share it modulo that; else the
-    // element-wise kernel
-    int64_t head = common_head(addr, elt, align, n_contrib + 1);
-    L.pieces = 1;
-    for (int a = 8; head < 0 && a >= 4; a /= 2) {
-        for (int k = 0; k <= n_contrib; ++k) align[k] = a;
-        head = common_head(addr, elt, align, n_contrib + 1);
-        if (head >= 0) L.pieces = 16 / a;
+    // else the shift kernel: the output 16-byte aligned from head, each
+    // contribution read at its own phase s_r (head >= s_r elements, one whole
+    // run kept after the body)
+    const int64_t head = common_head(addr, elt, align, n_contrib + 1);
+    L.shift = 0;
+    int64_t h0 = head >= 0 ? -1 : common_head(&addr[n_contrib], &elt[n_contrib], &align[n_contrib], 1);
+    if (h0 < 0) {
+        split(len, head, W, &L.head, &L.nvec, &L.vec_ok);
+    } else {
+        int64_t smax = 0;
+        for (int r = 0; r < n_contrib; ++r) {
+            const int64_t sr = (int64_t)((addr[r] + (uintptr_t)h0 * h->esz) & 15u) / h->esz;
+            if (sr > smax) smax = sr;
+        }
+        if (smax > h0) h0 += W;
+        L.shift = 1;
+        L.vec_ok = 1;
+        L.head = h0 < len ? h0 : len;
+        const int64_t whole = (len - L.head) / W;
+        L.nvec = whole > 1 ? whole - 1 : 0;
     }
-    split(len, head, W, &L.head, &L.nvec, &L.vec_ok);
     L.R = n_contrib;
     L.lp = (int32_t)h->d.lp;
     L.inv_r = (float)(1.0 / (double)n_contrib);
     L.inv_scale = (float)(1.0 / h->scale);
     L.partial = h->partial;
     L.slot_base = slot_base;
-    L.lds_reserve = n_contrib >= zk::kRedWideR   ? h->lds_reduce_wide
-                    : n_contrib >= zk::kRedManyR ? h->lds_reduce_many
-                                                 : h->lds_reduce;
+    if (L.shift)
+        L.lds_reserve = n_contrib >= zk::kRedManyR ? h->lds_shift_many : h->lds_shift;
+    else
+        L.lds_reserve = n_contrib >= zk::kRedWideR   ? h->lds_reduce_wide
+                        : n_contrib >= zk::kRedManyR ? h->lds_reduce_many
+                                                     : h->lds_reduce;
     L.dev = dev;
     L.snapshot = snapshot;
     L.small = zk::shard_small(h->S) ? 1 : 0;
     const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W,
-                                             zk::red_runs(L.R, L.nvec, L.small != 0, L.pieces),
-                                             zk::red_block(L.R, L.small != 0, L.pieces));
+                                             zk::red_runs(L.R, L.nvec, L.small != 0, L.shift != 0),
+                                             zk::red_block(L.R, L.small != 0));
     if (L.slot_base + blocks > h->nslots)
         return fail(ZERO_ERR_UNSUPPORTED, "%s: partial slots exhausted", who);
     if (!launch) {
