@@ -44,14 +44,20 @@ def kernel_code_hash() -> str:
     return h()
 
 
-def measured_traffic(workload: str, per_launch_elems: int):
+def traffic_file(workload: str, contrib_phase: int = 16) -> str:
+    tag = workload if contrib_phase == 16 else f"{workload}_phase{contrib_phase}"
+    return os.path.join(PROFILES, f"traffic_{tag}.json")
+
+
+def measured_traffic(workload: str, per_launch_elems: int, contrib_phase: int = 16):
     """HBM bytes per update launch from the committed rocprofv3 counter summary
-    of this workload, if it was taken on the current kernel source and the
-    in-tree library is the one loaded (not a ZERO_SHARD_LIB variant); else None."""
+    of this workload (and contribution phase), if it was taken on the current
+    kernel source and the in-tree library is the one loaded (not a
+    ZERO_SHARD_LIB variant); else None."""
     if os.environ.get("ZERO_SHARD_LIB"):
         return None
     try:
-        with open(os.path.join(PROFILES, f"traffic_{workload}.json")) as f:
+        with open(traffic_file(workload, contrib_phase)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -236,6 +242,11 @@ def main() -> int:
                          "(gated), synchronous check (sync), device-resident steps enqueued "
                          "back to back (device), or device-resident steps captured in a HIP "
                          "graph (up to 10 per graph) and replayed (graph); all four are timed")
+    ap.add_argument("--contrib-phase", type=int, choices=[16, 8, 4, 2], default=16,
+                    help="contribution r starts (r * P) mod 16 bytes past a 16-byte boundary "
+                         "(16: every contribution aligned; 8, 4, 2: the phases of "
+                         "contributions carved back to back from one buffer, which the "
+                         "reduce reads at their own phase)")
     ap.add_argument("--mode", choices=["pos_g", "pos"], default="pos_g",
                     help="pos_g: gradient partitioning (bucket reduces + check + Adam); "
                          "pos: optimizer-state partitioning only (the owner's slice of an "
@@ -282,7 +293,7 @@ def main() -> int:
         bufs = []
         synth.fill_contribs(dataclasses.replace(w, R=1), [grad], 0, w.scale, seed=0)
     else:
-        bufs = synth.alloc_contribs(w, dev)
+        bufs = synth.alloc_contribs(w, dev, phase_step=args.contrib_phase)
         synth.fill_contribs(w, bufs, 0, w.scale, seed=0)
     torch.cuda.synchronize()
     print("[bench] inputs resident", file=sys.stderr, flush=True)
@@ -413,7 +424,7 @@ def main() -> int:
     # the update kernel alone: the synchronous-check flow brackets only its enqueue
     achieved = adam_bytes / (adam_sync * 1e-3) / 1e9
     step_bytes = adam_bytes + reduce_bytes
-    traffic = measured_traffic(args.workload, S)
+    traffic = measured_traffic(args.workload, S, args.contrib_phase)
 
     cpu = None
     parity = None
@@ -479,9 +490,12 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic (seeded; same contribution batch every step)",
         "config": {"workload": w.name + (" -- P_os: scan check + Adam on the owner's slice of an "
-                                          "all-reduced gradient" if args.mode == "pos" else ""),
+                                          "all-reduced gradient" if args.mode == "pos" else "")
+                               + (f", contribution r at (r*{args.contrib_phase}) mod 16 B"
+                                  if args.contrib_phase != 16 and args.mode == "pos_g" else ""),
                    "mode": args.mode, "psi": w.psi, "nd": w.nd, "rank": w.rank,
                    "shard_elems": S, "contributions": R if args.mode == "pos_g" else 0,
+                   "contrib_phase_bytes": args.contrib_phase,
                    "bucket_elems": cb,
                    "storage": w.lp, "optimizer": (f"sgd(momentum={w.momentum})" if sgd
                                                    else "adamw"),

@@ -41,6 +41,10 @@ def test_traffic_only_from_counters_of_the_current_kernels(tmp_path, monkeypatch
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     assert bench.measured_traffic("w", 10) == 123.0
     assert bench.measured_traffic("w", 11) is None              # another shard size
+    assert bench.measured_traffic("w", 10, contrib_phase=2) is None   # no phase-2 counters
+    (tmp_path / "traffic_w_phase2.json").write_text(json.dumps(dict(d, hbm_bytes_per_launch=7.0)))
+    assert bench.measured_traffic("w", 10, contrib_phase=2) == 7.0
+    assert bench.measured_traffic("w", 10) == 123.0
     d["kernel_code_sha256_16"] = "0" * 16
     (tmp_path / "traffic_w.json").write_text(json.dumps(d))
     assert bench.measured_traffic("w", 10) is None              # stale kernels

@@ -3,6 +3,8 @@ and the GPU side), checked on the CPU: the stated distributions hold (mean and
 standard deviation within 4 sigma of their sampling error), draws are
 reproducible and independent across steps, contributions and seeds, the +inf
 event lands where the workload says, and the shapes follow the workloads."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -104,3 +106,18 @@ def test_workload_shapes():
             assert w.has_m and w.has_v
     assert synth.WORKLOADS["128b"].shard == 2_000_000_000
     assert synth.WORKLOADS["c1_7.5b_sgdm"].shard == 117_187_500
+
+
+@pytest.mark.parametrize("lp,step", [("fp16", 2), ("bf16", 4), ("fp16", 8), ("fp32", 4),
+                                     ("fp32", 8)])
+def test_contributions_at_carved_phases(lp, step):
+    """phase_step p puts contribution r at (r * p) mod 16 bytes past a 16-byte
+    boundary, each a full buffer of its own; 16 keeps them aligned; an fp32
+    buffer cannot start 2 bytes off."""
+    w = dataclasses.replace(synth.WORKLOADS["gpt2_1.5b"], lp=lp, R=9)
+    bufs = synth.alloc_contribs(w, "cpu", elems=1001, phase_step=step)
+    assert [b.data_ptr() % 16 for b in bufs] == [(r * step) % 16 for r in range(9)]
+    assert all(b.numel() == 1001 and b.dtype == w.torch_lp for b in bufs)
+    assert all(b.data_ptr() % 16 == 0 for b in synth.alloc_contribs(w, "cpu", elems=5))
+    with pytest.raises(ValueError):
+        synth.alloc_contribs(dataclasses.replace(w, lp="fp32"), "cpu", elems=5, phase_step=2)

@@ -202,6 +202,22 @@ def inject_index(n: int) -> int:
     return n // 2 + 1
 
 
-def alloc_contribs(w: Workload, device, elems: Optional[int] = None) -> List[torch.Tensor]:
+def alloc_contribs(w: Workload, device, elems: Optional[int] = None,
+                   phase_step: int = 16) -> List[torch.Tensor]:
+    """R contribution buffers of `elems` (default: shard) elements.  With
+    phase_step p < 16, contribution r starts (r * p) mod 16 bytes past a
+    16-byte boundary, as contributions carved back to back from one buffer do
+    when the shard size is not a multiple of 8 elements (p = 8, 4 or 2; fp32
+    data takes 8 or 4)."""
     n = w.shard if elems is None else elems
-    return [torch.empty(n, dtype=w.torch_lp, device=device) for _ in range(w.R)]
+    if phase_step == 16:
+        return [torch.empty(n, dtype=w.torch_lp, device=device) for _ in range(w.R)]
+    esz = torch.empty(0, dtype=w.torch_lp).element_size()
+    if phase_step not in (8, 4, 2) or phase_step % esz:
+        raise ValueError(f"phase_step {phase_step} for {esz}-byte elements")
+    out = []
+    for r in range(w.R):
+        base = torch.empty(n + 16 // esz, dtype=w.torch_lp, device=device)
+        k = (r * phase_step) % 16 // esz
+        out.append(base[k:k + n])
+    return out

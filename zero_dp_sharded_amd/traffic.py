@@ -102,7 +102,7 @@ def traffic(args) -> int:
            "kernels": {}}
     for label, needle, algo in (("update", args.update_kernel,
                                  args.update_bytes_per_elem * args.elems),
-                                ("reduce", "reduce_vec_kernel", None)):
+                                ("reduce", args.reduce_kernel, None)):
         try:
             f, nf = _match(fetch, needle)
             w, nw = _match(write, needle)
@@ -159,6 +159,9 @@ def main() -> int:
                    help="name fragment of the update kernel (adam_vec_kernel, sgd_vec_kernel)")
     t.add_argument("--update-bytes-per-elem", type=int, default=28,
                    help="algorithmic bytes of the update per element")
+    t.add_argument("--reduce-kernel", default="reduce_vec_kernel",
+                   help="name fragment of the bucket reduce kernel (reduce_vec_kernel, or "
+                        "reduce_shift_kernel for contributions off the output's phase)")
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
     t.add_argument("--out", required=True)
