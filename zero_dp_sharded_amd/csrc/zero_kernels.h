@@ -265,6 +265,13 @@ struct ReduceLaunch {
     uint32_t lds_reserve;  // dynamic LDS that caps workgroups per CU
     int32_t small;         // 1: a bucket of a small shard (see shard_small)
     int32_t shift;         // 1: contributions off the output's 16-byte phase (see above)
+    // Element-wise part (the head [0, sc_a_len) and [sc_b_start, sc_b_start +
+    // sc_b_len)) done by the last workgroup of the launch, one element per
+    // lane, when sc_inline is set: the dispatch sets it on the last launch of
+    // a vector body when the part fits one workgroup's lanes, and then runs no
+    // element-wise kernel.
+    int32_t sc_inline;
+    int64_t sc_a_len, sc_b_start, sc_b_len;
     const DevState* dev;
     DevState* snapshot;    // set: workgroup 0 copies *dev there (see InlineFold)
 };
@@ -362,12 +369,14 @@ struct SgdLaunch {
 inline int run_width(int32_t lp) { return lp == 3 ? 4 : 8; }
 
 // Partial slots a reduce / scan of this layout writes: one per workgroup of
-// the vector kernel plus one per workgroup of the element-wise kernel.  W is
+// the vector kernel plus one per workgroup of the element-wise kernel, which a
+// reduce (inline_scalars) does not launch when it has a vector body and at
+// most BS element-wise elements (its last vector workgroup takes them).  W is
 // the run width of the storage format, U the runs per lane and BS the lanes
 // per workgroup (red_runs(R, nvec) and red_block(R) for a reduce, kScanRuns
 // and kScanBlock for a scan).
 int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok, int W, int U,
-                      int BS);
+                      int BS, bool inline_scalars = false);
 
 hipError_t launch_reduce(const ReduceLaunch& L, hipStream_t s);
 hipError_t launch_scan(const ScanLaunch& L, hipStream_t s);

@@ -218,6 +218,14 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 
 // ----------------------------------------------------------------- reduce
 
+// Whether a reduce's element-wise elements go to its last vector workgroup
+// (one per lane) instead of an element-wise launch.
+__host__ __device__ inline bool scalars_inline(int64_t vblocks, int64_t scalars, int BS)
+{
+    return vblocks >= 1 && scalars <= BS;
+}
+
+
 // Finish run vi of the vector body (elements head + W vi ..): acc holds the
 // fp32 sum over r = 0..R-1 in order from +0; scale by fp32(1/R), convert to
 // the storage format (round to nearest even), store, check.
@@ -245,6 +253,20 @@ __device__ __forceinline__ void reduce_s(const ReduceLaunch& L, int64_t e, float
     const T o = static_cast<T>(pin_f32(acc * L.inv_r));
     static_cast<T*>(L.out)[e] = o;
     check_s<LP>(o, inv_scale, flag, ss);
+}
+
+// The last workgroup of a launch with L.sc_inline set reduces the element-wise
+// elements, lane k the k-th of them, into its own flag and sum.
+template <int LP>
+__device__ __forceinline__ void reduce_scalars_inline(const ReduceLaunch& L, float inv_scale,
+                                                      int& flag, double& ss)
+{
+    if (L.sc_inline && blockIdx.x == gridDim.x - 1) {
+        const int64_t k = threadIdx.x;
+        if (k < L.sc_a_len + L.sc_b_len)
+            reduce_s<LP>(L, k < L.sc_a_len ? k : L.sc_b_start + (k - L.sc_a_len), inv_scale, flag,
+                         ss);
+    }
 }
 
 // Device-resident steps: workgroup 0 of each reduce or scan launch copies the
@@ -321,6 +343,7 @@ __global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
             reduce_finish<LP, NT>(L, vi, acc, inv_scale, flag, ss);
         }
     }
+    reduce_scalars_inline<LP>(L, inv_scale, flag, ss);
     if constexpr (SNAP) snapshot_state(L.dev, L.snapshot);
     block_partial<BS>(L.partial + L.slot_base + blockIdx.x, flag, ss);
 }
@@ -463,6 +486,7 @@ __global__ __launch_bounds__(BS) void reduce_shift_kernel(ReduceLaunch L)
         const int64_t vi = v0 + u * BS;
         if (vi < L.nvec) reduce_finish<LP, NT>(L, vi, acc[u], inv_scale, flag, ss);
     }
+    reduce_scalars_inline<LP>(L, inv_scale, flag, ss);
     if constexpr (SNAP) snapshot_state(L.dev, L.snapshot);
     block_partial<BS>(L.partial + L.slot_base + blk, flag, ss);
 }
@@ -1040,18 +1064,24 @@ hipError_t reduce_dispatch(const ReduceLaunch& L, hipStream_t s)
     // consecutive launches of at most kMaxLaunchItems work-items; each starts
     // its runs and its partial slots where the previous one stopped
     const int64_t max_blocks = kMaxLaunchItems / BS;
+    const Ranges rg = ranges_of(L.n, L.head, W * L.nvec, L.vec_ok);
+    const bool inl = scalars_inline(vblocks, rg.a_len + rg.b_len, BS);
     for (int64_t b0 = 0; b0 < vblocks; b0 += max_blocks) {
         const int64_t nb = vblocks - b0 < max_blocks ? vblocks - b0 : max_blocks;
         ReduceLaunch part = L;
         part.head = L.head + W * runs_per_block * b0;
         part.nvec = L.nvec - runs_per_block * b0;
         part.slot_base = L.slot_base + b0;
+        // the element-wise elements ride on the last workgroup of the last launch
+        part.sc_inline = inl && b0 + nb == vblocks;
+        part.sc_a_len = rg.a_len;
+        part.sc_b_start = rg.b_start;
+        part.sc_b_len = rg.b_len;
         hipError_t e = L.shift ? reduce_shift_launch<LP>(part, (unsigned)nb, U, small, s)
                                 : reduce_vec_launch<LP>(part, (unsigned)nb, U, small, s);
         if (e != hipSuccess) return e;
     }
-    const Ranges rg = ranges_of(L.n, L.head, W * L.nvec, L.vec_ok);
-    const int64_t sblocks = ceil_div(rg.a_len + rg.b_len, kScalarElemsPerBlock);
+    const int64_t sblocks = inl ? 0 : ceil_div(rg.a_len + rg.b_len, kScalarElemsPerBlock);
     if (sblocks > 0)
         reduce_elem_kernel<LP><<<(unsigned)sblocks, kScalarBlock, 0, s>>>(L, rg, L.slot_base + vblocks);
     return hipGetLastError();
@@ -1192,11 +1222,12 @@ hipError_t sgd_dispatch_kind(const SgdLaunch& a, hipStream_t s)
 }  // namespace
 
 int64_t reduce_blocks(int64_t n, int64_t head, int64_t nvec, int32_t vec_ok, int W, int U,
-                      int BS)
+                      int BS, bool inline_scalars)
 {
     (void)head;
     const int64_t vblocks = vec_ok ? ceil_div(nvec, (int64_t)BS * U) : 0;
     const int64_t scalars = vec_ok ? n - (int64_t)W * nvec : n;
+    if (inline_scalars && scalars_inline(vblocks, scalars, BS)) return vblocks;
     return vblocks + ceil_div(scalars, kScalarElemsPerBlock);
 }
 

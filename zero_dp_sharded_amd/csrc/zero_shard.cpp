@@ -637,7 +637,7 @@ static zero_status enqueue_reduce(zero_shard_s* h, const void* const* ptrs, int3
     L.small = zk::shard_small(h->S) ? 1 : 0;
     const int64_t blocks = zk::reduce_blocks(L.n, L.head, L.nvec, L.vec_ok, W,
                                              zk::red_runs(L.R, L.nvec, L.small != 0, L.shift != 0),
-                                             zk::red_block(L.R, L.small != 0));
+                                             zk::red_block(L.R, L.small != 0), true);
     if (L.slot_base + blocks > h->nslots)
         return fail(ZERO_ERR_UNSUPPORTED, "%s: partial slots exhausted", who);
     if (!launch) {
