@@ -17,10 +17,12 @@ constexpr int kMaxContrib = 64;
 //                    for buckets too small to fill the chip, where more
 //                    workgroups finish sooner);
 //   reduce, R >= 8:  64 lanes, 1 run, 12 workgroups per CU with 2-byte storage
-//                    and 10 with fp32 (6 from R = 16);
+//                    and 10 with fp32 (6 from R = 16); up to R = 8 the loads go
+//                    out in groups of 4 contributions;
 //   shift reduce (contributions off the output's 16-byte phase): 64 lanes,
 //                    2 runs and 14 workgroups per CU below R = 8; 1 run and 16
 //                    (2-byte storage) or 12 (fp32) workgroups per CU from R = 8;
+//                    batches of 4 contributions;
 //   scan (1 stream): 256 lanes, 4 runs, 8 workgroups per CU.
 // (The ZK_* macros exist only to build tuning variants; the defaults are the
 // measured optimum.)
@@ -50,6 +52,12 @@ constexpr int kMaxContrib = 64;
 #endif
 #ifndef ZK_RED_PER_CU_WIDE
 #define ZK_RED_PER_CU_WIDE 6
+#endif
+#ifndef ZK_RED_GROUP
+#define ZK_RED_GROUP 4
+#endif
+#ifndef ZK_RED_SHIFT_K
+#define ZK_RED_SHIFT_K 4
 #endif
 #ifndef ZK_RED_SHIFT_RUNS
 #define ZK_RED_SHIFT_RUNS 2
@@ -102,6 +110,12 @@ constexpr int kRedRuns = ZK_RED_RUNS;
 constexpr int kRedRunsMany = ZK_RED_RUNS_MANY;   // runs per lane when R >= 8
 constexpr int kRedManyR = 8;
 constexpr int kRedRunsSmall = ZK_RED_RUNS_SMALL;   // R < 8, bucket below kRedSmallNvec runs
+// contributions (of at most 8) whose loads a one-run-per-lane reduce issues
+// together
+constexpr int kRedGroup = ZK_RED_GROUP;
+// contributions the shift kernel takes per batch of loads (measured with one
+// run per lane: 4 beat 8 by 1-4 points)
+constexpr int kRedShiftK = ZK_RED_SHIFT_K;
 // runs per lane of the shift kernel below 8 contributions (its registers hold
 // two words per run and contribution in flight)
 constexpr int kRedShiftRuns = ZK_RED_SHIFT_RUNS;

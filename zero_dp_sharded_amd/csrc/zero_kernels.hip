@@ -296,8 +296,41 @@ __global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
     double ss = 0.0;
     const float inv_scale = check_inv_scale(L.inv_scale, L.dev);
     const int64_t v0 = (int64_t)blockIdx.x * (BS * U) + threadIdx.x;
-    if constexpr (RT > 0 && RT * U <= 16) {
-        // every load of all U runs in flight before the arithmetic
+    if constexpr (RT > 0 && RT <= 8 && U == 1) {
+        // One run per lane, up to 8 contributions: their loads in groups of
+        // kRedGroup, each group in flight together before its arithmetic.
+        // Lanes past the body load the body's last run again (a cache hit)
+        // and discard it: with the loads under a condition the compiler moved
+        // a run's first conversion and add in among them, so that the last
+        // load waited for the first.  Measured for R = 8 (fp16 / bf16 / fp32):
+        // groups of 4 beat all 8 at once by 1.5-3 points and groups of 2 by
+        // 6-8.
+        constexpr int G = RT < kRedGroup ? RT : kRedGroup;
+        const int64_t vc = v0 < L.nvec ? v0 : L.nvec - 1;
+        FW acc = (FW)(0.f);
+#pragma unroll
+        for (int r0 = 0; r0 < RT; r0 += G) {
+            // (L.R == RT: the test only keeps a later group's loads below the
+            // earlier group's arithmetic, where the compiler would hoist them)
+            if (r0 == 0 || r0 < L.R) {
+                VW x[G];
+#pragma unroll
+                for (int k = 0; k < G; ++k) x[k] = ld_v<VW, NT>(adv<LP>(L.c.p[r0 + k], L.head), vc);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int k = 0; k < G; ++k) acc = acc + __builtin_convertvector(x[k], FW);
+            }
+        }
+        if (v0 < L.nvec) reduce_finish<LP, NT>(L, v0, acc, inv_scale, flag, ss);
+    } else if constexpr (RT > 0) {
+        // Several runs per lane, or 16 contributions.  Each run's loads sit
+        // under its own condition, and the compiler widens each contribution
+        // as it arrives: with several runs, one run in flight at a time before
+        // every sum and store; with 16 contributions, a window of 6-10 loads.
+        // (Issuing all runs' loads first measured 3.4% slower for the R = 4
+        // reduce of three runs per lane, storing each run before the next
+        // one's loads 0.9% slower; for R = 16, groups of 8 loads measured 1.7%
+        // slower, all 16 at once 3.5%.)
         VW x[U][RT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -318,27 +351,21 @@ __global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
             }
         }
     } else {
+        // a contribution count known only at run time: batches of 8
         for (int u = 0; u < U; ++u) {
             const int64_t vi = v0 + u * BS;
             if (vi >= L.nvec) break;
             FW acc = (FW)(0.f);
-            if constexpr (RT > 0) {
-                VW x[RT];
+            for (int r0 = 0; r0 < L.R; r0 += 8) {
+                const int cnt = L.R - r0 < 8 ? L.R - r0 : 8;
+                VW x[8];
 #pragma unroll
-                for (int r = 0; r < RT; ++r) x[r] = ld_v<VW, NT>(adv<LP>(L.c.p[r], L.head), vi);
+                for (int k = 0; k < 8; ++k)
+                    if (k < cnt) x[k] = ld_v<VW, NT>(adv<LP>(L.c.p[r0 + k], L.head), vi);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int r = 0; r < RT; ++r) acc = acc + __builtin_convertvector(x[r], FW);
-            } else {
-                for (int r0 = 0; r0 < L.R; r0 += 8) {
-                    const int cnt = L.R - r0 < 8 ? L.R - r0 : 8;
-                    VW x[8];
-#pragma unroll
-                    for (int k = 0; k < 8; ++k)
-                        if (k < cnt) x[k] = ld_v<VW, NT>(adv<LP>(L.c.p[r0 + k], L.head), vi);
-#pragma unroll
-                    for (int k = 0; k < 8; ++k)
-                        if (k < cnt) acc = acc + __builtin_convertvector(x[k], FW);
-                }
+                for (int k = 0; k < 8; ++k)
+                    if (k < cnt) acc = acc + __builtin_convertvector(x[k], FW);
             }
             reduce_finish<LP, NT>(L, vi, acc, inv_scale, flag, ss);
         }
@@ -433,11 +460,11 @@ __device__ __forceinline__ unsigned shift_block(unsigned b, unsigned n)
 // the body, so every word lies inside the bucket.  Contributions are taken K at
 // a time with every load in flight before the arithmetic and added in
 // ascending r from +0: each element's result is the vector kernel's.
-template <int LP, int U, int BS, int SNAP, int NT>
+template <int LP, int RT, int U, int BS, int SNAP, int NT>
 __global__ __launch_bounds__(BS) void reduce_shift_kernel(ReduceLaunch L)
 {
     using FW = typename Fmt<LP>::FW;
-    constexpr int K = U == 1 ? 8 : 4;
+    constexpr int K = kRedShiftK;
     static_assert(U == 1 || BS == 64, "runs of one lane chain across one wave only");
     int flag = 0;
     double ss = 0.0;
@@ -448,25 +475,40 @@ __global__ __launch_bounds__(BS) void reduce_shift_kernel(ReduceLaunch L)
     FW acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) acc[u] = (FW)(0.f);
-    for (int r0 = 0; r0 < L.R; r0 += K) {
-        const int cnt = L.R - r0 < K ? L.R - r0 : K;
-        u4 lo[K][U], nx[K];
+    // lane 63's words past its last run, cleared once here: a clear inside a
+    // batch loop makes the loads of the next batch wait for this one's
+    u4 nx[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) nx[k] = u4{0u, 0u, 0u, 0u};
+    // Contributions r0 .. r0 + cnt - 1, every load in flight before the
+    // arithmetic: lanes past the word after the body load that word again (a
+    // cache hit) rather than branch around their loads, and lane 63's extra
+    // words come after all the others.
+    auto batch = [&](int r0, int cnt) {
+        u4 lo[K][U];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            nx[k] = u4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int u = 0; u < U; ++u) lo[k][u] = u4{0u, 0u, 0u, 0u};
             if (k < cnt) {
                 const char* p = static_cast<const char*>(adv<LP>(L.c.p[r0 + k], L.head));
                 const void* base = p - ((uintptr_t)p & 15u);
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int64_t vi = v0 + u * BS;
-                    if (vi <= L.nvec) lo[k][u] = ld_v<u4, NT>(base, vi);
-                    if (u == U - 1 && last_lane && vi < L.nvec) nx[k] = ld_v<u4, NT>(base, vi + 1);
+                    lo[k][u] = ld_v<u4, NT>(base, vi <= L.nvec ? vi : L.nvec);
                 }
             }
         }
+        if (last_lane && v0 + (U - 1) * BS < L.nvec) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                if (k < cnt) {
+                    const char* p = static_cast<const char*>(adv<LP>(L.c.p[r0 + k], L.head));
+                    const void* base = p - ((uintptr_t)p & 15u);
+                    nx[k] = ld_v<u4, NT>(base, v0 + (U - 1) * BS + 1);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             if (k < cnt) {
@@ -480,6 +522,13 @@ __global__ __launch_bounds__(BS) void reduce_shift_kernel(ReduceLaunch L)
                 }
             }
         }
+    };
+    if constexpr (RT > 0) {
+        // a known contribution count: straight-line batches
+#pragma unroll
+        for (int r0 = 0; r0 < RT; r0 += K) batch(r0, RT - r0 < K ? RT - r0 : K);
+    } else {
+        for (int r0 = 0; r0 < L.R; r0 += K) batch(r0, L.R - r0 < K ? L.R - r0 : K);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -1028,14 +1077,26 @@ hipError_t reduce_vec_launch(const ReduceLaunch& L, unsigned grid, int U, bool s
 }
 
 // The shift kernel of a bucket (L.shift = 1): the vector kernel's workgroups,
-// with kRedShiftRuns runs per lane below 8 contributions on large shards.
+// with kRedShiftRuns runs per lane below 8 contributions on large shards, and
+// a compiled-in contribution count for R = 4, 8 and 16.
+template <int LP, int RT, int U, int BS, int NT>
+void reduce_shift_rt(const ReduceLaunch& L, unsigned grid, hipStream_t s)
+{
+    if (L.snapshot != nullptr)
+        reduce_shift_kernel<LP, RT, U, BS, 1, NT><<<grid, BS, L.lds_reserve, s>>>(L);
+    else
+        reduce_shift_kernel<LP, RT, U, BS, 0, NT><<<grid, BS, L.lds_reserve, s>>>(L);
+}
+
 template <int LP, int U, int BS, int NT>
 void reduce_shift_go(const ReduceLaunch& L, unsigned grid, hipStream_t s)
 {
-    if (L.snapshot != nullptr)
-        reduce_shift_kernel<LP, U, BS, 1, NT><<<grid, BS, L.lds_reserve, s>>>(L);
-    else
-        reduce_shift_kernel<LP, U, BS, 0, NT><<<grid, BS, L.lds_reserve, s>>>(L);
+    switch (L.R) {
+    case 4: reduce_shift_rt<LP, 4, U, BS, NT>(L, grid, s); break;
+    case 8: reduce_shift_rt<LP, 8, U, BS, NT>(L, grid, s); break;
+    case 16: reduce_shift_rt<LP, 16, U, BS, NT>(L, grid, s); break;
+    default: reduce_shift_rt<LP, 0, U, BS, NT>(L, grid, s); break;
+    }
 }
 
 template <int LP>
