@@ -141,3 +141,9 @@ def test_copy_helper_refuses_bad_arguments_before_device_work():
     for dst, src, n in ((None, b, 16), (a, None, 16), (a, b, 0), (a, b, -16), (a, b, 24),
                         (a + 8, b, 16), (a, b + 4, 16), (a, b, (1 << 34) + 16)):
         assert lib.hbm_copy(dst, src, n, None) == 1, (dst, src, n)
+
+
+def test_ab_reduce_prints_usage_without_builds(capsys):
+    from zero_dp_sharded_amd import ab_reduce
+    assert ab_reduce.main([]) == 2
+    assert "ab_reduce" in capsys.readouterr().err
