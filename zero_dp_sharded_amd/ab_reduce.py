@@ -1,16 +1,19 @@
-"""Interleaved A/B of the bucket reduce between builds of the library.
+"""Interleaved A/B of the bucket reduce or the update between builds of the library.
 
     python -m zero_dp_sharded_amd.ab_reduce WORKLOAD PHASE REPS NAME=LIB [NAME=LIB ...]
+    python -m zero_dp_sharded_amd.ab_reduce --update WORKLOAD PHASE REPS NAME=LIB [...]
 
 Loads every listed libzeroshard.so into one process (the binding once per
 build), makes one handle per build over the same seeded shard and
 contributions (contribution r at (r * PHASE) mod 16 bytes; 16 = aligned), and
-times all C_B bucket reduces of a step with HIP events, three steps per build
-per round, the builds in alternating order over REPS rounds.  Each step is
-completed with the check and the update, so the handles stay in step.  Prints
-one JSON line: per build the median step-reduce time and the bandwidth of the
-reduce's algorithmic bytes ((R + 1) x element size per shard element) as a
-percentage of 8 TB/s, with the range over the rounds.  Interleaving in one
+times, with HIP events, all C_B bucket reduces of a step or (--update) the
+step's update kernel (the synchronous-check flow's zero_adam_step), three
+steps per build per round, the builds in alternating order over REPS rounds.
+Each step is completed with the check and the update, so the handles stay in
+step.  Prints one JSON line: per build the median time and the bandwidth of
+the kernel's algorithmic bytes ((R + 1) x element size per shard element for
+the reduce, 28 B for the Adam update) as
+a percentage of 8 TB/s, with the range over the rounds.  Interleaving in one
 process puts every build on the same box, placement and HBM temperature,
 which sequential runs do not (on MI355X their spread was several points).
 
@@ -40,6 +43,9 @@ def load_binding(name: str, lib: str):
 
 
 def main(argv) -> int:
+    update = bool(argv) and argv[0] == "--update"
+    if update:
+        argv = argv[1:]
     if len(argv) < 4:
         print(__doc__, file=sys.stderr)
         return 2
@@ -67,11 +73,17 @@ def main(argv) -> int:
 
     def step(zs, h):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        if not update:
+            e0.record()
         zs.reduce_buckets(h, bufs, S, w.bucket_elems)
-        e1.record()
+        if not update:
+            e1.record()
         zs.zero_overflow_check(h)
+        if update:
+            e0.record()
         zs.zero_adam_step(h)
+        if update:
+            e1.record()
         return e0, e1
 
     try:
@@ -88,9 +100,11 @@ def main(argv) -> int:
     finally:
         for _, zs, h in handles:
             zs.zero_shard_destroy(h)
-    nbytes = S * (w.R + 1) * grad.element_size()
+    esz = grad.element_size()
+    nbytes = S * 28 if update else S * (w.R + 1) * esz
     pct = lambda ms: round(nbytes / (ms * 1e-3) / 8e12 * 100, 2)
-    out = {"workload": wname, "contrib_phase_bytes": phase, "rounds": reps}
+    out = {"workload": wname, "kernel": "update" if update else "reduce",
+           "contrib_phase_bytes": phase, "rounds": reps}
     for n, x in times.items():
         med = statistics.median(x)
         out[n] = {"median_ms": round(med, 4), "pct_of_8tbs": pct(med),
