@@ -39,8 +39,11 @@ PHASES = {
     "2-byte phases": ([0, 2, 6], 0),
     # output at 6 mod 16: head 5, then a phase of 6 elements moves it to 13
     "2-byte phases, output off": ([14, 2, 6, 0], 6),
-    # nine contributions: one full batch of eight and one more
+    # nine contributions: two full batches of four and one more (a count the
+    # kernel is not compiled for)
     "nine contributions": ([2, 4, 6, 8, 10, 12, 14, 0, 2], 4),
+    # sixteen: the compiled-in count, four batches
+    "sixteen contributions": ([(2 * r) % 16 for r in range(16)], 10),
 }
 
 
@@ -124,7 +127,7 @@ def test_shift_above_the_small_shard_limit(lp):
     more contributions) and three (fewer)."""
     for offs, goff in (([0, 8, 0, 8, 8, 0, 0, 8], 0), ([4, 0, 12], 8), ([0, 8, 8, 0], 8),
                        ([12, 4, 4, 8, 0, 4, 8, 12, 0], 0), ([2, 0, 14, 6], 10),
-                       ([6, 2, 0, 14, 12, 10, 8, 4], 2)):
+                       ([6, 2, 0, 14, 12, 10, 8, 4], 2), ([(6 * r) % 16 for r in range(16)], 14)):
         if lp == "fp32":
             offs, goff = _fp32_offsets(offs, goff)
         _run(lp, 8_400_017, 2_100_001, offs, goff, "device")

@@ -33,6 +33,7 @@ class Case:
     max_norm: float = 0.0
     plant_inf: bool = False
     steps: int = 1
+    phase: int = 16        # contribution r at (r * phase) mod 16 bytes (16: aligned)
 
 
 def _make(case, seed):
@@ -44,14 +45,17 @@ def _make(case, seed):
     grad = torch.zeros(case.S, dtype=case.lp, device=DEV)
     contribs = []
     if case.R:
-        contribs = synth.alloc_contribs(w, DEV, elems=case.S)
+        contribs = synth.alloc_contribs(w, DEV, elems=case.S, phase_step=case.phase)
     steps = []
     for s in range(case.steps):
         if case.R:
             synth.fill_contribs(w, contribs, s, case.counters[1], seed)
             if case.plant_inf and s == case.steps - 1:
                 contribs[case.R - 1][case.S - 3] = float("inf")
-            steps.append([c.clone() for c in contribs])
+            kept = synth.alloc_contribs(w, DEV, elems=case.S, phase_step=case.phase)
+            for d, c in zip(kept, contribs):
+                d.copy_(c)
+            steps.append(kept)
         else:
             g = torch.empty(case.S, dtype=case.lp, device=DEV)
             synth.fill_contribs(dataclasses.replace(w, R=1), [g], s, case.counters[1], seed)
@@ -128,6 +132,8 @@ CASES = [
     # every later case smaller than the one before it
     Case("fp16 R=4, 1,000,003 elements, clipping", 1_000_003, 4, torch.float16, 262_144,
          (0, 1024.0, 0), max_norm=0.05),
+    Case("fp16 R=8, 500,009 elements, contributions at 2-byte phases", 500_009, 8,
+         torch.float16, 131_072, (3, 256.0, 1), phase=2),
     Case("bf16 R=9, 300,007 elements, +inf: skipped, scale halved", 300_007, 9, torch.bfloat16,
          65_536, (5, 64.0, 3), plant_inf=True),
     Case("fp16 scan of a caller-filled grad_shard, 70,001 elements", 70_001, 0, torch.float16,
@@ -147,8 +153,8 @@ def test_noalloc_back_to_back_equals_handle_flow():
     for c, st, ref, (ia, ca) in zip(CASES, states, saved, got):
         ib, cb = _handle(c, ref)
         _compare(c, st, ref, ia, ib, ca, cb)
-    assert got[1][0][-1].overflow == 1 and got[1][1] == (5, 32.0, 0)
-    assert got[3][1][1] == 4.0                                   # grew 2 -> 4 after 4 clean
+    assert got[2][0][-1].overflow == 1 and got[2][1] == (5, 32.0, 0)
+    assert got[4][1][1] == 4.0                                   # grew 2 -> 4 after 4 clean
 
 
 def test_noalloc_refuses_a_shard_beyond_its_scratch():
