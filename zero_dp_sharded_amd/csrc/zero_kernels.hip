@@ -225,7 +225,6 @@ __host__ __device__ inline bool scalars_inline(int64_t vblocks, int64_t scalars,
     return vblocks >= 1 && scalars <= BS;
 }
 
-
 // Finish run vi of the vector body (elements head + W vi ..): acc holds the
 // fp32 sum over r = 0..R-1 in order from +0; scale by fp32(1/R), convert to
 // the storage format (round to nearest even), store, check.
