@@ -174,7 +174,14 @@ constexpr int kSgdPlainPerCU = ZK_SGD_PLAIN_PER_CU;
 #define ZK_SMALL_ELEMS (int64_t(1) << 23)
 #endif
 constexpr int64_t kSmallElems = ZK_SMALL_ELEMS;
-constexpr int kSmallBlock = 256;
+#ifndef ZK_SMALL_BLOCK
+#define ZK_SMALL_BLOCK 256
+#endif
+#ifndef ZK_SMALL_UPD_BLOCK
+#define ZK_SMALL_UPD_BLOCK 256
+#endif
+constexpr int kSmallBlock = ZK_SMALL_BLOCK;         // reduce lanes per workgroup
+constexpr int kSmallUpdBlock = ZK_SMALL_UPD_BLOCK;  // update lanes per workgroup
 inline bool shard_small(int64_t S) { return S <= kSmallElems; }
 // Lanes per workgroup and runs per lane of a bucket reduce (nvec runs, R
 // contributions) of a small shard or not, in the vector or the shift kernel.
@@ -191,9 +198,9 @@ inline int red_runs(int R, int64_t nvec, bool small, bool shift = false)
     return nvec < kRedSmallNvec ? kRedRunsSmall : kRedRuns;
 }
 // Update of an S-element shard: lanes per workgroup and groups per lane.
-inline int adam_lanes(int64_t S) { return shard_small(S) ? kSmallBlock : kAdamBlock; }
+inline int adam_lanes(int64_t S) { return shard_small(S) ? kSmallUpdBlock : kAdamBlock; }
 inline int adam_groups(int64_t S) { return shard_small(S) ? 1 : kAdamGroups; }
-inline int sgd_lanes(int64_t S) { return shard_small(S) ? kSmallBlock : kSgdBlock; }
+inline int sgd_lanes(int64_t S) { return shard_small(S) ? kSmallUpdBlock : kSgdBlock; }
 inline int sgd_groups(int64_t S, bool mom)
 {
     return shard_small(S) ? 1 : (mom ? kSgdMomGroups : kSgdPlainGroups);

@@ -1209,7 +1209,7 @@ hipError_t adam_dispatch(const AdamLaunch& a, hipStream_t s)
          !one_launch(a.ngroups, lanes, groups) || a.src.fold.n < 1 ||
          a.src.fold.n > kInlineFoldMax))
         return hipErrorInvalidValue;          // the inline fold needs one vector launch
-    hipError_t e = small ? adam_vec_launches<LP, WD, kSmallBlock, 1, 0>(a, vblocks, s)
+    hipError_t e = small ? adam_vec_launches<LP, WD, kSmallUpdBlock, 1, 0>(a, vblocks, s)
                          : adam_vec_launches<LP, WD, kAdamBlock, kAdamGroups, 1>(a, vblocks, s);
     if (e != hipSuccess || a.src.fold.partial != nullptr) return e;
     const Ranges rg = ranges_of(a.n, a.head, 4 * a.ngroups, a.vec_ok);
@@ -1261,7 +1261,7 @@ hipError_t sgd_dispatch(const SgdLaunch& a, hipStream_t s)
          !one_launch(a.ngroups, lanes, groups) || a.src.fold.n < 1 ||
          a.src.fold.n > kInlineFoldMax))
         return hipErrorInvalidValue;          // the inline fold needs one vector launch
-    hipError_t e = small ? sgd_vec_launches<LP, MOM, WD, kSmallBlock, 1, 0>(a, vblocks, s)
+    hipError_t e = small ? sgd_vec_launches<LP, MOM, WD, kSmallUpdBlock, 1, 0>(a, vblocks, s)
                          : sgd_vec_launches<LP, MOM, WD, kSgdBlock, G, 1>(a, vblocks, s);
     if (e != hipSuccess || a.src.fold.partial != nullptr) return e;
     const Ranges rg = ranges_of(a.n, a.head, 4 * a.ngroups, a.vec_ok);
