@@ -197,6 +197,26 @@ inline int red_runs(int R, int64_t nvec, bool small, bool shift = false)
     if (shift) return kRedShiftRuns;
     return nvec < kRedSmallNvec ? kRedRunsSmall : kRedRuns;
 }
+// The block of runs (and partial slot) workgroup b of n takes in the shift
+// kernel.  Workgroups are dealt round-robin to the 8 XCDs; within each full
+// set of 8 * kRedShiftGroup workgroups this hands XCD x (workgroups b = x mod 8)
+// the kRedShiftGroup consecutive blocks x * kRedShiftGroup + (0 ..), so all
+// XCDs still sweep one narrow front while neighbouring blocks mostly share an
+// L2.  A bijection on [0, n): the last, partial set keeps the plain order.
+__host__ __device__ inline unsigned shift_block(unsigned b, unsigned n)
+{
+    if constexpr (kRedShiftGroup <= 1) {
+        (void)n;
+        return b;
+    } else {
+        constexpr unsigned set = 8u * kRedShiftGroup;
+        const unsigned s0 = b - b % set;
+        if (s0 + set > n) return b;
+        const unsigned j = b - s0;
+        return s0 + (j % 8u) * kRedShiftGroup + j / 8u;
+    }
+}
+
 // Update of an S-element shard: lanes per workgroup and groups per lane.
 inline int adam_lanes(int64_t S) { return shard_small(S) ? kSmallUpdBlock : kAdamBlock; }
 inline int adam_groups(int64_t S) { return shard_small(S) ? 1 : kAdamGroups; }

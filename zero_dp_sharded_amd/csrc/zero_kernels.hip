@@ -423,26 +423,6 @@ __device__ __forceinline__ void add_cut(typename Fmt<LP>::FW (&acc)[U], const u4
     }
 }
 
-// The block of runs (and partial slot) workgroup b of n takes in the shift
-// kernel.  Workgroups are dealt round-robin to the 8 XCDs; within each full
-// set of 8 * kRedShiftGroup workgroups this hands XCD x (workgroups b = x mod 8)
-// the kRedShiftGroup consecutive blocks x * kRedShiftGroup + (0 ..), so all
-// XCDs still sweep one narrow front while neighbouring blocks mostly share an
-// L2.  A bijection on [0, n): the last, partial set keeps the plain order.
-__device__ __forceinline__ unsigned shift_block(unsigned b, unsigned n)
-{
-    if constexpr (kRedShiftGroup <= 1) {
-        (void)n;
-        return b;
-    } else {
-        constexpr unsigned set = 8u * kRedShiftGroup;
-        const unsigned s0 = b - b % set;
-        if (s0 + set > n) return b;
-        const unsigned j = b - s0;
-        return s0 + (j % 8u) * kRedShiftGroup + j / 8u;
-    }
-}
-
 // Vector body of a bucket whose contributions do not all share the output's
 // address phase modulo 16 bytes (for example contributions carved back to back
 // from one buffer when the shard size is not a multiple of 8).  The output
