@@ -13,15 +13,19 @@
 //  - a cap on resident workgroups per CU, set by reserving dynamic LDS the
 //    kernels never touch: with the 3 to 17 concurrent streams of the update
 //    and reduce kernels, fewer resident waves (10 per CU for Adam, 16 or 24
-//    for SGD, 12 or 8 for the reduce) sustain more HBM bandwidth than full
-//    occupancy; the one-stream scan keeps 32 waves with 4 runs per lane.  The
-//    measured optimum keeps roughly 96-144 KiB of loads in flight per CU;
+//    for SGD, 6 to 12 for the reduce, 12 to 16 for the shift reduce) sustain
+//    more HBM bandwidth than full occupancy; the one-stream scan keeps 32
+//    waves with 4 runs per lane;
+//  - in the reduce, loads issued in measured groups (a run of up to 8
+//    contributions in groups of 4, several runs one run at a time), each group
+//    ahead of its arithmetic;
 //  - shards of at most 8M elements, whose step fits the caches, instead run
 //    256-lane workgroups with one run or group per lane and plain (cached)
 //    loads and stores in every bucket reduce and in the update.
-// The only cross-lane work is the fixed-shape reduction of the overflow flag
-// and the squared gradient norm: wave butterfly, one LDS slot per wave, one
-// fp64 partial per workgroup, then a fixed-order fold of one or two levels
+// Cross-lane work: the shift reduce takes each lane's next 16-byte word from
+// the neighbouring lane (DPP); the overflow flag and the squared gradient norm
+// go through a fixed-shape reduction: wave butterfly, one LDS slot per wave,
+// one fp64 partial per workgroup, then a fixed-order fold of one or two levels
 // whose last lane also computes the clipping coefficient and, in the
 // device-resident flow, decides the step.  A device-resident step of at most
 // 512 partials has no fold launch: every update workgroup repeats the fold in
