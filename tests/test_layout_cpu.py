@@ -1,8 +1,8 @@
 """Host-side layout helpers of the kernels, compiled for the CPU from
 zero_kernels.h: the shift reduce's block order (shift_block) is a bijection on
 [0, n) for every grid size, hands each XCD (workgroups b = x mod 8) consecutive
-blocks in groups of kRedShiftGroup, and leaves a last, partial set of 8 groups
-in the plain order."""
+blocks in groups of G, and leaves a last, partial set of 8 groups in the plain
+order; G is kRedShiftGroupRuns wave-runs for the kernel's shapes."""
 import os
 import shutil
 import subprocess
@@ -13,27 +13,35 @@ PROGRAM = r"""
 #include <cstdio>
 #include <vector>
 #include "zero_kernels.h"
-int main() {
-    const unsigned G = zk::kRedShiftGroup, set = 8u * G;
+template <unsigned G>
+static int check() {
+    const unsigned set = 8u * G;
     for (unsigned n = 1; n <= 5000; n += (n < 600 ? 1 : 37)) {
         std::vector<int> seen(n, 0);
         for (unsigned b = 0; b < n; ++b) {
-            const unsigned m = zk::shift_block(b, n);
-            if (m >= n || seen[m]++) { std::printf("not a bijection n=%u b=%u\n", n, b); return 1; }
+            const unsigned m = zk::shift_block<G>(b, n);
+            if (m >= n || seen[m]++) { std::printf("not a bijection G=%u n=%u b=%u\n", G, n, b); return 1; }
             const unsigned s0 = b - b % set;
-            if (s0 + set <= n) {
+            if (G > 1 && s0 + set <= n) {
                 // within a full set, XCD b % 8 takes G consecutive blocks
                 const unsigned j = b - s0;
-                if (m != s0 + (j % 8u) * G + j / 8u) { std::printf("order n=%u b=%u\n", n, b); return 1; }
-                if (b >= 8 && b - 8 >= s0 && zk::shift_block(b - 8, n) + 1 != m) {
-                    std::printf("not consecutive n=%u b=%u\n", n, b); return 1;
+                if (m != s0 + (j % 8u) * G + j / 8u) { std::printf("order G=%u n=%u b=%u\n", G, n, b); return 1; }
+                if (b >= 8 && b - 8 >= s0 && zk::shift_block<G>(b - 8, n) + 1 != m) {
+                    std::printf("not consecutive G=%u n=%u b=%u\n", G, n, b); return 1;
                 }
             } else if (m != b) {
-                std::printf("partial set reordered n=%u b=%u\n", n, b); return 1;
+                std::printf("reordered G=%u n=%u b=%u\n", G, n, b); return 1;
             }
         }
     }
-    std::printf("ok %u\n", G);
+    return 0;
+}
+int main() {
+    if (check<1>() || check<16>() || check<zk::shift_group<64, 2>()>() ||
+        check<zk::shift_group<64, 1>()>())
+        return 1;
+    std::printf("ok %u %u %u\n", zk::shift_group<64, 1>(), zk::shift_group<64, 2>(),
+                zk::shift_group<256, 1>());
     return 0;
 }
 """
@@ -51,4 +59,5 @@ def test_shift_block_order(tmp_path):
     assert r.returncode == 0, r.stderr[-2000:]
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stdout
-    assert out.stdout.startswith("ok 32")
+    # 64 wave-runs: 64 one-wave workgroups of one run, 32 of two, 16 of four waves
+    assert out.stdout.startswith("ok 64 32 16")

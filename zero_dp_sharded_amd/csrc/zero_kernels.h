@@ -71,8 +71,14 @@ constexpr int kMaxContrib = 64;
 #ifndef ZK_RED_SHIFT_PER_CU_MANY_2B
 #define ZK_RED_SHIFT_PER_CU_MANY_2B 16
 #endif
-#ifndef ZK_RED_SHIFT_GROUP
-#define ZK_RED_SHIFT_GROUP 32
+#ifndef ZK_RED_SHIFT_NX_EARLY_2B
+#define ZK_RED_SHIFT_NX_EARLY_2B 1
+#endif
+#ifndef ZK_RED_SHIFT_NX_EARLY_F32
+#define ZK_RED_SHIFT_NX_EARLY_F32 0
+#endif
+#ifndef ZK_RED_SHIFT_GROUP_RUNS
+#define ZK_RED_SHIFT_GROUP_RUNS 64
 #endif
 #ifndef ZK_SCAN_BLOCK
 #define ZK_SCAN_BLOCK 256
@@ -119,10 +125,20 @@ constexpr int kRedShiftK = ZK_RED_SHIFT_K;
 // runs per lane of the shift kernel below 8 contributions (its registers hold
 // two words per run and contribution in flight)
 constexpr int kRedShiftRuns = ZK_RED_SHIFT_RUNS;
-// The shift kernel hands each XCD kRedShiftGroup consecutive workgroups' runs
-// at a time, so that the word a wave's last lane reads past its runs is
-// usually read by a wave of the same XCD (same L2) as well (0: plain order).
-constexpr int kRedShiftGroup = ZK_RED_SHIFT_GROUP;
+// The shift kernel hands each XCD kRedShiftGroupRuns consecutive wave-runs
+// (kRedShiftGroupRuns / U workgroups of U runs per lane) at a time, so that the
+// word a wave's last lane reads past its runs is usually read by a wave of the
+// same XCD (same L2) as well (0: plain order).  64 measured best for one and
+// two runs per lane (32 or 128 lose up to 2.5 points with two).
+constexpr int kRedShiftGroupRuns = ZK_RED_SHIFT_GROUP_RUNS;
+// Lane 63's word past its last run: loaded before the contribution runs with
+// the default cache policy (true), or after them, nontemporal (false).  Early
+// and cached, for 2-byte data, it reads x1.005 of the algorithmic bytes instead
+// of x1.020 and runs 1-4 points faster; for fp32 it made every wave wait for
+// those loads before issuing its runs (8 points slower), so fp32 keeps them
+// last.
+constexpr bool kRedShiftNxEarly2B = ZK_RED_SHIFT_NX_EARLY_2B != 0;
+constexpr bool kRedShiftNxEarlyF32 = ZK_RED_SHIFT_NX_EARLY_F32 != 0;
 // Resident shift-kernel workgroups per CU below 8 contributions, and from 8
 // with fp32 and with 2-byte storage: more than the vector kernel's, whose
 // loads it matches, to cover its extra exchange and shift instructions.
@@ -198,23 +214,33 @@ inline int red_runs(int R, int64_t nvec, bool small, bool shift = false)
     return nvec < kRedSmallNvec ? kRedRunsSmall : kRedRuns;
 }
 // The block of runs (and partial slot) workgroup b of n takes in the shift
-// kernel.  Workgroups are dealt round-robin to the 8 XCDs; within each full
-// set of 8 * kRedShiftGroup workgroups this hands XCD x (workgroups b = x mod 8)
-// the kRedShiftGroup consecutive blocks x * kRedShiftGroup + (0 ..), so all
-// XCDs still sweep one narrow front while neighbouring blocks mostly share an
-// L2.  A bijection on [0, n): the last, partial set keeps the plain order.
+// kernel, for groups of G workgroups.  Workgroups are dealt round-robin to the
+// 8 XCDs; within each full set of 8 * G workgroups this hands XCD x
+// (workgroups b = x mod 8) the G consecutive blocks x * G + (0 ..), so all XCDs
+// still sweep one narrow front while neighbouring blocks mostly share an L2.
+// A bijection on [0, n): the last, partial set keeps the plain order (as does
+// G <= 1).
+template <unsigned G>
 __host__ __device__ inline unsigned shift_block(unsigned b, unsigned n)
 {
-    if constexpr (kRedShiftGroup <= 1) {
+    if constexpr (G <= 1) {
         (void)n;
         return b;
     } else {
-        constexpr unsigned set = 8u * kRedShiftGroup;
+        constexpr unsigned set = 8u * G;
         const unsigned s0 = b - b % set;
         if (s0 + set > n) return b;
         const unsigned j = b - s0;
-        return s0 + (j % 8u) * kRedShiftGroup + j / 8u;
+        return s0 + (j % 8u) * G + j / 8u;
     }
+}
+
+// The shift kernel's group: kRedShiftGroupRuns wave-runs in workgroups of BS
+// lanes with U runs per lane.
+template <int BS, int U>
+__host__ __device__ constexpr unsigned shift_group()
+{
+    return (unsigned)(kRedShiftGroupRuns / (U * (BS / 64)));
 }
 
 // Update of an S-element shard: lanes per workgroup and groups per lane.

@@ -9,7 +9,10 @@
 //  - every load and store instruction of a wave covers one contiguous span
 //    (lane-consecutive 16-byte runs, or the 8-byte groups of four 2-byte
 //    values of the update);
-//  - nontemporal loads and stores (each byte is touched once per step);
+//  - nontemporal loads and stores (each byte is touched once per step), but
+//    for the one word per wave of 2-byte data that the shift reduce reads
+//    twice (the next workgroup of its XCD reads the same line): cached, and
+//    issued first;
 //  - a cap on resident workgroups per CU, set by reserving dynamic LDS the
 //    kernels never touch: with the 3 to 17 concurrent streams of the update
 //    and reduce kernels, fewer resident waves (10 per CU for Adam, 16 or 24
@@ -448,11 +451,12 @@ __global__ __launch_bounds__(BS) void reduce_shift_kernel(ReduceLaunch L)
 {
     using FW = typename Fmt<LP>::FW;
     constexpr int K = kRedShiftK;
+    constexpr bool kNxEarly = LP == 3 ? kRedShiftNxEarlyF32 : kRedShiftNxEarly2B;
     static_assert(U == 1 || BS == 64, "runs of one lane chain across one wave only");
     int flag = 0;
     double ss = 0.0;
     const float inv_scale = check_inv_scale(L.inv_scale, L.dev);
-    const unsigned blk = shift_block(blockIdx.x, gridDim.x);
+    const unsigned blk = shift_block<shift_group<BS, U>()>(blockIdx.x, gridDim.x);
     const int64_t v0 = (int64_t)blk * (BS * U) + threadIdx.x;
     const bool last_lane = (threadIdx.x & 63) == 63;
     FW acc[U];
@@ -465,10 +469,24 @@ __global__ __launch_bounds__(BS) void reduce_shift_kernel(ReduceLaunch L)
     for (int k = 0; k < K; ++k) nx[k] = u4{0u, 0u, 0u, 0u};
     // Contributions r0 .. r0 + cnt - 1, every load in flight before the
     // arithmetic: lanes past the word after the body load that word again (a
-    // cache hit) rather than branch around their loads, and lane 63's extra
-    // words come after all the others.
+    // cache hit) rather than branch around their loads.  Lane 63's extra words
+    // go out before the others with the default cache policy for 2-byte data,
+    // after them and nontemporal for fp32 (kRedShiftNxEarly*).
     auto batch = [&](int r0, int cnt) {
         u4 lo[K][U];
+        auto load_nx = [&]() {
+            if (last_lane && v0 + (U - 1) * BS < L.nvec) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    if (k < cnt) {
+                        const char* p = static_cast<const char*>(adv<LP>(L.c.p[r0 + k], L.head));
+                        const void* base = p - ((uintptr_t)p & 15u);
+                        nx[k] = ld_v<u4, kNxEarly ? 0 : NT>(base, v0 + (U - 1) * BS + 1);
+                    }
+                }
+            }
+        };
+        if constexpr (kNxEarly) load_nx();
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             if (k < cnt) {
@@ -481,16 +499,7 @@ __global__ __launch_bounds__(BS) void reduce_shift_kernel(ReduceLaunch L)
                 }
             }
         }
-        if (last_lane && v0 + (U - 1) * BS < L.nvec) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                if (k < cnt) {
-                    const char* p = static_cast<const char*>(adv<LP>(L.c.p[r0 + k], L.head));
-                    const void* base = p - ((uintptr_t)p & 15u);
-                    nx[k] = ld_v<u4, NT>(base, v0 + (U - 1) * BS + 1);
-                }
-            }
-        }
+        if constexpr (!kNxEarly) load_nx();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
