@@ -40,7 +40,7 @@
  *    update then runs element-wise, measured 12-23% slower for an offset
  *    2-byte array on MI355X.  A bucket reduce whose contributions do not
  *    share the output's phase modulo 16 bytes cuts each contribution's runs
- *    out of aligned 16-byte loads (any phase, 2-byte or fp32), measured 4-10%
+ *    out of aligned 16-byte loads (any phase, 2-byte or fp32), measured 1-5%
  *    slower than aligned contributions.  Before any launch the library asks
  *    the HIP runtime about every array and contribution and refuses (INVALID_ARG)
  *    pageable host memory, another device's memory, and a range that runs
