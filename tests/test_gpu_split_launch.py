@@ -22,8 +22,8 @@ pytestmark = pytest.mark.gpu
 SPLIT_LIB = os.path.join(ROOT, "zero_dp_sharded_amd", "variants", "split_launch",
                          "libzeroshard.so")
 FILES = ["test_gpu_parity.py", "test_gpu_edges.py", "test_gpu_variants.py", "test_gpu_phases.py",
-         "test_gpu_clip_device.py", "test_gpu_inline_fold.py", "test_gpu_random.py",
-         "test_gpu_shapes.py", "test_gpu_scale.py", "test_gpu_stage1.py",
+         "test_gpu_random_phases.py", "test_gpu_clip_device.py", "test_gpu_inline_fold.py",
+         "test_gpu_random.py", "test_gpu_shapes.py", "test_gpu_scale.py", "test_gpu_stage1.py",
          "test_gpu_extremes.py", "test_zz_no_alloc.py"]
 
 PROBE = r"""
