@@ -10,11 +10,17 @@ instruction out of the kernels, and likewise the packed-fp32 arithmetic the
 build disables."""
 import re
 
+import pytest
+
 from zero_dp_sharded_amd import build
 
 
-def test_kernels_have_no_fused_narrowing_or_packed_fp32():
-    asm = build.device_asm("zero_kernels.hip")
+@pytest.fixture(scope="module")
+def asm():
+    return build.device_asm("zero_kernels.hip")
+
+
+def test_kernels_have_no_fused_narrowing_or_packed_fp32(asm):
     body = [ln for ln in asm.splitlines() if ln.startswith("\t") and not ln.startswith("\t.")]
     assert len(body) > 1000
     bad = [ln.strip() for ln in body
@@ -22,3 +28,26 @@ def test_kernels_have_no_fused_narrowing_or_packed_fp32():
     assert bad == [], bad[:8]
     # the fp16 narrowing is a plain conversion
     assert any(re.match(r"\s*v_cvt_(pk_)?f16_f32", ln) for ln in body)
+
+
+def test_shift_reduce_loads_the_word_past_its_runs_as_measured(asm):
+    """In every streaming (nontemporal) shift reduce, lane 63's word past its
+    runs goes out, for 2-byte data, before that batch's contribution runs and
+    without the nontemporal hint (the next workgroup of the XCD then finds the
+    line in L2), and for fp32 after them, nontemporal (issued first it made
+    every wave wait for it).  The sequence of 16-byte loads shows it: plain
+    loads (c) then nontemporal ones (N) per batch for 2-byte data, all N for
+    fp32.  (Kernels that also copy the step's state snapshot, with plain
+    16-byte loads at their end, are left out.)"""
+    names = re.findall(r"^(_Z\S*reduce_shift_kernelILi(\d)ELi(\d+)ELi(\d)ELi(\d+)ELi0ELi1E\S*):",
+                       asm, re.M)
+    assert len(names) >= 8
+    for name, lp, rt, u, bs in names:
+        body = asm[asm.index(name + ":"):]
+        body = body[:body.index(".Lfunc_end")]
+        seq = "".join("N" if " nt" in ln else "c" for ln in body.splitlines()
+                      if "global_load_dwordx4" in ln)
+        if lp == "3":
+            assert re.fullmatch(r"N+", seq), (name, seq)
+        else:
+            assert re.fullmatch(r"(c{1,4}N+)+", seq), (name, seq)
