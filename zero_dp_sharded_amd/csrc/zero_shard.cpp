@@ -18,6 +18,7 @@
 
 #include "../../include/zero_shard.h"
 #include "zero_kernels.h"
+#include "zero_layout.h"
 
 namespace {
 
@@ -214,38 +215,6 @@ zero_status check_sgd_hparams(const zero_sgd_hparams* hp, bool has_buffer)
 
 // Bytes per stored gradient / parameter element of a storage format.
 int lp_bytes(zero_lp_dtype lp) { return lp == ZERO_FP32 ? 4 : 2; }
-
-// Leading elements to peel so that every listed address, advanced by that many
-// elements of size elt[k], is aligned to align[k] bytes; -1 if none below 8
-// exists.
-int64_t common_head(const uintptr_t* addr, const int* elt, const int* align, int count)
-{
-    for (int64_t h = 0; h < 8; ++h) {
-        bool ok = true;
-        for (int k = 0; k < count && ok; ++k)
-            ok = ((addr[k] + (uintptr_t)h * elt[k]) % (uintptr_t)align[k]) == 0;
-        if (ok) return h;
-    }
-    return -1;
-}
-
-// Layout of n elements for a kernel working on runs of `run` elements:
-// `head` scalar elements, then nrun aligned runs, then a scalar tail.
-// head < 0 (no common alignment) selects the element-wise path.
-void split(int64_t n, int64_t head, int64_t run, int64_t* out_head, int64_t* out_nrun,
-           int32_t* vec_ok)
-{
-    if (head < 0) {
-        *vec_ok = 0;
-        *out_head = 0;
-        *out_nrun = 0;
-        return;
-    }
-    if (head > n) head = n;
-    *vec_ok = 1;
-    *out_head = head;
-    *out_nrun = (n - head) / run;
-}
 
 // Dynamic LDS that leaves room for `per_cu` workgroups of a kernel per CU.
 uint32_t lds_reserve_for(int lds_per_cu, int lds_per_block_max, int per_cu)
@@ -584,42 +553,23 @@ static zero_status enqueue_reduce(zero_shard_s* h, const void* const* ptrs, int3
     zk::ReduceLaunch L;
     std::memset(&L, 0, sizeof(L));
     uintptr_t addr[ZERO_MAX_CONTRIB + 1];
-    int elt[ZERO_MAX_CONTRIB + 1], align[ZERO_MAX_CONTRIB + 1];
     for (int r = 0; r < n_contrib; ++r) {
         L.c.p[r] = ptrs[r];
         addr[r] = (uintptr_t)ptrs[r];
-        elt[r] = h->esz;
-        align[r] = 16;
     }
     char* out = static_cast<char*>(h->d.grad_shard) + off * h->esz;
     addr[n_contrib] = (uintptr_t)out;
-    elt[n_contrib] = h->esz;
-    align[n_contrib] = 16;
     L.out = out;
     L.n = len;
     const int W = zk::run_width(h->d.lp);
     // whole 16-byte runs when every array shares its address phase modulo 16;
-    // else the shift kernel: the output 16-byte aligned from head, each
-    // contribution read at its own phase s_r (head >= s_r elements, one whole
-    // run kept after the body)
-    const int64_t head = common_head(addr, elt, align, n_contrib + 1);
-    L.shift = 0;
-    int64_t h0 = head >= 0 ? -1 : common_head(&addr[n_contrib], &elt[n_contrib], &align[n_contrib], 1);
-    if (h0 < 0) {
-        split(len, head, W, &L.head, &L.nvec, &L.vec_ok);
-    } else {
-        int64_t smax = 0;
-        for (int r = 0; r < n_contrib; ++r) {
-            const int64_t sr = (int64_t)((addr[r] + (uintptr_t)h0 * h->esz) & 15u) / h->esz;
-            if (sr > smax) smax = sr;
-        }
-        if (smax > h0) h0 += W;
-        L.shift = 1;
-        L.vec_ok = 1;
-        L.head = h0 < len ? h0 : len;
-        const int64_t whole = (len - L.head) / W;
-        L.nvec = whole > 1 ? whole - 1 : 0;
-    }
+    // else the shift kernel (each contribution read at its own phase), else
+    // element by element
+    const zl::ReduceLayout lay = zl::reduce_layout(addr, n_contrib, h->esz, len);
+    L.shift = lay.shift;
+    L.vec_ok = lay.vec_ok;
+    L.head = lay.head;
+    L.nvec = lay.nvec;
     L.R = n_contrib;
     L.lp = (int32_t)h->d.lp;
     L.inv_r = (float)(1.0 / (double)n_contrib);
@@ -765,7 +715,7 @@ static zero_status enqueue_scan(zero_shard_s* h, const zk::DevState* dev, hipStr
     const int W = zk::run_width(h->d.lp);
     L.g = h->d.grad_shard;
     L.n = h->S;
-    split(h->S, common_head(&a, &el, &al, 1), W, &L.head, &L.nvec, &L.vec_ok);
+    zl::split(h->S, zl::common_head(&a, &el, &al, 1), W, &L.head, &L.nvec, &L.vec_ok);
     L.lp = (int32_t)h->d.lp;
     L.inv_scale = (float)(1.0 / h->scale);
     L.partial = h->partial;
@@ -864,7 +814,7 @@ static void update_layout(const zero_shard_s* h, int64_t* head, int64_t* ngroups
         align[cnt] = 4 * el[k];
         ++cnt;
     }
-    split(h->S, common_head(addr, elt, align, cnt), 4, head, ngroups, vec_ok);
+    zl::split(h->S, zl::common_head(addr, elt, align, cnt), 4, head, ngroups, vec_ok);
 }
 
 // Whether a device-resident step with `slots` partials folds them inside the
