@@ -44,6 +44,8 @@ PHASES = {
     "nine contributions": ([2, 4, 6, 8, 10, 12, 14, 0, 2], 4),
     # sixteen: the compiled-in count, four batches
     "sixteen contributions": ([(2 * r) % 16 for r in range(16)], 10),
+    # the most the library takes: sixteen batches in the kernel's run-time loop
+    "sixty-four contributions": ([(2 * (5 * r + r // 8)) % 16 for r in range(64)], 12),
 }
 
 
