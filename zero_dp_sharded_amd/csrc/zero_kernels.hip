@@ -283,6 +283,11 @@ __device__ __forceinline__ void snapshot_state(const DevState* dev, DevState* sn
     if (snap != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *snap = *dev;
 }
 // The unscale factor of a check: the launch argument, or the device state's.
+// The vector reduce and scan kernels read it after issuing their loads (but
+// for a contribution count that is not compiled in): read first, its scalar
+// load made every wave wait for that round trip before loading (a wave waits
+// for all its outstanding scalar loads at once, and the loads' addresses come
+// from scalar loads of the launch arguments).
 __device__ __forceinline__ float check_inv_scale(float arg, const DevState* dev)
 {
     return dev != nullptr ? dev->inv_scale : arg;
@@ -300,7 +305,7 @@ __global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
     using FW = typename Fmt<LP>::FW;
     int flag = 0;
     double ss = 0.0;
-    const float inv_scale = check_inv_scale(L.inv_scale, L.dev);
+    float inv_scale;
     const int64_t v0 = (int64_t)blockIdx.x * (BS * U) + threadIdx.x;
     if constexpr (RT > 0 && RT <= 8 && U == 1) {
         // One run per lane, up to 8 contributions: their loads in groups of
@@ -327,6 +332,7 @@ __global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
                 for (int k = 0; k < G; ++k) acc = acc + __builtin_convertvector(x[k], FW);
             }
         }
+        inv_scale = check_inv_scale(L.inv_scale, L.dev);
         if (v0 < L.nvec) reduce_finish<LP, NT>(L, v0, acc, inv_scale, flag, ss);
     } else if constexpr (RT > 0) {
         // Several runs per lane, or 16 contributions.  Each run's loads sit
@@ -346,6 +352,7 @@ __global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
                 for (int r = 0; r < RT; ++r) x[u][r] = ld_v<VW, NT>(adv<LP>(L.c.p[r], L.head), vi);
             }
         }
+        inv_scale = check_inv_scale(L.inv_scale, L.dev);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t vi = v0 + u * BS;
@@ -358,6 +365,7 @@ __global__ __launch_bounds__(BS) void reduce_vec_kernel(ReduceLaunch L)
         }
     } else {
         // a contribution count known only at run time: batches of 8
+        inv_scale = check_inv_scale(L.inv_scale, L.dev);
         for (int u = 0; u < U; ++u) {
             const int64_t vi = v0 + u * BS;
             if (vi >= L.nvec) break;
@@ -455,7 +463,6 @@ __global__ __launch_bounds__(BS) void reduce_shift_kernel(ReduceLaunch L)
     static_assert(U == 1 || BS == 64, "runs of one lane chain across one wave only");
     int flag = 0;
     double ss = 0.0;
-    const float inv_scale = check_inv_scale(L.inv_scale, L.dev);
     const unsigned blk = shift_block<shift_group<BS, U>()>(blockIdx.x, gridDim.x);
     const int64_t v0 = (int64_t)blk * (BS * U) + threadIdx.x;
     const bool last_lane = (threadIdx.x & 63) == 63;
@@ -522,6 +529,7 @@ __global__ __launch_bounds__(BS) void reduce_shift_kernel(ReduceLaunch L)
     } else {
         for (int r0 = 0; r0 < L.R; r0 += K) batch(r0, L.R - r0 < K ? L.R - r0 : K);
     }
+    const float inv_scale = check_inv_scale(L.inv_scale, L.dev);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t vi = v0 + u * BS;
@@ -555,7 +563,6 @@ __global__ __launch_bounds__(kScanBlock) void scan_vec_kernel(ScanLaunch L)
     using VW = typename Fmt<LP>::VW;
     int flag = 0;
     double ss = 0.0;
-    const float inv_scale = check_inv_scale(L.inv_scale, L.dev);
     const int64_t v0 = (int64_t)blockIdx.x * (kScanBlock * kScanRuns) + threadIdx.x;
     VW x[kScanRuns];
 #pragma unroll
@@ -563,6 +570,7 @@ __global__ __launch_bounds__(kScanBlock) void scan_vec_kernel(ScanLaunch L)
         const int64_t vi = v0 + u * kScanBlock;
         if (vi < L.nvec) x[u] = ld_nt<VW>(adv<LP>(L.g, L.head), vi);
     }
+    const float inv_scale = check_inv_scale(L.inv_scale, L.dev);
 #pragma unroll
     for (int u = 0; u < kScanRuns; ++u)
         if (v0 + u * kScanBlock < L.nvec) check_v<LP>(x[u], inv_scale, flag, ss);
