@@ -178,16 +178,60 @@ __device__ __forceinline__ void check_s(typename Fmt<LP>::T o, float inv_scale, 
 // One fp64 partial per workgroup: the sum of its lanes' squares, or NaN when
 // any lane saw a non-finite unscaled value.  Fixed reduction shape, so the
 // value is bitwise reproducible.
+// Wave butterflies.  Each lane adds (or ORs) its partner's value at lane
+// distance 32, 16, 8, 4, 2 and 1, in that order, and ends with the total of
+// the wave, as a butterfly of xor shuffles computes it (the same operations
+// on the same values, so the same bits).  The first two steps cross rows of 16
+// lanes by shuffle; the last four stay inside rows and use DPP: row_ror:8
+// hands lane l the value of lane l ^ 8; after that step lanes l and l ^ 8
+// agree, so row_ror:4 hands it the value of lane l ^ 4; quad_perm swaps lanes
+// l and l ^ 2, then l and l ^ 1.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint64_t lo = dpp_u32<CTRL>((uint32_t)u), hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+
+constexpr int kDppRowRor8 = 0x128, kDppRowRor4 = 0x124;
+constexpr int kDppQuadXor2 = 0x4E, kDppQuadXor1 = 0xB1;   // quad_perm [2,3,0,1], [1,0,3,2]
+
+__device__ __forceinline__ double wave_sum(double x)
+{
+    x += __shfl_xor(x, 32, 64);
+    x += __shfl_xor(x, 16, 64);
+    x += dpp_f64<kDppRowRor8>(x);
+    x += dpp_f64<kDppRowRor4>(x);
+    x += dpp_f64<kDppQuadXor2>(x);
+    x += dpp_f64<kDppQuadXor1>(x);
+    return x;
+}
+
+__device__ __forceinline__ int wave_or(int f)
+{
+    f |= __shfl_xor(f, 32, 64);
+    f |= __shfl_xor(f, 16, 64);
+    f |= (int)dpp_u32<kDppRowRor8>((uint32_t)f);
+    f |= (int)dpp_u32<kDppRowRor4>((uint32_t)f);
+    f |= (int)dpp_u32<kDppQuadXor2>((uint32_t)f);
+    f |= (int)dpp_u32<kDppQuadXor1>((uint32_t)f);
+    return f;
+}
+
 template <int BS>
 __device__ __forceinline__ void block_partial(double* slot, int flag, double ss)
 {
     __shared__ double sh_ss[BS / 64];
     __shared__ int sh_f[BS / 64];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        ss += __shfl_xor(ss, off, 64);
-        flag |= __shfl_xor(flag, off, 64);
-    }
+    ss = wave_sum(ss);
+    flag = wave_or(flag);
     if ((threadIdx.x & 63) == 0) {
         sh_ss[threadIdx.x >> 6] = ss;
         sh_f[threadIdx.x >> 6] = flag;
@@ -752,10 +796,7 @@ __device__ __forceinline__ double fold_small_t(const double* p, int n)
         w[k] = s;
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) w[k] += __shfl_xor(w[k], off, 64);
-    }
+    for (int k = 0; k < 4; ++k) w[k] = wave_sum(w[k]);
     return ((w[0] + w[1]) + w[2]) + w[3];
 }
 
