@@ -133,10 +133,10 @@ constexpr int kRedShiftRuns = ZK_RED_SHIFT_RUNS;
 constexpr int kRedShiftGroupRuns = ZK_RED_SHIFT_GROUP_RUNS;
 // Lane 63's word past its last run: loaded before the contribution runs with
 // the default cache policy (true), or after them, nontemporal (false).  Early
-// and cached, for 2-byte data, it reads x1.005 of the algorithmic bytes instead
-// of x1.020 and runs 1-4 points faster; for fp32 it made every wave wait for
-// those loads before issuing its runs (8 points slower), so fp32 keeps them
-// last.
+// and cached, for 2-byte data, the reduce reads x1.005-1.006 of its
+// algorithmic bytes instead of x1.020 and runs 1-4 points faster; for fp32 it
+// made every wave wait for those loads before issuing its runs (8 points
+// slower), so fp32 keeps them last.
 constexpr bool kRedShiftNxEarly2B = ZK_RED_SHIFT_NX_EARLY_2B != 0;
 constexpr bool kRedShiftNxEarlyF32 = ZK_RED_SHIFT_NX_EARLY_F32 != 0;
 // Resident shift-kernel workgroups per CU below 8 contributions, and from 8
