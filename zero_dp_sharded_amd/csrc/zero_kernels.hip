@@ -800,9 +800,40 @@ __device__ __forceinline__ double fold_small_t(const double* p, int n)
     return ((w[0] + w[1]) + w[2]) + w[3];
 }
 
+// The same fold with a 256-lane workgroup's four waves each taking one of the
+// fold's waves: wave k loads and sums only the partials of fold wave k, and
+// the four totals meet in LDS and add in wave order (the same bits, a quarter
+// of the loads and butterflies per wave).
+template <int T>
+__device__ __forceinline__ double fold_split_t(const double* p, int n)
+{
+    __shared__ double sh_w[4];
+    const int k = (int)(threadIdx.x >> 6);
+    double x[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int i = (int)(threadIdx.x & 63) + 64 * k + 256 * t;
+        x[t] = p[i < n ? i : 0];
+    }
+    double s = 0.0;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int i = (int)(threadIdx.x & 63) + 64 * k + 256 * t;
+        if (i < n) s += x[t];
+    }
+    s = wave_sum(s);
+    if ((threadIdx.x & 63) == 0) sh_w[k] = s;
+    __syncthreads();
+    return ((sh_w[0] + sh_w[1]) + sh_w[2]) + sh_w[3];
+}
+
+template <int B>
 __device__ __forceinline__ double fold_small(const double* p, int n)
 {
-    return n <= 256 ? fold_small_t<1>(p, n) : fold_small_t<2>(p, n);
+    if constexpr (B == 256)
+        return n <= 256 ? fold_split_t<1>(p, n) : fold_split_t<2>(p, n);
+    else
+        return n <= 256 ? fold_small_t<1>(p, n) : fold_small_t<2>(p, n);
 }
 
 // The step as the fold's last lane decides it, computed by every workgroup
@@ -813,10 +844,11 @@ struct InlineDecision {
     float clip;
 };
 
+template <int B>
 __device__ __forceinline__ StepVals step_vals_inline(const InlineFold& f, InlineDecision& d)
 {
     d.next = *f.snapshot;                  // loaded while the partials are in flight
-    d.sumsq = fold_small(f.partial, f.n);
+    d.sumsq = fold_small<B>(f.partial, f.n);
     prepare_step(&d.next, d.sumsq, f.pa);
     d.clip = clip_coef(d.sumsq, f.max_norm);
     return StepVals{d.next.upd_inv_scale, d.next.bc1, d.next.bc2, d.clip, d.next.skip != 0};
@@ -885,7 +917,7 @@ __global__ __launch_bounds__(B) void adam_vec_kernel(AdamLaunch a)
     StepVals sv;
     InlineDecision dec;
     if constexpr (INL) {
-        sv = step_vals_inline(a.src.fold, dec);
+        sv = step_vals_inline<B>(a.src.fold, dec);
     } else {
         sv = step_vals(a.src, a.inv_scale, a.bc1, a.bc2);
         if (sv.skip) return;
@@ -978,7 +1010,7 @@ __global__ __launch_bounds__(B) void sgd_vec_kernel(SgdLaunch a)
     StepVals sv;
     InlineDecision dec;
     if constexpr (INL) {
-        sv = step_vals_inline(a.src.fold, dec);
+        sv = step_vals_inline<B>(a.src.fold, dec);
     } else {
         sv = step_vals(a.src, a.inv_scale, 1.0f, 1.0f);
         if (sv.skip) return;
