@@ -803,24 +803,32 @@ __device__ __forceinline__ double fold_small_t(const double* p, int n)
 // The same fold with a 256-lane workgroup's four waves each taking one of the
 // fold's waves: wave k loads and sums only the partials of fold wave k, and
 // the four totals meet in LDS and add in wave order (the same bits, a quarter
-// of the loads and butterflies per wave).
-template <int T>
-__device__ __forceinline__ double fold_split_t(const double* p, int n)
+// of the loads and butterflies per wave).  The kernels issue these loads
+// before their own, so that the fold's arithmetic overlaps the wait for their
+// data: lane l of wave k loads partials l + 64k and l + 64k + 256 (the second
+// is added only when there are more than 256, as the fold kernel does; below
+// that it loads partial 0 again).
+struct FoldLoads {
+    double x[2];
+};
+
+__device__ __forceinline__ FoldLoads fold_split_issue(const double* p, int n)
+{
+    FoldLoads fl;
+    const int i = (int)(threadIdx.x & 63) + 64 * (int)(threadIdx.x >> 6);
+    fl.x[0] = p[i < n ? i : 0];
+    fl.x[1] = p[i + 256 < n ? i + 256 : 0];
+    return fl;
+}
+
+__device__ __forceinline__ double fold_split_finish(const FoldLoads& fl, int n)
 {
     __shared__ double sh_w[4];
     const int k = (int)(threadIdx.x >> 6);
-    double x[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const int i = (int)(threadIdx.x & 63) + 64 * k + 256 * t;
-        x[t] = p[i < n ? i : 0];
-    }
+    const int i = (int)(threadIdx.x & 63) + 64 * k;
     double s = 0.0;
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const int i = (int)(threadIdx.x & 63) + 64 * k + 256 * t;
-        if (i < n) s += x[t];
-    }
+    if (i < n) s += fl.x[0];
+    if (i + 256 < n) s += fl.x[1];
     s = wave_sum(s);
     if ((threadIdx.x & 63) == 0) sh_w[k] = s;
     __syncthreads();
@@ -828,12 +836,22 @@ __device__ __forceinline__ double fold_split_t(const double* p, int n)
 }
 
 template <int B>
-__device__ __forceinline__ double fold_small(const double* p, int n)
+__device__ __forceinline__ FoldLoads fold_issue(const InlineFold& f)
 {
-    if constexpr (B == 256)
-        return n <= 256 ? fold_split_t<1>(p, n) : fold_split_t<2>(p, n);
-    else
+    if constexpr (B == 256) return fold_split_issue(f.partial, f.n);
+    else return FoldLoads{};
+}
+
+template <int B>
+__device__ __forceinline__ double fold_small(const double* p, int n, const FoldLoads& fl)
+{
+    if constexpr (B == 256) {
+        (void)p;
+        return fold_split_finish(fl, n);
+    } else {
+        (void)fl;
         return n <= 256 ? fold_small_t<1>(p, n) : fold_small_t<2>(p, n);
+    }
 }
 
 // The step as the fold's last lane decides it, computed by every workgroup
@@ -845,10 +863,11 @@ struct InlineDecision {
 };
 
 template <int B>
-__device__ __forceinline__ StepVals step_vals_inline(const InlineFold& f, InlineDecision& d)
+__device__ __forceinline__ StepVals step_vals_inline(const InlineFold& f, const FoldLoads& fl,
+                                                     InlineDecision& d)
 {
     d.next = *f.snapshot;                  // loaded while the partials are in flight
-    d.sumsq = fold_small<B>(f.partial, f.n);
+    d.sumsq = fold_small<B>(f.partial, f.n, fl);
     prepare_step(&d.next, d.sumsq, f.pa);
     d.clip = clip_coef(d.sumsq, f.max_norm);
     return StepVals{d.next.upd_inv_scale, d.next.bc1, d.next.bc2, d.clip, d.next.skip != 0};
@@ -902,22 +921,32 @@ __global__ __launch_bounds__(B) void adam_vec_kernel(AdamLaunch a)
     float* mb = a.m + a.head;
     float* vb = a.v + a.head;
     const int64_t q0 = (int64_t)blockIdx.x * (B * G) + threadIdx.x;
+    FoldLoads fl{};
+    if constexpr (INL) {
+        fl = fold_issue<B>(a.src.fold);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     V4 g[G];
     f4 p[G], m[G], v[G];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
         const int64_t q = q0 + u * B;
-        if (q < a.ngroups) {
-            g[u] = ld_v<V4, NT>(gb, q);
-            p[u] = ld_v<f4, NT>(pb, q);
-            m[u] = ld_v<f4, NT>(mb, q);
-            v[u] = ld_v<f4, NT>(vb, q);
+        if (INL || q < a.ngroups) {
+            // (an inline-fold launch has groups: lanes past them reload the
+            // last one, so that no branch hides from the compiler how many
+            // loads follow the fold's)
+            const int64_t qc = q < a.ngroups ? q : a.ngroups - 1;
+            g[u] = ld_v<V4, NT>(gb, qc);
+            p[u] = ld_v<f4, NT>(pb, qc);
+            m[u] = ld_v<f4, NT>(mb, qc);
+            v[u] = ld_v<f4, NT>(vb, qc);
         }
     }
+    if constexpr (INL) __builtin_amdgcn_sched_barrier(0);   // the fold's arithmetic after every load
     StepVals sv;
     InlineDecision dec;
     if constexpr (INL) {
-        sv = step_vals_inline<B>(a.src.fold, dec);
+        sv = step_vals_inline<B>(a.src.fold, fl, dec);
     } else {
         sv = step_vals(a.src, a.inv_scale, a.bc1, a.bc2);
         if (sv.skip) return;
@@ -996,21 +1025,28 @@ __global__ __launch_bounds__(B) void sgd_vec_kernel(SgdLaunch a)
     float* pb = a.master + a.head;
     float* bb = MOM ? a.mom + a.head : nullptr;
     const int64_t q0 = (int64_t)blockIdx.x * (B * G) + threadIdx.x;
+    FoldLoads fl{};
+    if constexpr (INL) {
+        fl = fold_issue<B>(a.src.fold);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     V4 g[G];
     f4 p[G], b[G];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
         const int64_t q = q0 + u * B;
-        if (q < a.ngroups) {
-            g[u] = ld_v<V4, NT>(gb, q);
-            p[u] = ld_v<f4, NT>(pb, q);
-            if constexpr (MOM) b[u] = ld_v<f4, NT>(bb, q);
+        if (INL || q < a.ngroups) {
+            const int64_t qc = q < a.ngroups ? q : a.ngroups - 1;   // as in adam_vec_kernel
+            g[u] = ld_v<V4, NT>(gb, qc);
+            p[u] = ld_v<f4, NT>(pb, qc);
+            if constexpr (MOM) b[u] = ld_v<f4, NT>(bb, qc);
         }
     }
+    if constexpr (INL) __builtin_amdgcn_sched_barrier(0);
     StepVals sv;
     InlineDecision dec;
     if constexpr (INL) {
-        sv = step_vals_inline<B>(a.src.fold, dec);
+        sv = step_vals_inline<B>(a.src.fold, fl, dec);
     } else {
         sv = step_vals(a.src, a.inv_scale, 1.0f, 1.0f);
         if (sv.skip) return;
