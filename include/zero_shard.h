@@ -406,10 +406,10 @@ zero_status zero_step_resolve(zero_shard_t h, zero_step_info* out);
  *   - the update (Adam or SGD with the init hyper-parameters), which reads
  *     the decision and the step's scalars from device memory and writes
  *     nothing on a skipped step.
- * When the step has at most 512 per-workgroup partials and the update covers
+ * When the step has at most 1024 per-workgroup partials and the update covers
  * the shard in one vector launch (every array 16-byte aligned, S a multiple of
  * 4), the update itself folds the partials in the same fixed order and takes
- * the same decision, and its last workgroup advances the counters: one launch
+ * the same decision, and its workgroup 0 advances the counters: one launch
  * fewer, bitwise the same results (see zero_shard_inline_folds).
  * Because every launch argument is fixed for fixed contribution pointers,
  * the enqueue of zero_step_device may be captured in a HIP graph and

@@ -136,13 +136,15 @@ def test_device_flow_misaligned(name):
 
 
 @pytest.mark.parametrize("n,inline", [(300_007, 0), (300_000, 1), (2_097_152, 1),
-                                      (4_194_304, 1), (4_202_496, 0)])
+                                      (4_194_304, 1), (4_202_496, 1), (8_388_608, 1),
+                                      (8_396_800, 0)])
 def test_device_flow_scan_of_caller_filled_gradient(n, inline):
     """contribs = None: the device step scans grad_shard (the P_os case).  An
-    aligned shard of at most 512 scan workgroups of 8192 elements (2,097,152
-    elements: 256; 4,194,304: 512) folds the partials inside the update;
-    4,202,496 elements (513 workgroups) take the fold launch, and so do
-    300,007 elements, which leave the update a scalar tail."""
+    aligned shard of at most 1024 scan workgroups of 8192 elements (2,097,152
+    elements: 256; 4,194,304: 512; 4,202,496: 513; 8,388,608: 1024) folds the
+    partials inside the update; 8,396,800 elements (1025 workgroups) take the
+    fold launch, and so do 300,007 elements, which leave the update a scalar
+    tail."""
     dev = torch.device("cuda", 0)
     gen = torch.Generator(device=dev).manual_seed(5)
     master = torch.randn(n, generator=gen, device=dev) * 0.02

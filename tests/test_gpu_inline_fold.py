@@ -1,5 +1,5 @@
 """GPU parity of the fold inside the update, the device-resident step of small
-shards.  When a step has at most 512 per-workgroup partials and the update is
+shards.  When a step has at most 1024 per-workgroup partials and the update is
 one vector launch over the whole shard, every update workgroup folds the
 partials itself in the fold kernel's order and decides the step from the state
 snapshot the step's reduce took, and workgroup 0 advances the device counters.  The results must be bitwise
@@ -34,15 +34,19 @@ def _w(base, **over):
 
 
 # name -> (workload, shard elements, C_B): 256 partials (one partial per fold
-# lane) or 512 (two per lane, the limit)
+# lane), 512 (two per lane), 513 (the first count folded with four loads per
+# lane) or 1024 (four per lane, the limit)
 CASES = {
     "adam_fp16_r4": (_w(W["tiny"], steps=5), 524_288, 131_072),       # 4 x 64
     "adam_fp16_r4_512": (_w(W["tiny"], steps=5), 1_048_576, 1_048_576),   # 512
+    "adam_fp16_r4_513": (_w(W["tiny"], steps=5), 1_050_624, 1_050_624),   # 513
+    "adam_fp16_r4_1024": (_w(W["tiny"], steps=5), 2_097_152, 2_097_152),  # 1024
     "adam_bf16_r8": (_w(W["7.5b_bf16"], steps=5), 524_288, 262_144),  # 2 x 128
     "adam_fp16_r16": (_w(W["13b_inf"], steps=5, inject_step=None), 524_288, 524_288),  # 256
     "sgdm_fp32_r8": (_w(W["c1_7.5b_sgdm"], steps=5), 262_144, 262_144),  # 256
     "sgdm_fp32_r8_512": (_w(W["c1_7.5b_sgdm"], steps=5), 524_288, 131_072),  # 4 x 128
     "sgd_fp32_r8": (_w(W["c2_1.5b_sgd"], steps=5), 262_144, 131_072),  # 2 x 128
+    "sgdm_fp32_r8_1024": (_w(W["c1_7.5b_sgdm"], steps=5), 1_048_576, 262_144),  # 4 x 256
 }
 
 
@@ -108,7 +112,7 @@ def test_inline_fold_uninterrupted_steps(name):
 
 
 @pytest.mark.parametrize("elems,cb,why", [
-    (1_050_624, 1_050_624, "513 partials"),          # 131,328 runs / 256 per workgroup
+    (2_099_200, 2_099_200, "1025 partials"),         # 262,400 runs / 256 per workgroup
     (200_002, 200_002, "update with a scalar tail"),  # 98 partials, S not a multiple of 4
 ])
 def test_past_the_limits_takes_the_fold_launch(elems, cb, why):
@@ -136,7 +140,8 @@ def test_misaligned_update_takes_the_fold_launch():
     _same(a, b, "misaligned master")
 
 
-@pytest.mark.parametrize("name", ["adam_fp16_r4", "sgdm_fp32_r8", "adam_fp16_r4_512"])
+@pytest.mark.parametrize("name", ["adam_fp16_r4", "sgdm_fp32_r8", "adam_fp16_r4_512",
+                                  "adam_fp16_r4_1024"])
 def test_inline_fold_graph_replays(name):
     """Three inline-fold steps captured in one CUDA graph, replayed twice with
     eager refills of the contributions between replays (an overflow planted

@@ -368,7 +368,11 @@ struct ScanLaunch {
 // `dev` (and the check result) while the others still read: no counter, no
 // atomics.  This saves the fold's launch on launch-bound shards.  The update
 // must run as one vector launch with no element-wise part.
-constexpr int kInlineFoldMax = 512;
+#ifndef ZK_INLINE_FOLD_MAX
+#define ZK_INLINE_FOLD_MAX 1024
+#endif
+constexpr int kInlineFoldMax = ZK_INLINE_FOLD_MAX;   // 512 or 1024
+static_assert(kInlineFoldMax == 512 || kInlineFoldMax == 1024, "fold of 2 or 4 loads per lane");
 struct InlineFold {
     const double* partial;     // nullptr: off
     int32_t n;                 // partials, at most kInlineFoldMax

@@ -31,7 +31,7 @@
 // one fp64 partial per workgroup, then a fixed-order fold of one or two levels
 // whose last lane also computes the clipping coefficient and, in the
 // device-resident flow, decides the step.  A device-resident step of at most
-// 512 partials has no fold launch: every update workgroup repeats the fold in
+// 1024 partials has no fold launch: every update workgroup repeats the fold in
 // the same order and takes the same decision (see InlineFold).
 //
 // Storage formats: fp16 and bf16 (2-byte grads and params beside the fp32
@@ -764,13 +764,13 @@ __device__ __forceinline__ StepVals step_vals(const StepSource& src, float inv_s
     return v;
 }
 
-// The inline fold (InlineFold): the one-workgroup fold of at most 512
+// The inline fold (InlineFold): the one-workgroup fold of at most 1024
 // partials, reproduced by one wave.  Lane l stands for the fold's lanes l,
-// l+64, l+128 and l+192; fold lane j adds the partials j, j+256 (T = 2 when
-// there are more than 256) to 0.0 in that order, the four 64-lane butterflies
-// are the fold's four waves, and their totals add in wave order, so the sum is
-// bitwise the fold kernel's.  Every lane ends with the same value.  (Up to 1024
-// partials, T = 4, the redundant loads cost what the fold launch saves.)
+// l+64, l+128 and l+192; fold lane j adds the partials j, j+256, j+512, j+768
+// (those below n) to 0.0 in that order, the four 64-lane butterflies are the
+// fold's four waves, and their totals add in wave order, so the sum is bitwise
+// the fold kernel's.  Every lane ends with the same value.  (Workgroups of 256
+// lanes split it over their four waves instead, below.)
 template <int T>
 __device__ __forceinline__ double fold_small_t(const double* p, int n)
 {
@@ -809,47 +809,54 @@ __device__ __forceinline__ double fold_small_t(const double* p, int n)
 // is added only when there are more than 256, as the fold kernel does; below
 // that it loads partial 0 again).
 struct FoldLoads {
-    double x[2];
+    double x[4];
 };
 
+// T loads per lane: partials l + 64k + 256t, t < T (T = 2 up to 512
+// partials, 4 up to 1024).
+template <int T>
 __device__ __forceinline__ FoldLoads fold_split_issue(const double* p, int n)
 {
     FoldLoads fl;
     const int i = (int)(threadIdx.x & 63) + 64 * (int)(threadIdx.x >> 6);
-    fl.x[0] = p[i < n ? i : 0];
-    fl.x[1] = p[i + 256 < n ? i + 256 : 0];
+#pragma unroll
+    for (int t = 0; t < T; ++t) fl.x[t] = p[i + 256 * t < n ? i + 256 * t : 0];
     return fl;
 }
 
+template <int T>
 __device__ __forceinline__ double fold_split_finish(const FoldLoads& fl, int n)
 {
     __shared__ double sh_w[4];
     const int k = (int)(threadIdx.x >> 6);
     const int i = (int)(threadIdx.x & 63) + 64 * k;
     double s = 0.0;
-    if (i < n) s += fl.x[0];
-    if (i + 256 < n) s += fl.x[1];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        if (i + 256 * t < n) s += fl.x[t];
     s = wave_sum(s);
     if ((threadIdx.x & 63) == 0) sh_w[k] = s;
     __syncthreads();
     return ((sh_w[0] + sh_w[1]) + sh_w[2]) + sh_w[3];
 }
 
-template <int B>
+template <int B, int T>
 __device__ __forceinline__ FoldLoads fold_issue(const InlineFold& f)
 {
-    if constexpr (B == 256) return fold_split_issue(f.partial, f.n);
+    if constexpr (B == 256) return fold_split_issue<T>(f.partial, f.n);
     else return FoldLoads{};
 }
 
-template <int B>
+template <int B, int T>
 __device__ __forceinline__ double fold_small(const double* p, int n, const FoldLoads& fl)
 {
     if constexpr (B == 256) {
         (void)p;
-        return fold_split_finish(fl, n);
+        return fold_split_finish<T>(fl, n);
     } else {
         (void)fl;
+        if constexpr (kInlineFoldMax > 512)
+            if (n > 512) return fold_small_t<4>(p, n);
         return n <= 256 ? fold_small_t<1>(p, n) : fold_small_t<2>(p, n);
     }
 }
@@ -862,12 +869,12 @@ struct InlineDecision {
     float clip;
 };
 
-template <int B>
+template <int B, int T>
 __device__ __forceinline__ StepVals step_vals_inline(const InlineFold& f, const FoldLoads& fl,
                                                      InlineDecision& d)
 {
     d.next = *f.snapshot;                  // loaded while the partials are in flight
-    d.sumsq = fold_small<B>(f.partial, f.n, fl);
+    d.sumsq = fold_small<B, T>(f.partial, f.n, fl);
     prepare_step(&d.next, d.sumsq, f.pa);
     d.clip = clip_coef(d.sumsq, f.max_norm);
     return StepVals{d.next.upd_inv_scale, d.next.bc1, d.next.bc2, d.clip, d.next.skip != 0};
@@ -910,7 +917,8 @@ __device__ __forceinline__ void adam_e(float graw, float& p, float& m, float& v,
 // covers groups [b*B*G, (b+1)*B*G) for B lanes and G groups per lane; lane l
 // owns groups b*B*G + u*B + l, u < G, and issues all loads before any
 // arithmetic.  With fp32 storage there is no 2-byte parameter to write.
-// INL = 1: the step's values come from the inline fold (a.src.fold).  NT as
+// INL > 0: the step's values come from the inline fold (a.src.fold), whose
+// partials each lane loads INL of (2 up to 512 partials, 4 up to 1024).  NT as
 // for the reduce (plain loads and stores for small shards).
 template <int LP, int WD, int INL, int B, int G, int NT>
 __global__ __launch_bounds__(B) void adam_vec_kernel(AdamLaunch a)
@@ -923,7 +931,7 @@ __global__ __launch_bounds__(B) void adam_vec_kernel(AdamLaunch a)
     const int64_t q0 = (int64_t)blockIdx.x * (B * G) + threadIdx.x;
     FoldLoads fl{};
     if constexpr (INL) {
-        fl = fold_issue<B>(a.src.fold);
+        fl = fold_issue<B, INL>(a.src.fold);
         __builtin_amdgcn_sched_barrier(0);
     }
     V4 g[G];
@@ -946,7 +954,7 @@ __global__ __launch_bounds__(B) void adam_vec_kernel(AdamLaunch a)
     StepVals sv;
     InlineDecision dec;
     if constexpr (INL) {
-        sv = step_vals_inline<B>(a.src.fold, fl, dec);
+        sv = step_vals_inline<B, INL>(a.src.fold, fl, dec);
     } else {
         sv = step_vals(a.src, a.inv_scale, a.bc1, a.bc2);
         if (sv.skip) return;
@@ -1027,7 +1035,7 @@ __global__ __launch_bounds__(B) void sgd_vec_kernel(SgdLaunch a)
     const int64_t q0 = (int64_t)blockIdx.x * (B * G) + threadIdx.x;
     FoldLoads fl{};
     if constexpr (INL) {
-        fl = fold_issue<B>(a.src.fold);
+        fl = fold_issue<B, INL>(a.src.fold);
         __builtin_amdgcn_sched_barrier(0);
     }
     V4 g[G];
@@ -1046,7 +1054,7 @@ __global__ __launch_bounds__(B) void sgd_vec_kernel(SgdLaunch a)
     StepVals sv;
     InlineDecision dec;
     if constexpr (INL) {
-        sv = step_vals_inline<B>(a.src.fold, fl, dec);
+        sv = step_vals_inline<B, INL>(a.src.fold, fl, dec);
     } else {
         sv = step_vals(a.src, a.inv_scale, 1.0f, 1.0f);
         if (sv.skip) return;
@@ -1292,7 +1300,10 @@ hipError_t adam_vec_launches(const AdamLaunch& a, int64_t vblocks, hipStream_t s
 {
     constexpr int64_t groups_per_block = (int64_t)B * G;
     if (a.src.fold.partial != nullptr) {
-        adam_vec_kernel<LP, WD, 1, B, G, NT><<<(unsigned)vblocks, B, a.lds_reserve, s>>>(a);
+        if (a.src.fold.n <= 512)
+            adam_vec_kernel<LP, WD, 2, B, G, NT><<<(unsigned)vblocks, B, a.lds_reserve, s>>>(a);
+        else
+            adam_vec_kernel<LP, WD, 4, B, G, NT><<<(unsigned)vblocks, B, a.lds_reserve, s>>>(a);
         return hipGetLastError();
     }
     const int64_t max_blocks = kMaxLaunchItems / B;
@@ -1343,7 +1354,10 @@ hipError_t sgd_vec_launches(const SgdLaunch& a, int64_t vblocks, hipStream_t s)
 {
     constexpr int64_t groups_per_block = (int64_t)B * G;
     if (a.src.fold.partial != nullptr) {
-        sgd_vec_kernel<LP, MOM, WD, G, 1, B, NT><<<(unsigned)vblocks, B, a.lds_reserve, s>>>(a);
+        if (a.src.fold.n <= 512)
+            sgd_vec_kernel<LP, MOM, WD, G, 2, B, NT><<<(unsigned)vblocks, B, a.lds_reserve, s>>>(a);
+        else
+            sgd_vec_kernel<LP, MOM, WD, G, 4, B, NT><<<(unsigned)vblocks, B, a.lds_reserve, s>>>(a);
         return hipGetLastError();
     }
     const int64_t max_blocks = kMaxLaunchItems / B;
